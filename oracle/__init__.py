@@ -1,0 +1,154 @@
+"""Python access to the CPU oracle (``oracle.cpp``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check and by the
+benchmark's CPU-baseline leg. The product path never imports this module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+CXXFLAGS = ["-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(_LIB_PATH):
+        subprocess.run(["g++", *CXXFLAGS, _SRC, "-o", _LIB_PATH + ".tmp"], check=True)
+        os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        p, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_doc_begin.argtypes = [p, i32, i64]
+        L.oracle_doc_begin.restype = i64
+        L.oracle_key_layernorm.argtypes = [p, i64, i32, p, p, d, p, p]
+        L.oracle_index_scores.argtypes = [p, p, i32, i32, p, i64, i64, p]
+        L.oracle_index_score_scale.argtypes = [p, p, i32, i32, p, i64, i64, p]
+        L.oracle_topk.argtypes = [i64, p, p, p, i32, i32, p, p, i32, i32, p, p, p]
+        L.oracle_sparse_mla.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
+        L.oracle_dense_causal.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def _opt(a, dtype):
+    if a is None:
+        return None, None
+    return _c(a, dtype)
+
+
+def key_layernorm(k_I, eps=1e-5, gamma=None, beta=None, want_pre=False):
+    k_I, pk = _c(k_I, np.uint16)
+    T, d_I = k_I.shape
+    out = np.empty_like(k_I)
+    pre = np.empty((T, d_I), dtype=np.float64) if want_pre else None
+    g, pg = _opt(gamma, np.float32)
+    b, pb = _opt(beta, np.float32)
+    lib().oracle_key_layernorm(pk, T, d_I, pg, pb, eps, out.ctypes.data, pre.ctypes.data if want_pre else None)
+    return (out, pre) if want_pre else out
+
+
+def doc_begin(cu_seqlens, t):
+    cu, pc = _c(cu_seqlens, np.int32)
+    return int(lib().oracle_doc_begin(pc, len(cu) - 1, t))
+
+
+def index_scores(qI_row, w_row, LNk, s0, s1):
+    """FP32 scores of one query (qI_row [H_I,d_I], w_row [H_I]) over keys s0..s1 inclusive."""
+    q, pq = _c(qI_row, np.uint16)
+    w, pw = _c(w_row, np.uint16)
+    L, pl = _c(LNk, np.uint16)
+    H_I, d_I = q.shape
+    out = np.empty(s1 - s0 + 1, dtype=np.float32)
+    lib().oracle_index_scores(pq, pw, H_I, d_I, pl, s0, s1, out.ctypes.data)
+    return out
+
+
+def index_score_scale(qI_row, w_row, LNk, s0, s1):
+    q, pq = _c(qI_row, np.uint16)
+    w, pw = _c(w_row, np.uint16)
+    L, pl = _c(LNk, np.uint16)
+    H_I, d_I = q.shape
+    out = np.empty(s1 - s0 + 1, dtype=np.float64)
+    lib().oracle_index_score_scale(pq, pw, H_I, d_I, pl, s0, s1, out.ctypes.data)
+    return out
+
+
+def topk(rows, qI_rows, w_rows, LNk, cu_seqlens, k):
+    """Top-k indices of the listed global rows; returns (idx [n,k] int32, theta [n], keff [n])."""
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(qI_rows, np.uint16)
+    w, pw = _c(w_rows, np.uint16)
+    L, pl = _c(LNk, np.uint16)
+    cu, pc = _c(cu_seqlens, np.int32)
+    n = len(rows)
+    H_I, d_I = q.shape[-2], q.shape[-1]
+    idx = np.empty((n, k), dtype=np.int32)
+    theta = np.empty(n, dtype=np.float32)
+    keff = np.empty(n, dtype=np.int32)
+    lib().oracle_topk(n, pr, pq, pw, H_I, d_I, pl, pc, len(cu) - 1, k, idx.ctypes.data, theta.ctypes.data,
+                      keff.ctypes.data)
+    return idx, theta, keff
+
+
+def sparse_mla(rows, q_rows, kv, idx, W_UV, gate_rows, scale):
+    """Returns dict with o_pre, out (float64), out_bf16, lse, psum for the listed rows."""
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(q_rows, np.uint16)
+    kvc, pkv = _c(kv, np.uint16)
+    ix, pi = _c(idx, np.int32)
+    W, pw = _c(W_UV, np.uint16)
+    g, pg = _c(gate_rows, np.uint16)
+    n, H = q.shape[0], q.shape[1]
+    k = ix.shape[1]
+    res = {
+        "o_pre": np.empty((n, H, 128)), "out": np.empty((n, H, 128)),
+        "out_bf16": np.empty((n, H, 128), dtype=np.uint16), "lse": np.empty((n, H)), "psum": np.empty((n, H)),
+    }
+    lib().oracle_sparse_mla(n, pr, pq, pkv, kvc.shape[0], pi, k, pw, pg, H, scale,
+                            res["o_pre"].ctypes.data, res["out"].ctypes.data, res["out_bf16"].ctypes.data,
+                            res["lse"].ctypes.data, res["psum"].ctypes.data)
+    return res
+
+
+def dense_causal(rows, q_rows, kv, cu_seqlens, W_UV, gate_rows, scale):
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(q_rows, np.uint16)
+    kvc, pkv = _c(kv, np.uint16)
+    cu, pc = _c(cu_seqlens, np.int32)
+    W, pw = _c(W_UV, np.uint16)
+    g, pg = _c(gate_rows, np.uint16)
+    n, H = q.shape[0], q.shape[1]
+    out = np.empty((n, H, 128))
+    lib().oracle_dense_causal(n, pr, pq, pkv, kvc.shape[0], pc, len(cu) - 1, pw, pg, H, scale, out.ctypes.data)
+    return out
+
+
+def forward(cfg, inputs, rows):
+    """Whole path for the listed rows of a testgen workload: (idx, theta, keff, mla-dict)."""
+    LNk = key_layernorm(inputs["k_I"], cfg.ln_eps)
+    rows = np.asarray(rows, dtype=np.int64)
+    idx, theta, keff = topk(rows, inputs["q_I"][rows], inputs["w"][rows], LNk, inputs["cu_seqlens"], cfg.topk)
+    mla = sparse_mla(rows, inputs["q"][rows], inputs["kv"], idx, inputs["W_UV"], inputs["gate"][rows],
+                     cfg.softmax_scale)
+    return idx, theta, keff, mla

@@ -1,0 +1,304 @@
+// CPU oracle for the gated DSA forward: learned indexer, hard top-k, sparse latent attention,
+// per-head V up-projection and sigmoid output gate.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load this file; only
+// the tests, the package smoke check and the benchmark's CPU-baseline leg use it. It shares no
+// code, header, table or constant with the GPU library: even the bf16 helpers are written here
+// again.
+//
+// Sources (the pages are cited by title and section):
+//  [KC] NeMo AutoModel, "Kimi-K3.1-Pro" model-coverage page.
+//       - summary paragraph: every one of the 24 gated MLA layers has a learned indexer that keeps
+//         at most 2,048 causal keys for each query.
+//       - Implementation Limits, 1st bullet: the indexer produces top-k coordinates and the sparse
+//         kernels attend directly to the selected latent KV; eager/sdpa are dense-mask references.
+//       - Implementation Limits, 2nd bullet: indexer projections are BF16 with FP32 score
+//         accumulation; the indexer scans every causal key; sparse MLA never expands per-head K/V.
+//       - Implementation Limits, 3rd bullet: selection is hard top-k.
+//       - Implementation Limits, 4th bullet: a sequence of at most 2,048 valid tokens keeps every
+//         causal key.
+//       - paragraph after the bullets on the output gate and kv_b_proj: the gate is kept; the V
+//         projection is taken through its effective weight; packed documents are contiguous.
+//  [AD] archdiff.com "Kimi K3.1 Pro" blueprint: LayerNorm on the indexer key; output gate
+//       sigma(x W_g) * o; no positional encoding (tagline).
+//  [API] NeMo AutoModel kimi_k3 API index, KimiK3TextConfig: 96 heads, kv_lora_rank 512,
+//       qk_rope_head_dim 64 (left unrotated: mla_use_nope), v_head_dim 128.
+//  The scoring form  S(t,s) = sum_h w[t,h] * ReLU(q_I[t,h] . LN(k_I[s]))  and the tie rule (equal
+//  scores go to the lower key index) are not on the pages; they are the problem statement's
+//  reading and are used here verbatim.
+//
+// Readings where the pages are silent (each is listed in the design notes):
+//  - LayerNorm: biased variance, eps given by the caller (1e-5), optional affine; computed in
+//    double and rounded once to bf16 (round-to-nearest-even) because the indexer contraction
+//    consumes bf16 operands.
+//  - Causal keys of token t are the tokens of its own document up to and including t.
+//  - Scores: FP32 products and FP32 sequential accumulation, first over the d_I dims of each
+//    indexer head, then over heads in head order. ReLU returns +0 for non-positive dots.
+//  - Attention: softmax scale given by the caller (1/sqrt(192)); no sink; the first 512 latent
+//    dims are V, all 576 are K; no rotation of the last 64 dims.
+//  - Gate: one logit per (token, head), applied after the up-projection.
+//  - Attention arithmetic is in double; the gated output is rounded once to bf16 (RNE).
+//
+// Build: g++ -O2 -std=c++17 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math, so every
+// FP32 sum below is evaluated in the order written).
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <vector>
+
+namespace {
+
+constexpr int kDL = 576;  // latent row: kv_lora_rank 512 + 64 unrotated dims  [API]
+constexpr int kDV = 512;  // V part of a latent row                            [API]
+constexpr int kDO = 128;  // v_head_dim                                        [API]
+
+float bf16_bits_to_float(uint16_t h) {
+  uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// Round a finite double to the nearest bf16 (ties to even), in one step.
+uint16_t double_to_bf16_rne(double x) {
+  if (x == 0.0) return std::signbit(x) ? 0x8000 : 0x0000;
+  int e = 0;
+  double m = std::frexp(x, &e);            // |m| in [0.5, 1)
+  double r = std::nearbyint(std::ldexp(m, 8));  // 8 significant bits, ties to even
+  float f = static_cast<float>(std::ldexp(r, e - 8));  // exact: at most 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// First token of the document holding token t. cu has n_docs+1 entries, strictly increasing,
+// cu[0] = 0, cu[n_docs] = T. NULL cu means one document [0, T).
+int64_t doc_begin(const int32_t* cu, int32_t n_docs, int64_t t) {
+  if (cu == nullptr) return 0;
+  for (int32_t d = 0; d < n_docs; ++d)
+    if (t < cu[d + 1]) return cu[d];
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_abi_version() { return 1; }
+
+int64_t oracle_doc_begin(const int32_t* cu, int32_t n_docs, int64_t t) { return doc_begin(cu, n_docs, t); }
+
+// Step: LayerNorm on the indexer key ([AD] "LayerNorm on the indexer key").
+// LNk[s,i] = bf16( (x_i - mean) / sqrt(var + eps) * gamma_i + beta_i ), var biased, in double.
+// pre (optional, [T,d_I]) receives the double value before rounding.
+void oracle_key_layernorm(const uint16_t* k_I, int64_t T, int32_t d_I, const float* gamma, const float* beta,
+                          double eps, uint16_t* LNk, double* pre) {
+#pragma omp parallel for schedule(static)
+  for (int64_t s = 0; s < T; ++s) {
+    const uint16_t* x = k_I + s * d_I;
+    double mean = 0.0;
+    for (int32_t i = 0; i < d_I; ++i) mean += bf16_bits_to_float(x[i]);
+    mean /= d_I;
+    double var = 0.0;
+    for (int32_t i = 0; i < d_I; ++i) {
+      double c = bf16_bits_to_float(x[i]) - mean;
+      var += c * c;
+    }
+    var /= d_I;
+    double inv = 1.0 / std::sqrt(var + eps);
+    for (int32_t i = 0; i < d_I; ++i) {
+      double y = (bf16_bits_to_float(x[i]) - mean) * inv;
+      if (gamma) y *= gamma[i];
+      if (beta) y += beta[i];
+      if (pre) pre[s * d_I + i] = y;
+      LNk[s * d_I + i] = double_to_bf16_rne(y);
+    }
+  }
+}
+
+// Step: indexer scores of one query over keys s0..s1 inclusive ([KC] Implementation Limits,
+// 2nd bullet: BF16 operands, FP32 accumulation).
+// S[s-s0] = sum_h w[h] * ReLU( sum_i qI[h,i] * LNk[s,i] ), all in FP32, in the order written.
+void oracle_index_scores(const uint16_t* qI_row, const uint16_t* w_row, int32_t H_I, int32_t d_I,
+                         const uint16_t* LNk, int64_t s0, int64_t s1, float* S) {
+  for (int64_t s = s0; s <= s1; ++s) {
+    const uint16_t* k = LNk + s * d_I;
+    float score = 0.0f;
+    for (int32_t h = 0; h < H_I; ++h) {
+      const uint16_t* q = qI_row + static_cast<int64_t>(h) * d_I;
+      float dot = 0.0f;
+      for (int32_t i = 0; i < d_I; ++i) dot += bf16_bits_to_float(q[i]) * bf16_bits_to_float(k[i]);
+      float r = dot > 0.0f ? dot : 0.0f;  // +0 for every non-positive dot
+      score += bf16_bits_to_float(w_row[h]) * r;
+    }
+    S[s - s0] = score;
+  }
+}
+
+// Error scale of one score: sum_h |w[h]| * sum_i |qI[h,i] * LNk[s,i]| in double. Any FP32
+// evaluation of a score (any summation order) lies within (d_I + H_I) * 2^-24 / (1 - ...) times
+// this value of the exact score.
+void oracle_index_score_scale(const uint16_t* qI_row, const uint16_t* w_row, int32_t H_I, int32_t d_I,
+                              const uint16_t* LNk, int64_t s0, int64_t s1, double* out) {
+  for (int64_t s = s0; s <= s1; ++s) {
+    const uint16_t* k = LNk + s * d_I;
+    double acc = 0.0;
+    for (int32_t h = 0; h < H_I; ++h) {
+      const uint16_t* q = qI_row + static_cast<int64_t>(h) * d_I;
+      double dot = 0.0;
+      for (int32_t i = 0; i < d_I; ++i)
+        dot += std::fabs(static_cast<double>(bf16_bits_to_float(q[i])) * bf16_bits_to_float(k[i]));
+      acc += std::fabs(static_cast<double>(bf16_bits_to_float(w_row[h]))) * dot;
+    }
+    out[s - s0] = acc;
+  }
+}
+
+// Step: hard top-k ([KC] summary; Implementation Limits 3rd and 4th bullets).
+// For each listed query row t (global index rows[r]) with causal keys b(t)..t (n_t of them):
+//  - n_t <= k: every causal key is kept (the short-sequence rule);
+//  - otherwise the k keys that come first when the causal keys, listed in ascending index order,
+//    are stably sorted by score, highest first (so equal scores keep the lower index).
+// idx_out[r, :] holds the kept global indices in ascending order, then -1 up to k.
+// theta_out[r] = score of the k-th kept key (NaN when n_t <= k); keff_out[r] = min(k, n_t).
+void oracle_topk(int64_t n_rows, const int64_t* rows, const uint16_t* qI_rows, const uint16_t* w_rows,
+                 int32_t H_I, int32_t d_I, const uint16_t* LNk, const int32_t* cu, int32_t n_docs, int32_t k,
+                 int32_t* idx_out, float* theta_out, int32_t* keff_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t t = rows[r];
+    const int64_t b = doc_begin(cu, n_docs, t);
+    const int64_t n_t = t - b + 1;
+    int32_t* out = idx_out + r * k;
+    std::vector<int64_t> kept;
+    float theta = std::numeric_limits<float>::quiet_NaN();
+    if (n_t <= k) {
+      for (int64_t s = b; s <= t; ++s) kept.push_back(s);
+    } else {
+      std::vector<float> S(static_cast<size_t>(n_t));
+      oracle_index_scores(qI_rows + r * static_cast<int64_t>(H_I) * d_I, w_rows + r * H_I, H_I, d_I, LNk, b, t,
+                          S.data());
+      std::vector<int64_t> order(static_cast<size_t>(n_t));
+      std::iota(order.begin(), order.end(), b);  // ascending key index
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int64_t x, int64_t y) { return S[x - b] > S[y - b]; });
+      kept.assign(order.begin(), order.begin() + k);
+      theta = S[kept.back() - b];
+      std::sort(kept.begin(), kept.end());
+    }
+    for (int32_t j = 0; j < k; ++j) out[j] = j < static_cast<int32_t>(kept.size()) ? static_cast<int32_t>(kept[j]) : -1;
+    theta_out[r] = theta;
+    keff_out[r] = static_cast<int32_t>(kept.size());
+  }
+}
+
+// Step: sparse latent attention over the given key indices, then the per-head V up-projection
+// and the sigmoid output gate ([KC] Implementation Limits 1st/2nd bullets and the paragraph on
+// the output gate and kv_b_proj; [AD] output gate; [API] shapes).
+// For row r (global token rows[r]) and head h, over the valid entries s_j of idx[r, :] (entries
+// outside [0, T) are skipped):
+//   l_j  = scale * sum_{i<576} q[r,h,i] * kv[s_j,i]
+//   p_j  = exp(l_j - max l) / sum_j exp(l_j - max l)
+//   ol_c = sum_j p_j * kv[s_j, c]                    (c < 512)
+//   o_d  = sum_c ol_c * W_UV[h, c, d]                 (d < 128)
+//   out  = o_d * 1 / (1 + exp(-gate[r, h]))
+// All in double. Outputs (each optional): o_pre [n,H,128] before the gate, out_f64 [n,H,128],
+// out_bf16 (RNE of out_f64), lse [n,H] = max l + log sum exp(l - max l), psum [n,H] = sum_j p_j.
+void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T,
+                       const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
+                       double scale, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
+  (void)rows;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::vector<int64_t> sel;
+    for (int32_t j = 0; j < k; ++j) {
+      int64_t s = idx[r * k + j];
+      if (s >= 0 && s < T) sel.push_back(s);
+    }
+    const size_t n = sel.size();
+    std::vector<double> l(n), ol(kDV);
+    for (int32_t h = 0; h < H; ++h) {
+      const uint16_t* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
+      for (size_t j = 0; j < n; ++j) {
+        const uint16_t* kr = kv + sel[j] * kDL;
+        double dot = 0.0;
+        for (int i = 0; i < kDL; ++i)
+          dot += static_cast<double>(bf16_bits_to_float(qh[i])) * bf16_bits_to_float(kr[i]);
+        l[j] = scale * dot;
+      }
+      double m = -std::numeric_limits<double>::infinity();
+      for (size_t j = 0; j < n; ++j) m = std::max(m, l[j]);
+      double z = 0.0;
+      for (size_t j = 0; j < n; ++j) z += std::exp(l[j] - m);
+      std::fill(ol.begin(), ol.end(), 0.0);
+      double ps = 0.0;
+      for (size_t j = 0; j < n; ++j) {
+        double p = std::exp(l[j] - m) / z;
+        ps += p;
+        const uint16_t* vr = kv + sel[j] * kDL;
+        for (int c = 0; c < kDV; ++c) ol[c] += p * bf16_bits_to_float(vr[c]);
+      }
+      const double g = bf16_bits_to_float(gate_rows[r * H + h]);
+      const double sig = 1.0 / (1.0 + std::exp(-g));
+      const uint16_t* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
+      for (int d = 0; d < kDO; ++d) {
+        double o = 0.0;
+        for (int c = 0; c < kDV; ++c) o += ol[c] * bf16_bits_to_float(Wh[c * kDO + d]);
+        const int64_t at = (r * H + h) * static_cast<int64_t>(kDO) + d;
+        if (o_pre) o_pre[at] = o;
+        const double y = o * sig;
+        if (out_f64) out_f64[at] = y;
+        if (out_bf16) out_bf16[at] = double_to_bf16_rne(y);
+      }
+      if (lse) lse[r * H + h] = m + std::log(z);
+      if (psum) psum[r * H + h] = ps;
+    }
+  }
+}
+
+// Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are
+// dense-mask references). Written independently of oracle_sparse_mla: for each listed row the
+// logits of all T keys are formed and keys outside the causal window of the row's own document
+// are masked to -inf before a full-length softmax. Same gate and up-projection definition.
+void oracle_dense_causal(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T,
+                         const int32_t* cu, int32_t n_docs, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
+                         double scale, double* out_f64) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t t = rows[r];
+    const int64_t b = doc_begin(cu, n_docs, t);
+    std::vector<double> logits(static_cast<size_t>(T)), attn(kDV);
+    for (int32_t h = 0; h < H; ++h) {
+      const uint16_t* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
+      for (int64_t s = 0; s < T; ++s) {
+        if (s < b || s > t) {
+          logits[s] = -std::numeric_limits<double>::infinity();
+          continue;
+        }
+        double dot = 0.0;
+        for (int i = 0; i < kDL; ++i) dot += static_cast<double>(bf16_bits_to_float(qh[i])) * bf16_bits_to_float(kv[s * kDL + i]);
+        logits[s] = dot * scale;
+      }
+      const double mx = *std::max_element(logits.begin(), logits.end());
+      double den = 0.0;
+      for (int64_t s = 0; s < T; ++s) den += std::exp(logits[s] - mx);
+      for (int c = 0; c < kDV; ++c) {
+        double acc = 0.0;
+        for (int64_t s = b; s <= t; ++s) acc += std::exp(logits[s] - mx) / den * bf16_bits_to_float(kv[s * kDL + c]);
+        attn[c] = acc;
+      }
+      const double gl = bf16_bits_to_float(gate_rows[r * H + h]);
+      for (int d = 0; d < kDO; ++d) {
+        double o = 0.0;
+        for (int c = 0; c < kDV; ++c) o += attn[c] * bf16_bits_to_float(W_UV[(static_cast<int64_t>(h) * kDV + c) * kDO + d]);
+        out_f64[(r * H + h) * static_cast<int64_t>(kDO) + d] = o / (1.0 + std::exp(-gl));
+      }
+    }
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,425 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+Pages cited: the Kimi-K3.1-Pro model-coverage page ("KC"), the archdiff "Kimi K3.1 Pro" blueprint
+("AD"), and the kimi_k3 API index ("API").
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import testgen as tg
+from tests.parity import check_index_row, gamma
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+bf = tg.f32_to_bf16
+f32 = tg.bf16_to_f32
+
+
+def _bf(a):
+    return bf(np.asarray(a, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- generator (not the method)
+
+def test_generator_rows_are_counter_based():
+    cfg = tg.get_config("tiny")
+    full = tg.make_inputs(cfg)
+    rows = [0, 1, 2, 511, 1023]
+    part = tg.query_rows(cfg, rows)
+    for name in ["q_I", "w", "q", "gate"]:
+        assert np.array_equal(part[name].reshape(len(rows), -1), full[name][rows].reshape(len(rows), -1))
+
+
+def test_generator_distributions():
+    x = f32(tg.normal_bf16(9, 1, 0, 200000, 1.0))
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+    u = f32(tg.uniform_bf16(9, 3, 0, 200000, 0.125))
+    assert u.min() >= 0 and u.max() <= 0.125 and abs(u.mean() - 0.0625) < 0.001
+    kv = f32(tg.key_side(tg.get_config("tiny"))["kv"])
+    rms = np.sqrt((kv.astype(np.float64) ** 2).mean(1))
+    assert np.all(np.abs(rms - 1) < 0.01)
+
+
+def test_packed_lengths_in_range():
+    c = tg.get_config("packed")
+    assert len(c.doc_lens) == 8 and all(1024 <= n <= 8192 for n in c.doc_lens)
+    assert c.T == sum(c.doc_lens) and max(c.doc_lens) > 2048
+
+
+# ---------------------------------------------------------------- LayerNorm on the indexer key (AD)
+
+def test_layernorm_matches_torch_float64():
+    """P9: before rounding, the oracle's LN equals torch's layer_norm in float64."""
+    k_I = tg.normal_bf16(3, 2, 0, 300 * 128, 1.0).reshape(300, 128)
+    LNk, pre = oracle.key_layernorm(k_I, 1e-5, want_pre=True)
+    x = torch.from_numpy(f32(k_I).astype(np.float64))
+    ref = torch.nn.functional.layer_norm(x, (128,), eps=1e-5).numpy()
+    assert np.abs(pre - ref).max() < 1e-12
+    # Rounding: LNk is a bf16 value within half a bf16 ulp of the double value (round to nearest).
+    y = f32(LNk).astype(np.float64)
+    ulp = np.ldexp(1.0, (np.frexp(np.abs(pre))[1] - 8))
+    assert np.all(np.abs(y - pre) <= ulp / 2 + 1e-300)
+
+
+def test_layernorm_affine_and_closed_forms():
+    d = 64
+    rows = np.zeros((3, d), dtype=np.float32)
+    rows[0] = 1.5                                   # constant row -> all zeros
+    rows[1] = np.where(np.arange(d) % 2 == 0, 2.0, -2.0)  # mean 0, var 4 -> +-2/sqrt(4+eps)
+    rows[2] = np.arange(d) - 31.5                   # symmetric ramp
+    k_I = _bf(rows)
+    gamma_ = np.full(d, 2.0, np.float32)
+    beta_ = np.full(d, -0.5, np.float32)
+    LNk, pre = oracle.key_layernorm(k_I, 1e-5, gamma_, beta_, want_pre=True)
+    assert np.all(pre[0] == -0.5)
+    expect = 2.0 * np.where(np.arange(d) % 2 == 0, 1, -1) * 2 / math.sqrt(4 + 1e-5) - 0.5
+    assert np.abs(pre[1] - expect).max() < 1e-12
+    var = ((np.arange(d) - 31.5) ** 2).mean()
+    assert np.abs(pre[2] - (2 * (np.arange(d) - 31.5) / math.sqrt(var + 1e-5) - 0.5)).max() < 1e-12
+
+
+# ---------------------------------------------------------------- indexer scores (KC bullet 2)
+
+def test_hand_worked_indexer_example():
+    g = json.load(open(os.path.join(GOLDEN, "indexer_hand.json")))
+    k_I = _bf(g["k_I"])
+    LNk = oracle.key_layernorm(k_I, 1e-5)
+    assert np.array_equal(f32(LNk), np.array(g["LNk_expected"], np.float32))
+    cu = np.array([0, 5], np.int32)
+    for case in g["cases"]:
+        q = _bf(case["q_I"])
+        w = _bf(case["w"])
+        t = case["t"]
+        S = oracle.index_scores(q, w, LNk, 0, t)
+        assert np.array_equal(S, np.array(case["scores_expected"], np.float32)), case["name"]
+        for k, exp_idx in case["topk"].items():
+            k = int(k)
+            idx, theta, keff = oracle.topk([t], q[None], w[None], LNk, cu, k)
+            want = exp_idx + [-1] * (k - len(exp_idx)) if len(exp_idx) < k else exp_idx
+            assert list(idx[0]) == want, (case["name"], k)
+            if str(k) in case["theta"]:
+                assert theta[0] == case["theta"][str(k)]
+
+
+def test_scores_one_hot_closed_form():
+    """q_I[h] = c_h e_{i_h} and one-hot w: S(s) = w * max(c * LNk[s, i], 0) exactly."""
+    H_I, d_I, T = 4, 64, 40
+    LNk = _bf(np.random.default_rng(0).standard_normal((T, d_I)))
+    for h_star, i_star, c, wv in [(0, 0, 1.0, 1.0), (3, 63, -2.0, 0.5), (2, 17, 4.0, -1.5)]:
+        q = np.zeros((H_I, d_I), np.float32)
+        for h in range(H_I):
+            q[h, (h * 7) % d_I] = 3.0          # other heads are live but carry zero weight
+        q[h_star] = 0
+        q[h_star, i_star] = c
+        w = np.zeros(H_I, np.float32)
+        w[h_star] = wv
+        S = oracle.index_scores(_bf(q), _bf(w), LNk, 0, T - 1)
+        want = np.float32(wv) * np.maximum(np.float32(c) * f32(LNk[:, i_star]), 0)
+        assert np.array_equal(S, want.astype(np.float32))
+
+
+def test_scores_exact_within_fp32_bound():
+    """Scores equal the exact value (rational arithmetic) within the FP32 accumulation bound."""
+    from fractions import Fraction
+    rng = np.random.default_rng(1)
+    H_I, d_I = 4, 64
+    LNk = _bf(rng.standard_normal((6, d_I)))
+    q = _bf(rng.standard_normal((H_I, d_I)))
+    w = _bf(rng.uniform(-1, 1, H_I))
+    S = oracle.index_scores(q, w, LNk, 0, 5)
+    sc = oracle.index_score_scale(q, w, LNk, 0, 5)
+    qf, wf, kf = f32(q), f32(w), f32(LNk)
+    for s in range(6):
+        exact = Fraction(0)
+        for h in range(H_I):
+            dot = sum(Fraction(float(qf[h, i])) * Fraction(float(kf[s, i])) for i in range(d_I))
+            exact += Fraction(float(wf[h])) * max(dot, Fraction(0))
+        assert abs(float(S[s]) - float(exact)) <= gamma(d_I + H_I) * sc[s] + 1e-30
+
+
+def test_scores_scaling_and_head_permutation():
+    """P8: scaling q_I or w by 2 doubles S exactly; permuting heads keeps S within the FP32 bound."""
+    rng = np.random.default_rng(2)
+    H_I, d_I, T = 4, 64, 50
+    LNk = oracle.key_layernorm(_bf(rng.standard_normal((T, d_I))))
+    q = _bf(rng.standard_normal((H_I, d_I)))
+    w = _bf(rng.uniform(0, 0.5, H_I))
+    S = oracle.index_scores(q, w, LNk, 0, T - 1)
+    assert np.array_equal(oracle.index_scores(_bf(2 * f32(q)), w, LNk, 0, T - 1), 2 * S)
+    assert np.array_equal(oracle.index_scores(q, _bf(2 * f32(w)), LNk, 0, T - 1), 2 * S)
+    perm = [2, 0, 3, 1]
+    Sp = oracle.index_scores(q[perm], w[perm], LNk, 0, T - 1)
+    sc = oracle.index_score_scale(q, w, LNk, 0, T - 1)
+    assert np.all(np.abs(Sp - S) <= 2 * gamma(d_I + H_I) * sc)
+
+
+# ---------------------------------------------------------------- hard top-k (KC summary, bullets 3-4)
+
+def _brute_topk_is_dominant(S, kept, b, t):
+    """The top-k set is the unique set whose members all beat all non-members in (score desc, idx asc)."""
+    kept = set(kept)
+    out = [s for s in range(b, t + 1) if s not in kept]
+    for u in kept:
+        for v in out:
+            su, sv = S[u - b], S[v - b]
+            if not (su > sv or (su == sv and u < v)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("k", [1, 3, 8, 40])
+def test_topk_brute_force_tiny(k):
+    """P1: brute force on tiny inputs, plus numpy lexsort and torch stable sort as library cross-checks."""
+    rng = np.random.default_rng(10 + k)
+    T, H_I, d_I = 40, 4, 64
+    LNk = oracle.key_layernorm(_bf(rng.standard_normal((T, d_I))))
+    rows = np.arange(T)
+    q = _bf(rng.standard_normal((T, H_I, d_I)))
+    w = _bf(rng.uniform(0, 0.5, (T, H_I)))
+    cu = np.array([0, T], np.int32)
+    idx, theta, keff = oracle.topk(rows, q, w, LNk, cu, k)
+    for t in range(T):
+        n = t + 1
+        assert keff[t] == min(k, n)
+        kept = [int(x) for x in idx[t] if x >= 0]
+        assert kept == sorted(kept) and len(kept) == keff[t]
+        S = oracle.index_scores(q[t], w[t], LNk, 0, t)
+        assert _brute_topk_is_dominant(S, kept, 0, t)
+        order = np.lexsort((np.arange(n), -S.astype(np.float64)))[: min(k, n)]
+        assert sorted(order.tolist()) == kept
+        tv, ti = torch.sort(torch.from_numpy(-S), stable=True)
+        assert sorted(ti[: min(k, n)].tolist()) == kept
+
+
+def test_topk_constructed_ties():
+    """P2: equal scores resolve to the lower index, exactly."""
+    T, H_I, d_I, k = 30, 4, 64, 5
+    rng = np.random.default_rng(3)
+    same = rng.standard_normal(d_I)
+    k_I = _bf(np.tile(same, (T, 1)))                 # duplicated rows: all scores equal
+    LNk = oracle.key_layernorm(k_I)
+    q = _bf(rng.standard_normal((T, H_I, d_I)))
+    w = _bf(rng.uniform(0, 1, (T, H_I)))
+    idx, _, _ = oracle.topk(np.arange(T), q, w, LNk, np.array([0, T], np.int32), k)
+    for t in range(k, T):
+        assert list(idx[t]) == list(range(k))
+    const = _bf(np.full((T, d_I), 0.75))              # LN of a constant row is 0, so S = +0
+    LNc = oracle.key_layernorm(const)
+    assert np.all(f32(LNc) == 0)
+    idx, theta, _ = oracle.topk(np.arange(T), q, w, LNc, np.array([0, 10, T], np.int32), k)
+    assert np.all(theta[np.arange(T) >= 10 + k] == 0)
+    for t in range(10 + k, T):
+        assert list(idx[t]) == list(range(10, 10 + k))
+
+
+def test_topk_short_rows_keep_all_and_respect_documents():
+    """P3: a row with at most k causal keys keeps them all (KC bullet 4); keys never cross documents."""
+    cfg = tg.Config("mini", 11, [50, 7, 300, 1], topk=64, H=16, H_I=4, d_I=64)
+    inp = tg.make_inputs(cfg)
+    LNk = oracle.key_layernorm(inp["k_I"])
+    cu = cfg.cu_seqlens
+    rows = np.arange(cfg.T)
+    idx, theta, keff = oracle.topk(rows, inp["q_I"], inp["w"], LNk, cu, cfg.topk)
+    for t in rows:
+        b = oracle.doc_begin(cu, t)
+        n = t - b + 1
+        kept = idx[t][: keff[t]]
+        assert keff[t] == min(n, cfg.topk)
+        assert kept.min() >= b and kept.max() <= t
+        if n <= cfg.topk:
+            assert list(kept) == list(range(b, t + 1)) and np.isnan(theta[t])
+
+
+def test_topk_scale_invariance():
+    """P8: doubling q_I or w leaves the index sets unchanged."""
+    cfg = tg.get_config("tiny")
+    inp = tg.make_inputs(cfg)
+    LNk = oracle.key_layernorm(inp["k_I"])
+    rows = np.arange(600, 1024, 7)
+    a, _, _ = oracle.topk(rows, inp["q_I"][rows], inp["w"][rows], LNk, inp["cu_seqlens"], cfg.topk)
+    b, _, _ = oracle.topk(rows, _bf(2 * f32(inp["q_I"][rows])), inp["w"][rows], LNk, inp["cu_seqlens"], cfg.topk)
+    c, _, _ = oracle.topk(rows, inp["q_I"][rows], _bf(2 * f32(inp["w"][rows])), LNk, inp["cu_seqlens"], cfg.topk)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_near_tie_checker_flags_planted_mistake():
+    """The index rule accepts the oracle's own rows and rejects a planted non-tie swap."""
+    cfg = tg.get_config("tiny")
+    inp = tg.make_inputs(cfg)
+    LNk = oracle.key_layernorm(inp["k_I"])
+    t = 900
+    idx, theta, keff = oracle.topk([t], inp["q_I"][[t]], inp["w"][[t]], LNk, inp["cu_seqlens"], cfg.topk)
+    row = idx[0].copy()
+    assert check_index_row(row, idx[0], keff[0], 0, t, cfg.topk, inp["q_I"][t], inp["w"][t], LNk, theta[0]) is None
+    S = oracle.index_scores(inp["q_I"][t], inp["w"][t], LNk, 0, t)
+    kept = set(row.tolist())
+    worst_out = min((s for s in range(t + 1) if s not in kept), key=lambda s: S[s])
+    best_in = max(kept, key=lambda s: S[s])
+    bad = np.array(sorted((kept - {best_in}) | {worst_out}), np.int32)
+    assert check_index_row(bad, idx[0], keff[0], 0, t, cfg.topk, inp["q_I"][t], inp["w"][t], LNk, theta[0]) is not None
+
+
+# ---------------------------------------------------------------- sparse MLA, V up-projection, gate
+
+def _hand_case(case):
+    H, T = 1, len(case["kv_rows"])
+    kv = np.zeros((T, 576), np.float32)
+    for r, entries in enumerate(case["kv_rows"]):
+        for c, v in entries:
+            kv[r, c] = v
+    q = np.zeros((1, H, 576), np.float32)
+    for c, v in case["q"]:
+        q[0, 0, c] = v
+    W = np.zeros((H, 512, 128), np.float32)
+    for c, d, v in case["W"]:
+        W[0, c, d] = v
+    gate = np.array([[case["gate"]]], np.float32)
+    idx = np.array([case["idx"]], np.int32)
+    return _bf(kv), _bf(q), _bf(W), _bf(gate), idx
+
+
+def test_hand_worked_mla_example():
+    g = json.load(open(os.path.join(GOLDEN, "mla_hand.json")))
+    for case in g["cases"]:
+        kv, q, W, gate, idx = _hand_case(case)
+        r = oracle.sparse_mla([len(case["idx"]) - 1], q, kv, idx, W, gate, case["scale"])
+        assert np.allclose(r["o_pre"][0, 0, :2], case["o_expected"], atol=1e-11), case["name"]
+        assert np.allclose(r["out"][0, 0, :2], case["out_expected"], atol=1e-11), case["name"]
+        assert np.all(r["o_pre"][0, 0, 2:] == 0)
+        assert abs(r["lse"][0, 0] - case["lse"]) < 1e-11
+
+
+def test_softmax_rows_sum_to_one():
+    """P5 on the tiny workload."""
+    cfg = tg.get_config("tiny")
+    inp = tg.make_inputs(cfg)
+    rows = np.arange(0, 1024, 13)
+    idx, theta, keff, mla = oracle.forward(cfg, inp, rows)
+    assert np.abs(mla["psum"] - 1).max() <= 1e-12
+
+
+def test_mla_closed_forms():
+    """P6: one key -> its V row; zero query -> mean of the rows; zero gate -> half; block-identity W_UV -> slice."""
+    cfg = tg.get_config("tiny")
+    inp = tg.make_inputs(cfg)
+    kv, W = inp["kv"], inp["W_UV"]
+    H = cfg.H
+    rows = np.array([0, 300, 1023])
+    q = inp["q"][rows]
+    gate = inp["gate"][rows]
+    kvf, Wf = f32(kv).astype(np.float64), f32(W).astype(np.float64)
+    # one key: first token of the document
+    idx1 = np.full((3, 8), -1, np.int32)
+    idx1[:, 0] = [0, 17, 1023]
+    r = oracle.sparse_mla(rows, q, kv, idx1, W, gate, cfg.softmax_scale)
+    for j, s in enumerate([0, 17, 1023]):
+        want = np.einsum("c,hcd->hd", kvf[s, :512], Wf)
+        assert np.abs(r["o_pre"][j] - want).max() < 1e-9 * np.abs(want).max()
+    # zero query: uniform weights
+    idx = np.stack([np.arange(0, 40), np.arange(100, 140), np.arange(900, 940)]).astype(np.int32)
+    r0 = oracle.sparse_mla(rows, np.zeros_like(q), kv, idx, W, gate, cfg.softmax_scale)
+    for j in range(3):
+        want = np.einsum("c,hcd->hd", kvf[idx[j], :512].mean(0), Wf)
+        assert np.abs(r0["o_pre"][j] - want).max() < 1e-9 * np.abs(want).max()
+    # zero gate halves the output exactly
+    rz = oracle.sparse_mla(rows, q, kv, idx, W, np.zeros_like(gate), cfg.softmax_scale)
+    assert np.array_equal(rz["out"], rz["o_pre"] / 2)
+    # block identity: W[h, c, d] = 1 when c == 128 * (h % 4) + d
+    Wi = np.zeros((H, 512, 128), np.float32)
+    for h in range(H):
+        Wi[h, 128 * (h % 4) + np.arange(128), np.arange(128)] = 1
+    ri = oracle.sparse_mla(rows, q, kv, idx, _bf(Wi), gate, cfg.softmax_scale)
+    rI = oracle.sparse_mla(rows, q, kv, idx, _bf(np.tile(np.eye(512, 128, dtype=np.float32), (H, 1, 1))), gate,
+                           cfg.softmax_scale)
+    # o_lat rebuilt directly from its closed form: the block-identity run must return its slice
+    qf = f32(q).astype(np.float64)
+    for j in range(3):
+        sel = idx[j]
+        for h in range(H):
+            l = cfg.softmax_scale * (kvf[sel] @ qf[j, h])
+            p = np.exp(l - l.max()); p /= p.sum()
+            o_lat = p @ kvf[sel, :512]
+            b0 = 128 * (h % 4)
+            assert np.abs(ri["o_pre"][j, h] - o_lat[b0:b0 + 128]).max() < 1e-12
+            assert np.abs(rI["o_pre"][j, h] - o_lat[:128]).max() < 1e-12
+
+
+def _torch_dense_reference(cfg, inp, rows):
+    """Library cross-check: torch SDPA (float64, causal within the document) then W_UV and the gate."""
+    out = []
+    cu = inp["cu_seqlens"]
+    kv = torch.from_numpy(f32(inp["kv"]).astype(np.float64))
+    W = torch.from_numpy(f32(inp["W_UV"]).astype(np.float64))
+    for t in rows:
+        b = oracle.doc_begin(cu, t)
+        q = torch.from_numpy(f32(inp["q"][t]).astype(np.float64))[:, None, :]   # [H,1,576]
+        K = kv[b:t + 1][None].expand(cfg.H, -1, -1)
+        V = kv[b:t + 1, :512][None].expand(cfg.H, -1, -1)
+        o = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=cfg.softmax_scale)[:, 0]  # [H,512]
+        o = torch.bmm(o[:, None, :], W)[:, 0]
+        g = torch.from_numpy(f32(inp["gate"][t]).astype(np.float64))
+        out.append((o * torch.sigmoid(g)[:, None]).numpy())
+    return np.stack(out)
+
+
+def test_dense_equivalence_tiny_shape():
+    """P4 (KC bullet 4 with bullet 1): for T <= k the sparse path equals dense causal attention."""
+    cfg = tg.Config("dense-tiny", 21, [256], topk=256, H=16, H_I=4, d_I=64, w_scale=0.5)
+    inp = tg.make_inputs(cfg)
+    rows = np.arange(cfg.T)
+    idx, theta, keff, mla = oracle.forward(cfg, inp, rows)
+    dense = oracle.dense_causal(rows, inp["q"], inp["kv"], inp["cu_seqlens"], inp["W_UV"], inp["gate"],
+                                cfg.softmax_scale)
+    assert np.abs(mla["out"] - dense).max() <= 1e-12 * np.abs(dense).max()
+    sub = rows[::17]
+    ref = _torch_dense_reference(cfg, inp, sub)
+    assert np.abs(mla["out"][sub] - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+def test_dense_equivalence_production_shape():
+    """P4 at T = k = 2048 with 96 heads, on sampled rows (the dense reference is slow)."""
+    cfg = tg.get_config("dense2048")
+    keys = tg.key_side(cfg)
+    rows = np.array([0, 1, 700, 2047])
+    inp = dict(keys, cu_seqlens=cfg.cu_seqlens)
+    qr = tg.query_rows(cfg, rows)
+    full_q = np.zeros((cfg.T, cfg.H, 576), np.uint16)
+    full_g = np.zeros((cfg.T, cfg.H), np.uint16)
+    full_q[rows] = qr["q"].reshape(len(rows), cfg.H, 576)
+    full_g[rows] = qr["gate"]
+    LNk = oracle.key_layernorm(keys["k_I"])
+    idx, theta, keff = oracle.topk(rows, qr["q_I"].reshape(len(rows), cfg.H_I, cfg.d_I), qr["w"], LNk,
+                                   cfg.cu_seqlens, cfg.topk)
+    assert list(keff) == [1, 2, 701, 2048]
+    mla = oracle.sparse_mla(rows, full_q[rows], keys["kv"], idx, keys["W_UV"], full_g[rows], cfg.softmax_scale)
+    dense = oracle.dense_causal(rows, full_q[rows], keys["kv"], cfg.cu_seqlens, keys["W_UV"], full_g[rows],
+                                cfg.softmax_scale)
+    assert np.abs(mla["out"] - dense).max() <= 1e-12 * np.abs(dense).max()
+    inp["q"], inp["gate"] = full_q, full_g
+    ref = _torch_dense_reference(cfg, inp, rows)
+    assert np.abs(mla["out"] - ref).max() <= 1e-10 * np.abs(ref).max()
+
+
+def test_packed_equals_per_document():
+    """P7: a packed run equals the per-document runs, indices offset by the document start (KC: packed
+    documents are contiguous)."""
+    lens = [300, 40, 420]
+    cfg = tg.Config("p7", 31, lens, topk=128, H=16, H_I=4, d_I=64, w_scale=0.5)
+    inp = tg.make_inputs(cfg)
+    rows = np.arange(cfg.T)
+    idx, theta, keff, mla = oracle.forward(cfg, inp, rows)
+    cu = cfg.cu_seqlens
+    for d in range(len(lens)):
+        b, e = int(cu[d]), int(cu[d + 1])
+        sub = {k: (v[b:e] if k != "W_UV" else v) for k, v in inp.items() if k != "cu_seqlens"}
+        sub["cu_seqlens"] = np.array([0, e - b], np.int32)
+        c1 = tg.Config("p7d", 31, [e - b], topk=128, H=16, H_I=4, d_I=64)
+        i1, th1, k1, m1 = oracle.forward(c1, sub, np.arange(e - b))
+        shifted = np.where(i1 >= 0, i1 + b, -1)
+        assert np.array_equal(idx[b:e], shifted)
+        assert np.array_equal(mla["out_bf16"][b:e], m1["out_bf16"])
