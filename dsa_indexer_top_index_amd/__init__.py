@@ -1,0 +1,180 @@
+"""Python binding of libdsa.so (include/dsa.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; PyTorch provides device memory and the
+current stream. There is no fallback: if the library is missing, importing the entry points
+raises.
+
+Entry points (same names as the C ABI):
+  dsa_workspace_size(shape) -> int
+  dsa_check_shape(shape) -> int status
+  dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
+  dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None)
+  dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace,
+                ln_gamma=None, ln_beta=None, lse=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH = range(5)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32),
+        ("n_docs", ctypes.c_int32),
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("cu_seqlens_dev", ctypes.c_void_p),
+        ("q_begin", ctypes.c_int32),
+        ("q_end", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("H_I", ctypes.c_int32),
+        ("d_I", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("ln_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Shape)
+        v = ctypes.c_void_p
+        L.dsa_status_string.argtypes = [ctypes.c_int]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_check_shape.argtypes = [P]
+        L.dsa_check_shape.restype = ctypes.c_int
+        L.dsa_workspace_size.argtypes = [P]
+        L.dsa_workspace_size.restype = ctypes.c_size_t
+        L.dsa_index_topk.argtypes = [P, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_index_topk.restype = ctypes.c_int
+        L.dsa_sparse_mla_fwd.argtypes = [P, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_sparse_mla_fwd.restype = ctypes.c_int
+        L.dsa_fused_fwd.argtypes = [P, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_fused_fwd.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().dsa_status_string(status).decode()
+
+
+def make_shape(T, topk, H_I, d_I, H, cu_seqlens=None, cu_seqlens_dev=None, q_begin=0, q_end=0,
+               ln_eps=1e-5, softmax_scale=1.0 / math.sqrt(192.0)) -> Shape:
+    """cu_seqlens: host sequence of n_docs+1 ints (None = one document);
+    cu_seqlens_dev: the same values as an int32 device tensor (required when n_docs > 1)."""
+    s = Shape()
+    s.T = int(T)
+    if cu_seqlens is None:
+        s.n_docs = 1
+        s.cu_seqlens_host = None
+        s._cu_keep = None
+    else:
+        arr = (ctypes.c_int32 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+        s._cu_keep = arr
+        s.n_docs = len(cu_seqlens) - 1
+        s.cu_seqlens_host = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    if cu_seqlens_dev is not None:
+        _check(cu_seqlens_dev, torch.int32, "cu_seqlens_dev")
+        s._cu_dev_keep = cu_seqlens_dev
+        s.cu_seqlens_dev = cu_seqlens_dev.data_ptr()
+    else:
+        s.cu_seqlens_dev = None
+    s.q_begin, s.q_end = int(q_begin), int(q_end)
+    s.topk, s.H_I, s.d_I, s.H = int(topk), int(H_I), int(d_I), int(H)
+    s.ln_eps, s.softmax_scale = float(ln_eps), float(softmax_scale)
+    return s
+
+
+def _check(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _p(t, dtype, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    _check(t, dtype, name)
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _raise(st, where):
+    if st != DSA_OK:
+        raise DsaError(st, where)
+
+
+def dsa_check_shape(shape: Shape) -> int:
+    return lib().dsa_check_shape(ctypes.byref(shape))
+
+
+def dsa_workspace_size(shape: Shape) -> int:
+    return int(lib().dsa_workspace_size(ctypes.byref(shape)))
+
+
+def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
+    n = dsa_workspace_size(shape)
+    if n == 0:
+        _raise(dsa_check_shape(shape), "dsa_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None):
+    bf = torch.bfloat16
+    st = lib().dsa_index_topk(
+        ctypes.byref(shape), _p(q_I, bf, "q_I"), _p(k_I, bf, "k_I"), _p(ln_gamma, torch.float32, "ln_gamma", True),
+        _p(ln_beta, torch.float32, "ln_beta", True), _p(w, bf, "w"), _p(topk_idx, torch.int32, "topk_idx"),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_index_topk")
+
+
+def dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None):
+    bf = torch.bfloat16
+    st = lib().dsa_sparse_mla_fwd(
+        ctypes.byref(shape), _p(q, bf, "q"), _p(kv, bf, "kv"), _p(topk_idx, torch.int32, "topk_idx"),
+        _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"), _p(out, bf, "out"), _p(lse, torch.float32, "lse", True),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_sparse_mla_fwd")
+
+
+def dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace, ln_gamma=None, ln_beta=None,
+                  lse=None):
+    bf = torch.bfloat16
+    st = lib().dsa_fused_fwd(
+        ctypes.byref(shape), _p(q_I, bf, "q_I"), _p(k_I, bf, "k_I"), _p(ln_gamma, torch.float32, "ln_gamma", True),
+        _p(ln_beta, torch.float32, "ln_beta", True), _p(w, bf, "w"), _p(q, bf, "q"), _p(kv, bf, "kv"),
+        _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"), _p(topk_idx, torch.int32, "topk_idx"), _p(out, bf, "out"),
+        _p(lse, torch.float32, "lse", True), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_fused_fwd")

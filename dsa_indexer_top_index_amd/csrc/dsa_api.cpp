@@ -1,0 +1,189 @@
+// Host side of the C ABI declared in include/dsa.h: argument checks (pure host code, no HIP
+// call), workspace layout and the launch sequence of each entry point.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "dsa_kernels.h"
+
+namespace {
+
+constexpr int kMaxTopk = 2048;         // summary of the model-coverage page: at most 2,048 keys
+constexpr int64_t kMlaChunkRows = 16384;  // rows per attention/up-projection pass (bounds o_lat)
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t rows_of(const dsa_shape* s) { return (s->q_end == 0 ? s->T : s->q_end) - s->q_begin; }
+
+struct Layout {
+  size_t lnk_off, lnk_bytes, olat_off, olat_bytes, total;
+  int64_t chunk_rows;
+};
+
+Layout layout_of(const dsa_shape* s) {
+  Layout L{};
+  L.lnk_off = 0;
+  L.lnk_bytes = align_up(static_cast<size_t>(s->T) * s->d_I * 2);
+  const int64_t rows = rows_of(s);
+  L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
+  L.olat_off = L.lnk_bytes;
+  L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * s->H * 512 * 2);
+  L.total = L.olat_off + L.olat_bytes;
+  return L;
+}
+
+dsa_status check_ws(const dsa_shape* s, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr || ws_bytes < layout_of(s).total) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status st) {
+  switch (st) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+dsa_status dsa_check_shape(const dsa_shape* s) {
+  if (s == nullptr) return DSA_ERR_INVALID_ARG;
+  if (s->T < 1 || s->n_docs < 1 || s->n_docs > s->T) return DSA_ERR_INVALID_ARG;
+  if (s->n_docs > 1 && (s->cu_seqlens_host == nullptr || s->cu_seqlens_dev == nullptr)) return DSA_ERR_INVALID_ARG;
+  if (s->cu_seqlens_host != nullptr) {
+    const int32_t* cu = s->cu_seqlens_host;
+    if (cu[0] != 0 || cu[s->n_docs] != s->T) return DSA_ERR_INVALID_ARG;
+    for (int32_t d = 0; d < s->n_docs; ++d)
+      if (cu[d + 1] <= cu[d]) return DSA_ERR_INVALID_ARG;
+  }
+  const int32_t q_end = s->q_end == 0 ? s->T : s->q_end;
+  if (s->q_begin < 0 || q_end > s->T || s->q_begin >= q_end) return DSA_ERR_INVALID_ARG;
+  if (s->topk < 1) return DSA_ERR_INVALID_ARG;
+  if (!(s->ln_eps > 0.0f) || !std::isfinite(s->ln_eps)) return DSA_ERR_INVALID_ARG;
+  if (!(s->softmax_scale > 0.0f) || !std::isfinite(s->softmax_scale)) return DSA_ERR_INVALID_ARG;
+  if (s->topk > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+  const bool idx_ok = (s->H_I == 64 && s->d_I == 128) || (s->H_I == 4 && s->d_I == 64);
+  if (!idx_ok) return DSA_ERR_UNSUPPORTED;
+  if (s->H != 96 && s->H != 16) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+size_t dsa_workspace_size(const dsa_shape* s) {
+  if (dsa_check_shape(s) != DSA_OK) return 0;
+  return layout_of(s).total;
+}
+
+static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* gamma,
+                            const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, hipStream_t st) {
+  const auto L = layout_of(s);
+  uint16_t* lnk = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.lnk_off);
+  if (dsa::launch_key_layernorm(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->T, s->d_I, lnk, st) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  dsa::IndexArgs a{};
+  a.q_I = q_I;
+  a.w = w;
+  a.LNk = lnk;
+  a.topk_idx = topk_idx;
+  a.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
+  a.n_docs = s->n_docs;
+  a.T = s->T;
+  a.row0 = s->q_begin;
+  a.nrows = rows_of(s);
+  a.k = s->topk;
+  if (dsa::launch_index_topk(a, s->H_I, s->d_I, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  return DSA_OK;
+}
+
+static dsa_status run_mla(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                          const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws, hipStream_t st) {
+  const auto L = layout_of(s);
+  uint16_t* olat = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.olat_off);
+  const int64_t rows = rows_of(s);
+  for (int64_t c0 = 0; c0 < rows; c0 += L.chunk_rows) {
+    const int64_t n = (rows - c0) < L.chunk_rows ? (rows - c0) : L.chunk_rows;
+    dsa::MlaArgs m{};
+    m.q = q;
+    m.kv = kv;
+    m.idx = idx;
+    m.o_lat = olat;
+    m.lse = lse;
+    m.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
+    m.n_docs = s->n_docs;
+    m.T = s->T;
+    m.row0 = s->q_begin;
+    m.chunk_r0 = static_cast<int>(c0);
+    m.chunk_rows = static_cast<int>(n);
+    m.k = s->topk;
+    m.H = s->H;
+    m.scale_log2 = s->softmax_scale * 1.4426950408889634f;
+    if (dsa::launch_sparse_mla(m, st) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::UpArgs u{};
+    u.o_lat = olat;
+    u.W_UV = W_UV;
+    u.gate = gate;
+    u.out = out;
+    u.chunk_r0 = static_cast<int>(c0);
+    u.chunk_rows = static_cast<int>(n);
+    u.H = s->H;
+    if (dsa::launch_up_gate(u, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  }
+  return DSA_OK;
+}
+
+dsa_status dsa_index_topk(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
+                          const float* ln_beta, const uint16_t* w, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                          void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q_I || !k_I || !w || !topk_idx) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(topk_idx, 4) || !aligned(ln_gamma, 4) ||
+      !aligned(ln_beta, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
+  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
+                              const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q || !kv || !topk_idx || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 4) || !aligned(gate, 2) ||
+      !aligned(out, 2) || !aligned(lse, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
+  return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
+                         const float* ln_beta, const uint16_t* w, const uint16_t* q, const uint16_t* kv,
+                         const uint16_t* W_UV, const uint16_t* gate, int32_t* topk_idx, uint16_t* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q_I || !k_I || !w || !q || !kv || !W_UV || !gate || !topk_idx || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(ln_gamma, 4) || !aligned(ln_beta, 4) ||
+      !aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 4) || !aligned(gate, 2) ||
+      !aligned(out, 2) || !aligned(lse, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, hs)) != DSA_OK) return st;
+  return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, hs);
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Launch wrappers of the gfx950 kernels (internal to libdsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexArgs {
+  const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
+  const uint16_t* w;     // [nrows, H_I]
+  const uint16_t* LNk;   // [T, d_I]
+  int32_t* topk_idx;     // [nrows, k]
+  const int32_t* cu;     // device cu_seqlens or nullptr
+  int n_docs;
+  int T;
+  int row0;              // global token of local row 0
+  int nrows;
+  int k;
+};
+
+struct MlaArgs {
+  const uint16_t* q;     // [nrows, H, 576] local rows
+  const uint16_t* kv;    // [T, 576]
+  const int32_t* idx;    // [nrows, k]
+  uint16_t* o_lat;       // [chunk_rows, H, 512] workspace, local to the chunk
+  float* lse;            // [nrows, H] or nullptr
+  const int32_t* cu;
+  int n_docs;
+  int T;
+  int row0;              // global token of local row 0
+  int chunk_r0;          // first local row of this chunk
+  int chunk_rows;
+  int k;
+  int H;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct UpArgs {
+  const uint16_t* o_lat;  // [chunk_rows, H, 512]
+  const uint16_t* W_UV;   // [H, 512, 128]
+  const uint16_t* gate;   // [nrows, H]
+  uint16_t* out;          // [nrows, H, 128]
+  int chunk_r0;
+  int chunk_rows;
+  int H;
+};
+
+hipError_t launch_key_layernorm(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int T, int d_I,
+                                uint16_t* LNk, hipStream_t st);
+hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
+hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,116 @@
+// Per-head V up-projection and sigmoid output gate (gfx950).
+//
+// Method (NeMo AutoModel "Kimi-K3.1-Pro" model-coverage page, paragraph on the output gate and
+// kv_b_proj: the gate is kept and the V projection is applied through its effective weight;
+// archdiff "Kimi K3.1 Pro" blueprint, output gate sigma(x W_g) * o; kimi_k3 API index,
+// v_head_dim 128):
+//   o[t,h,d]   = sum_c o_lat[t,h,c] * W_UV[h,c,d]      (c < 512, d < 128)
+//   out[t,h,d] = bf16( o[t,h,d] / (1 + exp(-gate[t,h])) )
+//
+// Kernel design: a workgroup owns one head and 128 query rows (four waves of 32 rows), so the
+// head's 128 KB weight is read once per 128 rows. The batched product runs on
+// v_mfma_f32_32x32x16_bf16 with rows as M, the 128 outputs as N (four tiles) and c as K.
+// W_UV[h] streams through LDS in 64-row chunks (asynchronous 16-byte copies, double buffered)
+// and is read transposed with ds_read_b64_tr_b16, so no transposed copy of the weight exists.
+// The gate is applied in FP32 in the epilogue.
+#include "dsa_device.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+constexpr int kUpRows = 128;   // rows per workgroup
+constexpr int kUpChunk = 64;   // c rows of W_UV per LDS chunk
+constexpr int kUpChunkBytes = kUpChunk * kODim * 2;  // 16 KB
+
+// Chunk layout: granule g (16 B, 8 outputs) of weight row c lives at slot 16*c + (g ^ 4*(c%4)).
+__device__ __forceinline__ int up_slot(int c, int g) { return 16 * c + (g ^ (4 * (c & 3))); }
+
+__global__ __launch_bounds__(256, 2) void k_up_gate(UpArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kUpChunkBytes];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int h = blockIdx.y;
+  const int row0 = blockIdx.x * kUpRows + 32 * wave;  // first chunk-local row of this wave
+  const int H = a.H;
+  const uint16_t* __restrict__ W = a.W_UV + static_cast<int64_t>(h) * kVDim * kODim;
+
+  auto issue_chunk = [&](int cc, int buf) {
+    DSA_LDS uint8_t* dst = (DSA_LDS uint8_t*)(&s_w[buf][0]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int P0 = 256 * wave + 64 * j;
+      const int P = P0 + lane;
+      const int c = P >> 4;
+      const int g = (P & 15) ^ (4 * (c & 3));
+      copy16_to_lds(W + static_cast<int64_t>(kUpChunk * cc + c) * kODim + 8 * g, dst + 16 * P0);
+    }
+  };
+
+  // A operand: row m = lane%32, c = 16*step + 8*(lane/32) .. +8
+  const int arow = min(row0 + (lane & 31), a.chunk_rows - 1);
+  const uint16_t* arow_p = a.o_lat + (static_cast<int64_t>(arow) * H + h) * kVDim + 8 * (lane >> 5);
+  // B operand (transposed reads): rows c0 + 8*hh + s4 (+4), outputs 32*nt + 16*chh + 4*q4
+  const int g16 = lane >> 4, i16 = lane & 15, hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
+
+  issue_chunk(0, 0);
+  bf16x8 af[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) af[s] = *reinterpret_cast<const bf16x8*>(arow_p + 16 * s);
+  wait_vmem();
+  __syncthreads();
+  constexpr int nchunks = kVDim / kUpChunk;
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int buf = cc & 1;
+    bf16x8 an[4];
+    if (cc + 1 < nchunks) {
+      issue_chunk(cc + 1, buf ^ 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) an[s] = *reinterpret_cast<const bf16x8*>(arow_p + kUpChunk * (cc + 1) + 16 * s);
+    }
+    const DSA_LDS uint8_t* wb = (const DSA_LDS uint8_t*)(&s_w[buf][0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c1 = 16 * s + 8 * hh + s4, c2 = c1 + 4;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int g = 4 * nt + 2 * chh + (q4 >> 1);
+        const u32x2 v1 = lds_read_tr16(wb + up_slot(c1, g) * 16 + 8 * (q4 & 1));
+        const u32x2 v2 = lds_read_tr16(wb + up_slot(c2, g) * 16 + 8 * (q4 & 1));
+        const u32x4 vb = {v1[0], v1[1], v2[0], v2[1]};
+        acc[nt] = mfma32(af[s], __builtin_bit_cast(bf16x8, vb), acc[nt]);
+      }
+    }
+    if (cc + 1 < nchunks) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) af[s] = an[s];
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // Epilogue: rows 8*i + 4*hh + j of the wave's 32, output column 32*nt + lane%32.
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = row0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+    if (row < a.chunk_rows) {
+      const int64_t lrow = a.chunk_r0 + row;  // local row of the call
+      const float g = bf16_to_f32(a.gate[lrow * H + h]);
+      const float sig = 1.0f / (1.0f + __expf(-g));
+      uint16_t* o = a.out + (lrow * H + h) * kODim + (lane & 31);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) o[32 * nt] = f32_to_bf16(acc[nt][e] * sig);
+    }
+  }
+}
+
+hipError_t launch_up_gate(const UpArgs& a, hipStream_t st) {
+  dim3 grid((a.chunk_rows + kUpRows - 1) / kUpRows, a.H), block(256);
+  hipLaunchKernelGGL(k_up_gate, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

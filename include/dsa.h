@@ -1,0 +1,116 @@
+/*
+ * dsa.h - C ABI of libdsa.so: forward hot path of a gated DSA layer on MI355X (gfx950).
+ *
+ * The path (NeMo AutoModel "Kimi-K3.1-Pro" model-coverage page, summary and Implementation
+ * Limits; archdiff.com "Kimi K3.1 Pro" blueprint; kimi_k3 API index, KimiK3TextConfig):
+ *   1. LayerNorm on the indexer key k_I (blueprint: "LayerNorm on the indexer key").
+ *   2. Indexer scores S(t,s) = sum_h w[t,h] * ReLU(q_I[t,h,:] . LN(k_I)[s,:]) over every causal
+ *      key s of token t, bf16 operands with FP32 accumulation (Implementation Limits, 2nd bullet).
+ *      The T x T score matrix is never stored. The scoring form and the tie rule below are the
+ *      problem statement's; the pages only name a fused indexer.
+ *   3. Hard top-k (k <= 2048) per query, ties to the lower key index; a token with at most k
+ *      causal keys keeps all of them (summary; Implementation Limits, 3rd and 4th bullets).
+ *   4. Sparse latent attention over the selected rows of the latent KV (kv_lora_rank 512 plus
+ *      64 unrotated dims, no positional encoding), softmax in FP32 (Implementation Limits, 1st
+ *      and 2nd bullets; blueprint tagline; API index mla_use_nope).
+ *   5. Per-head V up-projection 512 -> 128 (the effective kv_b_proj V weight) and the sigmoid
+ *      output gate out = sigma(g) * o (paragraph on the output gate and kv_b_proj; blueprint
+ *      "Output gate").
+ *
+ * Conventions for every entry point
+ *  - bf16 tensors are passed as bf16 bit patterns (uint16_t) in device memory, row-major,
+ *    contiguous, 16-byte aligned. Integer tensors are int32, device memory, 4-byte aligned.
+ *  - Token axis: keys and key-side tensors (k_I, kv) cover all T tokens. Query-side tensors
+ *    (q_I, w, q, gate) and outputs (topk_idx, out, lse) cover only the rows
+ *    [q_begin, q_end) of the shape, indexed from 0 (local row r is global token q_begin + r).
+ *  - Packed documents are contiguous (model-coverage page: interior holes are not supported);
+ *    cu_seqlens gives their boundaries. A token's causal keys are the tokens of its own
+ *    document up to and including itself.
+ *  - The caller owns every buffer. The library never allocates, frees or synchronises; work is
+ *    enqueued on the given HIP stream (a hipStream_t passed as void*, NULL = default stream).
+ *  - Argument checks run on the host before any HIP call and return a status; nothing is
+ *    enqueued when a check fails. A failed launch returns DSA_ERR_LAUNCH. Faults inside kernels
+ *    surface at the caller's next synchronisation. No C++ exception crosses this ABI.
+ *  - Calls that share a workspace must not overlap.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad cu_seqlens */
+  DSA_ERR_UNSUPPORTED = 2, /* shape outside the supported set */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_size() */
+  DSA_ERR_LAUNCH = 4       /* a kernel launch failed */
+} dsa_status;
+
+/* Shapes of one call. Supported: (H_I, d_I) in {(64,128), (4,64)}; H in {96, 16};
+ * 1 <= topk <= 2048. Latent rows are 576 wide (512 V dims + 64 key-only dims); the head output
+ * is 128 wide. */
+typedef struct dsa_shape {
+  int32_t T;                      /* tokens (keys) over all packed documents, >= 1 */
+  int32_t n_docs;                 /* >= 1 */
+  const int32_t* cu_seqlens_host; /* [n_docs+1] host memory: 0 = c0 < c1 < ... < c_n = T;
+                                     may be NULL only when n_docs == 1 */
+  const int32_t* cu_seqlens_dev;  /* the same values in device memory; NULL only when n_docs == 1 */
+  int32_t q_begin;                /* first query row processed, 0 <= q_begin < q_end */
+  int32_t q_end;                  /* one past the last query row; 0 means T */
+  int32_t topk;                   /* k */
+  int32_t H_I;                    /* indexer heads */
+  int32_t d_I;                    /* indexer head dim */
+  int32_t H;                      /* attention heads */
+  float ln_eps;                   /* LayerNorm eps on the indexer key (> 0), e.g. 1e-5 */
+  float softmax_scale;            /* logit scale (> 0), e.g. 1/sqrt(192) */
+} dsa_shape;
+
+/* Bytes of device workspace the entry points need for this shape (256-byte aligned start
+ * required). Returns 0 if the shape is invalid or unsupported. Pure host function. */
+size_t dsa_workspace_size(const dsa_shape* shape);
+
+/* Host-only argument check of a shape (no HIP call): DSA_OK, DSA_ERR_INVALID_ARG or
+ * DSA_ERR_UNSUPPORTED. Every entry point runs it first. */
+dsa_status dsa_check_shape(const dsa_shape* shape);
+
+/* Steps 1-3. Inputs: q_I [rows, H_I, d_I] bf16; k_I [T, d_I] bf16; ln_gamma, ln_beta [d_I]
+ * float32 device arrays or NULL (identity); w [rows, H_I] bf16 (any sign).
+ * Output: topk_idx [rows, topk] int32. Row r holds min(topk, n) distinct global token indices of
+ * its causal keys (n = number of causal keys), in ascending order, then -1 up to topk.
+ * Workspace: >= dsa_workspace_size(shape) bytes (holds LN(k_I)). */
+dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
+                          const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                          int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps 4-5 for caller-supplied indices. Inputs: q [rows, H, 576] bf16 (already absorbed into
+ * the latent space; dims 0..511 pair with the compressed KV, 512..575 with the key-only dims);
+ * kv [T, 576] bf16; topk_idx [rows, topk] int32 (entries outside [0, T) are ignored; a row with
+ * no usable entry yields zeros and lse = -inf); W_UV [H, 512, 128] bf16; gate [rows, H] bf16
+ * gate logits. Outputs: out [rows, H, 128] bf16 = bf16(sigmoid(gate) * o);
+ * lse [rows, H] float32 natural-log softmax normaliser, or NULL. Every usable index is
+ * attended; causality of the indices is the caller's contract. */
+dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
+                              const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
+                              uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Steps 1-5 in one call: the union of the two argument lists; topk_idx is written and then used. */
+dsa_status dsa_fused_fwd(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
+                         const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                         const uint16_t* q, const uint16_t* kv, const uint16_t* W_UV,
+                         const uint16_t* gate, int32_t* topk_idx, uint16_t* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English text of a status. Never NULL. */
+const char* dsa_status_string(dsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

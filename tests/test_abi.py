@@ -1,0 +1,101 @@
+"""C ABI checks that need no GPU: the library loads, exports every function include/dsa.h declares,
+and the host-side argument checks return the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_indexer_top_index_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_sparse_mla_fwd",
+                     "dsa_status_string", "dsa_workspace_size"]
+    L = dsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for st in range(5):
+        assert dsa.status_string(st)
+    assert dsa.status_string(99) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(T=4096, topk=2048, H_I=64, d_I=128, H=96)
+    base.update(kw)
+    return dsa.make_shape(**base)
+
+
+def test_supported_shapes_and_workspace():
+    assert dsa.dsa_check_shape(_shape()) == dsa.DSA_OK
+    assert dsa.dsa_check_shape(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)) == dsa.DSA_OK
+    ws = dsa.dsa_workspace_size(_shape())
+    # LN(k_I) (T x d_I bf16) plus the latent output of one row chunk (rows x H x 512 bf16)
+    assert ws == 4096 * 128 * 2 + 4096 * 96 * 512 * 2
+    big = dsa.dsa_workspace_size(_shape(T=131072))
+    assert big == 131072 * 128 * 2 + 16384 * 96 * 512 * 2
+    assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(topk=2049), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(H_I=32), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(d_I=96), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(H=128), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(T=0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_begin=5, q_end=5), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_begin=-1), dsa.DSA_ERR_INVALID_ARG),
+    (dict(q_end=4097), dsa.DSA_ERR_INVALID_ARG),
+    (dict(ln_eps=0.0), dsa.DSA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), dsa.DSA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=[0, 100, 100, 4096]), dsa.DSA_ERR_INVALID_ARG),   # empty document
+    (dict(cu_seqlens=[0, 100, 4000]), dsa.DSA_ERR_INVALID_ARG),        # does not end at T
+    (dict(cu_seqlens=[1, 100, 4096]), dsa.DSA_ERR_INVALID_ARG),        # does not start at 0
+])
+def test_invalid_shapes(kw, status):
+    s = _shape(**kw)
+    if "cu_seqlens" in kw:
+        s.cu_seqlens_dev = 16  # a non-null stand-in; never dereferenced by the host checks
+    assert dsa.dsa_check_shape(s) == status
+
+
+def test_multi_document_needs_device_offsets():
+    s = _shape(cu_seqlens=[0, 1000, 4096])
+    assert dsa.dsa_check_shape(s) == dsa.DSA_ERR_INVALID_ARG
+    s.cu_seqlens_dev = 256
+    assert dsa.dsa_check_shape(s) == dsa.DSA_OK
+
+
+def test_entry_points_reject_before_any_hip_call():
+    """Null pointers, misalignment and small workspaces are caught on the host (no GPU here)."""
+    L = dsa.lib()
+    s = _shape()
+    P = ctypes.byref(s)
+    fake = 1 << 20  # aligned, never dereferenced: every call below fails its host checks first
+    n = dsa.dsa_workspace_size(s)
+    assert L.dsa_index_topk(P, None, fake, None, None, fake, fake, fake, n, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk(P, fake + 2, fake, None, None, fake, fake, fake, n, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk(P, fake, fake, None, None, fake, fake, None, n, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_index_topk(P, fake, fake, None, None, fake, fake, fake, n - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_index_topk(P, fake, fake, None, None, fake, fake, fake + 16, n, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_fwd(P, fake, None, fake, fake, fake, fake, None, fake, n, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_fwd(P, fake, fake + 8, fake, fake, fake, fake, None, fake, n, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_fused_fwd(P, fake, fake, None, None, fake, fake, fake, fake, fake, fake, None, None, fake, n,
+                           None) == dsa.DSA_ERR_INVALID_ARG
+    bad = _shape(H=8)
+    assert L.dsa_fused_fwd(ctypes.byref(bad), fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake, None,
+                           fake, n, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_check_shape(None) == dsa.DSA_ERR_INVALID_ARG

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Index rule and output rule: see tests/parity.py. Outputs are compared with the oracle's attention
+computed on the GPU's own indices, so a legitimate near-tie swap cannot fail the output check.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_indexer_top_index_amd as dsa
+import oracle
+import testgen as tg
+from tests import gpu_util as gu
+from tests.parity import check_index_row, check_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_rows(cfg, keys, qrows, rows, idx_gpu, out_gpu, lse_gpu=None, LNk=None):
+    """keys: host k_I/kv/W_UV; qrows: tg.query_rows for `rows`; idx_gpu/out_gpu: host arrays for `rows`."""
+    cu = cfg.cu_seqlens
+    LNk = oracle.key_layernorm(keys["k_I"], cfg.ln_eps) if LNk is None else LNk
+    q_I = qrows["q_I"].reshape(len(rows), cfg.H_I, cfg.d_I)
+    w = qrows["w"].reshape(len(rows), cfg.H_I)
+    o_idx, theta, keff = oracle.topk(rows, q_I, w, LNk, cu, cfg.topk)
+    bad = []
+    for j, t in enumerate(rows):
+        b = oracle.doc_begin(cu, t)
+        msg = check_index_row(idx_gpu[j], o_idx[j], keff[j], b, t, cfg.topk, q_I[j], w[j], LNk, theta[j])
+        if msg:
+            bad.append(msg)
+    assert not bad, f"{len(bad)} index rows fail, first: {bad[:3]}"
+    q = qrows["q"].reshape(len(rows), cfg.H, 576)
+    gate = qrows["gate"].reshape(len(rows), cfg.H)
+    ref = oracle.sparse_mla(rows, q, keys["kv"], idx_gpu, keys["W_UV"], gate, cfg.softmax_scale)
+    ok, err, mx = check_outputs(out_gpu, ref["out"])
+    assert ok, f"output max err {err} > 2e-2 * {mx}"
+    if lse_gpu is not None:
+        assert np.abs(lse_gpu - ref["lse"]).max() < 5e-3
+    same = np.array([set(idx_gpu[j]) == set(o_idx[j]) for j in range(len(rows))])
+    return same.mean(), err / mx
+
+
+_cache = {}
+
+
+def _inputs(name_or_cfg):
+    cfg = tg.get_config(name_or_cfg) if isinstance(name_or_cfg, str) else name_or_cfg
+    if cfg.name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        _say(f"[gpu] generating inputs for {cfg.name} (T={cfg.T})")
+        keys, dev = gu.device_inputs(cfg)
+        _cache[cfg.name] = (cfg, keys, dev)
+    return _cache[cfg.name]
+
+
+def _run_and_check(cfg, keys, dev, rows, with_lse=True):
+    _say(f"[gpu] fused forward {cfg.name}: T={cfg.T} docs={cfg.n_docs} k={cfg.topk} H={cfg.H}")
+    res = gu.run_fused(cfg, dev, with_lse=with_lse)
+    torch.cuda.synchronize()
+    idx = res["topk_idx"].cpu().numpy()
+    out = gu.bf16_tensor_to_f32(res["out"])
+    lse = res["lse"].cpu().numpy() if with_lse else None
+    rows = np.asarray(rows, dtype=np.int64)
+    qrows = tg.query_rows(cfg, rows)
+    frac, rel = _check_rows(cfg, keys, qrows, rows, idx[rows], out[rows], None if lse is None else lse[rows])
+    _say(f"[gpu] {cfg.name}: {len(rows)} rows ok, identical index sets {frac:.3f}, out rel err {rel:.2e}")
+    return res, idx, out
+
+
+# ------------------------------------------------------------------ element-by-element, small sizes
+
+def test_tiny_all_rows():
+    cfg, keys, dev = _inputs("tiny")
+    _run_and_check(cfg, keys, dev, np.arange(cfg.T))
+
+
+MID = tg.Config("mid", 7, [2203], topk=512, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24, W_UV_std=0.02)
+PACKED_SMALL = tg.Config("packed-small", 8, [700, 1, 33, 900, 256, 257, 1400], topk=256, H=96, H_I=64, d_I=128,
+                         w_scale=1 / 8, q_std=1.0, W_UV_std=0.02)
+
+
+def test_mid_production_shapes_all_rows():
+    """96 heads, 64x128 indexer, k=512, T=2203: every row, ragged final query block and key chunk."""
+    cfg, keys, dev = _inputs(MID)
+    _run_and_check(cfg, keys, dev, np.arange(cfg.T))
+
+
+def test_packed_small_all_rows():
+    """Packed documents (lengths 700, 1, 33, 900, 256, 257, 1400), k=256: every row."""
+    cfg, keys, dev = _inputs(PACKED_SMALL)
+    _run_and_check(cfg, keys, dev, np.arange(cfg.T))
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+
+def _sample(cfg, extra, n=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(int(x) for x in extra if 0 <= x < cfg.T)
+    rows |= set(int(x) for x in rng.integers(0, cfg.T, n))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["t4096", "t8192"])
+def test_single_document_full_size(name):
+    cfg, keys, dev = _inputs(name)
+    rows = _sample(cfg, [0, 1, 2047, 2048, 2049, cfg.T // 2, cfg.T - 2, cfg.T - 1])
+    _run_and_check(cfg, keys, dev, rows)
+
+
+def test_dense_check_t2048_equals_dense_attention():
+    """T = k = 2048: every row keeps every causal key; outputs equal dense causal attention."""
+    cfg, keys, dev = _inputs("dense2048")
+    res = gu.run_fused(cfg, dev)
+    torch.cuda.synchronize()
+    idx = res["topk_idx"].cpu().numpy()
+    for t in range(cfg.T):
+        assert np.array_equal(idx[t, :t + 1], np.arange(t + 1)) and np.all(idx[t, t + 1:] == -1)
+    rows = np.array([0, 1, 5, 1024, 2047])
+    qr = tg.query_rows(cfg, rows)
+    dense = oracle.dense_causal(rows, qr["q"].reshape(len(rows), cfg.H, 576), keys["kv"], cfg.cu_seqlens,
+                                keys["W_UV"], qr["gate"].reshape(len(rows), cfg.H), cfg.softmax_scale)
+    ok, err, mx = check_outputs(gu.bf16_tensor_to_f32(res["out"])[rows], dense)
+    assert ok, (err, mx)
+
+
+def test_packed_full_size():
+    cfg, keys, dev = _inputs("packed")
+    cu = cfg.cu_seqlens
+    extra = []
+    for d in range(cfg.n_docs):
+        b, e = int(cu[d]), int(cu[d + 1])
+        extra += [b, b + 1, min(b + 2047, e - 1), min(b + 2048, e - 1), e - 1]
+    rows = _sample(cfg, extra, n=8)
+    _run_and_check(cfg, keys, dev, rows)
+
+
+def test_long_context_131072_sampled():
+    cfg, keys, dev = _inputs("t131072")
+    rows = _sample(cfg, [0, 2047, 2048, 2049, 65535, 131070, 131071], n=5)
+    _run_and_check(cfg, keys, dev, rows, with_lse=False)
+    _cache.clear()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_determinism_and_row_range():
+    """Two runs are bit-identical; a query-row range [q_begin, q_end) equals that slice of the full run."""
+    cfg, keys, dev = _inputs("t4096")
+    a = gu.run_fused(cfg, dev)
+    b = gu.run_fused(cfg, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(a["topk_idx"], b["topk_idx"])
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+    part = gu.run_fused(cfg, dev, q_begin=1000, q_end=3001)
+    torch.cuda.synchronize()
+    assert torch.equal(part["topk_idx"], a["topk_idx"][1000:3001])
+    assert torch.equal(part["out"].view(torch.int16), a["out"][1000:3001].view(torch.int16))
+
+
+def test_key_layernorm_bit_exact_with_affine():
+    """The LN(k_I) the indexer consumes (first workspace region) equals the oracle's bf16 LN bit for bit."""
+    cfg = tg.get_config("t4096")
+    keys = tg.key_side(cfg)
+    rng = np.random.default_rng(5)
+    gamma = rng.uniform(0.5, 1.5, cfg.d_I).astype(np.float32)
+    beta = rng.uniform(-0.2, 0.2, cfg.d_I).astype(np.float32)
+    for g, bb in [(None, None), (gamma, beta)]:
+        shape = gu.shape_of(cfg, q_begin=cfg.T - 4, q_end=cfg.T)
+        ws = dsa.alloc_workspace(shape)
+        q_I = gu.bf16_np_to_tensor(tg.query_rows(cfg, range(cfg.T - 4, cfg.T))["q_I"])
+        w = gu.bf16_np_to_tensor(tg.query_rows(cfg, range(cfg.T - 4, cfg.T))["w"])
+        idx = torch.empty((4, cfg.topk), dtype=torch.int32, device="cuda")
+        dsa.dsa_index_topk(shape, q_I, gu.bf16_np_to_tensor(keys["k_I"]), w, idx, ws,
+                           ln_gamma=None if g is None else torch.from_numpy(g).cuda(),
+                           ln_beta=None if bb is None else torch.from_numpy(bb).cuda())
+        torch.cuda.synchronize()
+        lnk_gpu = ws[: cfg.T * cfg.d_I * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(cfg.T, cfg.d_I)
+        lnk_ref = oracle.key_layernorm(keys["k_I"], cfg.ln_eps, g, bb)
+        assert np.array_equal(lnk_gpu, lnk_ref)
+
+
+def _small_cfg(name, seed, lens, topk, H=16, H_I=4, d_I=64, **kw):
+    return tg.Config(name, seed, lens, topk=topk, H=H, H_I=H_I, d_I=d_I, w_scale=kw.pop("w_scale", 0.5), **kw)
+
+
+@pytest.mark.parametrize("case", ["T1", "k1", "k3-negw", "ties", "const-keys"])
+def test_edge_cases(case):
+    if case == "T1":
+        cfg = _small_cfg("T1", 40, [1], topk=1, H=96, H_I=64, d_I=128)
+    elif case == "k1":
+        cfg = _small_cfg("k1", 41, [300], topk=1)
+    elif case == "k3-negw":
+        cfg = _small_cfg("k3", 42, [97, 200], topk=3, w_scale=-1.0)
+    else:
+        cfg = _small_cfg(case, 43, [333], topk=40)
+    inp = tg.make_inputs(cfg)
+    if case == "ties":  # duplicated key rows: equal scores, resolved to the lower index
+        inp["k_I"][1::3] = inp["k_I"][0::3][: len(inp["k_I"][1::3])]
+    if case == "const-keys":  # LN of a constant row is 0: every score is exactly +0
+        inp["k_I"][:] = tg.f32_to_bf16(np.full(inp["k_I"].shape, 0.5, np.float32))
+    dev = gu.to_device(inp)
+    _say(f"[gpu] edge case {case}: T={cfg.T} k={cfg.topk}")
+    res = gu.run_fused(cfg, dev, with_lse=True)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.T)
+    keys = {k: inp[k] for k in ["k_I", "kv", "W_UV"]}
+    qrows = {k: inp[k].reshape(cfg.T, -1) for k in ["q_I", "w", "q", "gate"]}
+    idx = res["topk_idx"].cpu().numpy()
+    _check_rows(cfg, keys, qrows, rows, idx, gu.bf16_tensor_to_f32(res["out"]), res["lse"].cpu().numpy())
+    if case in ("ties", "const-keys"):  # exact ties must resolve exactly as the oracle does
+        LNk = oracle.key_layernorm(inp["k_I"], cfg.ln_eps)
+        o_idx, _, _ = oracle.topk(rows, inp["q_I"], inp["w"], LNk, cfg.cu_seqlens, cfg.topk)
+        if case == "const-keys":
+            assert np.array_equal(idx, o_idx)
+
+
+def test_sparse_mla_caller_indices():
+    """dsa_sparse_mla_fwd with caller indices: -1, out-of-range entries and duplicates; only the first
+    min(k, n_t) entries of a row are read."""
+    cfg = _small_cfg("mla-idx", 44, [500], topk=64, H=96)
+    inp = tg.make_inputs(cfg)
+    rng = np.random.default_rng(3)
+    T, k = cfg.T, cfg.topk
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        keff = min(k, t + 1)
+        row = rng.integers(0, t + 1, keff).astype(np.int32)  # duplicates allowed
+        kill = rng.random(keff) < 0.2
+        row[kill] = rng.choice([-1, -7, T, T + 100], kill.sum())
+        idx[t, :keff] = row
+    idx[7, :] = -1  # a row with no usable entry: zeros, lse -inf
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_workspace(shape)
+    out = torch.empty((T, cfg.H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    _say("[gpu] sparse_mla_fwd with caller indices")
+    dsa.dsa_sparse_mla_fwd(shape, dev["q"], dev["kv"], torch.from_numpy(idx).cuda(), dev["W_UV"], dev["gate"], out,
+                           ws, lse=lse)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_mla(np.arange(T), inp["q"], inp["kv"], idx, inp["W_UV"], inp["gate"], cfg.softmax_scale)
+    got = gu.bf16_tensor_to_f32(out)
+    ok, err, mx = check_outputs(got, ref["out"])
+    assert ok, (err, mx)
+    lse_g = lse.cpu().numpy()
+    empty = np.isneginf(ref["lse"])
+    assert empty[7].all() and np.all(got[7] == 0)
+    assert np.array_equal(np.isneginf(lse_g), empty)
+    assert np.abs(lse_g[~empty] - ref["lse"][~empty]).max() < 5e-3
