@@ -1,0 +1,213 @@
+"""Benchmark of the gated DSA forward hot path on one MI355X.
+
+A step is one dsa_fused_fwd call (key LayerNorm, indexer + top-k, sparse latent attention, V
+up-projection and gate) over one batch of synthetic input. The default workload is a single
+4,096-token document (top-2048, 96 heads, indexer 64 heads x 128, latent 512+64), seed 2. All
+inputs are resident in device memory before timing starts.
+
+Prints one JSON line: throughput (query tokens/s), the roofline of the dominant kernel (the sparse
+latent attention kernel at this size), and the CPU oracle timed on a bounded sample of rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/sec for indexer+top-2048+sparse MLA fwd; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "dsa_indexer_top_index_amd", "csrc", "k_mla.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_sparse_attention_t4096.json")
+
+WORKLOAD_TEXT = {
+    "t4096": "single document T=4096, top-2048, 96 heads, indexer 64x128 with key LayerNorm, latent 512+64, "
+             "W_UV 96x512x128, per-head gate",
+    "t8192": "single document T=8192, top-2048, 96 heads, indexer 64x128, latent 512+64",
+    "packed": "8 packed documents (lengths U[1024,8192], seed 4), top-2048, 96 heads, indexer 64x128, latent 512+64",
+    "t131072": "single document T=131072, top-2048, 96 heads, indexer 64x128, latent 512+64",
+    "tiny": "single document T=1024, top-256, 16 heads, indexer 4x64, latent 512+64",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sum_keff(cfg):
+    cu = cfg.cu_seqlens
+    total = 0
+    sel_pairs = 0
+    all_pairs = 0
+    for d in range(cfg.n_docs):
+        L = int(cu[d + 1] - cu[d])
+        n = np.arange(1, L + 1, dtype=np.int64)
+        total += int(np.minimum(n, cfg.topk).sum())
+        all_pairs += int(n.sum())
+        sel_pairs += int(n[n > cfg.topk].sum())
+    return total, all_pairs, sel_pairs
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launch_bytes_alg):
+    """HBM bytes per attention launch from the committed counter summary, if it still matches the kernel."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    d = json.load(open(PMC_FILE))
+    if d.get("kernel_source_sha256_16") != src_hash(ATTN_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, keys, stride):
+    import oracle
+    import testgen as tg
+
+    rows = np.arange(cfg.T - 1, -1, -stride)[::-1]
+    t0 = time.perf_counter()
+    LNk = oracle.key_layernorm(keys["k_I"], cfg.ln_eps)
+    qr = tg.query_rows(cfg, rows)
+    gen_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx, theta, keff = oracle.topk(rows, qr["q_I"].reshape(len(rows), cfg.H_I, cfg.d_I), qr["w"], LNk,
+                                   cfg.cu_seqlens, cfg.topk)
+    oracle.sparse_mla(rows, qr["q"].reshape(len(rows), cfg.H, 576), keys["kv"], idx, keys["W_UV"],
+                      qr["gate"].reshape(len(rows), cfg.H), cfg.softmax_scale)
+    el = time.perf_counter() - t0
+    return {
+        "value": len(rows) / el, "unit": "query tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+        "sample": f"{len(rows)} of {cfg.T} rows (every {stride}th row, ending at the last), top-k + attention + "
+                  f"up-projection + gate in the plain C++ oracle (FP32 scores, FP64 attention); LayerNorm of all "
+                  f"keys ({gen_s:.1f}s with input drawing) excluded; {el:.1f}s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t4096", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-stride", type=int, default=4)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    import dsa_indexer_top_index_amd as dsa
+    import testgen as tg
+    from tests import gpu_util as gu
+
+    cfg = tg.get_config(args.workload)
+    log(f"[bench] generating {cfg.name} inputs (T={cfg.T})")
+    keys, dev = gu.device_inputs(cfg)
+    shape = gu.shape_of(cfg, dev.get("cu_seqlens"))
+    ws = dsa.alloc_workspace(shape)
+    T = cfg.T
+    topk_idx = torch.empty((T, cfg.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, cfg.H, 128), dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty((T, cfg.H, 512), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        dsa.dsa_fused_fwd(shape, dev["q_I"], dev["k_I"], dev["w"], dev["q"], dev["kv"], dev["W_UV"], dev["gate"],
+                          topk_idx, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el / args.steps * 1e3
+    value = T * args.steps / el
+
+    # Per-stage launch durations, HIP events on the stream the kernels run on.
+    stream = torch.cuda.current_stream()
+    n_stage = max(args.steps, 3)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_stage)]
+    for i in range(n_stage):
+        ev[i][0].record(stream)
+        dsa.dsa_index_topk(shape, dev["q_I"], dev["k_I"], dev["w"], topk_idx, ws)
+        ev[i][1].record(stream)
+        dsa.dsa_sparse_attention_latent(shape, dev["q"], dev["kv"], topk_idx, o_lat)
+        ev[i][2].record(stream)
+        dsa.dsa_up_gate(shape, o_lat, dev["W_UV"], dev["gate"], out)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    t_up = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    keff_sum, all_pairs, sel_pairs = sum_keff(cfg)
+    att_flop = 2.0 * cfg.H * (576 + 512) * keff_sum          # QK^T over 576 dims + PV over 512, per selected key
+    idx_flop_sel = 2.0 * cfg.H_I * cfg.d_I * sel_pairs       # scores the selection needs (rows with n_t > k)
+    idx_flop_all = 2.0 * cfg.H_I * cfg.d_I * all_pairs       # every causal pair, short rows included
+    up_flop = 2.0 * cfg.H * 512 * 128 * T
+    up_bytes = T * cfg.H * (512 + 128) * 2 + T * cfg.H * 2 + cfg.H * 512 * 128 * 2
+    att_tflops = att_flop / (t_att * 1e-3) / 1e12
+    total_flop = att_flop + idx_flop_sel + up_flop
+    traffic = traffic_from_profile(None)
+    roof = {
+        "kernel": "k_sparse_mla (dsa_sparse_attention_latent)",
+        "bound": "mfma", "achieved": round(att_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "alg_flop_per_launch": att_flop, "launch_ms": round(t_att, 4),
+    }
+    stages = {
+        "index_topk_ms": round(t_idx, 4), "attention_ms": round(t_att, 4), "up_gate_ms": round(t_up, 4),
+        "indexer_tflops_needed_rows": round(idx_flop_sel / (t_idx * 1e-3) / 1e12, 2),
+        "indexer_tflops_all_pairs": round(idx_flop_all / (t_idx * 1e-3) / 1e12, 2),
+        "indexer_frac_needed_rows": round(idx_flop_sel / (t_idx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "up_gate_gbs": round(up_bytes / (t_up * 1e-3) / 1e9, 1),
+        "path_tflops": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        cpu = cpu_baseline(cfg, keys, args.cpu_stride)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[cfg.name], "T": T, "docs": cfg.n_docs, "topk": cfg.topk, "H": cfg.H,
+                   "H_I": cfg.H_I, "d_I": cfg.d_I, "seed": cfg.seed},
+        "roofline": roof, "stages": stages, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
   dsa_check_shape(shape) -> int status
   dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
   dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None)
+  dsa_sparse_attention_latent(shape, q, kv, topk_idx, o_lat, lse=None)
+  dsa_up_gate(shape, o_lat, W_UV, gate, out)
   dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace,
                 ln_gamma=None, ln_beta=None, lse=None)
 """
@@ -70,6 +72,10 @@ def lib():
         L.dsa_index_topk.restype = ctypes.c_int
         L.dsa_sparse_mla_fwd.argtypes = [P, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_sparse_mla_fwd.restype = ctypes.c_int
+        L.dsa_sparse_attention_latent.argtypes = [P, v, v, v, v, v, v]
+        L.dsa_sparse_attention_latent.restype = ctypes.c_int
+        L.dsa_up_gate.argtypes = [P, v, v, v, v, v]
+        L.dsa_up_gate.restype = ctypes.c_int
         L.dsa_fused_fwd.argtypes = [P, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_fused_fwd.restype = ctypes.c_int
         _lib = L
@@ -167,6 +173,21 @@ def dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=N
         _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"), _p(out, bf, "out"), _p(lse, torch.float32, "lse", True),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_sparse_mla_fwd")
+
+
+def dsa_sparse_attention_latent(shape, q, kv, topk_idx, o_lat, lse=None):
+    bf = torch.bfloat16
+    st = lib().dsa_sparse_attention_latent(
+        ctypes.byref(shape), _p(q, bf, "q"), _p(kv, bf, "kv"), _p(topk_idx, torch.int32, "topk_idx"),
+        _p(o_lat, bf, "o_lat"), _p(lse, torch.float32, "lse", True), _stream())
+    _raise(st, "dsa_sparse_attention_latent")
+
+
+def dsa_up_gate(shape, o_lat, W_UV, gate, out):
+    bf = torch.bfloat16
+    st = lib().dsa_up_gate(ctypes.byref(shape), _p(o_lat, bf, "o_lat"), _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"),
+                           _p(out, bf, "out"), _stream())
+    _raise(st, "dsa_up_gate")
 
 
 def dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace, ln_gamma=None, ln_beta=None,

@@ -107,6 +107,39 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   return DSA_OK;
 }
 
+static dsa_status launch_attention(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                                   uint16_t* olat, float* lse, int64_t c0, int64_t n, hipStream_t st) {
+  dsa::MlaArgs m{};
+  m.q = q;
+  m.kv = kv;
+  m.idx = idx;
+  m.o_lat = olat;
+  m.lse = lse;
+  m.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
+  m.n_docs = s->n_docs;
+  m.T = s->T;
+  m.row0 = s->q_begin;
+  m.chunk_r0 = static_cast<int>(c0);
+  m.chunk_rows = static_cast<int>(n);
+  m.k = s->topk;
+  m.H = s->H;
+  m.scale_log2 = s->softmax_scale * 1.4426950408889634f;
+  return dsa::launch_sparse_mla(m, st) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+static dsa_status launch_up(const dsa_shape* s, const uint16_t* olat, const uint16_t* W_UV, const uint16_t* gate,
+                            uint16_t* out, int64_t c0, int64_t n, hipStream_t st) {
+  dsa::UpArgs u{};
+  u.o_lat = olat;
+  u.W_UV = W_UV;
+  u.gate = gate;
+  u.out = out;
+  u.chunk_r0 = static_cast<int>(c0);
+  u.chunk_rows = static_cast<int>(n);
+  u.H = s->H;
+  return dsa::launch_up_gate(u, st) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 static dsa_status run_mla(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                           const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws, hipStream_t st) {
   const auto L = layout_of(s);
@@ -114,31 +147,9 @@ static dsa_status run_mla(const dsa_shape* s, const uint16_t* q, const uint16_t*
   const int64_t rows = rows_of(s);
   for (int64_t c0 = 0; c0 < rows; c0 += L.chunk_rows) {
     const int64_t n = (rows - c0) < L.chunk_rows ? (rows - c0) : L.chunk_rows;
-    dsa::MlaArgs m{};
-    m.q = q;
-    m.kv = kv;
-    m.idx = idx;
-    m.o_lat = olat;
-    m.lse = lse;
-    m.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
-    m.n_docs = s->n_docs;
-    m.T = s->T;
-    m.row0 = s->q_begin;
-    m.chunk_r0 = static_cast<int>(c0);
-    m.chunk_rows = static_cast<int>(n);
-    m.k = s->topk;
-    m.H = s->H;
-    m.scale_log2 = s->softmax_scale * 1.4426950408889634f;
-    if (dsa::launch_sparse_mla(m, st) != hipSuccess) return DSA_ERR_LAUNCH;
-    dsa::UpArgs u{};
-    u.o_lat = olat;
-    u.W_UV = W_UV;
-    u.gate = gate;
-    u.out = out;
-    u.chunk_r0 = static_cast<int>(c0);
-    u.chunk_rows = static_cast<int>(n);
-    u.H = s->H;
-    if (dsa::launch_up_gate(u, st) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa_status r = launch_attention(s, q, kv, idx, olat, lse, c0, n, st);
+    if (r != DSA_OK) return r;
+    if ((r = launch_up(s, olat, W_UV, gate, out, c0, n, st)) != DSA_OK) return r;
   }
   return DSA_OK;
 }
@@ -167,6 +178,25 @@ dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint1
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
   return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_attention_latent(const dsa_shape* s, const uint16_t* q, const uint16_t* kv,
+                                       const int32_t* topk_idx, uint16_t* o_lat, float* lse, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q || !kv || !topk_idx || !o_lat) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(topk_idx, 4) || !aligned(o_lat, 16) || !aligned(lse, 4))
+    return DSA_ERR_INVALID_ARG;
+  return launch_attention(s, q, kv, topk_idx, o_lat, lse, 0, rows_of(s), static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_up_gate(const dsa_shape* s, const uint16_t* o_lat, const uint16_t* W_UV, const uint16_t* gate,
+                       uint16_t* out, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!o_lat || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(o_lat, 16) || !aligned(W_UV, 16) || !aligned(gate, 2) || !aligned(out, 2)) return DSA_ERR_INVALID_ARG;
+  return launch_up(s, o_lat, W_UV, gate, out, 0, rows_of(s), static_cast<hipStream_t>(stream));
 }
 
 dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,

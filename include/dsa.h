@@ -92,12 +92,25 @@ dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uin
  * kv [T, 576] bf16; topk_idx [rows, topk] int32 (entries outside [0, T) are ignored; a row with
  * no usable entry yields zeros and lse = -inf); W_UV [H, 512, 128] bf16; gate [rows, H] bf16
  * gate logits. Outputs: out [rows, H, 128] bf16 = bf16(sigmoid(gate) * o);
- * lse [rows, H] float32 natural-log softmax normaliser, or NULL. Every usable index is
- * attended; causality of the indices is the caller's contract. */
+ * lse [rows, H] float32 natural-log softmax normaliser, or NULL. Only the first min(topk, n)
+ * entries of a row are read (n = the row's number of causal keys); every usable one among them
+ * is attended, duplicates included; causality of the indices is the caller's contract.
+ * Workspace: >= dsa_workspace_size(shape) bytes (holds o_lat for up to 16384 rows at a time). */
 dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
                               const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
                               uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Step 4 alone: sparse latent attention into a caller buffer. Inputs as dsa_sparse_mla_fwd.
+ * Output: o_lat [rows, H, 512] bf16 = softmax-weighted sum of the V parts (dims 0..511) of the
+ * selected latent rows, before the up-projection; lse as in dsa_sparse_mla_fwd. No workspace. */
+dsa_status dsa_sparse_attention_latent(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
+                                       const int32_t* topk_idx, uint16_t* o_lat, float* lse, void* stream);
+
+/* Step 5 alone: out [rows, H, 128] bf16 = bf16(sigmoid(gate) * (o_lat . W_UV[h])) per head, from
+ * o_lat [rows, H, 512] bf16, W_UV [H, 512, 128] bf16 and gate [rows, H] bf16. No workspace. */
+dsa_status dsa_up_gate(const dsa_shape* shape, const uint16_t* o_lat, const uint16_t* W_UV, const uint16_t* gate,
+                       uint16_t* out, void* stream);
 
 /* Steps 1-5 in one call: the union of the two argument lists; topk_idx is written and then used. */
 dsa_status dsa_fused_fwd(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,

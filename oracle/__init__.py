@@ -34,6 +34,7 @@ def lib():
         build()
         L = ctypes.CDLL(_LIB_PATH)
         p, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_doc_begin.argtypes = [p, i32, i64]
         L.oracle_doc_begin.restype = i64
         L.oracle_key_layernorm.argtypes = [p, i64, i32, p, p, d, p, p]
@@ -66,6 +67,10 @@ def key_layernorm(k_I, eps=1e-5, gamma=None, beta=None, want_pre=False):
     b, pb = _opt(beta, np.float32)
     lib().oracle_key_layernorm(pk, T, d_I, pg, pb, eps, out.ctypes.data, pre.ctypes.data if want_pre else None)
     return (out, pre) if want_pre else out
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def doc_begin(cu_seqlens, t):

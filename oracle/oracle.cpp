@@ -50,6 +50,10 @@
 #include <numeric>
 #include <vector>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 namespace {
 
 constexpr int kDL = 576;  // latent row: kv_lora_rank 512 + 64 unrotated dims  [API]
@@ -89,6 +93,15 @@ int64_t doc_begin(const int32_t* cu, int32_t n_docs, int64_t t) {
 extern "C" {
 
 int oracle_abi_version() { return 1; }
+
+// Threads the OpenMP loops below run with.
+int oracle_num_threads() {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 int64_t oracle_doc_begin(const int32_t* cu, int32_t n_docs, int64_t t) { return doc_begin(cu, n_docs, t); }
 

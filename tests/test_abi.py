@@ -19,8 +19,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_sparse_mla_fwd",
-                     "dsa_status_string", "dsa_workspace_size"]
+    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_sparse_attention_latent",
+                     "dsa_sparse_mla_fwd", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
