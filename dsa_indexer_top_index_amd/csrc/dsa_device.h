@@ -29,10 +29,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// 2^x on the hardware exponential unit (no range reduction; results below the normal range flush to 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // double -> bf16 bits in one rounding step (nearest, ties to even), for |x| in the normal float range or 0.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
@@ -66,8 +72,33 @@ __device__ __forceinline__ void wave_lds_sync() { __asm__ volatile("s_waitcnt lg
 __device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 16-byte asynchronous copy global -> LDS. Lane i of the wave writes lds_wave_base + 16*i.
+// Issued as inline assembly on purpose: the compiler then does not treat the copy as an LDS write
+// and does not drain every outstanding copy before the next LDS read of another buffer. Callers
+// order the copies themselves with wait_vmem_le<N>() and a barrier.
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, DSA_LDS void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+  // the LDS base is wave-uniform by contract; readfirstlane puts it in an SGPR for M0
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete in order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads(): it does not wait for
+// this wave's outstanding global->LDS copies. LDS reads and writes issued before it are complete.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS byte address of a __shared__ object, and the LDS pointer of a byte address. Working on 32-bit
+// offsets lets the compiler fold constant displacements into the ds_read immediate offset.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* shared_obj) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const DSA_LDS void*)shared_obj));
+}
+__device__ __forceinline__ DSA_LDS uint8_t* lds_ptr(uint32_t addr) {
+  return reinterpret_cast<DSA_LDS uint8_t*>(static_cast<uintptr_t>(addr));
 }
 
 __device__ __forceinline__ bf16x8 lds_read16(const DSA_LDS void* p) {
@@ -80,6 +111,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const DSA_LDS void* p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<DSA_LDS s16x4*>(const_cast<DSA_LDS void*>(p)));
   return __builtin_bit_cast(u32x2, v);
 }
+
+// O += A * B on v_mfma_f32_32x32x16_bf16 with the accumulator pinned to AGPRs. Issued as inline
+// assembly so that a kernel whose other MFMAs use the VGPR form keeps a large accumulator set in
+// AGPRs. The compiler cannot see this instruction's hazards, so callers must (1) leave at least 4
+// wait states between a VALU write of a or b and this instruction, and (2) leave 40 wait states
+// after the last of these instructions before any VALU access to acc (mfma_agpr_drain()).
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, u32x4 a, u32x4 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_agpr_settle() { asm volatile("s_nop 4" ::: "memory"); }
+__device__ __forceinline__ void mfma_agpr_drain() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory"); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

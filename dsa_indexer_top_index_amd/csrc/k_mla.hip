@@ -8,259 +8,369 @@
 //     l_j = scale * q[t,h,:] . kv[s_j,:]          (576 dims)
 //     o_lat[t,h,:] = softmax_j(l) . kv[s_j, 0:512]
 //
-// Kernel design: one wave per (query row, group of 32 heads), four independent waves per
-// workgroup, rows taken longest first, and the three head groups of a row placed on one XCD so
-// its gathered rows are shared through that XCD's L2.
-//  - Gather: the 16 selected rows of a tile (16 x 1152 bytes) are copied global -> LDS with
-//    asynchronous 16-byte copies (18 wave instructions, each filling four 16-byte columns of all
-//    16 rows), double buffered so the next tile's gather overlaps this tile's math. The layout
-//    is column-major in 16-byte granules with a row XOR, so the QK operand reads and the
-//    transposed V reads are bank-conflict free and every address is affine in the loop index.
-//  - QK^T: v_mfma_f32_16x16x32_bf16 computes S^T[16 keys x 16 heads] (two head tiles), K = 576,
-//    with the head group's q fragments resident in registers.
-//  - Softmax in FP32 (base 2) against a per-head reference maximum taken from the first tile;
-//    the accumulators are never rescaled inside the loop. If a later logit exceeds the
-//    reference by more than 2^64 (never for bounded inputs, but possible in principle), the row
-//    restarts with the larger reference, so no value can overflow.
-//  - PV: P (bf16) becomes the A operand of v_mfma_f32_32x32x16_bf16 with the 32 heads as M
-//    through one permlane16 swap per register; V is read straight from the natural row layout
-//    with ds_read_b64_tr_b16, N = 512 latent dims, K = 16 keys.
-//  - Epilogue: divide by the softmax sum, write o_lat (bf16) for the up-projection kernel, and
-//    the natural-log normaliser lse if requested.
+// Kernel design: one workgroup per query row (rows longest first, consecutive rows on one XCD),
+// with two kinds of waves that meet in LDS, so every SIMD of the CU runs matrix instructions:
+//  - Value waves (two): each owns the output accumulators of all heads for half of the 512 latent
+//    dims (384 FP32 per lane, two thirds of them in AGPRs). They issue every asynchronous 16-byte
+//    global->LDS copy of the gathered rows into a ring of six 16-row tiles (copies run four tiles
+//    ahead), and compute O += P V on v_mfma_f32_32x32x16_bf16: heads as M (32-head tiles), latent
+//    dims as N, 16 keys as K. V is read straight from the natural row layout with
+//    ds_read_b64_tr_b16 and P from LDS. They run one tile behind the score waves.
+//  - Score waves (two for 96 heads, 48 heads each; one for 16 heads): q fragments stay in
+//    registers; S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys as M, 16-head tiles as N,
+//    K = 576); softmax numerators in FP32 (base 2) against a per-head reference maximum set by the
+//    first usable tile; P (bf16) goes to a two-slot LDS ring already in the value waves' operand
+//    layout.
+//  One barrier per tile hands both rings over. Each gathered row is read from memory once per
+//  query. The tile layout is column-major in 16-byte granules with a row XOR, so the QK operand
+//  reads and the transposed V reads are bank-conflict free and every address is affine in the
+//  loop index. Accumulators are never rescaled: if a logit exceeds its head's reference by more
+//  than 2^64 (impossible for bounded inputs, but possible in principle), the row is redone, first
+//  a QK-only pass for each head's exact maximum, then the full pass against it, so no numerator
+//  can overflow.
+//  Epilogue: divide by the softmax sum, write o_lat (bf16) for the up-projection kernel, and the
+//  natural-log normaliser lse if requested.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
 namespace dsa {
 
-constexpr int kMlaWaves = 4;
 constexpr int kTileKeys = 16;
 constexpr int kRowGran = kLatent * 2 / 16;            // 72 granules (16 B) per latent row
 constexpr int kTileBytes = kTileKeys * kRowGran * 16;  // 18432: 18 wave copies of 1 KB
-constexpr float kRestartGap = 64.0f;                   // log2 headroom of the running maximum
-constexpr int kMaxRestarts = 8;
+constexpr int kRing = 6;                               // tiles in the shared LDS ring
+constexpr int kAhead = kRing - 2;                      // tiles whose copies run ahead of the scores
+constexpr float kRestartGap = 64.0f;                   // log2 headroom of a head's reference maximum
+constexpr int kMaxIdx = 2048;
 
 // Tile layout in LDS: granule (row r, column c) lives at slot c*16 + (r ^ 4*(c%4)). One wave
 // copy fills four columns of all 16 rows; the QK operand reads (16 rows, one column) and the
-// transposed V reads (4 rows x 4 columns per 16 lanes) both hit 16 distinct bank quads, and
-// every read address is affine in the loop counter.
-__device__ __forceinline__ int mla_slot(int r, int c) { return c * 16 + (r ^ (4 * (c & 3))); }
+// transposed V reads (4 rows x 4 columns per 16 lanes) both hit 16 distinct bank quads.
 
-// One wave handles 32 heads; a layer with fewer heads per group zero-fills the rest.
+// Head split: NS score waves of HS heads (NTS 16-head tiles each); the value waves hold MT
+// 32-head M tiles (rows of heads beyond H stay zero).
+template <int H> struct MlaRoles;
+template <> struct MlaRoles<96> { static constexpr int NS = 2, HS = 48, NTS = 3, MT = 3; };
+template <> struct MlaRoles<16> { static constexpr int NS = 1, HS = 16, NTS = 1, MT = 1; };
+
+// O += P V with the accumulator pinned to AGPRs. The compiler does not see this instruction's
+// hazards: the operands must not be written by VALU within 4 wait states before it (here they
+// come straight from LDS reads), and VALU access to acc must wait for mfma_agpr_drain().
+__device__ __forceinline__ void mfma32_a(f32x16& acc, const u32x4& x, const u32x4& y) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+}
+
+// S^T += K Q^T step on v_mfma_f32_16x16x32_bf16 with the q fragment read from AGPRs (the VGPRs
+// stay free for prefetched K fragments). The first step of a tile takes 0 as the accumulator.
+// VALU reads of acc must follow qk_settle().
+__device__ __forceinline__ void mfma16_q0(f32x4& acc, const bf16x8& k, const bf16x8& q) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma16_q(f32x4& acc, const bf16x8& k, const bf16x8& q) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
+}
+// Wait states between the last 8-pass MFMA writing acc and VALU access to it. The accumulators
+// are operands of the same statement, so every MFMA that writes them comes before the padding and
+// every VALU access after it.
+__device__ __forceinline__ void qk_settle(f32x4 (&acc)[1]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc[0]));
+}
+__device__ __forceinline__ void qk_settle(f32x4 (&acc)[3]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
+}
+
+template <int H>
 __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
-  constexpr int NT = 2;        // 16-head tiles per wave
-  constexpr int HG = 16 * NT;  // heads per wave
-  __shared__ __attribute__((aligned(16))) uint8_t s_tiles[kMlaWaves][2][kTileBytes];
-  __shared__ float s_vec[kMlaWaves][32];
+  using R = MlaRoles<H>;
+  constexpr int NS = R::NS, HS = R::HS, NTS = R::NTS, MT = R::MT;
+  constexpr int NV = 2;                 // value waves, 256 latent dims each
+  constexpr int NW = NS + NV;
+  constexpr int CT = kVDim / 32 / NV;   // 32-wide latent tiles per value wave
+  constexpr int CPV = 18 / NV;          // copies per value wave per tile
+  constexpr int MA = MT < 2 ? MT : 2;   // M tiles accumulated in AGPRs (the rest in VGPRs)
+  static_assert(CPV * (kAhead - 1) <= 63, "vmcnt range");
+  static_assert(MT * 32 * kVDim * 2 <= kRing * kTileBytes, "epilogue staging fits in the ring");
 
-  const int wave = threadIdx.x / kWave;
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][MT][64 * 16];  // P in MFMA A layout
+  __shared__ int32_t s_idx[kMaxIdx + kTileKeys];
+  __shared__ float s_inv[MT * 32];
+  __shared__ int s_flag;
+
+  const int wave = threadIdx.x / kWave;  // the block has exactly NW waves
   const int lane = threadIdx.x % kWave;
-  const int n_hg = (a.H + HG - 1) / HG;
-  const int items = a.chunk_rows * n_hg;
-  const int item = kMlaWaves * xcd_local_block(blockIdx.x, gridDim.x) + wave;
-  if (item >= items) return;  // waves are independent: no workgroup barrier in this kernel
-
-  const int rr = a.chunk_rows - 1 - item / n_hg;  // longest rows first
-  const int hg = item % n_hg;
-  const int r = a.chunk_r0 + rr;                  // local row
-  const int t = a.row0 + r;
-  const int b = doc_begin(a.cu, a.n_docs, t);
-  const int keff = min(a.k, t - b + 1);
+  const int rr = a.chunk_rows - 1 - xcd_local_block(blockIdx.x, gridDim.x);  // longest rows first
+  const int r = a.chunk_r0 + rr;  // local row
+  const int t_row = a.row0 + r;
+  const int b = doc_begin(a.cu, a.n_docs, t_row);
+  const int keff = min(a.k, t_row - b + 1);
   const int ntiles = (keff + kTileKeys - 1) / kTileKeys;
-  const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
   const int T = a.T;
   const int g16 = lane >> 4, i16 = lane & 15;
+  const uint32_t ring = lds_addr_of(&s_ring[0][0]);
+  const uint32_t pbase = lds_addr_of(&s_p[0][0][0]);
+  constexpr uint32_t kPSlot = MT * 1024;
 
-  // q fragments: B operand of S^T = K Q^T. lane: head 16*nt + i16, dims 32*st + 8*g16 .. +8.
-  bf16x8 qf[NT][18];
-  const int hv = min(HG, a.H - hg * HG);  // valid heads in this group (32, or 16 for a 16-head layer)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const bool live = 16 * nt + i16 < hv;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(r) * a.H + hg * HG + (live ? 16 * nt + i16 : 0)) * kLatent + 8 * g16;
-#pragma unroll
-    for (int st = 0; st < 18; ++st) qf[nt][st] = live ? *reinterpret_cast<const bf16x8*>(qrow + 32 * st) : bf16x8{};
+  // The row's indices, checked once: entries outside [0, T) become -1 (masked). P starts at zero.
+  const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
+  for (int j = threadIdx.x; j < ntiles * kTileKeys; j += 64 * NW) {
+    const int v = j < keff ? ix[j] : -1;
+    s_idx[j] = (v >= 0 && v < T) ? v : -1;
   }
+  for (int j = threadIdx.x; j < 2 * MT * 256; j += 64 * NW) reinterpret_cast<uint32_t*>(&s_p[0][0][0])[j] = 0u;
+  if (threadIdx.x == 0) s_flag = 0;
+  __syncthreads();
 
-  DSA_LDS uint8_t* tiles = (DSA_LDS uint8_t*)(&s_tiles[wave][0][0]);
-  // gather: this lane always fills row slot i16 of column 4*i + g16
-  const int my_row = i16 ^ (4 * g16);
-  const uint8_t* kv_col = reinterpret_cast<const uint8_t*>(a.kv) + 16 * g16;
-  // QK operand: row i16, column 4*st + g16
-  const int qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;
-  // V operand (transposed reads): rows 8*hh + s4 (+4), column 4*ct + 2*chh + q4/2
-  const int hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
-  const int vc = 2 * chh + (q4 >> 1);
-  const int v_off1 = (vc * 16 + ((8 * hh + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1);
-  const int v_off2 = (vc * 16 + ((8 * hh + 4 + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1);
-
-  auto fetch_idx = [&](int tile) -> int {
-    const int j = tile * kTileKeys + lane;
-    return (lane < kTileKeys && tile < ntiles && j < keff) ? ix[j] : -1;
-  };
-  auto issue_tile = [&](int my_idx, int buf) {
-    const int src = (my_idx >= 0 && my_idx < T) ? my_idx : 0;
-    const uint8_t* g = kv_col + static_cast<int64_t>(__shfl(src, my_row)) * (kLatent * 2);
-    DSA_LDS uint8_t* dst = tiles + buf * kTileBytes;
+  if (wave < NS) {
+    // ================================ score wave ================================
+    const int sw = wave;
+    // q fragments, B operand of S^T = K Q^T. lane: head sw*HS + 16*nt + i16, dims 32*st + 8*g16.
+    bf16x8 qf[NTS][18];
 #pragma unroll
-    for (int i = 0; i < kRowGran / 4; ++i) copy16_to_lds(g + 64 * i, dst + 1024 * i);
-  };
-  auto valid_mask = [&](int my_idx) -> uint32_t {
-    return static_cast<uint32_t>(ballot(my_idx >= 0 && my_idx < T) & 0xffffull);
-  };
-
-  f32x16 O[16];
-  float m_ref[NT], l_part[NT];
+    for (int nt = 0; nt < NTS; ++nt) {
+      const uint16_t* qrow = a.q + (static_cast<int64_t>(r) * a.H + sw * HS + 16 * nt + i16) * kLatent + 8 * g16;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) m_ref[nt] = -INFINITY;
-
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct) O[ct] = f32x16{};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l_part[nt] = 0.0f;
-    int idx_cur = fetch_idx(0);
-    uint32_t vmask = valid_mask(idx_cur);
-    issue_tile(idx_cur, 0);
-    int idx_next = fetch_idx(1);
-    bool restart = false;
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int buf = tile & 1;
-      wait_vmem();  // this tile is in LDS and idx_next has arrived
-      const uint32_t vmask_next = valid_mask(idx_next);
-      if (tile + 1 < ntiles) issue_tile(idx_next, buf ^ 1);
-      const int idx_after = fetch_idx(tile + 2);
-      const DSA_LDS uint8_t* tb = tiles + buf * kTileBytes;
-
-      // ---- S^T = K Q^T : rows = 16 keys, cols = heads, K = 576 in 18 steps
-      f32x4 sacc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{};
-#pragma unroll
-      for (int st = 0; st < 18; ++st) {
-        const bf16x8 kf = lds_read16(tb + qk_off + 1024 * st);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt] = mfma16(kf, qf[nt][st], sacc[nt]);
-      }
-
-      // ---- softmax numerators (base 2). lane: head 16*nt + i16, keys 4*g16 + j.
-      float x[NT][4], tmax[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        tmax[nt] = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool valid = (vmask >> (4 * g16 + j)) & 1u;
-          x[nt][j] = valid ? sacc[nt][j] * a.scale_log2 : -INFINITY;
-          tmax[nt] = fmaxf(tmax[nt], x[nt][j]);
-        }
-        tmax[nt] = fmaxf(tmax[nt], __shfl_xor(tmax[nt], 16));
-        tmax[nt] = fmaxf(tmax[nt], __shfl_xor(tmax[nt], 32));
-      }
-      // The reference maximum is fixed once set; a logit more than 2^64 above it restarts the
-      // row with the larger reference (the accumulators are never rescaled in the loop).
-      bool risk = false, used = false;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        risk |= tmax[nt] > m_ref[nt] + kRestartGap;
-        used |= l_part[nt] > 0.0f;
-      }
-      if (ballot(risk) != 0ull) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
-        if (ballot(used) != 0ull && pass < kMaxRestarts) {
-          restart = true;
-          break;
-        }
-      }
-      uint32_t pk[NT][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[j] = (x[nt][j] == -INFINITY) ? 0.0f : exp2f(x[nt][j] - m_ref[nt]);
-          l_part[nt] += p[j];
-        }
-        pk[nt][0] = pack_bf16x2(p[0], p[1]);
-        pk[nt][1] = pack_bf16x2(p[2], p[3]);
-      }
-      // ---- P as the A operand (rows = 32 heads, K = 16 keys): even 16-lane rows take head
-      // block 0, odd rows block 1; the swap gathers keys 0..7 / 8..15 into one lane.
-      const uint32_t y0 = NT == 2 ? pk[NT - 1][0] : 0u;
-      const uint32_t y1 = NT == 2 ? pk[NT - 1][1] : 0u;
-      const auto sw0 = __builtin_amdgcn_permlane16_swap(pk[0][0], y0, false, false);
-      const auto sw1 = __builtin_amdgcn_permlane16_swap(pk[0][1], y1, false, false);
-      const u32x4 pa_u = {sw0[0], sw1[0], sw0[1], sw1[1]};
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, pa_u);
-
-      // ---- O += P V : N = 512 latent dims in 16 tiles of 32, V read transposed from LDS.
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct) {
-        const u32x2 v1 = lds_read_tr16(tb + v_off1 + 1024 * ct);
-        const u32x2 v2 = lds_read_tr16(tb + v_off2 + 1024 * ct);
-        const u32x4 vb_u = {v1[0], v1[1], v2[0], v2[1]};
-        O[ct] = mfma32(pa, __builtin_bit_cast(bf16x8, vb_u), O[ct]);
-      }
-      vmask = vmask_next;
-      idx_next = idx_after;
+      for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
     }
-    if (!restart) break;
-    wait_vmem();  // no copy may still target the tile buffers
-  }
+    // the fragments live in AGPRs (MFMA operands only); VALU writes them 4+ wait states ahead
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt)
+#pragma unroll
+      for (int st = 0; st < 18; ++st) asm volatile("" : "+a"(qf[nt][st]));
+    mfma_agpr_settle();
+    const int qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // row i16, column 4*st + g16
+    // This lane's numerators (head gh, keys 4*g16 .. +3) in the A operand of the value waves:
+    // M tile gh/32, lane 32*(g16/2) + gh%32, bytes 8*(g16&1) of that lane's 16.
+    uint32_t p_off[NTS];
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) {
+      const int gh = sw * HS + 16 * nt + i16;
+      p_off[nt] = pbase + ((gh >> 5) * 64 + 32 * (g16 >> 1) + (gh & 31)) * 16 + 8 * (g16 & 1);
+    }
+    float m_ref[NTS], l_part[NTS];
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
 
-  // ---- epilogue: 1/sum, lse, o_lat (bf16) through LDS for 16-byte stores
-  float* sv = s_vec[wave];
-  float l_tot[NT];
+    // One pass over the row; ntiles+1 barriers. mode 0: numerators, checking growth against the
+    // first usable tile's maxima; mode 1: exact maxima only; mode 2: numerators against them.
+    auto score_pass = [&](int mode) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float l = l_part[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    l_tot[nt] = l;
-  }
-  wave_lds_sync();
-  if (lane < 16) {
+      for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
+      for (int t = 0;; ++t) {
+        barrier_lds();  // tile t has landed; the P slot of tile t-2 has been consumed
+        if (t == ntiles) break;
+        // S^T of tile t: rows = 16 keys, cols = heads, K = 576 in 18 steps
+        const DSA_LDS uint8_t* tq = lds_ptr(ring + (t % kRing) * kTileBytes + qk_off);
+        // all 18 K fragments are requested up front, so that one LDS latency covers the tile
+        bf16x8 kf[18];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      sv[16 * nt + lane] = l_tot[nt] > 0.0f ? 1.0f / l_tot[nt] : 0.0f;
-      if (a.lse && 16 * nt + lane < hv) {
-        const float lse = l_tot[nt] > 0.0f ? (m_ref[nt] + log2f(l_tot[nt])) * 0.69314718055994531f : -INFINITY;
-        a.lse[static_cast<int64_t>(r) * a.H + hg * HG + 16 * nt + lane] = lse;
+        for (int st = 0; st < 18; ++st) kf[st] = lds_read16(tq + 1024 * st);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sacc[NTS];
+#pragma unroll
+        for (int st = 0; st < 18; ++st) {
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) {
+            if (st == 0) mfma16_q0(sacc[nt], kf[st], qf[nt][st]);
+            else mfma16_q(sacc[nt], kf[st], qf[nt][st]);
+          }
+        }
+        qk_settle(sacc);
+        const uint32_t vmask =
+            static_cast<uint32_t>(ballot(lane < kTileKeys && s_idx[t * kTileKeys + (lane & 15)] >= 0) & 0xffffull);
+        if (vmask != 0xffffu) {  // ragged tail or unusable indices
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (!((vmask >> (4 * g16 + j)) & 1u)) sacc[nt][j] = -INFINITY;
+        }
+        // per-head maxima in log2 units; lanes i16 + 16*g hold the same head
+        float tmax[NTS];
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) {
+          float m = fmaxf(fmaxf(sacc[nt][0], sacc[nt][1]), fmaxf(sacc[nt][2], sacc[nt][3]));
+          const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
+          const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
+        }
+        if (mode == 1) {
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
+          continue;
+        }
+        if (mode == 0) {
+          bool grow = false;
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) {
+            grow |= m_ref[nt] != -INFINITY && tmax[nt] > m_ref[nt] + kRestartGap;
+            if (m_ref[nt] == -INFINITY) m_ref[nt] = tmax[nt];  // the first usable tile sets it
+          }
+          if (ballot(grow) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
+        }
+        const uint32_t pslot = (t & 1) * kPSlot;
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) {
+          const float msub = fmaxf(m_ref[nt], -3.0e38f);  // finite even before the first usable key
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = fast_exp2(__builtin_fmaf(sacc[nt][j], a.scale_log2, -msub));  // -inf scores give 0
+            l_part[nt] += p[j];
+          }
+          const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + pslot)) = pk;
+        }
+      }
+    };
+    score_pass(0);
+    barrier_lds();  // (1) the value waves have consumed the last P; s_flag is final
+    if (s_flag) {
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
+      score_pass(1);
+      score_pass(2);
+    }
+    // 1/sum for the value waves, and lse
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) {
+      float l = l_part[nt];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+      const int gh = sw * HS + 16 * nt + i16;
+      if (lane < 16) {
+        s_inv[gh] = l > 0.0f ? 1.0f / l : 0.0f;
+        if (a.lse)
+          a.lse[static_cast<int64_t>(r) * a.H + gh] = l > 0.0f ? (m_ref[nt] + log2f(l)) * 0.69314718055994531f : -INFINITY;
       }
     }
-  }
-  wave_lds_sync();
-  f32x16 inv;
+    if (MT * 32 > H && lane < MT * 32 - H) s_inv[H + lane] = 0.0f;
+    barrier_lds();  // (2) s_inv is ready
+  } else {
+    // ================================ value wave ================================
+    const int vw = wave - NS;
+    // gather: this lane fills row slot i16 of column 4*i + g16, i.e. tile row my_row
+    const int my_row = i16 ^ (4 * g16);
+    const uint8_t* kv_col = reinterpret_cast<const uint8_t*>(a.kv) + 16 * g16;
+    auto issue_tile = [&](int t) {
+      const int src = max(s_idx[t * kTileKeys + my_row], 0);
+      const uint8_t* g = kv_col + static_cast<int64_t>(src) * (kLatent * 2);
+      const uint32_t dst = ring + (t % kRing) * kTileBytes;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) inv[e] = sv[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)];
-  // stage [HG heads][512] bf16 in this wave's tile buffers (no copy is in flight now)
-  uint16_t* so = reinterpret_cast<uint16_t*>(&s_tiles[wave][0][0]);
+      for (int c = 0; c < CPV; ++c) {
+        const int i = vw + NV * c;  // this wave's copies of the tile's 18
+        copy16_to_lds(g + 64 * i, lds_ptr(dst + 1024 * i));
+      }
+    };
+    // Waits until this wave's copies of tile t have landed; later tiles stay in flight.
+    auto wait_tile = [&](int t) {
+      const int later = min(kAhead - 1, ntiles - 1 - t);
+      if (later >= 3) wait_vmem_le<3 * CPV>();
+      else if (later == 2) wait_vmem_le<2 * CPV>();
+      else if (later == 1) wait_vmem_le<CPV>();
+      else wait_vmem_le<0>();
+    };
+    // V operand (transposed reads): keys 8*hh + s4 (+4), latent granule 4*(CT*vw + ct) + vc
+    const int hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
+    const int vc = 2 * chh + (q4 >> 1);
+    const uint32_t v_off1 = (vc * 16 + ((8 * hh + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1) + 1024 * CT * vw;
+    const uint32_t v_off2 = (vc * 16 + ((8 * hh + 4 + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1) + 1024 * CT * vw;
+    const uint32_t p_rd = pbase + lane * 16;
+
+    f32x16 O[MT][CT];
+    // Ties the accumulators to this program point, so that no access to them moves across the
+    // wait-state padding placed next to it.
+    auto pin_acc = [&]() {
 #pragma unroll
-  for (int ct = 0; ct < 16; ++ct) {
-    const f32x16 ov = O[ct] * inv;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int head = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      so[head * kVDim + 32 * ct + (lane & 31)] = f32_to_bf16(ov[e]);
+        for (int ct = 0; ct < CT; ++ct) {
+          if (mt < MA) asm volatile("" : "+a"(O[mt][ct]));
+          else asm volatile("" : "+v"(O[mt][ct]));
+        }
+    };
+    // One pass over the row; ntiles+1 barriers. mode 1 copies tiles only (the scores redo their
+    // maxima); modes 0 and 2 accumulate P V.
+    auto value_pass = [&](int mode) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) O[mt][ct] = f32x16{};
+      pin_acc();
+      mfma_agpr_settle();
+#pragma unroll
+      for (int p = 0; p < kAhead; ++p)
+        if (p < ntiles) issue_tile(p);
+      for (int t = 0;; ++t) {
+        if (t < ntiles) wait_tile(t);
+        barrier_lds();  // every copy of tile t has landed; P of tile t-1 is complete
+        if (t + kAhead < ntiles) issue_tile(t + kAhead);  // into the slot of tile t-2
+        if (t > 0 && mode != 1) {
+          const int tv = t - 1;
+          const uint32_t tb = ring + (tv % kRing) * kTileBytes;
+          const uint32_t pp = p_rd + (tv & 1) * kPSlot;
+          u32x4 pa[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) pa[mt] = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(pp + mt * 1024));
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const u32x2 v1 = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * ct));
+            const u32x2 v2 = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * ct));
+            const u32x4 vb = {v1[0], v1[1], v2[0], v2[1]};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              if (mt < MA) mfma32_a(O[mt][ct], pa[mt], vb);
+              else
+                O[mt][ct] = mfma32(__builtin_bit_cast(bf16x8, pa[mt]), __builtin_bit_cast(bf16x8, vb), O[mt][ct]);
+            }
+          }
+        }
+        if (t == ntiles) break;
+      }
+    };
+    value_pass(0);
+    barrier_lds();  // (1)
+    if (s_flag) {
+      value_pass(1);
+      value_pass(2);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  wave_lds_sync();
-  uint16_t* dst = a.o_lat + (static_cast<int64_t>(rr) * a.H + hg * HG) * kVDim;
+    mfma_agpr_drain();  // the accumulators are read by VALU below
+    pin_acc();
+    barrier_lds();      // (2) s_inv is ready; the score waves are done with the ring
+    // normalise, stage [heads][this wave's 256 dims] as bf16 in the ring, then 16-byte stores
+    uint16_t* so = reinterpret_cast<uint16_t*>(&s_ring[0][0]);
 #pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    if (h < hv) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(so + h * kVDim + 8 * lane);
-      *reinterpret_cast<u32x4*>(dst + h * kVDim + 8 * lane) = v;
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 inv;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) inv[e] = s_inv[32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3)];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const f32x16 ov = O[mt][ct] * inv;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int head = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          so[head * kVDim + 32 * (CT * vw + ct) + (lane & 31)] = f32_to_bf16(ov[e]);
+        }
+      }
+    }
+    wave_lds_sync();
+    uint16_t* dst = a.o_lat + static_cast<int64_t>(rr) * H * kVDim;
+    const int c0 = 256 * vw + 8 * (lane & 31);  // 32 lanes cover this wave's 256 dims
+    for (int h = hh; h < H; h += 2) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(so + h * kVDim + c0);
+      *reinterpret_cast<u32x4*>(dst + h * kVDim + c0) = v;
     }
   }
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
-  const int items = a.chunk_rows * ((a.H + 31) / 32);
-  dim3 grid((items + kMlaWaves - 1) / kMlaWaves), block(kMlaWaves * kWave);
-  hipLaunchKernelGGL(k_sparse_mla, grid, block, 0, st, a);
+  if (a.k > kMaxIdx) return hipErrorInvalidValue;
+  const dim3 grid(a.chunk_rows);
+  if (a.H == 96) hipLaunchKernelGGL((k_sparse_mla<96>), grid, dim3(64 * (MlaRoles<96>::NS + 2)), 0, st, a);
+  else if (a.H == 16) hipLaunchKernelGGL((k_sparse_mla<16>), grid, dim3(64 * (MlaRoles<16>::NS + 2)), 0, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
