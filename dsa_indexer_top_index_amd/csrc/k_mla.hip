@@ -53,7 +53,7 @@ template <int H> struct MlaRoles;
 template <> struct MlaRoles<96> { static constexpr int NS = 2, HS = 48, NTS = 3, MT = 3; };
 template <> struct MlaRoles<16> { static constexpr int NS = 1, HS = 16, NTS = 1, MT = 1; };
 
-// O += P V with the accumulator pinned to AGPRs. The compiler does not see this instruction's
+// O^T += V^T P^T with the accumulator pinned to AGPRs. The compiler does not see this instruction's
 // hazards: the operands must not be written by VALU within 4 wait states before it (here they
 // come straight from LDS reads), and VALU access to acc must wait for mfma_agpr_drain().
 __device__ __forceinline__ void mfma32_a(f32x16& acc, const u32x4& x, const u32x4& y) {
@@ -89,7 +89,6 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
   constexpr int CPV = 18 / NV;          // copies per value wave per tile
   constexpr int MA = MT < 2 ? MT : 2;   // M tiles accumulated in AGPRs (the rest in VGPRs)
   static_assert(CPV * (kAhead - 1) <= 63, "vmcnt range");
-  static_assert(MT * 32 * kVDim * 2 <= kRing * kTileBytes, "epilogue staging fits in the ring");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[2][MT][64 * 16];  // P in MFMA A layout
@@ -99,7 +98,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
 
   const int wave = threadIdx.x / kWave;  // the block has exactly NW waves
   const int lane = threadIdx.x % kWave;
-  const int rr = a.chunk_rows - 1 - xcd_local_block(blockIdx.x, gridDim.x);  // longest rows first
+  // Rows longest first, in dispatch order: consecutive blocks go to different XCDs, so every XCD
+  // receives the same mix of long and short rows.
+  const int rr = a.chunk_rows - 1 - static_cast<int>(blockIdx.x);
   const int r = a.chunk_r0 + rr;  // local row
   const int t_row = a.row0 + r;
   const int b = doc_begin(a.cu, a.n_docs, t_row);
@@ -112,10 +113,19 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
   constexpr uint32_t kPSlot = MT * 1024;
 
   // The row's indices, checked once: entries outside [0, T) become -1 (masked). P starts at zero.
+  // All loads are issued before the first store, so the row's index list arrives in one latency.
   const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
-  for (int j = threadIdx.x; j < ntiles * kTileKeys; j += 64 * NW) {
-    const int v = j < keff ? ix[j] : -1;
-    s_idx[j] = (v >= 0 && v < T) ? v : -1;
+  constexpr int kPer = (kMaxIdx + 64 * NW - 1) / (64 * NW);
+  int iv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = threadIdx.x + 64 * NW * i;
+    iv[i] = j < keff ? ix[j] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = threadIdx.x + 64 * NW * i;
+    if (j < ntiles * kTileKeys) s_idx[j] = (iv[i] >= 0 && iv[i] < T) ? iv[i] : -1;
   }
   for (int j = threadIdx.x; j < 2 * MT * 256; j += 64 * NW) reinterpret_cast<uint32_t*>(&s_p[0][0][0])[j] = 0u;
   if (threadIdx.x == 0) s_flag = 0;
@@ -320,9 +330,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
             const u32x4 vb = {v1[0], v1[1], v2[0], v2[1]};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-              if (mt < MA) mfma32_a(O[mt][ct], pa[mt], vb);
+              // A = V^T (lane: latent dim, 8 keys), B = P^T (lane: head, 8 keys), D = O^T
+              if (mt < MA) mfma32_a(O[mt][ct], vb, pa[mt]);
               else
-                O[mt][ct] = mfma32(__builtin_bit_cast(bf16x8, pa[mt]), __builtin_bit_cast(bf16x8, vb), O[mt][ct]);
+                O[mt][ct] = mfma32(__builtin_bit_cast(bf16x8, vb), __builtin_bit_cast(bf16x8, pa[mt]), O[mt][ct]);
             }
           }
         }
@@ -338,20 +349,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     mfma_agpr_drain();  // the accumulators are read by VALU below
     pin_acc();
     barrier_lds();      // (2) s_inv is ready; the score waves are done with the ring
-    // normalise, stage [heads][this wave's 256 dims] as bf16 in the ring, then 16-byte stores
-    uint16_t* so = reinterpret_cast<uint16_t*>(&s_ring[0][0]);
+    // Normalise and stage [heads][512 dims] as bf16 in the ring (rows padded by 16 bytes against
+    // bank conflicts), then 16-byte stores. O^T tile (mt, ct), lane: head 32*mt + lane%32,
+    // element e: latent dim 32*(CT*vw + ct) + 8*(e/4) + 4*hh + e%4.
+    constexpr uint32_t kStageRow = kVDim * 2 + 16;
+    static_assert(MT * 32 * kStageRow <= kRing * kTileBytes, "staging fits in the ring");
+    const uint32_t stage = ring + (lane & 31) * kStageRow + 2 * (32 * CT * vw + 4 * hh);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x16 inv;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) inv[e] = s_inv[32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3)];
+      const float inv = s_inv[32 * mt + (lane & 31)];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const f32x16 ov = O[mt][ct] * inv;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int head = 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          so[head * kVDim + 32 * (CT * vw + ct) + (lane & 31)] = f32_to_bf16(ov[e]);
+        for (int j = 0; j < 4; ++j) {
+          const u32x2 pk = {pack_bf16x2(ov[4 * j], ov[4 * j + 1]), pack_bf16x2(ov[4 * j + 2], ov[4 * j + 3])};
+          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(stage + mt * 32 * kStageRow + 2 * (32 * ct + 8 * j))) = pk;
         }
       }
     }
@@ -359,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     uint16_t* dst = a.o_lat + static_cast<int64_t>(rr) * H * kVDim;
     const int c0 = 256 * vw + 8 * (lane & 31);  // 32 lanes cover this wave's 256 dims
     for (int h = hh; h < H; h += 2) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(so + h * kVDim + c0);
+      const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(ring + h * kStageRow + 2 * c0));
       *reinterpret_cast<u32x4*>(dst + h * kVDim + c0) = v;
     }
   }
