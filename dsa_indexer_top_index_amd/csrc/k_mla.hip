@@ -33,13 +33,15 @@
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
+#include <type_traits>
+
 namespace dsa {
 
 constexpr int kTileKeys = 16;
 constexpr int kRowGran = kLatent * 2 / 16;            // 72 granules (16 B) per latent row
 constexpr int kTileBytes = kTileKeys * kRowGran * 16;  // 18432: 18 wave copies of 1 KB
-constexpr int kRing = 6;                               // tiles in the shared LDS ring
-constexpr int kAhead = kRing - 2;                      // tiles whose copies run ahead of the scores
+constexpr int kRing = 7;                               // tiles in the shared LDS ring
+constexpr int kAhead = kRing - 3;                      // tiles whose copies run ahead of the scores
 constexpr float kRestartGap = 64.0f;                   // log2 headroom of a head's reference maximum
 constexpr int kMaxIdx = 2048;
 
@@ -58,25 +60,6 @@ template <> struct MlaRoles<16> { static constexpr int NS = 1, HS = 16, NTS = 1,
 // come straight from LDS reads), and VALU access to acc must wait for mfma_agpr_drain().
 __device__ __forceinline__ void mfma32_a(f32x16& acc, const u32x4& x, const u32x4& y) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
-}
-
-// S^T += K Q^T step on v_mfma_f32_16x16x32_bf16 with the q fragment read from AGPRs (the VGPRs
-// stay free for prefetched K fragments). The first step of a tile takes 0 as the accumulator.
-// VALU reads of acc must follow qk_settle().
-__device__ __forceinline__ void mfma16_q0(f32x4& acc, const bf16x8& k, const bf16x8& q) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(k), "a"(q));
-}
-__device__ __forceinline__ void mfma16_q(f32x4& acc, const bf16x8& k, const bf16x8& q) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(k), "a"(q));
-}
-// Wait states between the last 8-pass MFMA writing acc and VALU access to it. The accumulators
-// are operands of the same statement, so every MFMA that writes them comes before the padding and
-// every VALU access after it.
-__device__ __forceinline__ void qk_settle(f32x4 (&acc)[1]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc[0]));
-}
-__device__ __forceinline__ void qk_settle(f32x4 (&acc)[3]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
 }
 
 template <int H>
@@ -142,14 +125,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
 #pragma unroll
       for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
     }
-    // the fragments live in AGPRs (MFMA operands only); VALU writes them 4+ wait states ahead
+    // the fragments live in AGPRs, which the MFMAs read directly; the VGPRs hold K fragments
 #pragma unroll
     for (int nt = 0; nt < NTS; ++nt)
 #pragma unroll
       for (int st = 0; st < 18; ++st) asm volatile("" : "+a"(qf[nt][st]));
     mfma_agpr_settle();
-    const int qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // row i16, column 4*st + g16
-    // This lane's numerators (head gh, keys 4*g16 .. +3) in the A operand of the value waves:
+    const uint32_t qk_base = ring + (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // row i16, column 4*st + g16
+    // This lane's numerators (head gh, keys 4*g16 .. +3) in the B operand of the value waves:
     // M tile gh/32, lane 32*(g16/2) + gh%32, bytes 8*(g16&1) of that lane's 16.
     uint32_t p_off[NTS];
 #pragma unroll
@@ -160,87 +143,162 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     float m_ref[NTS], l_part[NTS];
 #pragma unroll
     for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
+    bool grow = false;
 
-    // One pass over the row; ntiles+1 barriers. mode 0: numerators, checking growth against the
-    // first usable tile's maxima; mode 1: exact maxima only; mode 2: numerators against them.
-    auto score_pass = [&](int mode) {
+    // K fragments of tile t (row i16, dims 32*st + 8*g16), all requested at once
+    auto load_k = [&](int t, bf16x8 (&kf)[18]) {
+      const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
 #pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
-      for (int t = 0;; ++t) {
-        barrier_lds();  // tile t has landed; the P slot of tile t-2 has been consumed
-        if (t == ntiles) break;
-        // S^T of tile t: rows = 16 keys, cols = heads, K = 576 in 18 steps
-        const DSA_LDS uint8_t* tq = lds_ptr(ring + (t % kRing) * kTileBytes + qk_off);
-        // all 18 K fragments are requested up front, so that one LDS latency covers the tile
-        bf16x8 kf[18];
+      for (int st = 0; st < 18; ++st) kf[st] = lds_read16(tq + 1024 * st);
+    };
+    // S^T of one tile: rows = 16 keys, cols = heads, K = 576 in 18 steps
+    auto qk = [&](const bf16x8 (&kf)[18], f32x4 (&sc)[NTS]) {
 #pragma unroll
-        for (int st = 0; st < 18; ++st) kf[st] = lds_read16(tq + 1024 * st);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 sacc[NTS];
+      for (int st = 0; st < 18; ++st)
 #pragma unroll
-        for (int st = 0; st < 18; ++st) {
+        for (int nt = 0; nt < NTS; ++nt) sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
+    };
+    // Key-validity bits of a tile (bit j: key j has a usable index), from the index lanes 0..15 hold.
+    auto valid_bits = [&](int idx_val) -> uint32_t {
+      return static_cast<uint32_t>(ballot(idx_val >= 0) & 0xffffull);
+    };
+    // Masked scores -> per-head maxima in log2 units (lanes i16 + 16*g hold the same head).
+    auto mask_max = [&](f32x4 (&sc)[NTS], uint32_t vm, float (&tmax)[NTS]) {
+      const uint32_t bits = vm >> (4 * g16);
 #pragma unroll
-          for (int nt = 0; nt < NTS; ++nt) {
-            if (st == 0) mfma16_q0(sacc[nt], kf[st], qf[nt][st]);
-            else mfma16_q(sacc[nt], kf[st], qf[nt][st]);
+      for (int nt = 0; nt < NTS; ++nt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[nt][j] = ((bits >> j) & 1u) ? sc[nt][j] : -INFINITY;
+        float m = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
+        const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
+        const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
+      }
+    };
+    // Softmax numerators of one tile into P slot `slot`, in six steps per 16-head tile so that
+    // they can be spread between the MFMAs of the next tile. CHECK: the reference maxima come
+    // from the first usable tile and growth beyond them is recorded; otherwise m_ref holds the
+    // exact maxima.
+    struct SoftmaxState {
+      float m, tmax, msub, p[4];
+    };
+    auto softmax_step = [&](int step, int nt, f32x4 (&sc)[NTS], uint32_t vm, uint32_t slot, SoftmaxState& st,
+                            auto check_c) {
+      switch (step) {
+        case 0: {  // mask, then the maximum over this lane's 4 keys
+          const uint32_t bits = vm >> (4 * g16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[nt][j] = ((bits >> j) & 1u) ? sc[nt][j] : -INFINITY;
+          st.m = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
+          break;
+        }
+        case 1: {  // across the four 16-lane rows holding the same head (compare-select: no NaNs here)
+          const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);
+          const float u = __uint_as_float(m16[0]), v = __uint_as_float(m16[1]);
+          st.m = u > v ? u : v;
+          break;
+        }
+        case 2: {
+          const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);
+          const float u = __uint_as_float(m32[0]), v = __uint_as_float(m32[1]);
+          st.tmax = (u > v ? u : v) * a.scale_log2;
+          break;
+        }
+        case 3: {
+          if constexpr (decltype(check_c)::value) {
+            grow |= m_ref[nt] != -INFINITY && st.tmax > m_ref[nt] + kRestartGap;
+            m_ref[nt] = m_ref[nt] == -INFINITY ? st.tmax : m_ref[nt];
           }
+          st.msub = fmaxf(m_ref[nt], -3.0e38f);  // finite even before the first usable key
+          break;
         }
-        qk_settle(sacc);
-        const uint32_t vmask =
-            static_cast<uint32_t>(ballot(lane < kTileKeys && s_idx[t * kTileKeys + (lane & 15)] >= 0) & 0xffffull);
-        if (vmask != 0xffffu) {  // ragged tail or unusable indices
+        case 4: {
 #pragma unroll
-          for (int nt = 0; nt < NTS; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (!((vmask >> (4 * g16 + j)) & 1u)) sacc[nt][j] = -INFINITY;
+          for (int j = 0; j < 4; ++j) st.p[j] = fast_exp2(__builtin_fmaf(sc[nt][j], a.scale_log2, -st.msub));
+          break;
         }
-        // per-head maxima in log2 units; lanes i16 + 16*g hold the same head
-        float tmax[NTS];
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) {
-          float m = fmaxf(fmaxf(sacc[nt][0], sacc[nt][1]), fmaxf(sacc[nt][2], sacc[nt][3]));
-          const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          m = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
-          const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
-        }
-        if (mode == 1) {
-#pragma unroll
-          for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
-          continue;
-        }
-        if (mode == 0) {
-          bool grow = false;
-#pragma unroll
-          for (int nt = 0; nt < NTS; ++nt) {
-            grow |= m_ref[nt] != -INFINITY && tmax[nt] > m_ref[nt] + kRestartGap;
-            if (m_ref[nt] == -INFINITY) m_ref[nt] = tmax[nt];  // the first usable tile sets it
-          }
-          if (ballot(grow) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
-        }
-        const uint32_t pslot = (t & 1) * kPSlot;
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) {
-          const float msub = fmaxf(m_ref[nt], -3.0e38f);  // finite even before the first usable key
-          float p[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(sacc[nt][j], a.scale_log2, -msub));  // -inf scores give 0
-            l_part[nt] += p[j];
-          }
-          const u32x2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + pslot)) = pk;
+        default: {
+          l_part[nt] += (st.p[0] + st.p[1]) + (st.p[2] + st.p[3]);
+          const u32x2 pk = {pack_bf16x2(st.p[0], st.p[1]), pack_bf16x2(st.p[2], st.p[3])};
+          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + slot)) = pk;
+          break;
         }
       }
     };
-    score_pass(0);
-    barrier_lds();  // (1) the value waves have consumed the last P; s_flag is final
+    auto numerators = [&](f32x4 (&sc)[NTS], uint32_t vm, uint32_t slot, auto check_c) {
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) {
+        SoftmaxState st;
+#pragma unroll
+        for (int step = 0; step < 6; ++step) softmax_step(step, nt, sc, vm, slot, st, check_c);
+      }
+    };
+    // One pass writing numerators; ntiles+2 barriers. The MFMAs of tile t are issued in 18 groups
+    // with one softmax step of tile t-1 after each, so the VALU work runs under the matrix
+    // instructions; the value waves consume that P one tile later.
+    auto numerator_pass = [&](auto check_c) {
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
+      f32x4 sprev[NTS];
+      uint32_t vprev;
+      {
+        barrier_lds();  // tile 0 has landed
+        bf16x8 kf[18];
+        load_k(0, kf);
+        const int iv0 = s_idx[lane & 15];
+        qk(kf, sprev);
+        vprev = valid_bits(iv0);
+      }
+      for (int t = 1; t < ntiles; ++t) {
+        barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
+        bf16x8 kf[18];
+        load_k(t, kf);
+        const int ivt = s_idx[t * kTileKeys + (lane & 15)];
+        const uint32_t slot = ((t - 1) & 1) * kPSlot;
+        f32x4 sc[NTS];
+        SoftmaxState sst;
+#pragma unroll
+        for (int st = 0; st < 18; ++st) {
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (st < 6 * NTS) softmax_step(st % 6, st / 6, sprev, vprev, slot, sst, check_c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        vprev = valid_bits(ivt);
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) sprev[nt] = sc[nt];
+      }
+      barrier_lds();  // B_ntiles
+      numerators(sprev, vprev, ((ntiles - 1) & 1) * kPSlot, check_c);
+      barrier_lds();  // B_ntiles+1
+    };
+    // Exact per-head maxima (QK only); ntiles+2 barriers.
+    auto max_pass = [&]() {
+      for (int t = 0;; ++t) {
+        barrier_lds();
+        if (t == ntiles + 1) break;
+        if (t == ntiles) continue;
+        bf16x8 kf[18];
+        load_k(t, kf);
+        const int ivt = s_idx[t * kTileKeys + (lane & 15)];
+        f32x4 sc[NTS];
+        qk(kf, sc);
+        float tmax[NTS];
+        mask_max(sc, valid_bits(ivt), tmax);
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
+      }
+    };
+    numerator_pass(std::true_type{});
+    if (ballot(grow) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
+    barrier_lds();  // (1) s_flag is final
     if (s_flag) {
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
-      score_pass(1);
-      score_pass(2);
+      max_pass();
+      numerator_pass(std::false_type{});
     }
     // 1/sum for the value waves, and lse
 #pragma unroll
@@ -300,8 +358,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
           else asm volatile("" : "+v"(O[mt][ct]));
         }
     };
-    // One pass over the row; ntiles+1 barriers. mode 1 copies tiles only (the scores redo their
-    // maxima); modes 0 and 2 accumulate P V.
+    // One pass over the row; ntiles+2 barriers. mode 1 copies tiles only (the scores redo their
+    // maxima); modes 0 and 2 accumulate P V, two tiles behind the scores.
     auto value_pass = [&](int mode) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -314,10 +372,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         if (p < ntiles) issue_tile(p);
       for (int t = 0;; ++t) {
         if (t < ntiles) wait_tile(t);
-        barrier_lds();  // every copy of tile t has landed; P of tile t-1 is complete
-        if (t + kAhead < ntiles) issue_tile(t + kAhead);  // into the slot of tile t-2
-        if (t > 0 && mode != 1) {
-          const int tv = t - 1;
+        barrier_lds();  // every copy of tile t has landed; P of tile t-2 is complete
+        if (t + kAhead < ntiles) issue_tile(t + kAhead);  // into the slot of tile t-3
+        if (t > 1 && mode != 1) {
+          const int tv = t - 2;
           const uint32_t tb = ring + (tv % kRing) * kTileBytes;
           const uint32_t pp = p_rd + (tv & 1) * kPSlot;
           u32x4 pa[MT];
@@ -337,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
             }
           }
         }
-        if (t == ntiles) break;
+        if (t == ntiles + 1) break;
       }
     };
     value_pass(0);
