@@ -105,14 +105,17 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     const int j = threadIdx.x + 64 * NW * i;
     iv[i] = j < keff ? ix[j] : -1;
   }
+  bool bad = false;  // an unusable index before the last tile
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = threadIdx.x + 64 * NW * i;
-    if (j < ntiles * kTileKeys) s_idx[j] = (iv[i] >= 0 && iv[i] < T) ? iv[i] : -1;
+    const bool ok = iv[i] >= 0 && iv[i] < T;
+    if (j < ntiles * kTileKeys) s_idx[j] = ok ? iv[i] : -1;
+    bad |= !ok && j < (ntiles - 1) * kTileKeys;
   }
   for (int j = threadIdx.x; j < 2 * MT * 256; j += 64 * NW) reinterpret_cast<uint32_t*>(&s_p[0][0][0])[j] = 0u;
   if (threadIdx.x == 0) s_flag = 0;
-  __syncthreads();
+  const bool any_bad = __syncthreads_or(bad);
 
   if (wave < NS) {
     // ================================ score wave ================================
@@ -143,7 +146,6 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     float m_ref[NTS], l_part[NTS];
 #pragma unroll
     for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
-    bool grow = false;
 
     // K fragments of tile t (row i16, dims 32*st + 8*g16), all requested at once
     auto load_k = [&](int t, bf16x8 (&kf)[18]) {
@@ -176,68 +178,46 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
       }
     };
-    // Softmax numerators of one tile into P slot `slot`, in six steps per 16-head tile so that
-    // they can be spread between the MFMAs of the next tile. CHECK: the reference maxima come
-    // from the first usable tile and growth beyond them is recorded; otherwise m_ref holds the
-    // exact maxima.
-    struct SoftmaxState {
-      float m, tmax, msub, p[4];
+    // Softmax numerators: x = scale*s - m_ref (log2 units), p = 2^x; masked keys get x = -inf
+    // and p = 0. gx keeps the largest x of the pass: while the references are the first tile's
+    // maxima, a value above kRestartGap means that the row has to be redone with exact maxima.
+    float msub[NTS], gx = -INFINITY;
+    struct Soft {
+      float x[4], p[4];
     };
-    auto softmax_step = [&](int step, int nt, f32x4 (&sc)[NTS], uint32_t vm, uint32_t slot, SoftmaxState& st,
-                            auto check_c) {
-      switch (step) {
-        case 0: {  // mask, then the maximum over this lane's 4 keys
-          const uint32_t bits = vm >> (4 * g16);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sc[nt][j] = ((bits >> j) & 1u) ? sc[nt][j] : -INFINITY;
-          st.m = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
-          break;
-        }
-        case 1: {  // across the four 16-lane rows holding the same head (compare-select: no NaNs here)
-          const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);
-          const float u = __uint_as_float(m16[0]), v = __uint_as_float(m16[1]);
-          st.m = u > v ? u : v;
-          break;
-        }
-        case 2: {
-          const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.m), __float_as_uint(st.m), false, false);
-          const float u = __uint_as_float(m32[0]), v = __uint_as_float(m32[1]);
-          st.tmax = (u > v ? u : v) * a.scale_log2;
-          break;
-        }
-        case 3: {
-          if constexpr (decltype(check_c)::value) {
-            grow |= m_ref[nt] != -INFINITY && st.tmax > m_ref[nt] + kRestartGap;
-            m_ref[nt] = m_ref[nt] == -INFINITY ? st.tmax : m_ref[nt];
-          }
-          st.msub = fmaxf(m_ref[nt], -3.0e38f);  // finite even before the first usable key
-          break;
-        }
-        case 4: {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) st.p[j] = fast_exp2(__builtin_fmaf(sc[nt][j], a.scale_log2, -st.msub));
-          break;
-        }
-        default: {
-          l_part[nt] += (st.p[0] + st.p[1]) + (st.p[2] + st.p[3]);
-          const u32x2 pk = {pack_bf16x2(st.p[0], st.p[1]), pack_bf16x2(st.p[2], st.p[3])};
-          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + slot)) = pk;
-          break;
-        }
+    // Micro-step k of a tile's softmax (12 per 16-head tile, a few VALU instructions each), so
+    // that the steps fit between the MFMAs of the next tile. ok[j]: key 4*g16 + j is usable.
+    auto micro = [&](int k, const f32x4 (&sc)[NTS], const bool (&ok)[4], uint32_t slot, Soft (&sf)[NTS],
+                     auto masked_c) {
+      const int nt = k / 12, s = k % 12;
+      Soft& f = sf[nt];
+      if (s < 4) {
+        f.x[s] = __builtin_fmaf(sc[nt][s], a.scale_log2, -msub[nt]);
+        if constexpr (decltype(masked_c)::value) f.x[s] = ok[s] ? f.x[s] : -INFINITY;
+      } else if (s < 8) {
+        f.p[s - 4] = fast_exp2(f.x[s - 4]);  // -inf gives 0
+      } else if (s == 8) {
+        gx = fmaxf(gx, fmaxf(fmaxf(f.x[0], f.x[1]), fmaxf(f.x[2], f.x[3])));
+      } else if (s == 9) {
+        l_part[nt] += f.p[0] + f.p[1];
+      } else if (s == 10) {
+        l_part[nt] += f.p[2] + f.p[3];
+      } else {
+        const u32x2 pk = {pack_bf16x2(f.p[0], f.p[1]), pack_bf16x2(f.p[2], f.p[3])};
+        *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + slot)) = pk;
       }
     };
-    auto numerators = [&](f32x4 (&sc)[NTS], uint32_t vm, uint32_t slot, auto check_c) {
+    auto key_ok = [&](uint32_t vm, bool (&ok)[4]) {
+      const uint32_t bits = vm >> (4 * g16);
 #pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) {
-        SoftmaxState st;
-#pragma unroll
-        for (int step = 0; step < 6; ++step) softmax_step(step, nt, sc, vm, slot, st, check_c);
-      }
+      for (int j = 0; j < 4; ++j) ok[j] = (bits >> j) & 1u;
     };
-    // One pass writing numerators; ntiles+2 barriers. The MFMAs of tile t are issued in 18 groups
-    // with one softmax step of tile t-1 after each, so the VALU work runs under the matrix
-    // instructions; the value waves consume that P one tile later.
-    auto numerator_pass = [&](auto check_c) {
+    // One pass writing numerators; ntiles+2 barriers. CHECK: the first tile's maxima become the
+    // references and gx records growth beyond them; otherwise m_ref holds exact maxima. MASKED:
+    // some full tile holds unusable indices (the last tile is always masked). The MFMAs of tile t
+    // are interleaved with the micro-steps of tile t-1, so the VALU work runs while the matrix
+    // core is busy; the value waves consume that P one tile later.
+    auto numerator_pass = [&](auto check_c, auto masked_c) {
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
       f32x4 sprev[NTS];
@@ -249,6 +229,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         const int iv0 = s_idx[lane & 15];
         qk(kf, sprev);
         vprev = valid_bits(iv0);
+        if constexpr (decltype(check_c)::value) {
+          float tmax[NTS];
+          mask_max(sprev, vprev, tmax);
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = tmax[nt];
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) msub[nt] = fmaxf(m_ref[nt], -3.0e38f);  // finite without usable keys
       }
       for (int t = 1; t < ntiles; ++t) {
         barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
@@ -256,14 +244,18 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         load_k(t, kf);
         const int ivt = s_idx[t * kTileKeys + (lane & 15)];
         const uint32_t slot = ((t - 1) & 1) * kPSlot;
+        bool ok[4];
+        key_ok(vprev, ok);
+        Soft sf[NTS];
         f32x4 sc[NTS];
-        SoftmaxState sst;
 #pragma unroll
-        for (int st = 0; st < 18; ++st) {
-#pragma unroll
-          for (int nt = 0; nt < NTS; ++nt) sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
+        for (int i = 0; i < 18 * NTS; ++i) {
+          const int st = i / NTS, nt = i % NTS;
+          sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
           __builtin_amdgcn_sched_barrier(0);
-          if (st < 6 * NTS) softmax_step(st % 6, st / 6, sprev, vprev, slot, sst, check_c);
+#pragma unroll
+          for (int k = 0; k < 12 * NTS; ++k)
+            if (k * 3 / 2 == i) micro(k, sprev, ok, slot, sf, masked_c);
           __builtin_amdgcn_sched_barrier(0);
         }
         vprev = valid_bits(ivt);
@@ -271,7 +263,13 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         for (int nt = 0; nt < NTS; ++nt) sprev[nt] = sc[nt];
       }
       barrier_lds();  // B_ntiles
-      numerators(sprev, vprev, ((ntiles - 1) & 1) * kPSlot, check_c);
+      {
+        bool ok[4];
+        key_ok(vprev, ok);
+        Soft sf[NTS];
+#pragma unroll
+        for (int k = 0; k < 12 * NTS; ++k) micro(k, sprev, ok, ((ntiles - 1) & 1) * kPSlot, sf, std::true_type{});
+      }
       barrier_lds();  // B_ntiles+1
     };
     // Exact per-head maxima (QK only); ntiles+2 barriers.
@@ -291,14 +289,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
       }
     };
-    numerator_pass(std::true_type{});
-    if (ballot(grow) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
+    if (any_bad) numerator_pass(std::true_type{}, std::true_type{});
+    else numerator_pass(std::true_type{}, std::false_type{});
+    if (ballot(gx > kRestartGap) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
     barrier_lds();  // (1) s_flag is final
     if (s_flag) {
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
       max_pass();
-      numerator_pass(std::false_type{});
+      numerator_pass(std::false_type{}, std::true_type{});
     }
     // 1/sum for the value waves, and lse
 #pragma unroll
