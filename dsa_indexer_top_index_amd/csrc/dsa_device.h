@@ -78,7 +78,18 @@ __device__ __forceinline__ void wait_vmem() { __asm__ volatile("s_waitcnt vmcnt(
 __device__ __forceinline__ void copy16_to_lds(const void* gsrc, DSA_LDS void* lds_wave_base) {
   // the LDS base is wave-uniform by contract; readfirstlane puts it in an SGPR for M0
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr) : "memory", "m0");
+  // one wait state between the M0 write and the LDS DMA that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+// The same copy with a scalar base address: lane i reads sbase + voff + OFF and writes
+// lds + OFF + 16*i. The immediate offset moves both addresses; lds must be wave-uniform.
+template <int OFF>
+__device__ __forceinline__ void copy16_to_lds_imm(const void* sbase, uint32_t voff, uint32_t lds) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(sbase), "s"(lds),
+               "n"(OFF)
+               : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding (they complete in order).

@@ -34,6 +34,7 @@
 #include "dsa_kernels.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace dsa {
 
@@ -42,6 +43,7 @@ constexpr int kRowGran = kLatent * 2 / 16;            // 72 granules (16 B) per 
 constexpr int kTileBytes = kTileKeys * kRowGran * 16;  // 18432: 18 wave copies of 1 KB
 constexpr int kRing = 7;                               // tiles in the shared LDS ring
 constexpr int kAhead = kRing - 3;                      // tiles whose copies run ahead of the scores
+constexpr int kPre = 4;                                // K fragments read ahead in the score loop
 constexpr float kRestartGap = 64.0f;                   // log2 headroom of a head's reference maximum
 constexpr int kMaxIdx = 2048;
 
@@ -62,6 +64,16 @@ __device__ __forceinline__ void mfma32_a(f32x16& acc, const u32x4& x, const u32x
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int H>
 __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
   using R = MlaRoles<H>;
@@ -79,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
   __shared__ float s_inv[MT * 32];
   __shared__ int s_flag;
 
-  const int wave = threadIdx.x / kWave;  // the block has exactly NW waves
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // the block has exactly NW waves
   const int lane = threadIdx.x % kWave;
   // Rows longest first, in dispatch order: consecutive blocks go to different XCDs, so every XCD
   // receives the same mix of long and short rows.
@@ -240,8 +252,12 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
       }
       for (int t = 1; t < ntiles; ++t) {
         barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
+        // K fragments are read kPre steps ahead of their MFMAs rather than all at once: right
+        // after the barrier every wave of the CU reads LDS, and a burst would delay them all.
+        const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
         bf16x8 kf[18];
-        load_k(t, kf);
+#pragma unroll
+        for (int st = 0; st < kPre; ++st) kf[st] = lds_read16(tq + 1024 * st);
         const int ivt = s_idx[t * kTileKeys + (lane & 15)];
         const uint32_t slot = ((t - 1) & 1) * kPSlot;
         bool ok[4];
@@ -251,6 +267,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
 #pragma unroll
         for (int i = 0; i < 18 * NTS; ++i) {
           const int st = i / NTS, nt = i % NTS;
+          if (nt == 0 && st + kPre < 18) kf[st + kPre] = lds_read16(tq + 1024 * (st + kPre));
           sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -317,18 +334,23 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
   } else {
     // ================================ value wave ================================
     const int vw = wave - NS;
-    // gather: this lane fills row slot i16 of column 4*i + g16, i.e. tile row my_row
+    // Gather: copy i (of a tile's 18) fills tile column 4*i + g16 with this lane's 16 bytes of
+    // row my_row; this wave does copies i = vw + 2c. The per-lane global offset of a tile is
+    // computed once (it includes 64*vw); the immediate offset 128*c moves both the global and the
+    // LDS address, so M0 carries the rest of the LDS displacement, 1024*i - 128*c.
     const int my_row = i16 ^ (4 * g16);
-    const uint8_t* kv_col = reinterpret_cast<const uint8_t*>(a.kv) + 16 * g16;
-    auto issue_tile = [&](int t) {
+    auto tile_voff = [&](int t) -> uint32_t {
       const int src = max(s_idx[t * kTileKeys + my_row], 0);
-      const uint8_t* g = kv_col + static_cast<int64_t>(src) * (kLatent * 2);
-      const uint32_t dst = ring + (t % kRing) * kTileBytes;
-#pragma unroll
-      for (int c = 0; c < CPV; ++c) {
-        const int i = vw + NV * c;  // this wave's copies of the tile's 18
-        copy16_to_lds(g + 64 * i, lds_ptr(dst + 1024 * i));
-      }
+      return static_cast<uint32_t>(src) * (kLatent * 2) + 16 * g16;
+    };
+    auto copy = [&](int t, uint32_t voff, auto c_const) {
+      constexpr int c = decltype(c_const)::value;
+      const uint32_t lds = ring + (t % kRing) * kTileBytes + 1024 * vw + (1024 - 64) * NV * c;
+      copy16_to_lds_imm<64 * NV * c>(a.kv, voff + 64 * vw, lds);
+    };
+    auto issue_tile = [&](int t) {
+      const uint32_t voff = tile_voff(t);
+      static_for<CPV>([&](auto c) { copy(t, voff, c); });
     };
     // Waits until this wave's copies of tile t have landed; later tiles stay in flight.
     auto wait_tile = [&](int t) {
@@ -372,19 +394,31 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
       for (int t = 0;; ++t) {
         if (t < ntiles) wait_tile(t);
         barrier_lds();  // every copy of tile t has landed; P of tile t-2 is complete
-        if (t + kAhead < ntiles) issue_tile(t + kAhead);  // into the slot of tile t-3
+        const int tn = t + kAhead;  // copied into the slot of tile t-3
         if (t > 1 && mode != 1) {
           const int tv = t - 2;
           const uint32_t tb = ring + (tv % kRing) * kTileBytes;
           const uint32_t pp = p_rd + (tv & 1) * kPSlot;
+          const bool dma = tn < ntiles;
+          const uint32_t voff = dma ? tile_voff(tn) : 0u;
           u32x4 pa[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) pa[mt] = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(pp + mt * 1024));
+          // V fragments two steps ahead of their MFMAs (see the K reads of the score waves)
+          u32x2 v1[CT], v2[CT];
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const u32x2 v1 = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * ct));
-            const u32x2 v2 = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * ct));
-            const u32x4 vb = {v1[0], v1[1], v2[0], v2[1]};
+          for (int ct = 0; ct < 2; ++ct) {
+            v1[ct] = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * ct));
+            v2[ct] = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * ct));
+          }
+          // the copies of tile tn go between the MFMAs, one after each group of three
+          static_for<CT>([&](auto ct_c) {
+            constexpr int ct = decltype(ct_c)::value;
+            if constexpr (ct + 2 < CT) {
+              v1[ct + 2] = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * (ct + 2)));
+              v2[ct + 2] = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * (ct + 2)));
+            }
+            const u32x4 vb = {v1[ct][0], v1[ct][1], v2[ct][0], v2[ct][1]};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               // A = V^T (lane: latent dim, 8 keys), B = P^T (lane: head, 8 keys), D = O^T
@@ -392,7 +426,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
               else
                 O[mt][ct] = mfma32(__builtin_bit_cast(bf16x8, vb), __builtin_bit_cast(bf16x8, pa[mt]), O[mt][ct]);
             }
-          }
+            __builtin_amdgcn_sched_barrier(0);
+            if (dma) {
+              copy(tn, voff, std::integral_constant<int, ct>{});
+              if constexpr (ct == CT - 1 && CPV > CT) copy(tn, voff, std::integral_constant<int, CT>{});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        } else if (tn < ntiles) {
+          issue_tile(tn);
         }
         if (t == ntiles + 1) break;
       }
