@@ -15,7 +15,10 @@ SOURCES = ["dsa_api.cpp", "k_index.hip", "k_mla.hip", "k_up.hip"]
 # Per-file code generation options. The attention kernel keeps 256 fp32 accumulators per lane in
 # AGPRs; selecting the VGPR form of MFMA lets the query fragments live in AGPRs as MFMA operands and
 # the QK^T accumulators in VGPRs, instead of evicting an output tile every key tile.
-FILE_FLAGS = {"k_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+FILE_FLAGS = {
+    "k_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed FP32 VALU instructions anywhere in the device code

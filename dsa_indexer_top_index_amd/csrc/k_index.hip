@@ -24,6 +24,9 @@
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace dsa {
 
 // ---------------------------------------------------------------------------------------------
@@ -70,7 +73,8 @@ __global__ __launch_bounds__(256) void k_key_layernorm(const uint16_t* __restric
 // ---------------------------------------------------------------------------------------------
 constexpr int kIdxWaves = 4;      // query rows per workgroup
 constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
-constexpr int kCap = 3840;        // candidate capacity per row (>= k + 2 * kChunk for k <= 2048)
+constexpr int kIdxRing = 3;       // staged chunks (copies run two chunks ahead)
+constexpr int kCap = 3328;        // candidate capacity per row (>= k + 2 * kChunk for k <= 2048)
 
 // Granule (16 bytes) position inside a staged key chunk: rows of GPR granules, XOR-swizzled.
 template <int GPR>
@@ -78,6 +82,9 @@ __device__ __forceinline__ int stage_granule(int key, int g) {
   const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
   return key * GPR + (g ^ f);
 }
+
+// max(x, +0) as an integer max on the bit pattern: negative values and -0 (sign bit set) give +0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ uint32_t hi_mask(int lo) { return lo >= 32 ? 0u : ~((1u << lo) - 1u); }
 
@@ -194,21 +201,35 @@ __device__ uint32_t wave_select_topk(uint32_t* keys, int32_t* idxs, uint32_t* hi
   return lo == 0 ? cur + 1u : cur;
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void idx_static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void idx_static_for(F&& f) {
+  idx_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int H_I, int D_I>
 __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
   constexpr int MT = (H_I + 31) / 32;   // 32-row M tiles of indexer heads
   constexpr int KS = D_I / 16;          // MFMA K steps
   constexpr int GPR = D_I / 8;          // 16-byte granules per key row
   constexpr int CHUNK_GRAN = kChunk * GPR;
+  constexpr int CPW = CHUNK_GRAN / (kIdxWaves * kWave);  // wave copies per chunk and wave
+  constexpr int NMF = MT * 2 * KS;      // MFMAs per chunk
+  constexpr int NEL = MT * 2 * 16;      // score elements per lane per chunk
+  constexpr int NMICRO = NEL / 2 + 2;   // epilogue micro-steps per chunk
   static_assert(CHUNK_GRAN % (kIdxWaves * kWave) == 0, "chunk copy split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2][kChunk * D_I];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kIdxRing][kChunk * D_I];
   __shared__ uint32_t s_keys[kIdxWaves][kCap];
   __shared__ int32_t s_idx[kIdxWaves][kCap];
   __shared__ uint32_t s_hist[kIdxWaves][256];
   __shared__ int s_range[2][kIdxWaves];
 
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int k = a.k;
 
@@ -237,7 +258,8 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
   }
   if (ke < 0) return;  // uniform: no row of this block needs a selection
 
-  // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims.
+  // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
+  // the MFMAs read directly. wr: head weight of each accumulator row this lane holds.
   bf16x8 qa[MT][KS];
   float wr[MT][16];
 #pragma unroll
@@ -257,6 +279,10 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
       wr[mt][i] = (select && hr < H_I) ? bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + hr]) : 0.0f;
     }
   }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qa[mt][s]));
 
   uint32_t* keys = s_keys[wave];
   int32_t* idxs = s_idx[wave];
@@ -268,11 +294,11 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
   const uint16_t* __restrict__ LNk = a.LNk;
   const int T = a.T;
 
-  auto issue_chunk = [&](int c, int buf) {
+  auto issue_chunk = [&](int c) {
     const int K0 = kb + c * kChunk;
-    DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[buf]);
+    DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c % kIdxRing]);
 #pragma unroll
-    for (int j = 0; j < CHUNK_GRAN / (kIdxWaves * kWave); ++j) {
+    for (int j = 0; j < CPW; ++j) {
       const int P0 = (wave * (CHUNK_GRAN / kIdxWaves)) + j * kWave;  // first granule of this wave copy
       const int P = P0 + lane;
       const int key = P / GPR;
@@ -283,65 +309,103 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
       copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
     }
   };
+  // Waits for this wave's copies of chunk c; the copies of chunk c+1 may stay in flight.
+  auto wait_chunk = [&](int c) {
+    if (c + 1 < nchunks) wait_vmem_le<CPW>();
+    else wait_vmem_le<0>();
+  };
 
-  issue_chunk(0, 0);
-  wait_vmem();
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchunks) issue_chunk(c + 1, buf ^ 1);
-    const int K0 = kb + c * kChunk;
-    if (select && K0 <= t && K0 + kChunk - 1 >= b) {
-      const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)(stage[buf]);
-      f32x16 acc[MT][2];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][0] = f32x16{};
-        acc[mt][1] = f32x16{};
-      }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int g = 2 * s + (lane >> 5);
-        const bf16x8 b0 = lds_read16(sb + stage_granule<GPR>(lane & 31, g) * 16);
-        const bf16x8 b1 = lds_read16(sb + stage_granule<GPR>(32 + (lane & 31), g) * 16);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][0] = mfma32(qa[mt][s], b0, acc[mt][0]);
-          acc[mt][1] = mfma32(qa[mt][s], b1, acc[mt][1]);
-        }
-      }
-      float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p0 += wr[mt][i] * fmaxf(acc[mt][0][i], 0.0f);
-          p1 += wr[mt][i] * fmaxf(acc[mt][1][i], 0.0f);
-        }
-      }
+  // Chunk c's scores: two 32-key N tiles, K = d_I. acc[mt][nb]: heads 32*mt.., keys 32*nb..
+  auto mfma_step = [&](int c, int i, f32x16 (&acc)[MT][2], bf16x8 (&kb0)[KS], bf16x8 (&kb1)[KS]) {
+    const int s = i / (2 * MT), rem = i % (2 * MT), nb = rem / MT, mt = rem % MT;
+    const bf16x8& bb = nb == 0 ? kb0[s] : kb1[s];
+    acc[mt][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bb, s == 0 ? f32x16{} : acc[mt][nb], 0, 0, 0);
+  };
+  auto load_b = [&](int c, int s, bf16x8 (&kb0)[KS], bf16x8 (&kb1)[KS]) {
+    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)(stage[c % kIdxRing]);
+    const int g = 2 * s + (lane >> 5);
+    kb0[s] = lds_read16(sb + stage_granule<GPR>(lane & 31, g) * 16);
+    kb1[s] = lds_read16(sb + stage_granule<GPR>(32 + (lane & 31), g) * 16);
+  };
+  // Epilogue of a chunk in micro-steps: ReLU, head weight and head sum (two elements a step),
+  // then the join of the half-waves and the append of the keys that reach the threshold.
+  float p0 = 0.0f, p1 = 0.0f;
+  auto micro = [&](int m, int c, const f32x16 (&acc)[MT][2]) {
+    if (m < NEL / 2) {
+      const int e = 2 * m;  // elements e, e+1: same (mt, nb), rows i, i+1
+      const int mt = e / 32, nb = (e / 16) % 2, i = e % 16;
+      float& pp = nb == 0 ? p0 : p1;
+      pp = __builtin_fmaf(wr[mt][i], relu(acc[mt][nb][i]), pp);
+      pp = __builtin_fmaf(wr[mt][i + 1], relu(acc[mt][nb][i + 1]), pp);
+    } else if (m == NEL / 2) {
       // Lanes < 32 end with key K0+lane of tile 0, lanes >= 32 with key K0+lane of tile 1.
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-      const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const int s_key = K0 + lane;
-      const uint32_t key = score_key(score);
-      const bool take = s_key >= b && s_key <= t && key >= thr;
-      const uint64_t m = ballot(take);
+      p0 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    } else {
+      const int s_key = kb + c * kChunk + lane;
+      const uint32_t key = score_key(p0);
+      const bool take = select && s_key >= b && s_key <= t && key >= thr;
+      const uint64_t msk = ballot(take);
       if (take) {
-        const int pos = cnt + lanes_below(m);
+        const int pos = cnt + lanes_below(msk);
         keys[pos] = key;
         idxs[pos] = s_key;
       }
-      cnt += __popcll(m);
-      if (cnt > kCap - kChunk) {
-        wave_lds_sync();
-        thr = wave_select_topk(keys, idxs, hist, cnt, k);
-        cnt = k;
-      }
+      cnt += __popcll(msk);
+      p0 = 0.0f;
+      p1 = 0.0f;
     }
-    wait_vmem();
-    __syncthreads();
+  };
+  auto maybe_select = [&]() {
+    if (cnt > kCap - kChunk) {  // rare after the first few thousand keys
+      wave_lds_sync();
+      thr = wave_select_topk(keys, idxs, hist, cnt, k);
+      cnt = k;
+    }
+  };
+  // One chunk: the MFMAs of chunk c (if any) interleaved with the epilogue of chunk c-1 (if any).
+  auto chunk_step = [&](int c, f32x16 (&cur)[MT][2], const f32x16 (&prev)[MT][2]) {
+    if (c < nchunks) wait_chunk(c);
+    barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
+    if (c + 2 < nchunks) issue_chunk(c + 2);
+    if (c < nchunks && c > 0) {
+      bf16x8 kb0[KS], kb1[KS];
+      load_b(c, 0, kb0, kb1);
+      load_b(c, 1, kb0, kb1);
+      idx_static_for<NMF>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        if constexpr (i % (2 * MT) == 0 && i / (2 * MT) + 2 < KS) load_b(c, i / (2 * MT) + 2, kb0, kb1);
+        mfma_step(c, i, cur, kb0, kb1);
+        __builtin_amdgcn_sched_barrier(0);
+        idx_static_for<NMICRO>([&](auto m_c) {
+          constexpr int m = decltype(m_c)::value;
+          if constexpr (m * NMF / NMICRO == i) micro(m, c - 1, prev);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      maybe_select();
+    } else if (c < nchunks) {
+      bf16x8 kb0[KS], kb1[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) load_b(c, s, kb0, kb1);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) mfma_step(c, i, cur, kb0, kb1);
+    } else {
+#pragma unroll
+      for (int m = 0; m < NMICRO; ++m) micro(m, c - 1, prev);
+      maybe_select();
+    }
+  };
+
+  issue_chunk(0);
+  if (nchunks > 1) issue_chunk(1);
+  f32x16 accA[MT][2], accB[MT][2];
+  int c = 0;
+  for (; c + 1 <= nchunks; c += 2) {
+    chunk_step(c, accA, accB);
+    chunk_step(c + 1, accB, accA);
   }
+  if (c <= nchunks) chunk_step(c, accA, accB);
 
   if (select) {
     wave_lds_sync();
