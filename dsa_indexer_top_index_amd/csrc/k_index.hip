@@ -113,13 +113,26 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
 // Keep the k best of the cnt candidates (keys desc, then list order = ascending token index).
 // The list is compacted in place and stays in ascending token order. Returns the new threshold:
 // every future candidate must have key >= the returned value to possibly enter the top k.
-__device__ uint32_t wave_select_topk(uint32_t* keys, int32_t* idxs, uint32_t* hist, int cnt, int k) {
+// Every pass reads kSelU entries per lane before using them, so a pass over the list costs a few
+// LDS latencies rather than one per 64 entries.
+constexpr int kSelU = 8;
+__device__ __forceinline__ uint32_t wave_select_topk(DSA_LDS uint32_t* keys, DSA_LDS int32_t* idxs, DSA_LDS uint32_t* hist,
+                                                     int cnt, int k) {
   const int lane = lane_id();
   uint32_t o = 0u, a = 0xffffffffu;
-  for (int i = lane; i < cnt; i += kWave) {
-    uint32_t v = keys[i];
-    o |= v;
-    a &= v;
+  for (int base = 0; base < cnt; base += kWave * kSelU) {
+    uint32_t v[kSelU];
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int i = base + kWave * u + lane;
+      v[u] = i < cnt ? keys[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const bool in = base + kWave * u + lane < cnt;
+      o |= v[u];
+      a &= in ? v[u] : 0xffffffffu;
+    }
   }
   o = wave_or(o);
   a = wave_and(a);
@@ -140,9 +153,18 @@ __device__ uint32_t wave_select_topk(uint32_t* keys, int32_t* idxs, uint32_t* hi
       const uint32_t hm = hi_mask(lo);
       for (int i = lane; i < 256; i += kWave) hist[i] = 0u;
       wave_lds_sync();
-      for (int i = lane; i < cnt; i += kWave) {
-        uint32_t v = keys[i];
-        if ((v & hm) == cur) atomicAdd(hist + ((v >> sh) & dmask), 1u);
+      for (int base = 0; base < cnt; base += kWave * kSelU) {
+        uint32_t v[kSelU];
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+          const int i = base + kWave * u + lane;
+          v[u] = i < cnt ? keys[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kSelU; ++u) {
+          const bool in = base + kWave * u + lane < cnt;
+          if (in && (v[u] & hm) == cur) __hip_atomic_fetch_add(hist + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        }
       }
       wave_lds_sync();
       // lane owns bins 4*lane .. 4*lane+3; find the bin holding the need-th largest entry
@@ -174,30 +196,39 @@ __device__ uint32_t wave_select_topk(uint32_t* keys, int32_t* idxs, uint32_t* hi
     }
   }
   // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur.
+  // Entries are written at or below their own position, so reading ahead is safe.
   const uint32_t hm = hi_mask(lo);
   int kept = 0, eq_seen = 0;
-  for (int base = 0; base < cnt; base += kWave) {
-    const int i = base + lane;
-    const bool in = i < cnt;
-    const uint32_t v = in ? keys[i] : 0u;
-    const int32_t x = in ? idxs[i] : 0;
-    const uint32_t vh = v & hm;
-    const bool gt = in && vh > cur;
-    const bool eq = in && vh == cur;
-    const uint64_t me = ballot(eq);
-    const int r_eq = eq_seen + lanes_below(me);
-    const bool keep = gt || (eq && r_eq < need);
-    const uint64_t mk = ballot(keep);
-    const int pos = kept + lanes_below(mk);
-    wave_lds_sync();
-    if (keep) {
-      keys[pos] = v;
-      idxs[pos] = x;
+  for (int base = 0; base < cnt; base += kWave * kSelU) {
+    uint32_t v[kSelU];
+    int32_t x[kSelU];
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const int i = base + kWave * u + lane;
+      v[u] = i < cnt ? keys[i] : 0u;
+      x[u] = i < cnt ? idxs[i] : 0;
     }
-    kept += __popcll(mk);
-    eq_seen += __popcll(me);
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < kSelU; ++u) {
+      const bool in = base + kWave * u + lane < cnt;
+      const uint32_t vh = v[u] & hm;
+      const bool gt = in && vh > cur;
+      const bool eq = in && vh == cur;
+      const uint64_t me = ballot(eq);
+      const int r_eq = eq_seen + lanes_below(me);
+      const bool keep = gt || (eq && r_eq < need);
+      const uint64_t mk = ballot(keep);
+      const int pos = kept + lanes_below(mk);
+      if (keep) {
+        keys[pos] = v[u];
+        idxs[pos] = x[u];
+      }
+      kept += __popcll(mk);
+      eq_seen += __popcll(me);
+    }
+    wave_lds_sync();
   }
-  wave_lds_sync();
   return lo == 0 ? cur + 1u : cur;
 }
 
@@ -284,9 +315,10 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qa[mt][s]));
 
-  uint32_t* keys = s_keys[wave];
-  int32_t* idxs = s_idx[wave];
-  uint32_t* hist = s_hist[wave];
+  // LDS-typed pointers, so that every access is a ds_ instruction
+  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[wave][0])));
+  DSA_LDS int32_t* idxs = reinterpret_cast<DSA_LDS int32_t*>(lds_ptr(lds_addr_of(&s_idx[wave][0])));
+  DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[wave][0])));
   int cnt = 0;
   uint32_t thr = 0u;
 
@@ -294,20 +326,23 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
   const uint16_t* __restrict__ LNk = a.LNk;
   const int T = a.T;
 
-  auto issue_chunk = [&](int c) {
+  // Copy j of this wave's share of chunk c: 64 granules, LDS slot P holds granule g = gl ^ f(key)
+  // of key P / GPR (the swizzle of stage_granule).
+  auto issue_copy = [&](int c, int j) {
     const int K0 = kb + c * kChunk;
     DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c % kIdxRing]);
+    const int P0 = (wave * (CHUNK_GRAN / kIdxWaves)) + j * kWave;  // first granule of this wave copy
+    const int P = P0 + lane;
+    const int key = P / GPR;
+    const int gl = P % GPR;
+    const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
+    const int g = gl ^ f;
+    const int row = min(K0 + key, T - 1);
+    copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
+  };
+  auto issue_chunk = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int P0 = (wave * (CHUNK_GRAN / kIdxWaves)) + j * kWave;  // first granule of this wave copy
-      const int P = P0 + lane;
-      const int key = P / GPR;
-      const int gl = P % GPR;
-      const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
-      const int g = gl ^ f;
-      const int row = min(K0 + key, T - 1);
-      copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
-    }
+    for (int j = 0; j < CPW; ++j) issue_copy(c, j);
   };
   // Waits for this wave's copies of chunk c; the copies of chunk c+1 may stay in flight.
   auto wait_chunk = [&](int c) {
@@ -367,11 +402,20 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
   auto chunk_step = [&](int c, f32x16 (&cur)[MT][2], const f32x16 (&prev)[MT][2]) {
     if (c < nchunks) wait_chunk(c);
     barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
+    // Copies issued between the MFMAs stall the matrix pipe for longer than they take here.
     if (c + 2 < nchunks) issue_chunk(c + 2);
     if (c < nchunks && c > 0) {
+      // Order: first B fragments, the first epilogue steps of chunk c-1 (they cover the LDS
+      // latency), then the MFMAs of chunk c with the remaining steps spread between them.
+      constexpr int kLead = 3;
       bf16x8 kb0[KS], kb1[KS];
       load_b(c, 0, kb0, kb1);
       load_b(c, 1, kb0, kb1);
+      idx_static_for<NMICRO>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m * NMF / NMICRO - kLead < 0) micro(m, c - 1, prev);
+      });
+      __builtin_amdgcn_sched_barrier(0);
       idx_static_for<NMF>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
         if constexpr (i % (2 * MT) == 0 && i / (2 * MT) + 2 < KS) load_b(c, i / (2 * MT) + 2, kb0, kb1);
@@ -379,9 +423,13 @@ __global__ __launch_bounds__(256, 1) void k_index_topk(IndexArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         idx_static_for<NMICRO>([&](auto m_c) {
           constexpr int m = decltype(m_c)::value;
-          if constexpr (m * NMF / NMICRO == i) micro(m, c - 1, prev);
+          if constexpr (m * NMF / NMICRO - kLead == i) micro(m, c - 1, prev);
         });
         __builtin_amdgcn_sched_barrier(0);
+      });
+      idx_static_for<NMICRO>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m * NMF / NMICRO - kLead >= NMF) micro(m, c - 1, prev);
       });
       maybe_select();
     } else if (c < nchunks) {
