@@ -27,6 +27,8 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "dsa_indexer_top_index_amd", "csrc", "k_mla.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_sparse_attention_t4096.json")
+COPY_BYTES = 1 << 30         # plain device copy used to scale the HBM byte counters
+COPY_LAUNCHES = 5
 
 WORKLOAD_TEXT = {
     "t4096": "single document T=4096, top-2048, 96 heads, indexer 64x128 with key LayerNorm, latent 512+64, "
@@ -70,6 +72,58 @@ def traffic_from_profile(launch_bytes_alg):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(d):
+    """Rows of every rocprofv3 counter-collection CSV under directory d."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch_kib(rows, name_part, counter):
+    """Per-dispatch values of `counter` (KiB; summed over the counter's instances) for kernels
+    whose name contains name_part."""
+    per = {}
+    for r in rows:
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r}")
+    return list(per.values())
+
+
+def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, commands):
+    """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE counter runs, each scaled by
+    what the same counter reads for a plain device copy of known size."""
+    copy_name = "copyBuffer"
+    cal_bytes = COPY_LAUNCHES * COPY_BYTES  # every copy dispatch of the calibration run together
+    fv = _per_dispatch_kib(_counter_rows(fetch_dir), "k_sparse_mla", "FETCH_SIZE")
+    wv = _per_dispatch_kib(_counter_rows(write_dir), "k_sparse_mla", "WRITE_SIZE")
+    f_kib, nf = sum(fv) / len(fv), len(fv)
+    w_kib, nw = sum(wv) / len(wv), len(wv)
+    cf_kib = sum(_per_dispatch_kib(_counter_rows(cal_fetch_dir), copy_name, "FETCH_SIZE"))
+    cw_kib = sum(_per_dispatch_kib(_counter_rows(cal_write_dir), copy_name, "WRITE_SIZE"))
+    f_scale = cal_bytes / (cf_kib * 1024.0)
+    w_scale = cal_bytes / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    res = {
+        "kernel": "k_sparse_mla", "workload": "t4096", "kernel_source_sha256_16": src_hash(ATTN_SRC),
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
+        "copy_calibration": {"bytes_each_way_all_copies": cal_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b, "commands": commands,
+    }
+    with open(PMC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def cpu_baseline(cfg, keys, stride):
     import oracle
     import testgen as tg
@@ -103,7 +157,14 @@ def main():
     ap.add_argument("--cpu-stride", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write the attention kernel's HBM bytes per launch from rocprofv3 counter runs")
+    ap.add_argument("--pmc-commands", default="", help="the profiling commands, recorded in the summary")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, commands=args.pmc_commands)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -114,14 +175,13 @@ def main():
     import torch
 
     if args.copy_calibration:
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         a.fill_(1)
         b = torch.empty_like(a)
-        for _ in range(5):
+        for _ in range(COPY_LAUNCHES):
             b.copy_(a)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": COPY_LAUNCHES}))
         return
 
     import dsa_indexer_top_index_amd as dsa
@@ -186,8 +246,13 @@ def main():
         "traffic": traffic,
         "alg_flop_per_launch": att_flop, "launch_ms": round(t_att, 4),
     }
+    mla_frac = (att_flop + up_flop) / ((t_att + t_up) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     stages = {
         "index_topk_ms": round(t_idx, 4), "attention_ms": round(t_att, 4), "up_gate_ms": round(t_up, 4),
+        # fractions of bf16 MFMA peak: the indexer over every causal pair (16,384 flop each), and sparse
+        # MLA over QK^T + PV of the selected keys plus W_UV (attention + up-projection/gate kernels)
+        "indexer_frac_all_pairs": round(idx_flop_all / (t_idx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "sparse_mla_frac_incl_up_gate": round(mla_frac, 4),
         "indexer_tflops_needed_rows": round(idx_flop_sel / (t_idx * 1e-3) / 1e12, 2),
         "indexer_tflops_all_pairs": round(idx_flop_all / (t_idx * 1e-3) / 1e12, 2),
         "indexer_frac_needed_rows": round(idx_flop_sel / (t_idx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -3,7 +3,7 @@
  *
  * The path (NeMo AutoModel "Kimi-K3.1-Pro" model-coverage page, summary and Implementation
  * Limits; archdiff.com "Kimi K3.1 Pro" blueprint; kimi_k3 API index, KimiK3TextConfig):
- *   1. LayerNorm on the indexer key k_I (blueprint: "LayerNorm on the indexer key").
+ *   1. LayerNorm on the indexer key k_I (blueprint component list: the indexer key is layer-normed).
  *   2. Indexer scores S(t,s) = sum_h w[t,h] * ReLU(q_I[t,h,:] . LN(k_I)[s,:]) over every causal
  *      key s of token t, bf16 operands with FP32 accumulation (Implementation Limits, 2nd bullet).
  *      The T x T score matrix is never stored. The scoring form and the tie rule below are the
@@ -15,7 +15,7 @@
  *      and 2nd bullets; blueprint tagline; API index mla_use_nope).
  *   5. Per-head V up-projection 512 -> 128 (the effective kv_b_proj V weight) and the sigmoid
  *      output gate out = sigma(g) * o (paragraph on the output gate and kv_b_proj; blueprint
- *      "Output gate").
+ *      output-gate component).
  *
  * Conventions for every entry point
  *  - bf16 tensors are passed as bf16 bit patterns (uint16_t) in device memory, row-major,
