@@ -2,6 +2,9 @@
 // call), workspace layout and the launch sequence of each entry point.
 #include "dsa.h"
 
+#include <algorithm>
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -13,6 +16,7 @@ namespace {
 
 constexpr int kMaxTopk = 2048;         // summary of the model-coverage page: at most 2,048 keys
 constexpr int64_t kMlaChunkRows = 16384;  // rows per attention/up-projection pass (bounds o_lat)
+constexpr int64_t kIdxPairedBelow = 4096;  // rows with a selection under which indexer blocks pair long and short rows
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -103,7 +107,55 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   a.row0 = s->q_begin;
   a.nrows = rows_of(s);
   a.k = s->topk;
-  if (dsa::launch_index_topk(a, s->H_I, s->d_I, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  // The candidate token indices of the rows in flight use the o_lat part of the workspace (the
+  // attention writes it only after the indexer is done); rows go in launches that fit there.
+  a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.olat_off);
+  const int64_t per_row = static_cast<int64_t>(dsa::index_candidate_capacity()) * 4;
+  const int64_t cap_rows = static_cast<int64_t>(L.olat_bytes) / per_row;  // >= 1: 16 KB of o_lat per row at least
+  if (cap_rows <= 0) return DSA_ERR_WORKSPACE;
+  if (dsa::launch_index_short_rows(a, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  // Rows with more than k causal keys, per document, in launches whose candidate lists fit.
+  // With few such rows per CU, blocks pair long and short rows of a document so that every block
+  // carries about the same work; otherwise blocks take consecutive rows, longest first.
+  struct Seg { int r0, m, b; };
+  std::vector<Seg> segs;
+  int64_t nsel = 0;
+  for (int d = 0; d < s->n_docs; ++d) {
+    const int64_t b0 = s->cu_seqlens_host ? s->cu_seqlens_host[d] : 0;
+    const int64_t b1 = s->cu_seqlens_host ? s->cu_seqlens_host[d + 1] : s->T;
+    const int64_t lo = std::max<int64_t>(b0 + s->topk, s->q_begin) - s->q_begin;
+    const int64_t hi = std::min<int64_t>(b1, s->q_begin + a.nrows) - s->q_begin;
+    for (int64_t h = hi; h > lo; h -= cap_rows) {  // pieces that fit the candidate space
+      const int64_t l = std::max<int64_t>(lo, h - cap_rows);
+      segs.push_back({static_cast<int>(l), static_cast<int>(h - l), static_cast<int>(b0)});
+      nsel += h - l;
+    }
+  }
+  a.paired = nsel < kIdxPairedBelow ? 1 : 0;
+  // longest rows first: the longest row of a segment is its last
+  std::stable_sort(segs.begin(), segs.end(),
+                   [&](const Seg& x, const Seg& y) { return x.r0 + x.m - x.b > y.r0 + y.m - y.b; });
+  size_t i = 0;
+  while (i < segs.size()) {
+    // one launch: consecutive segments whose rows fit the candidate space together
+    a.row_lo = segs[i].r0;
+    int row_hi = segs[i].r0 + segs[i].m;
+    a.nseg = 0;
+    a.seg_blk0[0] = 0;
+    while (i < segs.size() && a.nseg < dsa::kIdxMaxSeg) {
+      const int lo = std::min(a.row_lo, segs[i].r0), hi = std::max(row_hi, segs[i].r0 + segs[i].m);
+      if (hi - lo > cap_rows) break;
+      a.row_lo = lo;
+      row_hi = hi;
+      a.seg_r0[a.nseg] = segs[i].r0;
+      a.seg_m[a.nseg] = segs[i].m;
+      a.seg_b[a.nseg] = segs[i].b;
+      a.seg_blk0[a.nseg + 1] = a.seg_blk0[a.nseg] + dsa::index_blocks(segs[i].m, a.paired);
+      ++a.nseg;
+      ++i;
+    }
+    if (dsa::launch_index_topk(a, s->H_I, s->d_I, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  }
   return DSA_OK;
 }
 

@@ -6,6 +6,8 @@
 
 namespace dsa {
 
+constexpr int kIdxMaxSeg = 16;  // row segments per indexer launch
+
 struct IndexArgs {
   const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
   const uint16_t* w;     // [nrows, H_I]
@@ -17,6 +19,18 @@ struct IndexArgs {
   int row0;              // global token of local row 0
   int nrows;
   int k;
+  int32_t* cand;         // candidate token indices: index_candidate_capacity() per local row from row_lo on
+  int row_lo;            // first local row of the candidate space
+  // Rows that need a selection, as segments of consecutive local rows of one document each.
+  // Segment s: rows [seg_r0, seg_r0 + seg_m), document start token seg_b, blocks
+  // [seg_blk0[s], seg_blk0[s + 1]). paired != 0: each block takes 4 of the longest and 4 of the
+  // shortest rows left in its segment; else 8 consecutive rows, longest first.
+  int nseg;
+  int paired;
+  int seg_r0[kIdxMaxSeg];
+  int seg_m[kIdxMaxSeg];
+  int seg_b[kIdxMaxSeg];
+  int seg_blk0[kIdxMaxSeg + 1];
 };
 
 struct MlaArgs {
@@ -49,6 +63,10 @@ struct UpArgs {
 hipError_t launch_key_layernorm(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int T, int d_I,
                                 uint16_t* LNk, hipStream_t st);
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
+int index_blocks(int m, int paired);  // blocks of a segment of m rows
+// Output of the rows whose causal range holds at most k keys (no scores needed).
+hipError_t launch_index_short_rows(const IndexArgs& a, hipStream_t st);
+int index_candidate_capacity();  // candidate slots per row needed in IndexArgs::cand
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
 

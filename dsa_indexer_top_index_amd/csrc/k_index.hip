@@ -68,11 +68,10 @@ __global__ __launch_bounds__(256) void k_key_layernorm(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------------------------
-constexpr int kIdxRows = 4;       // query rows per workgroup (two waves each)
 constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
-constexpr int kIdxRing = 3;       // staged chunks (copies run two chunks ahead)
-constexpr int kCap = 3328;        // candidate capacity per row (>= k + 2 * kChunk for k <= 2048)
+constexpr int kCap = 3840;        // candidate capacity per row (>= k + kSelSlack + 2 * kChunk for k <= 2048)
 constexpr int kSelSlack = 256;    // extra entries a selection before the end of the row may keep
+constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
 
 // Granule (16 bytes) position inside a staged key chunk: rows of GPR granules, XOR-swizzled.
 template <int GPR>
@@ -116,23 +115,25 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
 // k-th key leaves at most `slack` extra entries: then every entry at or above that bin's lower
 // bound is kept (at least k) and the bound becomes the threshold, which is still at or below the
 // k-th key, so no key of the final top k is dropped. *kept_out receives the number kept.
-// scratch: 4*NW words of LDS. Must be called by every thread of the workgroup.
-constexpr int kSelU = 8;  // list entries per lane and wave slice (a slice holds kSelU * 64 entries)
+// keys live in LDS, their token indices in global memory (idxs). scratch: 4*NW words of LDS.
+// Must be called by every thread of the workgroup.
 template <int NW>
-__device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, DSA_LDS int32_t* idxs, DSA_LDS uint32_t* hist,
+__device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
                                                    DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out) {
-  static_assert(NW * kWave * kSelU >= kCap, "the wave slices cover the candidate list");
+  constexpr int kSelU = (kCap + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   // This wave's slice of the list: [s0, s0 + kSelU*64), entries s0 + 64*u + lane.
   const int s0 = wave * kWave * kSelU;
   uint32_t v[kSelU];
+  int32_t x[kSelU];
   bool in[kSelU];
 #pragma unroll
   for (int u = 0; u < kSelU; ++u) {
     const int i = s0 + kWave * u + lane;
     in[u] = i < cnt;
     v[u] = in[u] ? keys[i] : 0u;
+    x[u] = in[u] ? idxs[i] : 0;  // global loads, needed only by the compaction
   }
   uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
@@ -215,9 +216,6 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, DSA_L
   // of the waves before it. All entries were read into registers first, so writes cannot
   // overwrite an entry another wave has yet to read.
   const uint32_t hm = hi_mask(lo);
-  int32_t x[kSelU];
-#pragma unroll
-  for (int u = 0; u < kSelU; ++u) x[u] = in[u] ? idxs[s0 + kWave * u + lane] : 0;
   int gt_w = 0, eq_w = 0;
 #pragma unroll
   for (int u = 0; u < kSelU; ++u) {
@@ -260,60 +258,63 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, DSA_L
     kept += __popcll(mk);
     eq_seen += __popcll(me);
   }
+  wait_vmem();     // the compacted indices are written before any wave reads them
   barrier_lds();  // the compacted list and the scratch words are free for the next use
   *kept_out = total;
   return lo == 0 ? cur + 1u : cur;
 }
 
 template <int H_I, int D_I>
-__global__ __launch_bounds__(2 * kIdxRows * kWave, 1) void k_index_topk(IndexArgs a) {
+__global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a) {
   constexpr int MT = (H_I + 31) / 32;   // 32-row M tiles of indexer heads
   constexpr int KS = D_I / 16;          // MFMA K steps
   constexpr int GPR = D_I / 8;          // 16-byte granules per key row
   constexpr int CHUNK_GRAN = kChunk * GPR;
-  constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies per chunk and second-half wave
+  constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies per chunk and wave
   static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0, "chunk copy split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t stage[kIdxRing][kChunk * D_I];
-  __shared__ uint32_t s_keys[kIdxRows][kCap];
-  __shared__ int32_t s_idx[kIdxRows][kCap];
-  __shared__ uint32_t s_hist[kIdxRows][256];
-  __shared__ float s_xch[kIdxRows][2][32];  // second-half scores of a chunk, handed to the row's first wave
-  __shared__ int s_range[2][kIdxRows];
-  __shared__ int s_need[kIdxRows];          // candidate count of a row whose list must be compacted, else 0
-  __shared__ uint32_t s_sel[4 * 2 * kIdxRows];  // selection scratch
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2][kChunk * D_I];
+  __shared__ uint32_t s_keys[kIdxRows][kCap];     // candidate score keys (token indices: global)
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_need[kIdxRows];                // candidate count of a row whose list must be compacted, else 0
+  __shared__ int s_row[kIdxRows];                 // local row of each wave
+  __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the row slot of this wave
   const int lane = threadIdx.x % kWave;
-  const int slot = wave % kIdxRows;   // the row of this wave
-  const int half = wave / kIdxRows;   // 0: keys 0..31 of every chunk and the row's top-k; 1: keys 32..63
   const int k = a.k;
 
-  // Rows are taken from the end (longest causal ranges first).
-  const int r = a.nrows - kIdxRows * (blockIdx.x + 1) + slot;
-  const bool has_row = r >= 0;
-  const int t = a.row0 + r;
-  const int b = has_row ? doc_begin(a.cu, a.n_docs, t) : 0;
-  const int n = t - b + 1;
-  const bool select = has_row && n > k;
-  int32_t* out = a.topk_idx + static_cast<int64_t>(r) * k;
-
-  if (half == 0 && has_row && !select) {  // short row: every causal key, then -1
-    for (int j = lane; j < k; j += kWave) out[j] = j < n ? b + j : -1;
+  // This block's segment and its rows. Every row here has more than k causal keys, all in the
+  // segment's document, so the block's key range is [doc start, longest row + 1).
+  int sg = 0;
+  while (sg + 1 < a.nseg && static_cast<int>(blockIdx.x) >= a.seg_blk0[sg + 1]) ++sg;
+  const int blk = blockIdx.x - a.seg_blk0[sg];
+  const int m = a.seg_m[sg], A = a.seg_r0[sg];
+  int i_row, i_top;  // position of this wave's row and of the block's longest row in the segment
+  bool has_row;
+  if (a.paired) {
+    // waves w and w + 4 share a SIMD: one of the longest rows left and one of the shortest
+    const int h = (m + 1) >> 1;
+    const int p = 4 * blk + (wave & 3);
+    has_row = wave < 4 ? p < h : p < m - h;
+    i_row = wave < 4 ? m - 1 - p : p;
+    i_top = m - 1 - 4 * blk;
+  } else {
+    i_row = m - kIdxRows * (blk + 1) + wave;
+    has_row = i_row >= 0;
+    i_top = m - 1 - kIdxRows * blk;
   }
-  if (half == 0 && lane == 0) {
-    s_range[0][slot] = select ? b : 0x7fffffff;
-    s_range[1][slot] = select ? t + 1 : -1;
-    s_need[slot] = 0;
+  const int r = A + i_row;
+  const int t = a.row0 + r;
+  const int b = a.seg_b[sg];
+  const bool select = has_row;
+  int32_t* out = a.topk_idx + static_cast<int64_t>(r) * k;
+  if (lane == 0) {
+    s_need[wave] = 0;
+    s_row[wave] = r;
   }
   __syncthreads();
-  int kb = 0x7fffffff, ke = -1;
-#pragma unroll
-  for (int w = 0; w < kIdxRows; ++w) {
-    kb = min(kb, s_range[0][w]);
-    ke = max(ke, s_range[1][w]);
-  }
-  if (ke < 0) return;  // uniform: no row of this block needs a selection
+  const int kb = b, ke = a.row0 + A + i_top + 1;
 
   // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
   // the MFMAs read directly. wr: head weight of each accumulator row this lane holds.
@@ -341,45 +342,44 @@ __global__ __launch_bounds__(2 * kIdxRows * kWave, 1) void k_index_topk(IndexArg
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qa[mt][s]));
 
-  // LDS-typed pointers, so that every access is a ds_ instruction
-  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[slot][0])));
-  DSA_LDS int32_t* idxs = reinterpret_cast<DSA_LDS int32_t*>(lds_ptr(lds_addr_of(&s_idx[slot][0])));
-  DSA_LDS float* xch = reinterpret_cast<DSA_LDS float*>(lds_ptr(lds_addr_of(&s_xch[slot][0][0])));
+  // LDS-typed pointers, so that every access is a ds_ instruction; candidate indices in global memory
+  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[wave][0])));
+  DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[0])));
   DSA_LDS uint32_t* sel_scratch = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_sel[0])));
+  int32_t* cand = a.cand + static_cast<int64_t>(r - a.row_lo) * kCap;
   int cnt = 0;
   uint32_t thr = 0u;
+
   // Every wave selects for the rows that asked (rare): all waves of the workgroup share the work.
   auto run_selections = [&](int slack) {
     for (int rw = 0; rw < kIdxRows; ++rw) {
       const int c_rw = s_need[rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
-      DSA_LDS int32_t* ir = reinterpret_cast<DSA_LDS int32_t*>(lds_ptr(lds_addr_of(&s_idx[rw][0])));
-      DSA_LDS uint32_t* hr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[rw][0])));
+      int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCap;
       int kept = 0;
-      const uint32_t th = wg_select_topk<2 * kIdxRows>(kr, ir, hr, sel_scratch, c_rw, k, slack, &kept);
-      if (rw == slot && half == 0) {
+      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
+      if (rw == wave) {
         cnt = kept;
         thr = th;
       }
     }
     barrier_lds();  // every wave has read the flags
-    if (half == 0 && lane == 0) s_need[slot] = 0;
+    if (lane == 0) s_need[wave] = 0;
   };
 
   const int nchunks = (ke - kb + kChunk - 1) / kChunk;
   const uint16_t* __restrict__ LNk = a.LNk;
   const int T = a.T;
 
-  // The second-half waves copy the chunks (the first-half waves also keep the row's top-k).
   // Copy j of this wave's share of chunk c: 64 granules, LDS slot P holds granule g = gl ^ f(key)
   // of key P / GPR (the swizzle of stage_granule).
   auto issue_chunk = [&](int c) {
     const int K0 = kb + c * kChunk;
-    DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c % kIdxRing]);
+    DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c & 1]);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-      const int P0 = (slot * (CHUNK_GRAN / kIdxRows)) + j * kWave;  // first granule of this wave copy
+      const int P0 = (wave * (CHUNK_GRAN / kIdxRows)) + j * kWave;  // first granule of this wave copy
       const int P = P0 + lane;
       const int key = P / GPR;
       const int gl = P % GPR;
@@ -389,37 +389,36 @@ __global__ __launch_bounds__(2 * kIdxRows * kWave, 1) void k_index_topk(IndexArg
       copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
     }
   };
-  // Waits for this wave's copies of chunk c; the copies of chunk c+1 may stay in flight.
-  auto wait_chunk = [&](int c) {
-    if (c + 1 < nchunks) wait_vmem_le<CPW>();
-    else wait_vmem_le<0>();
-  };
-  // Scores of this wave's 32 keys of chunk c (keys 32*half ..): lanes l and l+32 both end with
-  // the full score of key 32*half + l%32.
+  // Scores of the 64 keys of chunk c: two 32-key N tiles, K = d_I; lane l ends with the score of
+  // key l (ReLU, head weight and head sum in FP32 registers, one swap joins the half-waves).
   auto chunk_scores = [&](int c) -> float {
-    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)(stage[c % kIdxRing]);
-    const int key = 32 * half + (lane & 31);
-    f32x16 acc[MT];
+    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)(stage[c & 1]);
+    f32x16 acc[MT][2];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const bf16x8 kf = lds_read16(sb + stage_granule<GPR>(key, 2 * s + (lane >> 5)) * 16);
+      const int g = 2 * s + (lane >> 5);
+      const bf16x8 b0 = lds_read16(sb + stage_granule<GPR>(lane & 31, g) * 16);
+      const bf16x8 b1 = lds_read16(sb + stage_granule<GPR>(32 + (lane & 31), g) * 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], kf, s == 0 ? f32x16{} : acc[mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], b0, s == 0 ? f32x16{} : acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], b1, s == 0 ? f32x16{} : acc[mt][1], 0, 0, 0);
+      }
     }
-    float p = 0.0f;
+    float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p = __builtin_fmaf(wr[mt][i], relu(acc[mt][i]), p);
-    // the two half-waves hold the two halves of the head sum
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      for (int i = 0; i < 16; ++i) {
+        p0 = __builtin_fmaf(wr[mt][i], relu(acc[mt][0][i]), p0);
+        p1 = __builtin_fmaf(wr[mt][i], relu(acc[mt][1][i]), p1);
+      }
+    // lanes < 32 end with key lane of tile 0, lanes >= 32 with key lane of tile 1
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
-  // Append the keys of chunk c that reach the threshold: lanes < 32 hold keys 0..31 (own scores),
-  // lanes >= 32 keys 32..63 (the second wave's, read from LDS beforehand).
-  auto append = [&](int c, float own, float other) {
-    const float score = lane < 32 ? own : other;
+  // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global.
+  auto append = [&](int c, float score) {
     const int s_key = kb + c * kChunk + lane;
     const uint32_t key = score_key(score);
     const bool take = select && s_key >= b && s_key <= t && key >= thr;
@@ -427,41 +426,33 @@ __global__ __launch_bounds__(2 * kIdxRows * kWave, 1) void k_index_topk(IndexArg
     if (take) {
       const int pos = cnt + lanes_below(msk);
       keys[pos] = key;
-      idxs[pos] = s_key;
+      cand[pos] = s_key;
     }
     cnt += __popcll(msk);
     // a full list is compacted at the start of the next step, before the next append
-    if (cnt > kCap - kChunk && lane == 0) s_need[slot] = cnt;
+    if (cnt > kCap - kChunk && lane == 0) s_need[wave] = cnt;
   };
 
-  if (half == 1) {
-    issue_chunk(0);
-    if (nchunks > 1) issue_chunk(1);
-  }
-  float prev = 0.0f;
-  for (int c = 0; c <= nchunks; ++c) {
-    if (half == 1 && c < nchunks) wait_chunk(c);
-    barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free; chunk c-1's hand-over is visible
-    if (s_need[0] | s_need[1] | s_need[2] | s_need[3]) run_selections(kSelSlack);  // uniform, rare
-    if (half == 1 && c + 2 < nchunks) issue_chunk(c + 2);
-    // the hand-over is read before this chunk's MFMAs, so its latency is hidden under them
-    const float other = (half == 0 && c > 0) ? xch[((c - 1) & 1) * 32 + (lane & 31)] : 0.0f;
-    float cur = 0.0f;
-    if (c < nchunks) cur = chunk_scores(c);
-    if (half == 1) {
-      if (c < nchunks && lane < 32) xch[(c & 1) * 32 + lane] = cur;
-    } else if (c > 0) {
-      append(c - 1, prev, other);
-    }
-    prev = cur;
+  issue_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    wait_vmem();    // this wave's copies of chunk c and its index stores are complete
+    barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
+    int any_need = 0;
+#pragma unroll
+    for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[w];
+    if (any_need) run_selections(kSelSlack);  // uniform, rare
+    if (c + 1 < nchunks) issue_chunk(c + 1);
+    // a wave whose row ends before this chunk leaves its SIMD to the other wave there
+    if (select && kb + c * kChunk <= t) append(c, chunk_scores(c));
   }
 
-  // Final exact selections (every wave takes part), then each row's first wave writes the row.
-  if (half == 0 && lane == 0) s_need[slot] = (select && cnt > k) ? cnt : 0;
+  // Final exact selections (every wave takes part), then each row's wave writes its row.
+  wait_vmem();
+  if (lane == 0) s_need[wave] = (select && cnt > k) ? cnt : 0;
   barrier_lds();
   run_selections(0);
-  if (half == 0 && select) {
-    for (int j = lane; j < k; j += kWave) out[j] = idxs[j];
+  if (select) {
+    for (int j = lane; j < k; j += kWave) out[j] = cand[j];
   }
 }
 
@@ -474,10 +465,34 @@ hipError_t launch_key_layernorm(const uint16_t* k_I, const float* gamma, const f
   return hipGetLastError();
 }
 
+int index_candidate_capacity() { return kCap; }
+
+int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
+
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st) {
-  dim3 grid((a.nrows + kIdxRows - 1) / kIdxRows), block(2 * kIdxRows * kWave);
+  if (a.nseg < 1 || a.nseg > kIdxMaxSeg) return hipErrorInvalidValue;
+  dim3 grid(a.seg_blk0[a.nseg]), block(kIdxRows * kWave);
   if (H_I == 64 && d_I == 128) hipLaunchKernelGGL((k_index_topk<64, 128>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((k_index_topk<4, 64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// Rows with at most k causal keys keep all of them in token order, then -1. One block per row
+// at a time; rows with more keys are left to k_index_topk.
+__global__ __launch_bounds__(256) void k_index_short_rows(IndexArgs a) {
+  for (int r = blockIdx.x; r < a.nrows; r += gridDim.x) {
+    const int t = a.row0 + r;
+    const int b = doc_begin(a.cu, a.n_docs, t);
+    const int n = t - b + 1;
+    if (n > a.k) continue;  // uniform
+    int32_t* out = a.topk_idx + static_cast<int64_t>(r) * a.k;
+    for (int j = threadIdx.x; j < a.k; j += blockDim.x) out[j] = j < n ? b + j : -1;
+  }
+}
+
+hipError_t launch_index_short_rows(const IndexArgs& a, hipStream_t st) {
+  dim3 grid(a.nrows < 2048 ? a.nrows : 2048), block(256);
+  hipLaunchKernelGGL(k_index_short_rows, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -82,7 +82,8 @@ dsa_status dsa_check_shape(const dsa_shape* shape);
  * float32 device arrays or NULL (identity); w [rows, H_I] bf16 (any sign).
  * Output: topk_idx [rows, topk] int32. Row r holds min(topk, n) distinct global token indices of
  * its causal keys (n = number of causal keys), in ascending order, then -1 up to topk.
- * Workspace: >= dsa_workspace_size(shape) bytes (holds LN(k_I)). */
+ * Workspace: >= dsa_workspace_size(shape) bytes (holds LN(k_I) and the candidate lists of the
+ * rows being selected). */
 dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
                           const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                           int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
