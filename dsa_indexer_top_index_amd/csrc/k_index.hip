@@ -273,12 +273,13 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies per chunk and wave
   static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0, "chunk copy split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2][kChunk * D_I];
+  __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
   __shared__ uint32_t s_keys[kIdxRows][kCap];     // candidate score keys (token indices: global)
   __shared__ uint32_t s_hist[256];
   __shared__ int s_need[kIdxRows];                // candidate count of a row whose list must be compacted, else 0
   __shared__ int s_row[kIdxRows];                 // local row of each wave
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
+  __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the row slot of this wave
   const int lane = threadIdx.x % kWave;
@@ -317,9 +318,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   const int kb = b, ke = a.row0 + A + i_top + 1;
 
   // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
-  // the MFMAs read directly. wr: head weight of each accumulator row this lane holds.
+  // the MFMAs read directly. Head weights go to LDS, read back by the score epilogue.
   bf16x8 qa[MT][KS];
-  float wr[MT][16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = 32 * mt + (lane & 31);
@@ -331,11 +331,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
         qa[mt][s] = bf16x8{};
       }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hr = 32 * mt + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      wr[mt][i] = (select && hr < H_I) ? bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + hr]) : 0.0f;
-    }
+    if (lane < 32) s_w[wave][32 * mt + lane] = (select && head < H_I) ? bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + head]) : 0.0f;
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -389,30 +385,58 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
     }
   };
-  // Scores of the 64 keys of chunk c: two 32-key N tiles, K = d_I; lane l ends with the score of
-  // key l (ReLU, head weight and head sum in FP32 registers, one swap joins the half-waves).
-  auto chunk_scores = [&](int c) -> float {
-    const DSA_LDS uint8_t* sb = (const DSA_LDS uint8_t*)(stage[c & 1]);
-    f32x16 acc[MT][2];
+  // Head dot products of the 64 keys of chunk c: two 32-key N tiles, K = d_I, into acc.
+  f32x16 acc[MT][2];
+  // The key operands of K step s are read kPf steps ahead of their MFMAs (scheduling fences keep
+  // that distance), so LDS latency hides behind the MFMAs of the steps in between.
+  auto chunk_mfma = [&](int c) {
+    constexpr int kPf = KS < 4 ? KS : 4;
+    bf16x8 bk[kPf][2];
+    // Granule 2s + lane/32 of key lane%32 sits at row base + 16 * ((2s + lane/32) ^ f(key)), and
+    // with a 256-byte aligned row base that is (row base ^ 16 * (lane/32 ^ f)) ^ 32s. Key
+    // 32 + lane%32 has the same swizzle, 32 rows further.
+    uint32_t a0 = (lds_addr_of(stage[c & 1]) + (lane & 31) * (GPR * 16)) ^ (16 * stage_granule<GPR>(lane & 31, lane >> 5) % (GPR * 16));
+    asm volatile("" : "+v"(a0));  // recomputed per chunk, not kept per K step
+    auto read_step = [&](int s, bf16x8& x0, bf16x8& x1) {
+      const uint32_t as = a0 ^ static_cast<uint32_t>(32 * s);
+      x0 = lds_read16(lds_ptr(as));
+      x1 = lds_read16(lds_ptr(as + 32 * GPR * 16));
+    };
+#pragma unroll
+    for (int s = 0; s < kPf; ++s) read_step(s, bk[s][0], bk[s][1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int g = 2 * s + (lane >> 5);
-      const bf16x8 b0 = lds_read16(sb + stage_granule<GPR>(lane & 31, g) * 16);
-      const bf16x8 b1 = lds_read16(sb + stage_granule<GPR>(32 + (lane & 31), g) * 16);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], b0, s == 0 ? f32x16{} : acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], b1, s == 0 ? f32x16{} : acc[mt][1], 0, 0, 0);
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf][0], s == 0 ? f32x16{} : acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf][1], s == 0 ? f32x16{} : acc[mt][1], 0, 0, 0);
       }
+      if (s + kPf < KS) read_step(s + kPf, bk[s % kPf][0], bk[s % kPf][1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // Scores from acc: lane l ends with the score of key l of the chunk (ReLU, head weight and head
+  // sum in FP32 registers, one swap joins the half-waves).
+  auto acc_score = [&]() -> float {
+    // accumulator element i of tile mt holds head 32*mt + 8*(i/4) + 4*(lane/32) + i%4
+    const DSA_LDS float* wrow = reinterpret_cast<const DSA_LDS float*>(lds_ptr(lds_addr_of(&s_w[wave][0])));
+    f32x4 w4[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) w4[mt][g] = *reinterpret_cast<const DSA_LDS f32x4*>(wrow + 32 * mt + 8 * g + 4 * (lane >> 5));
+    __builtin_amdgcn_sched_barrier(0);  // all weight reads in flight before the first use
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p0 = __builtin_fmaf(wr[mt][i], relu(acc[mt][0][i]), p0);
-        p1 = __builtin_fmaf(wr[mt][i], relu(acc[mt][1][i]), p1);
-      }
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p0 = __builtin_fmaf(w4[mt][g][e], relu(acc[mt][0][4 * g + e]), p0);
+          p1 = __builtin_fmaf(w4[mt][g][e], relu(acc[mt][1][4 * g + e]), p1);
+        }
     // lanes < 32 end with key lane of tile 0, lanes >= 32 with key lane of tile 1
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -443,7 +467,10 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     if (any_need) run_selections(kSelSlack);  // uniform, rare
     if (c + 1 < nchunks) issue_chunk(c + 1);
     // a wave whose row ends before this chunk leaves its SIMD to the other wave there
-    if (select && kb + c * kChunk <= t) append(c, chunk_scores(c));
+    if (select && kb + c * kChunk <= t) {
+      chunk_mfma(c);
+      append(c, acc_score());
+    }
   }
 
   // Final exact selections (every wave takes part), then each row's wave writes its row.
