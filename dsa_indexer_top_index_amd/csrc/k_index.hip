@@ -108,18 +108,22 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
 }
 
 // Keep the k best of a row's cnt candidates (keys desc, then list order = ascending token index).
-// Every wave of the workgroup takes part (NW waves, each on a slice of the list); the list is
-// compacted in place and stays in ascending token order. Returns the new threshold: a future
-// candidate must have key >= the returned value to possibly enter the top k.
+// Every wave of the workgroup takes part (NW waves, each on a slice of the list). Returns the new
+// threshold: a future candidate must have key >= the returned value to possibly enter the top k.
 // With slack > 0 the selection may stop early, at the first radix level whose bin holding the
 // k-th key leaves at most `slack` extra entries: then every entry at or above that bin's lower
 // bound is kept (at least k) and the bound becomes the threshold, which is still at or below the
 // k-th key, so no key of the final top k is dropped. *kept_out receives the number kept.
-// keys live in LDS, their token indices in global memory (idxs). scratch: 4*NW words of LDS.
-// Must be called by every thread of the workgroup.
+// keys live in LDS, their token indices in global memory (idxs). out == nullptr: the list is
+// compacted in place and stays in ascending token order; else the kept token indices go to
+// out[0 .. kept) in that order and the list is left as it was.
+// hist: 3 * 256 words, scratch: 4*NW words of LDS. Must be called by every thread of the
+// workgroup. The compacted indices are not waited for: a later reader of idxs from another wave
+// waits for this workgroup's stores (s_waitcnt vmcnt(0)) and a barrier first.
 template <int NW>
 __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
-                                                   DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out) {
+                                                   DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out,
+                                                   int32_t* __restrict__ out) {
   constexpr int kSelU = (kCap + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -147,6 +151,9 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     scratch[wave] = o;
     scratch[NW + wave] = a;
   }
+  // Radix level L counts into histogram L % 3 and clears histogram (L + 1) % 3, last read two
+  // levels earlier: one barrier per level.
+  for (int i = threadIdx.x; i < 256; i += NW * kWave) hist[i] = 0u;
   barrier_lds();
   o = 0u;
   a = 0xffffffffu;
@@ -165,23 +172,25 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
   } else {
     lo = 32 - __clz(static_cast<int>(varying));
     cur = a & hi_mask(lo);
+    int hb = 0;  // histogram of this level
     while (true) {
       const int sh = lo > 8 ? lo - 8 : 0;
       const int nb = lo - sh;
       const uint32_t dmask = (1u << nb) - 1u;
       const uint32_t hm = hi_mask(lo);
-      for (int i = threadIdx.x; i < 256; i += NW * kWave) hist[i] = 0u;
-      barrier_lds();
+      DSA_LDS uint32_t* h_cur = hist + 256 * hb;
+      const int hn = hb == 2 ? 0 : hb + 1;
 #pragma unroll
       for (int u = 0; u < kSelU; ++u)
         if (in[u] && (v[u] & hm) == cur)
-          __hip_atomic_fetch_add(hist + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(h_cur + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int i = threadIdx.x; i < 256; i += NW * kWave) hist[256 * hn + i] = 0u;
       barrier_lds();
       // lane owns bins 4*lane .. 4*lane+3; find the bin holding the need-th largest entry (every
       // wave computes the same answer)
       uint32_t h[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
+      for (int j = 0; j < 4; ++j) h[j] = h_cur[4 * lane + j];
       const uint32_t mine = h[0] + h[1] + h[2] + h[3];
       uint32_t above = wave_suffix_sum(mine) - mine;
       int found = -1;
@@ -200,10 +209,10 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
       const int d = __shfl(found, src);
       const uint32_t dab = __shfl(f_above, src);
       const uint32_t dcnt = __shfl(f_cnt, src);
-      barrier_lds();  // every wave has read the histogram before it is cleared again
       need -= static_cast<int>(dab);
       cur |= static_cast<uint32_t>(d) << sh;
       lo = sh;
+      hb = hn;
       if (dcnt == static_cast<uint32_t>(need) || sh == 0) break;
       if (static_cast<int>(dcnt) - need <= slack) {  // early stop: keep the whole bin
         need = static_cast<int>(dcnt);
@@ -213,8 +222,7 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
   }
   // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur.
   // Phase 1: per-wave counts; phase 2: each wave writes its kept entries after the kept entries
-  // of the waves before it. All entries were read into registers first, so writes cannot
-  // overwrite an entry another wave has yet to read.
+  // of the waves before it. Every wave holds its entries in registers before any wave writes.
   const uint32_t hm = hi_mask(lo);
   int gt_w = 0, eq_w = 0;
 #pragma unroll
@@ -227,6 +235,7 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     scratch[2 * NW + wave] = static_cast<uint32_t>(gt_w);
     scratch[3 * NW + wave] = static_cast<uint32_t>(eq_w);
   }
+  wait_vmem();    // this wave's index loads are complete before another wave overwrites them
   barrier_lds();
   // kept: entries kept by the waves before this one; eq_seen: their equal entries
   int kept = 0, eq_seen = 0, total = 0, eq_before = 0;
@@ -252,14 +261,16 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     const uint64_t mk = ballot(keep);
     const int pos = kept + lanes_below(mk);
     if (keep) {
-      keys[pos] = v[u];
-      idxs[pos] = x[u];
+      if (out != nullptr) {
+        out[pos] = x[u];
+      } else {
+        keys[pos] = v[u];
+        idxs[pos] = x[u];
+      }
     }
     kept += __popcll(mk);
     eq_seen += __popcll(me);
   }
-  wait_vmem();     // the compacted indices are written before any wave reads them
-  barrier_lds();  // the compacted list and the scratch words are free for the next use
   *kept_out = total;
   return lo == 0 ? cur + 1u : cur;
 }
@@ -275,7 +286,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
   __shared__ uint32_t s_keys[kIdxRows][kCap];     // candidate score keys (token indices: global)
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_hist[3 * 256];
   __shared__ int s_need[kIdxRows];                // candidate count of a row whose list must be compacted, else 0
   __shared__ int s_row[kIdxRows];                 // local row of each wave
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
@@ -347,14 +358,16 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   uint32_t thr = 0u;
 
   // Every wave selects for the rows that asked (rare): all waves of the workgroup share the work.
-  auto run_selections = [&](int slack) {
+  // final: exact selections whose kept indices go straight to the rows' outputs.
+  auto run_selections = [&](int slack, bool final) {
     for (int rw = 0; rw < kIdxRows; ++rw) {
       const int c_rw = s_need[rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
       int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCap;
       int kept = 0;
-      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
+      int32_t* o_rw = final ? a.topk_idx + static_cast<int64_t>(s_row[rw]) * k : nullptr;
+      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept, o_rw);
       if (rw == wave) {
         cnt = kept;
         thr = th;
@@ -464,7 +477,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     int any_need = 0;
 #pragma unroll
     for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[w];
-    if (any_need) run_selections(kSelSlack);  // uniform, rare
+    if (any_need) run_selections(kSelSlack, false);  // uniform, rare
     if (c + 1 < nchunks) issue_chunk(c + 1);
     // a wave whose row ends before this chunk leaves its SIMD to the other wave there
     if (select && kb + c * kChunk <= t) {
@@ -473,12 +486,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     }
   }
 
-  // Final exact selections (every wave takes part), then each row's wave writes its row.
+  // Final exact selections (every wave takes part) write their rows; a list of exactly k
+  // candidates is copied as it is.
   wait_vmem();
+  const bool as_is = select && cnt == k;
   if (lane == 0) s_need[wave] = (select && cnt > k) ? cnt : 0;
   barrier_lds();
-  run_selections(0);
-  if (select) {
+  run_selections(0, true);
+  if (as_is) {
     for (int j = lane; j < k; j += kWave) out[j] = cand[j];
   }
 }
