@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_key_layernorm(const uint16_t* __restric
 // ---------------------------------------------------------------------------------------------
 constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
 constexpr int kCap = 3840;        // candidate capacity per row (>= k + kSelSlack + 2 * kChunk for k <= 2048)
-constexpr int kSelSlack = 256;    // extra entries a selection before the end of the row may keep
+constexpr int kSelSlack = 64;    // extra entries a selection before the end of the row may keep
 constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
 
 // Granule (16 bytes) position inside a staged key chunk: rows of GPR granules, XOR-swizzled.
@@ -85,26 +85,36 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 __device__ __forceinline__ uint32_t hi_mask(int lo) { return lo >= 32 ? 0u : ~((1u << lo) - 1u); }
 
-// Wave-wide inclusive suffix sum (lane i gets the sum over lanes i..63).
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_down(x, off);
-    if (lane + off < kWave) x += y;
-  }
+// Wave-wide scans on DPP lane moves (VALU only, no LDS traffic). A moved-in value from a lane
+// outside the row, or into a row that row_mask leaves out, is the identity `id`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t id, uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(x), CTRL, ROW_MASK, 0xf, false));
+}
+// Inclusive scan of op over lanes 0..i: row_shr 1, 2, 4, 8 within each row of 16 lanes, then
+// row_bcast15 and row_bcast31 carry the totals of earlier rows.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, uint32_t id, Op op) {
+  x = op(x, dpp_move<0x111, 0xf>(id, x));
+  x = op(x, dpp_move<0x112, 0xf>(id, x));
+  x = op(x, dpp_move<0x114, 0xf>(id, x));
+  x = op(x, dpp_move<0x118, 0xf>(id, x));
+  x = op(x, dpp_move<0x142, 0xa>(id, x));
+  x = op(x, dpp_move<0x143, 0xc>(id, x));
   return x;
 }
-
 __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o);
-  return x;
+  x = wave_inclusive_scan(x, 0u, [](uint32_t p, uint32_t q) { return p | q; });
+  return __builtin_amdgcn_readlane(x, 63);
 }
 __device__ __forceinline__ uint32_t wave_and(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x &= __shfl_xor(x, o);
-  return x;
+  x = wave_inclusive_scan(x, 0xffffffffu, [](uint32_t p, uint32_t q) { return p & q; });
+  return __builtin_amdgcn_readlane(x, 63);
+}
+// Lane i gets the sum over lanes i..63.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t x) {
+  const uint32_t inc = wave_inclusive_scan(x, 0u, [](uint32_t p, uint32_t q) { return p + q; });
+  return __builtin_amdgcn_readlane(inc, 63) - inc + x;
 }
 
 // Keep the k best of a row's cnt candidates (keys desc, then list order = ascending token index).
@@ -205,10 +215,10 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
         above += h[j];
       }
       const uint64_t fm = ballot(found >= 0);
-      const int src = __ffsll(static_cast<unsigned long long>(fm)) - 1;
-      const int d = __shfl(found, src);
-      const uint32_t dab = __shfl(f_above, src);
-      const uint32_t dcnt = __shfl(f_cnt, src);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(fm)) - 1);
+      const int d = __builtin_amdgcn_readlane(found, src);
+      const uint32_t dab = __builtin_amdgcn_readlane(f_above, src);
+      const uint32_t dcnt = __builtin_amdgcn_readlane(f_cnt, src);
       need -= static_cast<int>(dab);
       cur |= static_cast<uint32_t>(d) << sh;
       lo = sh;
