@@ -297,7 +297,10 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
   __shared__ uint32_t s_keys[kIdxRows][kCap];     // candidate score keys (token indices: global)
   __shared__ uint32_t s_hist[3 * 256];
-  __shared__ int s_need[kIdxRows];                // candidate count of a row whose list must be compacted, else 0
+  // Candidate count of a row whose list must be compacted, else 0. Step c reads buffer c % 2 after
+  // its barrier while appends of that step write buffer (c + 1) % 2, so no wave can see a flag
+  // that another wave of the same step has not seen.
+  __shared__ int s_need[2][kIdxRows];
   __shared__ int s_row[kIdxRows];                 // local row of each wave
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
   __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
@@ -332,7 +335,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   const bool select = has_row;
   int32_t* out = a.topk_idx + static_cast<int64_t>(r) * k;
   if (lane == 0) {
-    s_need[wave] = 0;
+    s_need[0][wave] = 0;
+    s_need[1][wave] = 0;
     s_row[wave] = r;
   }
   __syncthreads();
@@ -369,9 +373,9 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 
   // Every wave selects for the rows that asked (rare): all waves of the workgroup share the work.
   // final: exact selections whose kept indices go straight to the rows' outputs.
-  auto run_selections = [&](int slack, bool final) {
+  auto run_selections = [&](int slack, bool final, int nbuf) {
     for (int rw = 0; rw < kIdxRows; ++rw) {
-      const int c_rw = s_need[rw];
+      const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
       int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCap;
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       }
     }
     barrier_lds();  // every wave has read the flags
-    if (lane == 0) s_need[wave] = 0;
+    if (lane == 0) s_need[nbuf][wave] = 0;
   };
 
   const int nchunks = (ke - kb + kChunk - 1) / kChunk;
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
   // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global.
-  auto append = [&](int c, float score) {
+  auto append = [&](int c, float score, int nbuf) {
     const int s_key = kb + c * kChunk + lane;
     const uint32_t key = score_key(score);
     const bool take = select && s_key >= b && s_key <= t && key >= thr;
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     }
     cnt += __popcll(msk);
     // a full list is compacted at the start of the next step, before the next append
-    if (cnt > kCap - kChunk && lane == 0) s_need[wave] = cnt;
+    if (cnt > kCap - kChunk && lane == 0) s_need[nbuf][wave] = cnt;
   };
 
   issue_chunk(0);
@@ -486,13 +490,13 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
     int any_need = 0;
 #pragma unroll
-    for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[w];
-    if (any_need) run_selections(kSelSlack, false);  // uniform, rare
+    for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[c & 1][w];
+    if (any_need) run_selections(kSelSlack, false, c & 1);  // uniform, rare
     if (c + 1 < nchunks) issue_chunk(c + 1);
     // a wave whose row ends before this chunk leaves its SIMD to the other wave there
     if (select && kb + c * kChunk <= t) {
       chunk_mfma(c);
-      append(c, acc_score());
+      append(c, acc_score(), (c + 1) & 1);
     }
   }
 
@@ -500,9 +504,9 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // candidates is copied as it is.
   wait_vmem();
   const bool as_is = select && cnt == k;
-  if (lane == 0) s_need[wave] = (select && cnt > k) ? cnt : 0;
+  if (lane == 0) s_need[nchunks & 1][wave] = (select && cnt > k) ? cnt : 0;
   barrier_lds();
-  run_selections(0, true);
+  run_selections(0, true, nchunks & 1);
   if (as_is) {
     for (int j = lane; j < k; j += kWave) out[j] = cand[j];
   }

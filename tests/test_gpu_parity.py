@@ -64,11 +64,30 @@ def _inputs(name_or_cfg):
     return _cache[cfg.name]
 
 
+def _check_structure(cfg, idx):
+    """Every row: min(k, n_t) distinct causal indices of its document in ascending order, then -1."""
+    T, k = idx.shape
+    t = np.arange(T)
+    b = np.zeros(T, dtype=np.int64)
+    cu = cfg.cu_seqlens
+    for d in range(cfg.n_docs):
+        b[cu[d]:cu[d + 1]] = cu[d]
+    keff = np.minimum(k, t - b + 1)
+    pos = np.arange(k)[None, :]
+    live = pos < keff[:, None]
+    assert np.all(idx[~live] == -1), "entries past min(k, n_t) are not -1"
+    assert np.all(np.where(live, idx >= b[:, None], True)), "index before the document start"
+    assert np.all(np.where(live, idx <= t[:, None], True)), "index after the query token"
+    inc = np.diff(idx.astype(np.int64), axis=1) > 0
+    assert np.all(np.where(live[:, 1:], inc, True)), "row not strictly ascending"
+
+
 def _run_and_check(cfg, keys, dev, rows, with_lse=True):
     _say(f"[gpu] fused forward {cfg.name}: T={cfg.T} docs={cfg.n_docs} k={cfg.topk} H={cfg.H}")
     res = gu.run_fused(cfg, dev, with_lse=with_lse)
     torch.cuda.synchronize()
     idx = res["topk_idx"].cpu().numpy()
+    _check_structure(cfg, idx)
     out = gu.bf16_tensor_to_f32(res["out"])
     lse = res["lse"].cpu().numpy() if with_lse else None
     rows = np.asarray(rows, dtype=np.int64)
@@ -113,8 +132,11 @@ def _sample(cfg, extra, n=24, seed=0):
 
 @pytest.mark.parametrize("name", ["t4096", "t8192"])
 def test_single_document_full_size(name):
+    """Sampled rows plus every 8th row of 3584..4095 (rows whose candidate lists first fill near
+    their last key chunk) and of the last 128 rows; the structure of every row."""
     cfg, keys, dev = _inputs(name)
-    rows = _sample(cfg, [0, 1, 2047, 2048, 2049, cfg.T // 2, cfg.T - 2, cfg.T - 1])
+    band = list(range(3584, 4096, 8)) + list(range(cfg.T - 128, cfg.T, 8))
+    rows = _sample(cfg, [0, 1, 2047, 2048, 2049, cfg.T // 2, cfg.T - 2, cfg.T - 1] + band)
     _run_and_check(cfg, keys, dev, rows)
 
 
