@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="t4096", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one by one after a 512 MB cache flush (0: none)")
     ap.add_argument("--cpu-stride", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -226,6 +228,21 @@ def main():
         dsa.dsa_up_gate(shape, o_lat, dev["W_UV"], dev["gate"], out)
         ev[i][3].record(stream)
     torch.cuda.synchronize()
+    warm_steps = [e[0].elapsed_time(e[3]) for e in ev]
+    # The same steps with L2 and the Infinity Cache flushed before each one (a 512 MB write,
+    # outside the timed interval): the cold-cache protocol.
+    cold_steps = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0x7f)
+            evc[i][0].record(stream)
+            step()
+            evc[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_steps = [e[0].elapsed_time(e[1]) for e in evc]
+        del flush
     t_idx = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     t_att = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     t_up = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
@@ -258,6 +275,11 @@ def main():
         "indexer_frac_needed_rows": round(idx_flop_sel / (t_idx * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "up_gate_gbs": round(up_bytes / (t_up * 1e-3) / 1e9, 1),
         "path_tflops": round(total_flop / (ms_step * 1e-3) / 1e12, 2),
+        # per-step times of the three kernels back to back (warm), and of whole steps after a cache flush
+        "warm_ms_per_step_median": round(float(np.median(warm_steps)), 4),
+        "warm_ms_per_step_min": round(float(np.min(warm_steps)), 4),
+        "cold_cache_ms_per_step_median": round(float(np.median(cold_steps)), 4) if cold_steps else None,
+        "cold_cache_ms_per_step_min": round(float(np.min(cold_steps)), 4) if cold_steps else None,
     }
     cpu = None
     if not args.no_cpu_baseline:
