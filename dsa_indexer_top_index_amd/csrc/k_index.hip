@@ -124,16 +124,14 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t x) {
 // k-th key leaves at most `slack` extra entries: then every entry at or above that bin's lower
 // bound is kept (at least k) and the bound becomes the threshold, which is still at or below the
 // k-th key, so no key of the final top k is dropped. *kept_out receives the number kept.
-// keys live in LDS, their token indices in global memory (idxs). out == nullptr: the list is
-// compacted in place and stays in ascending token order; else the kept token indices go to
-// out[0 .. kept) in that order and the list is left as it was.
+// keys live in LDS, their token indices in global memory (idxs); the list is compacted in place
+// and stays in ascending token order.
 // hist: 3 * 256 words, scratch: 4*NW words of LDS. Must be called by every thread of the
 // workgroup. The compacted indices are not waited for: a later reader of idxs from another wave
 // waits for this workgroup's stores (s_waitcnt vmcnt(0)) and a barrier first.
 template <int NW>
 __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
-                                                   DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out,
-                                                   int32_t* __restrict__ out) {
+                                                   DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out) {
   constexpr int kSelU = (kCap + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -271,18 +269,113 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     const uint64_t mk = ballot(keep);
     const int pos = kept + lanes_below(mk);
     if (keep) {
-      if (out != nullptr) {
-        out[pos] = x[u];
-      } else {
-        keys[pos] = v[u];
-        idxs[pos] = x[u];
-      }
+      keys[pos] = v[u];
+      idxs[pos] = x[u];
     }
     kept += __popcll(mk);
     eq_seen += __popcll(me);
   }
   *kept_out = total;
   return lo == 0 ? cur + 1u : cur;
+}
+
+// Exact top k of one row's cnt candidates (k < cnt <= kCap) by one wave, without workgroup
+// barriers, so that every wave can finish its own row at the same time. Keys in LDS and token
+// indices in global memory (idxs), both in ascending token order; the k kept indices go to
+// out[0 .. k) in that order (keys desc, ties to the lower index). hist: 256 words of LDS that
+// only this wave uses.
+__device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, const int32_t* __restrict__ idxs,
+                                                DSA_LDS uint32_t* hist, int cnt, int k, int32_t* __restrict__ out) {
+  constexpr int U = kCap / kWave;  // entries per lane: entry 64*u + lane
+  static_assert(kCap % kWave == 0, "whole list rows");
+  const int lane = lane_id();
+  uint32_t v[U];
+  uint32_t o = 0u, a = 0xffffffffu;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool in = kWave * u + lane < cnt;
+    v[u] = in ? keys[kWave * u + lane] : 0u;
+    o |= v[u];
+    a &= in ? v[u] : 0xffffffffu;
+  }
+  o = wave_or(o);
+  a = wave_and(a);
+  const uint32_t varying = o ^ a;
+  int lo;  // bits >= lo of the k-th key are known: cur
+  uint32_t cur;
+  int need = k;  // how many of the entries matching cur (in list order) are kept
+  if (varying == 0u) {
+    lo = 0;
+    cur = a;
+  } else {
+    lo = 32 - __clz(static_cast<int>(varying));
+    cur = a & hi_mask(lo);
+    while (true) {
+      const int sh = lo > 8 ? lo - 8 : 0;
+      const uint32_t dmask = (1u << (lo - sh)) - 1u;
+      const uint32_t hm = hi_mask(lo);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (kWave * u + lane < cnt && (v[u] & hm) == cur)
+          __hip_atomic_fetch_add(hist + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      wave_lds_sync();
+      // lane owns bins 4*lane .. 4*lane+3; find the bin holding the need-th largest entry
+      uint32_t h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
+      const uint32_t mine = h[0] + h[1] + h[2] + h[3];
+      uint32_t above = wave_suffix_sum(mine) - mine;
+      int found = -1;
+      uint32_t f_above = 0, f_cnt = 0;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (found < 0 && above < static_cast<uint32_t>(need) && static_cast<uint32_t>(need) <= above + h[j]) {
+          found = 4 * lane + j;
+          f_above = above;
+          f_cnt = h[j];
+        }
+        above += h[j];
+      }
+      const uint64_t fm = ballot(found >= 0);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<unsigned long long>(fm)) - 1);
+      const int d = __builtin_amdgcn_readlane(found, src);
+      const uint32_t dab = __builtin_amdgcn_readlane(f_above, src);
+      const uint32_t dcnt = __builtin_amdgcn_readlane(f_cnt, src);
+      need -= static_cast<int>(dab);
+      cur |= static_cast<uint32_t>(d) << sh;
+      lo = sh;
+      if (dcnt == static_cast<uint32_t>(need) || sh == 0) break;
+    }
+  }
+  // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur.
+  const uint32_t hm = hi_mask(lo);
+  int kept = 0, eq_seen = 0;
+  constexpr int G = 12;  // index loads in flight
+  static_assert(U % G == 0, "index load groups");
+#pragma unroll
+  for (int g = 0; g < U; g += G) {
+    int32_t x[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int i = kWave * (g + e) + lane;
+      x[e] = i < cnt ? idxs[i] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const bool in = kWave * (g + e) + lane < cnt;
+      const uint32_t vh = v[g + e] & hm;
+      const bool gt = in && vh > cur;
+      const bool eq = in && vh == cur;
+      const uint64_t me = ballot(eq);
+      const bool keep = gt || (eq && eq_seen + lanes_below(me) < need);
+      const uint64_t mk = ballot(keep);
+      if (keep) out[kept + lanes_below(mk)] = x[e];
+      kept += __popcll(mk);
+      eq_seen += __popcll(me);
+    }
+  }
 }
 
 template <int H_I, int D_I>
@@ -372,16 +465,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   uint32_t thr = 0u;
 
   // Every wave selects for the rows that asked (rare): all waves of the workgroup share the work.
-  // final: exact selections whose kept indices go straight to the rows' outputs.
-  auto run_selections = [&](int slack, bool final, int nbuf) {
+  auto run_selections = [&](int slack, int nbuf) {
     for (int rw = 0; rw < kIdxRows; ++rw) {
       const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
       int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCap;
       int kept = 0;
-      int32_t* o_rw = final ? a.topk_idx + static_cast<int64_t>(s_row[rw]) * k : nullptr;
-      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept, o_rw);
+      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
       if (rw == wave) {
         cnt = kept;
         thr = th;
@@ -491,7 +582,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     int any_need = 0;
 #pragma unroll
     for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[c & 1][w];
-    if (any_need) run_selections(kSelSlack, false, c & 1);  // uniform, rare
+    if (any_need) run_selections(kSelSlack, c & 1);  // uniform, rare
     if (c + 1 < nchunks) issue_chunk(c + 1);
     // a wave whose row ends before this chunk leaves its SIMD to the other wave there
     if (select && kb + c * kChunk <= t) {
@@ -500,15 +591,17 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     }
   }
 
-  // Final exact selections (every wave takes part) write their rows; a list of exactly k
-  // candidates is copied as it is.
-  wait_vmem();
-  const bool as_is = select && cnt == k;
-  if (lane == 0) s_need[nchunks & 1][wave] = (select && cnt > k) ? cnt : 0;
-  barrier_lds();
-  run_selections(0, true, nchunks & 1);
-  if (as_is) {
-    for (int j = lane; j < k; j += kWave) out[j] = cand[j];
+  // Final exact selection: each wave finishes its own row, with a histogram in the staging ring,
+  // which no wave uses any more.
+  wait_vmem();    // this wave's candidate index stores are complete
+  barrier_lds();  // every wave is done with the staging ring
+  if (select) {
+    if (cnt > k) {
+      DSA_LDS uint32_t* whist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(stage[0]) + 1024 * wave));
+      wave_select_out(keys, cand, whist, cnt, k, out);
+    } else {  // exactly k candidates
+      for (int j = lane; j < k; j += kWave) out[j] = cand[j];
+    }
   }
 }
 
