@@ -8,8 +8,9 @@
 //     l_j = scale * q[t,h,:] . kv[s_j,:]          (576 dims)
 //     o_lat[t,h,:] = softmax_j(l) . kv[s_j, 0:512]
 //
-// Kernel design: one workgroup per query row (rows longest first, consecutive rows on one XCD),
-// with two kinds of waves that meet in LDS, so every SIMD of the CU runs matrix instructions:
+// Kernel design: persistent workgroups, one per CU, each running query rows one after another
+// (longest rows first, dealt out zig-zag). Two kinds of waves meet in LDS, so every SIMD of the
+// CU runs matrix instructions:
 //  - Value waves (two): each owns the output accumulators of all heads for half of the 512 latent
 //    dims (384 FP32 per lane, two thirds of them in AGPRs). They issue every asynchronous 16-byte
 //    global->LDS copy of the gathered rows into a ring of six 16-row tiles (copies run four tiles
@@ -28,8 +29,9 @@
 //  than 2^64 (impossible for bounded inputs, but possible in principle), the row is redone, first
 //  a QK-only pass for each head's exact maximum, then the full pass against it, so no numerator
 //  can overflow.
-//  Epilogue: divide by the softmax sum, write o_lat (bf16) for the up-projection kernel, and the
-//  natural-log normaliser lse if requested.
+//  Epilogue: divide by the softmax sum, write o_lat (bf16) for the up-projection kernel straight
+//  from the value waves' accumulators, and the natural-log normaliser lse if requested. While the
+//  value waves store a row, the score waves already load the next row's indices and q fragments.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -93,59 +95,82 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // the block has exactly NW waves
   const int lane = threadIdx.x % kWave;
-  // Rows longest first, in dispatch order: consecutive blocks go to different XCDs, so every XCD
-  // receives the same mix of long and short rows.
-  const int rr = a.chunk_rows - 1 - static_cast<int>(blockIdx.x);
-  const int r = a.chunk_r0 + rr;  // local row
-  const int t_row = a.row0 + r;
-  const int b = doc_begin(a.cu, a.n_docs, t_row);
-  const int keff = min(a.k, t_row - b + 1);
-  const int ntiles = (keff + kTileKeys - 1) / kTileKeys;
   const int T = a.T;
   const int g16 = lane >> 4, i16 = lane & 15;
   const uint32_t ring = lds_addr_of(&s_ring[0][0]);
   const uint32_t pbase = lds_addr_of(&s_p[0][0][0]);
   constexpr uint32_t kPSlot = MT * 1024;
+  __shared__ int s_bad[2];  // by row parity: some full tile of the row holds unusable indices
 
-  // The row's indices, checked once: entries outside [0, T) become -1 (masked). P starts at zero.
-  // All loads are issued before the first store, so the row's index list arrives in one latency.
-  const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
-  constexpr int kPer = (kMaxIdx + 64 * NW - 1) / (64 * NW);
-  int iv[kPer];
+  // Persistent blocks: in round j, block b runs dispatch row G*j + b (j even) or G*j + G-1-b
+  // (j odd), G blocks in all; dispatch row i is local row chunk_r0 + chunk_rows-1-i, so rows go
+  // longest first and the zig-zag evens out the blocks' work. Consecutive dispatch rows run on
+  // different XCDs, so every XCD receives the same mix of long and short rows.
+  const int G = gridDim.x, bid = blockIdx.x;
+  auto dispatch_row = [&](int j) -> int { return G * j + ((j & 1) ? G - 1 - bid : bid); };
+  struct Row {
+    int rr, r, keff, ntiles;
+  };
+  auto row_of = [&](int i) -> Row {
+    Row w;
+    w.rr = a.chunk_rows - 1 - i;
+    w.r = a.chunk_r0 + w.rr;
+    const int t_row = a.row0 + w.r;
+    w.keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
+    w.ntiles = (w.keff + kTileKeys - 1) / kTileKeys;
+    return w;
+  };
+  // Threads [0, NT) load a row's indices into s_idx, checked once: entries outside [0, T) become
+  // -1 (masked), and one before the last tile flags the row in s_bad[par]. All loads are issued
+  // before the first store, so the list arrives in one latency. P starts at zero.
+  auto load_row = [&](const Row& w, auto nt_c, int par) {
+    constexpr int NT = decltype(nt_c)::value;
+    constexpr int kPer = (kMaxIdx + NT - 1) / NT;
+    const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(w.r) * a.k;
+    int iv[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = threadIdx.x + 64 * NW * i;
-    iv[i] = j < keff ? ix[j] : -1;
-  }
-  bool bad = false;  // an unusable index before the last tile
+    for (int i = 0; i < kPer; ++i) {
+      const int j = threadIdx.x + NT * i;
+      iv[i] = j < w.keff ? ix[j] : -1;
+    }
+    bool bad = false;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = threadIdx.x + 64 * NW * i;
-    const bool ok = iv[i] >= 0 && iv[i] < T;
-    if (j < ntiles * kTileKeys) s_idx[j] = ok ? iv[i] : -1;
-    bad |= !ok && j < (ntiles - 1) * kTileKeys;
-  }
-  for (int j = threadIdx.x; j < 2 * MT * 256; j += 64 * NW) reinterpret_cast<uint32_t*>(&s_p[0][0][0])[j] = 0u;
+    for (int i = 0; i < kPer; ++i) {
+      const int j = threadIdx.x + NT * i;
+      const bool ok = iv[i] >= 0 && iv[i] < T;
+      if (j < w.ntiles * kTileKeys) s_idx[j] = ok ? iv[i] : -1;
+      bad |= !ok && j < (w.ntiles - 1) * kTileKeys;
+    }
+    for (int j = threadIdx.x; j < 2 * MT * 256; j += NT) reinterpret_cast<uint32_t*>(&s_p[0][0][0])[j] = 0u;
+    if (bad) s_bad[par] = 1;
+  };
+
+  if (threadIdx.x < 2) s_bad[threadIdx.x] = 0;
   if (threadIdx.x == 0) s_flag = 0;
-  const bool any_bad = __syncthreads_or(bad);
+  __syncthreads();
+  Row w = row_of(dispatch_row(0));  // the launch has at least G rows
+  load_row(w, std::integral_constant<int, 64 * NW>{}, 0);
 
   if (wave < NS) {
     // ================================ score wave ================================
     const int sw = wave;
-    // q fragments, B operand of S^T = K Q^T. lane: head sw*HS + 16*nt + i16, dims 32*st + 8*g16.
     bf16x8 qf[NTS][18];
+    auto load_q = [&](int row) {
+      // q fragments, B operand of S^T = K Q^T. lane: head sw*HS + 16*nt + i16, dims 32*st + 8*g16.
 #pragma unroll
-    for (int nt = 0; nt < NTS; ++nt) {
-      const uint16_t* qrow = a.q + (static_cast<int64_t>(r) * a.H + sw * HS + 16 * nt + i16) * kLatent + 8 * g16;
+      for (int nt = 0; nt < NTS; ++nt) {
+        const uint16_t* qrow = a.q + (static_cast<int64_t>(row) * a.H + sw * HS + 16 * nt + i16) * kLatent + 8 * g16;
 #pragma unroll
-      for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
-    }
-    // the fragments live in AGPRs, which the MFMAs read directly; the VGPRs hold K fragments
+        for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
+      }
+      // the fragments live in AGPRs, which the MFMAs read directly; the VGPRs hold K fragments
 #pragma unroll
-    for (int nt = 0; nt < NTS; ++nt)
+      for (int nt = 0; nt < NTS; ++nt)
 #pragma unroll
-      for (int st = 0; st < 18; ++st) asm volatile("" : "+a"(qf[nt][st]));
-    mfma_agpr_settle();
+        for (int st = 0; st < 18; ++st) asm volatile("" : "+a"(qf[nt][st]));
+      mfma_agpr_settle();
+    };
+    load_q(w.r);
     const uint32_t qk_base = ring + (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // row i16, column 4*st + g16
     // This lane's numerators (head gh, keys 4*g16 .. +3) in the B operand of the value waves:
     // M tile gh/32, lane 32*(g16/2) + gh%32, bytes 8*(g16&1) of that lane's 16.
@@ -155,185 +180,199 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
       const int gh = sw * HS + 16 * nt + i16;
       p_off[nt] = pbase + ((gh >> 5) * 64 + 32 * (g16 >> 1) + (gh & 31)) * 16 + 8 * (g16 & 1);
     }
-    float m_ref[NTS], l_part[NTS];
-#pragma unroll
-    for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
-
-    // K fragments of tile t (row i16, dims 32*st + 8*g16), all requested at once
-    auto load_k = [&](int t, bf16x8 (&kf)[18]) {
-      const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
-#pragma unroll
-      for (int st = 0; st < 18; ++st) kf[st] = lds_read16(tq + 1024 * st);
-    };
-    // S^T of one tile: rows = 16 keys, cols = heads, K = 576 in 18 steps
-    auto qk = [&](const bf16x8 (&kf)[18], f32x4 (&sc)[NTS]) {
-#pragma unroll
-      for (int st = 0; st < 18; ++st)
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
-    };
-    // Key-validity bits of a tile (bit j: key j has a usable index), from the index lanes 0..15 hold.
-    auto valid_bits = [&](int idx_val) -> uint32_t {
-      return static_cast<uint32_t>(ballot(idx_val >= 0) & 0xffffull);
-    };
-    // Masked scores -> per-head maxima in log2 units (lanes i16 + 16*g hold the same head).
-    auto mask_max = [&](f32x4 (&sc)[NTS], uint32_t vm, float (&tmax)[NTS]) {
-      const uint32_t bits = vm >> (4 * g16);
-#pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc[nt][j] = ((bits >> j) & 1u) ? sc[nt][j] : -INFINITY;
-        float m = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
-        const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        m = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
-        const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
-      }
-    };
-    // Softmax numerators: x = scale*s - m_ref (log2 units), p = 2^x; masked keys get x = -inf
-    // and p = 0. gx keeps the largest x of the pass: while the references are the first tile's
-    // maxima, a value above kRestartGap means that the row has to be redone with exact maxima.
-    float msub[NTS], gx = -INFINITY;
-    struct Soft {
-      float x[4], p[4];
-    };
-    // Micro-step k of a tile's softmax (12 per 16-head tile, a few VALU instructions each), so
-    // that the steps fit between the MFMAs of the next tile. ok[j]: key 4*g16 + j is usable.
-    auto micro = [&](int k, const f32x4 (&sc)[NTS], const bool (&ok)[4], uint32_t slot, Soft (&sf)[NTS],
-                     auto masked_c) {
-      const int nt = k / 12, s = k % 12;
-      Soft& f = sf[nt];
-      if (s < 4) {
-        f.x[s] = __builtin_fmaf(sc[nt][s], a.scale_log2, -msub[nt]);
-        if constexpr (decltype(masked_c)::value) f.x[s] = ok[s] ? f.x[s] : -INFINITY;
-      } else if (s < 8) {
-        f.p[s - 4] = fast_exp2(f.x[s - 4]);  // -inf gives 0
-      } else if (s == 8) {
-        gx = fmaxf(gx, fmaxf(fmaxf(f.x[0], f.x[1]), fmaxf(f.x[2], f.x[3])));
-      } else if (s == 9) {
-        l_part[nt] += f.p[0] + f.p[1];
-      } else if (s == 10) {
-        l_part[nt] += f.p[2] + f.p[3];
-      } else {
-        const u32x2 pk = {pack_bf16x2(f.p[0], f.p[1]), pack_bf16x2(f.p[2], f.p[3])};
-        *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + slot)) = pk;
-      }
-    };
-    auto key_ok = [&](uint32_t vm, bool (&ok)[4]) {
-      const uint32_t bits = vm >> (4 * g16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ok[j] = (bits >> j) & 1u;
-    };
-    // One pass writing numerators; ntiles+2 barriers. CHECK: the first tile's maxima become the
-    // references and gx records growth beyond them; otherwise m_ref holds exact maxima. MASKED:
-    // some full tile holds unusable indices (the last tile is always masked). The MFMAs of tile t
-    // are interleaved with the micro-steps of tile t-1, so the VALU work runs while the matrix
-    // core is busy; the value waves consume that P one tile later.
-    auto numerator_pass = [&](auto check_c, auto masked_c) {
-#pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
-      f32x4 sprev[NTS];
-      uint32_t vprev;
-      {
-        barrier_lds();  // tile 0 has landed
-        bf16x8 kf[18];
-        load_k(0, kf);
-        const int iv0 = s_idx[lane & 15];
-        qk(kf, sprev);
-        vprev = valid_bits(iv0);
-        if constexpr (decltype(check_c)::value) {
-          float tmax[NTS];
-          mask_max(sprev, vprev, tmax);
-#pragma unroll
-          for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = tmax[nt];
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) msub[nt] = fmaxf(m_ref[nt], -3.0e38f);  // finite without usable keys
-      }
-      for (int t = 1; t < ntiles; ++t) {
-        barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
-        // K fragments are read kPre steps ahead of their MFMAs rather than all at once: right
-        // after the barrier every wave of the CU reads LDS, and a burst would delay them all.
-        const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
-        bf16x8 kf[18];
-#pragma unroll
-        for (int st = 0; st < kPre; ++st) kf[st] = lds_read16(tq + 1024 * st);
-        const int ivt = s_idx[t * kTileKeys + (lane & 15)];
-        const uint32_t slot = ((t - 1) & 1) * kPSlot;
-        bool ok[4];
-        key_ok(vprev, ok);
-        Soft sf[NTS];
-        f32x4 sc[NTS];
-#pragma unroll
-        for (int i = 0; i < 18 * NTS; ++i) {
-          const int st = i / NTS, nt = i % NTS;
-          if (nt == 0 && st + kPre < 18) kf[st + kPre] = lds_read16(tq + 1024 * (st + kPre));
-          sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int k = 0; k < 12 * NTS; ++k)
-            if (k * 3 / 2 == i) micro(k, sprev, ok, slot, sf, masked_c);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        vprev = valid_bits(ivt);
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) sprev[nt] = sc[nt];
-      }
-      barrier_lds();  // B_ntiles
-      {
-        bool ok[4];
-        key_ok(vprev, ok);
-        Soft sf[NTS];
-#pragma unroll
-        for (int k = 0; k < 12 * NTS; ++k) micro(k, sprev, ok, ((ntiles - 1) & 1) * kPSlot, sf, std::true_type{});
-      }
-      barrier_lds();  // B_ntiles+1
-    };
-    // Exact per-head maxima (QK only); ntiles+2 barriers.
-    auto max_pass = [&]() {
-      for (int t = 0;; ++t) {
-        barrier_lds();
-        if (t == ntiles + 1) break;
-        if (t == ntiles) continue;
-        bf16x8 kf[18];
-        load_k(t, kf);
-        const int ivt = s_idx[t * kTileKeys + (lane & 15)];
-        f32x4 sc[NTS];
-        qk(kf, sc);
-        float tmax[NTS];
-        mask_max(sc, valid_bits(ivt), tmax);
-#pragma unroll
-        for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
-      }
-    };
-    if (any_bad) numerator_pass(std::true_type{}, std::true_type{});
-    else numerator_pass(std::true_type{}, std::false_type{});
-    if (ballot(gx > kRestartGap) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
-    barrier_lds();  // (1) s_flag is final
-    if (s_flag) {
+    for (int j = 0;; ++j) {
+      barrier_lds();  // (A) the row's indices, zeroed P and q fragments are ready
+      const bool any_bad = s_bad[j & 1] != 0;
+      const int r = w.r, ntiles = w.ntiles;
+      float m_ref[NTS], l_part[NTS];
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
-      max_pass();
-      numerator_pass(std::false_type{}, std::true_type{});
-    }
-    // 1/sum for the value waves, and lse
+
+      // K fragments of tile t (row i16, dims 32*st + 8*g16), all requested at once
+      auto load_k = [&](int t, bf16x8 (&kf)[18]) {
+        const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
 #pragma unroll
-    for (int nt = 0; nt < NTS; ++nt) {
-      float l = l_part[nt];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
-      const int gh = sw * HS + 16 * nt + i16;
-      if (lane < 16) {
-        s_inv[gh] = l > 0.0f ? 1.0f / l : 0.0f;
-        if (a.lse)
-          a.lse[static_cast<int64_t>(r) * a.H + gh] = l > 0.0f ? (m_ref[nt] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        for (int st = 0; st < 18; ++st) kf[st] = lds_read16(tq + 1024 * st);
+      };
+      // S^T of one tile: rows = 16 keys, cols = heads, K = 576 in 18 steps
+      auto qk = [&](const bf16x8 (&kf)[18], f32x4 (&sc)[NTS]) {
+#pragma unroll
+        for (int st = 0; st < 18; ++st)
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
+      };
+      // Key-validity bits of a tile (bit j: key j has a usable index), from the index lanes 0..15 hold.
+      auto valid_bits = [&](int idx_val) -> uint32_t {
+        return static_cast<uint32_t>(ballot(idx_val >= 0) & 0xffffull);
+      };
+      // Masked scores -> per-head maxima in log2 units (lanes i16 + 16*g hold the same head).
+      auto mask_max = [&](f32x4 (&sc)[NTS], uint32_t vm, float (&tmax)[NTS]) {
+        const uint32_t bits = vm >> (4 * g16);
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[nt][j] = ((bits >> j) & 1u) ? sc[nt][j] : -INFINITY;
+          float m = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
+          const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
+          const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          tmax[nt] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1])) * a.scale_log2;
+        }
+      };
+      // Softmax numerators: x = scale*s - m_ref (log2 units), p = 2^x; masked keys get x = -inf
+      // and p = 0. gx keeps the largest x of the pass: while the references are the first tile's
+      // maxima, a value above kRestartGap means that the row has to be redone with exact maxima.
+      float msub[NTS], gx = -INFINITY;
+      struct Soft {
+        float x[4], p[4];
+      };
+      // Micro-step k of a tile's softmax (12 per 16-head tile, a few VALU instructions each), so
+      // that the steps fit between the MFMAs of the next tile. ok[j]: key 4*g16 + j is usable.
+      auto micro = [&](int k, const f32x4 (&sc)[NTS], const bool (&ok)[4], uint32_t slot, Soft (&sf)[NTS],
+                       auto masked_c) {
+        const int nt = k / 12, s = k % 12;
+        Soft& f = sf[nt];
+        if (s < 4) {
+          f.x[s] = __builtin_fmaf(sc[nt][s], a.scale_log2, -msub[nt]);
+          if constexpr (decltype(masked_c)::value) f.x[s] = ok[s] ? f.x[s] : -INFINITY;
+        } else if (s < 8) {
+          f.p[s - 4] = fast_exp2(f.x[s - 4]);  // -inf gives 0
+        } else if (s == 8) {
+          gx = fmaxf(gx, fmaxf(fmaxf(f.x[0], f.x[1]), fmaxf(f.x[2], f.x[3])));
+        } else if (s == 9) {
+          l_part[nt] += f.p[0] + f.p[1];
+        } else if (s == 10) {
+          l_part[nt] += f.p[2] + f.p[3];
+        } else {
+          const u32x2 pk = {pack_bf16x2(f.p[0], f.p[1]), pack_bf16x2(f.p[2], f.p[3])};
+          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(p_off[nt] + slot)) = pk;
+        }
+      };
+      auto key_ok = [&](uint32_t vm, bool (&ok)[4]) {
+        const uint32_t bits = vm >> (4 * g16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ok[j] = (bits >> j) & 1u;
+      };
+      // One pass writing numerators; ntiles+2 barriers. CHECK: the first tile's maxima become the
+      // references and gx records growth beyond them; otherwise m_ref holds exact maxima. MASKED:
+      // some full tile holds unusable indices (the last tile is always masked). The MFMAs of tile t
+      // are interleaved with the micro-steps of tile t-1, so the VALU work runs while the matrix
+      // core is busy; the value waves consume that P one tile later.
+      auto numerator_pass = [&](auto check_c, auto masked_c) {
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
+        f32x4 sprev[NTS];
+        uint32_t vprev;
+        {
+          barrier_lds();  // tile 0 has landed
+          bf16x8 kf[18];
+          load_k(0, kf);
+          const int iv0 = s_idx[lane & 15];
+          qk(kf, sprev);
+          vprev = valid_bits(iv0);
+          if constexpr (decltype(check_c)::value) {
+            float tmax[NTS];
+            mask_max(sprev, vprev, tmax);
+#pragma unroll
+            for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = tmax[nt];
+          }
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) msub[nt] = fmaxf(m_ref[nt], -3.0e38f);  // finite without usable keys
+        }
+        for (int t = 1; t < ntiles; ++t) {
+          barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
+          // K fragments are read kPre steps ahead of their MFMAs rather than all at once: right
+          // after the barrier every wave of the CU reads LDS, and a burst would delay them all.
+          const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
+          bf16x8 kf[18];
+#pragma unroll
+          for (int st = 0; st < kPre; ++st) kf[st] = lds_read16(tq + 1024 * st);
+          const int ivt = s_idx[t * kTileKeys + (lane & 15)];
+          const uint32_t slot = ((t - 1) & 1) * kPSlot;
+          bool ok[4];
+          key_ok(vprev, ok);
+          Soft sf[NTS];
+          f32x4 sc[NTS];
+#pragma unroll
+          for (int i = 0; i < 18 * NTS; ++i) {
+            const int st = i / NTS, nt = i % NTS;
+            if (nt == 0 && st + kPre < 18) kf[st + kPre] = lds_read16(tq + 1024 * (st + kPre));
+            sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 12 * NTS; ++k)
+              if (k * 3 / 2 == i) micro(k, sprev, ok, slot, sf, masked_c);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          vprev = valid_bits(ivt);
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) sprev[nt] = sc[nt];
+        }
+        barrier_lds();  // B_ntiles
+        {
+          bool ok[4];
+          key_ok(vprev, ok);
+          Soft sf[NTS];
+#pragma unroll
+          for (int k = 0; k < 12 * NTS; ++k) micro(k, sprev, ok, ((ntiles - 1) & 1) * kPSlot, sf, std::true_type{});
+        }
+        barrier_lds();  // B_ntiles+1
+      };
+      // Exact per-head maxima (QK only); ntiles+2 barriers.
+      auto max_pass = [&]() {
+        for (int t = 0;; ++t) {
+          barrier_lds();
+          if (t == ntiles + 1) break;
+          if (t == ntiles) continue;
+          bf16x8 kf[18];
+          load_k(t, kf);
+          const int ivt = s_idx[t * kTileKeys + (lane & 15)];
+          f32x4 sc[NTS];
+          qk(kf, sc);
+          float tmax[NTS];
+          mask_max(sc, valid_bits(ivt), tmax);
+#pragma unroll
+          for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = fmaxf(m_ref[nt], tmax[nt]);
+        }
+      };
+      if (any_bad) numerator_pass(std::true_type{}, std::true_type{});
+      else numerator_pass(std::true_type{}, std::false_type{});
+      if (ballot(gx > kRestartGap) != 0ull && lane == 0) s_flag = 1;  // rare: the row is redone
+      barrier_lds();  // (1) s_flag is final
+      if (s_flag) {
+#pragma unroll
+        for (int nt = 0; nt < NTS; ++nt) m_ref[nt] = -INFINITY;
+        max_pass();
+        numerator_pass(std::false_type{}, std::true_type{});
       }
+      // 1/sum for the value waves, and lse
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) {
+        float l = l_part[nt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const int gh = sw * HS + 16 * nt + i16;
+        if (lane < 16) {
+          s_inv[gh] = l > 0.0f ? 1.0f / l : 0.0f;
+          if (a.lse)
+            a.lse[static_cast<int64_t>(r) * a.H + gh] = l > 0.0f ? (m_ref[nt] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        }
+      }
+      if (MT * 32 > H && lane < MT * 32 - H) s_inv[H + lane] = 0.0f;
+      barrier_lds();  // (2) s_inv is ready
+      // While the value waves finish the row, load the next one.
+      if (threadIdx.x == 0) s_bad[j & 1] = 0;  // every wave read it after (A)
+      const int in = dispatch_row(j + 1);
+      if (in >= a.chunk_rows) break;
+      w = row_of(in);
+      if (threadIdx.x == 0) s_flag = 0;  // the value waves read it between (1) and (2)
+      load_row(w, std::integral_constant<int, 64 * NS>{}, (j + 1) & 1);
+      load_q(w.r);
     }
-    if (MT * 32 > H && lane < MT * 32 - H) s_inv[H + lane] = 0.0f;
-    barrier_lds();  // (2) s_inv is ready
   } else {
     // ================================ value wave ================================
     const int vw = wave - NS;
+    int ntiles = w.ntiles;
     // Gather: copy i (of a tile's 18) fills tile column 4*i + g16 with this lane's 16 bytes of
     // row my_row; this wave does copies i = vw + 2c. The per-lane global offset of a tile is
     // computed once (it includes 64*vw); the immediate offset 128*c moves both the global and the
@@ -382,10 +421,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     // One pass over the row; ntiles+2 barriers. mode 1 copies tiles only (the scores redo their
     // maxima); modes 0 and 2 accumulate P V, two tiles behind the scores.
     auto value_pass = [&](int mode) {
+      // a zero the compiler cannot see as a constant, so the accumulators' initial value is made
+      // here in every row instead of being kept live across the row loop
+      float z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) O[mt][ct] = f32x16{};
+        for (int ct = 0; ct < CT; ++ct) O[mt][ct] = f32x16{} + z;
       pin_acc();
       mfma_agpr_settle();
 #pragma unroll
@@ -439,47 +482,59 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         if (t == ntiles + 1) break;
       }
     };
-    value_pass(0);
-    barrier_lds();  // (1)
-    if (s_flag) {
-      value_pass(1);
-      value_pass(2);
-    }
-    mfma_agpr_drain();  // the accumulators are read by VALU below
-    pin_acc();
-    barrier_lds();      // (2) s_inv is ready; the score waves are done with the ring
-    // Normalise and stage [heads][512 dims] as bf16 in the ring (rows padded by 16 bytes against
-    // bank conflicts), then 16-byte stores. O^T tile (mt, ct), lane: head 32*mt + lane%32,
-    // element e: latent dim 32*(CT*vw + ct) + 8*(e/4) + 4*hh + e%4.
-    constexpr uint32_t kStageRow = kVDim * 2 + 16;
-    static_assert(MT * 32 * kStageRow <= kRing * kTileBytes, "staging fits in the ring");
-    const uint32_t stage = ring + (lane & 31) * kStageRow + 2 * (32 * CT * vw + 4 * hh);
+    for (int j = 0;; ++j) {
+      barrier_lds();  // (A)
+      ntiles = w.ntiles;
+      value_pass(0);
+      barrier_lds();  // (1)
+      if (s_flag) {
+        value_pass(1);
+        value_pass(2);
+      }
+      mfma_agpr_drain();  // the accumulators are read by VALU below
+      pin_acc();
+      barrier_lds();      // (2) s_inv is ready; the score waves are done with the ring
+      // Normalise and stage [heads][512 dims] as bf16 in the ring (rows padded by 16 bytes against
+      // bank conflicts), then 16-byte stores. O^T tile (mt, ct), lane: head 32*mt + lane%32,
+      // element e: latent dim 32*(CT*vw + ct) + 8*(e/4) + 4*hh + e%4.
+      constexpr uint32_t kStageRow = kVDim * 2 + 16;
+      static_assert(MT * 32 * kStageRow <= kRing * kTileBytes, "staging fits in the ring");
+      const uint32_t stage = ring + (lane & 31) * kStageRow + 2 * (32 * CT * vw + 4 * hh);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float inv = s_inv[32 * mt + (lane & 31)];
+      for (int mt = 0; mt < MT; ++mt) {
+        const float inv = s_inv[32 * mt + (lane & 31)];
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const f32x16 ov = O[mt][ct] * inv;
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x16 ov = O[mt][ct] * inv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x2 pk = {pack_bf16x2(ov[4 * j], ov[4 * j + 1]), pack_bf16x2(ov[4 * j + 2], ov[4 * j + 3])};
-          *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(stage + mt * 32 * kStageRow + 2 * (32 * ct + 8 * j))) = pk;
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const u32x2 pk = {pack_bf16x2(ov[4 * e4], ov[4 * e4 + 1]), pack_bf16x2(ov[4 * e4 + 2], ov[4 * e4 + 3])};
+            *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(stage + mt * 32 * kStageRow + 2 * (32 * ct + 8 * e4))) = pk;
+          }
         }
       }
-    }
-    wave_lds_sync();
-    uint16_t* dst = a.o_lat + static_cast<int64_t>(rr) * H * kVDim;
-    const int c0 = 256 * vw + 8 * (lane & 31);  // 32 lanes cover this wave's 256 dims
-    for (int h = hh; h < H; h += 2) {
-      const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(ring + h * kStageRow + 2 * c0));
-      *reinterpret_cast<u32x4*>(dst + h * kVDim + c0) = v;
+      wave_lds_sync();
+      uint16_t* dst = a.o_lat + static_cast<int64_t>(w.rr) * H * kVDim;
+      const int c0 = 256 * vw + 8 * (lane & 31);  // 32 lanes cover this wave's 256 dims
+      for (int h = hh; h < H; h += 2) {
+        const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(ring + h * kStageRow + 2 * c0));
+        *reinterpret_cast<u32x4*>(dst + h * kVDim + c0) = v;
+      }
+      const int in = dispatch_row(j + 1);
+      if (in >= a.chunk_rows) break;
+      w = row_of(in);
     }
   }
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
-  if (a.k > kMaxIdx) return hipErrorInvalidValue;
-  const dim3 grid(a.chunk_rows);
+  if (a.k > kMaxIdx || a.chunk_rows < 1) return hipErrorInvalidValue;
+  // one persistent workgroup per CU (its LDS use allows no second one), at most one per row
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return hipErrorInvalidValue;
+  const dim3 grid(a.chunk_rows < cus ? a.chunk_rows : cus);
   if (a.H == 96) hipLaunchKernelGGL((k_sparse_mla<96>), grid, dim3(64 * (MlaRoles<96>::NS + 2)), 0, st, a);
   else if (a.H == 16) hipLaunchKernelGGL((k_sparse_mla<16>), grid, dim3(64 * (MlaRoles<16>::NS + 2)), 0, st, a);
   else return hipErrorInvalidValue;
