@@ -26,6 +26,7 @@ METRIC = "query tokens/sec for indexer+top-2048+sparse MLA fwd; % of bf16 MFMA p
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "dsa_indexer_top_index_amd", "csrc", "k_mla.hip")
+IDX_SRC = os.path.join(ROOT, "dsa_indexer_top_index_amd", "csrc", "k_index.hip")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_sparse_attention_t4096.json")
 COPY_BYTES = 1 << 30         # plain device copy used to scale the HBM byte counters
 COPY_LAUNCHES = 5
@@ -124,6 +125,57 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, commands):
     print(json.dumps(res, indent=1))
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4   # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def pmc_mfma_summary(mfma_dir, commands):
+    """Per-kernel MFMA counters of a bench run (t4096): bf16 MFMA flops the hardware executed
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against the algorithmic flops, the rate both give over
+    the dispatch time, and the share of SIMD cycles the matrix cores were busy."""
+    import testgen as tg
+    rows = _counter_rows(mfma_dir)
+    cfg = tg.get_config("t4096")
+    keff_sum, all_pairs, sel_pairs = sum_keff(cfg)
+    alg = {
+        "k_sparse_mla": 2.0 * cfg.H * (576 + 512) * keff_sum,
+        "k_index_topk": 2.0 * cfg.H_I * cfg.d_I * all_pairs,   # every causal pair (the spec's count)
+        "k_up_gate": 2.0 * cfg.H * 512 * 128 * cfg.T,
+    }
+    out = {"workload": "t4096", "counters": list(MFMA_COUNTERS), "simds": SIMDS, "kernels": {},
+           "kernel_sources_sha256_16": {"attention": src_hash(ATTN_SRC), "indexer": src_hash(IDX_SRC)},
+           "commands": commands}
+    for name, alg_flop in alg.items():
+        per = {}
+        for r in rows:
+            if name in r["Kernel_Name"]:
+                d = per.setdefault(r["Dispatch_Id"], {"t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ds = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
+        if not ds:
+            raise SystemExit(f"no complete counter rows for {name}")
+        t = float(np.mean([d["t"] for d in ds]))
+        mops = float(np.mean([d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds]))
+        busy = float(np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds]))
+        gui = float(np.mean([d["GRBM_GUI_ACTIVE"] for d in ds]))
+        hw_flop = mops * 512.0
+        out["kernels"][name] = {
+            "dispatches": len(ds), "mean_dispatch_us": t * 1e6,
+            "hw_bf16_mfma_flop": hw_flop, "alg_flop": alg_flop, "hw_over_alg": hw_flop / alg_flop,
+            "hw_tflops": hw_flop / t / 1e12, "alg_tflops": alg_flop / t / 1e12,
+            "hw_frac_of_peak": hw_flop / t / 1e12 / PEAK_BF16_TFLOPS,
+            "mfma_busy_cycles": busy, "grbm_gui_active": gui,
+            # GRBM_GUI_ACTIVE comes summed over the XCDs; per-XCD active cycles x all SIMDs
+            "mfma_busy_frac": busy / (gui / XCDS * SIMDS),
+            "implied_clock_ghz": gui / XCDS / t / 1e9,
+        }
+    path = os.path.join(ROOT, "profiles", "pmc_mfma_t4096.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(cfg, keys, stride):
     import oracle
     import testgen as tg
@@ -162,10 +214,15 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
                     help="write the attention kernel's HBM bytes per launch from rocprofv3 counter runs")
     ap.add_argument("--pmc-commands", default="", help="the profiling commands, recorded in the summary")
+    ap.add_argument("--pmc-mfma-summary", metavar="MFMA_DIR",
+                    help="write per-kernel MFMA counters from a rocprofv3 run of " + ", ".join(MFMA_COUNTERS))
     args = ap.parse_args()
 
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, commands=args.pmc_commands)
+        return
+    if args.pmc_mfma_summary:
+        pmc_mfma_summary(args.pmc_mfma_summary, commands=args.pmc_commands)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
