@@ -12,7 +12,8 @@
 // v_mfma_f32_32x32x16_bf16 with rows as M, the 128 outputs as N (four tiles) and c as K.
 // W_UV[h] streams through LDS in 64-row chunks (asynchronous 16-byte copies, double buffered)
 // and is read transposed with ds_read_b64_tr_b16, so no transposed copy of the weight exists.
-// The gate is applied in FP32 in the epilogue.
+// The gate is applied in FP32 in the epilogue, which stages each wave's 32 x 128 outputs in the
+// then idle weight buffer so that every row leaves in 16-byte stores.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -21,11 +22,12 @@ namespace dsa {
 constexpr int kUpRows = 128;   // rows per workgroup
 constexpr int kUpChunk = 64;   // c rows of W_UV per LDS chunk
 constexpr int kUpChunkBytes = kUpChunk * kODim * 2;  // 16 KB
+constexpr int kUpWavesPerSimd = 4;   // waves per SIMD the register use must allow
 
 // Chunk layout: granule g (16 B, 8 outputs) of weight row c lives at slot 16*c + (g ^ 4*(c%4)).
 __device__ __forceinline__ int up_slot(int c, int g) { return 16 * c + (g ^ (4 * (c & 3))); }
 
-__global__ __launch_bounds__(256, 2) void k_up_gate(UpArgs a) {
+__global__ __launch_bounds__(256, kUpWavesPerSimd) void k_up_gate(UpArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kUpChunkBytes];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -92,18 +94,29 @@ __global__ __launch_bounds__(256, 2) void k_up_gate(UpArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: rows 8*i + 4*hh + j of the wave's 32, output column 32*nt + lane%32.
+  // Epilogue: accumulator element e of tile nt is row 8*(e/4) + 4*hh + e%4 of the wave's 32,
+  // output column 32*nt + lane%32. The gated bf16 values go to this wave's 8 KB of the weight
+  // buffer as [32 rows][128 outputs] (every wave is past the last read of it), then each row's
+  // 256 bytes leave as sixteen 16-byte stores.
+  static_assert(4 * 32 * kODim * 2 <= 2 * kUpChunkBytes, "staging fits the weight buffer");
+  DSA_LDS uint16_t* st = reinterpret_cast<DSA_LDS uint16_t*>(lds_ptr(lds_addr_of(&s_w[0][0]))) + wave * 32 * kODim;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = row0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-    if (row < a.chunk_rows) {
-      const int64_t lrow = a.chunk_r0 + row;  // local row of the call
-      const float g = bf16_to_f32(a.gate[lrow * H + h]);
-      const float sig = 1.0f / (1.0f + __expf(-g));
-      uint16_t* o = a.out + (lrow * H + h) * kODim + (lane & 31);
+    const int rw = 8 * (e >> 2) + 4 * hh + (e & 3);
+    const int row = min(row0 + rw, a.chunk_rows - 1);
+    const float g = bf16_to_f32(a.gate[(static_cast<int64_t>(a.chunk_r0) + row) * H + h]);
+    const float sig = 1.0f / (1.0f + __expf(-g));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) o[32 * nt] = f32_to_bf16(acc[nt][e] * sig);
-    }
+    for (int nt = 0; nt < 4; ++nt) st[rw * kODim + 32 * nt + (lane & 31)] = f32_to_bf16(acc[nt][e] * sig);
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rw = 4 * i + (lane >> 4);  // 16 lanes per row, 16 bytes each
+    const int row = row0 + rw;
+    const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(st + rw * kODim + 8 * (lane & 15));
+    if (row < a.chunk_rows)
+      *reinterpret_cast<u32x4*>(a.out + ((static_cast<int64_t>(a.chunk_r0) + row) * H + h) * kODim + 8 * (lane & 15)) = v;
   }
 }
 
