@@ -94,8 +94,6 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
                             const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, hipStream_t st) {
   const auto L = layout_of(s);
   uint16_t* lnk = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.lnk_off);
-  if (dsa::launch_key_layernorm(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->T, s->d_I, lnk, st) != hipSuccess)
-    return DSA_ERR_LAUNCH;
   dsa::IndexArgs a{};
   a.q_I = q_I;
   a.w = w;
@@ -113,7 +111,8 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   const int64_t per_row = static_cast<int64_t>(dsa::index_candidate_capacity()) * 4;
   const int64_t cap_rows = static_cast<int64_t>(L.olat_bytes) / per_row;  // >= 1: 16 KB of o_lat per row at least
   if (cap_rows <= 0) return DSA_ERR_WORKSPACE;
-  if (dsa::launch_index_short_rows(a, st) != hipSuccess) return DSA_ERR_LAUNCH;
+  if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st) != hipSuccess)
+    return DSA_ERR_LAUNCH;
   // Rows with more than k causal keys, per document, in launches whose candidate lists fit.
   // With few such rows per CU, blocks pair long and short rows of a document so that every block
   // carries about the same work; otherwise blocks take consecutive rows, longest first.

@@ -60,12 +60,11 @@ struct UpArgs {
   int H;
 };
 
-hipError_t launch_key_layernorm(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int T, int d_I,
-                                uint16_t* LNk, hipStream_t st);
+// Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
+hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
+                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st);
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
 int index_blocks(int m, int paired);  // blocks of a segment of m rows
-// Output of the rows whose causal range holds at most k keys (no scores needed).
-hipError_t launch_index_short_rows(const IndexArgs& a, hipStream_t st);
 int index_candidate_capacity();  // candidate slots per row needed in IndexArgs::cand
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);

@@ -29,11 +29,11 @@ namespace dsa {
 // ---------------------------------------------------------------------------------------------
 // Key LayerNorm: one wave per key row, double precision, one rounding to bf16.
 template <int D_I>
-__global__ __launch_bounds__(256) void k_key_layernorm(const uint16_t* __restrict__ k_I, const float* __restrict__ gamma,
-                                                       const float* __restrict__ beta, double eps, int T,
-                                                       uint16_t* __restrict__ LNk) {
+__device__ __forceinline__ void key_layernorm_block(const uint16_t* __restrict__ k_I, const float* __restrict__ gamma,
+                                                    const float* __restrict__ beta, double eps, int T,
+                                                    uint16_t* __restrict__ LNk, int blk) {
   constexpr int PER = D_I / kWave;
-  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int row = blk * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (row >= T) return;
   const uint16_t* x = k_I + static_cast<int64_t>(row) * D_I;
@@ -606,14 +606,6 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-hipError_t launch_key_layernorm(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int T, int d_I,
-                                uint16_t* LNk, hipStream_t st) {
-  dim3 grid((T + 3) / 4), block(256);
-  if (d_I == 128) hipLaunchKernelGGL((k_key_layernorm<128>), grid, block, 0, st, k_I, gamma, beta, eps, T, LNk);
-  else hipLaunchKernelGGL((k_key_layernorm<64>), grid, block, 0, st, k_I, gamma, beta, eps, T, LNk);
-  return hipGetLastError();
-}
-
 int index_candidate_capacity() { return kCap; }
 
 int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
@@ -627,9 +619,9 @@ hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t s
 }
 
 // Rows with at most k causal keys keep all of them in token order, then -1. One block per row
-// at a time; rows with more keys are left to k_index_topk.
-__global__ __launch_bounds__(256) void k_index_short_rows(IndexArgs a) {
-  for (int r = blockIdx.x; r < a.nrows; r += gridDim.x) {
+// at a time (block blk of nblk); rows with more keys are left to k_index_topk.
+__device__ __forceinline__ void short_rows_block(const IndexArgs& a, int blk, int nblk) {
+  for (int r = blk; r < a.nrows; r += nblk) {
     const int t = a.row0 + r;
     const int b = doc_begin(a.cu, a.n_docs, t);
     const int n = t - b + 1;
@@ -639,9 +631,24 @@ __global__ __launch_bounds__(256) void k_index_short_rows(IndexArgs a) {
   }
 }
 
-hipError_t launch_index_short_rows(const IndexArgs& a, hipStream_t st) {
-  dim3 grid(a.nrows < 2048 ? a.nrows : 2048), block(256);
-  hipLaunchKernelGGL(k_index_short_rows, grid, block, 0, st, a);
+// The two independent parts before the scoring kernel, in one launch: blocks [0, nln) normalise
+// four keys each, the others write the rows with at most k causal keys.
+template <int D_I>
+__global__ __launch_bounds__(256) void k_index_prologue(const uint16_t* __restrict__ k_I, const float* __restrict__ gamma,
+                                                        const float* __restrict__ beta, double eps,
+                                                        uint16_t* __restrict__ LNk, IndexArgs a, int nln) {
+  const int blk = blockIdx.x;
+  if (blk < nln) key_layernorm_block<D_I>(k_I, gamma, beta, eps, a.T, LNk, blk);
+  else short_rows_block(a, blk - nln, gridDim.x - nln);
+}
+
+hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
+                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st) {
+  const int nln = (a.T + 3) / 4;
+  const int nfill = a.nrows < 2048 ? a.nrows : 2048;
+  dim3 grid(nln + nfill), block(256);
+  if (d_I == 128) hipLaunchKernelGGL((k_index_prologue<128>), grid, block, 0, st, k_I, gamma, beta, eps, LNk, a, nln);
+  else hipLaunchKernelGGL((k_index_prologue<64>), grid, block, 0, st, k_I, gamma, beta, eps, LNk, a, nln);
   return hipGetLastError();
 }
 
