@@ -8,19 +8,25 @@
 //   topk(t)  = the min(k, n_t) causal keys largest by (score desc, index asc); a token with at
 //              most k causal keys keeps all of them.
 //
-// Kernel design (one wave per query row, four rows per workgroup, rows taken longest first):
+// Kernel design (one wave per query row, eight rows per workgroup, two waves per SIMD):
+//  - The host describes the rows that need a selection as per-document segments; a workgroup
+//    takes eight consecutive rows of a segment (longest first) or, when such rows are few, four of
+//    the longest and four of the shortest rows left, so that workgroups carry similar work. Rows
+//    with at most k causal keys are never scored: the prologue kernel writes them.
 //  - The LNk keys of the workgroup's causal range stream through LDS in chunks of 64 keys
-//    (asynchronous 16-byte global->LDS copies, double buffered, XOR-swizzled granules so the
-//    MFMA operand reads are bank-conflict free).
+//    (asynchronous 16-byte global->LDS copies, double buffered, one barrier per chunk,
+//    XOR-swizzled granules so that the MFMA operand reads are bank-conflict free). All eight rows
+//    share every staged chunk.
 //  - Scores: v_mfma_f32_32x32x16_bf16 with the indexer heads as M (q_I of the row held in
-//    registers), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head
-//    weight and the sum over heads happen in registers, and one permlane32 swap joins the two
-//    half-waves, leaving one full score per lane for 64 consecutive keys.
-//  - Top-k: scores become order-preserving uint32 keys. A key is appended to the row's LDS
-//    candidate list when it reaches the running threshold (ballot + mbcnt compaction, so the list
-//    stays in ascending token order). When the list nears capacity, a radix select over the
-//    candidates' varying bits (LDS histograms, wave prefix sums) finds the k-th key and a stable
-//    ballot compaction keeps exactly k (ties to the lower index), which also raises the threshold.
+//    AGPRs), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head weight
+//    and the sum over heads happen in registers, and one permlane32 swap joins the two half-waves,
+//    leaving one full score per lane for 64 consecutive keys.
+//  - Top-k: scores become order-preserving uint32 keys. A key is appended to the row's candidate
+//    list (keys in LDS, token indices in the workspace) when it reaches the running threshold
+//    (ballot + mbcnt compaction, so the list stays in ascending token order). When a list nears
+//    capacity, the whole workgroup runs a radix select over its varying bits (LDS histograms, DPP
+//    scans) and a stable compaction keeps the k best (ties to the lower index), which raises the
+//    threshold. At the end each wave finishes its own row's exact selection.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 

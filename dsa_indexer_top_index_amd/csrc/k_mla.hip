@@ -13,10 +13,10 @@
 // CU runs matrix instructions:
 //  - Value waves (two): each owns the output accumulators of all heads for half of the 512 latent
 //    dims (384 FP32 per lane, two thirds of them in AGPRs). They issue every asynchronous 16-byte
-//    global->LDS copy of the gathered rows into a ring of six 16-row tiles (copies run four tiles
-//    ahead), and compute O += P V on v_mfma_f32_32x32x16_bf16: heads as M (32-head tiles), latent
-//    dims as N, 16 keys as K. V is read straight from the natural row layout with
-//    ds_read_b64_tr_b16 and P from LDS. They run one tile behind the score waves.
+//    global->LDS copy of the gathered rows into a ring of seven 16-row tiles (copies run four
+//    tiles ahead), and compute O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: latent dims as M,
+//    32-head tiles as N, 16 keys as K. V is read straight from the natural row layout with
+//    ds_read_b64_tr_b16 and P from LDS. They run two tiles behind the score waves.
 //  - Score waves (two for 96 heads, 48 heads each; one for 16 heads): q fragments stay in
 //    registers; S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys as M, 16-head tiles as N,
 //    K = 576); softmax numerators in FP32 (base 2) against a per-head reference maximum set by the
@@ -29,9 +29,9 @@
 //  than 2^64 (impossible for bounded inputs, but possible in principle), the row is redone, first
 //  a QK-only pass for each head's exact maximum, then the full pass against it, so no numerator
 //  can overflow.
-//  Epilogue: divide by the softmax sum, write o_lat (bf16) for the up-projection kernel straight
-//  from the value waves' accumulators, and the natural-log normaliser lse if requested. While the
-//  value waves store a row, the score waves already load the next row's indices and q fragments.
+//  Epilogue: divide by the softmax sum, stage o_lat (bf16) in the ring and store it for the
+//  up-projection kernel, and write the natural-log normaliser lse if requested. While the value
+//  waves store a row, the score waves already load the next row's indices and q fragments.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
