@@ -60,7 +60,13 @@ def sum_keff(cfg):
 
 
 def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source's code: comments and layout are left out, so that editing a comment
+    does not invalidate counters taken on the same code."""
+    import re
+    t = open(path).read()
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return hashlib.sha256(" ".join(t.split()).encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(launch_bytes_alg):
@@ -68,7 +74,7 @@ def traffic_from_profile(launch_bytes_alg):
     if not os.path.exists(PMC_FILE):
         return None
     d = json.load(open(PMC_FILE))
-    if d.get("kernel_source_sha256_16") != src_hash(ATTN_SRC):
+    if d.get("kernel_code_sha256_16") != src_hash(ATTN_SRC):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -113,7 +119,7 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, commands):
     fetch_b = f_kib * 1024.0 * f_scale
     write_b = w_kib * 1024.0 * w_scale
     res = {
-        "kernel": "k_sparse_mla", "workload": "t4096", "kernel_source_sha256_16": src_hash(ATTN_SRC),
+        "kernel": "k_sparse_mla", "workload": "t4096", "kernel_code_sha256_16": src_hash(ATTN_SRC),
         "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [nf, nw],
         "copy_calibration": {"bytes_each_way_all_copies": cal_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
                              "fetch_scale": f_scale, "write_scale": w_scale},
@@ -144,7 +150,7 @@ def pmc_mfma_summary(mfma_dir, commands):
         "k_up_gate": 2.0 * cfg.H * 512 * 128 * cfg.T,
     }
     out = {"workload": "t4096", "counters": list(MFMA_COUNTERS), "simds": SIMDS, "kernels": {},
-           "kernel_sources_sha256_16": {"attention": src_hash(ATTN_SRC), "indexer": src_hash(IDX_SRC)},
+           "kernel_code_sha256_16": {"attention": src_hash(ATTN_SRC), "indexer": src_hash(IDX_SRC)},
            "commands": commands}
     for name, alg_flop in alg.items():
         per = {}

@@ -76,6 +76,7 @@ __device__ __forceinline__ void key_layernorm_block(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------------------------
 constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
 constexpr int kCap = 3840;        // candidate capacity per row (>= k + kSelSlack + 2 * kChunk for k <= 2048)
+constexpr int kCandStride = kCap + 64;  // per-row list stride: the last 64 slots take the lanes an append drops
 constexpr int kSelSlack = 64;    // extra entries a selection before the end of the row may keep
 constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
 
@@ -281,6 +282,11 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     kept += __popcll(mk);
     eq_seen += __popcll(me);
   }
+  // Consume every index load on every path: otherwise the compiler's wait insertion treats them as
+  // possibly outstanding at the caller's loop head and drains all vector memory operations (the
+  // next chunk's copies included) before the first MFMA that reuses their registers.
+#pragma unroll
+  for (int u = 0; u < kSelU; ++u) asm volatile("" ::"v"(x[u]));
   *kept_out = total;
   return lo == 0 ? cur + 1u : cur;
 }
@@ -394,12 +400,12 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0, "chunk copy split");
 
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
-  __shared__ uint32_t s_keys[kIdxRows][kCap];     // candidate score keys (token indices: global)
+  __shared__ uint32_t s_keys[kIdxRows][kCandStride];  // candidate score keys (token indices: global)
   __shared__ uint32_t s_hist[3 * 256];
   // Candidate count of a row whose list must be compacted, else 0. Step c reads buffer c % 2 after
   // its barrier while appends of that step write buffer (c + 1) % 2, so no wave can see a flag
   // that another wave of the same step has not seen.
-  __shared__ int s_need[2][kIdxRows];
+  __shared__ __attribute__((aligned(16))) int s_need[2][kIdxRows];
   __shared__ int s_row[kIdxRows];                 // local row of each wave
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
   __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
@@ -460,13 +466,13 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qa[mt][s]));
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qa[mt][s]));
 
   // LDS-typed pointers, so that every access is a ds_ instruction; candidate indices in global memory
   DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[wave][0])));
   DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[0])));
   DSA_LDS uint32_t* sel_scratch = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_sel[0])));
-  int32_t* cand = a.cand + static_cast<int64_t>(r - a.row_lo) * kCap;
+  int32_t* cand = a.cand + static_cast<int64_t>(r - a.row_lo) * kCandStride;
   int cnt = 0;
   uint32_t thr = 0u;
 
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
-      int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCap;
+      int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCandStride;
       int kept = 0;
       const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
       if (rw == wave) {
@@ -494,106 +500,162 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 
   // Copy j of this wave's share of chunk c: 64 granules, LDS slot P holds granule g = gl ^ f(key)
   // of key P / GPR (the swizzle of stage_granule).
-  auto issue_chunk = [&](int c) {
+  auto issue_copy = [&](int c, int j) {
     const int K0 = kb + c * kChunk;
     DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c & 1]);
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int P0 = (wave * (CHUNK_GRAN / kIdxRows)) + j * kWave;  // first granule of this wave copy
-      const int P = P0 + lane;
-      const int key = P / GPR;
-      const int gl = P % GPR;
-      const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
-      const int g = gl ^ f;
-      const int row = min(K0 + key, T - 1);
-      copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
-    }
+    const int P0 = (wave * (CHUNK_GRAN / kIdxRows)) + j * kWave;  // first granule of this wave copy
+    const int P = P0 + lane;
+    const int key = P / GPR;
+    const int gl = P % GPR;
+    const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
+    const int g = gl ^ f;
+    const int row = min(K0 + key, T - 1);
+    copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
   };
-  // Head dot products of the 64 keys of chunk c: two 32-key N tiles, K = d_I, into acc.
-  f32x16 acc[MT][2];
-  // The key operands of K step s are read kPf steps ahead of their MFMAs (scheduling fences keep
-  // that distance), so LDS latency hides behind the MFMAs of the steps in between.
-  auto chunk_mfma = [&](int c) {
-    constexpr int kPf = KS < 4 ? KS : 4;
-    bf16x8 bk[kPf][2];
-    // Granule 2s + lane/32 of key lane%32 sits at row base + 16 * ((2s + lane/32) ^ f(key)), and
-    // with a 256-byte aligned row base that is (row base ^ 16 * (lane/32 ^ f)) ^ 32s. Key
-    // 32 + lane%32 has the same swizzle, 32 rows further.
-    uint32_t a0 = (lds_addr_of(stage[c & 1]) + (lane & 31) * (GPR * 16)) ^ (16 * stage_granule<GPR>(lane & 31, lane >> 5) % (GPR * 16));
-    asm volatile("" : "+v"(a0));  // recomputed per chunk, not kept per K step
-    auto read_step = [&](int s, bf16x8& x0, bf16x8& x1) {
-      const uint32_t as = a0 ^ static_cast<uint32_t>(32 * s);
-      x0 = lds_read16(lds_ptr(as));
-      x1 = lds_read16(lds_ptr(as + 32 * GPR * 16));
-    };
+  auto issue_chunk = [&](int c) {
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) read_step(s, bk[s][0], bk[s][1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf][0], s == 0 ? f32x16{} : acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf][1], s == 0 ? f32x16{} : acc[mt][1], 0, 0, 0);
-      }
-      if (s + kPf < KS) read_step(s + kPf, bk[s % kPf][0], bk[s % kPf][1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int j = 0; j < CPW; ++j) issue_copy(c, j);
   };
-  // Scores from acc: lane l ends with the score of key l of the chunk (ReLU, head weight and head
-  // sum in FP32 registers, one swap joins the half-waves).
-  auto acc_score = [&]() -> float {
-    // accumulator element i of tile mt holds head 32*mt + 8*(i/4) + 4*(lane/32) + i%4
+  // Scores of a chunk come from two 32-key N tiles (K = d_I): tile 0 into accA, tile 1 into accB.
+  // The loop is software pipelined by half a chunk: the MFMAs of one tile run interleaved with
+  // the VALU epilogue of the tile before it (ReLU, head weight, partial head sums), so the matrix
+  // core and the vector ALU work at the same time. Step c runs tile 0 of chunk c beside the
+  // epilogue of tile 1 of chunk c-1, then tile 1 of chunk c beside the epilogue of tile 0 of
+  // chunk c and the append of chunk c-1.
+  f32x16 accA[MT], accB[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) accB[mt] = f32x16{};  // the epilogue of "chunk -1" adds nothing
+  // Head weights in registers: element 4*g + e of an accumulator tile mt holds head
+  // 32*mt + 8*g + 4*(lane/32) + e.
+  f32x4 w4[MT][4];
+  {
     const DSA_LDS float* wrow = reinterpret_cast<const DSA_LDS float*>(lds_ptr(lds_addr_of(&s_w[wave][0])));
-    f32x4 w4[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) w4[mt][g] = *reinterpret_cast<const DSA_LDS f32x4*>(wrow + 32 * mt + 8 * g + 4 * (lane >> 5));
-    __builtin_amdgcn_sched_barrier(0);  // all weight reads in flight before the first use
-    float p0 = 0.0f, p1 = 0.0f;
+  }
+  constexpr int kEl = MT * 16;        // accumulator elements per lane of one N tile
+  constexpr int kEps = kEl / KS;      // epilogue elements per K step
+  static_assert(kEl % KS == 0 && kEps >= 1 && kEps <= 8, "epilogue split");
+  constexpr int kPf = KS < 2 ? KS : 2;  // key operands are read kPf K steps ahead of their MFMAs
+  // One N tile of chunk c into acc, interleaved with the epilogue of `prev`; returns this lane's
+  // partial sum over its heads of the previous tile (one key column per lane).
+  auto tile_step = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
+    // Granule 2s + lane/32 of key lane%32 sits at row base + 16 * ((2s + lane/32) ^ f(key)); with a
+    // 256-byte aligned row base that is (row base ^ 16 * (lane/32 ^ f)) ^ 32s. Tile 1 is 32 rows on.
+    uint32_t a0 = (lds_addr_of(stage[c & 1]) + n * (32 * GPR * 16) + (lane & 31) * (GPR * 16)) ^
+                  (16 * stage_granule<GPR>(lane & 31, lane >> 5) % (GPR * 16));
+    asm volatile("" : "+v"(a0));
+    bf16x8 bk[kPf];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int s = 0; s < kPf; ++s) bk[s] = lds_read16(lds_ptr(a0 ^ static_cast<uint32_t>(32 * s)));
+    float part[kEps];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+    for (int j = 0; j < kEps; ++j) part[j] = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p0 = __builtin_fmaf(w4[mt][g][e], relu(acc[mt][0][4 * g + e]), p0);
-          p1 = __builtin_fmaf(w4[mt][g][e], relu(acc[mt][1][4 * g + e]), p1);
-        }
-    // lanes < 32 end with key lane of tile 0, lanes >= 32 with key lane of tile 1
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf], s == 0 ? f32x16{} : acc[mt], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kEps; ++j) {
+        const int el = s * kEps + j, mt = el / 16, i = el % 16;
+        part[j] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j]);
+      }
+      // keep this step's share of the epilogue in this step (IR passes would sink it below the MFMAs)
+#pragma unroll
+      for (int j = 0; j < kEps; ++j) asm volatile("" : "+v"(part[j]));
+      if (s + kPf < KS) bk[s % kPf] = lds_read16(lds_ptr(a0 ^ static_cast<uint32_t>(32 * (s + kPf))));
+      side(s);  // branch-free work of the caller, scheduled beside this step's MFMAs
+      // one MFMA, then half of the epilogue, the other MFMA(s), the other half, the next read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kEps, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT - 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kEps + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float p = part[0];
+#pragma unroll
+    for (int j = 1; j < kEps; ++j) p += part[j];
+    return p;
+  };
+  // The epilogue of `prev` alone (a row's last chunk, or a wave whose row has ended).
+  auto tile_drain = [&](const f32x16 (&prev)[MT]) -> float {
+    float part[kEps];
+#pragma unroll
+    for (int j = 0; j < kEps; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < kEps; ++j) {
+        const int el = s * kEps + j, mt = el / 16, i = el % 16;
+        part[j] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j]);
+      }
+    float p = part[0];
+#pragma unroll
+    for (int j = 1; j < kEps; ++j) p += part[j];
+    return p;
+  };
+  // lanes < 32 hold key lane of tile 0 in p0 and of tile 1 in p1 (heads with lane/32 = 0), lanes
+  // >= 32 the other heads: one swap leaves lane l with the full score of key l of the chunk
+  auto join = [](float p0, float p1) -> float {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
     return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   };
-  // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global.
+  // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global, in
+  // ascending token order. Branch-free, so that it can sit between MFMAs: lanes that do not take
+  // their key write it to a slot past the list. A list that may not take another chunk raises its
+  // flag for the next step.
   auto append = [&](int c, float score, int nbuf) {
     const int s_key = kb + c * kChunk + lane;
     const uint32_t key = score_key(score);
     const bool take = select && s_key >= b && s_key <= t && key >= thr;
     const uint64_t msk = ballot(take);
-    if (take) {
-      const int pos = cnt + lanes_below(msk);
-      keys[pos] = key;
-      cand[pos] = s_key;
-    }
+    const int pos = take ? cnt + lanes_below(msk) : kCap + lane;
+    keys[pos] = key;
+    cand[pos] = s_key;
     cnt += __popcll(msk);
-    // a full list is compacted at the start of the next step, before the next append
-    if (cnt > kCap - kChunk && lane == 0) s_need[nbuf][wave] = cnt;
+    s_need[nbuf][wave] = cnt > kCap - kChunk ? cnt : 0;  // every lane writes the same value
   };
+  auto no_side = [](int) {};
 
+  float p0_prev = 0.0f;  // tile-0 partial sums of the previous chunk
   issue_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
+  // Step c: tile 0 of chunk c (the next chunk's copies issued between its MFMAs), then the
+  // selections that the lists filled by step c-1 asked for, then tile 1 of chunk c with the append
+  // of chunk c-1 between its MFMAs. Step nchunks runs no MFMAs: it only finishes the last chunk.
+  for (int c = 0; c <= nchunks; ++c) {
     wait_vmem();    // this wave's copies of chunk c and its index stores are complete
     barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
-    int any_need = 0;
+    // flags of the lists that step c-1 filled: read now, used after tile 0
+    const i32x4 f0 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][0])));
+    const i32x4 f1 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][4])));
+    const bool act = select && c < nchunks && kb + c * kChunk <= t;      // row still has keys in chunk c
+    const bool act_prev = select && c > 0 && kb + (c - 1) * kChunk <= t;  // chunk c-1 still to finish
+    // copies of chunk c+1 (at c+1 == nchunks they fill a free slot with clamped rows, unused)
+    auto copies = [&](int st) {
+      if (st < CPW) issue_copy(c + 1, st);
+    };
+    float score_prev = 0.0f;
+    if (act) {
+      // a wave whose row ends before this chunk leaves its SIMD to the other wave there
+      score_prev = join(p0_prev, tile_step(c, 0, accA, accB, copies));
+    } else if (c + 1 < nchunks) {
 #pragma unroll
-    for (int w = 0; w < kIdxRows; ++w) any_need |= s_need[c & 1][w];
-    if (any_need) run_selections(kSelSlack, c & 1);  // uniform, rare
-    if (c + 1 < nchunks) issue_chunk(c + 1);
-    // a wave whose row ends before this chunk leaves its SIMD to the other wave there
-    if (select && kb + c * kChunk <= t) {
-      chunk_mfma(c);
-      append(c, acc_score(), (c + 1) & 1);
+      for (int j = 0; j < CPW; ++j) issue_copy(c + 1, j);
+    }
+    if ((f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0)
+      run_selections(kSelSlack, c & 1);  // uniform, rare
+    if (act) {
+      auto app = [&](int st) {
+        if (st == KS / 2) append(c - 1, score_prev, (c + 1) & 1);
+      };
+      p0_prev = tile_step(c, 1, accB, accA, app);
+    } else if (act_prev) {
+      append(c - 1, join(p0_prev, tile_drain(accB)), (c + 1) & 1);
     }
   }
 
@@ -612,7 +674,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-int index_candidate_capacity() { return kCap; }
+int index_candidate_capacity() { return kCandStride; }
 
 int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
 
