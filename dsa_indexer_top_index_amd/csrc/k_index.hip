@@ -251,6 +251,11 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     scratch[3 * NW + wave] = static_cast<uint32_t>(eq_w);
   }
   wait_vmem();    // this wave's index loads are complete before another wave overwrites them
+  // Consume every index load here, on every path: the stores below then need no wait each, and the
+  // compiler's wait insertion does not treat the loads as possibly outstanding at the caller's loop
+  // head (it would drain every memory operation, the next chunk's copies included, there).
+#pragma unroll
+  for (int u = 0; u < kSelU; ++u) asm volatile("" ::"v"(x[u]));
   barrier_lds();
   // kept: entries kept by the waves before this one; eq_seen: their equal entries
   int kept = 0, eq_seen = 0, total = 0, eq_before = 0;
@@ -282,11 +287,6 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     kept += __popcll(mk);
     eq_seen += __popcll(me);
   }
-  // Consume every index load on every path: otherwise the compiler's wait insertion treats them as
-  // possibly outstanding at the caller's loop head and drains all vector memory operations (the
-  // next chunk's copies included) before the first MFMA that reuses their registers.
-#pragma unroll
-  for (int u = 0; u < kSelU; ++u) asm volatile("" ::"v"(x[u]));
   *kept_out = total;
   return lo == 0 ? cur + 1u : cur;
 }
@@ -301,6 +301,12 @@ __device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, co
   constexpr int U = kCap / kWave;  // entries per lane: entry 64*u + lane
   static_assert(kCap % kWave == 0, "whole list rows");
   const int lane = lane_id();
+  // Every token index is loaded first: the loads complete while the radix levels run, and the
+  // output loop then issues stores only (a store between loads would make each later load wait
+  // for every earlier memory operation).
+  int32_t x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) x[u] = kWave * u + lane < cnt ? idxs[kWave * u + lane] : 0;
   uint32_t v[U];
   uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
@@ -361,32 +367,24 @@ __device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, co
       if (dcnt == static_cast<uint32_t>(need) || sh == 0) break;
     }
   }
-  // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur.
+  // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur. One
+  // wait covers every index load before the first store.
+#pragma unroll
+  for (int u = 0; u < U; ++u) asm volatile("" ::"v"(x[u]));
   const uint32_t hm = hi_mask(lo);
   int kept = 0, eq_seen = 0;
-  constexpr int G = 12;  // index loads in flight
-  static_assert(U % G == 0, "index load groups");
 #pragma unroll
-  for (int g = 0; g < U; g += G) {
-    int32_t x[G];
-#pragma unroll
-    for (int e = 0; e < G; ++e) {
-      const int i = kWave * (g + e) + lane;
-      x[e] = i < cnt ? idxs[i] : 0;
-    }
-#pragma unroll
-    for (int e = 0; e < G; ++e) {
-      const bool in = kWave * (g + e) + lane < cnt;
-      const uint32_t vh = v[g + e] & hm;
-      const bool gt = in && vh > cur;
-      const bool eq = in && vh == cur;
-      const uint64_t me = ballot(eq);
-      const bool keep = gt || (eq && eq_seen + lanes_below(me) < need);
-      const uint64_t mk = ballot(keep);
-      if (keep) out[kept + lanes_below(mk)] = x[e];
-      kept += __popcll(mk);
-      eq_seen += __popcll(me);
-    }
+  for (int u = 0; u < U; ++u) {
+    const bool in = kWave * u + lane < cnt;
+    const uint32_t vh = v[u] & hm;
+    const bool gt = in && vh > cur;
+    const bool eq = in && vh == cur;
+    const uint64_t me = ballot(eq);
+    const bool keep = gt || (eq && eq_seen + lanes_below(me) < need);
+    const uint64_t mk = ballot(keep);
+    if (keep) out[kept + lanes_below(mk)] = x[u];
+    kept += __popcll(mk);
+    eq_seen += __popcll(me);
   }
 }
 
