@@ -649,7 +649,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       run_selections(kSelSlack, c & 1);  // uniform, rare
     if (act) {
       auto app = [&](int st) {
-        if (st == KS / 2) append(c - 1, score_prev, (c + 1) & 1);
+        if (st == 0) append(c - 1, score_prev, (c + 1) & 1);  // early, so its index stores land before the next step's wait
       };
       p0_prev = tile_step(c, 1, accB, accA, app);
     } else if (act_prev) {
