@@ -17,16 +17,20 @@
 //    (asynchronous 16-byte global->LDS copies, double buffered, one barrier per chunk,
 //    XOR-swizzled granules so that the MFMA operand reads are bank-conflict free). All eight rows
 //    share every staged chunk.
-//  - Scores: v_mfma_f32_32x32x16_bf16 with the indexer heads as M (q_I of the row held in
-//    AGPRs), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head weight
-//    and the sum over heads happen in registers, and one permlane32 swap joins the two half-waves,
-//    leaving one full score per lane for 64 consecutive keys.
+//  - Scores: v_mfma_f32_32x32x16_bf16 with the indexer heads as M (q_I of the row in
+//    registers), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head
+//    weight and the sum over heads happen in registers, and one permlane32 swap joins the two
+//    half-waves, leaving one full score per lane for 64 consecutive keys. The loop is software
+//    pipelined by half a chunk: the MFMAs of one 32-key tile run interleaved with the VALU epilogue
+//    of the tile before it, and the next chunk's copies and the previous chunk's append sit
+//    between MFMAs too.
 //  - Top-k: scores become order-preserving uint32 keys. A key is appended to the row's candidate
 //    list (keys in LDS, token indices in the workspace) when it reaches the running threshold
-//    (ballot + mbcnt compaction, so the list stays in ascending token order). When a list nears
-//    capacity, the whole workgroup runs a radix select over its varying bits (LDS histograms, DPP
-//    scans) and a stable compaction keeps the k best (ties to the lower index), which raises the
-//    threshold. At the end each wave finishes its own row's exact selection.
+//    (ballot + mbcnt compaction, so the list stays in ascending token order; branch-free, lanes
+//    that drop their key write past the list). When a list nears capacity, the whole workgroup
+//    runs a radix select over its varying bits (LDS histograms, DPP scans) and a stable
+//    compaction keeps the k best (ties to the lower index), which raises the threshold. At the
+//    end each wave finishes its own row's exact selection.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
