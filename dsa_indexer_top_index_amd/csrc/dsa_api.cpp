@@ -33,7 +33,7 @@ struct Layout {
 Layout layout_of(const dsa_shape* s) {
   Layout L{};
   L.lnk_off = 0;
-  L.lnk_bytes = align_up(static_cast<size_t>(s->T) * s->d_I * 2);
+  L.lnk_bytes = align_up(static_cast<size_t>(s->T + dsa::kIdxKeyPad) * s->d_I * 2);
   const int64_t rows = rows_of(s);
   L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
   L.olat_off = L.lnk_bytes;

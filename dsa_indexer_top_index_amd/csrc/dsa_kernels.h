@@ -7,11 +7,13 @@
 namespace dsa {
 
 constexpr int kIdxMaxSeg = 16;  // row segments per indexer launch
+constexpr int kIdxKeyPad = 128; // LNk rows past T in the workspace: the indexer stages whole 64-key
+                                // chunks (up to two past the last key) and never scores those rows
 
 struct IndexArgs {
   const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
   const uint16_t* w;     // [nrows, H_I]
-  const uint16_t* LNk;   // [T, d_I]
+  const uint16_t* LNk;   // [T + kIdxKeyPad, d_I]; rows past T are staged but never scored
   int32_t* topk_idx;     // [nrows, k]
   const int32_t* cu;     // device cu_seqlens or nullptr
   int n_docs;

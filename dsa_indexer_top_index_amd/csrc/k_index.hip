@@ -14,9 +14,10 @@
 //    the longest and four of the shortest rows left, so that workgroups carry similar work. Rows
 //    with at most k causal keys are never scored: the prologue kernel writes them.
 //  - The LNk keys of the workgroup's causal range stream through LDS in chunks of 64 keys
-//    (asynchronous 16-byte global->LDS copies, double buffered, one barrier per chunk,
-//    XOR-swizzled granules so that the MFMA operand reads are bank-conflict free). All eight rows
-//    share every staged chunk.
+//    (asynchronous 16-byte global->LDS copies, double buffered, one barrier per chunk). A staged
+//    chunk is laid out by MFMA operand: each 1 KB block is the B operand of one K step of one
+//    32-key tile, so operand reads take constant offsets and are bank-conflict free. All eight
+//    rows share every staged chunk.
 //  - Scores: v_mfma_f32_32x32x16_bf16 with the indexer heads as M (q_I of the row in
 //    registers), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head
 //    weight and the sum over heads happen in registers, and one permlane32 swap joins the two
@@ -84,12 +85,6 @@ constexpr int kCandStride = kCap + 64;  // per-row list stride: the last 64 slot
 constexpr int kSelSlack = 64;    // extra entries a selection before the end of the row may keep
 constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
 
-// Granule (16 bytes) position inside a staged key chunk: rows of GPR granules, XOR-swizzled.
-template <int GPR>
-__device__ __forceinline__ int stage_granule(int key, int g) {
-  const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
-  return key * GPR + (g ^ f);
-}
 
 // max(x, +0) as an integer max on the bit pattern: negative values and -0 (sign bit set) give +0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -398,8 +393,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   constexpr int KS = D_I / 16;          // MFMA K steps
   constexpr int GPR = D_I / 8;          // 16-byte granules per key row
   constexpr int CHUNK_GRAN = kChunk * GPR;
-  constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies per chunk and wave
-  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0, "chunk copy split");
+  constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies (1 KB operand blocks) per chunk and wave
+  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && 2 * KS * kWave == CHUNK_GRAN, "chunk copy split");
 
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
   __shared__ uint32_t s_keys[kIdxRows][kCandStride];  // candidate score keys (token indices: global)
@@ -498,21 +493,24 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 
   const int nchunks = (ke - kb + kChunk - 1) / kChunk;
   const uint16_t* __restrict__ LNk = a.LNk;
-  const int T = a.T;
 
-  // Copy j of this wave's share of chunk c: 64 granules, LDS slot P holds granule g = gl ^ f(key)
-  // of key P / GPR (the swizzle of stage_granule).
+  // A staged chunk is laid out by MFMA operand: block n*KS + s (1 KB) holds, at lane i's 16 bytes,
+  // granule 2s + i/32 of key 32n + i%32, i.e. the B operand of K step s of 32-key tile n. Operand
+  // reads are then whole 1 KB blocks at constant offsets (bank-conflict free) and every copy fills
+  // one block. Copy j of this wave fills block CPW*wave + j; its per-lane source offset within a
+  // chunk is fixed, the chunk's first key row a scalar base.
+  uint32_t cp_off[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int blk_j = CPW * wave + j, n = blk_j / KS, st = blk_j % KS;
+    cp_off[j] = static_cast<uint32_t>(((32 * n + (lane & 31)) * D_I + 8 * (2 * st + (lane >> 5))) * 2);
+  }
+  // A chunk may reach past the last key row (up to two chunks past it, see kIdxKeyPad): those rows
+  // of the padded LNk are staged but never scored.
   auto issue_copy = [&](int c, int j) {
     const int K0 = kb + c * kChunk;
-    DSA_LDS uint8_t* base = (DSA_LDS uint8_t*)(stage[c & 1]);
-    const int P0 = (wave * (CHUNK_GRAN / kIdxRows)) + j * kWave;  // first granule of this wave copy
-    const int P = P0 + lane;
-    const int key = P / GPR;
-    const int gl = P % GPR;
-    const int f = (GPR == 16) ? (key & 15) : ((key >> 1) & 7);
-    const int g = gl ^ f;
-    const int row = min(K0 + key, T - 1);
-    copy16_to_lds(LNk + static_cast<int64_t>(row) * D_I + g * 8, base + P0 * 16);
+    const uint32_t lds = lds_addr_of(stage[c & 1]) + 1024 * (CPW * wave + j);
+    copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
   };
   auto issue_chunk = [&](int c) {
 #pragma unroll
@@ -544,14 +542,12 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // One N tile of chunk c into acc, interleaved with the epilogue of `prev`; returns this lane's
   // partial sum over its heads of the previous tile (one key column per lane).
   auto tile_step = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
-    // Granule 2s + lane/32 of key lane%32 sits at row base + 16 * ((2s + lane/32) ^ f(key)); with a
-    // 256-byte aligned row base that is (row base ^ 16 * (lane/32 ^ f)) ^ 32s. Tile 1 is 32 rows on.
-    uint32_t a0 = (lds_addr_of(stage[c & 1]) + n * (32 * GPR * 16) + (lane & 31) * (GPR * 16)) ^
-                  (16 * stage_granule<GPR>(lane & 31, lane >> 5) % (GPR * 16));
+    // the operand of K step s of tile n: block n*KS + s of the staged chunk, 16 bytes per lane
+    uint32_t a0 = lds_addr_of(stage[c & 1]) + n * (KS * 1024) + 16 * lane;
     asm volatile("" : "+v"(a0));
     bf16x8 bk[kPf];
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) bk[s] = lds_read16(lds_ptr(a0 ^ static_cast<uint32_t>(32 * s)));
+    for (int s = 0; s < kPf; ++s) bk[s] = lds_read16(lds_ptr(a0 + 1024 * s));
     float part[kEps];
 #pragma unroll
     for (int j = 0; j < kEps; ++j) part[j] = 0.0f;
@@ -569,7 +565,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       // keep this step's share of the epilogue in this step (IR passes would sink it below the MFMAs)
 #pragma unroll
       for (int j = 0; j < kEps; ++j) asm volatile("" : "+v"(part[j]));
-      if (s + kPf < KS) bk[s % kPf] = lds_read16(lds_ptr(a0 ^ static_cast<uint32_t>(32 * (s + kPf))));
+      if (s + kPf < KS) bk[s % kPf] = lds_read16(lds_ptr(a0 + 1024 * (s + kPf)));
       side(s);  // branch-free work of the caller, scheduled beside this step's MFMAs
       // one MFMA, then half of the epilogue, the other MFMA(s), the other half, the next read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
