@@ -42,10 +42,11 @@ def test_supported_shapes_and_workspace():
     assert dsa.dsa_check_shape(_shape()) == dsa.DSA_OK
     assert dsa.dsa_check_shape(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)) == dsa.DSA_OK
     ws = dsa.dsa_workspace_size(_shape())
-    # LN(k_I) (T x d_I bf16) plus the latent output of one row chunk (rows x H x 512 bf16)
-    assert ws == 4096 * 128 * 2 + 4096 * 96 * 512 * 2
+    # LN(k_I) ((T + 128 padding rows) x d_I bf16) plus the latent output of one row chunk
+    # (rows x H x 512 bf16)
+    assert ws == (4096 + 128) * 128 * 2 + 4096 * 96 * 512 * 2
     big = dsa.dsa_workspace_size(_shape(T=131072))
-    assert big == 131072 * 128 * 2 + 16384 * 96 * 512 * 2
+    assert big == (131072 + 128) * 128 * 2 + 16384 * 96 * 512 * 2
     assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
 
 
