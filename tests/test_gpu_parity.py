@@ -281,3 +281,44 @@ def test_sparse_mla_caller_indices():
     assert empty[7].all() and np.all(got[7] == 0)
     assert np.array_equal(np.isneginf(lse_g), empty)
     assert np.abs(lse_g[~empty] - ref["lse"][~empty]).max() < 5e-3
+
+
+@pytest.mark.parametrize("H", [96, 16])
+def test_sparse_mla_logit_growth_redo(H):
+    """Rows whose logits grow far beyond the first key tile's maximum (more than 2^64 in base 2):
+    the kernel redoes such a row against exact per-head maxima. One head's query is twice the
+    latent row of the query token itself, which is the last selected key of its row; the result
+    must still match the oracle, and the construction is checked to reach the redo condition."""
+    cfg = _small_cfg(f"growth{H}", 45 + H, [300], topk=96, H=H)
+    inp = tg.make_inputs(cfg)
+    T, k, big = cfg.T, cfg.topk, 5
+    kv32 = tg.bf16_to_f32(inp["kv"]).astype(np.float64)
+    q = inp["q"].copy()
+    q[:, big, :] = tg.f32_to_bf16((2.0 * kv32).astype(np.float32))  # exact: a power-of-two scale
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        keff = min(k, t + 1)
+        idx[t, :keff] = np.arange(t - keff + 1, t + 1, dtype=np.int32)  # ascending, the token itself last
+    # base-2 logits of the big head: first 16-key tile's maximum against the token's own key
+    log2e = 1.0 / np.log(2.0)
+    qb = tg.bf16_to_f32(q[:, big, :]).astype(np.float64)
+    gaps = []
+    for t in range(16, T):
+        first = idx[t, :16]
+        m0 = (cfg.softmax_scale * log2e * (kv32[first] @ qb[t])).max()
+        gaps.append(cfg.softmax_scale * log2e * (kv32[t] @ qb[t]) - m0)
+    gaps = np.array(gaps)
+    assert (gaps > 64.0).sum() > 200 and gaps.max() < 127.0, (gaps.min(), gaps.max())
+    dev = gu.to_device(dict(inp, q=q))
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_workspace(shape)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    _say(f"[gpu] sparse_mla_fwd logit-growth redo, H={H}")
+    dsa.dsa_sparse_mla_fwd(shape, dev["q"], dev["kv"], torch.from_numpy(idx).cuda(), dev["W_UV"], dev["gate"], out,
+                           ws, lse=lse)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_mla(np.arange(T), q, inp["kv"], idx, inp["W_UV"], inp["gate"], cfg.softmax_scale)
+    ok, err, mx = check_outputs(gu.bf16_tensor_to_f32(out), ref["out"])
+    assert ok, (err, mx)
+    assert np.abs(lse.cpu().numpy() - ref["lse"]).max() < 5e-3
