@@ -9,19 +9,22 @@
 //     o_lat[t,h,:] = softmax_j(l) . kv[s_j, 0:512]
 //
 // Kernel design: persistent workgroups, one per CU, each running query rows one after another
-// (longest rows first, dealt out zig-zag). Two kinds of waves meet in LDS, so every SIMD of the
-// CU runs matrix instructions:
-//  - Value waves (two): each owns the output accumulators of all heads for half of the 512 latent
-//    dims (384 FP32 per lane, two thirds of them in AGPRs). They issue every asynchronous 16-byte
-//    global->LDS copy of the gathered rows into a ring of seven 16-row tiles (copies run four
-//    tiles ahead), and compute O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: latent dims as M,
-//    32-head tiles as N, 16 keys as K. V is read straight from the natural row layout with
-//    ds_read_b64_tr_b16 and P from LDS. They run two tiles behind the score waves.
-//  - Score waves (two for 96 heads, 48 heads each; one for 16 heads): q fragments stay in
+// (longest rows first, dealt out zig-zag). Three kinds of waves meet in LDS; with 96 heads there
+// are eight, two per SIMD, so every SIMD runs matrix instructions:
+//  - Score waves (three for 96 heads, 32 heads each; one for 16 heads): q fragments stay in
 //    registers; S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 keys as M, 16-head tiles as N,
 //    K = 576); softmax numerators in FP32 (base 2) against a per-head reference maximum set by the
 //    first usable tile; P (bf16) goes to a two-slot LDS ring already in the value waves' operand
 //    layout.
+//  - Value waves (four for 96 heads, 128 latent dims each; two for 16 heads): each owns the
+//    output accumulators of all heads for its latent dims and computes O^T += V^T P^T on
+//    v_mfma_f32_32x32x16_bf16: latent dims as M, 32-head tiles as N, 16 keys as K. V is read
+//    straight from the natural row layout with ds_read_b64_tr_b16 and P from LDS. They run two
+//    tiles behind the score waves.
+//  - One copy wave issues every asynchronous 16-byte global->LDS copy of the gathered rows into a
+//    ring of seven 16-row tiles (copies run four tiles ahead) and does nothing else. A CU accepts
+//    about one 64-lane copy per 64 cycles, so a wave that issues copies stalls; with the copies on
+//    a wave of their own, no MFMA wave does.
 //  One barrier per tile hands both rings over. Each gathered row is read from memory once per
 //  query. The tile layout is column-major in 16-byte granules with a row XOR, so the QK operand
 //  reads and the transposed V reads are bank-conflict free and every address is affine in the
@@ -53,11 +56,15 @@ constexpr int kMaxIdx = 2048;
 // copy fills four columns of all 16 rows; the QK operand reads (16 rows, one column) and the
 // transposed V reads (4 rows x 4 columns per 16 lanes) both hit 16 distinct bank quads.
 
-// Head split: NS score waves of HS heads (NTS 16-head tiles each); the value waves hold MT
-// 32-head M tiles (rows of heads beyond H stay zero).
+// Roles: NS score waves of HS heads (NTS 16-head tiles each); NV value waves, each holding MT
+// 32-head M tiles (rows of heads beyond H stay zero) for 512/NV latent dims, NA of its
+// accumulator tiles in AGPRs; one copy wave. Waves go to SIMDs round-robin, so with 96 heads
+// (eight waves, two per SIMD) three SIMDs run a score wave beside a value wave and the fourth a
+// value wave beside the copy wave.
 template <int H> struct MlaRoles;
-template <> struct MlaRoles<96> { static constexpr int NS = 2, HS = 48, NTS = 3, MT = 3; };
-template <> struct MlaRoles<16> { static constexpr int NS = 1, HS = 16, NTS = 1, MT = 1; };
+template <> struct MlaRoles<96> { static constexpr int NS = 3, HS = 32, NTS = 2, MT = 3, NV = 4, NA = 8; };
+template <> struct MlaRoles<16> { static constexpr int NS = 1, HS = 16, NTS = 1, MT = 1, NV = 2, NA = 8; };
+template <int H> constexpr int mla_waves() { return MlaRoles<H>::NS + MlaRoles<H>::NV + 1; }
 
 // O^T += V^T P^T with the accumulator pinned to AGPRs. The compiler does not see this instruction's
 // hazards: the operands must not be written by VALU within 4 wait states before it (here they
@@ -77,15 +84,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int H>
-__global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
+__global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a) {
   using R = MlaRoles<H>;
   constexpr int NS = R::NS, HS = R::HS, NTS = R::NTS, MT = R::MT;
-  constexpr int NV = 2;                 // value waves, 256 latent dims each
-  constexpr int NW = NS + NV;
+  constexpr int NV = R::NV, NA = R::NA;
+  constexpr int NW = mla_waves<H>();  // score, value and copy waves
   constexpr int CT = kVDim / 32 / NV;   // 32-wide latent tiles per value wave
-  constexpr int CPV = 18 / NV;          // copies per value wave per tile
-  constexpr int MA = MT < 2 ? MT : 2;   // M tiles accumulated in AGPRs (the rest in VGPRs)
-  static_assert(CPV * (kAhead - 1) <= 63, "vmcnt range");
+  constexpr int kCopies = kTileBytes / 1024;  // 1 KB wave copies per tile, all by the copy wave
+  static_assert(kCopies * (kAhead - 1) <= 63, "vmcnt range");
+  static_assert(kCopies * 64 <= 4095 && kVDim % (32 * NV) == 0 && NA <= MT * CT, "role shapes");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[2][MT][64 * 16];  // P in MFMA A layout
@@ -369,36 +376,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
       load_row(w, std::integral_constant<int, 64 * NS>{}, (j + 1) & 1);
       load_q(w.r);
     }
-  } else {
+  } else if (wave < NS + NV) {
     // ================================ value wave ================================
     const int vw = wave - NS;
     int ntiles = w.ntiles;
-    // Gather: copy i (of a tile's 18) fills tile column 4*i + g16 with this lane's 16 bytes of
-    // row my_row; this wave does copies i = vw + 2c. The per-lane global offset of a tile is
-    // computed once (it includes 64*vw); the immediate offset 128*c moves both the global and the
-    // LDS address, so M0 carries the rest of the LDS displacement, 1024*i - 128*c.
-    const int my_row = i16 ^ (4 * g16);
-    auto tile_voff = [&](int t) -> uint32_t {
-      const int src = max(s_idx[t * kTileKeys + my_row], 0);
-      return static_cast<uint32_t>(src) * (kLatent * 2) + 16 * g16;
-    };
-    auto copy = [&](int t, uint32_t voff, auto c_const) {
-      constexpr int c = decltype(c_const)::value;
-      const uint32_t lds = ring + (t % kRing) * kTileBytes + 1024 * vw + (1024 - 64) * NV * c;
-      copy16_to_lds_imm<64 * NV * c>(a.kv, voff + 64 * vw, lds);
-    };
-    auto issue_tile = [&](int t) {
-      const uint32_t voff = tile_voff(t);
-      static_for<CPV>([&](auto c) { copy(t, voff, c); });
-    };
-    // Waits until this wave's copies of tile t have landed; later tiles stay in flight.
-    auto wait_tile = [&](int t) {
-      const int later = min(kAhead - 1, ntiles - 1 - t);
-      if (later >= 3) wait_vmem_le<3 * CPV>();
-      else if (later == 2) wait_vmem_le<2 * CPV>();
-      else if (later == 1) wait_vmem_le<CPV>();
-      else wait_vmem_le<0>();
-    };
     // V operand (transposed reads): keys 8*hh + s4 (+4), latent granule 4*(CT*vw + ct) + vc
     const int hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
     const int vc = 2 * chh + (q4 >> 1);
@@ -406,6 +387,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
     const uint32_t v_off2 = (vc * 16 + ((8 * hh + 4 + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1) + 1024 * CT * vw;
     const uint32_t p_rd = pbase + lane * 16;
 
+    // Accumulator tile (mt, ct) lives in AGPRs when mt*CT + ct < NA, else in VGPRs.
     f32x16 O[MT][CT];
     // Ties the accumulators to this program point, so that no access to them moves across the
     // wait-state padding placed next to it.
@@ -414,12 +396,13 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          if (mt < MA) asm volatile("" : "+a"(O[mt][ct]));
+          if (mt * CT + ct < NA) asm volatile("" : "+a"(O[mt][ct]));
           else asm volatile("" : "+v"(O[mt][ct]));
         }
     };
-    // One pass over the row; ntiles+2 barriers. mode 1 copies tiles only (the scores redo their
-    // maxima); modes 0 and 2 accumulate P V, two tiles behind the scores.
+    // One pass over the row; ntiles+2 barriers. mode 1 only keeps step (the scores redo their
+    // maxima); modes 0 and 2 accumulate P V, two tiles behind the scores. The copy wave has waited
+    // for tile t's copies before barrier t.
     auto value_pass = [&](int mode) {
       // a zero the compiler cannot see as a constant, so the accumulators' initial value is made
       // here in every row instead of being kept live across the row loop
@@ -431,30 +414,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         for (int ct = 0; ct < CT; ++ct) O[mt][ct] = f32x16{} + z;
       pin_acc();
       mfma_agpr_settle();
-#pragma unroll
-      for (int p = 0; p < kAhead; ++p)
-        if (p < ntiles) issue_tile(p);
       for (int t = 0;; ++t) {
-        if (t < ntiles) wait_tile(t);
-        barrier_lds();  // every copy of tile t has landed; P of tile t-2 is complete
-        const int tn = t + kAhead;  // copied into the slot of tile t-3
+        barrier_lds();  // tile t has landed; P of tile t-2 is complete
         if (t > 1 && mode != 1) {
           const int tv = t - 2;
           const uint32_t tb = ring + (tv % kRing) * kTileBytes;
           const uint32_t pp = p_rd + (tv & 1) * kPSlot;
-          const bool dma = tn < ntiles;
-          const uint32_t voff = dma ? tile_voff(tn) : 0u;
           u32x4 pa[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) pa[mt] = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(pp + mt * 1024));
           // V fragments two steps ahead of their MFMAs (see the K reads of the score waves)
           u32x2 v1[CT], v2[CT];
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
+          for (int ct = 0; ct < 2 && ct < CT; ++ct) {
             v1[ct] = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * ct));
             v2[ct] = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * ct));
           }
-          // the copies of tile tn go between the MFMAs, one after each group of three
           static_for<CT>([&](auto ct_c) {
             constexpr int ct = decltype(ct_c)::value;
             if constexpr (ct + 2 < CT) {
@@ -465,19 +440,12 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               // A = V^T (lane: latent dim, 8 keys), B = P^T (lane: head, 8 keys), D = O^T
-              if (mt < MA) mfma32_a(O[mt][ct], vb, pa[mt]);
+              if (mt * CT + ct < NA) mfma32_a(O[mt][ct], vb, pa[mt]);
               else
                 O[mt][ct] = mfma32(__builtin_bit_cast(bf16x8, vb), __builtin_bit_cast(bf16x8, pa[mt]), O[mt][ct]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (dma) {
-              copy(tn, voff, std::integral_constant<int, ct>{});
-              if constexpr (ct == CT - 1 && CPV > CT) copy(tn, voff, std::integral_constant<int, CT>{});
-            }
-            __builtin_amdgcn_sched_barrier(0);
           });
-        } else if (tn < ntiles) {
-          issue_tile(tn);
         }
         if (t == ntiles + 1) break;
       }
@@ -514,12 +482,67 @@ __global__ __launch_bounds__(256, 1) void k_sparse_mla(MlaArgs a) {
         }
       }
       wave_lds_sync();
+      // this wave's dims of each head row: kLph lanes of 16 bytes per row, kHpi rows at a time
+      constexpr int kDimsV = kVDim / NV, kLph = kDimsV / 8, kHpi = kWave / kLph;
       uint16_t* dst = a.o_lat + static_cast<int64_t>(w.rr) * H * kVDim;
-      const int c0 = 256 * vw + 8 * (lane & 31);  // 32 lanes cover this wave's 256 dims
-      for (int h = hh; h < H; h += 2) {
+      const int c0 = kDimsV * vw + 8 * (lane % kLph);
+      for (int h = lane / kLph; h < H; h += kHpi) {
         const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(ring + h * kStageRow + 2 * c0));
         *reinterpret_cast<u32x4*>(dst + h * kVDim + c0) = v;
       }
+      const int in = dispatch_row(j + 1);
+      if (in >= a.chunk_rows) break;
+      w = row_of(in);
+    }
+  } else {
+    // ================================ copy wave ================================
+    // Issues every global->LDS copy of the gathered rows and nothing else, so that no MFMA wave
+    // stalls on the vector-memory unit (a CU takes one 64-lane copy about every 64 cycles).
+    // Copy c (of a tile's 18) fills tile column 4*c + g16 with this lane's 16 bytes of row
+    // my_row. The per-lane global offset of a tile is computed once; the immediate offset 64*c
+    // moves both the global and the LDS address, so M0 carries the rest of the LDS displacement,
+    // 1024*c - 64*c.
+    int ntiles = w.ntiles;
+    const int my_row = i16 ^ (4 * g16);
+    auto issue_tile = [&](int t) {
+      const uint32_t voff = static_cast<uint32_t>(max(s_idx[t * kTileKeys + my_row], 0)) * (kLatent * 2) + 16 * g16;
+      const uint32_t base = ring + (t % kRing) * kTileBytes;
+      static_for<kCopies>([&](auto c_const) {
+        constexpr int c = decltype(c_const)::value;
+        copy16_to_lds_imm<64 * c>(a.kv, voff, base + (1024 - 64) * c);
+      });
+    };
+    // Waits until the copies of tile t have landed; later tiles stay in flight.
+    auto wait_tile = [&](int t) {
+      const int later = min(kAhead - 1, ntiles - 1 - t);
+      if (later >= 3) wait_vmem_le<3 * kCopies>();
+      else if (later == 2) wait_vmem_le<2 * kCopies>();
+      else if (later == 1) wait_vmem_le<kCopies>();
+      else wait_vmem_le<0>();
+    };
+    // One pass over the row's tiles; ntiles+2 barriers. Tile t+kAhead goes into the slot of tile
+    // t-3, which every wave is done with after barrier t.
+    auto copy_pass = [&]() {
+#pragma unroll
+      for (int p = 0; p < kAhead; ++p)
+        if (p < ntiles) issue_tile(p);
+      for (int t = 0;; ++t) {
+        if (t < ntiles) wait_tile(t);
+        barrier_lds();
+        if (t + kAhead < ntiles) issue_tile(t + kAhead);
+        if (t == ntiles + 1) break;
+      }
+    };
+    for (int j = 0;; ++j) {
+      barrier_lds();  // (A)
+      ntiles = w.ntiles;
+      copy_pass();
+      barrier_lds();  // (1)
+      if (s_flag) {   // the row is redone: once for the maxima, once for the numerators
+        copy_pass();
+        copy_pass();
+      }
+      barrier_lds();  // (2)
       const int in = dispatch_row(j + 1);
       if (in >= a.chunk_rows) break;
       w = row_of(in);
@@ -535,8 +558,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st) {
       cus < 1)
     return hipErrorInvalidValue;
   const dim3 grid(a.chunk_rows < cus ? a.chunk_rows : cus);
-  if (a.H == 96) hipLaunchKernelGGL((k_sparse_mla<96>), grid, dim3(64 * (MlaRoles<96>::NS + 2)), 0, st, a);
-  else if (a.H == 16) hipLaunchKernelGGL((k_sparse_mla<16>), grid, dim3(64 * (MlaRoles<16>::NS + 2)), 0, st, a);
+  if (a.H == 96) hipLaunchKernelGGL((k_sparse_mla<96>), grid, dim3(64 * mla_waves<96>()), 0, st, a);
+  else if (a.H == 16) hipLaunchKernelGGL((k_sparse_mla<16>), grid, dim3(64 * mla_waves<16>()), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
