@@ -164,11 +164,13 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
     bf16x8 qf[NTS][18];
     auto load_q = [&](int row) {
       // q fragments, B operand of S^T = K Q^T. lane: head sw*HS + 16*nt + i16, dims 32*st + 8*g16.
+      // a wave-uniform row base and a 32-bit per-lane offset, so no per-lane 64-bit pointers are kept
+      const uint8_t* qbase = reinterpret_cast<const uint8_t*>(a.q + static_cast<int64_t>(row) * a.H * kLatent);
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) {
-        const uint16_t* qrow = a.q + (static_cast<int64_t>(row) * a.H + sw * HS + 16 * nt + i16) * kLatent + 8 * g16;
+        const uint32_t off = static_cast<uint32_t>(((sw * HS + 16 * nt + i16) * kLatent + 8 * g16) * 2);
 #pragma unroll
-        for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qrow + 32 * st);
+        for (int st = 0; st < 18; ++st) qf[nt][st] = *reinterpret_cast<const bf16x8*>(qbase + off + 64 * st);
       }
       // the fragments live in AGPRs, which the MFMAs read directly; the VGPRs hold K fragments
 #pragma unroll
@@ -270,12 +272,21 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
         for (int nt = 0; nt < NTS; ++nt) l_part[nt] = 0.0f;
         f32x4 sprev[NTS];
         uint32_t vprev;
+        // The first kPre K fragments of the next tile, read during the last K steps of the current
+        // one (the copy wave waits for tile t+1 before barrier t), so that a tile's MFMAs start
+        // right after its barrier instead of after an LDS read.
+        bf16x8 kn[kPre];
         {
-          barrier_lds();  // tile 0 has landed
+          barrier_lds();  // tiles 0 and 1 have landed
           bf16x8 kf[18];
           load_k(0, kf);
           const int iv0 = s_idx[lane & 15];
           qk(kf, sprev);
+          {
+            const DSA_LDS uint8_t* tqn = lds_ptr(qk_base + (1 % kRing) * kTileBytes);
+#pragma unroll
+            for (int st = 0; st < kPre; ++st) kn[st] = lds_read16(tqn + 1024 * st);
+          }
           vprev = valid_bits(iv0);
           if constexpr (decltype(check_c)::value) {
             float tmax[NTS];
@@ -287,13 +298,16 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
           for (int nt = 0; nt < NTS; ++nt) msub[nt] = fmaxf(m_ref[nt], -3.0e38f);  // finite without usable keys
         }
         for (int t = 1; t < ntiles; ++t) {
-          barrier_lds();  // tile t has landed; P slot (t-1)%2 has been consumed
+          barrier_lds();  // tiles t and t+1 have landed; P slot (t-1)%2 has been consumed
           // K fragments are read kPre steps ahead of their MFMAs rather than all at once: right
           // after the barrier every wave of the CU reads LDS, and a burst would delay them all.
+          // The last kPre steps read the next tile's first fragments (past the row's last tile
+          // they read a ring slot that is not used).
           const DSA_LDS uint8_t* tq = lds_ptr(qk_base + (t % kRing) * kTileBytes);
+          const DSA_LDS uint8_t* tqn = lds_ptr(qk_base + ((t + 1) % kRing) * kTileBytes);
           bf16x8 kf[18];
 #pragma unroll
-          for (int st = 0; st < kPre; ++st) kf[st] = lds_read16(tq + 1024 * st);
+          for (int st = 0; st < kPre; ++st) kf[st] = kn[st];
           const int ivt = s_idx[t * kTileKeys + (lane & 15)];
           const uint32_t slot = ((t - 1) & 1) * kPSlot;
           bool ok[4];
@@ -304,6 +318,7 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
           for (int i = 0; i < 18 * NTS; ++i) {
             const int st = i / NTS, nt = i % NTS;
             if (nt == 0 && st + kPre < 18) kf[st + kPre] = lds_read16(tq + 1024 * (st + kPre));
+            if (nt == 0 && st + kPre >= 18) kn[st + kPre - 18] = lds_read16(tqn + 1024 * (st + kPre - 18));
             sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -512,9 +527,10 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
         copy16_to_lds_imm<64 * c>(a.kv, voff, base + (1024 - 64) * c);
       });
     };
-    // Waits until the copies of tile t have landed; later tiles stay in flight.
-    auto wait_tile = [&](int t) {
-      const int later = min(kAhead - 1, ntiles - 1 - t);
+    // Before barrier t: waits until the copies of tile u have landed; the tiles after u issued so
+    // far (up to tile t + kAhead - 1) stay in flight.
+    auto wait_tile = [&](int u, int t) {
+      const int later = min(t + kAhead - 1, ntiles - 1) - u;
       if (later >= 3) wait_vmem_le<3 * kCopies>();
       else if (later == 2) wait_vmem_le<2 * kCopies>();
       else if (later == 1) wait_vmem_le<kCopies>();
@@ -527,7 +543,10 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
       for (int p = 0; p < kAhead; ++p)
         if (p < ntiles) issue_tile(p);
       for (int t = 0;; ++t) {
-        if (t < ntiles) wait_tile(t);
+        // tiles t and t+1 land before barrier t: the score waves read tile t+1's first fragments
+        // during step t
+        if (t + 1 < ntiles) wait_tile(t + 1, t);
+        else if (t < ntiles) wait_tile(t, t);
         barrier_lds();
         if (t + kAhead < ntiles) issue_tile(t + kAhead);
         if (t == ntiles + 1) break;
