@@ -49,6 +49,7 @@ constexpr int kTileBytes = kTileKeys * kRowGran * 16;  // 18432: 18 wave copies 
 constexpr int kRing = 7;                               // tiles in the shared LDS ring
 constexpr int kAhead = kRing - 3;                      // tiles whose copies run ahead of the scores
 constexpr int kPre = 4;                                // K fragments read ahead in the score loop
+constexpr int kRun = 3;                                // K steps per head tile before switching tiles
 constexpr float kRestartGap = 64.0f;                   // log2 headroom of a head's reference maximum
 constexpr int kMaxIdx = 2048;
 
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
   constexpr int kCopies = kTileBytes / 1024;  // 1 KB wave copies per tile, all by the copy wave
   static_assert(kCopies * (kAhead - 1) <= 63, "vmcnt range");
   static_assert(kCopies * 64 <= 4095 && kVDim % (32 * NV) == 0 && NA <= MT * CT, "role shapes");
+  static_assert(18 % kRun == 0, "whole runs of K steps");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[kRing][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[2][MT][64 * 16];  // P in MFMA A layout
@@ -316,7 +318,10 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
           f32x4 sc[NTS];
 #pragma unroll
           for (int i = 0; i < 18 * NTS; ++i) {
-            const int st = i / NTS, nt = i % NTS;
+            // runs of kRun K steps per head tile: a 16x16x32 MFMA that follows one with the same
+            // accumulator issues faster than one that switches accumulators
+            const int blk = i / (kRun * NTS), r = i % (kRun * NTS);
+            const int nt = r / kRun, st = kRun * blk + r % kRun;
             if (nt == 0 && st + kPre < 18) kf[st + kPre] = lds_read16(tq + 1024 * (st + kPre));
             if (nt == 0 && st + kPre >= 18) kn[st + kPre - 18] = lds_read16(tqn + 1024 * (st + kPre - 18));
             sc[nt] = mfma16(kf[st], qf[nt][st], st == 0 ? f32x4{} : sc[nt]);
