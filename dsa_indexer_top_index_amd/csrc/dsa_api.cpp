@@ -37,7 +37,9 @@ Layout layout_of(const dsa_shape* s) {
   const int64_t rows = rows_of(s);
   L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
   L.olat_off = L.lnk_bytes;
-  L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * s->H * 512 * 2);
+  // o_lat of a chunk of rows; the indexer's candidate lists use the same space, row for row
+  const size_t per_row = std::max<size_t>(static_cast<size_t>(s->H) * 512 * 2, static_cast<size_t>(dsa::index_candidate_capacity()) * 4);
+  L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * per_row);
   L.total = L.olat_off + L.olat_bytes;
   return L;
 }
@@ -109,7 +111,7 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   // attention writes it only after the indexer is done); rows go in launches that fit there.
   a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.olat_off);
   const int64_t per_row = static_cast<int64_t>(dsa::index_candidate_capacity()) * 4;
-  const int64_t cap_rows = static_cast<int64_t>(L.olat_bytes) / per_row;  // >= 1: 16 KB of o_lat per row at least
+  const int64_t cap_rows = static_cast<int64_t>(L.olat_bytes) / per_row;  // >= chunk rows, by the layout
   if (cap_rows <= 0) return DSA_ERR_WORKSPACE;
   if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st) != hipSuccess)
     return DSA_ERR_LAUNCH;

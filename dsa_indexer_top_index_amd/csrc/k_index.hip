@@ -80,8 +80,16 @@ __device__ __forceinline__ void key_layernorm_block(const uint16_t* __restrict__
 
 // ---------------------------------------------------------------------------------------------
 constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
-constexpr int kCap = 3840;        // candidate capacity per row (>= k + kSelSlack + 2 * kChunk for k <= 2048)
-constexpr int kCandStride = kCap + 64;  // per-row list stride: the last 64 slots take the lanes an append drops
+constexpr int kCap = 3840;        // candidate capacity of a row's list (>= k + kSelSlack + 2 * kChunk for k <= 2048)
+constexpr int kListSlots = kCap + 64;   // LDS slots per list: the last 64 take the lanes an append drops
+// Waves w and w + 4 share a SIMD and their lists sit side by side. When a block pairs long and
+// short rows, a long row that would overflow kCap may take kCapLong slots of the pair's space if
+// its partner row fits in the rest (kCapShort), so that it needs no selection before its end.
+constexpr int kCapLong = 4096;
+constexpr int kCapShort = 2 * kListSlots - (kCapLong + 64) - 64;
+constexpr int kCandStride = kCapLong + 64;  // per-row stride of the candidate token indices (global)
+static_assert(kCapShort >= 2048 + 64 + 2 * 64, "a short list still holds k + slack + two chunks");
+static_assert(kCap % 256 == 0 && kCapLong % 256 == 0 && kCapShort % 256 == 0, "the final selection copies 256 indices at a time");
 constexpr int kSelSlack = 64;    // extra entries a selection before the end of the row may keep
 constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
 
@@ -138,10 +146,12 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t x) {
 template <int NW>
 __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
                                                    DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out) {
-  constexpr int kSelU = (kCap + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
+  constexpr int kSelU = (kCapLong + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  // This wave's slice of the list: [s0, s0 + kSelU*64), entries s0 + 64*u + lane.
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  // This wave's slice of the list: [s0, s0 + kSelU*64), entries s0 + 64*u + lane. Slots past the
+  // list are skipped with uniform branches.
   const int s0 = wave * kWave * kSelU;
   uint32_t v[kSelU];
   int32_t x[kSelU];
@@ -150,8 +160,12 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
   for (int u = 0; u < kSelU; ++u) {
     const int i = s0 + kWave * u + lane;
     in[u] = i < cnt;
-    v[u] = in[u] ? keys[i] : 0u;
-    x[u] = in[u] ? idxs[i] : 0;  // global loads, needed only by the compaction
+    v[u] = 0u;
+    x[u] = 0;
+    if (s0 + kWave * u < cnt && in[u]) {
+      v[u] = keys[i];
+      x[u] = idxs[i];  // global loads, needed only by the compaction
+    }
   }
   uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
@@ -196,7 +210,7 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
       const int hn = hb == 2 ? 0 : hb + 1;
 #pragma unroll
       for (int u = 0; u < kSelU; ++u)
-        if (in[u] && (v[u] & hm) == cur)
+        if (s0 + kWave * u < cnt && in[u] && (v[u] & hm) == cur)
           __hip_atomic_fetch_add(h_cur + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       for (int i = threadIdx.x; i < 256; i += NW * kWave) hist[256 * hn + i] = 0u;
       barrier_lds();
@@ -290,37 +304,59 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
   return lo == 0 ? cur + 1u : cur;
 }
 
-// Exact top k of one row's cnt candidates (k < cnt <= kCap) by one wave, without workgroup
-// barriers, so that every wave can finish its own row at the same time. Keys in LDS and token
-// indices in global memory (idxs), both in ascending token order; the k kept indices go to
-// out[0 .. k) in that order (keys desc, ties to the lower index). hist: 256 words of LDS that
-// only this wave uses.
-__device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, const int32_t* __restrict__ idxs,
+// Exact top k of one row's cnt candidates (k < cnt <= kCapLong) by one wave, without workgroup
+// barriers, so that every wave can finish its own row at the same time. Keys in LDS (list, cap
+// words rounded up to 256) and token indices in global memory (idxs), both in ascending token
+// order; the k kept indices go to out[0 .. k) in that order (keys desc, ties to the lower index).
+// hist: 256 words of LDS that only this wave uses.
+//
+// A CU issues about one vector-memory instruction per 64 cycles, and the eight waves of a block
+// finish their rows together, so the token indices move in 16-byte pieces: once the keys are in
+// registers, the indices are copied into the list's own LDS slots (1 KB per copy), compacted
+// there in place, and the k kept ones leave in 16-byte stores.
+__device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const int32_t* __restrict__ idxs,
                                                 DSA_LDS uint32_t* hist, int cnt, int k, int32_t* __restrict__ out) {
-  constexpr int U = kCap / kWave;  // entries per lane: entry 64*u + lane
-  static_assert(kCap % kWave == 0, "whole list rows");
+  constexpr int U = kCapLong / kWave;  // entries per lane: entry 64*u + lane
+  constexpr int G = 8;                 // slots per group
+  static_assert(kCapLong % kWave == 0 && U % G == 0, "whole list rows and groups");
   const int lane = lane_id();
-  // Every token index is loaded first: the loads complete while the radix levels run, and the
-  // output loop then issues stores only (a store between loads would make each later load wait
-  // for every earlier memory operation).
-  int32_t x[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) x[u] = kWave * u + lane < cnt ? idxs[kWave * u + lane] : 0;
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  // Slots go in groups of G; the groups past the list are skipped by uniform branches, and within
+  // a group nothing branches, so that the LDS reads of a group issue back to back and wait once.
+  // The pad entries of the last group (past cnt) hold key 0: they take part in a level only if
+  // key 0 matches its prefix, and each histogram then takes them back out of bin 0.
+  const int ng = (cnt + G * kWave - 1) / (G * kWave);
+  const uint32_t pad = static_cast<uint32_t>(G * kWave * ng - cnt);
   uint32_t v[U];
   uint32_t o = 0u, a = 0xffffffffu;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool in = kWave * u + lane < cnt;
-    v[u] = in ? keys[kWave * u + lane] : 0u;
-    o |= v[u];
-    a &= in ? v[u] : 0xffffffffu;
+  for (int g = 0; g < U / G; ++g) {
+    if (g < ng) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[G * g + i] = list[min(kWave * (G * g + i) + lane, cnt - 1)];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int u = G * g + i;
+        const bool in = kWave * u + lane < cnt;
+        v[u] = in ? v[u] : 0u;
+        o |= v[u];
+        a &= in ? v[u] : 0xffffffffu;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[G * g + i] = 0u;
+    }
   }
+  wave_lds_sync();  // every key is in registers before the copies below overwrite the list
+  // entries [256j, 256j + 256) of idxs to list + 256j; they land while the radix levels run
+  for (int j = 0; 256 * j < cnt; ++j) copy16_to_lds(idxs + 256 * j + 4 * lane, list + 256 * j);
   o = wave_or(o);
   a = wave_and(a);
   const uint32_t varying = o ^ a;
   int lo;  // bits >= lo of the k-th key are known: cur
   uint32_t cur;
   int need = k;  // how many of the entries matching cur (in list order) are kept
+  bool whole_bin = false;  // every entry matching cur is kept: the kept entries are those >= cur
   if (varying == 0u) {
     lo = 0;
     cur = a;
@@ -328,20 +364,29 @@ __device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, co
     lo = 32 - __clz(static_cast<int>(varying));
     cur = a & hi_mask(lo);
     while (true) {
+      // digit: bits [sh, sh + 8) of the key; where lo < 8 the bits [lo, 8) are cur's in every
+      // matching entry, so the digits still order the matching entries
       const int sh = lo > 8 ? lo - 8 : 0;
-      const uint32_t dmask = (1u << (lo - sh)) - 1u;
       const uint32_t hm = hi_mask(lo);
 #pragma unroll
       for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0u;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (kWave * u + lane < cnt && (v[u] & hm) == cur)
-          __hip_atomic_fetch_add(hist + ((v[u] >> sh) & dmask), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      for (int g = 0; g < U / G; ++g) {
+        if (g < ng) {
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            const uint32_t e = v[G * g + i];
+            if ((e & hm) == cur) __hip_atomic_fetch_add(hist + __builtin_amdgcn_ubfe(e, sh, 8), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+          }
+        }
+      }
+      const uint32_t pad0 = cur == 0u ? pad : 0u;  // the pad entries (digit 0) matched
       wave_lds_sync();
       // lane owns bins 4*lane .. 4*lane+3; find the bin holding the need-th largest entry
       uint32_t h[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
+      if (lane == 0) h[0] -= pad0;
       const uint32_t mine = h[0] + h[1] + h[2] + h[3];
       uint32_t above = wave_suffix_sum(mine) - mine;
       int found = -1;
@@ -363,27 +408,68 @@ __device__ __forceinline__ void wave_select_out(const DSA_LDS uint32_t* keys, co
       need -= static_cast<int>(dab);
       cur |= static_cast<uint32_t>(d) << sh;
       lo = sh;
-      if (dcnt == static_cast<uint32_t>(need) || sh == 0) break;
+      if (dcnt == static_cast<uint32_t>(need)) {
+        whole_bin = true;
+        break;
+      }
+      if (sh == 0) break;
     }
   }
-  // Stable compaction: keep (key_hi > cur) and the first `need` entries with key_hi == cur. One
-  // wait covers every index load before the first store.
+  // Stable compaction in place, a group at a time: the group's indices are read before any of its
+  // kept entries is written, and a kept entry moves to a slot at or below its own, so no entry is
+  // overwritten before it is read.
+  wait_vmem();
+  int kept = 0;
+  if (whole_bin && cur != 0u) {
+    // keep exactly the entries >= cur (the bits of cur below lo are zero, so (v & hi_mask(lo)) >=
+    // cur exactly when v >= cur); the pad keys (0) are below cur
 #pragma unroll
-  for (int u = 0; u < U; ++u) asm volatile("" ::"v"(x[u]));
-  const uint32_t hm = hi_mask(lo);
-  int kept = 0, eq_seen = 0;
+    for (int g = 0; g < U / G; ++g) {
+      if (g < ng) {
+        uint32_t x[G];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool in = kWave * u + lane < cnt;
-    const uint32_t vh = v[u] & hm;
-    const bool gt = in && vh > cur;
-    const bool eq = in && vh == cur;
-    const uint64_t me = ballot(eq);
-    const bool keep = gt || (eq && eq_seen + lanes_below(me) < need);
-    const uint64_t mk = ballot(keep);
-    if (keep) out[kept + lanes_below(mk)] = x[u];
-    kept += __popcll(mk);
-    eq_seen += __popcll(me);
+        for (int i = 0; i < G; ++i) x[i] = list[kWave * (G * g + i) + lane];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const bool keep = v[G * g + i] >= cur;
+          const uint64_t mk = ballot(keep);
+          if (keep) list[kept + lanes_below(mk)] = x[i];
+          kept += __popcll(mk);
+        }
+      }
+    }
+  } else {
+    // keep (key_hi > cur) and the first `need` entries with key_hi == cur (ties: lower index)
+    const uint32_t hm = hi_mask(lo);
+    int eq_seen = 0;
+#pragma unroll
+    for (int g = 0; g < U / G; ++g) {
+      if (g < ng) {
+        uint32_t x[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) x[i] = list[kWave * (G * g + i) + lane];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          const int u = G * g + i;
+          const bool in = kWave * u + lane < cnt;
+          const uint32_t vh = v[u] & hm;
+          const bool eq = in && vh == cur;
+          const uint64_t me = ballot(eq);
+          const bool keep = (in && vh > cur) || (eq && eq_seen + lanes_below(me) < need);
+          const uint64_t mk = ballot(keep);
+          if (keep) list[kept + lanes_below(mk)] = x[i];
+          kept += __popcll(mk);
+          eq_seen += __popcll(me);
+        }
+      }
+    }
+  }
+  wave_lds_sync();
+  if ((k & 3) == 0) {  // rows of out are 16-byte aligned
+    for (int e = 4 * lane; e < k; e += 4 * kWave)
+      *reinterpret_cast<u32x4*>(out + e) = *reinterpret_cast<const DSA_LDS u32x4*>(list + e);
+  } else {
+    for (int e = lane; e < k; e += kWave) out[e] = static_cast<int32_t>(list[e]);
   }
 }
 
@@ -397,13 +483,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && 2 * KS * kWave == CHUNK_GRAN, "chunk copy split");
 
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
-  __shared__ uint32_t s_keys[kIdxRows][kCandStride];  // candidate score keys (token indices: global)
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kIdxRows * kListSlots];  // candidate score keys (token indices: global)
   __shared__ uint32_t s_hist[3 * 256];
   // Candidate count of a row whose list must be compacted, else 0. Step c reads buffer c % 2 after
   // its barrier while appends of that step write buffer (c + 1) % 2, so no wave can see a flag
   // that another wave of the same step has not seen.
   __shared__ __attribute__((aligned(16))) int s_need[2][kIdxRows];
   __shared__ int s_row[kIdxRows];                 // local row of each wave
+  __shared__ int s_lbase[kIdxRows];               // first LDS slot of each wave's list
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
   __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
 
@@ -436,10 +523,24 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   const int b = a.seg_b[sg];
   const bool select = has_row;
   int32_t* out = a.topk_idx + static_cast<int64_t>(r) * k;
+  // The lists of waves w and w + 4 share 2 * kListSlots slots; kCap each, unless a paired long row
+  // has more keys than that and its short partner fits in kCapShort.
+  const int pair_base = 2 * (wave & 3) * kListSlots;
+  int lbase = pair_base + (wave >> 2) * kListSlots, cap = kCap;
+  if (a.paired) {
+    const int h = (m + 1) >> 1, p = 4 * blk + (wave & 3);
+    const int n_long = p < h ? a.row0 + A + (m - 1 - p) - b + 1 : 0;
+    const int n_short = p < m - h ? a.row0 + A + p - b + 1 : 0;
+    if (n_long > kCap && n_short <= kCapShort) {
+      lbase = wave < 4 ? pair_base : pair_base + kCapLong + 64;
+      cap = wave < 4 ? kCapLong : kCapShort;
+    }
+  }
   if (lane == 0) {
     s_need[0][wave] = 0;
     s_need[1][wave] = 0;
     s_row[wave] = r;
+    s_lbase[wave] = lbase;
   }
   __syncthreads();
   const int kb = b, ke = a.row0 + A + i_top + 1;
@@ -466,7 +567,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qa[mt][s]));
 
   // LDS-typed pointers, so that every access is a ds_ instruction; candidate indices in global memory
-  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[wave][0])));
+  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[lbase])));
   DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[0])));
   DSA_LDS uint32_t* sel_scratch = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_sel[0])));
   int32_t* cand = a.cand + static_cast<int64_t>(r - a.row_lo) * kCandStride;
@@ -478,7 +579,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     for (int rw = 0; rw < kIdxRows; ++rw) {
       const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
-      DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[rw][0])));
+      DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[s_lbase[rw]])));
       int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCandStride;
       int kept = 0;
       const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
@@ -605,18 +706,19 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   };
   // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global, in
   // ascending token order. Branch-free, so that it can sit between MFMAs: lanes that do not take
-  // their key write it to a slot past the list. A list that may not take another chunk raises its
-  // flag for the next step.
+  // their key write it to a slot past the list. A list that may not take another chunk while the
+  // row still has keys in chunk c + 1 raises its flag for the next step.
   auto append = [&](int c, float score, int nbuf) {
     const int s_key = kb + c * kChunk + lane;
     const uint32_t key = score_key(score);
     const bool take = select && s_key >= b && s_key <= t && key >= thr;
     const uint64_t msk = ballot(take);
-    const int pos = take ? cnt + lanes_below(msk) : kCap + lane;
+    const int pos = take ? cnt + lanes_below(msk) : cap + lane;
     keys[pos] = key;
     cand[pos] = s_key;
     cnt += __popcll(msk);
-    s_need[nbuf][wave] = cnt > kCap - kChunk ? cnt : 0;  // every lane writes the same value
+    const bool more = kb + (c + 1) * kChunk <= t;
+    s_need[nbuf][wave] = cnt > cap - kChunk && more ? cnt : 0;  // every lane writes the same value
   };
   auto no_side = [](int) {};
 
