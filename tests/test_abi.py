@@ -48,6 +48,12 @@ def test_supported_shapes_and_workspace():
     big = dsa.dsa_workspace_size(_shape(T=131072))
     assert big == (131072 + 128) * 128 * 2 + 16384 * 96 * 512 * 2
     assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
+    # with 16 heads a row's latent output (16 KB) is smaller than the indexer's per-row candidate
+    # list of token indices (4,160 int32), which shares that space: the larger of the two counts
+    tiny = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16))
+    assert tiny == (1024 + 128) * 64 * 2 + 1024 * 4160 * 4
+    one = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16, q_begin=1000, q_end=1001))
+    assert one == (1024 + 128) * 64 * 2 + 4160 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
