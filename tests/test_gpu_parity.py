@@ -15,7 +15,8 @@ import dsa_indexer_top_index_amd as dsa
 import oracle
 import testgen as tg
 from tests import gpu_util as gu
-from tests.parity import check_index_row, check_outputs
+from tests.parity import (check_index_row, check_outputs, format_stats, gamma, lower_index_rule_violations,
+                          new_stats)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,11 +34,13 @@ def _check_rows(cfg, keys, qrows, rows, idx_gpu, out_gpu, lse_gpu=None, LNk=None
     w = qrows["w"].reshape(len(rows), cfg.H_I)
     o_idx, theta, keff = oracle.topk(rows, q_I, w, LNk, cu, cfg.topk)
     bad = []
+    st = new_stats()
     for j, t in enumerate(rows):
         b = oracle.doc_begin(cu, t)
-        msg = check_index_row(idx_gpu[j], o_idx[j], keff[j], b, t, cfg.topk, q_I[j], w[j], LNk, theta[j])
+        msg = check_index_row(idx_gpu[j], o_idx[j], keff[j], b, t, cfg.topk, q_I[j], w[j], LNk, theta[j], stats=st)
         if msg:
             bad.append(msg)
+    _say(f"[gpu] {cfg.name} index rule: {format_stats(st)}")
     assert not bad, f"{len(bad)} index rows fail, first: {bad[:3]}"
     q = qrows["q"].reshape(len(rows), cfg.H, 576)
     gate = qrows["gate"].reshape(len(rows), cfg.H)
@@ -45,7 +48,9 @@ def _check_rows(cfg, keys, qrows, rows, idx_gpu, out_gpu, lse_gpu=None, LNk=None
     ok, err, mx = check_outputs(out_gpu, ref["out"])
     assert ok, f"output max err {err} > 2e-2 * {mx}"
     if lse_gpu is not None:
-        assert np.abs(lse_gpu - ref["lse"]).max() < 5e-3
+        assert np.array_equal(np.isneginf(lse_gpu), np.isneginf(ref["lse"]))
+        fin = np.isfinite(ref["lse"])
+        assert np.abs(lse_gpu[fin] - ref["lse"][fin]).max() < 5e-3
     same = np.array([set(idx_gpu[j]) == set(o_idx[j]) for j in range(len(rows))])
     return same.mean(), err / mx
 
@@ -130,13 +135,23 @@ def _sample(cfg, extra, n=24, seed=0):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["t4096", "t8192"])
-def test_single_document_full_size(name):
+def test_t4096_full_size():
     """Sampled rows plus every 8th row of 3584..4095 (rows whose candidate lists first fill near
     their last key chunk) and of the last 128 rows; the structure of every row."""
-    cfg, keys, dev = _inputs(name)
+    cfg, keys, dev = _inputs("t4096")
     band = list(range(3584, 4096, 8)) + list(range(cfg.T - 128, cfg.T, 8))
     rows = _sample(cfg, [0, 1, 2047, 2048, 2049, cfg.T // 2, cfg.T - 2, cfg.T - 1] + band)
+    _run_and_check(cfg, keys, dev, rows)
+
+
+def test_t8192_full_size():
+    """Rows whose candidate lists first overflow (n_t around 3,840..3,904 keys, i.e. the list capacity
+    plus one or two chunks), rows that select several times mid-stream (the last 512 rows), the
+    longest rows, and a random sample; the structure of every row."""
+    cfg, keys, dev = _inputs("t8192")
+    first_fill = list(range(3800, 3940, 4))
+    many_sel = list(range(cfg.T - 512, cfg.T, 16)) + list(range(cfg.T - 16, cfg.T))
+    rows = _sample(cfg, [0, 1, 2047, 2048, 2049, 4095, 4096, 6000] + first_fill + many_sel, n=16)
     _run_and_check(cfg, keys, dev, rows)
 
 
@@ -168,9 +183,14 @@ def test_packed_full_size():
 
 
 def test_long_context_131072_sampled():
+    """Both sides of every 2,048-row boundary (this covers the attention's row chunks, whatever their
+    power-of-two size from 2,048 up), the first selected rows, the last 8 rows and a random sample;
+    indices, outputs and lse against the oracle, and the structure of every row."""
     cfg, keys, dev = _inputs("t131072")
-    rows = _sample(cfg, [0, 2047, 2048, 2049, 65535, 131070, 131071], n=5)
-    _run_and_check(cfg, keys, dev, rows, with_lse=False)
+    bounds = [x for j in range(1, cfg.T // 2048) for x in (2048 * j - 1, 2048 * j)]
+    rows = _sample(cfg, [0, 1, 2049, 2050] + bounds + list(range(cfg.T - 8, cfg.T)), n=16)
+    assert len(rows) >= 128
+    _run_and_check(cfg, keys, dev, rows, with_lse=True)
     _cache.clear()
     torch.cuda.empty_cache()
 
@@ -217,7 +237,7 @@ def _small_cfg(name, seed, lens, topk, H=16, H_I=4, d_I=64, **kw):
     return tg.Config(name, seed, lens, topk=topk, H=H, H_I=H_I, d_I=d_I, w_scale=kw.pop("w_scale", 0.5), **kw)
 
 
-@pytest.mark.parametrize("case", ["T1", "k1", "k3-negw", "ties", "const-keys"])
+@pytest.mark.parametrize("case", ["T1", "k1", "k3-negw", "ties", "const-keys", "few-keys", "few-keys-96"])
 def test_edge_cases(case):
     if case == "T1":
         cfg = _small_cfg("T1", 40, [1], topk=1, H=96, H_I=64, d_I=128)
@@ -225,6 +245,9 @@ def test_edge_cases(case):
         cfg = _small_cfg("k1", 41, [300], topk=1)
     elif case == "k3-negw":
         cfg = _small_cfg("k3", 42, [97, 200], topk=3, w_scale=-1.0)
+    elif case == "few-keys-96":
+        cfg = _small_cfg(case, 46, [1500, 700], topk=300, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                         W_UV_std=0.02)
     else:
         cfg = _small_cfg(case, 43, [333], topk=40)
     inp = tg.make_inputs(cfg)
@@ -232,6 +255,8 @@ def test_edge_cases(case):
         inp["k_I"][1::3] = inp["k_I"][0::3][: len(inp["k_I"][1::3])]
     if case == "const-keys":  # LN of a constant row is 0: every score is exactly +0
         inp["k_I"][:] = tg.f32_to_bf16(np.full(inp["k_I"].shape, 0.5, np.float32))
+    if case.startswith("few-keys"):  # 7 distinct key rows repeated: every k-th score is an exact tie
+        inp["k_I"][:] = inp["k_I"][np.arange(cfg.T) % 7]
     dev = gu.to_device(inp)
     _say(f"[gpu] edge case {case}: T={cfg.T} k={cfg.topk}")
     res = gu.run_fused(cfg, dev, with_lse=True)
@@ -241,11 +266,42 @@ def test_edge_cases(case):
     qrows = {k: inp[k].reshape(cfg.T, -1) for k in ["q_I", "w", "q", "gate"]}
     idx = res["topk_idx"].cpu().numpy()
     _check_rows(cfg, keys, qrows, rows, idx, gu.bf16_tensor_to_f32(res["out"]), res["lse"].cpu().numpy())
-    if case in ("ties", "const-keys"):  # exact ties must resolve exactly as the oracle does
+    if case in ("ties", "const-keys") or case.startswith("few-keys"):
+        # Equal scores must go to the lower index: no kept key may follow a dropped key of equal
+        # oracle score (the duplicated keys get bit-identical scores on both sides).
         LNk = oracle.key_layernorm(inp["k_I"], cfg.ln_eps)
-        o_idx, _, _ = oracle.topk(rows, inp["q_I"], inp["w"], LNk, cfg.cu_seqlens, cfg.topk)
+        o_idx, theta, keff = oracle.topk(rows, inp["q_I"], inp["w"], LNk, cfg.cu_seqlens, cfg.topk)
+        viol = []
+        for t in rows:
+            b = oracle.doc_begin(cfg.cu_seqlens, t)
+            if t - b + 1 <= cfg.topk:
+                continue
+            S = oracle.index_scores(inp["q_I"][t], inp["w"][t], LNk, b, t)
+            viol += [(int(t),) + v for v in lower_index_rule_violations(idx[t], S, b, t)]
+        assert not viol, f"lower-index tie rule broken: {viol[:5]}"
         if case == "const-keys":
             assert np.array_equal(idx, o_idx)
+        if case.startswith("few-keys"):
+            # At most seven distinct scores per row, and the k-th one is shared by a large group of
+            # keys, so the tie rule alone decides which of the group are kept. Where every other
+            # distinct score lies far from theta (beyond the near-tie band, or beyond the FP32 floor
+            # when theta is 0) the set is fixed exactly and must equal the oracle's.
+            exact, long_rows = 0, 0
+            for j, t in enumerate(rows):
+                b = oracle.doc_begin(cfg.cu_seqlens, t)
+                if t - b + 1 <= cfg.topk:
+                    continue
+                long_rows += 1
+                S = oracle.index_scores(inp["q_I"][t], inp["w"][t], LNk, b, t).astype(np.float64)
+                th = float(theta[j])
+                others = np.unique(S[S != th])
+                sep = 1e-3 * abs(th) if th != 0 else 2 * gamma(cfg.d_I + cfg.H_I) * float(
+                    oracle.index_score_scale(inp["q_I"][t], inp["w"][t], LNk, b, t).max())
+                if others.size == 0 or np.min(np.abs(others - th)) > sep:
+                    exact += 1
+                    assert np.array_equal(idx[t], o_idx[j]), f"row {t}: tie group resolved differently"
+            _say(f"[gpu] {case}: {exact} of {long_rows} selecting rows fixed by the tie rule, all equal to the oracle")
+            assert exact >= 0.9 * long_rows
 
 
 def test_sparse_mla_caller_indices():

@@ -142,6 +142,45 @@ def test_scores_exact_within_fp32_bound():
         assert abs(float(S[s]) - float(exact)) <= gamma(d_I + H_I) * sc[s] + 1e-30
 
 
+def test_score_scale_exact_rational():
+    """oracle_index_score_scale equals sum_h |w_h| sum_i |q_I[h,i] LNk[s,i]| computed in exact rational
+    arithmetic, to double rounding (it sets the parity floor where the k-th score is exactly 0)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(4)
+    for H_I, d_I in [(4, 64), (64, 128)]:
+        n = 5
+        LNk = _bf(rng.standard_normal((n, d_I)))
+        q = _bf(rng.standard_normal((H_I, d_I)))
+        w = _bf(rng.uniform(-1, 1, H_I))        # negative weights count by magnitude
+        sc = oracle.index_score_scale(q, w, LNk, 1, n - 1)
+        assert sc.shape == (n - 1,)
+        qf, wf, kf = f32(q), f32(w), f32(LNk)
+        for s in range(1, n):
+            exact = Fraction(0)
+            for h in range(H_I):
+                dot = sum(abs(Fraction(float(qf[h, i])) * Fraction(float(kf[s, i]))) for i in range(d_I))
+                exact += abs(Fraction(float(wf[h]))) * dot
+            assert abs(Fraction(float(sc[s - 1])) - exact) <= Fraction(1, 2 ** 40) * exact
+    # one-hot closed form: a single nonzero product
+    q = np.zeros((4, 64), np.float32)
+    q[2, 5] = -3.0
+    w = np.array([9, 9, -0.5, 9], np.float32)
+    LNk = np.zeros((2, 64), np.float32)
+    LNk[1, 5] = 1.25
+    assert list(oracle.index_score_scale(_bf(q), _bf(w), _bf(LNk), 0, 1)) == [0.0, 0.5 * 3.0 * 1.25]
+
+
+def test_lower_index_rule_helper():
+    """The tie-rule check used by the GPU tests flags a kept higher index over a dropped equal lower one."""
+    from tests.parity import lower_index_rule_violations
+    S = np.array([5, 3, 3, 3, 1, 3], np.float32)   # keys 10..15
+    assert lower_index_rule_violations([10, 11, 12, -1], S, 10, 15) == []
+    assert lower_index_rule_violations([10, 11, 13, -1], S, 10, 15) == [(11, 3.0)]
+    assert lower_index_rule_violations([10, 11, 12, 13, 15], S, 10, 15) == []
+    assert lower_index_rule_violations([10, 15], S, 10, 15) == [(11, 3.0)]
+    assert lower_index_rule_violations([10, 14], S, 10, 15) == []
+
+
 def test_scores_scaling_and_head_permutation():
     """P8: scaling q_I or w by 2 doubles S exactly; permuting heads keeps S within the FP32 bound."""
     rng = np.random.default_rng(2)
@@ -423,3 +462,14 @@ def test_packed_equals_per_document():
         shifted = np.where(i1 >= 0, i1 + b, -1)
         assert np.array_equal(idx[b:e], shifted)
         assert np.array_equal(mla["out_bf16"][b:e], m1["out_bf16"])
+
+
+def test_float_timing_variant_matches_double():
+    """The float-accumulated attention used only to time the CPU baseline computes the same outputs as
+    the double reference, to float rounding."""
+    cfg = tg.get_config("tiny")
+    inp = tg.make_inputs(cfg)
+    rows = np.arange(700, 1024, 41)
+    idx, theta, keff, mla = oracle.forward(cfg, inp, rows)
+    f = oracle.sparse_mla_f32(rows, inp["q"][rows], inp["kv"], idx, inp["W_UV"], inp["gate"][rows], cfg.softmax_scale)
+    assert np.abs(f - mla["out"]).max() <= 1e-4 * np.abs(mla["out"]).max()
