@@ -124,13 +124,31 @@ def _check(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _p(t, dtype, name, optional=False):
+def _p(t, dtype, name, optional=False, numel=None):
+    """Device pointer of t after dtype/device/contiguity checks and, if numel is given, a size check:
+    an undersized buffer would otherwise become an out-of-bounds device access."""
     if t is None:
         if optional:
             return None
         raise ValueError(f"{name} is required")
     _check(t, dtype, name)
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the shape needs {numel}")
     return t.data_ptr()
+
+
+def _rows(shape: Shape) -> int:
+    return (shape.q_end or shape.T) - shape.q_begin
+
+
+def _sizes(shape: Shape) -> dict:
+    """Element counts of every tensor argument for this shape (include/dsa.h)."""
+    r, T = _rows(shape), shape.T
+    return {
+        "q_I": r * shape.H_I * shape.d_I, "k_I": T * shape.d_I, "w": r * shape.H_I, "ln": shape.d_I,
+        "topk_idx": r * shape.topk, "q": r * shape.H * 576, "kv": T * 576, "W_UV": shape.H * 512 * 128,
+        "gate": r * shape.H, "out": r * shape.H * 128, "lse": r * shape.H, "o_lat": r * shape.H * 512,
+    }
 
 
 def _stream():
@@ -158,44 +176,52 @@ def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
 
 
 def dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None):
-    bf = torch.bfloat16
+    bf, n = torch.bfloat16, _sizes(shape)
     st = lib().dsa_index_topk(
-        ctypes.byref(shape), _p(q_I, bf, "q_I"), _p(k_I, bf, "k_I"), _p(ln_gamma, torch.float32, "ln_gamma", True),
-        _p(ln_beta, torch.float32, "ln_beta", True), _p(w, bf, "w"), _p(topk_idx, torch.int32, "topk_idx"),
+        ctypes.byref(shape), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_index_topk")
 
 
 def dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None):
-    bf = torch.bfloat16
+    bf, n = torch.bfloat16, _sizes(shape)
     st = lib().dsa_sparse_mla_fwd(
-        ctypes.byref(shape), _p(q, bf, "q"), _p(kv, bf, "kv"), _p(topk_idx, torch.int32, "topk_idx"),
-        _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"), _p(out, bf, "out"), _p(lse, torch.float32, "lse", True),
-        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+        ctypes.byref(shape), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(W_UV, bf, "W_UV", numel=n["W_UV"]),
+        _p(gate, bf, "gate", numel=n["gate"]), _p(out, bf, "out", numel=n["out"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _p(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream())
     _raise(st, "dsa_sparse_mla_fwd")
 
 
 def dsa_sparse_attention_latent(shape, q, kv, topk_idx, o_lat, lse=None):
-    bf = torch.bfloat16
+    bf, n = torch.bfloat16, _sizes(shape)
     st = lib().dsa_sparse_attention_latent(
-        ctypes.byref(shape), _p(q, bf, "q"), _p(kv, bf, "kv"), _p(topk_idx, torch.int32, "topk_idx"),
-        _p(o_lat, bf, "o_lat"), _p(lse, torch.float32, "lse", True), _stream())
+        ctypes.byref(shape), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(o_lat, bf, "o_lat", numel=n["o_lat"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _stream())
     _raise(st, "dsa_sparse_attention_latent")
 
 
 def dsa_up_gate(shape, o_lat, W_UV, gate, out):
-    bf = torch.bfloat16
-    st = lib().dsa_up_gate(ctypes.byref(shape), _p(o_lat, bf, "o_lat"), _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"),
-                           _p(out, bf, "out"), _stream())
+    bf, n = torch.bfloat16, _sizes(shape)
+    st = lib().dsa_up_gate(ctypes.byref(shape), _p(o_lat, bf, "o_lat", numel=n["o_lat"]),
+                           _p(W_UV, bf, "W_UV", numel=n["W_UV"]), _p(gate, bf, "gate", numel=n["gate"]),
+                           _p(out, bf, "out", numel=n["out"]), _stream())
     _raise(st, "dsa_up_gate")
 
 
 def dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace, ln_gamma=None, ln_beta=None,
                   lse=None):
-    bf = torch.bfloat16
+    bf, n = torch.bfloat16, _sizes(shape)
     st = lib().dsa_fused_fwd(
-        ctypes.byref(shape), _p(q_I, bf, "q_I"), _p(k_I, bf, "k_I"), _p(ln_gamma, torch.float32, "ln_gamma", True),
-        _p(ln_beta, torch.float32, "ln_beta", True), _p(w, bf, "w"), _p(q, bf, "q"), _p(kv, bf, "kv"),
-        _p(W_UV, bf, "W_UV"), _p(gate, bf, "gate"), _p(topk_idx, torch.int32, "topk_idx"), _p(out, bf, "out"),
-        _p(lse, torch.float32, "lse", True), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+        ctypes.byref(shape), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(W_UV, bf, "W_UV", numel=n["W_UV"]), _p(gate, bf, "gate", numel=n["gate"]),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(out, bf, "out", numel=n["out"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _p(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream())
     _raise(st, "dsa_fused_fwd")

@@ -25,8 +25,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int32_t rows_of(const dsa_shape* s) { return (s->q_end == 0 ? s->T : s->q_end) - s->q_begin; }
 
+// Workspace regions, each from a 256-byte-aligned offset:
+//   LNk    [T + kIdxKeyPad, d_I] bf16   key LayerNorm output (the padding rows are staged, never scored)
+//   flags  [kIdxSlots] int32           candidate-slot claims of the indexer's workgroups
+//   cand   [kIdxSlots, slot words]     candidate token indices of the rows in flight
+//   o_lat  [chunk rows, H, 512] bf16   latent attention output of one row chunk
 struct Layout {
-  size_t lnk_off, lnk_bytes, olat_off, olat_bytes, total;
+  size_t lnk_off, lnk_bytes, flags_off, cand_off, cand_bytes, olat_off, olat_bytes, total;
   int64_t chunk_rows;
 };
 
@@ -34,12 +39,13 @@ Layout layout_of(const dsa_shape* s) {
   Layout L{};
   L.lnk_off = 0;
   L.lnk_bytes = align_up(static_cast<size_t>(s->T + dsa::kIdxKeyPad) * s->d_I * 2);
+  L.flags_off = L.lnk_off + L.lnk_bytes;
+  L.cand_off = L.flags_off + align_up(static_cast<size_t>(dsa::kIdxSlots) * 4);
+  L.cand_bytes = align_up(static_cast<size_t>(dsa::kIdxSlots) * dsa::index_slot_words() * 4);
   const int64_t rows = rows_of(s);
   L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
-  L.olat_off = L.lnk_bytes;
-  // o_lat of a chunk of rows; the indexer's candidate lists use the same space, row for row
-  const size_t per_row = std::max<size_t>(static_cast<size_t>(s->H) * 512 * 2, static_cast<size_t>(dsa::index_candidate_capacity()) * 4);
-  L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * per_row);
+  L.olat_off = L.cand_off + L.cand_bytes;
+  L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * s->H * 512 * 2);
   L.total = L.olat_off + L.olat_bytes;
   return L;
 }
@@ -107,17 +113,16 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   a.row0 = s->q_begin;
   a.nrows = rows_of(s);
   a.k = s->topk;
-  // The candidate token indices of the rows in flight use the o_lat part of the workspace (the
-  // attention writes it only after the indexer is done); rows go in launches that fit there.
-  a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.olat_off);
-  const int64_t per_row = static_cast<int64_t>(dsa::index_candidate_capacity()) * 4;
-  const int64_t cap_rows = static_cast<int64_t>(L.olat_bytes) / per_row;  // >= chunk rows, by the layout
-  if (cap_rows <= 0) return DSA_ERR_WORKSPACE;
+  // Candidate token indices live in kIdxSlots slots, one per workgroup in flight; every launch
+  // frees the slots it claimed, and the prologue marks them all free first.
+  a.slot_flags = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + L.flags_off);
+  a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.cand_off);
+  a.n_slots = dsa::kIdxSlots;
   if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st) != hipSuccess)
     return DSA_ERR_LAUNCH;
-  // Rows with more than k causal keys, per document, in launches whose candidate lists fit.
-  // With few such rows per CU, blocks pair long and short rows of a document so that every block
-  // carries about the same work; otherwise blocks take consecutive rows, longest first.
+  // Rows with more than k causal keys, one segment per document. With few such rows per CU,
+  // blocks pair long and short rows of a document so that every block carries about the same
+  // work; otherwise blocks take consecutive rows, longest first.
   struct Seg { int r0, m, b; };
   std::vector<Seg> segs;
   int64_t nsel = 0;
@@ -126,36 +131,28 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
     const int64_t b1 = s->cu_seqlens_host ? s->cu_seqlens_host[d + 1] : s->T;
     const int64_t lo = std::max<int64_t>(b0 + s->topk, s->q_begin) - s->q_begin;
     const int64_t hi = std::min<int64_t>(b1, s->q_begin + a.nrows) - s->q_begin;
-    for (int64_t h = hi; h > lo; h -= cap_rows) {  // pieces that fit the candidate space
-      const int64_t l = std::max<int64_t>(lo, h - cap_rows);
-      segs.push_back({static_cast<int>(l), static_cast<int>(h - l), static_cast<int>(b0)});
-      nsel += h - l;
+    if (hi > lo) {
+      segs.push_back({static_cast<int>(lo), static_cast<int>(hi - lo), static_cast<int>(b0)});
+      nsel += hi - lo;
     }
   }
   a.paired = nsel < kIdxPairedBelow ? 1 : 0;
   // longest rows first: the longest row of a segment is its last
   std::stable_sort(segs.begin(), segs.end(),
                    [&](const Seg& x, const Seg& y) { return x.r0 + x.m - x.b > y.r0 + y.m - y.b; });
-  size_t i = 0;
-  while (i < segs.size()) {
-    // one launch: consecutive segments whose rows fit the candidate space together
-    a.row_lo = segs[i].r0;
-    int row_hi = segs[i].r0 + segs[i].m;
+  for (size_t i = 0; i < segs.size();) {
+    // one launch per kIdxMaxSeg documents
     a.nseg = 0;
     a.seg_blk0[0] = 0;
-    while (i < segs.size() && a.nseg < dsa::kIdxMaxSeg) {
-      const int lo = std::min(a.row_lo, segs[i].r0), hi = std::max(row_hi, segs[i].r0 + segs[i].m);
-      if (hi - lo > cap_rows) break;
-      a.row_lo = lo;
-      row_hi = hi;
+    for (; i < segs.size() && a.nseg < dsa::kIdxMaxSeg; ++i, ++a.nseg) {
       a.seg_r0[a.nseg] = segs[i].r0;
       a.seg_m[a.nseg] = segs[i].m;
       a.seg_b[a.nseg] = segs[i].b;
       a.seg_blk0[a.nseg + 1] = a.seg_blk0[a.nseg] + dsa::index_blocks(segs[i].m, a.paired);
-      ++a.nseg;
-      ++i;
     }
-    if (dsa::launch_index_topk(a, s->H_I, s->d_I, st) != hipSuccess) return DSA_ERR_LAUNCH;
+    const hipError_t e = dsa::launch_index_topk(a, s->H_I, s->d_I, st);
+    if (e == hipErrorInvalidConfiguration) return DSA_ERR_UNSUPPORTED;  // more resident workgroups than slots
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
   }
   return DSA_OK;
 }
@@ -213,7 +210,7 @@ dsa_status dsa_index_topk(const dsa_shape* s, const uint16_t* q_I, const uint16_
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (!q_I || !k_I || !w || !topk_idx) return DSA_ERR_INVALID_ARG;
-  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(topk_idx, 4) || !aligned(ln_gamma, 4) ||
+  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(topk_idx, 16) || !aligned(ln_gamma, 4) ||
       !aligned(ln_beta, 4))
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
@@ -227,7 +224,7 @@ dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint1
   if (st != DSA_OK) return st;
   if (!q || !kv || !topk_idx || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 4) || !aligned(gate, 2) ||
-      !aligned(out, 2) || !aligned(lse, 4))
+      !aligned(out, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
   return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, static_cast<hipStream_t>(stream));
@@ -248,7 +245,7 @@ dsa_status dsa_up_gate(const dsa_shape* s, const uint16_t* o_lat, const uint16_t
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (!o_lat || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
-  if (!aligned(o_lat, 16) || !aligned(W_UV, 16) || !aligned(gate, 2) || !aligned(out, 2)) return DSA_ERR_INVALID_ARG;
+  if (!aligned(o_lat, 16) || !aligned(W_UV, 16) || !aligned(gate, 2) || !aligned(out, 16)) return DSA_ERR_INVALID_ARG;
   return launch_up(s, o_lat, W_UV, gate, out, 0, rows_of(s), static_cast<hipStream_t>(stream));
 }
 
@@ -260,8 +257,8 @@ dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t
   if (st != DSA_OK) return st;
   if (!q_I || !k_I || !w || !q || !kv || !W_UV || !gate || !topk_idx || !out) return DSA_ERR_INVALID_ARG;
   if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(ln_gamma, 4) || !aligned(ln_beta, 4) ||
-      !aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 4) || !aligned(gate, 2) ||
-      !aligned(out, 2) || !aligned(lse, 4))
+      !aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 16) || !aligned(gate, 2) ||
+      !aligned(out, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);

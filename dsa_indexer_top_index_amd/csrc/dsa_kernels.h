@@ -6,9 +6,11 @@
 
 namespace dsa {
 
-constexpr int kIdxMaxSeg = 16;  // row segments per indexer launch
+constexpr int kIdxMaxSeg = 64;  // row segments per indexer launch
 constexpr int kIdxKeyPad = 128; // LNk rows past T in the workspace: the indexer stages whole 64-key
                                 // chunks (up to two past the last key) and never scores those rows
+constexpr int kIdxSlots = 256;  // candidate-list slots: one per indexer workgroup resident at a time
+                                // (one per CU on MI355X); launches check residency against this
 
 struct IndexArgs {
   const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
@@ -21,8 +23,9 @@ struct IndexArgs {
   int row0;              // global token of local row 0
   int nrows;
   int k;
-  int32_t* cand;         // candidate token indices: index_candidate_capacity() per local row from row_lo on
-  int row_lo;            // first local row of the candidate space
+  int32_t* cand;         // candidate token indices: n_slots slots of index_slot_words() int32 each
+  int* slot_flags;       // [n_slots] 1 while a workgroup holds the slot; zeroed by the prologue
+  int n_slots;
   // Rows that need a selection, as segments of consecutive local rows of one document each.
   // Segment s: rows [seg_r0, seg_r0 + seg_m), document start token seg_b, blocks
   // [seg_blk0[s], seg_blk0[s + 1]). paired != 0: each block takes 4 of the longest and 4 of the
@@ -67,7 +70,7 @@ hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const 
                                  uint16_t* LNk, const IndexArgs& a, hipStream_t st);
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
 int index_blocks(int m, int paired);  // blocks of a segment of m rows
-int index_candidate_capacity();  // candidate slots per row needed in IndexArgs::cand
+int index_slot_words();               // int32 words of one candidate slot (the lists of one workgroup's rows)
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
 

@@ -35,6 +35,8 @@
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
+#include <mutex>
+
 namespace dsa {
 
 // ---------------------------------------------------------------------------------------------
@@ -489,7 +491,6 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // its barrier while appends of that step write buffer (c + 1) % 2, so no wave can see a flag
   // that another wave of the same step has not seen.
   __shared__ __attribute__((aligned(16))) int s_need[2][kIdxRows];
-  __shared__ int s_row[kIdxRows];                 // local row of each wave
   __shared__ int s_lbase[kIdxRows];               // first LDS slot of each wave's list
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
   __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
@@ -539,10 +540,29 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   if (lane == 0) {
     s_need[0][wave] = 0;
     s_need[1][wave] = 0;
-    s_row[wave] = r;
     s_lbase[wave] = lbase;
   }
+  // Claim a candidate slot for the workgroup's lists of token indices. At most n_slots workgroups
+  // are resident at once (the host checks this before the launch) and each frees its slot before
+  // it ends, so a free slot always exists; the search is still bounded, and a workgroup that finds
+  // none writes -1 rows instead of touching memory it does not own.
+  __shared__ int s_slot;
+  if (threadIdx.x == 0) {
+    int got = -1;
+    for (int i = 0; i < 4 * a.n_slots && got < 0; ++i) {
+      const int sl = (static_cast<int>(blockIdx.x) + i) % a.n_slots;
+      if (atomicCAS(a.slot_flags + sl, 0, 1) == 0) got = sl;
+    }
+    __threadfence();
+    s_slot = got;
+  }
   __syncthreads();
+  const int slot = s_slot;
+  if (slot < 0) {
+    if (select)
+      for (int j = lane; j < k; j += kWave) out[j] = -1;
+    return;  // uniform over the workgroup
+  }
   const int kb = b, ke = a.row0 + A + i_top + 1;
 
   // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
@@ -570,7 +590,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[lbase])));
   DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[0])));
   DSA_LDS uint32_t* sel_scratch = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_sel[0])));
-  int32_t* cand = a.cand + static_cast<int64_t>(r - a.row_lo) * kCandStride;
+  int32_t* cand = a.cand + (static_cast<int64_t>(slot) * kIdxRows + wave) * kCandStride;
   int cnt = 0;
   uint32_t thr = 0u;
 
@@ -580,7 +600,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
       DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[s_lbase[rw]])));
-      int32_t* cr = a.cand + static_cast<int64_t>(s_row[rw] - a.row_lo) * kCandStride;
+      int32_t* cr = a.cand + (static_cast<int64_t>(slot) * kIdxRows + rw) * kCandStride;
       int kept = 0;
       const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
       if (rw == wave) {
@@ -720,7 +740,6 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     const bool more = kb + (c + 1) * kChunk <= t;
     s_need[nbuf][wave] = cnt > cap - kChunk && more ? cnt : 0;  // every lane writes the same value
   };
-  auto no_side = [](int) {};
 
   float p0_prev = 0.0f;  // tile-0 partial sums of the previous chunk
   issue_chunk(0);
@@ -771,15 +790,43 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       for (int j = lane; j < k; j += kWave) out[j] = cand[j];
     }
   }
+  // Free the slot once every wave's reads of its token indices have completed.
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicExch(a.slot_flags + slot, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
-int index_candidate_capacity() { return kCandStride; }
+int index_slot_words() { return kIdxRows * kCandStride; }
 
 int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
 
+// Workgroups of the indexer kernel that the current device can hold at once (CUs x occupancy),
+// computed once per device.
+static int index_resident_blocks(int H_I, int d_I) {
+  static std::mutex mu;
+  static int cached[2][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  const int v = (H_I == 64 && d_I == 128) ? 0 : 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[v][dev] == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    const void* fn = v == 0 ? reinterpret_cast<const void*>(k_index_topk<64, 128>) : reinterpret_cast<const void*>(k_index_topk<4, 64>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kIdxRows * kWave, 0) != hipSuccess) return -1;
+    cached[v][dev] = cus * occ;
+  }
+  return cached[v][dev];
+}
+
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st) {
-  if (a.nseg < 1 || a.nseg > kIdxMaxSeg) return hipErrorInvalidValue;
+  if (a.nseg < 1 || a.nseg > kIdxMaxSeg || a.n_slots < 1) return hipErrorInvalidValue;
+  const int resident = index_resident_blocks(H_I, d_I);
+  if (resident < 1 || resident > a.n_slots) return hipErrorInvalidConfiguration;  // slots could run out
   dim3 grid(a.seg_blk0[a.nseg]), block(kIdxRows * kWave);
   if (H_I == 64 && d_I == 128) hipLaunchKernelGGL((k_index_topk<64, 128>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((k_index_topk<4, 64>), grid, block, 0, st, a);
@@ -806,6 +853,8 @@ __global__ __launch_bounds__(256) void k_index_prologue(const uint16_t* __restri
                                                         const float* __restrict__ beta, double eps,
                                                         uint16_t* __restrict__ LNk, IndexArgs a, int nln) {
   const int blk = blockIdx.x;
+  if (blk == 0)  // every candidate slot starts free
+    for (int i = threadIdx.x; i < a.n_slots; i += blockDim.x) a.slot_flags[i] = 0;
   if (blk < nln) key_layernorm_block<D_I>(k_I, gamma, beta, eps, a.T, LNk, blk);
   else short_rows_block(a, blk - nln, gridDim.x - nln);
 }

@@ -19,7 +19,10 @@
  *
  * Conventions for every entry point
  *  - bf16 tensors are passed as bf16 bit patterns (uint16_t) in device memory, row-major,
- *    contiguous, 16-byte aligned. Integer tensors are int32, device memory, 4-byte aligned.
+ *    contiguous, 16-byte aligned (k_I, w and gate: 2-byte aligned suffices). Integer tensors are
+ *    int32 in device memory: topk_idx is written with 16-byte stores and must be 16-byte aligned
+ *    where an entry point writes it, 4-byte aligned where it is only read. float32 tensors are
+ *    4-byte aligned.
  *  - Token axis: keys and key-side tensors (k_I, kv) cover all T tokens. Query-side tensors
  *    (q_I, w, q, gate) and outputs (topk_idx, out, lse) cover only the rows
  *    [q_begin, q_end) of the shape, indexed from 0 (local row r is global token q_begin + r).
@@ -46,7 +49,8 @@ extern "C" {
 typedef enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad cu_seqlens */
-  DSA_ERR_UNSUPPORTED = 2, /* shape outside the supported set */
+  DSA_ERR_UNSUPPORTED = 2, /* shape outside the supported set, or a device that can hold more
+                              indexer workgroups at once than the workspace has candidate slots */
   DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_size() */
   DSA_ERR_LAUNCH = 4       /* a kernel launch failed */
 } dsa_status;
@@ -82,8 +86,8 @@ dsa_status dsa_check_shape(const dsa_shape* shape);
  * float32 device arrays or NULL (identity); w [rows, H_I] bf16 (any sign).
  * Output: topk_idx [rows, topk] int32. Row r holds min(topk, n) distinct global token indices of
  * its causal keys (n = number of causal keys), in ascending order, then -1 up to topk.
- * Workspace: >= dsa_workspace_size(shape) bytes (holds LN(k_I) and the candidate lists of the
- * rows being selected). */
+ * Workspace: >= dsa_workspace_size(shape) bytes (holds LN(k_I), and the candidate token indices of
+ * the rows being selected in 256 fixed slots, one per indexer workgroup in flight). */
 dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
                           const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                           int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);

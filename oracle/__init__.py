@@ -15,7 +15,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
+# -ffp-contract=off: no fused multiply-adds, so every sum is evaluated as written. The parity build
+# targets the generic x86-64 ISA so that the library built here also runs on other hosts.
 CXXFLAGS = ["-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
+# The CPU-baseline build: the same source and floating-point semantics, optimised for the host that
+# runs it (built there, into a temporary directory, each time it is timed).
+NATIVE_CXXFLAGS = ["-O3", "-march=native", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
 
 
 def build(force: bool = False) -> str:
@@ -28,23 +33,44 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def build_native() -> str:
+    """Compiles the oracle with NATIVE_CXXFLAGS for this host into a fresh temporary directory."""
+    import tempfile
+    d = tempfile.mkdtemp(prefix="oracle_native_")
+    path = os.path.join(d, "liboracle_native.so")
+    subprocess.run(["g++", *NATIVE_CXXFLAGS, _SRC, "-o", path], check=True)
+    return path
+
+
+def use_native():
+    """Switches this module to a host-optimised build of the same source (for timing only)."""
+    global _lib
+    _lib = _load(build_native())
+    return _lib
+
+
 def lib():
     global _lib
     if _lib is None:
         build()
-        L = ctypes.CDLL(_LIB_PATH)
-        p, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        L.oracle_num_threads.restype = ctypes.c_int
-        L.oracle_doc_begin.argtypes = [p, i32, i64]
-        L.oracle_doc_begin.restype = i64
-        L.oracle_key_layernorm.argtypes = [p, i64, i32, p, p, d, p, p]
-        L.oracle_index_scores.argtypes = [p, p, i32, i32, p, i64, i64, p]
-        L.oracle_index_score_scale.argtypes = [p, p, i32, i32, p, i64, i64, p]
-        L.oracle_topk.argtypes = [i64, p, p, p, i32, i32, p, p, i32, i32, p, p, p]
-        L.oracle_sparse_mla.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
-        L.oracle_dense_causal.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
-        _lib = L
+        _lib = _load(_LIB_PATH)
     return _lib
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    p, i32, i64, d = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_doc_begin.argtypes = [p, i32, i64]
+    L.oracle_doc_begin.restype = i64
+    L.oracle_key_layernorm.argtypes = [p, i64, i32, p, p, d, p, p]
+    L.oracle_index_scores.argtypes = [p, p, i32, i32, p, i64, i64, p]
+    L.oracle_index_score_scale.argtypes = [p, p, i32, i32, p, i64, i64, p]
+    L.oracle_topk.argtypes = [i64, p, p, p, i32, i32, p, p, i32, i32, p, p, p]
+    L.oracle_sparse_mla.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
+    L.oracle_dense_causal.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
+    L.oracle_sparse_mla_f32.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
+    return L
 
 
 def _c(a, dtype):
@@ -134,6 +160,20 @@ def sparse_mla(rows, q_rows, kv, idx, W_UV, gate_rows, scale):
                             res["o_pre"].ctypes.data, res["out"].ctypes.data, res["out_bf16"].ctypes.data,
                             res["lse"].ctypes.data, res["psum"].ctypes.data)
     return res
+
+
+def sparse_mla_f32(rows, q_rows, kv, idx, W_UV, gate_rows, scale):
+    """The attention, up-projection and gate accumulated in float (timing only); returns out [n,H,128]."""
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(q_rows, np.uint16)
+    kvc, pkv = _c(kv, np.uint16)
+    ix, pi = _c(idx, np.int32)
+    W, pw = _c(W_UV, np.uint16)
+    g, pg = _c(gate_rows, np.uint16)
+    n, H = q.shape[0], q.shape[1]
+    out = np.empty((n, H, 128))
+    lib().oracle_sparse_mla_f32(n, pr, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale, out.ctypes.data)
+    return out
 
 
 def dense_causal(rows, q_rows, kv, cu_seqlens, W_UV, gate_rows, scale):

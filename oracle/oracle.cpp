@@ -219,12 +219,16 @@ void oracle_topk(int64_t n_rows, const int64_t* rows, const uint16_t* qI_rows, c
 //   ol_c = sum_j p_j * kv[s_j, c]                    (c < 512)
 //   o_d  = sum_c ol_c * W_UV[h, c, d]                 (d < 128)
 //   out  = o_d * 1 / (1 + exp(-gate[r, h]))
-// All in double. Outputs (each optional): o_pre [n,H,128] before the gate, out_f64 [n,H,128],
-// out_bf16 (RNE of out_f64), lse [n,H] = max l + log sum exp(l - max l), psum [n,H] = sum_j p_j.
-void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T,
-                       const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
-                       double scale, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
-  (void)rows;
+}  // extern "C"
+
+// Accumulation type R: double on parity runs; float for the timed CPU baseline only (the same
+// steps in the same order, in single precision). Outputs (each optional): o_pre [n,H,128] before
+// the gate, out_f64 [n,H,128], out_bf16 (RNE of out_f64), lse [n,H] = max l + log sum exp(l - max l),
+// psum [n,H] = sum_j p_j.
+template <typename R>
+void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T, const int32_t* idx,
+                     int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H, double scale,
+                     double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
     std::vector<int64_t> sel;
@@ -233,44 +237,64 @@ void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_ro
       if (s >= 0 && s < T) sel.push_back(s);
     }
     const size_t n = sel.size();
-    std::vector<double> l(n), ol(kDV);
+    std::vector<R> l(n), ol(kDV);
     for (int32_t h = 0; h < H; ++h) {
       const uint16_t* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
       for (size_t j = 0; j < n; ++j) {
         const uint16_t* kr = kv + sel[j] * kDL;
-        double dot = 0.0;
+        R dot = 0;
         for (int i = 0; i < kDL; ++i)
-          dot += static_cast<double>(bf16_bits_to_float(qh[i])) * bf16_bits_to_float(kr[i]);
-        l[j] = scale * dot;
+          dot += static_cast<R>(bf16_bits_to_float(qh[i])) * static_cast<R>(bf16_bits_to_float(kr[i]));
+        l[j] = static_cast<R>(scale) * dot;
       }
-      double m = -std::numeric_limits<double>::infinity();
+      R m = -std::numeric_limits<R>::infinity();
       for (size_t j = 0; j < n; ++j) m = std::max(m, l[j]);
-      double z = 0.0;
+      R z = 0;
       for (size_t j = 0; j < n; ++j) z += std::exp(l[j] - m);
-      std::fill(ol.begin(), ol.end(), 0.0);
-      double ps = 0.0;
+      std::fill(ol.begin(), ol.end(), R(0));
+      R ps = 0;
       for (size_t j = 0; j < n; ++j) {
-        double p = std::exp(l[j] - m) / z;
+        R p = std::exp(l[j] - m) / z;
         ps += p;
         const uint16_t* vr = kv + sel[j] * kDL;
-        for (int c = 0; c < kDV; ++c) ol[c] += p * bf16_bits_to_float(vr[c]);
+        for (int c = 0; c < kDV; ++c) ol[c] += p * static_cast<R>(bf16_bits_to_float(vr[c]));
       }
-      const double g = bf16_bits_to_float(gate_rows[r * H + h]);
-      const double sig = 1.0 / (1.0 + std::exp(-g));
+      const R g = bf16_bits_to_float(gate_rows[r * H + h]);
+      const R sig = R(1) / (R(1) + std::exp(-g));
       const uint16_t* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
       for (int d = 0; d < kDO; ++d) {
-        double o = 0.0;
-        for (int c = 0; c < kDV; ++c) o += ol[c] * bf16_bits_to_float(Wh[c * kDO + d]);
+        R o = 0;
+        for (int c = 0; c < kDV; ++c) o += ol[c] * static_cast<R>(bf16_bits_to_float(Wh[c * kDO + d]));
         const int64_t at = (r * H + h) * static_cast<int64_t>(kDO) + d;
         if (o_pre) o_pre[at] = o;
-        const double y = o * sig;
+        const R y = o * sig;
         if (out_f64) out_f64[at] = y;
-        if (out_bf16) out_bf16[at] = double_to_bf16_rne(y);
+        if (out_bf16) out_bf16[at] = double_to_bf16_rne(static_cast<double>(y));
       }
       if (lse) lse[r * H + h] = m + std::log(z);
       if (psum) psum[r * H + h] = ps;
     }
   }
+}
+
+extern "C" {
+
+// All in double (the parity reference).
+void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T,
+                       const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
+                       double scale, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
+  (void)rows;
+  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, o_pre, out_f64, out_bf16, lse,
+                          psum);
+}
+
+// The same definition accumulated in float: used only to time the oracle as a CPU baseline.
+void oracle_sparse_mla_f32(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv,
+                           int64_t T, const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows,
+                           int32_t H, double scale, double* out_f64) {
+  (void)rows;
+  sparse_mla_impl<float>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, nullptr, out_f64, nullptr,
+                         nullptr, nullptr);
 }
 
 // Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are

@@ -41,19 +41,19 @@ def _shape(**kw):
 def test_supported_shapes_and_workspace():
     assert dsa.dsa_check_shape(_shape()) == dsa.DSA_OK
     assert dsa.dsa_check_shape(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)) == dsa.DSA_OK
+    # LN(k_I) ((T + 128 padding rows) x d_I bf16), 256 candidate-slot flags (1 KB), 256 candidate
+    # slots of 8 rows x 4,160 int32 token indices, and the latent output of one row chunk (rows x H x
+    # 512 bf16, at most 16,384 rows)
+    flags, slots = 1024, 256 * 8 * 4160 * 4
     ws = dsa.dsa_workspace_size(_shape())
-    # LN(k_I) ((T + 128 padding rows) x d_I bf16) plus the latent output of one row chunk
-    # (rows x H x 512 bf16)
-    assert ws == (4096 + 128) * 128 * 2 + 4096 * 96 * 512 * 2
+    assert ws == (4096 + 128) * 128 * 2 + flags + slots + 4096 * 96 * 512 * 2
     big = dsa.dsa_workspace_size(_shape(T=131072))
-    assert big == (131072 + 128) * 128 * 2 + 16384 * 96 * 512 * 2
+    assert big == (131072 + 128) * 128 * 2 + flags + slots + 16384 * 96 * 512 * 2
     assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
-    # with 16 heads a row's latent output (16 KB) is smaller than the indexer's per-row candidate
-    # list of token indices (4,160 int32), which shares that space: the larger of the two counts
     tiny = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16))
-    assert tiny == (1024 + 128) * 64 * 2 + 1024 * 4160 * 4
+    assert tiny == (1024 + 128) * 64 * 2 + flags + slots + 1024 * 16 * 512 * 2
     one = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16, q_begin=1000, q_end=1001))
-    assert one == (1024 + 128) * 64 * 2 + 4160 * 4
+    assert one == (1024 + 128) * 64 * 2 + flags + slots + 16 * 512 * 2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -106,3 +106,28 @@ def test_entry_points_reject_before_any_hip_call():
     assert L.dsa_fused_fwd(ctypes.byref(bad), fake, fake, None, None, fake, fake, fake, fake, fake, fake, fake, None,
                            fake, n, None) == dsa.DSA_ERR_UNSUPPORTED
     assert L.dsa_check_shape(None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_undersized_tensors():
+    """The binding checks each tensor's element count against the shape before calling the library
+    (an undersized buffer would become an out-of-bounds device access). CPU tensors are rejected
+    too, before any size check can pass, so nothing here reaches the GPU."""
+    import torch
+    s = _shape(T=64, topk=16, H_I=4, d_I=64, H=16)
+    sz = dsa._sizes(s)
+    assert sz["q_I"] == 64 * 4 * 64 and sz["out"] == 64 * 16 * 128 and sz["topk_idx"] == 64 * 16
+    part = _shape(T=64, topk=16, H_I=4, d_I=64, H=16, q_begin=10, q_end=20)
+    assert dsa._sizes(part)["q"] == 10 * 16 * 576 and dsa._sizes(part)["kv"] == 64 * 576
+    t = torch.empty(3, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dsa._p(t, torch.bfloat16, "x")   # host memory
+    fake = torch.empty(5, dtype=torch.bfloat16)
+    # exercise the size rule alone on a tensor that passes the other checks
+    orig = dsa._check
+    try:
+        dsa._check = lambda *a: None
+        with pytest.raises(ValueError, match="elements"):
+            dsa._p(fake, torch.bfloat16, "q", numel=6)
+        assert dsa._p(fake, torch.bfloat16, "q", numel=5) == fake.data_ptr()
+    finally:
+        dsa._check = orig
