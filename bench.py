@@ -120,13 +120,20 @@ def _counter_rows(d):
     return rows
 
 
-def _per_dispatch_kib(rows, name_part, counter):
+def _per_dispatch_kib(rows, name_part, counter, full_size_only=False):
     """Per-dispatch values of `counter` (KiB; summed over the counter's instances) for kernels
-    whose name contains name_part."""
-    per = {}
+    whose name contains name_part. full_size_only keeps the dispatches that run at least half as
+    long as the kernel's longest one: the fused step launches the attention and the up-projection
+    per row chunk, the stage window once over all rows, and only the latter is one launch of the
+    whole workload."""
+    per, dur = {}, {}
     for r in rows:
         if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if full_size_only and dur:
+        longest = max(dur.values())
+        return [v for d, v in per.items() if dur[d] >= 0.5 * longest]
     return list(per.values())
 
 
@@ -144,8 +151,8 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, co
     frows, wrows = _counter_rows(fetch_dir), _counter_rows(write_dir)
     out = {}
     for kernel in KERNEL_SRC:
-        fv = _per_dispatch_kib(frows, kernel, "FETCH_SIZE")
-        wv = _per_dispatch_kib(wrows, kernel, "WRITE_SIZE")
+        fv = _per_dispatch_kib(frows, kernel, "FETCH_SIZE", full_size_only=True)
+        wv = _per_dispatch_kib(wrows, kernel, "WRITE_SIZE", full_size_only=True)
         if not fv or not wv:
             continue
         f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
@@ -153,6 +160,7 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, co
         res = {
             "kernel": kernel, "workload": workload, "kernel_code_sha256_16": src_hash(KERNEL_SRC[kernel]),
             "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [len(fv), len(wv)],
+            "dispatch_rule": "launches over the whole workload only (at least half the longest dispatch)",
             "copy_calibration": {"bytes_each_way_all_copies": cal_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
                                  "fetch_scale": f_scale, "write_scale": w_scale},
             "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
@@ -193,6 +201,8 @@ def pmc_mfma_summary(mfma_dir, workload, commands):
         ds = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
         if not ds:
             continue
+        longest = max(d["t"] for d in ds)
+        ds = [d for d in ds if d["t"] >= 0.5 * longest]  # whole-workload launches only (see _per_dispatch_kib)
         t = float(np.mean([d["t"] for d in ds]))
         mops = float(np.mean([d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds]))
         busy = float(np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds]))
@@ -213,6 +223,48 @@ def pmc_mfma_summary(mfma_dir, workload, commands):
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def stats_summary(stats_dir, workload, command, bench_log):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats` run of this bench: the statistics of
+    every kernel, the mean duration of the whole-workload launches of the three path kernels, and the
+    bench line the same command printed (its HIP-event stage times)."""
+    import csv
+    import glob
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)[0])))
+    trace = list(csv.DictReader(open(glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)[0])))
+    line = None
+    for l in open(bench_log):
+        if l.startswith("{"):
+            line = json.loads(l)
+    lines = [f"# rocprofv3 kernel statistics: fused forward, {WORKLOAD_TEXT[workload]}", "",
+             "Command (on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; R is the repository root):",
+             "", "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", "Launches over the whole workload (at least half the kernel's longest launch; the fused step runs the "
+              "attention and the up-projection in row chunks, the bench's stage window once over all rows), against "
+              "the HIP-event stage times of the bench line printed by the same command:", "",
+              "| kernel | launches | trace average (us) | bench, HIP events (us) |", "|---|---|---|---|"]
+    ev = {"k_index_topk": ("index_topk_ms", "key LayerNorm prologue + indexer"), "k_sparse_mla": ("attention_ms", "attention"),
+          "k_up_gate": ("up_gate_ms", "up-projection + gate")}
+    for k, (field, what) in ev.items():
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace if k in r["Kernel_Name"]]
+        if not d:
+            continue
+        full = [x for x in d if x >= 0.5 * max(d)]
+        b = f"{line['stages'][field] * 1e3:.1f} ({what})" if line else "n/a"
+        lines.append(f"| `{k}` | {len(full)} | {np.mean(full):.1f} | {b} |")
+    if line:
+        st = line["stages"]
+        lines += ["", f"Bench line of the same command: {st['value']:.0f} query tokens/s, {st['ms_per_step']:.3f} ms per "
+                  f"fused step (profiled, few steps); indexer {st['indexer_frac_scored_rows']:.3f} and attention "
+                  f"{st['attention_frac']:.3f} of dense bf16 MFMA peak.",
+                  "", "Kernel code hashes (sha256[:16] of the source without comments): " +
+                  ", ".join(f"{k} {src_hash(v)}" for k, v in KERNEL_SRC.items()) + "."]
+    print("\n".join(lines))
 
 
 def cpu_model():
@@ -400,7 +452,13 @@ def main():
     ap.add_argument("--pmc-commands", default="", help="the profiling commands, recorded in the summary")
     ap.add_argument("--pmc-mfma-summary", metavar="MFMA_DIR",
                     help="write per-kernel MFMA counters from a rocprofv3 run of " + ", ".join(MFMA_COUNTERS))
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_DIR", "BENCH_LOG"),
+                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats run of --workload")
     args = ap.parse_args()
+
+    if args.stats_summary:
+        stats_summary(args.stats_summary[0], args.workload, args.pmc_commands, args.stats_summary[1])
+        return
 
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, workload=args.workload, commands=args.pmc_commands)
