@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
   dsa_up_gate(shape, o_lat, W_UV, gate, out)
   dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace,
                 ln_gamma=None, ln_beta=None, lse=None)
+  dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None)
 """
 from __future__ import annotations
 
@@ -25,7 +26,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
-DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH = range(5)
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_LAUNCH, DSA_ERR_TOO_LARGE = range(6)
+NOALLOC_MAX_T, NOALLOC_MAX_DOCS = 131072, 64   # limits of dsa_index_topk_noalloc
 
 
 class DsaError(RuntimeError):
@@ -78,6 +80,8 @@ def lib():
         L.dsa_up_gate.restype = ctypes.c_int
         L.dsa_fused_fwd.argtypes = [P, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_fused_fwd.restype = ctypes.c_int
+        L.dsa_index_topk_noalloc.argtypes = [P, v, v, v, v, v, v, v]
+        L.dsa_index_topk_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -183,6 +187,17 @@ def dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_be
         _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_index_topk")
+
+
+def dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None):
+    """dsa_index_topk without a workspace: the library's fixed per-GPU scratch is used instead
+    (T <= NOALLOC_MAX_T, at most NOALLOC_MAX_DOCS documents). Allocates nothing."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    st = lib().dsa_index_topk_noalloc(
+        ctypes.byref(shape), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _stream())
+    _raise(st, "dsa_index_topk_noalloc")
 
 
 def dsa_sparse_mla_fwd(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None):

@@ -3,6 +3,7 @@
 #include "dsa.h"
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -41,7 +42,7 @@ Layout layout_of(const dsa_shape* s) {
   L.lnk_bytes = align_up(static_cast<size_t>(s->T + dsa::kIdxKeyPad) * s->d_I * 2);
   L.flags_off = L.lnk_off + L.lnk_bytes;
   L.cand_off = L.flags_off + align_up(static_cast<size_t>(dsa::kIdxSlots) * 4);
-  L.cand_bytes = align_up(static_cast<size_t>(dsa::kIdxSlots) * dsa::index_slot_words() * 4);
+  L.cand_bytes = align_up(static_cast<size_t>(dsa::kIdxSlots) * dsa::kIdxSlotWords * 4);
   const int64_t rows = rows_of(s);
   L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
   L.olat_off = L.cand_off + L.cand_bytes;
@@ -67,6 +68,8 @@ const char* dsa_status_string(dsa_status st) {
     case DSA_ERR_UNSUPPORTED: return "unsupported shape";
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_LAUNCH: return "kernel launch failed";
+    case DSA_ERR_TOO_LARGE:
+      return "shape exceeds the fixed scratch of the allocation-free entry point (T <= 131072, at most 64 documents)";
   }
   return "unknown status";
 }
@@ -98,8 +101,16 @@ size_t dsa_workspace_size(const dsa_shape* s) {
   return layout_of(s).total;
 }
 
+// One document's rows that need a selection: local rows [r0, r0 + m), document start token b.
+struct Seg {
+  int r0, m, b, order;
+};
+
+// Steps 1-3 into topk_idx. ws holds the LNk, flag and candidate regions of layout_of(s); segs is
+// caller storage for at least s->n_docs entries (no allocation happens here).
 static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* gamma,
-                            const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, hipStream_t st) {
+                            const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, Seg* segs,
+                            hipStream_t st) {
   const auto L = layout_of(s);
   uint16_t* lnk = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.lnk_off);
   dsa::IndexArgs a{};
@@ -123,8 +134,7 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   // Rows with more than k causal keys, one segment per document. With few such rows per CU,
   // blocks pair long and short rows of a document so that every block carries about the same
   // work; otherwise blocks take consecutive rows, longest first.
-  struct Seg { int r0, m, b; };
-  std::vector<Seg> segs;
+  int nseg = 0;
   int64_t nsel = 0;
   for (int d = 0; d < s->n_docs; ++d) {
     const int64_t b0 = s->cu_seqlens_host ? s->cu_seqlens_host[d] : 0;
@@ -132,19 +142,22 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
     const int64_t lo = std::max<int64_t>(b0 + s->topk, s->q_begin) - s->q_begin;
     const int64_t hi = std::min<int64_t>(b1, s->q_begin + a.nrows) - s->q_begin;
     if (hi > lo) {
-      segs.push_back({static_cast<int>(lo), static_cast<int>(hi - lo), static_cast<int>(b0)});
+      segs[nseg] = {static_cast<int>(lo), static_cast<int>(hi - lo), static_cast<int>(b0), nseg};
+      ++nseg;
       nsel += hi - lo;
     }
   }
   a.paired = nsel < kIdxPairedBelow ? 1 : 0;
-  // longest rows first: the longest row of a segment is its last
-  std::stable_sort(segs.begin(), segs.end(),
-                   [&](const Seg& x, const Seg& y) { return x.r0 + x.m - x.b > y.r0 + y.m - y.b; });
-  for (size_t i = 0; i < segs.size();) {
+  // longest rows first (the longest row of a segment is its last), then document order
+  std::sort(segs, segs + nseg, [](const Seg& x, const Seg& y) {
+    const int lx = x.r0 + x.m - x.b, ly = y.r0 + y.m - y.b;
+    return lx != ly ? lx > ly : x.order < y.order;
+  });
+  for (int i = 0; i < nseg;) {
     // one launch per kIdxMaxSeg documents
     a.nseg = 0;
     a.seg_blk0[0] = 0;
-    for (; i < segs.size() && a.nseg < dsa::kIdxMaxSeg; ++i, ++a.nseg) {
+    for (; i < nseg && a.nseg < dsa::kIdxMaxSeg; ++i, ++a.nseg) {
       a.seg_r0[a.nseg] = segs[i].r0;
       a.seg_m[a.nseg] = segs[i].m;
       a.seg_b[a.nseg] = segs[i].b;
@@ -214,7 +227,8 @@ dsa_status dsa_index_topk(const dsa_shape* s, const uint16_t* q_I, const uint16_
       !aligned(ln_beta, 4))
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
-  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, static_cast<hipStream_t>(stream));
+  std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
+  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), static_cast<hipStream_t>(stream));
 }
 
 dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
@@ -262,8 +276,63 @@ dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t
     return DSA_ERR_INVALID_ARG;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, hs)) != DSA_OK) return st;
+  std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
+  if ((st = run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), hs)) != DSA_OK) return st;
   return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, hs);
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free indexer entry point, for callers that cannot allocate device memory. Its scratch
+// (LNk, candidate-slot flags, candidate slots: the first three workspace regions of the largest
+// shape it accepts) is a file-scope device array that each GPU holds from the library's first use
+// on it until the process ends. Host code never passes the array's name to a kernel: that is a
+// host-side stand-in. The device address comes from hipGetSymbolAddress, once per device.
+namespace {
+
+constexpr int32_t kNoAllocMaxT = 131072;
+constexpr int32_t kNoAllocMaxDocs = dsa::kIdxMaxSeg;
+constexpr size_t align_c(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+constexpr size_t kNoAllocBytes = align_c(static_cast<size_t>(kNoAllocMaxT + dsa::kIdxKeyPad) * 128 * 2) +
+                                 align_c(static_cast<size_t>(dsa::kIdxSlots) * 4) +
+                                 align_c(static_cast<size_t>(dsa::kIdxSlots) * dsa::kIdxSlotWords * 4);
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+// Device address of this GPU's copy of scratch (the current device), looked up on the first call
+// on each device. Returns nullptr on failure.
+static void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+extern "C" dsa_status dsa_index_topk_noalloc(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I,
+                                             const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                                             int32_t* topk_idx, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q_I || !k_I || !w || !topk_idx) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(topk_idx, 16) || !aligned(ln_gamma, 4) ||
+      !aligned(ln_beta, 4))
+    return DSA_ERR_INVALID_ARG;
+  if (s->T > kNoAllocMaxT || s->n_docs > kNoAllocMaxDocs) return DSA_ERR_TOO_LARGE;
+  const Layout L = layout_of(s);
+  if (L.cand_off + L.cand_bytes > kNoAllocBytes) return DSA_ERR_TOO_LARGE;
+  void* ws = scratch_address();
+  if (ws == nullptr) return DSA_ERR_LAUNCH;
+  Seg segs[kNoAllocMaxDocs];
+  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs, static_cast<hipStream_t>(stream));
+}

@@ -11,6 +11,7 @@ constexpr int kIdxKeyPad = 128; // LNk rows past T in the workspace: the indexer
                                 // chunks (up to two past the last key) and never scores those rows
 constexpr int kIdxSlots = 256;  // candidate-list slots: one per indexer workgroup resident at a time
                                 // (one per CU on MI355X); launches check residency against this
+constexpr int kIdxSlotWords = 8 * 4160;  // int32 words of one slot: 8 rows' candidate token indices
 
 struct IndexArgs {
   const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
@@ -70,7 +71,6 @@ hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const 
                                  uint16_t* LNk, const IndexArgs& a, hipStream_t st);
 hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
 int index_blocks(int m, int paired);  // blocks of a segment of m rows
-int index_slot_words();               // int32 words of one candidate slot (the lists of one workgroup's rows)
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
 

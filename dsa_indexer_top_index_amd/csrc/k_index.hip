@@ -800,7 +800,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-int index_slot_words() { return kIdxRows * kCandStride; }
+static_assert(kIdxSlotWords == kIdxRows * kCandStride, "slot size");
 
 int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
 

@@ -52,7 +52,8 @@ typedef enum dsa_status {
   DSA_ERR_UNSUPPORTED = 2, /* shape outside the supported set, or a device that can hold more
                               indexer workgroups at once than the workspace has candidate slots */
   DSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dsa_workspace_size() */
-  DSA_ERR_LAUNCH = 4       /* a kernel launch failed */
+  DSA_ERR_LAUNCH = 4,      /* a kernel launch failed */
+  DSA_ERR_TOO_LARGE = 5    /* beyond the fixed scratch of dsa_index_topk_noalloc */
 } dsa_status;
 
 /* Shapes of one call. Supported: (H_I, d_I) in {(64,128), (4,64)}; H in {96, 16};
@@ -91,6 +92,18 @@ dsa_status dsa_check_shape(const dsa_shape* shape);
 dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
                           const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                           int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Steps 1-3 without a workspace and without allocating device memory, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same inputs, output and results as dsa_index_topk. The scratch it needs instead of the workspace
+ * is a fixed 67,666,944-byte device array per GPU, held from the first call on that GPU until the
+ * process ends; it limits the shape to T <= 131072 and at most 64 documents (else
+ * DSA_ERR_TOO_LARGE, checked on the host before any HIP call). Every call on a GPU uses that GPU's
+ * one array and leaves its contents behind (each call clears what must start at zero itself):
+ * calls that overlap on one GPU, on any streams, race and must not be made. */
+dsa_status dsa_index_topk_noalloc(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
+                                  const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                                  int32_t* topk_idx, void* stream);
 
 /* Steps 4-5 for caller-supplied indices. Inputs: q [rows, H, 576] bf16 (already absorbed into
  * the latent space; dims 0..511 pair with the compressed KV, 512..575 with the key-only dims);

@@ -19,16 +19,18 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_sparse_attention_latent",
-                     "dsa_sparse_mla_fwd", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
+    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_index_topk_noalloc",
+                     "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd", "dsa_status_string", "dsa_up_gate",
+                     "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         assert dsa.status_string(st)
+    assert "allocation-free" in dsa.status_string(dsa.DSA_ERR_TOO_LARGE)
     assert dsa.status_string(99) == "unknown status"
 
 
@@ -131,3 +133,22 @@ def test_python_binding_rejects_undersized_tensors():
         assert dsa._p(fake, torch.bfloat16, "q", numel=5) == fake.data_ptr()
     finally:
         dsa._check = orig
+
+
+def test_noalloc_entry_point_host_checks():
+    """dsa_index_topk_noalloc rejects shapes beyond its fixed scratch (T > 131072, more than 64
+    documents) and bad pointers on the host, before any HIP call."""
+    L = dsa.lib()
+    fake = 1 << 20
+    ok = _shape(T=131072)
+    assert dsa.dsa_check_shape(ok) == dsa.DSA_OK
+    big = _shape(T=131073)
+    assert L.dsa_index_topk_noalloc(ctypes.byref(big), fake, fake, None, None, fake, fake, None) == dsa.DSA_ERR_TOO_LARGE
+    cu = list(range(0, 65 * 64, 64)) + [65 * 64 + 10]   # 65 documents
+    many = _shape(T=cu[-1], cu_seqlens=cu)
+    many.cu_seqlens_dev = 256
+    assert dsa.dsa_check_shape(many) == dsa.DSA_OK
+    assert L.dsa_index_topk_noalloc(ctypes.byref(many), fake, fake, None, None, fake, fake, None) == dsa.DSA_ERR_TOO_LARGE
+    assert L.dsa_index_topk_noalloc(ctypes.byref(ok), None, fake, None, None, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk_noalloc(ctypes.byref(ok), fake, fake, None, None, fake, fake + 4, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk_noalloc(ctypes.byref(_shape(H=8)), fake, fake, None, None, fake, fake, None) == dsa.DSA_ERR_UNSUPPORTED
