@@ -70,6 +70,7 @@ def _load(path):
     L.oracle_sparse_mla.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
     L.oracle_dense_causal.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
     L.oracle_sparse_mla_f32.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
+    L.oracle_sparse_mla_variant.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p, p, p, p]
     return L
 
 
@@ -159,6 +160,28 @@ def sparse_mla(rows, q_rows, kv, idx, W_UV, gate_rows, scale):
     lib().oracle_sparse_mla(n, pr, pq, pkv, kvc.shape[0], pi, k, pw, pg, H, scale,
                             res["o_pre"].ctypes.data, res["out"].ctypes.data, res["out_bf16"].ctypes.data,
                             res["lse"].ctypes.data, res["psum"].ctypes.data)
+    return res
+
+
+def sparse_mla_variant(rows, q_rows, kv, idx, W_UV, gate, scale, gate_per_dim=False, sink=None):
+    """Gate/sink variants: gate [n,H] or, with gate_per_dim, [n,H,128]; sink [H] float (natural-log
+    units) or None. Returns the same dict as sparse_mla."""
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(q_rows, np.uint16)
+    kvc, pkv = _c(kv, np.uint16)
+    ix, pi = _c(idx, np.int32)
+    W, pw = _c(W_UV, np.uint16)
+    g, pg = _c(gate, np.uint16)
+    sk, ps = _opt(sink, np.float64)
+    n, H = q.shape[0], q.shape[1]
+    assert g.size == n * H * (128 if gate_per_dim else 1)
+    res = {
+        "o_pre": np.empty((n, H, 128)), "out": np.empty((n, H, 128)),
+        "out_bf16": np.empty((n, H, 128), dtype=np.uint16), "lse": np.empty((n, H)), "psum": np.empty((n, H)),
+    }
+    lib().oracle_sparse_mla_variant(n, pr, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale,
+                                    1 if gate_per_dim else 0, ps, res["o_pre"].ctypes.data, res["out"].ctypes.data,
+                                    res["out_bf16"].ctypes.data, res["lse"].ctypes.data, res["psum"].ctypes.data)
     return res
 
 

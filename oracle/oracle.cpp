@@ -223,12 +223,18 @@ void oracle_topk(int64_t n_rows, const int64_t* rows, const uint16_t* qI_rows, c
 
 // Accumulation type R: double on parity runs; float for the timed CPU baseline only (the same
 // steps in the same order, in single precision). Outputs (each optional): o_pre [n,H,128] before
-// the gate, out_f64 [n,H,128], out_bf16 (RNE of out_f64), lse [n,H] = max l + log sum exp(l - max l),
+// the gate, out_f64 [n,H,128], out_bf16 (RNE of out_f64), lse [n,H] = log(sum_j exp(l_j) [+ exp(sink)]),
 // psum [n,H] = sum_j p_j.
+// Variants ([AD] blueprint entry "Output gate + sink": sigma(x W_g) * o and a learnable sink):
+//  - gate_per_dim = 0: gate_rows [n,H], one logit per (row, head), broadcast over the 128 outputs;
+//    gate_per_dim = 1: gate_rows [n,H,128], one logit per output element.
+//  - sink [H] or NULL: head h's softmax gains one more term exp(sink[h]) in its denominator, a
+//    logit whose value row is zero (it takes weight from the keys and adds nothing to o_lat).
 template <typename R>
 void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T, const int32_t* idx,
                      int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H, double scale,
-                     double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
+                     int32_t gate_per_dim, const double* sink, double* o_pre, double* out_f64, uint16_t* out_bf16,
+                     double* lse, double* psum) {
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < n_rows; ++r) {
     std::vector<int64_t> sel;
@@ -249,8 +255,10 @@ void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv,
       }
       R m = -std::numeric_limits<R>::infinity();
       for (size_t j = 0; j < n; ++j) m = std::max(m, l[j]);
+      if (sink) m = std::max(m, static_cast<R>(sink[h]));
       R z = 0;
       for (size_t j = 0; j < n; ++j) z += std::exp(l[j] - m);
+      if (sink) z += std::exp(static_cast<R>(sink[h]) - m);
       std::fill(ol.begin(), ol.end(), R(0));
       R ps = 0;
       for (size_t j = 0; j < n; ++j) {
@@ -259,14 +267,14 @@ void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv,
         const uint16_t* vr = kv + sel[j] * kDL;
         for (int c = 0; c < kDV; ++c) ol[c] += p * static_cast<R>(bf16_bits_to_float(vr[c]));
       }
-      const R g = bf16_bits_to_float(gate_rows[r * H + h]);
-      const R sig = R(1) / (R(1) + std::exp(-g));
       const uint16_t* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
       for (int d = 0; d < kDO; ++d) {
         R o = 0;
         for (int c = 0; c < kDV; ++c) o += ol[c] * static_cast<R>(bf16_bits_to_float(Wh[c * kDO + d]));
         const int64_t at = (r * H + h) * static_cast<int64_t>(kDO) + d;
         if (o_pre) o_pre[at] = o;
+        const R g = bf16_bits_to_float(gate_per_dim ? gate_rows[at] : gate_rows[r * H + h]);
+        const R sig = R(1) / (R(1) + std::exp(-g));
         const R y = o * sig;
         if (out_f64) out_f64[at] = y;
         if (out_bf16) out_bf16[at] = double_to_bf16_rne(static_cast<double>(y));
@@ -284,8 +292,20 @@ void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_ro
                        const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
                        double scale, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
   (void)rows;
-  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, o_pre, out_f64, out_bf16, lse,
-                          psum);
+  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, o_pre, out_f64,
+                          out_bf16, lse, psum);
+}
+
+// The gate and sink variants ([AD] "Output gate + sink"), in double: gate_per_dim selects a gate
+// [n,H,128] instead of [n,H]; sink [H] (or NULL) adds exp(sink[h]) to head h's softmax denominator.
+void oracle_sparse_mla_variant(int64_t n_rows, const int64_t* rows, const uint16_t* q_rows, const uint16_t* kv,
+                               int64_t T, const int32_t* idx, int32_t k, const uint16_t* W_UV,
+                               const uint16_t* gate_rows, int32_t H, double scale, int32_t gate_per_dim,
+                               const double* sink, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse,
+                               double* psum) {
+  (void)rows;
+  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, gate_per_dim, sink, o_pre,
+                          out_f64, out_bf16, lse, psum);
 }
 
 // The same definition accumulated in float: used only to time the oracle as a CPU baseline.
@@ -293,8 +313,8 @@ void oracle_sparse_mla_f32(int64_t n_rows, const int64_t* rows, const uint16_t* 
                            int64_t T, const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows,
                            int32_t H, double scale, double* out_f64) {
   (void)rows;
-  sparse_mla_impl<float>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, nullptr, out_f64, nullptr,
-                         nullptr, nullptr);
+  sparse_mla_impl<float>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, nullptr, out_f64,
+                         nullptr, nullptr, nullptr);
 }
 
 // Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are

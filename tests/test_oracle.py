@@ -473,3 +473,76 @@ def test_float_timing_variant_matches_double():
     idx, theta, keff, mla = oracle.forward(cfg, inp, rows)
     f = oracle.sparse_mla_f32(rows, inp["q"][rows], inp["kv"], idx, inp["W_UV"], inp["gate"][rows], cfg.softmax_scale)
     assert np.abs(f - mla["out"]).max() <= 1e-4 * np.abs(mla["out"]).max()
+
+
+# ---------------------------------------------------------------- gate and sink variants (AD "Output gate + sink")
+
+def _variant_inputs(seed=61, T=300, H=16, k=64):
+    cfg = tg.Config("variant", seed, [T], topk=k, H=H, H_I=4, d_I=64, w_scale=0.5)
+    inp = tg.make_inputs(cfg)
+    rng = np.random.default_rng(seed)
+    rows = np.array([0, 5, 63, 64, 150, 299])
+    idx = np.full((len(rows), k), -1, np.int32)
+    for j, t in enumerate(rows):
+        n = min(k, t + 1)
+        idx[j, :n] = np.sort(rng.choice(t + 1, n, replace=False))
+    return cfg, inp, rows, idx
+
+
+def test_sink_limits_and_mass():
+    """A sink far below every logit changes nothing; far above, it takes all the weight (output 0, lse =
+    sink); otherwise the keys' weights plus the sink's weight exp(sink - lse) sum to 1, and the lse is
+    log(exp(lse without sink) + exp(sink))."""
+    cfg, inp, rows, idx = _variant_inputs()
+    q, g = inp["q"][rows], inp["gate"][rows]
+    base = oracle.sparse_mla(rows, q, inp["kv"], idx, inp["W_UV"], g, cfg.softmax_scale)
+    lo = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], g, cfg.softmax_scale, sink=np.full(cfg.H, -1e4))
+    assert np.array_equal(lo["out"], base["out"]) and np.array_equal(lo["lse"], base["lse"])
+    hi = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], g, cfg.softmax_scale, sink=np.full(cfg.H, 1e4))
+    assert np.all(hi["out"] == 0) and np.all(hi["lse"] == 1e4)
+    sink = np.random.default_rng(1).normal(0, 2, cfg.H)
+    r = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], g, cfg.softmax_scale, sink=sink)
+    assert np.abs(r["psum"] + np.exp(sink[None, :] - r["lse"]) - 1).max() < 1e-12
+    assert np.abs(r["lse"] - np.logaddexp(base["lse"], sink[None, :])).max() < 1e-12
+    # the sink only rescales the keys' weights: o_pre = base o_pre * (sum of key weights)
+    assert np.abs(r["o_pre"] - base["o_pre"] * r["psum"][..., None]).max() < 1e-12 * np.abs(base["o_pre"]).max()
+
+
+def test_sink_one_key_is_logistic():
+    """One selected key and a sink s: the key's weight is the logistic function of (l - s), so
+    o_lat = sigma(l - s) * kv_row."""
+    cfg, inp, rows, idx = _variant_inputs()
+    idx1 = np.full((len(rows), 8), -1, np.int32)
+    idx1[:, 0] = rows
+    sink = np.linspace(-3, 3, cfg.H)
+    r = oracle.sparse_mla_variant(rows, inp["q"][rows], inp["kv"], idx1, inp["W_UV"], inp["gate"][rows],
+                                  cfg.softmax_scale, sink=sink)
+    kvf = f32(inp["kv"]).astype(np.float64)
+    Wf = f32(inp["W_UV"]).astype(np.float64)
+    qf = f32(inp["q"][rows]).astype(np.float64)
+    for j, t in enumerate(rows):
+        for h in range(cfg.H):
+            l = cfg.softmax_scale * (qf[j, h] @ kvf[t])
+            wgt = 1.0 / (1.0 + math.exp(-(l - sink[h])))
+            want = wgt * (kvf[t, :512] @ Wf[h])
+            assert np.abs(r["o_pre"][j, h] - want).max() <= 1e-12 * max(np.abs(want).max(), 1e-300)
+
+
+def test_gate_per_dim():
+    """An elementwise gate equal to the per-head gate on every output gives the same outputs; with a
+    block-identity W_UV each output is sigma(g[d]) times its own latent dim; g = 0 halves."""
+    cfg, inp, rows, idx = _variant_inputs()
+    q, g = inp["q"][rows], inp["gate"][rows]
+    base = oracle.sparse_mla(rows, q, inp["kv"], idx, inp["W_UV"], g, cfg.softmax_scale)
+    rep = np.repeat(g[:, :, None], 128, axis=2)
+    r = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], rep, cfg.softmax_scale, gate_per_dim=True)
+    assert np.array_equal(r["out"], base["out"]) and np.array_equal(r["out_bf16"], base["out_bf16"])
+    gd = tg.normal_bf16(7, 99, 0, len(rows) * cfg.H * 128, 1.0).reshape(len(rows), cfg.H, 128)
+    Wi = np.zeros((cfg.H, 512, 128), np.float32)
+    Wi[:, np.arange(128), np.arange(128)] = 1
+    ri = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, _bf(Wi), gd, cfg.softmax_scale, gate_per_dim=True)
+    sig = 1.0 / (1.0 + np.exp(-f32(gd).astype(np.float64)))
+    assert np.abs(ri["out"] - ri["o_pre"] * sig).max() <= 1e-15 * np.abs(ri["o_pre"]).max()
+    rz = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], np.zeros_like(gd), cfg.softmax_scale,
+                                   gate_per_dim=True)
+    assert np.array_equal(rz["out"], rz["o_pre"] / 2)
