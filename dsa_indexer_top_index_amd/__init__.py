@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace,
                 ln_gamma=None, ln_beta=None, lse=None)
   dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None)
+  dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
+  gate [rows,H,128] and per-head sink logits [H] float32)
 """
 from __future__ import annotations
 
@@ -53,6 +55,11 @@ class Shape(ctypes.Structure):
     ]
 
 
+class Variant(ctypes.Structure):
+    """dsa_mla_variant: elementwise gate and/or per-head sink (include/dsa.h)."""
+    _fields_ = [("gate_per_dim", ctypes.c_int32), ("sink", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -82,6 +89,11 @@ def lib():
         L.dsa_fused_fwd.restype = ctypes.c_int
         L.dsa_index_topk_noalloc.argtypes = [P, v, v, v, v, v, v, v]
         L.dsa_index_topk_noalloc.restype = ctypes.c_int
+        V = ctypes.POINTER(Variant)
+        L.dsa_sparse_mla_fwd_ex.argtypes = [P, V, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_sparse_mla_fwd_ex.restype = ctypes.c_int
+        L.dsa_fused_fwd_ex.argtypes = [P, V, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_fused_fwd_ex.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -240,3 +252,42 @@ def dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspac
         _p(lse, torch.float32, "lse", True, n["lse"]), _p(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream())
     _raise(st, "dsa_fused_fwd")
+
+
+def _variant(shape, gate_per_dim, sink):
+    """(Variant, element count of the gate) for the _ex entry points."""
+    var = Variant()
+    var.gate_per_dim = 1 if gate_per_dim else 0
+    var.sink = _p(sink, torch.float32, "sink", True, shape.H)
+    return var, _rows(shape) * shape.H * (128 if gate_per_dim else 1)
+
+
+def dsa_sparse_mla_fwd_ex(shape, q, kv, topk_idx, W_UV, gate, out, workspace, lse=None, gate_per_dim=False,
+                          sink=None):
+    """dsa_sparse_mla_fwd with the gate/sink variant: gate [rows,H] or, with gate_per_dim, [rows,H,128];
+    sink: float32 [H] (natural-log units) or None."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    var, n_gate = _variant(shape, gate_per_dim, sink)
+    st = lib().dsa_sparse_mla_fwd_ex(
+        ctypes.byref(shape), ctypes.byref(var), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(W_UV, bf, "W_UV", numel=n["W_UV"]),
+        _p(gate, bf, "gate", numel=n_gate), _p(out, bf, "out", numel=n["out"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _p(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream())
+    _raise(st, "dsa_sparse_mla_fwd_ex")
+
+
+def dsa_fused_fwd_ex(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace, ln_gamma=None, ln_beta=None,
+                     lse=None, gate_per_dim=False, sink=None):
+    """dsa_fused_fwd with the gate/sink variant of steps 4-5 (see dsa_sparse_mla_fwd_ex)."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    var, n_gate = _variant(shape, gate_per_dim, sink)
+    st = lib().dsa_fused_fwd_ex(
+        ctypes.byref(shape), ctypes.byref(var), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(W_UV, bf, "W_UV", numel=n["W_UV"]), _p(gate, bf, "gate", numel=n_gate),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(out, bf, "out", numel=n["out"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _p(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream())
+    _raise(st, "dsa_fused_fwd_ex")

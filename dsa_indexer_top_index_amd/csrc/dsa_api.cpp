@@ -170,14 +170,15 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   return DSA_OK;
 }
 
-static dsa_status launch_attention(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                                   uint16_t* olat, float* lse, int64_t c0, int64_t n, hipStream_t st) {
+static dsa_status launch_attention(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
+                                   const int32_t* idx, uint16_t* olat, float* lse, int64_t c0, int64_t n, hipStream_t st) {
   dsa::MlaArgs m{};
   m.q = q;
   m.kv = kv;
   m.idx = idx;
   m.o_lat = olat;
   m.lse = lse;
+  m.sink = v ? v->sink : nullptr;
   m.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
   m.n_docs = s->n_docs;
   m.T = s->T;
@@ -190,9 +191,10 @@ static dsa_status launch_attention(const dsa_shape* s, const uint16_t* q, const 
   return dsa::launch_sparse_mla(m, st) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
-static dsa_status launch_up(const dsa_shape* s, const uint16_t* olat, const uint16_t* W_UV, const uint16_t* gate,
-                            uint16_t* out, int64_t c0, int64_t n, hipStream_t st) {
+static dsa_status launch_up(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* olat, const uint16_t* W_UV,
+                            const uint16_t* gate, uint16_t* out, int64_t c0, int64_t n, hipStream_t st) {
   dsa::UpArgs u{};
+  u.gate_per_dim = v && v->gate_per_dim ? 1 : 0;
   u.o_lat = olat;
   u.W_UV = W_UV;
   u.gate = gate;
@@ -203,16 +205,17 @@ static dsa_status launch_up(const dsa_shape* s, const uint16_t* olat, const uint
   return dsa::launch_up_gate(u, st) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
-static dsa_status run_mla(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                          const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws, hipStream_t st) {
+static dsa_status run_mla(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
+                          const int32_t* idx, const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse,
+                          void* ws, hipStream_t st) {
   const auto L = layout_of(s);
   uint16_t* olat = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.olat_off);
   const int64_t rows = rows_of(s);
   for (int64_t c0 = 0; c0 < rows; c0 += L.chunk_rows) {
     const int64_t n = (rows - c0) < L.chunk_rows ? (rows - c0) : L.chunk_rows;
-    dsa_status r = launch_attention(s, q, kv, idx, olat, lse, c0, n, st);
+    dsa_status r = launch_attention(s, v, q, kv, idx, olat, lse, c0, n, st);
     if (r != DSA_OK) return r;
-    if ((r = launch_up(s, olat, W_UV, gate, out, c0, n, st)) != DSA_OK) return r;
+    if ((r = launch_up(s, v, olat, W_UV, gate, out, c0, n, st)) != DSA_OK) return r;
   }
   return DSA_OK;
 }
@@ -231,17 +234,34 @@ dsa_status dsa_index_topk(const dsa_shape* s, const uint16_t* q_I, const uint16_
   return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), static_cast<hipStream_t>(stream));
 }
 
-dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
-                              const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws,
-                              size_t ws_bytes, void* stream) {
+// Checks of the attention variant: an elementwise gate is read with 16-byte copies; the sink is
+// float32.
+static dsa_status check_variant(const dsa_mla_variant* v, const uint16_t* gate) {
+  if (v == nullptr) return DSA_OK;
+  if (v->gate_per_dim != 0 && v->gate_per_dim != 1) return DSA_ERR_INVALID_ARG;
+  if (v->gate_per_dim && !aligned(gate, 16)) return DSA_ERR_INVALID_ARG;
+  if (!aligned(v->sink, 4)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_fwd_ex(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
+                                 const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate, uint16_t* out,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (!q || !kv || !topk_idx || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 4) || !aligned(gate, 2) ||
       !aligned(out, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
+  if ((st = check_variant(v, gate)) != DSA_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
-  return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, static_cast<hipStream_t>(stream));
+  return run_mla(s, v, q, kv, topk_idx, W_UV, gate, out, lse, ws, static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
+                              const uint16_t* W_UV, const uint16_t* gate, uint16_t* out, float* lse, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return dsa_sparse_mla_fwd_ex(s, nullptr, q, kv, topk_idx, W_UV, gate, out, lse, ws, ws_bytes, stream);
 }
 
 dsa_status dsa_sparse_attention_latent(const dsa_shape* s, const uint16_t* q, const uint16_t* kv,
@@ -251,7 +271,7 @@ dsa_status dsa_sparse_attention_latent(const dsa_shape* s, const uint16_t* q, co
   if (!q || !kv || !topk_idx || !o_lat) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(topk_idx, 4) || !aligned(o_lat, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
-  return launch_attention(s, q, kv, topk_idx, o_lat, lse, 0, rows_of(s), static_cast<hipStream_t>(stream));
+  return launch_attention(s, nullptr, q, kv, topk_idx, o_lat, lse, 0, rows_of(s), static_cast<hipStream_t>(stream));
 }
 
 dsa_status dsa_up_gate(const dsa_shape* s, const uint16_t* o_lat, const uint16_t* W_UV, const uint16_t* gate,
@@ -260,13 +280,13 @@ dsa_status dsa_up_gate(const dsa_shape* s, const uint16_t* o_lat, const uint16_t
   if (st != DSA_OK) return st;
   if (!o_lat || !W_UV || !gate || !out) return DSA_ERR_INVALID_ARG;
   if (!aligned(o_lat, 16) || !aligned(W_UV, 16) || !aligned(gate, 2) || !aligned(out, 16)) return DSA_ERR_INVALID_ARG;
-  return launch_up(s, o_lat, W_UV, gate, out, 0, rows_of(s), static_cast<hipStream_t>(stream));
+  return launch_up(s, nullptr, o_lat, W_UV, gate, out, 0, rows_of(s), static_cast<hipStream_t>(stream));
 }
 
-dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
-                         const float* ln_beta, const uint16_t* w, const uint16_t* q, const uint16_t* kv,
-                         const uint16_t* W_UV, const uint16_t* gate, int32_t* topk_idx, uint16_t* out, float* lse,
-                         void* ws, size_t ws_bytes, void* stream) {
+dsa_status dsa_fused_fwd_ex(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q_I, const uint16_t* k_I,
+                            const float* ln_gamma, const float* ln_beta, const uint16_t* w, const uint16_t* q,
+                            const uint16_t* kv, const uint16_t* W_UV, const uint16_t* gate, int32_t* topk_idx,
+                            uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (!q_I || !k_I || !w || !q || !kv || !W_UV || !gate || !topk_idx || !out) return DSA_ERR_INVALID_ARG;
@@ -274,11 +294,20 @@ dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t
       !aligned(q, 16) || !aligned(kv, 16) || !aligned(W_UV, 16) || !aligned(topk_idx, 16) || !aligned(gate, 2) ||
       !aligned(out, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
+  if ((st = check_variant(v, gate)) != DSA_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
   if ((st = run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), hs)) != DSA_OK) return st;
-  return run_mla(s, q, kv, topk_idx, W_UV, gate, out, lse, ws, hs);
+  return run_mla(s, v, q, kv, topk_idx, W_UV, gate, out, lse, ws, hs);
+}
+
+dsa_status dsa_fused_fwd(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
+                         const float* ln_beta, const uint16_t* w, const uint16_t* q, const uint16_t* kv,
+                         const uint16_t* W_UV, const uint16_t* gate, int32_t* topk_idx, uint16_t* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return dsa_fused_fwd_ex(s, nullptr, q_I, k_I, ln_gamma, ln_beta, w, q, kv, W_UV, gate, topk_idx, out, lse, ws,
+                          ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -45,6 +45,7 @@ struct MlaArgs {
   const int32_t* idx;    // [nrows, k]
   uint16_t* o_lat;       // [chunk_rows, H, 512] workspace, local to the chunk
   float* lse;            // [nrows, H] or nullptr
+  const float* sink;     // [H] per-head sink logits (natural-log units) or nullptr: no sink
   const int32_t* cu;
   int n_docs;
   int T;
@@ -59,11 +60,12 @@ struct MlaArgs {
 struct UpArgs {
   const uint16_t* o_lat;  // [chunk_rows, H, 512]
   const uint16_t* W_UV;   // [H, 512, 128]
-  const uint16_t* gate;   // [nrows, H]
+  const uint16_t* gate;   // [nrows, H], or [nrows, H, 128] when gate_per_dim
   uint16_t* out;          // [nrows, H, 128]
   int chunk_r0;
   int chunk_rows;
   int H;
+  int gate_per_dim;       // 0: one gate logit per (row, head); 1: one per output element
 };
 
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.

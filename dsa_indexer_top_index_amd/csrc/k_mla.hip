@@ -7,6 +7,8 @@
 //   for query t, head h and selected rows s_j:
 //     l_j = scale * q[t,h,:] . kv[s_j,:]          (576 dims)
 //     o_lat[t,h,:] = softmax_j(l) . kv[s_j, 0:512]
+//   with an optional learnable sink per head (archdiff blueprint, "Output gate + sink"): the
+//   softmax denominator gains exp(sink[h]), a logit whose value row is zero.
 //
 // Kernel design: persistent workgroups, one per CU, each running query rows one after another
 // (longest rows first, dealt out zig-zag). Three kinds of waves meet in LDS; with 96 heads there
@@ -182,6 +184,10 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
       mfma_agpr_settle();
     };
     load_q(w.r);
+    // sink logit of this lane's head in log2 units, or nothing
+    float sink_l2[NTS];
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) sink_l2[nt] = a.sink ? a.sink[sw * HS + 16 * nt + i16] * 1.4426950408889634f : 0.0f;
     const uint32_t qk_base = ring + (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // row i16, column 4*st + g16
     // This lane's numerators (head gh, keys 4*g16 .. +3) in the B operand of the value waves:
     // M tile gh/32, lane 32*(g16/2) + gh%32, bytes 8*(g16&1) of that lane's 16.
@@ -372,17 +378,36 @@ __global__ __launch_bounds__(64 * mla_waves<H>(), 1) void k_sparse_mla(MlaArgs a
         max_pass();
         numerator_pass(std::false_type{}, std::true_type{});
       }
-      // 1/sum for the value waves, and lse
+      // 1/sum for the value waves, and lse. The numerators are 2^(x - m_ref); a sink s adds
+      // 2^(s - m_ref) to the sum (a logit with a zero value row). When the sink exceeds m_ref by
+      // more than 2^64 the sum is scaled by 2^-(s - m_ref) instead, so nothing overflows (a head
+      // with no usable key has m_ref = -inf and takes that branch: weight 0, lse = s).
 #pragma unroll
       for (int nt = 0; nt < NTS; ++nt) {
         float l = l_part[nt];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         const int gh = sw * HS + 16 * nt + i16;
+        float inv, lse2;
+        if (a.sink == nullptr) {
+          inv = l > 0.0f ? 1.0f / l : 0.0f;
+          lse2 = l > 0.0f ? m_ref[nt] + log2f(l) : -INFINITY;
+        } else {
+          const float d = sink_l2[nt] - m_ref[nt];
+          if (d <= kRestartGap) {
+            const float lt = l + fast_exp2(d);
+            inv = 1.0f / lt;
+            lse2 = m_ref[nt] + log2f(lt);
+          } else {
+            const float e = fast_exp2(-d);
+            const float lt = __builtin_fmaf(l, e, 1.0f);
+            inv = e / lt;
+            lse2 = sink_l2[nt] + log2f(lt);
+          }
+        }
         if (lane < 16) {
-          s_inv[gh] = l > 0.0f ? 1.0f / l : 0.0f;
-          if (a.lse)
-            a.lse[static_cast<int64_t>(r) * a.H + gh] = l > 0.0f ? (m_ref[nt] + log2f(l)) * 0.69314718055994531f : -INFINITY;
+          s_inv[gh] = inv;
+          if (a.lse) a.lse[static_cast<int64_t>(r) * a.H + gh] = lse2 * 0.69314718055994531f;
         }
       }
       if (MT * 32 > H && lane < MT * 32 - H) s_inv[H + lane] = 0.0f;

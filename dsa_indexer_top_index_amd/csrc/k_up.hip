@@ -6,6 +6,8 @@
 // v_head_dim 128):
 //   o[t,h,d]   = sum_c o_lat[t,h,c] * W_UV[h,c,d]      (c < 512, d < 128)
 //   out[t,h,d] = bf16( o[t,h,d] / (1 + exp(-gate[t,h])) )
+// or, with the elementwise gate of the blueprint's "Output gate + sink" entry (gate_per_dim),
+//   out[t,h,d] = bf16( o[t,h,d] / (1 + exp(-gate[t,h,d])) ).
 //
 // Kernel design: a workgroup owns one head and 256 query rows (four waves of 64 rows, two 32-row
 // M tiles each), so the head's 128 KB weight is read once per 256 rows. The batched product runs
@@ -17,7 +19,8 @@
 // every access is 16 bytes per lane except the gate: one 2-byte load per wave (lane l: the gate of
 // the wave's row l), spread to the lanes that need it by lane shuffles. The gate is applied in
 // FP32 in the epilogue, which stages each wave's 32 x 128 outputs of one M tile at a time in the
-// then idle weight buffer so that every row leaves in 16-byte stores.
+// then idle weight buffer so that every row leaves in 16-byte stores. An elementwise gate tile is
+// copied into that staging area first (16-byte copies) and overwritten in place by the gated outputs.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -76,8 +79,8 @@ __global__ __launch_bounds__(kUpWaves * kWave, kUpWavesPerSimd) void k_up_gate(U
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int s = 0; s < 4; ++s) af[mt][s] = *reinterpret_cast<const bf16x8*>(arow_p[mt] + 16 * s);
-  // the gate of the wave's row `lane`, as the sigmoid in FP32
-  const float gate_v = bf16_to_f32(a.gate[(static_cast<int64_t>(a.chunk_r0) + min(row0 + lane, a.chunk_rows - 1)) * H + h]);
+  // the gate of the wave's row `lane`, as the sigmoid in FP32 (per-head gates only)
+  const float gate_v = a.gate_per_dim ? 0.0f : bf16_to_f32(a.gate[(static_cast<int64_t>(a.chunk_r0) + min(row0 + lane, a.chunk_rows - 1)) * H + h]);
   wait_vmem();
   __syncthreads();
   const float sig_row = 1.0f / (1.0f + __expf(-gate_v));
@@ -124,12 +127,34 @@ __global__ __launch_bounds__(kUpWaves * kWave, kUpWavesPerSimd) void k_up_gate(U
   DSA_LDS uint16_t* st = reinterpret_cast<DSA_LDS uint16_t*>(lds_ptr(lds_addr_of(&s_w[0][0]))) + wave * 32 * kODim;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
+    if (a.gate_per_dim) {
+      // The tile's gate logits [32 rows][128] land in the staging area first (16-byte copies, four
+      // rows per copy); each element is then replaced in place by its gated output.
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rw = 8 * (e >> 2) + 4 * hh + (e & 3);
-      const float sig = __shfl(sig_row, 32 * mt + rw);
+      for (int j = 0; j < 8; ++j) {
+        const int row = min(row0 + 32 * mt + 4 * j + (lane >> 4), a.chunk_rows - 1);
+        copy16_to_lds(a.gate + ((static_cast<int64_t>(a.chunk_r0) + row) * H + h) * kODim + 8 * (lane & 15),
+                      st + 4 * j * kODim);
+      }
+      wait_vmem();
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) st[rw * kODim + 32 * nt + (lane & 31)] = f32_to_bf16(acc[mt][nt][e] * sig);
+      for (int e = 0; e < 16; ++e) {
+        const int rw = 8 * (e >> 2) + 4 * hh + (e & 3);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int at = rw * kODim + 32 * nt + (lane & 31);
+          const float sig = 1.0f / (1.0f + __expf(-bf16_to_f32(st[at])));
+          st[at] = f32_to_bf16(acc[mt][nt][e] * sig);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rw = 8 * (e >> 2) + 4 * hh + (e & 3);
+        const float sig = __shfl(sig_row, 32 * mt + rw);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) st[rw * kODim + 32 * nt + (lane & 31)] = f32_to_bf16(acc[mt][nt][e] * sig);
+      }
     }
     wave_lds_sync();
 #pragma unroll

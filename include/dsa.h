@@ -130,12 +130,38 @@ dsa_status dsa_sparse_attention_latent(const dsa_shape* shape, const uint16_t* q
 dsa_status dsa_up_gate(const dsa_shape* shape, const uint16_t* o_lat, const uint16_t* W_UV, const uint16_t* gate,
                        uint16_t* out, void* stream);
 
+/* Variants of steps 4-5 (archdiff.com "Kimi K3.1 Pro" blueprint, entry "Output gate + sink":
+ * sigma(x W_g) * o with a learnable sink). A NULL variant pointer means the defaults: gate
+ * [rows, H] and no sink. */
+typedef struct dsa_mla_variant {
+  int32_t gate_per_dim;   /* 0: gate [rows, H], one logit per (row, head), broadcast over the 128
+                             outputs; 1: gate [rows, H, 128], one logit per output element
+                             (16-byte aligned) */
+  const float* sink;      /* [H] float32 device array of per-head sink logits, in the units of the
+                             scaled logits (natural log), or NULL. Head h's softmax denominator gains
+                             exp(sink[h]), a logit whose value row is zero: the keys' weights then sum
+                             to 1 - exp(sink[h] - lse), and lse includes the sink. */
+} dsa_mla_variant;
+
+/* dsa_sparse_mla_fwd with a variant (NULL: identical to dsa_sparse_mla_fwd). */
+dsa_status dsa_sparse_mla_fwd_ex(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q,
+                                 const uint16_t* kv, const int32_t* topk_idx, const uint16_t* W_UV,
+                                 const uint16_t* gate, uint16_t* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Steps 1-5 in one call: the union of the two argument lists; topk_idx is written and then used. */
 dsa_status dsa_fused_fwd(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
                          const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                          const uint16_t* q, const uint16_t* kv, const uint16_t* W_UV,
                          const uint16_t* gate, int32_t* topk_idx, uint16_t* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* dsa_fused_fwd with a variant of steps 4-5 (NULL: identical to dsa_fused_fwd). */
+dsa_status dsa_fused_fwd_ex(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q_I,
+                            const uint16_t* k_I, const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                            const uint16_t* q, const uint16_t* kv, const uint16_t* W_UV, const uint16_t* gate,
+                            int32_t* topk_idx, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);

@@ -19,9 +19,9 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_index_topk", "dsa_index_topk_noalloc",
-                     "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd", "dsa_status_string", "dsa_up_gate",
-                     "dsa_workspace_size"]
+    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
+                     "dsa_index_topk_noalloc", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
+                     "dsa_sparse_mla_fwd_ex", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -152,3 +152,25 @@ def test_noalloc_entry_point_host_checks():
     assert L.dsa_index_topk_noalloc(ctypes.byref(ok), None, fake, None, None, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_index_topk_noalloc(ctypes.byref(ok), fake, fake, None, None, fake, fake + 4, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_index_topk_noalloc(ctypes.byref(_shape(H=8)), fake, fake, None, None, fake, fake, None) == dsa.DSA_ERR_UNSUPPORTED
+
+
+def test_variant_host_checks():
+    """The gate/sink variant is checked on the host: gate_per_dim must be 0 or 1, an elementwise gate
+    16-byte aligned, the sink 4-byte aligned."""
+    L = dsa.lib()
+    s = _shape()
+    P = ctypes.byref(s)
+    fake = 1 << 20
+    n = dsa.dsa_workspace_size(s)
+    var = dsa.Variant()
+    var.gate_per_dim, var.sink = 2, None
+    args = (fake, fake, fake, fake, fake, fake, None, fake, n, None)
+    assert L.dsa_sparse_mla_fwd_ex(P, ctypes.byref(var), *args) == dsa.DSA_ERR_INVALID_ARG
+    var.gate_per_dim = 1
+    bad_gate = (fake, fake, fake, fake, fake + 2, fake, None, fake, n, None)
+    assert L.dsa_sparse_mla_fwd_ex(P, ctypes.byref(var), *bad_gate) == dsa.DSA_ERR_INVALID_ARG
+    var.gate_per_dim, var.sink = 0, fake + 2
+    assert L.dsa_sparse_mla_fwd_ex(P, ctypes.byref(var), *args) == dsa.DSA_ERR_INVALID_ARG
+    var.sink = None
+    assert L.dsa_sparse_mla_fwd_ex(P, ctypes.byref(var), fake, fake, fake, fake, fake, fake, None, None, n,
+                                   None) == dsa.DSA_ERR_WORKSPACE
