@@ -71,6 +71,15 @@ def _load(path):
     L.oracle_dense_causal.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
     L.oracle_sparse_mla_f32.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
     L.oracle_sparse_mla_variant.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p, p, p, p]
+    L.oracle_quantize_fp8_rows.argtypes = [p, i64, i32, p, p]
+    L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.oracle_e4m3_decode.restype = d
+    L.oracle_e4m3_encode.argtypes = [d]
+    L.oracle_e4m3_encode.restype = ctypes.c_uint8
+    L.oracle_fp8_scale_exponent.argtypes = [d]
+    L.oracle_fp8_scale_exponent.restype = i32
+    L.oracle_index_scores_fp8.argtypes = [p, p, p, i32, i32, p, p, i64, i64, p]
+    L.oracle_topk_fp8.argtypes = [i64, p, p, p, p, i32, i32, p, p, p, i32, i32, p, p, p]
     return L
 
 
@@ -220,3 +229,59 @@ def forward(cfg, inputs, rows):
     mla = sparse_mla(rows, inputs["q"][rows], inputs["kv"], idx, inputs["W_UV"], inputs["gate"][rows],
                      cfg.softmax_scale)
     return idx, theta, keff, mla
+
+
+# ---- FP8 indexer (E4M3 with power-of-two row scales)
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().oracle_e4m3_decode(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(v)))
+
+
+def fp8_scale_exponent(amax: float) -> int:
+    return int(lib().oracle_fp8_scale_exponent(float(amax)))
+
+
+def quantize_fp8_rows(x):
+    """x: bf16 bits [..., d]; returns (E4M3 codes [..., d] uint8, scale exponents [...] int32)."""
+    x, px = _c(x, np.uint16)
+    d = x.shape[-1]
+    n = x.size // d
+    q8 = np.empty(x.shape, dtype=np.uint8)
+    e = np.empty(x.shape[:-1], dtype=np.int32)
+    lib().oracle_quantize_fp8_rows(px, n, d, q8.ctypes.data, e.ctypes.data)
+    return q8, e
+
+
+def index_scores_fp8(q8_row, eq, w_row, k8, ek, s0, s1):
+    q, pq = _c(q8_row, np.uint8)
+    e, pe = _c(eq, np.int32)
+    w, pw = _c(w_row, np.uint16)
+    K, pk = _c(k8, np.uint8)
+    E, pE = _c(ek, np.int32)
+    H_I, d_I = q.shape
+    out = np.empty(s1 - s0 + 1, dtype=np.float32)
+    lib().oracle_index_scores_fp8(pq, pe, pw, H_I, d_I, pk, pE, s0, s1, out.ctypes.data)
+    return out
+
+
+def topk_fp8(rows, q8_rows, eq_rows, w_rows, k8, ek, cu_seqlens, k):
+    """FP8-indexer top-k of the listed global rows; returns (idx [n,k] int32, theta [n], keff [n])."""
+    rows, pr = _c(rows, np.int64)
+    q, pq = _c(q8_rows, np.uint8)
+    e, pe = _c(eq_rows, np.int32)
+    w, pw = _c(w_rows, np.uint16)
+    K, pk = _c(k8, np.uint8)
+    E, pE = _c(ek, np.int32)
+    cu, pc = _c(cu_seqlens, np.int32)
+    n = len(rows)
+    H_I, d_I = q.shape[-2], q.shape[-1]
+    idx = np.empty((n, k), dtype=np.int32)
+    theta = np.empty(n, dtype=np.float32)
+    keff = np.empty(n, dtype=np.int32)
+    lib().oracle_topk_fp8(n, pr, pq, pe, pw, H_I, d_I, pk, pE, pc, len(cu) - 1, k, idx.ctypes.data,
+                          theta.ctypes.data, keff.ctypes.data)
+    return idx, theta, keff

@@ -88,6 +88,48 @@ int64_t doc_begin(const int32_t* cu, int32_t n_docs, int64_t t) {
   return -1;
 }
 
+// ---- FP8 E4M3 (the OCP 8-bit floating-point format "E4M3": 1 sign bit, 4 exponent bits with
+// bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; no infinities; S.1111.111
+// is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448). Written from that definition.
+
+// Value of an E4M3 code.
+double e4m3_decode(uint8_t c) {
+  const int sgn = c >> 7, E = (c >> 3) & 15, m = c & 7;
+  if (E == 15 && m == 7) return std::numeric_limits<double>::quiet_NaN();
+  const double mag = E == 0 ? std::ldexp(static_cast<double>(m), -9) : std::ldexp(1.0 + m / 8.0, E - 7);
+  return sgn ? -mag : mag;
+}
+
+// Nearest E4M3 code to v (ties to the even code), for |v| <= 448.
+uint8_t e4m3_encode(double v) {
+  const uint8_t sgn = std::signbit(v) ? 0x80 : 0x00;
+  const double a = std::fabs(v);
+  if (a == 0.0) return sgn;
+  if (a < std::ldexp(1.0, -6)) {  // subnormal range: multiples of 2^-9
+    const double q = std::nearbyint(std::ldexp(a, 9));  // default rounding mode: ties to even
+    return static_cast<uint8_t>(sgn | static_cast<int>(q));  // q == 8 is the smallest normal, code 0x08
+  }
+  int ex = 0;
+  const double m = std::frexp(a, &ex);  // a = m * 2^ex, m in [0.5, 1)
+  int E = ex - 1;                       // a = (2m) * 2^E, 2m in [1, 2)
+  double q = std::nearbyint((2.0 * m - 1.0) * 8.0);
+  if (q == 8.0) {
+    q = 0.0;
+    ++E;
+  }
+  return static_cast<uint8_t>(sgn | ((E + 7) << 3) | static_cast<int>(q));
+}
+
+// Exponent of a row's power-of-two scale: the smallest integer e with amax * 2^-e <= 448 (0 for an
+// all-zero row).
+int fp8_scale_exponent(double amax) {
+  if (amax == 0.0) return 0;
+  int e = std::ilogb(amax) - 8;
+  while (std::ldexp(amax, -e) > 448.0) ++e;
+  while (std::ldexp(amax, -(e - 1)) <= 448.0) --e;
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +220,36 @@ void oracle_index_score_scale(const uint16_t* qI_row, const uint16_t* w_row, int
 //    are stably sorted by score, highest first (so equal scores keep the lower index).
 // idx_out[r, :] holds the kept global indices in ascending order, then -1 up to k.
 // theta_out[r] = score of the k-th kept key (NaN when n_t <= k); keff_out[r] = min(k, n_t).
+}  // extern "C"
+
+// Selection of one row (t in the document starting at b), given a function that fills the scores of
+// keys b..t: every causal key when n_t <= k, else the first k of the causal keys listed in ascending
+// index order and stably sorted by score, highest first.
+template <typename ScoreFn>
+static void select_row(int64_t b, int64_t t, int32_t k, ScoreFn scores, int32_t* out, float* theta_out,
+                       int32_t* keff_out) {
+  const int64_t n_t = t - b + 1;
+  std::vector<int64_t> kept;
+  float theta = std::numeric_limits<float>::quiet_NaN();
+  if (n_t <= k) {
+    for (int64_t s = b; s <= t; ++s) kept.push_back(s);
+  } else {
+    std::vector<float> S(static_cast<size_t>(n_t));
+    scores(S.data());
+    std::vector<int64_t> order(static_cast<size_t>(n_t));
+    std::iota(order.begin(), order.end(), b);  // ascending key index
+    std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) { return S[x - b] > S[y - b]; });
+    kept.assign(order.begin(), order.begin() + k);
+    theta = S[kept.back() - b];
+    std::sort(kept.begin(), kept.end());
+  }
+  for (int32_t j = 0; j < k; ++j) out[j] = j < static_cast<int32_t>(kept.size()) ? static_cast<int32_t>(kept[j]) : -1;
+  *theta_out = theta;
+  *keff_out = static_cast<int32_t>(kept.size());
+}
+
+extern "C" {
+
 void oracle_topk(int64_t n_rows, const int64_t* rows, const uint16_t* qI_rows, const uint16_t* w_rows,
                  int32_t H_I, int32_t d_I, const uint16_t* LNk, const int32_t* cu, int32_t n_docs, int32_t k,
                  int32_t* idx_out, float* theta_out, int32_t* keff_out) {
@@ -185,27 +257,68 @@ void oracle_topk(int64_t n_rows, const int64_t* rows, const uint16_t* qI_rows, c
   for (int64_t r = 0; r < n_rows; ++r) {
     const int64_t t = rows[r];
     const int64_t b = doc_begin(cu, n_docs, t);
-    const int64_t n_t = t - b + 1;
-    int32_t* out = idx_out + r * k;
-    std::vector<int64_t> kept;
-    float theta = std::numeric_limits<float>::quiet_NaN();
-    if (n_t <= k) {
-      for (int64_t s = b; s <= t; ++s) kept.push_back(s);
-    } else {
-      std::vector<float> S(static_cast<size_t>(n_t));
-      oracle_index_scores(qI_rows + r * static_cast<int64_t>(H_I) * d_I, w_rows + r * H_I, H_I, d_I, LNk, b, t,
-                          S.data());
-      std::vector<int64_t> order(static_cast<size_t>(n_t));
-      std::iota(order.begin(), order.end(), b);  // ascending key index
-      std::stable_sort(order.begin(), order.end(),
-                       [&](int64_t x, int64_t y) { return S[x - b] > S[y - b]; });
-      kept.assign(order.begin(), order.begin() + k);
-      theta = S[kept.back() - b];
-      std::sort(kept.begin(), kept.end());
+    select_row(b, t, k, [&](float* S) {
+      oracle_index_scores(qI_rows + r * static_cast<int64_t>(H_I) * d_I, w_rows + r * H_I, H_I, d_I, LNk, b, t, S);
+    }, idx_out + r * k, theta_out + r, keff_out + r);
+  }
+}
+
+// ---- FP8 indexer ([KC] Implementation Limits, 2nd bullet: the BF16 indexer "is not the FP8 indexer"
+// of some serving kernels). The pages give no recipe; the one used here: each 128-wide row (a key's
+// LN output, one head of a query's q_I) is scaled by a power of two 2^-e, e the smallest integer
+// that brings its largest magnitude to at most 448, and rounded to E4M3 (nearest, ties to even).
+// The products of two E4M3 values are exact in FP32 and are summed in FP32; ReLU, the head weight
+// times the query row's head scale 2^e_q, the head sum in FP32, then the key's scale 2^e_k.
+
+// Quantise n rows of d bf16 values: q8 [n,d] E4M3 codes, e [n] scale exponents.
+void oracle_quantize_fp8_rows(const uint16_t* x, int64_t n, int32_t d, uint8_t* q8, int32_t* e) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    const uint16_t* xr = x + r * d;
+    double amax = 0.0;
+    for (int32_t i = 0; i < d; ++i) amax = std::max(amax, std::fabs(static_cast<double>(bf16_bits_to_float(xr[i]))));
+    const int ex = fp8_scale_exponent(amax);
+    e[r] = ex;
+    for (int32_t i = 0; i < d; ++i) q8[r * d + i] = e4m3_encode(std::ldexp(static_cast<double>(bf16_bits_to_float(xr[i])), -ex));
+  }
+}
+
+double oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+uint8_t oracle_e4m3_encode(double v) { return e4m3_encode(v); }
+int32_t oracle_fp8_scale_exponent(double amax) { return fp8_scale_exponent(amax); }
+
+// FP8 scores of one query (q8_row [H_I,d_I] codes, eq [H_I], w_row [H_I] bf16) over keys s0..s1 of
+// (k8 [*,d_I] codes, ek [*]):  S = 2^ek[s] * sum_h (w_h * 2^eq_h) * ReLU( sum_i q8[h,i] * k8[s,i] ).
+void oracle_index_scores_fp8(const uint8_t* q8_row, const int32_t* eq, const uint16_t* w_row, int32_t H_I,
+                             int32_t d_I, const uint8_t* k8, const int32_t* ek, int64_t s0, int64_t s1, float* S) {
+  std::vector<float> qv(static_cast<size_t>(H_I) * d_I), wq(H_I);
+  for (int64_t i = 0; i < static_cast<int64_t>(qv.size()); ++i) qv[i] = static_cast<float>(e4m3_decode(q8_row[i]));
+  for (int32_t h = 0; h < H_I; ++h) wq[h] = std::ldexp(bf16_bits_to_float(w_row[h]), eq[h]);  // exact
+  for (int64_t s = s0; s <= s1; ++s) {
+    float score = 0.0f;
+    for (int32_t h = 0; h < H_I; ++h) {
+      float dot = 0.0f;
+      for (int32_t i = 0; i < d_I; ++i) dot += qv[h * d_I + i] * static_cast<float>(e4m3_decode(k8[s * d_I + i]));
+      const float rl = dot > 0.0f ? dot : 0.0f;
+      score += wq[h] * rl;
     }
-    for (int32_t j = 0; j < k; ++j) out[j] = j < static_cast<int32_t>(kept.size()) ? static_cast<int32_t>(kept[j]) : -1;
-    theta_out[r] = theta;
-    keff_out[r] = static_cast<int32_t>(kept.size());
+    S[s - s0] = std::ldexp(score, ek[s]);
+  }
+}
+
+// Hard top-k on the FP8 scores; same outputs as oracle_topk.
+void oracle_topk_fp8(int64_t n_rows, const int64_t* rows, const uint8_t* q8_rows, const int32_t* eq_rows,
+                     const uint16_t* w_rows, int32_t H_I, int32_t d_I, const uint8_t* k8, const int32_t* ek,
+                     const int32_t* cu, int32_t n_docs, int32_t k, int32_t* idx_out, float* theta_out,
+                     int32_t* keff_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t t = rows[r];
+    const int64_t b = doc_begin(cu, n_docs, t);
+    select_row(b, t, k, [&](float* S) {
+      oracle_index_scores_fp8(q8_rows + r * static_cast<int64_t>(H_I) * d_I, eq_rows + r * H_I, w_rows + r * H_I,
+                              H_I, d_I, k8, ek, b, t, S);
+    }, idx_out + r * k, theta_out + r, keff_out + r);
   }
 }
 

@@ -546,3 +546,118 @@ def test_gate_per_dim():
     rz = oracle.sparse_mla_variant(rows, q, inp["kv"], idx, inp["W_UV"], np.zeros_like(gd), cfg.softmax_scale,
                                    gate_per_dim=True)
     assert np.array_equal(rz["out"], rz["o_pre"] / 2)
+
+
+# ---------------------------------------------------------------- FP8 indexer (KC Implementation Limits, 2nd bullet)
+
+def test_e4m3_decode_table():
+    """All 256 E4M3 codes against the format's closed forms and torch's float8_e4m3fn (library
+    cross-check): subnormals m*2^-9, normals (1+m/8)*2^(E-7), 448 the largest, S.1111.111 NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = np.array([oracle.e4m3_decode(c) for c in codes])
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+    assert [c for c in codes if np.isnan(mine[c])] == [0x7F, 0xFF]
+    assert mine[0x01] == 2.0 ** -9 and mine[0x07] == 7 * 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+    assert mine[0x38] == 1.0 and mine[0x7E] == 448.0 and mine[0x80] == 0.0 and np.signbit(mine[0x80])
+    assert np.nanmax(np.abs(mine)) == 448.0
+
+
+def test_e4m3_encode_round_to_nearest_even():
+    """Every finite code round-trips; every midpoint between neighbours goes to the neighbour with an
+    even code, and the smallest step off a midpoint goes to the nearer one; negative values mirror;
+    torch's conversion agrees on random values (library cross-check)."""
+    pos = [c for c in range(0x7F)]  # 0x00 .. 0x7E: every nonnegative finite code, increasing in value
+    vals = [oracle.e4m3_decode(c) for c in pos]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+    for c, v in zip(pos, vals):
+        assert oracle.e4m3_encode(v) == c and oracle.e4m3_encode(-v) == (c | 0x80)
+    for c in range(len(pos) - 1):
+        lo, hi = vals[c], vals[c + 1]
+        mid = (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, (hex(c), mid)
+        assert oracle.e4m3_encode(-mid) == (even | 0x80)
+        step = (hi - lo) * 2.0 ** -12
+        assert oracle.e4m3_encode(mid - step) == c and oracle.e4m3_encode(mid + step) == c + 1
+    x = np.random.default_rng(3).uniform(-448, 448, 20000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ref, np.array([oracle.e4m3_encode(float(v)) for v in x]))
+
+
+def test_fp8_scale_exponent_closed_forms():
+    """The smallest e with amax * 2^-e <= 448."""
+    cases = {448.0: 0, 450.0: 1, 224.0: -1, 225.0: 0, 1.0: -8, 1.75: -8, 1.875: -7, 3.5: -7, 2.0 ** -130: -138,
+             0.0: 0, 896.0: 1, 897.0: 2}
+    for amax, e in cases.items():
+        assert oracle.fp8_scale_exponent(amax) == e, (amax, e)
+        if amax > 0:
+            assert amax * 2.0 ** -e <= 448.0 < amax * 2.0 ** -(e - 1)
+
+
+def test_quantize_fp8_rows_bounds_and_torch():
+    """Each row's codes times 2^e lie within half a code step of the bf16 values, the row maximum uses
+    the top of the range, and the codes equal torch's E4M3 conversion of x * 2^-e."""
+    x = tg.normal_bf16(12, 1, 0, 300 * 128, 1.0).reshape(300, 128)
+    x[7] = 0
+    x[8, :] = _bf(np.full(128, 2.0 ** -20))
+    q8, e = oracle.quantize_fp8_rows(x)
+    xf = f32(x).astype(np.float64)
+    dec = np.vectorize(oracle.e4m3_decode)(q8) * np.ldexp(1.0, e)[:, None]
+    for r in range(300):
+        amax = np.abs(xf[r]).max()
+        if amax == 0:
+            assert e[r] == 0 and np.all(q8[r] == 0)
+            continue
+        assert 224.0 < amax * 2.0 ** -e[r] <= 448.0
+        # half a step of E4M3 at each value's magnitude (subnormal step 2^-9), times 2^e
+        mag = np.abs(xf[r]) * 2.0 ** -e[r]
+        step = np.where(mag < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 3))
+        assert np.all(np.abs(dec[r] - xf[r]) <= step / 2 * 2.0 ** e[r] * (1 + 1e-12))
+    scaled = torch.from_numpy((xf * np.ldexp(1.0, -e)[:, None]).astype(np.float32))
+    assert np.array_equal(scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), q8)
+
+
+def test_fp8_scores_equal_bf16_scores_when_exact():
+    """When every q_I and LNk value is exactly representable in E4M3 after its row's scaling, the FP8
+    indexer's scores equal the BF16 indexer's bit for bit (power-of-two scales commute with FP32
+    rounding here), for every key."""
+    rng = np.random.default_rng(13)
+    H_I, d_I, T = 4, 64, 50
+    grid = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 3, 4, 6], np.float32)
+    def rows(n, width, top):
+        v = rng.choice(grid, (n, width)) * rng.choice([-1, 1], (n, width))
+        v[:, 0] = top                                    # fixes each row's maximum magnitude
+        return v * np.ldexp(1.0, rng.integers(-3, 4, (n, 1))).astype(np.float32)
+    LNk = _bf(rows(T, d_I, 7.0))
+    q = _bf(rows(H_I, d_I, -5.0))
+    w = _bf(rng.uniform(0, 1, H_I))
+    k8, ek = oracle.quantize_fp8_rows(LNk)
+    q8, eq = oracle.quantize_fp8_rows(q)
+    assert np.array_equal(np.vectorize(oracle.e4m3_decode)(k8) * np.ldexp(1.0, ek)[:, None], f32(LNk))
+    S8 = oracle.index_scores_fp8(q8, eq, w, k8, ek, 0, T - 1)
+    S = oracle.index_scores(q, w, LNk, 0, T - 1)
+    assert np.array_equal(S8, S)
+
+
+def test_topk_fp8_brute_force_tiny():
+    """FP8 top-k against a full sort of the FP8 scores by (score desc, index asc)."""
+    rng = np.random.default_rng(14)
+    T, H_I, d_I, k = 120, 64, 128, 17
+    LNk = oracle.key_layernorm(_bf(rng.standard_normal((T, d_I))))
+    k8, ek = oracle.quantize_fp8_rows(LNk)
+    q = _bf(rng.standard_normal((T, H_I, d_I)))
+    w = _bf(rng.uniform(0, 1 / 8, (T, H_I)))
+    q8, eq = oracle.quantize_fp8_rows(q)
+    rows = np.arange(T)
+    idx, theta, keff = oracle.topk_fp8(rows, q8, eq, w, k8, ek, np.array([0, T], np.int32), k)
+    agree = []
+    for t in range(k, T):
+        S = oracle.index_scores_fp8(q8[t], eq[t], w[t], k8, ek, 0, t)
+        order = np.lexsort((np.arange(t + 1), -S.astype(np.float64)))[:k]
+        assert sorted(order.tolist()) == idx[t][:k].tolist()
+        assert theta[t] == S[order[-1]]
+        b16 = oracle.topk([t], q[[t]], w[[t]], LNk, np.array([0, T], np.int32), k)[0][0]
+        agree.append(len(set(b16.tolist()) & set(idx[t].tolist())) / k)
+    assert np.mean(agree) > 0.8   # the FP8 selection stays close to the BF16 one
