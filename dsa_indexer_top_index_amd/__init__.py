@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   dsa_fused_fwd(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace,
                 ln_gamma=None, ln_beta=None, lse=None)
   dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None)
+  dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
+  dsa_quantize_fp8(x, q8, scale)
   dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
   gate [rows,H,128] and per-head sink logits [H] float32)
 """
@@ -89,6 +91,10 @@ def lib():
         L.dsa_fused_fwd.restype = ctypes.c_int
         L.dsa_index_topk_noalloc.argtypes = [P, v, v, v, v, v, v, v]
         L.dsa_index_topk_noalloc.restype = ctypes.c_int
+        L.dsa_index_topk_fp8.argtypes = [P, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_index_topk_fp8.restype = ctypes.c_int
+        L.dsa_quantize_fp8.argtypes = [ctypes.c_int64, v, v, v, v]
+        L.dsa_quantize_fp8.restype = ctypes.c_int
         V = ctypes.POINTER(Variant)
         L.dsa_sparse_mla_fwd_ex.argtypes = [P, V, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_sparse_mla_fwd_ex.restype = ctypes.c_int
@@ -199,6 +205,25 @@ def dsa_index_topk(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_be
         _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_index_topk")
+
+
+def dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None):
+    """dsa_index_topk with the FP8 indexer (E4M3 operands, power-of-two row scales; H_I=64, d_I=128)."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    st = lib().dsa_index_topk_fp8(
+        ctypes.byref(shape), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_index_topk_fp8")
+
+
+def dsa_quantize_fp8(x, q8, scale):
+    """Rows of 128 bf16 values (x [n,128]) -> E4M3 codes q8 [n,128] uint8 and scale [n] float32."""
+    rows = x.numel() // 128
+    st = lib().dsa_quantize_fp8(rows, _p(x, torch.bfloat16, "x", numel=rows * 128), _p(q8, torch.uint8, "q8", numel=rows * 128),
+                                _p(scale, torch.float32, "scale", numel=rows), _stream())
+    _raise(st, "dsa_quantize_fp8")
 
 
 def dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None):

@@ -30,9 +30,12 @@ int32_t rows_of(const dsa_shape* s) { return (s->q_end == 0 ? s->T : s->q_end) -
 //   LNk    [T + kIdxKeyPad, d_I] bf16   key LayerNorm output (the padding rows are staged, never scored)
 //   flags  [kIdxSlots] int32           candidate-slot claims of the indexer's workgroups
 //   cand   [kIdxSlots, slot words]     candidate token indices of the rows in flight
+//   LNk8   [T + kIdxKeyPad, d_I] u8    FP8 indexer: E4M3 codes of LNk, and sk [T + kIdxKeyPad] f32
+//   q8     [rows, H_I, d_I] u8         FP8 indexer: E4M3 codes of q_I, and sq [rows, H_I] f32
 //   o_lat  [chunk rows, H, 512] bf16   latent attention output of one row chunk
 struct Layout {
-  size_t lnk_off, lnk_bytes, flags_off, cand_off, cand_bytes, olat_off, olat_bytes, total;
+  size_t lnk_off, lnk_bytes, flags_off, cand_off, cand_bytes, lnk8_off, sk_off, q8_off, sq_off, olat_off, olat_bytes,
+      total;
   int64_t chunk_rows;
 };
 
@@ -44,8 +47,13 @@ Layout layout_of(const dsa_shape* s) {
   L.cand_off = L.flags_off + align_up(static_cast<size_t>(dsa::kIdxSlots) * 4);
   L.cand_bytes = align_up(static_cast<size_t>(dsa::kIdxSlots) * dsa::kIdxSlotWords * 4);
   const int64_t rows = rows_of(s);
+  const size_t keys_pad = static_cast<size_t>(s->T + dsa::kIdxKeyPad);
+  L.lnk8_off = L.cand_off + L.cand_bytes;
+  L.sk_off = L.lnk8_off + align_up(keys_pad * s->d_I);
+  L.q8_off = L.sk_off + align_up(keys_pad * 4);
+  L.sq_off = L.q8_off + align_up(static_cast<size_t>(rows) * s->H_I * s->d_I);
   L.chunk_rows = rows < kMlaChunkRows ? rows : kMlaChunkRows;
-  L.olat_off = L.cand_off + L.cand_bytes;
+  L.olat_off = L.sq_off + align_up(static_cast<size_t>(rows) * s->H_I * 4);
   L.olat_bytes = align_up(static_cast<size_t>(L.chunk_rows) * s->H * 512 * 2);
   L.total = L.olat_off + L.olat_bytes;
   return L;
@@ -110,7 +118,7 @@ struct Seg {
 // caller storage for at least s->n_docs entries (no allocation happens here).
 static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* gamma,
                             const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, Seg* segs,
-                            hipStream_t st) {
+                            hipStream_t st, bool fp8 = false) {
   const auto L = layout_of(s);
   uint16_t* lnk = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.lnk_off);
   dsa::IndexArgs a{};
@@ -131,6 +139,21 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   a.n_slots = dsa::kIdxSlots;
   if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st) != hipSuccess)
     return DSA_ERR_LAUNCH;
+  if (fp8) {
+    // E4M3 codes and scales of LNk (the T key rows) and of q_I (every head row of the query rows)
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint8_t* lnk8 = base + L.lnk8_off;
+    float* sk = reinterpret_cast<float*>(base + L.sk_off);
+    uint8_t* q8 = base + L.q8_off;
+    float* sq = reinterpret_cast<float*>(base + L.sq_off);
+    a.LNk8 = lnk8;
+    a.sk = sk;
+    a.q8 = q8;
+    a.sq = sq;
+    if (dsa::launch_quantize_fp8(lnk, s->T, lnk8, sk, q_I, static_cast<int64_t>(a.nrows) * s->H_I, q8, sq, st) !=
+        hipSuccess)
+      return DSA_ERR_LAUNCH;
+  }
   // Rows with more than k causal keys, one segment per document. With few such rows per CU,
   // blocks pair long and short rows of a document so that every block carries about the same
   // work; otherwise blocks take consecutive rows, longest first.
@@ -163,7 +186,7 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
       a.seg_b[a.nseg] = segs[i].b;
       a.seg_blk0[a.nseg + 1] = a.seg_blk0[a.nseg] + dsa::index_blocks(segs[i].m, a.paired);
     }
-    const hipError_t e = dsa::launch_index_topk(a, s->H_I, s->d_I, st);
+    const hipError_t e = dsa::launch_index_topk(a, s->H_I, s->d_I, fp8, st);
     if (e == hipErrorInvalidConfiguration) return DSA_ERR_UNSUPPORTED;  // more resident workgroups than slots
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
   }
@@ -242,6 +265,31 @@ static dsa_status check_variant(const dsa_mla_variant* v, const uint16_t* gate) 
   if (v->gate_per_dim && !aligned(gate, 16)) return DSA_ERR_INVALID_ARG;
   if (!aligned(v->sink, 4)) return DSA_ERR_INVALID_ARG;
   return DSA_OK;
+}
+
+dsa_status dsa_index_topk_fp8(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
+                              const float* ln_beta, const uint16_t* w, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                              void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!(s->H_I == 64 && s->d_I == 128)) return DSA_ERR_UNSUPPORTED;
+  if (!q_I || !k_I || !w || !topk_idx) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_I, 16) || !aligned(k_I, 2) || !aligned(w, 2) || !aligned(topk_idx, 16) || !aligned(ln_gamma, 4) ||
+      !aligned(ln_beta, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
+  std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
+  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), static_cast<hipStream_t>(stream),
+                   true);
+}
+
+dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream) {
+  if (n_rows < 0 || (n_rows > 0 && (!x || !q8 || !scale))) return DSA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q8, 16) || !aligned(scale, 4)) return DSA_ERR_INVALID_ARG;
+  return dsa::launch_quantize_fp8(x, n_rows, q8, scale, nullptr, 0, nullptr, nullptr, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? DSA_OK
+             : DSA_ERR_LAUNCH;
 }
 
 dsa_status dsa_sparse_mla_fwd_ex(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,

@@ -24,7 +24,11 @@ struct IndexArgs {
   int row0;              // global token of local row 0
   int nrows;
   int k;
-  int32_t* cand;         // candidate token indices: n_slots slots of index_slot_words() int32 each
+  const uint8_t* q8;     // FP8 indexer: [nrows, H_I, d_I] E4M3 codes of q_I
+  const float* sq;       //   [nrows, H_I] their power-of-two scales
+  const uint8_t* LNk8;   //   [T + kIdxKeyPad, d_I] E4M3 codes of LNk
+  const float* sk;       //   [T + kIdxKeyPad] their power-of-two scales
+  int32_t* cand;         // candidate token indices: n_slots slots of kIdxSlotWords int32 each
   int* slot_flags;       // [n_slots] 1 while a workgroup holds the slot; zeroed by the prologue
   int n_slots;
   // Rows that need a selection, as segments of consecutive local rows of one document each.
@@ -71,7 +75,11 @@ struct UpArgs {
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
 hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
                                  uint16_t* LNk, const IndexArgs& a, hipStream_t st);
-hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st);
+hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st);
+// FP8 indexer operands: n rows of 128 bf16 values -> E4M3 codes and the rows' power-of-two scales
+// (smallest 2^e with amax * 2^-e <= 448). Two independent row sets in one launch (n2 may be 0).
+hipError_t launch_quantize_fp8(const uint16_t* x1, int64_t n1, uint8_t* q1, float* s1, const uint16_t* x2, int64_t n2,
+                               uint8_t* q2, float* s2, hipStream_t st);
 int index_blocks(int m, int paired);  // blocks of a segment of m rows
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);

@@ -36,6 +36,7 @@
 #include "dsa_kernels.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace dsa {
 
@@ -475,14 +476,18 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
   }
 }
 
-template <int H_I, int D_I>
+// F8: the FP8 indexer (E4M3 operands with power-of-two row scales, v_mfma_scale_f32_32x32x64_f8f6f4);
+// otherwise BF16 operands on v_mfma_f32_32x32x16_bf16. Everything after the scores is shared.
+template <int H_I, int D_I, bool F8>
 __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a) {
   constexpr int MT = (H_I + 31) / 32;   // 32-row M tiles of indexer heads
-  constexpr int KS = D_I / 16;          // MFMA K steps
-  constexpr int GPR = D_I / 8;          // 16-byte granules per key row
+  constexpr int KS = F8 ? D_I / 64 : D_I / 16;  // MFMA K steps
+  constexpr int GPR = F8 ? D_I / 16 : D_I / 8;  // 16-byte granules per key row
   constexpr int CHUNK_GRAN = kChunk * GPR;
   constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies (1 KB operand blocks) per chunk and wave
-  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && 2 * KS * kWave == CHUNK_GRAN, "chunk copy split");
+  // a 32-key tile's K step is one 1 KB block (BF16: 16 bytes per lane) or two (FP8: 32 bytes per lane)
+  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && (F8 ? 4 : 2) * KS * kWave == CHUNK_GRAN, "chunk copy split");
+  using QOp = typename std::conditional<F8, i32x8, bf16x8>::type;
 
   __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
   __shared__ __attribute__((aligned(16))) uint32_t s_keys[kIdxRows * kListSlots];  // candidate score keys (token indices: global)
@@ -567,19 +572,35 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 
   // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
   // the MFMAs read directly. Head weights go to LDS, read back by the score epilogue.
-  bf16x8 qa[MT][KS];
+  // FP8: 32 bytes per lane and K step, K values 64*s + 32*(lane/32) .. +32 of its head (the key
+  // operand takes the same K values, so the pairing does not depend on the instruction's K order);
+  // the head's scale goes into its weight.
+  QOp qa[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = 32 * mt + (lane & 31);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (select && head < H_I) {
-        qa[mt][s] = *reinterpret_cast<const bf16x8*>(a.q_I + (static_cast<int64_t>(r) * H_I + head) * D_I + 16 * s + 8 * (lane >> 5));
+        if constexpr (F8) {
+          const uint8_t* src = a.q8 + (static_cast<int64_t>(r) * H_I + head) * D_I + 64 * s + 32 * (lane >> 5);
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(src), hi = *reinterpret_cast<const i32x4*>(src + 16);
+          qa[mt][s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          qa[mt][s] = *reinterpret_cast<const bf16x8*>(a.q_I + (static_cast<int64_t>(r) * H_I + head) * D_I + 16 * s + 8 * (lane >> 5));
+        }
       } else {
-        qa[mt][s] = bf16x8{};
+        qa[mt][s] = QOp{};
       }
     }
-    if (lane < 32) s_w[wave][32 * mt + lane] = (select && head < H_I) ? bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + head]) : 0.0f;
+    if (lane < 32) {
+      float wv = 0.0f;
+      if (select && head < H_I) {
+        wv = bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + head]);
+        if constexpr (F8) wv *= a.sq[static_cast<int64_t>(r) * H_I + head];  // a power of two: exact
+      }
+      s_w[wave][32 * mt + lane] = wv;
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -620,18 +641,27 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // reads are then whole 1 KB blocks at constant offsets (bank-conflict free) and every copy fills
   // one block. Copy j of this wave fills block CPW*wave + j; its per-lane source offset within a
   // chunk is fixed, the chunk's first key row a scalar base.
+  // FP8: block (n, s, h) = 4 * ... holds, at lane i's 16 bytes, half h of lane i's 32-byte operand of
+  // K step s of tile n: key 32n + i%32, K bytes 64s + 32(i/32) + 16h .. +16.
   uint32_t cp_off[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int blk_j = CPW * wave + j, n = blk_j / KS, st = blk_j % KS;
-    cp_off[j] = static_cast<uint32_t>(((32 * n + (lane & 31)) * D_I + 8 * (2 * st + (lane >> 5))) * 2);
+    const int blk_j = CPW * wave + j;
+    if constexpr (F8) {
+      const int n = blk_j / (2 * KS), st = (blk_j % (2 * KS)) >> 1, hf = blk_j & 1;
+      cp_off[j] = static_cast<uint32_t>((32 * n + (lane & 31)) * D_I + 64 * st + 32 * (lane >> 5) + 16 * hf);
+    } else {
+      const int n = blk_j / KS, st = blk_j % KS;
+      cp_off[j] = static_cast<uint32_t>(((32 * n + (lane & 31)) * D_I + 8 * (2 * st + (lane >> 5))) * 2);
+    }
   }
   // A chunk may reach past the last key row (up to two chunks past it, see kIdxKeyPad): those rows
   // of the padded LNk are staged but never scored.
   auto issue_copy = [&](int c, int j) {
     const int K0 = kb + c * kChunk;
     const uint32_t lds = lds_addr_of(stage[c & 1]) + 1024 * (CPW * wave + j);
-    copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+    if constexpr (F8) copy16_to_lds_imm<0>(a.LNk8 + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+    else copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
   };
   auto issue_chunk = [&](int c) {
 #pragma unroll
@@ -658,7 +688,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   }
   constexpr int kEl = MT * 16;        // accumulator elements per lane of one N tile
   constexpr int kEps = kEl / KS;      // epilogue elements per K step
-  static_assert(kEl % KS == 0 && kEps >= 1 && kEps <= 8, "epilogue split");
+  static_assert(kEl % KS == 0 && kEps >= 1 && kEps <= (F8 ? 16 : 8), "epilogue split");
   constexpr int kPf = KS < 2 ? KS : 2;  // key operands are read kPf K steps ahead of their MFMAs
   // One N tile of chunk c into acc, interleaved with the epilogue of `prev`; returns this lane's
   // partial sum over its heads of the previous tile (one key column per lane).
@@ -677,7 +707,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf], s == 0 ? f32x16{} : acc[mt], 0, 0, 0);
+        if constexpr (!F8) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf], s == 0 ? f32x16{} : acc[mt], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < kEps; ++j) {
         const int el = s * kEps + j, mt = el / 16, i = el % 16;
@@ -700,6 +730,45 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 #pragma unroll
     for (int j = 1; j < kEps; ++j) p += part[j];
     return p;
+  };
+  // The FP8 form of tile_step: the tile's two K steps read as four 1 KB blocks at once, each K step
+  // one 32x32x64 MFMA per M tile beside its half of the epilogue (kept in four partial sums).
+  auto tile_step8 = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
+    uint32_t a0 = lds_addr_of(stage[c & 1]) + n * (2 * KS * 1024) + 16 * lane;
+    asm volatile("" : "+v"(a0));
+    i32x8 bk[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const i32x4 lo = __builtin_bit_cast(i32x4, lds_read16(lds_ptr(a0 + 2048 * s)));
+      const i32x4 hi = __builtin_bit_cast(i32x4, lds_read16(lds_ptr(a0 + 2048 * s + 1024)));
+      bk[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    constexpr int NP = 4;
+    float part[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) part[j] = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (F8) acc[mt] = mfma32_fp8(qa[mt][s], bk[s], s == 0 ? f32x16{} : acc[mt]);
+      }
+#pragma unroll
+      for (int j = 0; j < kEps; ++j) {
+        const int el = s * kEps + j, mt = el / 16, i = el % 16;
+        part[j % NP] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j % NP]);
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j) asm volatile("" : "+v"(part[j]));
+      side(s);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kEps, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT - 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kEps + 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return (part[0] + part[1]) + (part[2] + part[3]);
   };
   // The epilogue of `prev` alone (a row's last chunk, or a wave whose row has ended).
   auto tile_drain = [&](const f32x16 (&prev)[MT]) -> float {
@@ -741,7 +810,13 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     s_need[nbuf][wave] = cnt > cap - kChunk && more ? cnt : 0;  // every lane writes the same value
   };
 
+  auto tile = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
+    if constexpr (F8) return tile_step8(c, n, acc, prev, side);
+    else return tile_step(c, n, acc, prev, side);
+  };
   float p0_prev = 0.0f;  // tile-0 partial sums of the previous chunk
+  // FP8: the key scales of the previous chunk (lane l: key l), loaded a step before they are used
+  float sk_prev = 1.0f;
   issue_chunk(0);
   // Step c: tile 0 of chunk c (the next chunk's copies issued between its MFMAs), then the
   // selections that the lists filled by step c-1 asked for, then tile 1 of chunk c with the append
@@ -758,10 +833,15 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     auto copies = [&](int st) {
       if (st < CPW) issue_copy(c + 1, st);
     };
+    float sk_cur = 1.0f;
+    if constexpr (F8) {
+      if (c < nchunks) sk_cur = a.sk[kb + c * kChunk + lane];  // within the padded key rows
+    }
     float score_prev = 0.0f;
     if (act) {
       // a wave whose row ends before this chunk leaves its SIMD to the other wave there
-      score_prev = join(p0_prev, tile_step(c, 0, accA, accB, copies));
+      score_prev = join(p0_prev, tile(c, 0, accA, accB, copies));
+      if constexpr (F8) score_prev *= sk_prev;  // a power of two: exact
     } else if (c + 1 < nchunks) {
 #pragma unroll
       for (int j = 0; j < CPW; ++j) issue_copy(c + 1, j);
@@ -772,10 +852,13 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       auto app = [&](int st) {
         if (st == 0) append(c - 1, score_prev, (c + 1) & 1);  // early, so its index stores land before the next step's wait
       };
-      p0_prev = tile_step(c, 1, accB, accA, app);
+      p0_prev = tile(c, 1, accB, accA, app);
     } else if (act_prev) {
-      append(c - 1, join(p0_prev, tile_drain(accB)), (c + 1) & 1);
+      float sc = join(p0_prev, tile_drain(accB));
+      if constexpr (F8) sc *= sk_prev;
+      append(c - 1, sc, (c + 1) & 1);
     }
+    sk_prev = sk_cur;
   }
 
   // Final exact selection: each wave finishes its own row, with a histogram in the staging ring,
@@ -806,30 +889,78 @@ int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m
 
 // Workgroups of the indexer kernel that the current device can hold at once (CUs x occupancy),
 // computed once per device.
-static int index_resident_blocks(int H_I, int d_I) {
+static const void* index_kernel(int v) {
+  switch (v) {
+    case 0: return reinterpret_cast<const void*>(k_index_topk<64, 128, false>);
+    case 1: return reinterpret_cast<const void*>(k_index_topk<4, 64, false>);
+    default: return reinterpret_cast<const void*>(k_index_topk<64, 128, true>);
+  }
+}
+
+static int index_resident_blocks(int v) {
   static std::mutex mu;
-  static int cached[2][64] = {};
+  static int cached[3][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  const int v = (H_I == 64 && d_I == 128) ? 0 : 1;
   std::lock_guard<std::mutex> lock(mu);
   if (cached[v][dev] == 0) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    const void* fn = v == 0 ? reinterpret_cast<const void*>(k_index_topk<64, 128>) : reinterpret_cast<const void*>(k_index_topk<4, 64>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kIdxRows * kWave, 0) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, index_kernel(v), kIdxRows * kWave, 0) != hipSuccess) return -1;
     cached[v][dev] = cus * occ;
   }
   return cached[v][dev];
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, hipStream_t st) {
+hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st) {
   if (a.nseg < 1 || a.nseg > kIdxMaxSeg || a.n_slots < 1) return hipErrorInvalidValue;
-  const int resident = index_resident_blocks(H_I, d_I);
+  const bool big = H_I == 64 && d_I == 128;
+  if (fp8 && !big) return hipErrorInvalidValue;
+  const int v = fp8 ? 2 : (big ? 0 : 1);
+  const int resident = index_resident_blocks(v);
   if (resident < 1 || resident > a.n_slots) return hipErrorInvalidConfiguration;  // slots could run out
   dim3 grid(a.seg_blk0[a.nseg]), block(kIdxRows * kWave);
-  if (H_I == 64 && d_I == 128) hipLaunchKernelGGL((k_index_topk<64, 128>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_index_topk<4, 64>), grid, block, 0, st, a);
+  if (v == 2) hipLaunchKernelGGL((k_index_topk<64, 128, true>), grid, block, 0, st, a);
+  else if (v == 0) hipLaunchKernelGGL((k_index_topk<64, 128, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_index_topk<4, 64, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// FP8 operands: each 128-value bf16 row becomes E4M3 codes and one power-of-two scale 2^e, e the
+// smallest integer with amax * 2^-e <= 448. Half a wave per row, four values per lane; the scaling
+// is exact and v_cvt_pk_fp8_f32 rounds to the nearest code (ties to even).
+__device__ __forceinline__ void quantize_row128(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                                                float* __restrict__ scale, int sub) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(x + 4 * sub);
+  const float f0 = bf16_to_f32(static_cast<uint16_t>(v[0])), f1 = bf16_to_f32(static_cast<uint16_t>(v[0] >> 16));
+  const float f2 = bf16_to_f32(static_cast<uint16_t>(v[1])), f3 = bf16_to_f32(static_cast<uint16_t>(v[1] >> 16));
+  float m = fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3)));
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+  int E = 0;
+  const float mant = frexpf(m, &E);  // m = mant * 2^E, mant in [0.5, 1); 448 = 0.875 * 2^9
+  const int e = m == 0.0f ? 0 : E - 9 + (mant > 0.875f ? 1 : 0);
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f0, -e), ldexpf(f1, -e), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(f2, -e), ldexpf(f3, -e), w, true);
+  *reinterpret_cast<uint32_t*>(q + 4 * sub) = w;
+  if (sub == 0) *scale = ldexpf(1.0f, e);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_fp8(const uint16_t* __restrict__ x1, int64_t n1, uint8_t* __restrict__ q1,
+                                                      float* __restrict__ s1, const uint16_t* __restrict__ x2, int64_t n2,
+                                                      uint8_t* __restrict__ q2, float* __restrict__ s2) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + threadIdx.x / 32;
+  const int sub = threadIdx.x % 32;
+  if (row < n1) quantize_row128(x1 + row * 128, q1 + row * 128, s1 + row, sub);
+  else if (row - n1 < n2) quantize_row128(x2 + (row - n1) * 128, q2 + (row - n1) * 128, s2 + (row - n1), sub);
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* x1, int64_t n1, uint8_t* q1, float* s1, const uint16_t* x2, int64_t n2,
+                               uint8_t* q2, float* s2, hipStream_t st) {
+  const int64_t blocks = (n1 + n2 + 7) / 8;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_fp8, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x1, n1, q1, s1, x2, n2, q2, s2);
   return hipGetLastError();
 }
 

@@ -93,6 +93,24 @@ dsa_status dsa_index_topk(const dsa_shape* shape, const uint16_t* q_I, const uin
                           const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                           int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Steps 1-3 with the FP8 indexer, the alternative the model-coverage page sets beside its BF16
+ * one (Implementation Limits, 2nd bullet: the BF16 indexer is not the FP8 indexer of some serving
+ * kernels). The pages give no recipe; this one: each 128-value row (LN(k_I) of a key, one head of
+ * q_I) is scaled by a power of two 2^-e, e the smallest integer with max|row| * 2^-e <= 448, and
+ * rounded to OCP E4M3 (nearest, ties to even); scores are
+ *   S(t,s) = 2^e_k[s] * sum_h (w[t,h] * 2^e_q[t,h]) * ReLU(sum_i q8[t,h,i] * k8[s,i])
+ * with exact products and FP32 sums; top-k and its tie rule as in dsa_index_topk. Supported for
+ * (H_I, d_I) = (64, 128) only (else DSA_ERR_UNSUPPORTED). Same arguments and workspace as
+ * dsa_index_topk; the workspace also holds the E4M3 operands. */
+dsa_status dsa_index_topk_fp8(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
+                              const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                              int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The FP8 indexer's operand quantisation on its own: n_rows rows of 128 bf16 values (x, 16-byte
+ * aligned) -> q8 [n_rows, 128] E4M3 codes (16-byte aligned) and scale [n_rows] float32, the row's
+ * power of two 2^e as above. No workspace. */
+dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream);
+
 /* Steps 1-3 without a workspace and without allocating device memory, for callers that cannot
  * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same inputs, output and results as dsa_index_topk. The scratch it needs instead of the workspace

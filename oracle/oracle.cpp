@@ -291,14 +291,20 @@ int32_t oracle_fp8_scale_exponent(double amax) { return fp8_scale_exponent(amax)
 // (k8 [*,d_I] codes, ek [*]):  S = 2^ek[s] * sum_h (w_h * 2^eq_h) * ReLU( sum_i q8[h,i] * k8[s,i] ).
 void oracle_index_scores_fp8(const uint8_t* q8_row, const int32_t* eq, const uint16_t* w_row, int32_t H_I,
                              int32_t d_I, const uint8_t* k8, const int32_t* ek, int64_t s0, int64_t s1, float* S) {
+  // the value of every code, from e4m3_decode (finite codes are exact in float)
+  static const std::vector<float> dec = [] {
+    std::vector<float> v(256);
+    for (int c = 0; c < 256; ++c) v[c] = static_cast<float>(e4m3_decode(static_cast<uint8_t>(c)));
+    return v;
+  }();
   std::vector<float> qv(static_cast<size_t>(H_I) * d_I), wq(H_I);
-  for (int64_t i = 0; i < static_cast<int64_t>(qv.size()); ++i) qv[i] = static_cast<float>(e4m3_decode(q8_row[i]));
+  for (int64_t i = 0; i < static_cast<int64_t>(qv.size()); ++i) qv[i] = dec[q8_row[i]];
   for (int32_t h = 0; h < H_I; ++h) wq[h] = std::ldexp(bf16_bits_to_float(w_row[h]), eq[h]);  // exact
   for (int64_t s = s0; s <= s1; ++s) {
     float score = 0.0f;
     for (int32_t h = 0; h < H_I; ++h) {
       float dot = 0.0f;
-      for (int32_t i = 0; i < d_I; ++i) dot += qv[h * d_I + i] * static_cast<float>(e4m3_decode(k8[s * d_I + i]));
+      for (int32_t i = 0; i < d_I; ++i) dot += qv[h * d_I + i] * dec[k8[s * d_I + i]];
       const float rl = dot > 0.0f ? dot : 0.0f;
       score += wq[h] * rl;
     }

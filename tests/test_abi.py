@@ -14,13 +14,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "dsa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
-                     "dsa_index_topk_noalloc", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
+    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk", "dsa_index_topk_fp8",
+                     "dsa_index_topk_noalloc", "dsa_quantize_fp8", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
                      "dsa_sparse_mla_fwd_ex", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
@@ -44,18 +44,23 @@ def test_supported_shapes_and_workspace():
     assert dsa.dsa_check_shape(_shape()) == dsa.DSA_OK
     assert dsa.dsa_check_shape(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)) == dsa.DSA_OK
     # LN(k_I) ((T + 128 padding rows) x d_I bf16), 256 candidate-slot flags (1 KB), 256 candidate
-    # slots of 8 rows x 4,160 int32 token indices, and the latent output of one row chunk (rows x H x
-    # 512 bf16, at most 16,384 rows)
+    # slots of 8 rows x 4,160 int32 token indices, the FP8 indexer's operands (E4M3 codes of LN(k_I)
+    # and q_I, one float scale per 128-value row), and the latent output of one row chunk (rows x H x
+    # 512 bf16, at most 16,384 rows); each region starts 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
     flags, slots = 1024, 256 * 8 * 4160 * 4
+
+    def fp8(T, rows, H_I, d_I):
+        return al((T + 128) * d_I) + al((T + 128) * 4) + al(rows * H_I * d_I) + al(rows * H_I * 4)
     ws = dsa.dsa_workspace_size(_shape())
-    assert ws == (4096 + 128) * 128 * 2 + flags + slots + 4096 * 96 * 512 * 2
+    assert ws == (4096 + 128) * 128 * 2 + flags + slots + fp8(4096, 4096, 64, 128) + 4096 * 96 * 512 * 2
     big = dsa.dsa_workspace_size(_shape(T=131072))
-    assert big == (131072 + 128) * 128 * 2 + flags + slots + 16384 * 96 * 512 * 2
+    assert big == (131072 + 128) * 128 * 2 + flags + slots + fp8(131072, 131072, 64, 128) + 16384 * 96 * 512 * 2
     assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
     tiny = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16))
-    assert tiny == (1024 + 128) * 64 * 2 + flags + slots + 1024 * 16 * 512 * 2
+    assert tiny == (1024 + 128) * 64 * 2 + flags + slots + fp8(1024, 1024, 4, 64) + 1024 * 16 * 512 * 2
     one = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16, q_begin=1000, q_end=1001))
-    assert one == (1024 + 128) * 64 * 2 + flags + slots + 16 * 512 * 2
+    assert one == al((1024 + 128) * 64 * 2) + flags + slots + fp8(1024, 1, 4, 64) + 16 * 512 * 2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -174,3 +179,17 @@ def test_variant_host_checks():
     var.sink = None
     assert L.dsa_sparse_mla_fwd_ex(P, ctypes.byref(var), fake, fake, fake, fake, fake, fake, None, None, n,
                                    None) == dsa.DSA_ERR_WORKSPACE
+
+
+def test_fp8_entry_points_host_checks():
+    """The FP8 indexer takes only the 64x128 indexer shape; the quantiser checks its pointers."""
+    L = dsa.lib()
+    fake = 1 << 20
+    tiny = _shape(T=1024, topk=256, H_I=4, d_I=64, H=16)
+    n = dsa.dsa_workspace_size(tiny)
+    assert L.dsa_index_topk_fp8(ctypes.byref(tiny), fake, fake, None, None, fake, fake, fake, n, None) == dsa.DSA_ERR_UNSUPPORTED
+    s = _shape()
+    assert L.dsa_index_topk_fp8(ctypes.byref(s), fake, fake, None, None, fake, fake, fake, 16, None) == dsa.DSA_ERR_WORKSPACE
+    assert L.dsa_quantize_fp8(-1, fake, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(4, None, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_fp8(4, fake, fake + 8, fake, None) == dsa.DSA_ERR_INVALID_ARG
