@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "query tokens/sec for indexer+top-2048+sparse MLA fwd; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 CSRC = os.path.join(ROOT, "dsa_indexer_top_index_amd", "csrc")
 KERNEL_SRC = {
@@ -365,6 +366,18 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
     torch.cuda.synchronize()
     del o_lat
     warm_steps = [e[0].elapsed_time(e[3]) for e in ev]
+    # The FP8 indexer (an alternative to the BF16 one, same outputs' shape), timed the same way.
+    t_idx8 = None
+    if cfg.H_I == 64 and cfg.d_I == 128:
+        idx8 = torch.empty_like(topk_idx)
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_stage)]
+        for i in range(n_stage):
+            ev8[i][0].record(stream)
+            dsa.dsa_index_topk_fp8(shape, dev["q_I"], dev["k_I"], dev["w"], idx8, ws)
+            ev8[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_idx8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
+        del idx8
     cold = []
     if cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -401,8 +414,16 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
         "cold_cache_ms_per_step_median": round(float(np.median(cold)), 4) if cold else None,
         "scored_pairs": w["scored_pairs"], "keff_sum": w["keff_sum"],
     }
+    if t_idx8 is not None:
+        res.update({
+            # FP8 indexer: the same algorithmic flops against the dense fp8 MFMA peak
+            "index_topk_fp8_ms": round(t_idx8, 4),
+            "indexer_fp8_frac_of_fp8_peak": round(w["k_index_topk"] / (t_idx8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "indexer_fp8_speedup_over_bf16": round(t_idx / t_idx8, 3),
+            "fp8_indexer_path_tokens_per_s": round(T / ((t_idx8 + t_att + t_up) * 1e-3), 1),
+        })
     log(f"[bench] {name}: {res['value']:.0f} tokens/s, {ms_step:.3f} ms/step (indexer {t_idx:.3f}, "
-        f"attention {t_att:.3f}, up/gate {t_up:.3f} ms)")
+        f"attention {t_att:.3f}, up/gate {t_up:.3f} ms; fp8 indexer {t_idx8 if t_idx8 is None else round(t_idx8, 3)} ms)")
     del dev, ws, topk_idx, out
     torch.cuda.empty_cache()
     return (res, cfg, keys) if want_inputs else res
