@@ -72,6 +72,7 @@ def _load(path):
     L.oracle_sparse_mla_f32.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, p]
     L.oracle_sparse_mla_variant.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p, p, p, p]
     L.oracle_quantize_fp8_rows.argtypes = [p, i64, i32, p, p]
+    L.oracle_q_absorb.argtypes = [i64, p, p, p, i32, p, p]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = d
     L.oracle_e4m3_encode.argtypes = [d]
@@ -285,3 +286,18 @@ def topk_fp8(rows, q8_rows, eq_rows, w_rows, k8, ek, cu_seqlens, k):
     lib().oracle_topk_fp8(n, pr, pq, pe, pw, H_I, d_I, pk, pE, pc, len(cu) - 1, k, idx.ctypes.data,
                           theta.ctypes.data, keff.ctypes.data)
     return idx, theta, keff
+
+
+# ---- adjacent steps
+
+def q_absorb(q_nope, q_pe, W_UK, want_f64=False):
+    """q_nope [n,H,128], q_pe [n,H,64], W_UK [H,512,128] (bf16 bits) -> q [n,H,576] bf16 bits
+    (and the unrounded latent part [n,H,512] in float64)."""
+    qn, pn = _c(q_nope, np.uint16)
+    qp, pp = _c(q_pe, np.uint16)
+    W, pw = _c(W_UK, np.uint16)
+    n, H = qn.shape[0], qn.shape[1]
+    out = np.empty((n, H, 576), dtype=np.uint16)
+    f = np.empty((n, H, 512)) if want_f64 else None
+    lib().oracle_q_absorb(n, pn, pp, pw, H, out.ctypes.data, f.ctypes.data if want_f64 else None)
+    return (out, f) if want_f64 else out

@@ -436,6 +436,34 @@ void oracle_sparse_mla_f32(int64_t n_rows, const int64_t* rows, const uint16_t* 
                          nullptr, nullptr, nullptr);
 }
 
+// The step before the attention: the per-head W_UK absorption that gives the latent query ([KC]
+// Implementation Limits, 2nd bullet: sparse MLA never expands the per-head K; [API]
+// KimiK3TextConfig: qk_nope_head_dim 128, kv_lora_rank 512, qk_rope_head_dim 64, mla_use_nope).
+// W_UK [H,512,128] is the key half of the kv_b_proj effective weight: head h's expanded key of a
+// token would be k_nope[d] = sum_c c_KV[c] * W_UK[h,c,d]. So q_nope . k_nope = q_lat . c_KV with
+//   q[t,h,c]       = sum_d q_nope[t,h,d] * W_UK[h,c,d]     c < 512, in double, one bf16 rounding
+//   q[t,h,512 + j] = q_pe[t,h,j]                           j < 64, unrotated (no positional encoding)
+// q_lat_f64 (optional) receives the unrounded latent part.
+void oracle_q_absorb(int64_t n_rows, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* W_UK, int32_t H,
+                     uint16_t* q_out, double* q_lat_f64) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int32_t h = 0; h < H; ++h) {
+      const uint16_t* qn = q_nope + (r * H + h) * 128;
+      const uint16_t* Wh = W_UK + static_cast<int64_t>(h) * kDV * 128;
+      uint16_t* dst = q_out + (r * H + h) * static_cast<int64_t>(kDL);
+      for (int c = 0; c < kDV; ++c) {
+        double acc = 0.0;
+        for (int d = 0; d < 128; ++d)
+          acc += static_cast<double>(bf16_bits_to_float(qn[d])) * bf16_bits_to_float(Wh[c * 128 + d]);
+        if (q_lat_f64) q_lat_f64[(r * H + h) * kDV + c] = acc;
+        dst[c] = double_to_bf16_rne(acc);
+      }
+      for (int j = 0; j < kDL - kDV; ++j) dst[kDV + j] = q_pe[(r * H + h) * (kDL - kDV) + j];
+    }
+  }
+}
+
 // Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are
 // dense-mask references). Written independently of oracle_sparse_mla: for each listed row the
 // logits of all T keys are formed and keys outside the causal window of the row's own document

@@ -661,3 +661,47 @@ def test_topk_fp8_brute_force_tiny():
         b16 = oracle.topk([t], q[[t]], w[[t]], LNk, np.array([0, T], np.int32), k)[0][0]
         agree.append(len(set(b16.tolist()) & set(idx[t].tolist())) / k)
     assert np.mean(agree) > 0.8   # the FP8 selection stays close to the BF16 one
+
+
+# ---------------------------------------------------------------- W_UK absorption (KC bullet 2; API MLA fields)
+
+def test_q_absorb_matches_expanded_keys():
+    """The absorbed latent query gives the same attention logits as the unabsorbed form with the
+    per-head keys expanded: q_nope . (c_KV W_UK[h]) + q_pe . k_pe = q_lat . c_KV + q_pe . k_pe, for
+    every head and key, computed here directly from the expanded keys."""
+    rng = np.random.default_rng(31)
+    n, H, T = 3, 8, 40
+    q_nope = _bf(rng.standard_normal((n, H, 128)))
+    q_pe = _bf(rng.standard_normal((n, H, 64)))
+    W_UK = _bf(rng.standard_normal((H, 512, 128)) * 0.05)
+    kv = _bf(rng.standard_normal((T, 576)))
+    q, qf = oracle.q_absorb(q_nope, q_pe, W_UK, want_f64=True)
+    assert np.array_equal(q[:, :, 512:], q_pe)
+    Wf, kvf = f32(W_UK).astype(np.float64), f32(kv).astype(np.float64)
+    k_nope = np.einsum("sc,hcd->hsd", kvf[:, :512], Wf)                    # expanded per-head keys
+    expanded = np.einsum("nhd,hsd->nhs", f32(q_nope).astype(np.float64), k_nope) \
+        + np.einsum("nhj,sj->nhs", f32(q_pe).astype(np.float64), kvf[:, 512:])
+    absorbed = np.einsum("nhc,sc->nhs", qf, kvf[:, :512]) + np.einsum("nhj,sj->nhs", f32(q_pe).astype(np.float64),
+                                                                      kvf[:, 512:])
+    assert np.abs(absorbed - expanded).max() <= 1e-10 * np.abs(expanded).max()
+    # the stored bf16 latent query is the double value rounded once to nearest
+    y = f32(q[:, :, :512]).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(qf))[1] - 8)
+    assert np.all(np.abs(y - qf) <= ulp / 2 + 1e-300)
+
+
+def test_q_absorb_identity_weight():
+    """W_UK[h, c, d] = 1 when c == d + 128*(h % 4): the latent query is q_nope shifted into block h % 4."""
+    rng = np.random.default_rng(32)
+    n, H = 2, 8
+    q_nope = _bf(rng.standard_normal((n, H, 128)))
+    q_pe = _bf(rng.standard_normal((n, H, 64)))
+    W = np.zeros((H, 512, 128), np.float32)
+    for h in range(H):
+        W[h, 128 * (h % 4) + np.arange(128), np.arange(128)] = 1
+    q = oracle.q_absorb(q_nope, q_pe, _bf(W))
+    for h in range(H):
+        b0 = 128 * (h % 4)
+        assert np.array_equal(q[:, h, b0:b0 + 128], q_nope[:, h])
+        rest = np.delete(np.arange(512), np.arange(b0, b0 + 128))
+        assert np.all(f32(q[:, h, rest]) == 0)
