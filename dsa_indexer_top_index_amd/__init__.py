@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
   dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None)
   dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
   dsa_quantize_fp8(x, q8, scale)
+  dsa_q_absorb(shape, q_nope, q_pe, W_UK, q)
   dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
   gate [rows,H,128] and per-head sink logits [H] float32)
 """
@@ -95,6 +96,8 @@ def lib():
         L.dsa_index_topk_fp8.restype = ctypes.c_int
         L.dsa_quantize_fp8.argtypes = [ctypes.c_int64, v, v, v, v]
         L.dsa_quantize_fp8.restype = ctypes.c_int
+        L.dsa_q_absorb.argtypes = [P, v, v, v, v, v]
+        L.dsa_q_absorb.restype = ctypes.c_int
         V = ctypes.POINTER(Variant)
         L.dsa_sparse_mla_fwd_ex.argtypes = [P, V, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_sparse_mla_fwd_ex.restype = ctypes.c_int
@@ -216,6 +219,15 @@ def dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, l
         _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_index_topk_fp8")
+
+
+def dsa_q_absorb(shape, q_nope, q_pe, W_UK, q):
+    """q [rows,H,576] from q_nope [rows,H,128], q_pe [rows,H,64] and W_UK [H,512,128] (all bf16)."""
+    bf, r, H = torch.bfloat16, _rows(shape), shape.H
+    st = lib().dsa_q_absorb(ctypes.byref(shape), _p(q_nope, bf, "q_nope", numel=r * H * 128),
+                            _p(q_pe, bf, "q_pe", numel=r * H * 64), _p(W_UK, bf, "W_UK", numel=H * 512 * 128),
+                            _p(q, bf, "q", numel=r * H * 576), _stream())
+    _raise(st, "dsa_q_absorb")
 
 
 def dsa_quantize_fp8(x, q8, scale):

@@ -283,6 +283,16 @@ dsa_status dsa_index_topk_fp8(const dsa_shape* s, const uint16_t* q_I, const uin
                    true);
 }
 
+dsa_status dsa_q_absorb(const dsa_shape* s, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* W_UK,
+                        uint16_t* q, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!q_nope || !q_pe || !W_UK || !q) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(W_UK, 16) || !aligned(q, 16)) return DSA_ERR_INVALID_ARG;
+  dsa::AbsorbArgs a{q_nope, q_pe, W_UK, q, rows_of(s), s->H};
+  return dsa::launch_q_absorb(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream) {
   if (n_rows < 0 || (n_rows > 0 && (!x || !q8 || !scale))) return DSA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q8, 16) || !aligned(scale, 4)) return DSA_ERR_INVALID_ARG;

@@ -72,6 +72,15 @@ struct UpArgs {
   int gate_per_dim;       // 0: one gate logit per (row, head); 1: one per output element
 };
 
+struct AbsorbArgs {
+  const uint16_t* q_nope;  // [rows, H, 128]
+  const uint16_t* q_pe;    // [rows, H, 64]
+  const uint16_t* W_UK;    // [H, 512, 128]
+  uint16_t* q;             // [rows, H, 576]
+  int rows;
+  int H;
+};
+
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
 hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
                                  uint16_t* LNk, const IndexArgs& a, hipStream_t st);
@@ -83,5 +92,6 @@ hipError_t launch_quantize_fp8(const uint16_t* x1, int64_t n1, uint8_t* q1, floa
 int index_blocks(int m, int paired);  // blocks of a segment of m rows
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
+hipError_t launch_q_absorb(const AbsorbArgs& a, hipStream_t st);
 
 }  // namespace dsa

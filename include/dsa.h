@@ -181,6 +181,18 @@ dsa_status dsa_fused_fwd_ex(const dsa_shape* shape, const dsa_mla_variant* varia
                             int32_t* topk_idx, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* The step before sparse MLA: the per-head W_UK absorption that gives the latent query (model-coverage
+ * page, Implementation Limits, 2nd bullet: sparse MLA never expands the per-head keys;
+ * KimiK3TextConfig: qk_nope_head_dim 128, kv_lora_rank 512, qk_rope_head_dim 64, mla_use_nope).
+ * W_UK [H, 512, 128] bf16 is the key half of the kv_b_proj effective weight (head h's expanded key
+ * of a token is k_nope[d] = sum_c c_KV[c] * W_UK[h,c,d]). Inputs q_nope [rows, H, 128] and q_pe
+ * [rows, H, 64] bf16; output q [rows, H, 576] bf16 with
+ *   q[t,h,c] = bf16(sum_d q_nope[t,h,d] * W_UK[h,c,d]) for c < 512 (FP32 accumulation), and
+ *   q[t,h,512 + j] = q_pe[t,h,j] (unrotated),
+ * the q that dsa_sparse_mla_fwd and dsa_fused_fwd take. Rows as in dsa_shape; no workspace. */
+dsa_status dsa_q_absorb(const dsa_shape* shape, const uint16_t* q_nope, const uint16_t* q_pe,
+                        const uint16_t* W_UK, uint16_t* q, void* stream);
+
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);
 

@@ -1,0 +1,80 @@
+"""GPU parity of the steps on either side of the path: the W_UK absorption that produces the latent
+query (model-coverage page, Implementation Limits, 2nd bullet; KimiK3TextConfig MLA fields), through
+the C ABI, against the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_indexer_top_index_amd as dsa
+import oracle
+import testgen as tg
+from tests import gpu_util as gu
+from tests.parity import check_outputs, gamma
+
+pytestmark = pytest.mark.gpu
+
+TAG_QNOPE, TAG_QPE, TAG_WUK = 60, 61, 62
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _absorb_inputs(seed, rows, H):
+    q_nope = tg.normal_bf16(seed, TAG_QNOPE, 0, rows * H * 128, 1.0).reshape(rows, H, 128)
+    q_pe = tg.normal_bf16(seed, TAG_QPE, 0, rows * H * 64, 1.0 / 24).reshape(rows, H, 64)
+    W_UK = tg.normal_bf16(seed, TAG_WUK, 0, H * 512 * 128, 0.02).reshape(H, 512, 128)
+    return q_nope, q_pe, W_UK
+
+
+@pytest.mark.parametrize("rows,H", [(1000, 96), (333, 16), (1, 96)])
+def test_q_absorb_within_one_bf16_step(rows, H):
+    """Every latent element is one of the two bf16 neighbours of the exact value (FP32 accumulation is
+    far finer than a bf16 step; the second term covers values that cancel to near zero), and the 64
+    unrotated dims are copied bit for bit. Ragged row counts cover partial 256-row workgroups."""
+    _say(f"[gpu] q absorb rows={rows} H={H}")
+    q_nope, q_pe, W_UK = _absorb_inputs(90 + H, rows, H)
+    cfg = tg.Config("absorb", 1, [max(rows, 1)], topk=1, H=H, H_I=4, d_I=64)
+    shape = gu.shape_of(cfg)
+    q = torch.empty((rows, H, 576), dtype=torch.bfloat16, device="cuda")
+    dsa.dsa_q_absorb(shape, gu.bf16_np_to_tensor(q_nope), gu.bf16_np_to_tensor(q_pe), gu.bf16_np_to_tensor(W_UK), q)
+    torch.cuda.synchronize()
+    got = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref, exact = oracle.q_absorb(q_nope, q_pe, W_UK, want_f64=True)
+    assert np.array_equal(got[:, :, 512:], q_pe)
+    g = tg.bf16_to_f32(got[:, :, :512]).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 8)
+    absdot = np.einsum("nhd,hcd->nhc", np.abs(tg.bf16_to_f32(q_nope).astype(np.float64)),
+                       np.abs(tg.bf16_to_f32(W_UK).astype(np.float64)))
+    assert np.all(np.abs(g - exact) <= ulp + 2 * gamma(128) * absdot)
+    same = np.mean(got[:, :, :512] == ref[:, :, :512])
+    _say(f"[gpu] q absorb rows={rows} H={H}: {same:.4f} of elements equal the oracle's rounding")
+
+
+def test_absorbed_query_through_the_fused_forward():
+    """q from dsa_q_absorb drives dsa_fused_fwd; outputs match the oracle path fed by the oracle's own
+    absorption (differences: the bf16 roundings of q, within the output rule)."""
+    cfg = tg.Config("absorb-fused", 93, [900], topk=256, H=96, H_I=64, d_I=128, w_scale=1 / 8, W_UV_std=0.02)
+    inp = tg.make_inputs(cfg)
+    T, H = cfg.T, cfg.H
+    q_nope, q_pe, W_UK = _absorb_inputs(93, T, H)
+    shape = gu.shape_of(cfg)
+    dev = gu.to_device(inp)
+    q = torch.empty((T, H, 576), dtype=torch.bfloat16, device="cuda")
+    dsa.dsa_q_absorb(shape, gu.bf16_np_to_tensor(q_nope), gu.bf16_np_to_tensor(q_pe), gu.bf16_np_to_tensor(W_UK), q)
+    ws = dsa.alloc_workspace(shape)
+    idx = torch.empty((T, cfg.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    _say("[gpu] absorbed query through dsa_fused_fwd")
+    dsa.dsa_fused_fwd(shape, dev["q_I"], dev["k_I"], dev["w"], q, dev["kv"], dev["W_UV"], dev["gate"], idx, out, ws)
+    torch.cuda.synchronize()
+    q_ref = oracle.q_absorb(q_nope, q_pe, W_UK)
+    rows = np.arange(T)
+    ref = oracle.sparse_mla(rows, q_ref, inp["kv"], idx.cpu().numpy(), inp["W_UV"], inp["gate"], cfg.softmax_scale)
+    ok, err, mx = check_outputs(gu.bf16_tensor_to_f32(out), ref["out"])
+    assert ok, (err, mx)
