@@ -73,6 +73,7 @@ def _load(path):
     L.oracle_sparse_mla_variant.argtypes = [i64, p, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p, p, p, p]
     L.oracle_quantize_fp8_rows.argtypes = [p, i64, i32, p, p]
     L.oracle_q_absorb.argtypes = [i64, p, p, p, i32, p, p]
+    L.oracle_o_proj.argtypes = [i64, p, p, i32, i32, p, p]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = d
     L.oracle_e4m3_encode.argtypes = [d]
@@ -301,3 +302,16 @@ def q_absorb(q_nope, q_pe, W_UK, want_f64=False):
     f = np.empty((n, H, 512)) if want_f64 else None
     lib().oracle_q_absorb(n, pn, pp, pw, H, out.ctypes.data, f.ctypes.data if want_f64 else None)
     return (out, f) if want_f64 else out
+
+
+def o_proj(x, W_o, want_f64=False):
+    """x [n,K], W_o [N,K] (bf16 bits) -> y [n,N] bf16 bits (and the unrounded values in float64)."""
+    xc, px = _c(x, np.uint16)
+    W, pw = _c(W_o, np.uint16)
+    n, K = xc.shape[0], int(np.prod(xc.shape[1:]))
+    N = W.shape[0]
+    assert W.shape[1] == K
+    y = np.empty((n, N), dtype=np.uint16)
+    f = np.empty((n, N)) if want_f64 else None
+    lib().oracle_o_proj(n, px, pw, K, N, y.ctypes.data, f.ctypes.data if want_f64 else None)
+    return (y, f) if want_f64 else y

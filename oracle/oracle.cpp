@@ -464,6 +464,28 @@ void oracle_q_absorb(int64_t n_rows, const uint16_t* q_nope, const uint16_t* q_p
   }
 }
 
+// The step after the gate: the attention output projection o_proj ([KC] paragraph on the output
+// gate and kv_b_proj; [API] KimiK3TextConfig hidden_size 7168, v_head_dim 128, 96 heads). The
+// gated head outputs of a row, heads in order, form x [K = H * 128]; W_o [N, K] is in the
+// [out_features, in_features] layout:
+//   y[t,n] = bf16( sum_k x[t,k] * W_o[n,k] )     in double, one rounding
+// y_f64 (optional) receives the unrounded values.
+void oracle_o_proj(int64_t n_rows, const uint16_t* x, const uint16_t* W_o, int32_t K, int32_t N, uint16_t* y,
+                   double* y_f64) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::vector<double> xr(static_cast<size_t>(K));
+    for (int32_t k = 0; k < K; ++k) xr[k] = bf16_bits_to_float(x[r * K + k]);
+    for (int32_t n = 0; n < N; ++n) {
+      const uint16_t* wn = W_o + static_cast<int64_t>(n) * K;
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k) acc += xr[k] * bf16_bits_to_float(wn[k]);
+      if (y_f64) y_f64[r * N + n] = acc;
+      y[r * N + n] = double_to_bf16_rne(acc);
+    }
+  }
+}
+
 // Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are
 // dense-mask references). Written independently of oracle_sparse_mla: for each listed row the
 // logits of all T keys are formed and keys outside the causal window of the row's own document

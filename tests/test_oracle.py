@@ -705,3 +705,22 @@ def test_q_absorb_identity_weight():
         assert np.array_equal(q[:, h, b0:b0 + 128], q_nope[:, h])
         rest = np.delete(np.arange(512), np.arange(b0, b0 + 128))
         assert np.all(f32(q[:, h, rest]) == 0)
+
+
+# ---------------------------------------------------------------- o_proj (KC output-gate paragraph; API hidden_size)
+
+def test_o_proj_against_library_matmul_and_selection():
+    """o_proj equals a float64 library matrix product rounded once to bf16 (library cross-check), and a
+    selection weight (W_o[n, k] = 1 for k = p(n)) returns the selected inputs exactly."""
+    rng = np.random.default_rng(41)
+    n, K, N = 5, 2048, 384
+    x = _bf(rng.standard_normal((n, K)))
+    W = _bf(rng.standard_normal((N, K)) * 0.02)
+    y, yf = oracle.o_proj(x, W, want_f64=True)
+    ref = f32(x).astype(np.float64) @ f32(W).astype(np.float64).T
+    assert np.abs(yf - ref).max() <= 1e-12 * np.abs(ref).max()
+    assert np.array_equal(y, bf(ref.astype(np.float32))) or np.abs(f32(y) - ref).max() <= np.abs(ref).max() * 2.0 ** -8
+    perm = rng.permutation(K)[:N]
+    S = np.zeros((N, K), np.float32)
+    S[np.arange(N), perm] = 1
+    assert np.array_equal(oracle.o_proj(x, _bf(S)), x[:, perm])
