@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
   dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
   dsa_quantize_fp8(x, q8, scale)
   dsa_q_absorb(shape, q_nope, q_pe, W_UK, q)
+  dsa_o_proj(shape, x, W_o, y)
   dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
   gate [rows,H,128] and per-head sink logits [H] float32)
 """
@@ -96,6 +97,8 @@ def lib():
         L.dsa_index_topk_fp8.restype = ctypes.c_int
         L.dsa_quantize_fp8.argtypes = [ctypes.c_int64, v, v, v, v]
         L.dsa_quantize_fp8.restype = ctypes.c_int
+        L.dsa_o_proj.argtypes = [P, v, v, ctypes.c_int32, v, v]
+        L.dsa_o_proj.restype = ctypes.c_int
         L.dsa_q_absorb.argtypes = [P, v, v, v, v, v]
         L.dsa_q_absorb.restype = ctypes.c_int
         V = ctypes.POINTER(Variant)
@@ -228,6 +231,15 @@ def dsa_q_absorb(shape, q_nope, q_pe, W_UK, q):
                             _p(q_pe, bf, "q_pe", numel=r * H * 64), _p(W_UK, bf, "W_UK", numel=H * 512 * 128),
                             _p(q, bf, "q", numel=r * H * 576), _stream())
     _raise(st, "dsa_q_absorb")
+
+
+def dsa_o_proj(shape, x, W_o, y):
+    """y [rows, d_model] = x [rows, H*128] W_o^T, W_o [d_model, H*128] (bf16)."""
+    bf, r, K = torch.bfloat16, _rows(shape), shape.H * 128
+    d_model = W_o.shape[0]
+    st = lib().dsa_o_proj(ctypes.byref(shape), _p(x, bf, "x", numel=r * K), _p(W_o, bf, "W_o", numel=d_model * K),
+                          d_model, _p(y, bf, "y", numel=r * d_model), _stream())
+    _raise(st, "dsa_o_proj")
 
 
 def dsa_quantize_fp8(x, q8, scale):

@@ -293,6 +293,17 @@ dsa_status dsa_q_absorb(const dsa_shape* s, const uint16_t* q_nope, const uint16
   return dsa::launch_q_absorb(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
+dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o, int32_t d_model, uint16_t* y,
+                      void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!x || !W_o || !y) return DSA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(W_o, 16) || !aligned(y, 16)) return DSA_ERR_INVALID_ARG;
+  if (d_model < 256 || d_model % 256 != 0) return DSA_ERR_UNSUPPORTED;
+  dsa::GemmArgs g{x, W_o, y, rows_of(s), d_model, s->H * 128};
+  return dsa::launch_gemm_nt(g, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
 dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream) {
   if (n_rows < 0 || (n_rows > 0 && (!x || !q8 || !scale))) return DSA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q8, 16) || !aligned(scale, 4)) return DSA_ERR_INVALID_ARG;

@@ -81,6 +81,13 @@ struct AbsorbArgs {
   int H;
 };
 
+struct GemmArgs {
+  const uint16_t* A;  // [M, K] bf16, K contiguous
+  const uint16_t* B;  // [N, K] bf16, K contiguous
+  uint16_t* C;        // [M, N] bf16
+  int M, N, K;        // N a multiple of 256, K a multiple of 64
+};
+
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
 hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
                                  uint16_t* LNk, const IndexArgs& a, hipStream_t st);
@@ -93,5 +100,6 @@ int index_blocks(int m, int paired);  // blocks of a segment of m rows
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
 hipError_t launch_q_absorb(const AbsorbArgs& a, hipStream_t st);
+hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t st);
 
 }  // namespace dsa

@@ -193,6 +193,15 @@ dsa_status dsa_fused_fwd_ex(const dsa_shape* shape, const dsa_mla_variant* varia
 dsa_status dsa_q_absorb(const dsa_shape* shape, const uint16_t* q_nope, const uint16_t* q_pe,
                         const uint16_t* W_UK, uint16_t* q, void* stream);
 
+/* The step after the gate: the attention output projection o_proj (model-coverage page, paragraph
+ * on the output gate; KimiK3TextConfig hidden_size 7168). x [rows, H * 128] bf16 is the out of the
+ * path (the gated head outputs of a row, heads in order); W_o [d_model, H * 128] bf16 in the
+ * [out_features, in_features] layout; y [rows, d_model] bf16 = bf16(x W_o^T), FP32 accumulation.
+ * d_model must be a positive multiple of 256 (else DSA_ERR_UNSUPPORTED). Rows as in dsa_shape;
+ * no workspace. */
+dsa_status dsa_o_proj(const dsa_shape* shape, const uint16_t* x, const uint16_t* W_o, int32_t d_model,
+                      uint16_t* y, void* stream);
+
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);
 

@@ -20,7 +20,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk", "dsa_index_topk_fp8",
-                     "dsa_index_topk_noalloc", "dsa_q_absorb", "dsa_quantize_fp8", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
+                     "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb", "dsa_quantize_fp8", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
                      "dsa_sparse_mla_fwd_ex", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:

@@ -78,3 +78,34 @@ def test_absorbed_query_through_the_fused_forward():
     ref = oracle.sparse_mla(rows, q_ref, inp["kv"], idx.cpu().numpy(), inp["W_UV"], inp["gate"], cfg.softmax_scale)
     ok, err, mx = check_outputs(gu.bf16_tensor_to_f32(out), ref["out"])
     assert ok, (err, mx)
+
+
+TAG_X, TAG_WO = 63, 64
+
+
+@pytest.mark.parametrize("rows,H,d_model", [(1000, 96, 7168), (300, 16, 512), (1, 96, 256)])
+def test_o_proj_within_one_bf16_step(rows, H, d_model):
+    """y = x W_o^T: every checked element is one of the two bf16 neighbours of the exact value, up to
+    the FP32 accumulation bound over K = H * 128 terms. Rows are checked in full for the small shape and
+    sampled (first, last, partial tile, random) for the production one."""
+    K = H * 128
+    _say(f"[gpu] o_proj rows={rows} K={K} d_model={d_model}")
+    x = tg.normal_bf16(95, TAG_X, 0, rows * K, 0.5).reshape(rows, K)
+    W = tg.normal_bf16(95, TAG_WO, 0, d_model * K, 0.01).reshape(d_model, K)
+    cfg = tg.Config("oproj", 1, [rows], topk=1, H=H, H_I=4, d_I=64)
+    shape = gu.shape_of(cfg)
+    y = torch.empty((rows, d_model), dtype=torch.bfloat16, device="cuda")
+    dsa.dsa_o_proj(shape, gu.bf16_np_to_tensor(x), gu.bf16_np_to_tensor(W), y)
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    if rows > 400:
+        rng = np.random.default_rng(2)
+        sel = np.array(sorted(set([0, 1, 255, 256, 511, 767, 768, rows - 1] + rng.integers(0, rows, 40).tolist())))
+    else:
+        sel = np.arange(rows)
+    ref, exact = oracle.o_proj(x[sel], W, want_f64=True)
+    g = tg.bf16_to_f32(got[sel]).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 8)
+    absdot = np.abs(tg.bf16_to_f32(x[sel]).astype(np.float64)) @ np.abs(tg.bf16_to_f32(W).astype(np.float64)).T
+    assert np.all(np.abs(g - exact) <= ulp + 2 * gamma(K) * absdot)
+    _say(f"[gpu] o_proj rows={rows} K={K}: {np.mean(got[sel] == ref):.4f} of checked elements equal the oracle's rounding")
