@@ -36,6 +36,7 @@ KERNEL_SRC = {
 }
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30         # plain device copy used to scale the HBM byte counters
+D_MODEL = 7168               # hidden size of the model (KimiK3TextConfig), the width of o_proj's output
 COPY_LAUNCHES = 5
 
 WORKLOAD_TEXT = {
@@ -378,6 +379,27 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
         torch.cuda.synchronize()
         t_idx8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
         del idx8
+    # The steps on either side of the path: the W_UK absorption that produces q, and o_proj after the
+    # gate (hidden size 7168), on seeded synthetic operands of their shapes.
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed)
+    q_nope = torch.randn((T, cfg.H, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    q_pe = torch.randn((T, cfg.H, 64), generator=gen, device="cuda").to(torch.bfloat16)
+    W_UK = (0.02 * torch.randn((cfg.H, 512, 128), generator=gen, device="cuda")).to(torch.bfloat16)
+    W_o = (0.01 * torch.randn((D_MODEL, cfg.H * 128), generator=gen, device="cuda")).to(torch.bfloat16)
+    y = torch.empty((T, D_MODEL), dtype=torch.bfloat16, device="cuda")
+    q_abs = dev["q"]  # the absorbed query overwrites q, which nothing reads after this point
+    eva = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_stage)]
+    for i in range(n_stage):
+        eva[i][0].record(stream)
+        dsa.dsa_q_absorb(shape, q_nope, q_pe, W_UK, q_abs)
+        eva[i][1].record(stream)
+        dsa.dsa_o_proj(shape, out.view(T, cfg.H * 128), W_o, y)
+        eva[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_abs = float(np.mean([e[0].elapsed_time(e[1]) for e in eva]))
+    t_op = float(np.mean([e[1].elapsed_time(e[2]) for e in eva]))
+    del q_nope, q_pe, W_UK, W_o, y
     cold = []
     if cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -414,6 +436,14 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
         "cold_cache_ms_per_step_median": round(float(np.median(cold)), 4) if cold else None,
         "scored_pairs": w["scored_pairs"], "keff_sum": w["keff_sum"],
     }
+    abs_bytes = T * cfg.H * (128 + 64 + 576) * 2 + cfg.H * 512 * 128 * 2
+    op_flop = 2.0 * T * cfg.H * 128 * D_MODEL
+    res.update({
+        # adjacent steps: W_UK absorption (HBM-bound: bytes moved) and o_proj (an MFMA GEMM)
+        "q_absorb_ms": round(t_abs, 4), "q_absorb_gbs": round(abs_bytes / (t_abs * 1e-3) / 1e9, 1),
+        "o_proj_ms": round(t_op, 4), "o_proj_tflops": round(op_flop / (t_op * 1e-3) / 1e12, 1),
+        "o_proj_frac": round(op_flop / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    })
     if t_idx8 is not None:
         res.update({
             # FP8 indexer: the same algorithmic flops against the dense fp8 MFMA peak
