@@ -74,6 +74,8 @@ def _load(path):
     L.oracle_quantize_fp8_rows.argtypes = [p, i64, i32, p, p]
     L.oracle_q_absorb.argtypes = [i64, p, p, p, i32, p, p]
     L.oracle_o_proj.argtypes = [i64, p, p, i32, i32, p, p]
+    L.oracle_sparse_mla_f64in.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, p, p]
+    L.oracle_sparse_mla_bwd.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = d
     L.oracle_e4m3_encode.argtypes = [d]
@@ -315,3 +317,38 @@ def o_proj(x, W_o, want_f64=False):
     f = np.empty((n, N)) if want_f64 else None
     lib().oracle_o_proj(n, px, pw, K, N, y.ctypes.data, f.ctypes.data if want_f64 else None)
     return (y, f) if want_f64 else y
+
+
+# ---- backward (inputs as float64 arrays; bf16 inputs are converted exactly by the caller)
+
+def sparse_mla_f64in(q, kv, idx, W_UV, gate, scale):
+    """Forward with double inputs: q [n,H,576], kv [T,576], idx [n,k], W_UV [H,512,128], gate [n,H].
+    Returns (out [n,H,128], lse [n,H])."""
+    q, pq = _c(q, np.float64)
+    kvc, pkv = _c(kv, np.float64)
+    ix, pi = _c(idx, np.int32)
+    W, pw = _c(W_UV, np.float64)
+    g, pg = _c(gate, np.float64)
+    n, H = q.shape[0], q.shape[1]
+    out = np.empty((n, H, 128))
+    lse = np.empty((n, H))
+    lib().oracle_sparse_mla_f64in(n, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale, out.ctypes.data,
+                                  lse.ctypes.data)
+    return out, lse
+
+
+def sparse_mla_bwd(q, kv, idx, W_UV, gate, scale, dout):
+    """Gradients of L = sum(dout * out): returns dict dq [n,H,576], dkv [T,576], dW_UV [H,512,128], dgate [n,H]."""
+    q, pq = _c(q, np.float64)
+    kvc, pkv = _c(kv, np.float64)
+    ix, pi = _c(idx, np.int32)
+    W, pw = _c(W_UV, np.float64)
+    g, pg = _c(gate, np.float64)
+    do, pd = _c(dout, np.float64)
+    n, H = q.shape[0], q.shape[1]
+    T = kvc.shape[0]
+    res = {"dq": np.empty((n, H, 576)), "dkv": np.zeros((T, 576)), "dW_UV": np.zeros((H, 512, 128)),
+           "dgate": np.empty((n, H))}
+    lib().oracle_sparse_mla_bwd(n, pq, pkv, T, pi, ix.shape[1], pw, pg, H, scale, pd, res["dq"].ctypes.data,
+                                res["dkv"].ctypes.data, res["dW_UV"].ctypes.data, res["dgate"].ctypes.data)
+    return res

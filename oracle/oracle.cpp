@@ -67,6 +67,11 @@ float bf16_bits_to_float(uint16_t h) {
   return f;
 }
 
+// Value of one input element: bf16 bits, or a double (the double-input form used to pin the
+// backward by finite differences).
+inline double in_val(uint16_t b) { return bf16_bits_to_float(b); }
+inline double in_val(double x) { return x; }
+
 // Round a finite double to the nearest bf16 (ties to even), in one step.
 uint16_t double_to_bf16_rne(double x) {
   if (x == 0.0) return std::signbit(x) ? 0x8000 : 0x0000;
@@ -349,9 +354,9 @@ void oracle_topk_fp8(int64_t n_rows, const int64_t* rows, const uint8_t* q8_rows
 //    gate_per_dim = 1: gate_rows [n,H,128], one logit per output element.
 //  - sink [H] or NULL: head h's softmax gains one more term exp(sink[h]) in its denominator, a
 //    logit whose value row is zero (it takes weight from the keys and adds nothing to o_lat).
-template <typename R>
-void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv, int64_t T, const int32_t* idx,
-                     int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H, double scale,
+template <typename R, typename In>
+void sparse_mla_impl(int64_t n_rows, const In* q_rows, const In* kv, int64_t T, const int32_t* idx,
+                     int32_t k, const In* W_UV, const In* gate_rows, int32_t H, double scale,
                      int32_t gate_per_dim, const double* sink, double* o_pre, double* out_f64, uint16_t* out_bf16,
                      double* lse, double* psum) {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -364,12 +369,12 @@ void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv,
     const size_t n = sel.size();
     std::vector<R> l(n), ol(kDV);
     for (int32_t h = 0; h < H; ++h) {
-      const uint16_t* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
+      const In* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
       for (size_t j = 0; j < n; ++j) {
-        const uint16_t* kr = kv + sel[j] * kDL;
+        const In* kr = kv + sel[j] * kDL;
         R dot = 0;
         for (int i = 0; i < kDL; ++i)
-          dot += static_cast<R>(bf16_bits_to_float(qh[i])) * static_cast<R>(bf16_bits_to_float(kr[i]));
+          dot += static_cast<R>(in_val(qh[i])) * static_cast<R>(in_val(kr[i]));
         l[j] = static_cast<R>(scale) * dot;
       }
       R m = -std::numeric_limits<R>::infinity();
@@ -383,16 +388,16 @@ void sparse_mla_impl(int64_t n_rows, const uint16_t* q_rows, const uint16_t* kv,
       for (size_t j = 0; j < n; ++j) {
         R p = std::exp(l[j] - m) / z;
         ps += p;
-        const uint16_t* vr = kv + sel[j] * kDL;
-        for (int c = 0; c < kDV; ++c) ol[c] += p * static_cast<R>(bf16_bits_to_float(vr[c]));
+        const In* vr = kv + sel[j] * kDL;
+        for (int c = 0; c < kDV; ++c) ol[c] += p * static_cast<R>(in_val(vr[c]));
       }
-      const uint16_t* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
+      const In* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
       for (int d = 0; d < kDO; ++d) {
         R o = 0;
-        for (int c = 0; c < kDV; ++c) o += ol[c] * static_cast<R>(bf16_bits_to_float(Wh[c * kDO + d]));
+        for (int c = 0; c < kDV; ++c) o += ol[c] * static_cast<R>(in_val(Wh[c * kDO + d]));
         const int64_t at = (r * H + h) * static_cast<int64_t>(kDO) + d;
         if (o_pre) o_pre[at] = o;
-        const R g = bf16_bits_to_float(gate_per_dim ? gate_rows[at] : gate_rows[r * H + h]);
+        const R g = static_cast<R>(in_val(gate_per_dim ? gate_rows[at] : gate_rows[r * H + h]));
         const R sig = R(1) / (R(1) + std::exp(-g));
         const R y = o * sig;
         if (out_f64) out_f64[at] = y;
@@ -411,8 +416,8 @@ void oracle_sparse_mla(int64_t n_rows, const int64_t* rows, const uint16_t* q_ro
                        const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows, int32_t H,
                        double scale, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse, double* psum) {
   (void)rows;
-  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, o_pre, out_f64,
-                          out_bf16, lse, psum);
+  sparse_mla_impl<double, uint16_t>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, o_pre,
+                                    out_f64, out_bf16, lse, psum);
 }
 
 // The gate and sink variants ([AD] "Output gate + sink"), in double: gate_per_dim selects a gate
@@ -423,8 +428,8 @@ void oracle_sparse_mla_variant(int64_t n_rows, const int64_t* rows, const uint16
                                const double* sink, double* o_pre, double* out_f64, uint16_t* out_bf16, double* lse,
                                double* psum) {
   (void)rows;
-  sparse_mla_impl<double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, gate_per_dim, sink, o_pre,
-                          out_f64, out_bf16, lse, psum);
+  sparse_mla_impl<double, uint16_t>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, gate_per_dim, sink,
+                                    o_pre, out_f64, out_bf16, lse, psum);
 }
 
 // The same definition accumulated in float: used only to time the oracle as a CPU baseline.
@@ -432,8 +437,8 @@ void oracle_sparse_mla_f32(int64_t n_rows, const int64_t* rows, const uint16_t* 
                            int64_t T, const int32_t* idx, int32_t k, const uint16_t* W_UV, const uint16_t* gate_rows,
                            int32_t H, double scale, double* out_f64) {
   (void)rows;
-  sparse_mla_impl<float>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, nullptr, out_f64,
-                         nullptr, nullptr, nullptr);
+  sparse_mla_impl<float, uint16_t>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, nullptr,
+                                   out_f64, nullptr, nullptr, nullptr);
 }
 
 // The step before the attention: the per-head W_UK absorption that gives the latent query ([KC]
@@ -483,6 +488,93 @@ void oracle_o_proj(int64_t n_rows, const uint16_t* x, const uint16_t* W_o, int32
       if (y_f64) y_f64[r * N + n] = acc;
       y[r * N + n] = double_to_bf16_rne(acc);
     }
+  }
+}
+
+// The same forward with double inputs (q [n,H,576], kv [T,576], W_UV [H,512,128], gate [n,H]): the
+// point at which the backward below is checked by finite differences.
+void oracle_sparse_mla_f64in(int64_t n_rows, const double* q_rows, const double* kv, int64_t T, const int32_t* idx,
+                             int32_t k, const double* W_UV, const double* gate_rows, int32_t H, double scale,
+                             double* out_f64, double* lse) {
+  sparse_mla_impl<double, double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, nullptr,
+                                  out_f64, nullptr, lse, nullptr);
+}
+
+// Backward of sparse latent attention, the per-head V up-projection and the per-head sigmoid gate
+// ([KC] paragraph after the Implementation Limits bullets: the backward runs the native 96 heads;
+// 3rd bullet: hard top-k carries no gradient, so the indices are constants). For the loss
+// L = sum dout * out, with the forward's definitions and p_j = exp(l_j - lse), written out by the
+// chain rule in double (inputs as double arrays):
+//   sg = sigma(g); o = o_lat W_UV[h]; dgate = sg (1 - sg) sum_d dout[d] o[d]; do = sg dout
+//   dW_UV[h,c,d] += o_lat[c] do[d]; do_lat[c] = sum_d W_UV[h,c,d] do[d]
+//   dp_j = do_lat . kv_j[:512];  D = sum_j p_j dp_j;  dl_j = p_j (dp_j - D)
+//   dq = scale sum_j dl_j kv_j (576 dims);  dkv_j += scale dl_j q (576) + p_j do_lat (512)
+// Outputs: dq [n,H,576] and dgate [n,H] (written), dkv [T,576] and dW [H,512,128] (added to).
+void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* kv, int64_t T, const int32_t* idx,
+                           int32_t k, const double* W_UV, const double* gate_rows, int32_t H, double scale,
+                           const double* dout, double* dq, double* dkv, double* dW, double* dgate) {
+  for (int64_t r = 0; r < n_rows; ++r) {
+    std::vector<int64_t> sel;
+    for (int32_t j = 0; j < k; ++j) {
+      const int64_t s = idx[r * k + j];
+      if (s >= 0 && s < T) sel.push_back(s);
+    }
+    const size_t n = sel.size();
+    // per head: the contributions to the selected rows of dkv, summed over heads afterwards
+    std::vector<double> dkv_h(static_cast<size_t>(H) * n * kDL, 0.0);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t h = 0; h < H; ++h) {
+      const double* qh = q_rows + (r * H + h) * static_cast<int64_t>(kDL);
+      const double* Wh = W_UV + static_cast<int64_t>(h) * kDV * kDO;
+      std::vector<double> l(n), p(n), ol(kDV, 0.0), o(kDO, 0.0), dov(kDO), dol(kDV, 0.0), dp(n);
+      for (size_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int i = 0; i < kDL; ++i) dot += qh[i] * kv[sel[j] * kDL + i];
+        l[j] = scale * dot;
+      }
+      double m = -std::numeric_limits<double>::infinity();
+      for (size_t j = 0; j < n; ++j) m = std::max(m, l[j]);
+      double z = 0.0;
+      for (size_t j = 0; j < n; ++j) z += std::exp(l[j] - m);
+      for (size_t j = 0; j < n; ++j) p[j] = std::exp(l[j] - m) / z;
+      for (size_t j = 0; j < n; ++j)
+        for (int c = 0; c < kDV; ++c) ol[c] += p[j] * kv[sel[j] * kDL + c];
+      for (int d = 0; d < kDO; ++d)
+        for (int c = 0; c < kDV; ++c) o[d] += ol[c] * Wh[c * kDO + d];
+      const double sg = 1.0 / (1.0 + std::exp(-gate_rows[r * H + h]));
+      const double* dorow = dout + (r * H + h) * static_cast<int64_t>(kDO);
+      double dgo = 0.0;
+      for (int d = 0; d < kDO; ++d) dgo += dorow[d] * o[d];
+      dgate[r * H + h] = sg * (1.0 - sg) * dgo;
+      for (int d = 0; d < kDO; ++d) dov[d] = sg * dorow[d];
+      double* dWh = dW + static_cast<int64_t>(h) * kDV * kDO;
+      for (int c = 0; c < kDV; ++c)
+        for (int d = 0; d < kDO; ++d) {
+          dWh[c * kDO + d] += ol[c] * dov[d];
+          dol[c] += Wh[c * kDO + d] * dov[d];
+        }
+      double D = 0.0;
+      for (size_t j = 0; j < n; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < kDV; ++c) acc += dol[c] * kv[sel[j] * kDL + c];
+        dp[j] = acc;
+        D += p[j] * acc;
+      }
+      double* dqh = dq + (r * H + h) * static_cast<int64_t>(kDL);
+      for (int i = 0; i < kDL; ++i) dqh[i] = 0.0;
+      for (size_t j = 0; j < n; ++j) {
+        const double dl = p[j] * (dp[j] - D);
+        double* dk = dkv_h.data() + (static_cast<size_t>(h) * n + j) * kDL;
+        for (int i = 0; i < kDL; ++i) {
+          dqh[i] += scale * dl * kv[sel[j] * kDL + i];
+          dk[i] += scale * dl * qh[i];
+        }
+        for (int c = 0; c < kDV; ++c) dk[c] += p[j] * dol[c];
+      }
+    }
+    for (int32_t h = 0; h < H; ++h)
+      for (size_t j = 0; j < n; ++j)
+        for (int i = 0; i < kDL; ++i) dkv[sel[j] * kDL + i] += dkv_h[(static_cast<size_t>(h) * n + j) * kDL + i];
   }
 }
 

@@ -724,3 +724,71 @@ def test_o_proj_against_library_matmul_and_selection():
     S = np.zeros((N, K), np.float32)
     S[np.arange(N), perm] = 1
     assert np.array_equal(oracle.o_proj(x, _bf(S)), x[:, perm])
+
+
+# ---------------------------------------------------------------- sparse MLA backward (KC: native-96-head backward)
+
+def _bwd_case(seed, n, H, T, k):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, H, 576)) * 0.3
+    kv = rng.standard_normal((T, 576))
+    W = rng.standard_normal((H, 512, 128)) * 0.05
+    gate = rng.standard_normal((n, H))
+    dout = rng.standard_normal((n, H, 128))
+    idx = np.full((n, k), -1, np.int32)
+    for r in range(n):
+        m = rng.integers(1, k + 1)
+        idx[r, :m] = rng.integers(0, T, m)       # duplicates allowed
+    idx[0, 1] = idx[0, 0]                       # a duplicate for sure
+    idx[-1, 0] = T + 3                          # out of range: skipped
+    return q, kv, idx, W, gate, dout
+
+
+def test_backward_against_finite_differences():
+    """Directional derivatives of L = sum(dout * out) by central differences of the oracle's own forward
+    (double inputs) equal the backward's gradients, for q, kv, W_UV and the gate separately."""
+    q, kv, idx, W, gate, dout = _bwd_case(51, 3, 4, 20, 7)
+    scale = 1 / math.sqrt(192)
+    g = oracle.sparse_mla_bwd(q, kv, idx, W, gate, scale, dout)
+
+    def L(q_, kv_, W_, g_):
+        return float((oracle.sparse_mla_f64in(q_, kv_, idx, W_, g_, scale)[0] * dout).sum())
+    rng = np.random.default_rng(7)
+    eps = 1e-6
+    for name, x, grad in [("q", q, g["dq"]), ("kv", kv, g["dkv"]), ("W_UV", W, g["dW_UV"]), ("gate", gate, g["dgate"])]:
+        v = rng.standard_normal(x.shape)
+        args = {"q": q, "kv": kv, "W_UV": W, "gate": gate}
+        plus, minus = dict(args), dict(args)
+        plus[name], minus[name] = x + eps * v, x - eps * v
+        fd = (L(plus["q"], plus["kv"], plus["W_UV"], plus["gate"]) - L(minus["q"], minus["kv"], minus["W_UV"],
+                                                                      minus["gate"])) / (2 * eps)
+        an = float((grad * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
+
+
+def test_backward_against_torch_autograd():
+    """Library cross-check: torch autograd in float64 on a dense gathered formulation of the same
+    forward gives the same gradients."""
+    n, H, T, k = 4, 8, 30, 9
+    q, kv, idx, W, gate, dout = _bwd_case(52, n, H, T, k)
+    scale = 1 / math.sqrt(192)
+    g = oracle.sparse_mla_bwd(q, kv, idx, W, gate, scale, dout)
+    tq = torch.tensor(q, requires_grad=True)
+    tkv = torch.tensor(kv, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    tg_ = torch.tensor(gate, requires_grad=True)
+    outs = []
+    for r in range(n):
+        sel = [int(s) for s in idx[r] if 0 <= s < T]
+        K = tkv[sel]                                               # [m,576]
+        l = scale * torch.einsum("hi,mi->hm", tq[r], K)
+        p = torch.softmax(l, dim=1)
+        ol = p @ K[:, :512]                                        # [H,512]
+        o = torch.einsum("hc,hcd->hd", ol, tW)
+        outs.append(torch.sigmoid(tg_[r])[:, None] * o)
+    loss = (torch.stack(outs) * torch.tensor(dout)).sum()
+    loss.backward()
+    for name, ref, got in [("dq", tq.grad, g["dq"]), ("dkv", tkv.grad, g["dkv"]), ("dW_UV", tW.grad, g["dW_UV"]),
+                           ("dgate", tg_.grad, g["dgate"])]:
+        ref = ref.numpy()
+        assert np.abs(ref - got).max() <= 1e-12 * max(np.abs(ref).max(), 1e-30), name
