@@ -400,6 +400,29 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
     t_abs = float(np.mean([e[0].elapsed_time(e[1]) for e in eva]))
     t_op = float(np.mean([e[1].elapsed_time(e[2]) for e in eva]))
     del q_nope, q_pe, W_UK, W_o, y
+    # The backward of the attention, up-projection and gate (96 heads), on the fused step's indices,
+    # out and lse, with a seeded synthetic dout.
+    t_bwd = None
+    if cfg.H == 96:
+        lse = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+        dsa.dsa_fused_fwd(shape, dev["q_I"], dev["k_I"], dev["w"], dev["q"], dev["kv"], dev["W_UV"], dev["gate"],
+                          topk_idx, out, ws, lse=lse)
+        dout = torch.randn((T, cfg.H, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        wsb = dsa.alloc_bwd_workspace(shape)
+        dq = torch.empty((T, cfg.H, 576), dtype=torch.float32, device="cuda")
+        dkv = torch.empty((T, 576), dtype=torch.float32, device="cuda")
+        dW = torch.empty((cfg.H, 512, 128), dtype=torch.float32, device="cuda")
+        dg = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+        n_bwd = 3 if T > 65536 else n_stage
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_bwd)]
+        for i in range(n_bwd):
+            evb[i][0].record(stream)
+            dsa.dsa_sparse_mla_bwd(shape, dev["q"], dev["kv"], topk_idx, dev["W_UV"], dev["gate"], out, lse, dout, dq,
+                                   dkv, dW, dg, wsb)
+            evb[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_bwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evb]))
+        del lse, dout, wsb, dq, dkv, dW, dg
     cold = []
     if cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -444,6 +467,12 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
         "o_proj_ms": round(t_op, 4), "o_proj_tflops": round(op_flop / (t_op * 1e-3) / 1e12, 1),
         "o_proj_frac": round(op_flop / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     })
+    if t_bwd is not None:
+        # backward flops: S recompute (576), dP (512), dq (576), dkv (576 + 512) per selected key and head,
+        # the forward attention again for o_lat (1,088), and do_lat and dW_UV (2 * 512 * 128 each) per row and head
+        bwd_flop = 2.0 * cfg.H * (576 + 512 + 576 + 576 + 512 + 1088) * w["keff_sum"] + 2.0 * 2 * cfg.H * 512 * 128 * T
+        res.update({"bwd_ms": round(t_bwd, 4), "bwd_tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 1),
+                    "bwd_frac": round(bwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
     if t_idx8 is not None:
         res.update({
             # FP8 indexer: the same algorithmic flops against the dense fp8 MFMA peak

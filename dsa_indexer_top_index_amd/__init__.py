@@ -18,6 +18,7 @@ Entry points (same names as the C ABI):
   dsa_quantize_fp8(x, q8, scale)
   dsa_q_absorb(shape, q_nope, q_pe, W_UK, q)
   dsa_o_proj(shape, x, W_o, y)
+  dsa_sparse_mla_bwd(shape, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, workspace)
   dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
   gate [rows,H,128] and per-head sink logits [H] float32)
 """
@@ -97,6 +98,10 @@ def lib():
         L.dsa_index_topk_fp8.restype = ctypes.c_int
         L.dsa_quantize_fp8.argtypes = [ctypes.c_int64, v, v, v, v]
         L.dsa_quantize_fp8.restype = ctypes.c_int
+        L.dsa_bwd_workspace_size.argtypes = [P]
+        L.dsa_bwd_workspace_size.restype = ctypes.c_size_t
+        L.dsa_sparse_mla_bwd.argtypes = [P, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_sparse_mla_bwd.restype = ctypes.c_int
         L.dsa_o_proj.argtypes = [P, v, v, ctypes.c_int32, v, v]
         L.dsa_o_proj.restype = ctypes.c_int
         L.dsa_q_absorb.argtypes = [P, v, v, v, v, v]
@@ -231,6 +236,27 @@ def dsa_q_absorb(shape, q_nope, q_pe, W_UK, q):
                             _p(q_pe, bf, "q_pe", numel=r * H * 64), _p(W_UK, bf, "W_UK", numel=H * 512 * 128),
                             _p(q, bf, "q", numel=r * H * 576), _stream())
     _raise(st, "dsa_q_absorb")
+
+
+def alloc_bwd_workspace(shape: Shape, device="cuda") -> torch.Tensor:
+    n = int(lib().dsa_bwd_workspace_size(ctypes.byref(shape)))
+    if n == 0:
+        _raise(dsa_check_shape(shape), "dsa_bwd_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dsa_sparse_mla_bwd(shape, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, workspace):
+    """Gradients of sum(dout * out) for dsa_sparse_mla_fwd (H = 96): dq [rows,H,576], dkv [T,576],
+    dW_UV [H,512,128], dgate [rows,H], float32."""
+    bf, f, n = torch.bfloat16, torch.float32, _sizes(shape)
+    st = lib().dsa_sparse_mla_bwd(
+        ctypes.byref(shape), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(W_UV, bf, "W_UV", numel=n["W_UV"]),
+        _p(gate, bf, "gate", numel=n["gate"]), _p(out, bf, "out", numel=n["out"]), _p(lse, f, "lse", numel=n["lse"]),
+        _p(dout, bf, "dout", numel=n["out"]), _p(dq, f, "dq", numel=n["q"]), _p(dkv, f, "dkv", numel=n["kv"]),
+        _p(dW_UV, f, "dW_UV", numel=n["W_UV"]), _p(dgate, f, "dgate", numel=n["gate"]),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_sparse_mla_bwd")
 
 
 def dsa_o_proj(shape, x, W_o, y):

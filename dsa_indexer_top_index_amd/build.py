@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dsa_api.cpp", "k_index.hip", "k_mla.hip", "k_up.hip", "k_absorb.hip", "k_gemm.hip"]
+SOURCES = ["dsa_api.cpp", "k_index.hip", "k_mla.hip", "k_up.hip", "k_absorb.hip", "k_gemm.hip", "k_bwd.hip"]
 # Per-file code generation options. The attention kernel keeps 256 fp32 accumulators per lane in
 # AGPRs; selecting the VGPR form of MFMA lets the query fragments live in AGPRs as MFMA operands and
 # the QK^T accumulators in VGPRs, instead of evicting an output tile every key tile.

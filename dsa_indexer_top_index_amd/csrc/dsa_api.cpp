@@ -289,7 +289,7 @@ dsa_status dsa_q_absorb(const dsa_shape* s, const uint16_t* q_nope, const uint16
   if (st != DSA_OK) return st;
   if (!q_nope || !q_pe || !W_UK || !q) return DSA_ERR_INVALID_ARG;
   if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(W_UK, 16) || !aligned(q, 16)) return DSA_ERR_INVALID_ARG;
-  dsa::AbsorbArgs a{q_nope, q_pe, W_UK, q, rows_of(s), s->H};
+  dsa::AbsorbArgs a{q_nope, q_pe, W_UK, q, rows_of(s), s->H, 576};
   return dsa::launch_q_absorb(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
@@ -302,6 +302,88 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
   if (d_model < 256 || d_model % 256 != 0) return DSA_ERR_UNSUPPORTED;
   dsa::GemmArgs g{x, W_o, y, rows_of(s), d_model, s->H * 128};
   return dsa::launch_gemm_nt(g, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
+}
+
+// Backward workspace: the forward's layout, then for one row chunk do [rows, H, 128] bf16,
+// do_lat [rows, H, 512] bf16 and D [rows, H] f32 (the o_lat region holds the recomputed o_lat).
+struct BwdLayout {
+  size_t do_off, dolat_off, delta_off, total;
+};
+
+static BwdLayout bwd_layout_of(const dsa_shape* s) {
+  const Layout L = layout_of(s);
+  BwdLayout B{};
+  const size_t cr = static_cast<size_t>(L.chunk_rows) * s->H;
+  B.do_off = L.total;
+  B.dolat_off = B.do_off + align_up(cr * 128 * 2);
+  B.delta_off = B.dolat_off + align_up(cr * 512 * 2);
+  B.total = B.delta_off + align_up(cr * 4);
+  return B;
+}
+
+size_t dsa_bwd_workspace_size(const dsa_shape* s) {
+  if (dsa_check_shape(s) != DSA_OK) return 0;
+  return bwd_layout_of(s).total;
+}
+
+dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
+                              const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out, const float* lse,
+                              const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate, void* ws,
+                              size_t ws_bytes, void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (s->H != 96) return DSA_ERR_UNSUPPORTED;
+  if (!q || !kv || !topk_idx || !W_UV || !gate || !out || !lse || !dout || !dq || !dkv || !dW_UV || !dgate)
+    return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(topk_idx, 4) || !aligned(W_UV, 16) || !aligned(gate, 2) ||
+      !aligned(out, 16) || !aligned(lse, 4) || !aligned(dout, 16) || !aligned(dq, 4) || !aligned(dkv, 4) ||
+      !aligned(dW_UV, 4) || !aligned(dgate, 4))
+    return DSA_ERR_INVALID_ARG;
+  const BwdLayout B = bwd_layout_of(s);
+  if (ws == nullptr || ws_bytes < B.total) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return DSA_ERR_INVALID_ARG;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const Layout L = layout_of(s);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint16_t* olat = reinterpret_cast<uint16_t*>(base + L.olat_off);
+  uint16_t* d_o = reinterpret_cast<uint16_t*>(base + B.do_off);
+  uint16_t* dolat = reinterpret_cast<uint16_t*>(base + B.dolat_off);
+  float* delta = reinterpret_cast<float*>(base + B.delta_off);
+  if (dsa::launch_fill_zero(dkv, static_cast<int64_t>(s->T) * 576, hs) != hipSuccess ||
+      dsa::launch_fill_zero(dW_UV, static_cast<int64_t>(s->H) * 512 * 128, hs) != hipSuccess)
+    return DSA_ERR_LAUNCH;
+  const int64_t rows = rows_of(s);
+  for (int64_t c0 = 0; c0 < rows; c0 += L.chunk_rows) {
+    const int n = static_cast<int>(std::min<int64_t>(L.chunk_rows, rows - c0));
+    dsa::BwdPrepArgs p{dout, out, gate, d_o, delta, dgate, n, s->H, static_cast<int>(c0)};
+    if (dsa::launch_bwd_prep(p, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::AbsorbArgs ab{d_o, nullptr, W_UV, dolat, n, s->H, 512};  // do_lat = do W_UV[h]^T
+    if (dsa::launch_q_absorb(ab, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::BwdArgs b{};
+    b.q = q;
+    b.kv = kv;
+    b.idx = topk_idx;
+    b.lse = lse;
+    b.delta = delta;
+    b.do_lat = dolat;
+    b.dq = dq;
+    b.dkv = dkv;
+    b.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
+    b.n_docs = s->n_docs;
+    b.T = s->T;
+    b.row0 = s->q_begin;
+    b.chunk_r0 = static_cast<int>(c0);
+    b.chunk_rows = n;
+    b.k = s->topk;
+    b.H = s->H;
+    b.scale = s->softmax_scale;
+    if (dsa::launch_sparse_mla_bwd(b, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    // o_lat of the chunk again (the forward's attention kernel), for dW_UV
+    if ((st = launch_attention(s, nullptr, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
+    dsa::DwArgs dw{olat, d_o, dW_UV, n, s->H};
+    if (dsa::launch_dwuv(dw, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+  }
+  return DSA_OK;
 }
 
 dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream) {

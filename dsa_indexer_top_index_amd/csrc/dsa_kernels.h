@@ -74,11 +74,12 @@ struct UpArgs {
 
 struct AbsorbArgs {
   const uint16_t* q_nope;  // [rows, H, 128]
-  const uint16_t* q_pe;    // [rows, H, 64]
+  const uint16_t* q_pe;    // [rows, H, 64], or nullptr: no pass-through dims
   const uint16_t* W_UK;    // [H, 512, 128]
-  uint16_t* q;             // [rows, H, 576]
+  uint16_t* q;             // [rows, H, out_stride]
   int rows;
   int H;
+  int out_stride;          // 576 (the latent query), or 512 (no pass-through dims)
 };
 
 struct GemmArgs {
@@ -86,6 +87,46 @@ struct GemmArgs {
   const uint16_t* B;  // [N, K] bf16, K contiguous
   uint16_t* C;        // [M, N] bf16
   int M, N, K;        // N a multiple of 256, K a multiple of 64
+};
+
+struct BwdPrepArgs {
+  const uint16_t* dout;  // [nrows, H, 128] bf16, caller rows
+  const uint16_t* out;   // [nrows, H, 128] bf16, the forward's output
+  const uint16_t* gate;  // [nrows, H] bf16
+  uint16_t* d_o;         // [rows, H, 128] bf16, chunk-local: sigma(g) dout
+  float* delta;          // [rows, H], chunk-local: sum_d dout * out
+  float* dgate;          // [nrows, H], caller rows
+  int rows;              // rows of this chunk
+  int H;
+  int row_off;           // first caller row of the chunk
+};
+
+struct BwdArgs {
+  const uint16_t* q;       // [nrows, H, 576]
+  const uint16_t* kv;      // [T, 576]
+  const int32_t* idx;      // [nrows, k]
+  const float* lse;        // [nrows, H] natural log, from the forward
+  const float* delta;      // [chunk_rows, H]
+  const uint16_t* do_lat;  // [chunk_rows, H, 512]
+  float* dq;               // [nrows, H, 576]
+  float* dkv;              // [T, 576], added to
+  const int32_t* cu;
+  int n_docs;
+  int T;
+  int row0;                // global token of local row 0
+  int chunk_r0;
+  int chunk_rows;
+  int k;
+  int H;                   // a multiple of 32
+  float scale;
+};
+
+struct DwArgs {
+  const uint16_t* o_lat;  // [rows, H, 512] chunk-local
+  const uint16_t* d_o;    // [rows, H, 128] chunk-local
+  float* dW;              // [H, 512, 128], added to
+  int rows;
+  int H;
 };
 
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
@@ -101,5 +142,9 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t st);
 hipError_t launch_up_gate(const UpArgs& a, hipStream_t st);
 hipError_t launch_q_absorb(const AbsorbArgs& a, hipStream_t st);
 hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t st);
+hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_dwuv(const DwArgs& a, hipStream_t st);
 
 }  // namespace dsa

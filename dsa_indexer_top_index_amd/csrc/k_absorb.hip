@@ -15,6 +15,8 @@
 // (K = d) stay in registers; v_mfma_f32_32x32x16_bf16 takes rows as M, c as N (four 32-wide tiles)
 // and d as K (eight steps). Outputs leave through a per-wave LDS tile in 16-byte stores; the first
 // quarter also copies q_pe into dims 512..575. HBM-bound: 1.5 KB per (row, head) against 131 K flop.
+// The same product with a 512-wide output and no pass-through dims gives the backward's
+// do_lat = do W_UV[h]^T (W_UV has the same [H, 512, 128] layout).
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -93,11 +95,11 @@ __global__ __launch_bounds__(kAbWaves * kWave, 2) void k_q_absorb(AbsorbArgs a) 
       const int rw = 4 * i + (lane >> 4);  // 16 lanes per row, 16 bytes each
       const int row = row0 + 32 * mt + rw;
       const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(st + rw * kAbN + 8 * (lane & 15));
-      if (row < rows) *reinterpret_cast<u32x4*>(a.q + (static_cast<int64_t>(row) * H + h) * kLatent + c0 + 8 * (lane & 15)) = v;
+      if (row < rows) *reinterpret_cast<u32x4*>(a.q + (static_cast<int64_t>(row) * H + h) * a.out_stride + c0 + 8 * (lane & 15)) = v;
     }
     wave_lds_sync();  // the staged rows are read before the next M tile overwrites them
   }
-  if (quarter == 0) {
+  if (quarter == 0 && a.q_pe != nullptr) {
     // q_pe: 64 rows x 8 granules of this wave
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

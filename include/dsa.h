@@ -202,6 +202,22 @@ dsa_status dsa_q_absorb(const dsa_shape* shape, const uint16_t* q_nope, const ui
 dsa_status dsa_o_proj(const dsa_shape* shape, const uint16_t* x, const uint16_t* W_o, int32_t d_model,
                       uint16_t* y, void* stream);
 
+/* Backward of steps 4-5 on the native 96 heads (model-coverage page, paragraph after the
+ * Implementation Limits bullets: the backward runs 96 heads without padding; 3rd bullet: hard top-k
+ * carries no gradient, so topk_idx is a constant and the indexer has no backward). For the loss
+ * L = sum(dout * out) of dsa_sparse_mla_fwd (per-head gate, no sink) on the same q, kv, topk_idx,
+ * W_UV and gate, given that call's out [rows, H, 128] and lse [rows, H]:
+ *   dq [rows, H, 576], dkv [T, 576], dW_UV [H, 512, 128], dgate [rows, H], all float32.
+ * dkv and dW_UV are overwritten (zeroed, then accumulated over the rows with atomic adds, so their
+ * last bits depend on the order); dq and dgate are written. H must be 96 (else
+ * DSA_ERR_UNSUPPORTED). Workspace: >= dsa_bwd_workspace_size(shape) bytes. */
+size_t dsa_bwd_workspace_size(const dsa_shape* shape);
+dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
+                              const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
+                              const uint16_t* out, const float* lse, const uint16_t* dout, float* dq,
+                              float* dkv, float* dW_UV, float* dgate, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);
 

@@ -19,9 +19,10 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == ["dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk", "dsa_index_topk_fp8",
-                     "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb", "dsa_quantize_fp8", "dsa_sparse_attention_latent", "dsa_sparse_mla_fwd",
-                     "dsa_sparse_mla_fwd_ex", "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
+    assert names == ["dsa_bwd_workspace_size", "dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
+                     "dsa_index_topk_fp8", "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb", "dsa_quantize_fp8",
+                     "dsa_sparse_attention_latent", "dsa_sparse_mla_bwd", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_ex",
+                     "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -193,3 +194,19 @@ def test_fp8_entry_points_host_checks():
     assert L.dsa_quantize_fp8(-1, fake, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_quantize_fp8(4, None, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_quantize_fp8(4, fake, fake + 8, fake, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_backward_host_checks():
+    """The backward takes 96 heads only, checks its pointers and its (larger) workspace."""
+    L = dsa.lib()
+    fake = 1 << 20
+    s = _shape(T=1024)
+    nb = L.dsa_bwd_workspace_size(ctypes.byref(s))
+    assert nb > dsa.dsa_workspace_size(s)
+    args = [fake] * 12
+    assert L.dsa_sparse_mla_bwd(ctypes.byref(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)), *args, fake, nb,
+                                None) == dsa.DSA_ERR_UNSUPPORTED
+    assert L.dsa_sparse_mla_bwd(ctypes.byref(s), *args, fake, nb - 1, None) == dsa.DSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[7] = None  # dout
+    assert L.dsa_sparse_mla_bwd(ctypes.byref(s), *bad, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG

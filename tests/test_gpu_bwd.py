@@ -1,0 +1,138 @@
+"""GPU parity of the sparse MLA backward on the native 96 heads (model-coverage page: the backward runs
+96 heads without padding; hard top-k carries no gradient) against the oracle's double-precision
+backward, through the C ABI. The indices, out and lse come from the GPU forward; the oracle takes the
+same bf16 values as exact doubles. Each gradient must satisfy the output rule
+max |g - g_ref| <= 2e-2 * max |g_ref| (the GPU rounds do, do_lat, P and dS to bf16 for its MFMAs and
+takes D = sum dout * out from the bf16 out)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_indexer_top_index_amd as dsa
+import oracle
+import testgen as tg
+from tests import gpu_util as gu
+from tests.parity import check_outputs
+
+pytestmark = pytest.mark.gpu
+
+TAG_DOUT = 70
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _f64(a):
+    return tg.bf16_to_f32(a).astype(np.float64)
+
+
+def _run_bwd(cfg, inp, idx_t, out_t, lse_t, dout):
+    T, H = cfg.T, cfg.H
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg, dev["cu_seqlens"])
+    ws = dsa.alloc_bwd_workspace(shape)
+    dq = torch.empty((T, H, 576), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((T, 576), dtype=torch.float32, device="cuda")
+    dW = torch.empty((H, 512, 128), dtype=torch.float32, device="cuda")
+    dg = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_mla_bwd(shape, dev["q"], dev["kv"], idx_t, dev["W_UV"], dev["gate"], out_t, lse_t,
+                           gu.bf16_np_to_tensor(dout), dq, dkv, dW, dg, ws)
+    torch.cuda.synchronize()
+    return {"dq": dq.cpu().numpy(), "dkv": dkv.cpu().numpy(), "dW_UV": dW.cpu().numpy(), "dgate": dg.cpu().numpy()}
+
+
+def _compare(name, got, inp, idx, dout, cfg):
+    ref = oracle.sparse_mla_bwd(_f64(inp["q"]), _f64(inp["kv"]), idx, _f64(inp["W_UV"]), _f64(inp["gate"]),
+                                cfg.softmax_scale, _f64(dout))
+    msgs = []
+    for k in ["dq", "dkv", "dW_UV", "dgate"]:
+        ok, err, mx = check_outputs(got[k], ref[k])
+        msgs.append(f"{k} {err / mx:.2e}")
+        assert ok, (name, k, err, mx)
+    _say(f"[gpu] backward {name}: max error / max |ref|: " + ", ".join(msgs))
+
+
+@pytest.mark.parametrize("case", ["single", "packed"])
+def test_backward_after_fused_forward(case):
+    if case == "single":
+        cfg = tg.Config("bwd", 101, [700], topk=256, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24, W_UV_std=0.02)
+    else:
+        cfg = tg.Config("bwd-packed", 102, [300, 1, 40, 500], topk=128, H=96, H_I=64, d_I=128, w_scale=1 / 8,
+                        q_std=1 / 24, W_UV_std=0.02)
+    _say(f"[gpu] backward {case}: T={cfg.T} docs={cfg.n_docs} k={cfg.topk}")
+    inp = tg.make_inputs(cfg)
+    dev = gu.to_device(inp)
+    res = gu.run_fused(cfg, dev, with_lse=True)
+    torch.cuda.synchronize()
+    dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, cfg.T * cfg.H * 128, 1.0).reshape(cfg.T, cfg.H, 128)
+    got = _run_bwd(cfg, inp, res["topk_idx"], res["out"], res["lse"], dout)
+    _compare(case, got, inp, res["topk_idx"].cpu().numpy(), dout, cfg)
+
+
+def test_backward_caller_indices():
+    """Caller indices with duplicates, -1 and out-of-range entries, and a row with no usable index."""
+    cfg = tg.Config("bwd-idx", 103, [400], topk=64, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                    W_UV_std=0.02)
+    inp = tg.make_inputs(cfg)
+    T, k, H = cfg.T, cfg.topk, cfg.H
+    rng = np.random.default_rng(4)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        keff = min(k, t + 1)
+        row = rng.integers(0, t + 1, keff).astype(np.int32)
+        kill = rng.random(keff) < 0.15
+        row[kill] = rng.choice([-1, -5, T, T + 9], kill.sum())
+        idx[t, :keff] = row
+    idx[9, :] = -1
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_workspace(shape)
+    idx_t = torch.from_numpy(idx).cuda()
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    _say("[gpu] backward with caller indices")
+    dsa.dsa_sparse_mla_fwd(shape, dev["q"], dev["kv"], idx_t, dev["W_UV"], dev["gate"], out, ws, lse=lse)
+    dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128)
+    got = _run_bwd(cfg, inp, idx_t, out, lse, dout)
+    assert np.all(got["dq"][9] == 0) and np.all(got["dgate"][9] == 0)
+    _compare("caller indices", got, inp, idx, dout, cfg)
+
+
+def test_backward_t4096_sampled_rows():
+    """Full-size T=4096, top-2048: dq and dgate of sampled rows (each depends on its own row only), and
+    the dkv rows of keys 4088..4095, which by causality only rows 4088..4095 can select, so the oracle's
+    backward of those eight rows gives them in full. dW_UV sums over every row and is checked for
+    finiteness only at this size (the small cases above compare it in full)."""
+    cfg = tg.get_config("t4096")
+    keys, dev = gu.device_inputs(cfg)
+    res = gu.run_fused(cfg, dev, with_lse=True)
+    torch.cuda.synchronize()
+    dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, cfg.T * cfg.H * 128, 1.0).reshape(cfg.T, cfg.H, 128)
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_bwd_workspace(shape)
+    T, H = cfg.T, cfg.H
+    dq = torch.empty((T, H, 576), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((T, 576), dtype=torch.float32, device="cuda")
+    dW = torch.empty((H, 512, 128), dtype=torch.float32, device="cuda")
+    dg = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    _say("[gpu] backward t4096")
+    dsa.dsa_sparse_mla_bwd(shape, dev["q"], dev["kv"], res["topk_idx"], dev["W_UV"], dev["gate"], res["out"],
+                           res["lse"], gu.bf16_np_to_tensor(dout), dq, dkv, dW, dg, ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 2047, 2048, 3000] + list(range(4088, 4096)))
+    qr = tg.query_rows(cfg, rows)
+    idx = res["topk_idx"].cpu().numpy()[rows]
+    ref = oracle.sparse_mla_bwd(_f64(qr["q"].reshape(len(rows), H, 576)), _f64(keys["kv"]), idx, _f64(keys["W_UV"]),
+                                _f64(qr["gate"].reshape(len(rows), H)), cfg.softmax_scale, _f64(dout[rows]))
+    for k, g in [("dq", dq.cpu().numpy()[rows]), ("dgate", dg.cpu().numpy()[rows])]:
+        ok, err, mx = check_outputs(g, ref[k])
+        assert ok, (k, err, mx)
+    ok, err, mx = check_outputs(dkv.cpu().numpy()[4088:], ref["dkv"][4088:])
+    assert ok, ("dkv of the last keys", err, mx)
+    assert np.all(np.isfinite(dkv.cpu().numpy())) and np.all(np.isfinite(dW.cpu().numpy()))
