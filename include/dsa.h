@@ -131,7 +131,7 @@ dsa_status dsa_index_topk_noalloc(const dsa_shape* shape, const uint16_t* q_I, c
  * lse [rows, H] float32 natural-log softmax normaliser, or NULL. Only the first min(topk, n)
  * entries of a row are read (n = the row's number of causal keys); every usable one among them
  * is attended, duplicates included; causality of the indices is the caller's contract.
- * Workspace: >= dsa_workspace_size(shape) bytes (holds o_lat for up to 16384 rows at a time). */
+ * Workspace: >= dsa_workspace_size(shape) bytes (holds o_lat for up to 2048 rows at a time). */
 dsa_status dsa_sparse_mla_fwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
                               const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
                               uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,

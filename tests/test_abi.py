@@ -47,16 +47,16 @@ def test_supported_shapes_and_workspace():
     # LN(k_I) ((T + 128 padding rows) x d_I bf16), 256 candidate-slot flags (1 KB), 256 candidate
     # slots of 8 rows x 4,160 int32 token indices, the FP8 indexer's operands (E4M3 codes of LN(k_I)
     # and q_I, one float scale per 128-value row), and the latent output of one row chunk (rows x H x
-    # 512 bf16, at most 16,384 rows); each region starts 256-byte aligned
+    # 512 bf16, at most 2,048 rows); each region starts 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
     flags, slots = 1024, 256 * 8 * 4160 * 4
 
     def fp8(T, rows, H_I, d_I):
         return al((T + 128) * d_I) + al((T + 128) * 4) + al(rows * H_I * d_I) + al(rows * H_I * 4)
     ws = dsa.dsa_workspace_size(_shape())
-    assert ws == (4096 + 128) * 128 * 2 + flags + slots + fp8(4096, 4096, 64, 128) + 4096 * 96 * 512 * 2
+    assert ws == (4096 + 128) * 128 * 2 + flags + slots + fp8(4096, 4096, 64, 128) + 2048 * 96 * 512 * 2
     big = dsa.dsa_workspace_size(_shape(T=131072))
-    assert big == (131072 + 128) * 128 * 2 + flags + slots + fp8(131072, 131072, 64, 128) + 16384 * 96 * 512 * 2
+    assert big == (131072 + 128) * 128 * 2 + flags + slots + fp8(131072, 131072, 64, 128) + 2048 * 96 * 512 * 2
     assert dsa.dsa_workspace_size(_shape(topk=0)) == 0
     tiny = dsa.dsa_workspace_size(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16))
     assert tiny == (1024 + 128) * 64 * 2 + flags + slots + fp8(1024, 1024, 4, 64) + 1024 * 16 * 512 * 2
