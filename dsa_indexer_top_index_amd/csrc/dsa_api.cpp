@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kMaxTopk = 2048;         // summary of the model-coverage page: at most 2,048 keys
+constexpr int kMaxTopk = dsa::kIdxMaxTopk;  // summary of the model-coverage page: at most 2,048 keys
 constexpr int64_t kMlaChunkRows = 2048;  // rows per attention/up-projection pass: one chunk's o_lat (201 MB at 96 heads) stays in the Infinity Cache for the up-projection
 constexpr int64_t kIdxPairedBelow = 4096;  // rows with a selection under which indexer blocks pair long and short rows
 constexpr size_t kWsAlign = 256;
@@ -29,7 +29,7 @@ int32_t rows_of(const dsa_shape* s) { return (s->q_end == 0 ? s->T : s->q_end) -
 // Workspace regions, each from a 256-byte-aligned offset:
 //   LNk    [T + kIdxKeyPad, d_I] bf16   key LayerNorm output (the padding rows are staged, never scored)
 //   flags  [kIdxSlots] int32           candidate-slot claims of the indexer's workgroups
-//   cand   [kIdxSlots, slot words]     candidate token indices of the rows in flight
+//   cand   [kIdxSlots, slot words]     candidate lists (score keys, token indices) of the rows in flight
 //   LNk8   [T + kIdxKeyPad, d_I] u8    FP8 indexer: E4M3 codes of LNk, and sk [T + kIdxKeyPad] f32
 //   q8     [rows, H_I, d_I] u8         FP8 indexer: E4M3 codes of q_I, and sq [rows, H_I] f32
 //   o_lat  [chunk rows, H, 512] bf16   latent attention output of one row chunk
@@ -132,7 +132,7 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   a.row0 = s->q_begin;
   a.nrows = rows_of(s);
   a.k = s->topk;
-  // Candidate token indices live in kIdxSlots slots, one per workgroup in flight; every launch
+  // Candidate lists live in kIdxSlots slots, one per workgroup in flight; every launch
   // frees the slots it claimed, and the prologue marks them all free first.
   a.slot_flags = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + L.flags_off);
   a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.cand_off);

@@ -7,11 +7,15 @@
 namespace dsa {
 
 constexpr int kIdxMaxSeg = 64;  // row segments per indexer launch
-constexpr int kIdxKeyPad = 128; // LNk rows past T in the workspace: the indexer stages whole 64-key
-                                // chunks (up to two past the last key) and never scores those rows
+constexpr int kIdxKeyPad = 128; // LNk rows past T in the workspace: the indexer stages whole 128-key
+                                // chunks (the last one reaching up to 127 rows past the last key)
+                                // and never scores those rows
+constexpr int kIdxMaxTopk = 2048;  // largest k the indexer's buffers are sized for
 constexpr int kIdxSlots = 256;  // candidate-list slots: one per indexer workgroup resident at a time
                                 // (one per CU on MI355X); launches check residency against this
-constexpr int kIdxSlotWords = 8 * 4160;  // int32 words of one slot: 8 rows' candidate token indices
+constexpr int kIdxCap = 4608;   // candidate-list capacity of one indexer row
+constexpr int kIdxSlotWords = 8 * 2 * (kIdxCap + 64);  // int32 words of one slot: 8 rows' candidate score
+                                                      // keys and token indices (capacity + 64 of each)
 
 struct IndexArgs {
   const uint16_t* q_I;   // [nrows, H_I, d_I] local rows
@@ -28,7 +32,7 @@ struct IndexArgs {
   const float* sq;       //   [nrows, H_I] their power-of-two scales
   const uint8_t* LNk8;   //   [T + kIdxKeyPad, d_I] E4M3 codes of LNk
   const float* sk;       //   [T + kIdxKeyPad] their power-of-two scales
-  int32_t* cand;         // candidate token indices: n_slots slots of kIdxSlotWords int32 each
+  int32_t* cand;         // candidate lists (score keys, token indices): n_slots slots of kIdxSlotWords words each
   int* slot_flags;       // [n_slots] 1 while a workgroup holds the slot; zeroed by the prologue
   int n_slots;
   // Rows that need a selection, as segments of consecutive local rows of one document each.

@@ -13,23 +13,26 @@
 //    takes eight consecutive rows of a segment (longest first) or, when such rows are few, four of
 //    the longest and four of the shortest rows left, so that workgroups carry similar work. Rows
 //    with at most k causal keys are never scored: the prologue kernel writes them.
-//  - The LNk keys of the workgroup's causal range stream through LDS in chunks of 64 keys
+//  - The LNk keys of the workgroup's causal range stream through LDS in chunks of 128 keys
 //    (asynchronous 16-byte global->LDS copies, double buffered, one barrier per chunk). A staged
 //    chunk is laid out by MFMA operand: each 1 KB block is the B operand of one K step of one
-//    32-key tile, so operand reads take constant offsets and are bank-conflict free. All eight
-//    rows share every staged chunk.
-//  - Scores: v_mfma_f32_32x32x16_bf16 with the indexer heads as M (q_I of the row in
-//    registers), 32 keys as N and d_I as K. Each lane then owns one key column: ReLU, the head
-//    weight and the sum over heads happen in registers, and one permlane32 swap joins the two
-//    half-waves, leaving one full score per lane for 64 consecutive keys. The loop is software
-//    pipelined by half a chunk: the MFMAs of one 32-key tile run interleaved with the VALU epilogue
-//    of the tile before it, and the next chunk's copies and the previous chunk's append sit
-//    between MFMAs too.
+//    key tile, so operand reads take constant offsets and are bank-conflict free. All eight rows
+//    share every staged chunk; the candidate lists live in global memory, which leaves the LDS
+//    for the 128-key chunks.
+//  - Scores: v_mfma_f32_16x16x32_bf16 with the indexer heads as M (four 16-row tiles, q_I of the
+//    row in registers), 16 keys as N and d_I as K; each M tile's four K steps run as one
+//    same-accumulator chain, which the matrix core issues faster than alternating chains. Each
+//    lane then owns one key column for four heads per M tile: ReLU, the head weight and the sum
+//    over its heads happen in registers, and three lane swaps (permlane32, permlane16) join the
+//    four head groups of four 16-key tiles, leaving one full score per lane for 64 consecutive
+//    keys. The loop is software pipelined by one tile: the MFMAs of one tile run interleaved with
+//    the VALU epilogue of the tile before it, and the next chunk's copies and the appends sit
+//    between MFMAs too. (The FP8 form runs 32-key tiles on the 32x32x64 scaled MFMA.)
 //  - Top-k: scores become order-preserving uint32 keys. A key is appended to the row's candidate
-//    list (keys in LDS, token indices in the workspace) when it reaches the running threshold
-//    (ballot + mbcnt compaction, so the list stays in ascending token order; branch-free, lanes
-//    that drop their key write past the list). When a list nears capacity, the whole workgroup
-//    runs a radix select over its varying bits (LDS histograms, DPP scans) and a stable
+//    list (keys and token indices in the workspace, 4,608 per row) when it reaches the running
+//    threshold (ballot + mbcnt compaction, so the list stays in ascending token order; branch-free,
+//    lanes that drop their key write past the list). When a list nears capacity, the whole
+//    workgroup runs a radix select over its varying bits (LDS histograms, DPP scans) and a stable
 //    compaction keeps the k best (ties to the lower index), which raises the threshold. At the
 //    end each wave finishes its own row's exact selection.
 #include "dsa_device.h"
@@ -82,20 +85,15 @@ __device__ __forceinline__ void key_layernorm_block(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
-constexpr int kChunk = 64;        // keys per LDS chunk (two 32-key MFMA tiles)
-constexpr int kCap = 3840;        // candidate capacity of a row's list (>= k + kSelSlack + 2 * kChunk for k <= 2048)
-constexpr int kListSlots = kCap + 64;   // LDS slots per list: the last 64 take the lanes an append drops
-// Waves w and w + 4 share a SIMD and their lists sit side by side. When a block pairs long and
-// short rows, a long row that would overflow kCap may take kCapLong slots of the pair's space if
-// its partner row fits in the rest (kCapShort), so that it needs no selection before its end.
-constexpr int kCapLong = 4096;
-constexpr int kCapShort = 2 * kListSlots - (kCapLong + 64) - 64;
-constexpr int kCandStride = kCapLong + 64;  // per-row stride of the candidate token indices (global)
-static_assert(kCapShort >= 2048 + 64 + 2 * 64, "a short list still holds k + slack + two chunks");
-static_assert(kCap % 256 == 0 && kCapLong % 256 == 0 && kCapShort % 256 == 0, "the final selection copies 256 indices at a time");
-constexpr int kSelSlack = 64;    // extra entries a selection before the end of the row may keep
+constexpr int kHalf = 64;         // keys per score vector (one per lane)
+constexpr int kChunk = 128;       // keys per staged LDS chunk: four 32-key MFMA tiles, one barrier
+constexpr int kCap = kIdxCap;     // candidate capacity of a row's list
+constexpr int kCandStride = kCap + 64;  // per-row words of the keys and of the token indices; the last 64 take the lanes an append drops
+constexpr int kSelSlack = 64;     // extra entries a selection before the end of the row may keep
 constexpr int kIdxRows = 8;       // query rows per workgroup, one wave each (two per SIMD)
-
+static_assert(kCap >= kIdxMaxTopk + kSelSlack + kChunk, "a list takes a chunk after a selection that kept k + slack");
+static_assert(kCap % (kIdxRows * kWave) == 0, "whole wave slices in the workgroup selection");
+static_assert(kIdxSlotWords == kIdxRows * 2 * kCandStride, "slot size");
 
 // max(x, +0) as an integer max on the bit pattern: negative values and -0 (sign bit set) give +0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -141,15 +139,15 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t x) {
 // k-th key leaves at most `slack` extra entries: then every entry at or above that bin's lower
 // bound is kept (at least k) and the bound becomes the threshold, which is still at or below the
 // k-th key, so no key of the final top k is dropped. *kept_out receives the number kept.
-// keys live in LDS, their token indices in global memory (idxs); the list is compacted in place
-// and stays in ascending token order.
+// keys and their token indices live in global memory (the workspace); the list is compacted in
+// place and stays in ascending token order.
 // hist: 3 * 256 words, scratch: 4*NW words of LDS. Must be called by every thread of the
-// workgroup. The compacted indices are not waited for: a later reader of idxs from another wave
-// waits for this workgroup's stores (s_waitcnt vmcnt(0)) and a barrier first.
+// workgroup. The compacted list is not waited for: a later reader from another wave waits for
+// this workgroup's stores (s_waitcnt vmcnt(0)) and a barrier first.
 template <int NW>
-__device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
+__device__ __forceinline__ uint32_t wg_select_topk(uint32_t* __restrict__ keys, int32_t* __restrict__ idxs, DSA_LDS uint32_t* hist,
                                                    DSA_LDS uint32_t* scratch, int cnt, int k, int slack, int* kept_out) {
-  constexpr int kSelU = (kCapLong + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
+  constexpr int kSelU = (kCap + NW * kWave - 1) / (NW * kWave);  // list entries per lane of a wave slice
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   cnt = __builtin_amdgcn_readfirstlane(cnt);
@@ -167,7 +165,7 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     x[u] = 0;
     if (s0 + kWave * u < cnt && in[u]) {
       v[u] = keys[i];
-      x[u] = idxs[i];  // global loads, needed only by the compaction
+      x[u] = idxs[i];  // needed only by the compaction
     }
   }
   uint32_t o = 0u, a = 0xffffffffu;
@@ -266,7 +264,7 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
     scratch[2 * NW + wave] = static_cast<uint32_t>(gt_w);
     scratch[3 * NW + wave] = static_cast<uint32_t>(eq_w);
   }
-  wait_vmem();    // this wave's index loads are complete before another wave overwrites them
+  wait_vmem();    // this wave's list loads are complete before another wave overwrites them
   // Consume every index load here, on every path: the stores below then need no wait each, and the
   // compiler's wait insertion does not treat the loads as possibly outstanding at the caller's loop
   // head (it would drain every memory operation, the next chunk's copies included, there).
@@ -307,36 +305,53 @@ __device__ __forceinline__ uint32_t wg_select_topk(DSA_LDS uint32_t* keys, int32
   return lo == 0 ? cur + 1u : cur;
 }
 
-// Exact top k of one row's cnt candidates (k < cnt <= kCapLong) by one wave, without workgroup
-// barriers, so that every wave can finish its own row at the same time. Keys in LDS (list, cap
-// words rounded up to 256) and token indices in global memory (idxs), both in ascending token
-// order; the k kept indices go to out[0 .. k) in that order (keys desc, ties to the lower index).
-// hist: 256 words of LDS that only this wave uses.
+// Exact top k of one row's cnt candidates (k < cnt <= kCap) by one wave, without workgroup
+// barriers, so that every wave can finish its own row at the same time. Keys and token indices in
+// global memory (the row's list in the workspace), both in ascending token order; the k kept
+// indices go to out[0 .. k) in that order (keys desc, ties to the lower index). hist (256 words)
+// and obuf (k words) are LDS that only this wave uses.
 //
 // The eight waves of a block finish their rows together, so the selection keeps its memory
-// instructions few and its LDS reads batched: once the keys are in registers, the token indices
-// are copied into the list's own LDS slots (1 KB per copy), compacted there in place, and the k
-// kept ones leave in 16-byte stores.
-__device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const int32_t* __restrict__ idxs,
-                                                DSA_LDS uint32_t* hist, int cnt, int k, int32_t* __restrict__ out) {
-  constexpr int U = kCapLong / kWave;  // entries per lane: entry 64*u + lane
-  constexpr int G = 8;                 // slots per group
-  static_assert(kCapLong % kWave == 0 && U % G == 0, "whole list rows and groups");
+// instructions few and its waits few: every key and every token index of the list is loaded into
+// registers at the start, group by group (the index loads land while the radix levels run), and
+// the kept indices are compacted into obuf and leave from there in 16-byte stores.
+__device__ __forceinline__ void wave_select_out(const uint32_t* __restrict__ keys, const int32_t* __restrict__ idxs,
+                                                DSA_LDS uint32_t* hist, DSA_LDS uint32_t* obuf, int cnt, int k,
+                                                int32_t* __restrict__ out) {
+  constexpr int U = kCap / kWave;  // entries per lane: entry 64*u + lane
+  constexpr int G = 8;             // slots per group
+  static_assert(kCap % kWave == 0 && U % G == 0 && G * kWave * (U / G) <= kCandStride, "whole list rows and groups");
   const int lane = lane_id();
   cnt = __builtin_amdgcn_readfirstlane(cnt);
   // Slots go in groups of G; the groups past the list are skipped by uniform branches, and within
-  // a group nothing branches, so that the LDS reads of a group issue back to back and wait once.
-  // The pad entries of the last group (past cnt) hold key 0: they take part in a level only if
-  // key 0 matches its prefix, and each histogram then takes them back out of bin 0.
+  // a group nothing branches. The pad entries of the last group (past cnt) hold key 0: they take
+  // part in a level only if key 0 matches its prefix, and each histogram then takes them back out
+  // of bin 0. Their token-index slots lie inside the row's list area and are never kept.
   const int ng = (cnt + G * kWave - 1) / (G * kWave);
   const uint32_t pad = static_cast<uint32_t>(G * kWave * ng - cnt);
   uint32_t v[U];
-  uint32_t o = 0u, a = 0xffffffffu;
+  int32_t x[U];
 #pragma unroll
   for (int g = 0; g < U / G; ++g) {
     if (g < ng) {
 #pragma unroll
-      for (int i = 0; i < G; ++i) v[G * g + i] = list[min(kWave * (G * g + i) + lane, cnt - 1)];
+      for (int i = 0; i < G; ++i) v[G * g + i] = keys[min(kWave * (G * g + i) + lane, cnt - 1)];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < U / G; ++g) {
+    if (g < ng) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) x[G * g + i] = idxs[kWave * (G * g + i) + lane];
+    } else {
+#pragma unroll
+      for (int i = 0; i < G; ++i) x[G * g + i] = 0;
+    }
+  }
+  uint32_t o = 0u, a = 0xffffffffu;
+#pragma unroll
+  for (int g = 0; g < U / G; ++g) {
+    if (g < ng) {
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         const int u = G * g + i;
@@ -350,9 +365,6 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
       for (int i = 0; i < G; ++i) v[G * g + i] = 0u;
     }
   }
-  wave_lds_sync();  // every key is in registers before the copies below overwrite the list
-  // entries [256j, 256j + 256) of idxs to list + 256j; they land while the radix levels run
-  for (int j = 0; 256 * j < cnt; ++j) copy16_to_lds(idxs + 256 * j + 4 * lane, list + 256 * j);
   o = wave_or(o);
   a = wave_and(a);
   const uint32_t varying = o ^ a;
@@ -418,10 +430,7 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
       if (sh == 0) break;
     }
   }
-  // Stable compaction in place, a group at a time: the group's indices are read before any of its
-  // kept entries is written, and a kept entry moves to a slot at or below its own, so no entry is
-  // overwritten before it is read.
-  wait_vmem();
+  // Stable compaction into obuf (the indices are in registers; obuf's k words take exactly the kept ones).
   int kept = 0;
   if (whole_bin && cur != 0u) {
     // keep exactly the entries >= cur (the bits of cur below lo are zero, so (v & hi_mask(lo)) >=
@@ -429,14 +438,11 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
 #pragma unroll
     for (int g = 0; g < U / G; ++g) {
       if (g < ng) {
-        uint32_t x[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) x[i] = list[kWave * (G * g + i) + lane];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           const bool keep = v[G * g + i] >= cur;
           const uint64_t mk = ballot(keep);
-          if (keep) list[kept + lanes_below(mk)] = x[i];
+          if (keep) obuf[kept + lanes_below(mk)] = static_cast<uint32_t>(x[G * g + i]);
           kept += __popcll(mk);
         }
       }
@@ -448,9 +454,6 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
 #pragma unroll
     for (int g = 0; g < U / G; ++g) {
       if (g < ng) {
-        uint32_t x[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) x[i] = list[kWave * (G * g + i) + lane];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
           const int u = G * g + i;
@@ -460,7 +463,7 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
           const uint64_t me = ballot(eq);
           const bool keep = (in && vh > cur) || (eq && eq_seen + lanes_below(me) < need);
           const uint64_t mk = ballot(keep);
-          if (keep) list[kept + lanes_below(mk)] = x[i];
+          if (keep) obuf[kept + lanes_below(mk)] = static_cast<uint32_t>(x[u]);
           kept += __popcll(mk);
           eq_seen += __popcll(me);
         }
@@ -470,35 +473,55 @@ __device__ __forceinline__ void wave_select_out(DSA_LDS uint32_t* list, const in
   wave_lds_sync();
   if ((k & 3) == 0) {  // rows of out are 16-byte aligned
     for (int e = 4 * lane; e < k; e += 4 * kWave)
-      *reinterpret_cast<u32x4*>(out + e) = *reinterpret_cast<const DSA_LDS u32x4*>(list + e);
+      *reinterpret_cast<u32x4*>(out + e) = *reinterpret_cast<const DSA_LDS u32x4*>(obuf + e);
   } else {
-    for (int e = lane; e < k; e += kWave) out[e] = static_cast<int32_t>(list[e]);
+    for (int e = lane; e < k; e += kWave) out[e] = static_cast<int32_t>(obuf[e]);
   }
 }
 
-// F8: the FP8 indexer (E4M3 operands with power-of-two row scales, v_mfma_scale_f32_32x32x64_f8f6f4);
-// otherwise BF16 operands on v_mfma_f32_32x32x16_bf16. Everything after the scores is shared.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// F8: the FP8 indexer (E4M3 operands with power-of-two row scales, v_mfma_scale_f32_32x32x64_f8f6f4
+// on 32-key tiles); otherwise BF16 operands on v_mfma_f32_16x16x32_bf16 with 16-key tiles.
+// Everything after the scores is shared.
 template <int H_I, int D_I, bool F8>
 __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a) {
-  constexpr int MT = (H_I + 31) / 32;   // 32-row M tiles of indexer heads
-  constexpr int KS = F8 ? D_I / 64 : D_I / 16;  // MFMA K steps
-  constexpr int GPR = F8 ? D_I / 16 : D_I / 8;  // 16-byte granules per key row
+  constexpr int TK = F8 ? 32 : 16;               // keys per MFMA N tile
+  constexpr int NT = kChunk / TK;                // tiles per chunk
+  constexpr int NTH = NT / 2;                    // tiles per 64-key half (one score per lane)
+  constexpr int MT = F8 ? (H_I + 31) / 32 : (H_I + 15) / 16;  // M tiles of indexer heads
+  constexpr int KS = F8 ? D_I / 64 : D_I / 32;   // MFMA K steps
+  constexpr int NMF = MT * KS;                   // MFMAs per tile
+  constexpr int EL = F8 ? 16 : 4;                // accumulator elements per lane of one M tile
+  constexpr int GPR = F8 ? D_I / 16 : D_I / 8;   // 16-byte granules per key row
   constexpr int CHUNK_GRAN = kChunk * GPR;
   constexpr int CPW = CHUNK_GRAN / (kIdxRows * kWave);  // wave copies (1 KB operand blocks) per chunk and wave
-  // a 32-key tile's K step is one 1 KB block (BF16: 16 bytes per lane) or two (FP8: 32 bytes per lane)
-  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && (F8 ? 4 : 2) * KS * kWave == CHUNK_GRAN, "chunk copy split");
+  constexpr int TILE_BYTES = (F8 ? 2 : 1) * KS * 1024;  // one tile's operand blocks
+  constexpr int STAGE_BYTES = NT * TILE_BYTES;           // one staged chunk
+  // The ring holds two staged chunks; after the last chunk it holds each wave's k output indices.
+  constexpr int RING_BYTES = 2 * STAGE_BYTES > kIdxRows * kIdxMaxTopk * 4 ? 2 * STAGE_BYTES : kIdxRows * kIdxMaxTopk * 4;
+  // a tile's K step is one 1 KB block (BF16: 16 bytes per lane) or two (FP8: 32 bytes per lane)
+  static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && STAGE_BYTES == 16 * CHUNK_GRAN, "chunk copy split");
+  static_assert(CPW <= (F8 ? KS : NMF), "a chunk's copies fit beside the MFMAs of one tile");
+  static_assert(NTH == 2 || NTH == 4, "a half chunk is joined from two or four tiles");
   using QOp = typename std::conditional<F8, i32x8, bf16x8>::type;
+  using Acc = typename std::conditional<F8, f32x16, f32x4>::type;
 
-  __shared__ __attribute__((aligned(256))) uint16_t stage[2][kChunk * D_I];
-  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kIdxRows * kListSlots];  // candidate score keys (token indices: global)
-  __shared__ uint32_t s_hist[3 * 256];
+  __shared__ __attribute__((aligned(256))) uint8_t s_ring[RING_BYTES];
+  __shared__ uint32_t s_hist[kIdxRows * 256];  // the workgroup selection's three histograms; at the end one per wave
   // Candidate count of a row whose list must be compacted, else 0. Step c reads buffer c % 2 after
   // its barrier while appends of that step write buffer (c + 1) % 2, so no wave can see a flag
   // that another wave of the same step has not seen.
   __shared__ __attribute__((aligned(16))) int s_need[2][kIdxRows];
-  __shared__ int s_lbase[kIdxRows];               // first LDS slot of each wave's list
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
-  __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][MT * 32];  // head weights of each row (0 past H_I)
+  constexpr int WROW = ((H_I + 31) / 32) * 32;
+  __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][WROW];  // head weights of each row (0 past H_I)
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the row slot of this wave
   const int lane = threadIdx.x % kWave;
@@ -529,28 +552,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   const int b = a.seg_b[sg];
   const bool select = has_row;
   int32_t* out = a.topk_idx + static_cast<int64_t>(r) * k;
-  // The lists of waves w and w + 4 share 2 * kListSlots slots; kCap each, unless a paired long row
-  // has more keys than that and its short partner fits in kCapShort.
-  const int pair_base = 2 * (wave & 3) * kListSlots;
-  int lbase = pair_base + (wave >> 2) * kListSlots, cap = kCap;
-  if (a.paired) {
-    const int h = (m + 1) >> 1, p = 4 * blk + (wave & 3);
-    const int n_long = p < h ? a.row0 + A + (m - 1 - p) - b + 1 : 0;
-    const int n_short = p < m - h ? a.row0 + A + p - b + 1 : 0;
-    if (n_long > kCap && n_short <= kCapShort) {
-      lbase = wave < 4 ? pair_base : pair_base + kCapLong + 64;
-      cap = wave < 4 ? kCapLong : kCapShort;
-    }
-  }
   if (lane == 0) {
     s_need[0][wave] = 0;
     s_need[1][wave] = 0;
-    s_lbase[wave] = lbase;
   }
-  // Claim a candidate slot for the workgroup's lists of token indices. At most n_slots workgroups
-  // are resident at once (the host checks this before the launch) and each frees its slot before
-  // it ends, so a free slot always exists; the search is still bounded, and a workgroup that finds
-  // none writes -1 rows instead of touching memory it does not own.
+  // Claim a candidate slot for the workgroup's lists. At most n_slots workgroups are resident at
+  // once (the host checks this before the launch) and each frees its slot before it ends, so a
+  // free slot always exists; the search is still bounded, and a workgroup that finds none writes
+  // -1 rows instead of touching memory it does not own.
   __shared__ int s_slot;
   if (threadIdx.x == 0) {
     int got = -1;
@@ -570,15 +579,16 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   }
   const int kb = b, ke = a.row0 + A + i_top + 1;
 
-  // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in AGPRs, which
-  // the MFMAs read directly. Head weights go to LDS, read back by the score epilogue.
-  // FP8: 32 bytes per lane and K step, K values 64*s + 32*(lane/32) .. +32 of its head (the key
-  // operand takes the same K values, so the pairing does not depend on the instruction's K order);
-  // the head's scale goes into its weight.
+  // Query operand (A): rows = heads (zero beyond H_I), K = indexer dims; kept in registers, which
+  // the MFMAs read directly. Head weights go to LDS, read back into registers for the epilogue.
+  // BF16: M tile mt holds heads 16*mt + lane%16, K values 32*s + 8*(lane/16) .. +8.
+  // FP8: 32 bytes per lane and K step, K values 64*s + 32*(lane/32) .. +32 of head 32*mt + lane%32
+  // (the key operand takes the same K values, so the pairing does not depend on the instruction's
+  // K order); the head's scale goes into its weight.
   QOp qa[MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int head = 32 * mt + (lane & 31);
+    const int head = F8 ? 32 * mt + (lane & 31) : 16 * mt + (lane & 15);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (select && head < H_I) {
@@ -587,19 +597,23 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
           const i32x4 lo = *reinterpret_cast<const i32x4*>(src), hi = *reinterpret_cast<const i32x4*>(src + 16);
           qa[mt][s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         } else {
-          qa[mt][s] = *reinterpret_cast<const bf16x8*>(a.q_I + (static_cast<int64_t>(r) * H_I + head) * D_I + 16 * s + 8 * (lane >> 5));
+          qa[mt][s] = *reinterpret_cast<const bf16x8*>(a.q_I + (static_cast<int64_t>(r) * H_I + head) * D_I + 32 * s + 8 * (lane >> 4));
         }
       } else {
         qa[mt][s] = QOp{};
       }
     }
-    if (lane < 32) {
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int g = 0; g < WROW / 32; ++g) {
+      const int head = 32 * g + lane;
       float wv = 0.0f;
       if (select && head < H_I) {
         wv = bf16_to_f32(a.w[static_cast<int64_t>(r) * H_I + head]);
         if constexpr (F8) wv *= a.sq[static_cast<int64_t>(r) * H_I + head];  // a power of two: exact
       }
-      s_w[wave][32 * mt + lane] = wv;
+      s_w[wave][head] = wv;
     }
   }
 #pragma unroll
@@ -607,11 +621,15 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qa[mt][s]));
 
-  // LDS-typed pointers, so that every access is a ds_ instruction; candidate indices in global memory
-  DSA_LDS uint32_t* keys = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[lbase])));
+  // LDS-typed pointers, so that every access is a ds_ instruction
   DSA_LDS uint32_t* hist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_hist[0])));
   DSA_LDS uint32_t* sel_scratch = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_sel[0])));
-  int32_t* cand = a.cand + (static_cast<int64_t>(slot) * kIdxRows + wave) * kCandStride;
+  // Row rw's list in the claimed slot: kCandStride score keys, then kCandStride token indices.
+  auto list_keys = [&](int rw) -> uint32_t* {
+    return reinterpret_cast<uint32_t*>(a.cand) + (static_cast<int64_t>(slot) * kIdxRows + rw) * 2 * kCandStride;
+  };
+  uint32_t* ckeys = list_keys(wave);
+  int32_t* cidx = reinterpret_cast<int32_t*>(ckeys + kCandStride);
   int cnt = 0;
   uint32_t thr = 0u;
 
@@ -620,10 +638,10 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     for (int rw = 0; rw < kIdxRows; ++rw) {
       const int c_rw = s_need[nbuf][rw];
       if (c_rw == 0) continue;  // uniform: every wave reads the same flag
-      DSA_LDS uint32_t* kr = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(&s_keys[s_lbase[rw]])));
-      int32_t* cr = a.cand + (static_cast<int64_t>(slot) * kIdxRows + rw) * kCandStride;
+      uint32_t* kr = list_keys(rw);
       int kept = 0;
-      const uint32_t th = wg_select_topk<kIdxRows>(kr, cr, hist, sel_scratch, c_rw, k, slack, &kept);
+      const uint32_t th = wg_select_topk<kIdxRows>(kr, reinterpret_cast<int32_t*>(kr + kCandStride), hist, sel_scratch,
+                                                   c_rw, k, slack, &kept);
       if (rw == wave) {
         cnt = kept;
         thr = th;
@@ -636,13 +654,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   const int nchunks = (ke - kb + kChunk - 1) / kChunk;
   const uint16_t* __restrict__ LNk = a.LNk;
 
-  // A staged chunk is laid out by MFMA operand: block n*KS + s (1 KB) holds, at lane i's 16 bytes,
-  // granule 2s + i/32 of key 32n + i%32, i.e. the B operand of K step s of 32-key tile n. Operand
-  // reads are then whole 1 KB blocks at constant offsets (bank-conflict free) and every copy fills
-  // one block. Copy j of this wave fills block CPW*wave + j; its per-lane source offset within a
-  // chunk is fixed, the chunk's first key row a scalar base.
-  // FP8: block (n, s, h) = 4 * ... holds, at lane i's 16 bytes, half h of lane i's 32-byte operand of
-  // K step s of tile n: key 32n + i%32, K bytes 64s + 32(i/32) + 16h .. +16.
+  // A staged chunk is laid out by MFMA operand, one 1 KB block per copy, each copy with a per-lane
+  // source offset fixed for the kernel and the chunk's first key row as a scalar base. Operand
+  // reads are then whole 1 KB blocks at constant offsets (bank-conflict free).
+  // BF16: block n*KS + s holds, at lane i's 16 bytes, dims 32s + 8(i/16) .. +8 of key 16n + i%16:
+  // the B operand of K step s of 16-key tile n.
+  // FP8: block (n, s, h) = 4n + 2s + h holds, at lane i's 16 bytes, half h of lane i's 32-byte
+  // operand of K step s of 32-key tile n: key 32n + i%32, K bytes 64s + 32(i/32) + 16h .. +16.
+  // Copy j of this wave fills block CPW*wave + j.
   uint32_t cp_off[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
@@ -652,89 +671,89 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       cp_off[j] = static_cast<uint32_t>((32 * n + (lane & 31)) * D_I + 64 * st + 32 * (lane >> 5) + 16 * hf);
     } else {
       const int n = blk_j / KS, st = blk_j % KS;
-      cp_off[j] = static_cast<uint32_t>(((32 * n + (lane & 31)) * D_I + 8 * (2 * st + (lane >> 5))) * 2);
+      cp_off[j] = static_cast<uint32_t>(((16 * n + (lane & 15)) * D_I + 32 * st + 8 * (lane >> 4)) * 2);
     }
   }
-  // A chunk may reach past the last key row (up to two chunks past it, see kIdxKeyPad): those rows
-  // of the padded LNk are staged but never scored.
+  const uint32_t ring = lds_addr_of(&s_ring[0]);
+  // The last chunk may reach up to 127 rows past the last key row (see kIdxKeyPad): those rows of
+  // the padded LNk are staged but never scored. A copy for the chunk after the last one refills the
+  // free slot with the last chunk instead, which nothing reads.
   auto issue_copy = [&](int c, int j) {
-    const int K0 = kb + c * kChunk;
-    const uint32_t lds = lds_addr_of(stage[c & 1]) + 1024 * (CPW * wave + j);
+    const int K0 = kb + min(c, nchunks - 1) * kChunk;
+    const uint32_t lds = ring + (c & 1) * STAGE_BYTES + 1024 * (CPW * wave + j);
     if constexpr (F8) copy16_to_lds_imm<0>(a.LNk8 + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
     else copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
   };
-  auto issue_chunk = [&](int c) {
+  // Scores of a chunk come from NT tiles of TK keys (K = d_I), into accA and accB in turn. The loop
+  // is software pipelined by one tile: the MFMAs of one tile run interleaved with the VALU
+  // epilogue of the tile before it (ReLU, head weight, partial head sums), so the matrix core and
+  // the vector ALU work at the same time.
+  Acc accA[MT], accB[MT];
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) issue_copy(c, j);
-  };
-  // Scores of a chunk come from two 32-key N tiles (K = d_I): tile 0 into accA, tile 1 into accB.
-  // The loop is software pipelined by half a chunk: the MFMAs of one tile run interleaved with
-  // the VALU epilogue of the tile before it (ReLU, head weight, partial head sums), so the matrix
-  // core and the vector ALU work at the same time. Step c runs tile 0 of chunk c beside the
-  // epilogue of tile 1 of chunk c-1, then tile 1 of chunk c beside the epilogue of tile 0 of
-  // chunk c and the append of chunk c-1.
-  f32x16 accA[MT], accB[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) accB[mt] = f32x16{};  // the epilogue of "chunk -1" adds nothing
-  // Head weights in registers: element 4*g + e of an accumulator tile mt holds head
-  // 32*mt + 8*g + 4*(lane/32) + e.
-  f32x4 w4[MT][4];
+  for (int mt = 0; mt < MT; ++mt) accB[mt] = Acc{};  // the epilogue of "chunk -1" adds nothing
+  // Head weights in registers, in accumulator order: element 4*g + e of M tile mt holds head
+  // 32*mt + 8*g + 4*(lane/32) + e (FP8, 32x32 tiles) or 16*mt + 4*(lane/16) + e (BF16, 16x16).
+  f32x4 w4[MT][EL / 4];
   {
     const DSA_LDS float* wrow = reinterpret_cast<const DSA_LDS float*>(lds_ptr(lds_addr_of(&s_w[wave][0])));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) w4[mt][g] = *reinterpret_cast<const DSA_LDS f32x4*>(wrow + 32 * mt + 8 * g + 4 * (lane >> 5));
+      for (int g = 0; g < EL / 4; ++g)
+        w4[mt][g] = *reinterpret_cast<const DSA_LDS f32x4*>(
+            wrow + (F8 ? 32 * mt + 8 * g + 4 * (lane >> 5) : 16 * mt + 4 * (lane >> 4)));
   }
-  constexpr int kEl = MT * 16;        // accumulator elements per lane of one N tile
-  constexpr int kEps = kEl / KS;      // epilogue elements per K step
-  static_assert(kEl % KS == 0 && kEps >= 1 && kEps <= (F8 ? 16 : 8), "epilogue split");
-  constexpr int kPf = KS < 2 ? KS : 2;  // key operands are read kPf K steps ahead of their MFMAs
-  // One N tile of chunk c into acc, interleaved with the epilogue of `prev`; returns this lane's
-  // partial sum over its heads of the previous tile (one key column per lane).
-  auto tile_step = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
-    // the operand of K step s of tile n: block n*KS + s of the staged chunk, 16 bytes per lane
-    uint32_t a0 = lds_addr_of(stage[c & 1]) + n * (KS * 1024) + 16 * lane;
+  auto epi = [&](const Acc (&prev)[MT], int el, float p) -> float {
+    const int mt = el / EL, i = el % EL;
+    return __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), p);
+  };
+  // BF16: one 16-key tile n of chunk c. The K steps of each M tile run as one same-accumulator
+  // chain, each MFMA beside its share of the epilogue of `prev`. The tile's key operands were read
+  // by the tile before it (tile 0 reads its own after the chunk's barrier); this tile reads the
+  // next tile's while its MFMAs run. Returns this lane's partial head sum of the previous tile.
+  bf16x8 bkr[2][KS];
+  auto tile16 = [&](int c, auto nn, Acc (&acc)[MT], const Acc (&prev)[MT], auto&& side) -> float {
+    constexpr int n = decltype(nn)::value;
+    constexpr int EPM = MT * EL / NMF;  // epilogue elements per MFMA
+    static_assert(EPM * NMF == MT * EL && EPM >= 1, "epilogue split");
+    constexpr int PF_M = MT >= 2 ? MT - 2 : 0;  // the M tile beside whose MFMAs the next tile's operands are read
+    bf16x8 (&bk)[KS] = bkr[n & 1];
+    bf16x8 (&bn)[KS] = bkr[(n + 1) & 1];
+    uint32_t a0 = ring + (c & 1) * STAGE_BYTES + n * TILE_BYTES + 16 * lane;
     asm volatile("" : "+v"(a0));
-    bf16x8 bk[kPf];
+    if constexpr (n == 0) {
 #pragma unroll
-    for (int s = 0; s < kPf; ++s) bk[s] = lds_read16(lds_ptr(a0 + 1024 * s));
-    float part[kEps];
-#pragma unroll
-    for (int j = 0; j < kEps; ++j) part[j] = 0.0f;
+      for (int s = 0; s < KS; ++s) bk[s] = lds_read16(lds_ptr(a0 + 1024 * s));
+    }
+    float part[2] = {0.0f, 0.0f};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if constexpr (!F8) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][s], bk[s % kPf], s == 0 ? f32x16{} : acc[mt], 0, 0, 0);
+      for (int s = 0; s < KS; ++s) {
+        const int j = mt * KS + s;
+        if constexpr (!F8) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], s == 0 ? Acc{} : acc[mt], 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < kEps; ++j) {
-        const int el = s * kEps + j, mt = el / 16, i = el % 16;
-        part[j] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j]);
+        for (int e = 0; e < EPM; ++e) part[e & 1] = epi(prev, j * EPM + e, part[e & 1]);
+        asm volatile("" : "+v"(part[0]), "+v"(part[1]));
+        const bool rd = n + 1 < NT && mt == PF_M;
+        if (rd) bn[s] = lds_read16(lds_ptr(a0 + TILE_BYTES + 1024 * s));
+        side(j);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * EPM, 0);
+        if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (j < CPW) __builtin_amdgcn_sched_barrier(0);
       }
-      // keep this step's share of the epilogue in this step (IR passes would sink it below the MFMAs)
-#pragma unroll
-      for (int j = 0; j < kEps; ++j) asm volatile("" : "+v"(part[j]));
-      if (s + kPf < KS) bk[s % kPf] = lds_read16(lds_ptr(a0 + 1024 * (s + kPf)));
-      side(s);  // branch-free work of the caller, scheduled beside this step's MFMAs
-      // one MFMA, then half of the epilogue, the other MFMA(s), the other half, the next read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kEps, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MT - 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kEps + 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    float p = part[0];
-#pragma unroll
-    for (int j = 1; j < kEps; ++j) p += part[j];
-    return p;
+    __builtin_amdgcn_sched_barrier(0);
+    return part[0] + part[1];
   };
-  // The FP8 form of tile_step: the tile's two K steps read as four 1 KB blocks at once, each K step
-  // one 32x32x64 MFMA per M tile beside its half of the epilogue (kept in four partial sums).
-  auto tile_step8 = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
-    uint32_t a0 = lds_addr_of(stage[c & 1]) + n * (2 * KS * 1024) + 16 * lane;
+  // FP8: one 32-key tile n of chunk c; its two K steps read as four 1 KB blocks at once, each K
+  // step one 32x32x64 MFMA per M tile beside its half of the epilogue (kept in four partial sums).
+  auto tile_step8 = [&](int c, auto nn, Acc (&acc)[MT], const Acc (&prev)[MT], auto&& side) -> float {
+    constexpr int n = decltype(nn)::value;
+    constexpr int kEps = MT * EL / KS;  // epilogue elements per K step
+    uint32_t a0 = ring + (c & 1) * STAGE_BYTES + n * TILE_BYTES + 16 * lane;
     asm volatile("" : "+v"(a0));
     i32x8 bk[KS];
 #pragma unroll
@@ -752,13 +771,10 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     for (int s = 0; s < KS; ++s) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (F8) acc[mt] = mfma32_fp8(qa[mt][s], bk[s], s == 0 ? f32x16{} : acc[mt]);
+        if constexpr (F8) acc[mt] = mfma32_fp8(qa[mt][s], bk[s], s == 0 ? Acc{} : acc[mt]);
       }
 #pragma unroll
-      for (int j = 0; j < kEps; ++j) {
-        const int el = s * kEps + j, mt = el / 16, i = el % 16;
-        part[j % NP] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j % NP]);
-      }
+      for (int j = 0; j < kEps; ++j) part[j % NP] = epi(prev, s * kEps + j, part[j % NP]);
 #pragma unroll
       for (int j = 0; j < NP; ++j) asm volatile("" : "+v"(part[j]));
       side(s);
@@ -770,78 +786,104 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     }
     return (part[0] + part[1]) + (part[2] + part[3]);
   };
-  // The epilogue of `prev` alone (a row's last chunk, or a wave whose row has ended).
-  auto tile_drain = [&](const f32x16 (&prev)[MT]) -> float {
-    float part[kEps];
+  // The epilogue of `prev` alone (a row's last chunk, or a wave whose row has ended), summed in
+  // exactly the order of the tile functions above, so that equal keys get bit-identical scores
+  // wherever they fall.
+  auto tile_drain = [&](const Acc (&prev)[MT]) -> float {
+    if constexpr (F8) {
+      constexpr int kEps = MT * EL / KS;
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < kEps; ++j) part[j] = 0.0f;
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+        for (int j = 0; j < kEps; ++j) part[j % 4] = epi(prev, s * kEps + j, part[j % 4]);
+      return (part[0] + part[1]) + (part[2] + part[3]);
+    } else {
+      constexpr int EPM = MT * EL / NMF;
+      float part[2] = {0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < kEps; ++j) {
-        const int el = s * kEps + j, mt = el / 16, i = el % 16;
-        part[j] = __builtin_fmaf(w4[mt][i / 4][i % 4], relu(prev[mt][i]), part[j]);
-      }
-    float p = part[0];
+      for (int j = 0; j < NMF; ++j)
 #pragma unroll
-    for (int j = 1; j < kEps; ++j) p += part[j];
-    return p;
+        for (int e = 0; e < EPM; ++e) part[e & 1] = epi(prev, j * EPM + e, part[e & 1]);
+      return part[0] + part[1];
+    }
   };
-  // lanes < 32 hold key lane of tile 0 in p0 and of tile 1 in p1 (heads with lane/32 = 0), lanes
-  // >= 32 the other heads: one swap leaves lane l with the full score of key l of the chunk
-  auto join = [](float p0, float p1) -> float {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  // One score per lane for the 64 keys of a half chunk, from the partial head sums of its tiles.
+  // FP8 (two 32-key tiles): lanes < 32 hold key lane of tile 0 in p[0] and of tile 1 in p[1]
+  // (heads with lane/32 = 0), lanes >= 32 the other heads; one permlane32 swap leaves lane l with
+  // the full score of key l. BF16 (four 16-key tiles): lane l holds key l%16 of each tile for
+  // head group l/16; two permlane32 swaps add groups g and g + 2, one permlane16 swap adds the
+  // rest, again leaving lane l with key l.
+  auto join = [](const float (&p)[NTH]) -> float {
+    auto sum_swap32 = [](float x, float y) -> float {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+      return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+    if constexpr (NTH == 2) {
+      return sum_swap32(p[0], p[1]);
+    } else {
+      const float x = sum_swap32(p[0], p[2]), y = sum_swap32(p[1], p[3]);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+      return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
   };
-  // Append the keys of chunk c that reach the threshold: keys to LDS, token indices to global, in
-  // ascending token order. Branch-free, so that it can sit between MFMAs: lanes that do not take
-  // their key write it to a slot past the list. A list that may not take another chunk while the
-  // row still has keys in chunk c + 1 raises its flag for the next step.
-  auto append = [&](int c, float score, int nbuf) {
-    const int s_key = kb + c * kChunk + lane;
+  // Append the keys of half chunk u (keys kb + 64u ..) that reach the threshold: keys and token
+  // indices to the row's list, in ascending token order. Branch-free, so that it can sit between
+  // MFMAs: lanes that do not take their key write it to a slot past the list. A list that may not
+  // take another chunk while the row still has keys after half u raises its flag for the next step.
+  auto append = [&](int u, float score, int nbuf) {
+    const int s_key = kb + u * kHalf + lane;
     const uint32_t key = score_key(score);
     const bool take = select && s_key >= b && s_key <= t && key >= thr;
     const uint64_t msk = ballot(take);
-    const int pos = take ? cnt + lanes_below(msk) : cap + lane;
-    keys[pos] = key;
-    cand[pos] = s_key;
+    const int pos = take ? cnt + lanes_below(msk) : kCap + lane;
+    ckeys[pos] = key;
+    cidx[pos] = s_key;
     cnt += __popcll(msk);
-    const bool more = kb + (c + 1) * kChunk <= t;
-    s_need[nbuf][wave] = cnt > cap - kChunk && more ? cnt : 0;  // every lane writes the same value
+    const bool more = kb + (u + 1) * kHalf <= t;
+    s_need[nbuf][wave] = cnt > kCap - kChunk && more ? cnt : 0;  // every lane writes the same value
   };
 
-  auto tile = [&](int c, int n, f32x16 (&acc)[MT], const f32x16 (&prev)[MT], auto&& side) -> float {
-    if constexpr (F8) return tile_step8(c, n, acc, prev, side);
-    else return tile_step(c, n, acc, prev, side);
+  auto tile = [&](int c, auto nn, Acc (&acc)[MT], const Acc (&prev)[MT], auto&& side) -> float {
+    if constexpr (F8) return tile_step8(c, nn, acc, prev, side);
+    else return tile16(c, nn, acc, prev, side);
   };
-  float p0_prev = 0.0f;  // tile-0 partial sums of the previous chunk
-  // FP8: the key scales of the previous chunk (lane l: key l), loaded a step before they are used
+  float ph_prev[NTH];  // partial sums of the previous chunk's second-half tiles (the last one unused)
+#pragma unroll
+  for (int i = 0; i < NTH; ++i) ph_prev[i] = 0.0f;
+  // FP8: the key scales of the previous chunk's second half (lane l: key 64 + l), loaded a step
+  // before they are used
   float sk_prev = 1.0f;
-  issue_chunk(0);
-  // Step c: tile 0 of chunk c (the next chunk's copies issued between its MFMAs), then the
-  // selections that the lists filled by step c-1 asked for, then tile 1 of chunk c with the append
-  // of chunk c-1 between its MFMAs. Step nchunks runs no MFMAs: it only finishes the last chunk.
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) issue_copy(0, j);
+  // Step c: tile 0 of chunk c (the next chunk's copies issued between its MFMAs); the selections
+  // that the lists filled by step c-1 asked for; the other tiles, with the append of the second
+  // half of chunk c-1 beside tile 1 and that of the first half of chunk c beside tile NTH + 1.
+  // Step nchunks runs no MFMAs: it only finishes the last chunk.
   for (int c = 0; c <= nchunks; ++c) {
-    wait_vmem();    // this wave's copies of chunk c and its index stores are complete
+    wait_vmem();    // this wave's copies of chunk c and its list stores are complete
     barrier_lds();  // chunk c has landed; the slot of chunk c-1 is free
     // flags of the lists that step c-1 filled: read now, used after tile 0
     const i32x4 f0 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][0])));
     const i32x4 f1 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][4])));
-    const bool act = select && c < nchunks && kb + c * kChunk <= t;      // row still has keys in chunk c
-    const bool act_prev = select && c > 0 && kb + (c - 1) * kChunk <= t;  // chunk c-1 still to finish
-    // copies of chunk c+1 (at c+1 == nchunks they fill a free slot with clamped rows, unused)
-    auto copies = [&](int st) {
-      if (st < CPW) issue_copy(c + 1, st);
-    };
-    float sk_cur = 1.0f;
+    const bool act = select && c < nchunks && kb + c * kChunk <= t;                 // row has keys in chunk c
+    const bool act_prev = select && c > 0 && kb + (c - 1) * kChunk + kHalf <= t;  // and in the second half of chunk c-1
+    float sk_lo = 1.0f, sk_hi = 1.0f;
     if constexpr (F8) {
-      if (c < nchunks) sk_cur = a.sk[kb + c * kChunk + lane];  // within the padded key rows
+      if (c < nchunks) {  // within the padded key rows
+        sk_lo = a.sk[kb + c * kChunk + lane];
+        sk_hi = a.sk[kb + c * kChunk + kHalf + lane];
+      }
     }
-    float score_prev = 0.0f;
+    float score_hi = 0.0f;  // scores of the second half of chunk c-1
     if (act) {
       // a wave whose row ends before this chunk leaves its SIMD to the other wave there
-      score_prev = join(p0_prev, tile(c, 0, accA, accB, copies));
-      if constexpr (F8) score_prev *= sk_prev;  // a power of two: exact
+      auto copies = [&](int st) {
+        if (st < CPW) issue_copy(c + 1, st);
+      };
+      ph_prev[NTH - 1] = tile(c, std::integral_constant<int, 0>{}, accA, accB, copies);
+      score_hi = join(ph_prev);
+      if constexpr (F8) score_hi *= sk_prev;  // a power of two: exact
     } else if (c + 1 < nchunks) {
 #pragma unroll
       for (int j = 0; j < CPW; ++j) issue_copy(c + 1, j);
@@ -849,31 +891,52 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     if ((f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0)
       run_selections(kSelSlack, c & 1);  // uniform, rare
     if (act) {
-      auto app = [&](int st) {
-        if (st == 0) append(c - 1, score_prev, (c + 1) & 1);  // early, so its index stores land before the next step's wait
-      };
-      p0_prev = tile(c, 1, accB, accA, app);
+      float pc[NT];  // pc[i]: partial sums of tile i of chunk c
+      float score_lo = 0.0f;
+      static_for<1, NT>([&](auto nn) {
+        constexpr int n = decltype(nn)::value;
+        auto side = [&](int st) {
+          // early in the tile, so that the list stores land before the next step's wait
+          if constexpr (n == 1) {
+            if (st == 0) append(2 * c - 1, score_hi, (c + 1) & 1);
+          } else if constexpr (n == NTH + 1) {
+            if (st == 0) append(2 * c, score_lo, (c + 1) & 1);
+          }
+        };
+        if constexpr (n % 2 == 0) pc[n - 1] = tile(c, nn, accA, accB, side);
+        else pc[n - 1] = tile(c, nn, accB, accA, side);
+        if constexpr (n == NTH) {
+          float lo[NTH];
+#pragma unroll
+          for (int i = 0; i < NTH; ++i) lo[i] = pc[i];
+          score_lo = join(lo);
+          if constexpr (F8) score_lo *= sk_lo;
+        }
+      });
+#pragma unroll
+      for (int i = 0; i + 1 < NTH; ++i) ph_prev[i] = pc[NTH + i];
     } else if (act_prev) {
-      float sc = join(p0_prev, tile_drain(accB));
+      ph_prev[NTH - 1] = tile_drain(accB);  // the last tile of chunk c-1 (odd: accB)
+      float sc = join(ph_prev);
       if constexpr (F8) sc *= sk_prev;
-      append(c - 1, sc, (c + 1) & 1);
+      append(2 * c - 1, sc, (c + 1) & 1);
     }
-    sk_prev = sk_cur;
+    sk_prev = sk_hi;
   }
 
-  // Final exact selection: each wave finishes its own row, with a histogram in the staging ring,
-  // which no wave uses any more.
-  wait_vmem();    // this wave's candidate index stores are complete
+  // Final exact selection: each wave finishes its own row, with its histogram in s_hist and its
+  // output indices in the staging ring, which no wave uses any more.
+  wait_vmem();    // this wave's list stores are complete
   barrier_lds();  // every wave is done with the staging ring
   if (select) {
     if (cnt > k) {
-      DSA_LDS uint32_t* whist = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(lds_addr_of(stage[0]) + 1024 * wave));
-      wave_select_out(keys, cand, whist, cnt, k, out);
+      DSA_LDS uint32_t* obuf = reinterpret_cast<DSA_LDS uint32_t*>(lds_ptr(ring + wave * kIdxMaxTopk * 4));
+      wave_select_out(ckeys, cidx, hist + 256 * wave, obuf, cnt, k, out);
     } else {  // exactly k candidates
-      for (int j = lane; j < k; j += kWave) out[j] = cand[j];
+      for (int j = lane; j < k; j += kWave) out[j] = cidx[j];
     }
   }
-  // Free the slot once every wave's reads of its token indices have completed.
+  // Free the slot once every wave's reads of its list have completed.
   wait_vmem();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -883,8 +946,6 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-static_assert(kIdxSlotWords == kIdxRows * kCandStride, "slot size");
-
 int index_blocks(int m, int paired) { return paired ? ((m + 1) / 2 + 3) / 4 : (m + kIdxRows - 1) / kIdxRows; }
 
 // Workgroups of the indexer kernel that the current device can hold at once (CUs x occupancy),

@@ -49,7 +49,7 @@ def test_supported_shapes_and_workspace():
     # and q_I, one float scale per 128-value row), and the latent output of one row chunk (rows x H x
     # 512 bf16, at most 2,048 rows); each region starts 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
-    flags, slots = 1024, 256 * 8 * 4160 * 4
+    flags, slots = 1024, 256 * 8 * 2 * 4672 * 4  # per row: 4,672 score keys and 4,672 token indices
 
     def fp8(T, rows, H_I, d_I):
         return al((T + 128) * d_I) + al((T + 128) * 4) + al(rows * H_I * d_I) + al(rows * H_I * 4)

@@ -94,7 +94,7 @@ def _ws_fp8_keys(ws, cfg):
     """The indexer's E4M3 codes and scales of LN(k_I) in the workspace (regions after LNk, the slot
     flags and the candidate slots)."""
     al = lambda v: (v + 255) // 256 * 256
-    off = al((cfg.T + 128) * cfg.d_I * 2) + 1024 + 256 * 8 * 4160 * 4
+    off = al((cfg.T + 128) * cfg.d_I * 2) + 1024 + 256 * 8 * 2 * 4672 * 4
     k8 = ws[off: off + cfg.T * cfg.d_I].cpu().numpy().reshape(cfg.T, cfg.d_I)
     off_s = off + al((cfg.T + 128) * cfg.d_I)
     sk = ws[off_s: off_s + 4 * cfg.T].view(torch.float32).cpu().numpy()
