@@ -34,6 +34,13 @@ KERNEL_SRC = {
     "k_sparse_mla": os.path.join(CSRC, "k_mla.hip"),
     "k_up_gate": os.path.join(CSRC, "k_up.hip"),
 }
+# The rocprofv3 names of the three path kernels as the bench's workloads launch them (BF16 indexer,
+# 96 heads), matched exactly: the backward's k_sparse_mla_bwd and the FP8 indexer instance are other kernels.
+KERNEL_NAME = {
+    "k_index_topk": "k_index_topk<64, 128, false>",
+    "k_sparse_mla": "k_sparse_mla<96>",
+    "k_up_gate": "k_up_gate(",
+}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30         # plain device copy used to scale the HBM byte counters
 D_MODEL = 7168               # hidden size of the model (KimiK3TextConfig), the width of o_proj's output
@@ -97,13 +104,13 @@ def pmc_hbm_path(kernel, workload):
 
 
 def traffic_from_profile(kernel, workload):
-    """HBM bytes per launch of `kernel` on `workload` from its committed counter summary, or None when
-    there is none or the kernel's code has changed since the counters were taken."""
+    """HBM bytes per whole-workload launch of `kernel` on `workload` from its committed counter summary,
+    or None when there is none or the kernel's code has changed since the counters were taken."""
     path = pmc_hbm_path(kernel, workload)
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("kernel") != kernel or d.get("workload") != workload:
+    if d.get("kernel") != kernel or d.get("workload") != workload or d.get("instance") != KERNEL_NAME[kernel]:
         return None
     if d.get("kernel_code_sha256_16") != src_hash(KERNEL_SRC[kernel]):
         return None
@@ -122,47 +129,60 @@ def _counter_rows(d):
     return rows
 
 
-def _per_dispatch_kib(rows, name_part, counter, full_size_only=False):
-    """Per-dispatch values of `counter` (KiB; summed over the counter's instances) for kernels
-    whose name contains name_part. full_size_only keeps the dispatches that run at least half as
-    long as the kernel's longest one: the fused step launches the attention and the up-projection
-    per row chunk, the stage window once over all rows, and only the latter is one launch of the
-    whole workload."""
-    per, dur = {}, {}
+def _dispatches(rows, kernel):
+    """{dispatch id: duration (ns)} of the path kernel `kernel` (its exact instance name)."""
+    return {r["Dispatch_Id"]: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in rows if KERNEL_NAME[kernel] in r["Kernel_Name"]}
+
+
+def _whole_workload(dur):
+    """The dispatches of one kernel that run at least 0.8 times as long as its longest one: the bench's
+    stage window launches each path kernel once over all rows, while the fused step (and the backward's
+    recompute) launch the attention and the up-projection per 2,048-row chunk, at most two thirds of
+    the work of any bench workload (the last chunk at T=4,096)."""
+    longest = max(dur.values())
+    return {d for d, t in dur.items() if t >= 0.8 * longest}
+
+
+def _per_dispatch_kib(rows, kernel, counter):
+    """Values of `counter` (KiB; summed over the counter's instances) of the whole-workload launches of
+    the path kernel `kernel`."""
+    keep = _whole_workload(_dispatches(rows, kernel)) if _dispatches(rows, kernel) else set()
+    per = {}
     for r in rows:
-        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+        if r["Dispatch_Id"] in keep and KERNEL_NAME[kernel] in r["Kernel_Name"] and r["Counter_Name"] == counter:
             per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-    if full_size_only and dur:
-        longest = max(dur.values())
-        return [v for d, v in per.items() if dur[d] >= 0.5 * longest]
     return list(per.values())
 
 
 def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, commands):
-    """HBM bytes per launch of each kernel from FETCH_SIZE / WRITE_SIZE counter runs, each scaled by
-    what the same counter reads for a plain device copy of known size; one summary per kernel."""
+    """HBM bytes per whole-workload launch of each path kernel from FETCH_SIZE / WRITE_SIZE counter
+    runs, each scaled by what the same counter reads for a plain device copy of known size; one
+    summary per kernel."""
     import testgen as tg
     cfg = tg.get_config(workload)
     work = alg_work(cfg)
     cal_bytes = COPY_LAUNCHES * COPY_BYTES  # every copy dispatch of the calibration run together
-    cf_kib = sum(_per_dispatch_kib(_counter_rows(cal_fetch_dir), "copyBuffer", "FETCH_SIZE"))
-    cw_kib = sum(_per_dispatch_kib(_counter_rows(cal_write_dir), "copyBuffer", "WRITE_SIZE"))
+    cal_f, cal_w = _counter_rows(cal_fetch_dir), _counter_rows(cal_write_dir)
+    cf_kib = sum(float(r["Counter_Value"]) for r in cal_f if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == "FETCH_SIZE")
+    cw_kib = sum(float(r["Counter_Value"]) for r in cal_w if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == "WRITE_SIZE")
     f_scale = cal_bytes / (cf_kib * 1024.0)
     w_scale = cal_bytes / (cw_kib * 1024.0)
     frows, wrows = _counter_rows(fetch_dir), _counter_rows(write_dir)
     out = {}
     for kernel in KERNEL_SRC:
-        fv = _per_dispatch_kib(frows, kernel, "FETCH_SIZE", full_size_only=True)
-        wv = _per_dispatch_kib(wrows, kernel, "WRITE_SIZE", full_size_only=True)
+        fv = _per_dispatch_kib(frows, kernel, "FETCH_SIZE")
+        wv = _per_dispatch_kib(wrows, kernel, "WRITE_SIZE")
         if not fv or not wv:
             continue
         f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
         fetch_b, write_b = f_kib * 1024.0 * f_scale, w_kib * 1024.0 * w_scale
         res = {
-            "kernel": kernel, "workload": workload, "kernel_code_sha256_16": src_hash(KERNEL_SRC[kernel]),
+            "kernel": kernel, "instance": KERNEL_NAME[kernel], "workload": workload,
+            "kernel_code_sha256_16": src_hash(KERNEL_SRC[kernel]),
             "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib, "dispatches": [len(fv), len(wv)],
-            "dispatch_rule": "launches over the whole workload only (at least half the longest dispatch)",
+            "dispatch_rule": "the kernel's launches over the whole workload only (at least 0.8 of its longest launch: "
+                             "the bench's stage window; the fused step's row-chunk launches are left out)",
             "copy_calibration": {"bytes_each_way_all_copies": cal_bytes, "fetch_kib": cf_kib, "write_kib": cw_kib,
                                  "fetch_scale": f_scale, "write_scale": w_scale},
             "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
@@ -182,9 +202,9 @@ XCDS = 8
 
 
 def pmc_mfma_summary(mfma_dir, workload, commands):
-    """Per-kernel MFMA counters of a bench run: bf16 MFMA flops the hardware executed
-    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against the algorithmic flops, the rate both give over the
-    dispatch time, and the share of SIMD cycles the matrix cores were busy."""
+    """Per-kernel MFMA counters of the whole-workload launches of a bench run: bf16 MFMA flops the
+    hardware executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) against the algorithmic flops, the rate both
+    give over the dispatch time, and the share of SIMD cycles the matrix cores were busy."""
     import testgen as tg
     rows = _counter_rows(mfma_dir)
     cfg = tg.get_config(workload)
@@ -197,14 +217,14 @@ def pmc_mfma_summary(mfma_dir, workload, commands):
     for name in KERNEL_SRC:
         per = {}
         for r in rows:
-            if name in r["Kernel_Name"]:
+            if KERNEL_NAME[name] in r["Kernel_Name"]:
                 d = per.setdefault(r["Dispatch_Id"], {"t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         ds = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
         if not ds:
             continue
-        longest = max(d["t"] for d in ds)
-        ds = [d for d in ds if d["t"] >= 0.5 * longest]  # whole-workload launches only (see _per_dispatch_kib)
+        keep = _whole_workload({i: int(d["t"] * 1e9) for i, d in enumerate(ds)})
+        ds = [d for i, d in enumerate(ds) if i in keep]
         t = float(np.mean([d["t"] for d in ds]))
         mops = float(np.mean([d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds]))
         busy = float(np.mean([d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds]))
@@ -212,7 +232,7 @@ def pmc_mfma_summary(mfma_dir, workload, commands):
         hw_flop = mops * 512.0
         alg_flop = work[name]
         out["kernels"][name] = {
-            "dispatches": len(ds), "mean_dispatch_us": t * 1e6,
+            "instance": KERNEL_NAME[name], "dispatches": len(ds), "mean_dispatch_us": t * 1e6,
             "hw_bf16_mfma_flop": hw_flop, "alg_flop": alg_flop, "hw_over_alg": hw_flop / alg_flop,
             "hw_tflops": hw_flop / t / 1e12, "alg_tflops": alg_flop / t / 1e12,
             "alg_frac_of_peak": alg_flop / t / 1e12 / PEAK_BF16_TFLOPS,
@@ -246,19 +266,21 @@ def stats_summary(stats_dir, workload, command, bench_log):
     for r in stats:
         lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    lines += ["", "Launches over the whole workload (at least half the kernel's longest launch; the fused step runs the "
-              "attention and the up-projection in row chunks, the bench's stage window once over all rows), against "
-              "the HIP-event stage times of the bench line printed by the same command:", "",
-              "| kernel | launches | trace average (us) | bench, HIP events (us) |", "|---|---|---|---|"]
+    lines += ["", "Launches over the whole workload (at least 0.8 of the kernel's longest launch: the bench's stage "
+              "window launches each path kernel once over all rows, the fused step runs the attention and the "
+              "up-projection per row chunk), against the HIP-event stage times of the bench line printed by the "
+              "same command:", "",
+              "| kernel (instance) | launches | trace average (us) | bench, HIP events (us) |", "|---|---|---|---|"]
     ev = {"k_index_topk": ("index_topk_ms", "key LayerNorm prologue + indexer"), "k_sparse_mla": ("attention_ms", "attention"),
           "k_up_gate": ("up_gate_ms", "up-projection + gate")}
     for k, (field, what) in ev.items():
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace if k in r["Kernel_Name"]]
+        d = {r["Dispatch_Id"]: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+             if KERNEL_NAME[k] in r["Kernel_Name"]}
         if not d:
             continue
-        full = [x for x in d if x >= 0.5 * max(d)]
+        full = [d[i] for i in _whole_workload(d)]
         b = f"{line['stages'][field] * 1e3:.1f} ({what})" if line else "n/a"
-        lines.append(f"| `{k}` | {len(full)} | {np.mean(full):.1f} | {b} |")
+        lines.append(f"| `{KERNEL_NAME[k].rstrip('(')}` | {len(full)} | {np.mean(full):.1f} | {b} |")
     if line:
         st = line["stages"]
         lines += ["", f"Bench line of the same command: {st['value']:.0f} query tokens/s, {st['ms_per_step']:.3f} ms per "

@@ -37,6 +37,8 @@ constexpr int kBwKeys = 16;    // keys per gathered tile
 constexpr int kBwGran = kLatent * 2 / 16;             // 72 granules per latent row
 constexpr int kBwTileBytes = kBwKeys * kBwGran * 16;  // 18 KB
 constexpr int kBwMaxIdx = 2048;
+constexpr int kBwAtomics = kLatent / 16 / kBwWaves * 4;  // dkv atomics per wave and tile
+static_assert(kLatent / 16 % kBwWaves == 0 && kBwAtomics <= 63, "a whole number of dkv column tiles per wave; vmcnt range");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------------------------
@@ -154,20 +156,26 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
   const uint32_t qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // A of S^T / dP^T: key i16, dims 32*st + 8*g16
 
   for (int t = 0; t < ntiles; ++t) {
-    wait_vmem();
-    __syncthreads();  // tile t has landed; every wave is done with tile t - 1 and its P / dS'
+    // Tile t has landed and every wave is done with tile t - 1 and its P / dS'. The wait leaves
+    // out this wave's dkv atomics of tile t - 1, the last kBwAtomics vector-memory operations it
+    // issued (vector-memory operations complete in issue order): they drain while this tile runs.
+    if (t == 0) wait_vmem();
+    else wait_vmem_le<kBwAtomics>();
+    barrier_lds();
     if (t + 1 < ntiles) issue_tile(t + 1);
     const uint32_t tb = ring + (t & 1) * kBwTileBytes;
     // ---- S^T (waves 0, 1) or dP^T (waves 2, 3): 16 keys x 16 heads
+    // 18 K steps in both products (the dP waves' last two fragments are zero), so that the chain
+    // unrolls with constant register indices
     f32x4 acc = f32x4{};
-    const int nst = wave < 2 ? 18 : 16;
-    for (int st = 0; st < nst; ++st) acc = mfma16(lds_read16(lds_ptr(tb + qk_off + 1024 * st)), fr[st], acc);
+#pragma unroll
+    for (int st = 0; st < 18; ++st) acc = mfma16(lds_read16(lds_ptr(tb + qk_off + 1024 * st)), fr[st], acc);
     // lane: head column i16, keys 4*g16 + e
     if (wave >= 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s_dp[wave - 2][(4 * g16 + e) * 16 + i16] = acc[e];
     }
-    __syncthreads();
+    barrier_lds();
     if (wave < 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
         s_dsT[my_h * kBwKeys + key] = db;
       }
     }
-    __syncthreads();
+    barrier_lds();
     // ---- dq^T += K^T dS'^T: M = 32 latent dims, N = 32 heads, K = 16 keys
     const bf16x8 bds = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_dsT) + (lane & 31) * 32 + 16 * hh));
 #pragma unroll
@@ -201,14 +209,19 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
     int keyrow[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) keyrow[e] = s_idx[t * kBwKeys + 4 * g16 + e];
-    for (int n = wave; n < kLatent / 16; n += kBwWaves) {
+    // Every wave issues exactly kBwAtomics atomics per tile: a padding entry adds +0 to row 0.
+    float* dkv_row[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dkv_row[e] = a.dkv + static_cast<int64_t>(max(keyrow[e], 0)) * kLatent;
+#pragma unroll
+    for (int i = 0; i < kLatent / 16 / kBwWaves; ++i) {
+      const int n = wave + kBwWaves * i;
       const int dim = 16 * n + i16;
       f32x4 d = mfma16(a_ds, *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_qT) + dim * 64 + 16 * g16)), f32x4{});
       if (n < kVDim / 16)
         d = mfma16(a_p, *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_dT) + dim * 64 + 16 * g16)), d);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (keyrow[e] >= 0) atomicAdd(a.dkv + static_cast<int64_t>(keyrow[e]) * kLatent + dim, d[e]);
+      for (int e = 0; e < 4; ++e) atomicAdd(dkv_row[e] + dim, keyrow[e] >= 0 ? d[e] : 0.0f);
     }
   }
   // dq of the row: lane holds head (lane % 32), dims 32*dt + 8*(e/4) + 4*hh + e%4
