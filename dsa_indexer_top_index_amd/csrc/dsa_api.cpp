@@ -306,18 +306,26 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 
 // Backward workspace: the forward's layout, then for one row chunk do [rows, H, 128] bf16,
 // do_lat [rows, H, 512] bf16 and D [rows, H] f32 (the o_lat region holds the recomputed o_lat).
+// Backward workspace: the forward's regions (o_lat is recomputed into its region), then per row chunk
+//   do     [chunk rows, H, 128] bf16   sigma(g) dout
+//   do_lat [chunk rows, H, 512] bf16   do W_UV[h]^T
+//   delta  [chunk rows, H] f32         sum dout * out
+//   g      [chunk rows, g_stride, 2H] bf16   dS' and P of every selected key, for the dkv contraction
 struct BwdLayout {
-  size_t do_off, dolat_off, delta_off, total;
+  size_t do_off, dolat_off, delta_off, g_off, total;
+  int g_stride;
 };
 
 static BwdLayout bwd_layout_of(const dsa_shape* s) {
   const Layout L = layout_of(s);
   BwdLayout B{};
   const size_t cr = static_cast<size_t>(L.chunk_rows) * s->H;
+  B.g_stride = (s->topk + 31) / 32 * 32;
   B.do_off = L.total;
   B.dolat_off = B.do_off + align_up(cr * 128 * 2);
   B.delta_off = B.dolat_off + align_up(cr * 512 * 2);
-  B.total = B.delta_off + align_up(cr * 4);
+  B.g_off = B.delta_off + align_up(cr * 4);
+  B.total = B.g_off + align_up(static_cast<size_t>(L.chunk_rows) * B.g_stride * 2 * s->H * 2);
   return B;
 }
 
@@ -349,6 +357,7 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
   uint16_t* d_o = reinterpret_cast<uint16_t*>(base + B.do_off);
   uint16_t* dolat = reinterpret_cast<uint16_t*>(base + B.dolat_off);
   float* delta = reinterpret_cast<float*>(base + B.delta_off);
+  uint16_t* g = reinterpret_cast<uint16_t*>(base + B.g_off);
   if (dsa::launch_fill_zero(dkv, static_cast<int64_t>(s->T) * 576, hs) != hipSuccess ||
       dsa::launch_fill_zero(dW_UV, static_cast<int64_t>(s->H) * 512 * 128, hs) != hipSuccess)
     return DSA_ERR_LAUNCH;
@@ -367,7 +376,8 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
     b.delta = delta;
     b.do_lat = dolat;
     b.dq = dq;
-    b.dkv = dkv;
+    b.g = g;
+    b.g_stride = B.g_stride;
     b.cu = s->n_docs > 1 ? s->cu_seqlens_dev : nullptr;
     b.n_docs = s->n_docs;
     b.T = s->T;
@@ -378,6 +388,9 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
     b.H = s->H;
     b.scale = s->softmax_scale;
     if (dsa::launch_sparse_mla_bwd(b, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::DkvArgs dk{g, q, dolat, topk_idx, dkv, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
+                    B.g_stride};
+    if (dsa::launch_dkv(dk, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     // o_lat of the chunk again (the forward's attention kernel), for dW_UV
     if ((st = launch_attention(s, nullptr, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
     dsa::DwArgs dw{olat, d_o, dW_UV, n, s->H};

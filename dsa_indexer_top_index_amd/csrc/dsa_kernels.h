@@ -113,7 +113,8 @@ struct BwdArgs {
   const float* delta;      // [chunk_rows, H]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
   float* dq;               // [nrows, H, 576]
-  float* dkv;              // [T, 576], added to
+  uint16_t* g;             // [chunk_rows, g_stride, 2H] bf16 per selected key: dS' of the H heads, then P
+  int g_stride;            // keys per row of g: k rounded up to 32
   const int32_t* cu;
   int n_docs;
   int T;
@@ -123,6 +124,23 @@ struct BwdArgs {
   int k;
   int H;                   // a multiple of 32
   float scale;
+};
+
+// dkv[idx[r, j]] += dS'[r, j, :] q[r] + P[r, j, :] do_lat[r] over all H heads, from g.
+struct DkvArgs {
+  const uint16_t* g;       // as BwdArgs::g
+  const uint16_t* q;       // [nrows, H, 576]
+  const uint16_t* do_lat;  // [chunk_rows, H, 512]
+  const int32_t* idx;      // [nrows, k]
+  float* dkv;              // [T, 576], added to
+  const int32_t* cu;
+  int n_docs;
+  int T;
+  int row0;
+  int chunk_r0;
+  int chunk_rows;
+  int k;
+  int g_stride;
 };
 
 struct DwArgs {
@@ -149,6 +167,7 @@ hipError_t launch_gemm_nt(const GemmArgs& a, hipStream_t st);
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_dkv(const DkvArgs& a, hipStream_t st);
 hipError_t launch_dwuv(const DwArgs& a, hipStream_t st);
 
 }  // namespace dsa

@@ -17,11 +17,14 @@
 //     registers; waves 2 and 3 compute dP^T = V do_lat^T (K = 512) with do_lat fragments in registers
 //     and pass it through LDS;
 //   - waves 0 and 1 form P = 2^(scale log2e S - log2e lse) and dS' = scale P (dP - D) and write both
-//     in bf16 in the layouts of the next products;
+//     in bf16 to LDS, from where waves 2 and 3 store them to the workspace (g) for k_dkv;
 //   - all waves: dq^T += K^T dS'^T on 32x32x16 MFMAs (K^T read transposed from the gathered tile,
-//     the latent dims split over the waves, accumulators kept across the row), and the tile's dkv
-//     rows dS' Q + P do_lat on 16x16x32 MFMAs (Q and do_lat held transposed in LDS) added to dkv
-//     with FP32 atomics (16 consecutive dims of 4 keys per instruction).
+//     the latent dims split over the waves, accumulators kept across the row).
+// k_dkv: dkv rows of the selected keys, dS' Q + P do_lat, contracted over all 96 heads at once, so
+//   that each (key, dim) takes one FP32 atomic add per row (not one per head group): one workgroup
+//   per (row, 64 latent dims), Q and do_lat of its dims held in registers as MFMA operands, dS' and P
+//   streamed from g in 32-key tiles. FP32 atomics run at a fixed rate per lane (about 330 G lane
+//   operations per second on MI355X, whatever their scope or placement), which bounds the backward.
 // k_dwuv: dW_UV[h] += o_lat^T do over a chunk of rows, 16 rows per K step staged in LDS in the
 //   forward's tile layout so that both operands are read transposed; partial sums added with atomics.
 #include "dsa_device.h"
@@ -37,8 +40,7 @@ constexpr int kBwKeys = 16;    // keys per gathered tile
 constexpr int kBwGran = kLatent * 2 / 16;             // 72 granules per latent row
 constexpr int kBwTileBytes = kBwKeys * kBwGran * 16;  // 18 KB
 constexpr int kBwMaxIdx = 2048;
-constexpr int kBwAtomics = kLatent / 16 / kBwWaves * 4;  // dkv atomics per wave and tile
-static_assert(kLatent / 16 % kBwWaves == 0 && kBwAtomics <= 63, "a whole number of dkv column tiles per wave; vmcnt range");
+constexpr int kGCols = 2 * 96;  // g: dS' of the 96 heads, then P
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------------------------
@@ -72,10 +74,8 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 }
 
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs a) {
+__global__ __launch_bounds__(kBwWaves * kWave, 2) void k_sparse_mla_bwd(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[2][kBwTileBytes];       // 36 KB
-  __shared__ __attribute__((aligned(16))) uint16_t s_qT[kLatent * kBwHeads];       // Q^T [dim][head], 36 KB
-  __shared__ __attribute__((aligned(16))) uint16_t s_dT[kVDim * kBwHeads];         // do_lat^T [dim][head], 32 KB
   __shared__ __attribute__((aligned(16))) float s_dp[2][kBwKeys * 16];             // dP [key][head] per head tile
   __shared__ __attribute__((aligned(16))) uint16_t s_ds[kBwKeys * kBwHeads];       // dS' [key][head]
   __shared__ __attribute__((aligned(16))) uint16_t s_p[kBwKeys * kBwHeads];        // P [key][head]
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
   const int ntiles = (keff + kBwKeys - 1) / kBwKeys;
   const int h0 = hg * kBwHeads;
 
-  // the row's indices (-1: no usable key), and Q^T and do_lat^T of the head group in LDS
+  // the row's indices (-1: no usable key)
   const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
   for (int j = threadIdx.x; j < ntiles * kBwKeys; j += kBwWaves * kWave) {
     const int v = j < keff ? ix[j] : -1;
@@ -102,18 +102,8 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
   }
   const uint16_t* __restrict__ qrow = a.q + (static_cast<int64_t>(r) * H + h0) * kLatent;
   const uint16_t* __restrict__ drow = a.do_lat + (static_cast<int64_t>(crow) * H + h0) * kVDim;
-  for (int gi = threadIdx.x; gi < kBwHeads * kBwGran; gi += kBwWaves * kWave) {
-    const int h = gi / kBwGran, g = gi % kBwGran;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + h * kLatent + 8 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s_qT[(8 * g + e) * kBwHeads + h] = static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
-  }
-  for (int gi = threadIdx.x; gi < kBwHeads * (kVDim / 8); gi += kBwWaves * kWave) {
-    const int h = gi / (kVDim / 8), g = gi % (kVDim / 8);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(drow + h * kVDim + 8 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s_dT[(8 * g + e) * kBwHeads + h] = static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
-  }
+  // this head group's columns of the row's g rows
+  uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols + h0;
   // Waves 0 and 1: q fragments (B of S^T = K Q^T: head 16*wave + i16, dims 32*st + 8*g16); their
   // heads' lse (log2 units) and D. Waves 2 and 3: do_lat fragments of heads 16*(wave-2) + i16.
   const int my_h = 16 * (wave & 1) + i16;  // head within the group of this lane's score column
@@ -145,7 +135,7 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
     const uint32_t base = ring + (t & 1) * kBwTileBytes;
     for (int c = wave; c < 18; c += kBwWaves) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
   };
-  __syncthreads();  // indices, Q^T, do_lat^T
+  __syncthreads();  // indices
   if (ntiles > 0) issue_tile(0);
 
   // transposed reads of the tile (A = K^T: lane = latent dim, 8 keys), as in the forward's value waves
@@ -156,12 +146,8 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
   const uint32_t qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // A of S^T / dP^T: key i16, dims 32*st + 8*g16
 
   for (int t = 0; t < ntiles; ++t) {
-    // Tile t has landed and every wave is done with tile t - 1 and its P / dS'. The wait leaves
-    // out this wave's dkv atomics of tile t - 1, the last kBwAtomics vector-memory operations it
-    // issued (vector-memory operations complete in issue order): they drain while this tile runs.
-    if (t == 0) wait_vmem();
-    else wait_vmem_le<kBwAtomics>();
-    barrier_lds();
+    wait_vmem();
+    barrier_lds();  // tile t has landed; every wave is done with tile t - 1 and its P / dS'
     if (t + 1 < ntiles) issue_tile(t + 1);
     const uint32_t tb = ring + (t & 1) * kBwTileBytes;
     // ---- S^T (waves 0, 1) or dP^T (waves 2, 3): 16 keys x 16 heads
@@ -202,26 +188,12 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
         dq[i] = mfma32(__builtin_bit_cast(bf16x8, kt), bds, dq[i]);
       }
     }
-    // ---- dkv rows of the tile: dS' Q (576 dims) + P do_lat (512 dims): M = 16 keys, N = 16 dims,
-    // K = 32 heads; lane of the result: dim i16 of the tile, keys 4*g16 + e
-    const bf16x8 a_ds = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_ds) + i16 * 64 + 16 * g16));
-    const bf16x8 a_p = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_p) + i16 * 64 + 16 * g16));
-    int keyrow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keyrow[e] = s_idx[t * kBwKeys + 4 * g16 + e];
-    // Every wave issues exactly kBwAtomics atomics per tile: a padding entry adds +0 to row 0.
-    float* dkv_row[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dkv_row[e] = a.dkv + static_cast<int64_t>(max(keyrow[e], 0)) * kLatent;
-#pragma unroll
-    for (int i = 0; i < kLatent / 16 / kBwWaves; ++i) {
-      const int n = wave + kBwWaves * i;
-      const int dim = 16 * n + i16;
-      f32x4 d = mfma16(a_ds, *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_qT) + dim * 64 + 16 * g16)), f32x4{});
-      if (n < kVDim / 16)
-        d = mfma16(a_p, *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_dT) + dim * 64 + 16 * g16)), d);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(dkv_row[e] + dim, keyrow[e] >= 0 ? d[e] : 0.0f);
+    // ---- the tile's dS' and P (16 keys x 32 heads each) to g, for k_dkv: one 16-byte store per lane
+    if (wave >= 2) {
+      const uint32_t src = wave == 2 ? lds_addr_of(&s_ds[0]) : lds_addr_of(&s_p[0]);
+      const int key = lane >> 2, gr = lane & 3;
+      const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(src + key * 64 + 16 * gr));
+      *reinterpret_cast<u32x4*>(grow + static_cast<int64_t>(t * kBwKeys + key) * kGCols + (wave - 2) * 96 + 8 * gr) = v;
     }
   }
   // dq of the row: lane holds head (lane % 32), dims 32*dt + 8*(e/4) + 4*hh + e%4
@@ -232,6 +204,103 @@ __global__ __launch_bounds__(kBwWaves * kWave, 1) void k_sparse_mla_bwd(BwdArgs 
     if (dt < 18) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqrow[32 * dt + 8 * (e >> 2) + 4 * hh + (e & 3)] = dq[i][e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dkv rows of one row's selected keys for 64 latent dims: out[j, d] = sum_h dS'[j,h] q[h,d] + P[j,h] do_lat[h,d]
+// (the second term for d < 512), on 32x32x16 MFMAs with keys as M, dims as N and the 96 heads as K
+// (six K steps per operand pair). Q and do_lat of the workgroup's dims are the B operands, read once
+// (through LDS, transposed) into registers; each wave takes every fourth 32-key tile of the row, its
+// A operands (dS' and P rows of g) loaded straight from global memory, and adds its 32 x 64 results
+// to dkv with one atomic per element (lane: a dim; 32 consecutive dims of two keys per instruction).
+constexpr int kDkDims = 64;                 // latent dims per workgroup
+constexpr int kDkSlices = kLatent / kDkDims;  // 9
+constexpr int kDkWaves = 4;
+constexpr int kDkHeads = 96;
+
+__global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kDkHeads * kDkDims];  // Q, do_lat slices [head][dim]
+  __shared__ __attribute__((aligned(16))) int32_t s_idx[kBwMaxIdx + 32];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  // The nine slices of a row go to the same XCD (workgroups are dealt to the eight XCDs in turn),
+  // so that its g rows are read from HBM once and from that XCD's L2 afterwards.
+  const int b = blockIdx.x, xcd = b % 8, loc = b / 8;
+  const int crow = (loc / kDkSlices) * 8 + xcd, sl = loc % kDkSlices;
+  if (crow >= a.chunk_rows) return;  // uniform over the workgroup
+  const int r = a.chunk_r0 + crow;
+  const int t_row = a.row0 + r;
+  const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
+  const int ntiles = (keff + 31) / 32;
+  const int d0 = kDkDims * sl;
+  const bool has_v = d0 < kVDim;  // this slice has a P do_lat term
+  const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
+  for (int j = threadIdx.x; j < ntiles * 32; j += kDkWaves * kWave) {
+    const int v = j < keff ? ix[j] : -1;
+    s_idx[j] = (v >= 0 && v < a.T) ? v : -1;
+  }
+  // Q[r, :, d0 .. d0 + 64) and do_lat[crow, :, d0 .. +64): 96 x 8 granules each
+  for (int gi = threadIdx.x; gi < kDkHeads * (kDkDims / 8); gi += kDkWaves * kWave) {
+    const int h = gi / (kDkDims / 8), gg = gi % (kDkDims / 8);
+    *reinterpret_cast<u32x4*>(&s_x[0][h * kDkDims + 8 * gg]) =
+        *reinterpret_cast<const u32x4*>(a.q + (static_cast<int64_t>(r) * kDkHeads + h) * kLatent + d0 + 8 * gg);
+    if (has_v)
+      *reinterpret_cast<u32x4*>(&s_x[1][h * kDkDims + 8 * gg]) =
+          *reinterpret_cast<const u32x4*>(a.do_lat + (static_cast<int64_t>(crow) * kDkHeads + h) * kVDim + d0 + 8 * gg);
+  }
+  __syncthreads();
+  // B operands: part p (0: Q, 1: do_lat), K step ks (heads 16ks .. +16), N tile nt (dims 32nt .. +32 of
+  // the slice); lane: dim 32nt + lane%32, heads 16ks + 8(lane/32) .. +8
+  const int hh = lane >> 5, col = lane & 31;
+  bf16x8 bf[2][6][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 16 * ks + 8 * hh + 2 * i, d = 32 * nt + col;
+          v[i] = static_cast<uint32_t>(s_x[p][h * kDkDims + d]) | (static_cast<uint32_t>(s_x[p][(h + 1) * kDkDims + d]) << 16);
+        }
+        bf[p][ks][nt] = __builtin_bit_cast(bf16x8, v);
+      }
+  const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
+  float* __restrict__ dkv = a.dkv + d0 + col;
+  for (int t = wave; t < ntiles; t += kDkWaves) {
+    // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1)
+    const uint16_t* ga = grow + static_cast<int64_t>(32 * t + col) * kGCols + 8 * hh;
+    bf16x8 af[2][6];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) af[p][ks] = *reinterpret_cast<const bf16x8*>(ga + 96 * p + 16 * ks);
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[0][ks], bf[0][ks][nt], acc[nt]);
+    if (has_v) {
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[1][ks], bf[1][ks][nt], acc[nt]);
+    }
+    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 32nt + lane%32
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_idx[32 * t + 8 * g + 4 * hh])));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (kk[e] >= 0) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) atomicAdd(dkv + static_cast<int64_t>(kk[e]) * kLatent + 32 * nt, acc[nt][4 * g + e]);
+        }
+      }
     }
   }
 }
@@ -331,6 +400,13 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 16384);
   hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv(const DkvArgs& a, hipStream_t st) {
+  if (a.chunk_rows <= 0) return hipSuccess;
+  const int blocks = (a.chunk_rows + 7) / 8 * 8 * kDkSlices;
+  hipLaunchKernelGGL(k_dkv, dim3(blocks), dim3(kDkWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 

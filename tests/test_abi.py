@@ -202,7 +202,11 @@ def test_backward_host_checks():
     fake = 1 << 20
     s = _shape(T=1024)
     nb = L.dsa_bwd_workspace_size(ctypes.byref(s))
-    assert nb > dsa.dsa_workspace_size(s)
+    # the forward's workspace, then per chunk of (here all) 1,024 rows: do, do_lat, delta, and g (dS' and P
+    # of the 96 heads for every selected key, k rounded up to 32)
+    al = lambda x: (x + 255) // 256 * 256
+    cr, g_stride = 1024 * 96, (s.topk + 31) // 32 * 32
+    assert nb == dsa.dsa_workspace_size(s) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4) + al(1024 * g_stride * 192 * 2)
     args = [fake] * 12
     assert L.dsa_sparse_mla_bwd(ctypes.byref(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)), *args, fake, nb,
                                 None) == dsa.DSA_ERR_UNSUPPORTED
