@@ -390,7 +390,7 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
     del o_lat
     warm_steps = [e[0].elapsed_time(e[3]) for e in ev]
     # The FP8 indexer (an alternative to the BF16 one, same outputs' shape), timed the same way.
-    t_idx8 = None
+    t_idx8 = t_idx_ln = ln_same = None
     if cfg.H_I == 64 and cfg.d_I == 128:
         idx8 = torch.empty_like(topk_idx)
         ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_stage)]
@@ -400,6 +400,16 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
             ev8[i][1].record(stream)
         torch.cuda.synchronize()
         t_idx8 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev8]))
+        # The indexer with the key LayerNorm fused into its key-chunk loads (same results as the BF16
+        # indexer, checked here on the whole output).
+        ev_ln = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_stage)]
+        for i in range(n_stage):
+            ev_ln[i][0].record(stream)
+            dsa.dsa_index_topk_fused_ln(shape, dev["q_I"], dev["k_I"], dev["w"], idx8, ws)
+            ev_ln[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_idx_ln = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_ln]))
+        ln_same = bool(torch.equal(idx8, topk_idx))
         del idx8
     # The steps on either side of the path: the W_UK absorption that produces q, and o_proj after the
     # gate (hidden size 7168), on seeded synthetic operands of their shapes.
@@ -502,6 +512,11 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
             "indexer_fp8_frac_of_fp8_peak": round(w["k_index_topk"] / (t_idx8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
             "indexer_fp8_speedup_over_bf16": round(t_idx / t_idx8, 3),
             "fp8_indexer_path_tokens_per_s": round(T / ((t_idx8 + t_att + t_up) * 1e-3), 1),
+            # key LayerNorm fused into the indexer's key-chunk loads: time, and whether its indices
+            # equal the BF16 indexer's on every row
+            "index_topk_fused_ln_ms": round(t_idx_ln, 4),
+            "fused_ln_over_prologue": round(t_idx_ln / t_idx, 3),
+            "fused_ln_indices_equal": ln_same,
         })
     log(f"[bench] {name}: {res['value']:.0f} tokens/s, {ms_step:.3f} ms/step (indexer {t_idx:.3f}, "
         f"attention {t_att:.3f}, up/gate {t_up:.3f} ms; fp8 indexer {t_idx8 if t_idx8 is None else round(t_idx8, 3)} ms)")

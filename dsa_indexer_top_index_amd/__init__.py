@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
                 ln_gamma=None, ln_beta=None, lse=None)
   dsa_index_topk_noalloc(shape, q_I, k_I, w, topk_idx, ln_gamma=None, ln_beta=None)
   dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
+  dsa_index_topk_fused_ln(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None)
   dsa_quantize_fp8(x, q8, scale)
   dsa_q_absorb(shape, q_nope, q_pe, W_UK, q)
   dsa_o_proj(shape, x, W_o, y)
@@ -96,6 +97,8 @@ def lib():
         L.dsa_index_topk_noalloc.restype = ctypes.c_int
         L.dsa_index_topk_fp8.argtypes = [P, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_index_topk_fp8.restype = ctypes.c_int
+        L.dsa_index_topk_fused_ln.argtypes = [P, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_index_topk_fused_ln.restype = ctypes.c_int
         L.dsa_quantize_fp8.argtypes = [ctypes.c_int64, v, v, v, v]
         L.dsa_quantize_fp8.restype = ctypes.c_int
         L.dsa_bwd_workspace_size.argtypes = [P]
@@ -227,6 +230,18 @@ def dsa_index_topk_fp8(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, l
         _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
         _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
     _raise(st, "dsa_index_topk_fp8")
+
+
+def dsa_index_topk_fused_ln(shape, q_I, k_I, w, topk_idx, workspace, ln_gamma=None, ln_beta=None):
+    """dsa_index_topk with the key LayerNorm fused into the indexer's key-chunk loads (H_I=64, d_I=128;
+    k_I 16-byte aligned). Same results."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    st = lib().dsa_index_topk_fused_ln(
+        ctypes.byref(shape), _p(q_I, bf, "q_I", numel=n["q_I"]), _p(k_I, bf, "k_I", numel=n["k_I"]),
+        _p(ln_gamma, torch.float32, "ln_gamma", True, n["ln"]), _p(ln_beta, torch.float32, "ln_beta", True, n["ln"]),
+        _p(w, bf, "w", numel=n["w"]), _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, "dsa_index_topk_fused_ln")
 
 
 def dsa_q_absorb(shape, q_nope, q_pe, W_UK, q):

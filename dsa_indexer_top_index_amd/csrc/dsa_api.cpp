@@ -118,7 +118,7 @@ struct Seg {
 // caller storage for at least s->n_docs entries (no allocation happens here).
 static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* gamma,
                             const float* beta, const uint16_t* w, int32_t* topk_idx, void* ws, Seg* segs,
-                            hipStream_t st, bool fp8 = false) {
+                            hipStream_t st, bool fp8 = false, bool fused_ln = false) {
   const auto L = layout_of(s);
   uint16_t* lnk = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + L.lnk_off);
   dsa::IndexArgs a{};
@@ -137,7 +137,12 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
   a.slot_flags = reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + L.flags_off);
   a.cand = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.cand_off);
   a.n_slots = dsa::kIdxSlots;
-  if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st) != hipSuccess)
+  a.k_raw = k_I;
+  a.ln_gamma = gamma;
+  a.ln_beta = beta;
+  a.ln_eps = static_cast<double>(s->ln_eps);
+  if (dsa::launch_index_prologue(k_I, gamma, beta, static_cast<double>(s->ln_eps), s->d_I, lnk, a, st, !fused_ln) !=
+      hipSuccess)
     return DSA_ERR_LAUNCH;
   if (fp8) {
     // E4M3 codes and scales of LNk (the T key rows) and of q_I (every head row of the query rows)
@@ -186,7 +191,7 @@ static dsa_status run_index(const dsa_shape* s, const uint16_t* q_I, const uint1
       a.seg_b[a.nseg] = segs[i].b;
       a.seg_blk0[a.nseg + 1] = a.seg_blk0[a.nseg] + dsa::index_blocks(segs[i].m, a.paired);
     }
-    const hipError_t e = dsa::launch_index_topk(a, s->H_I, s->d_I, fp8, st);
+    const hipError_t e = dsa::launch_index_topk(a, s->H_I, s->d_I, fp8, st, fused_ln);
     if (e == hipErrorInvalidConfiguration) return DSA_ERR_UNSUPPORTED;  // more resident workgroups than slots
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
   }
@@ -281,6 +286,22 @@ dsa_status dsa_index_topk_fp8(const dsa_shape* s, const uint16_t* q_I, const uin
   std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
   return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), static_cast<hipStream_t>(stream),
                    true);
+}
+
+dsa_status dsa_index_topk_fused_ln(const dsa_shape* s, const uint16_t* q_I, const uint16_t* k_I, const float* ln_gamma,
+                                   const float* ln_beta, const uint16_t* w, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  dsa_status st = dsa_check_shape(s);
+  if (st != DSA_OK) return st;
+  if (!(s->H_I == 64 && s->d_I == 128)) return DSA_ERR_UNSUPPORTED;
+  if (!q_I || !k_I || !w || !topk_idx) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q_I, 16) || !aligned(k_I, 16) || !aligned(w, 2) || !aligned(topk_idx, 16) || !aligned(ln_gamma, 4) ||
+      !aligned(ln_beta, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((st = check_ws(s, ws, ws_bytes)) != DSA_OK) return st;
+  std::vector<Seg> segs(static_cast<size_t>(s->n_docs));
+  return run_index(s, q_I, k_I, ln_gamma, ln_beta, w, topk_idx, ws, segs.data(), static_cast<hipStream_t>(stream),
+                   false, true);
 }
 
 dsa_status dsa_q_absorb(const dsa_shape* s, const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* W_UK,

@@ -45,6 +45,10 @@ struct IndexArgs {
   int seg_m[kIdxMaxSeg];
   int seg_b[kIdxMaxSeg];
   int seg_blk0[kIdxMaxSeg + 1];
+  const uint16_t* k_raw; // key LayerNorm fused into the key-chunk loads: [T, d_I] the raw k_I,
+  const float* ln_gamma; //   its optional affine weight and bias [d_I] (nullptr: none)
+  const float* ln_beta;
+  double ln_eps;
 };
 
 struct MlaArgs {
@@ -152,9 +156,10 @@ struct DwArgs {
 };
 
 // Key LayerNorm of all T keys into LNk, and the outputs of the rows with at most k causal keys.
+// do_ln = false leaves the key LayerNorm out (the fused-LN indexer normalises keys as it stages them).
 hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
-                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st);
-hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st);
+                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st, bool do_ln = true);
+hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st, bool fused_ln = false);
 // FP8 indexer operands: n rows of 128 bf16 values -> E4M3 codes and the rows' power-of-two scales
 // (smallest 2^e with amax * 2^-e <= 448). Two independent row sets in one launch (n2 may be 0).
 hipError_t launch_quantize_fp8(const uint16_t* x1, int64_t n1, uint8_t* q1, float* s1, const uint16_t* x2, int64_t n2,

@@ -49,6 +49,7 @@ template <int D_I>
 __device__ __forceinline__ void key_layernorm_block(const uint16_t* __restrict__ k_I, const float* __restrict__ gamma,
                                                     const float* __restrict__ beta, double eps, int T,
                                                     uint16_t* __restrict__ LNk, int blk) {
+#pragma clang fp contract(off)  // every product and sum rounds on its own, as the definition states
   constexpr int PER = D_I / kWave;
   const int row = blk * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -490,7 +491,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // F8: the FP8 indexer (E4M3 operands with power-of-two row scales, v_mfma_scale_f32_32x32x64_f8f6f4
 // on 32-key tiles); otherwise BF16 operands on v_mfma_f32_16x16x32_bf16 with 16-key tiles.
 // Everything after the scores is shared.
-template <int H_I, int D_I, bool F8>
+template <int H_I, int D_I, bool F8, bool LNF = false>
 __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a) {
   constexpr int TK = F8 ? 32 : 16;               // keys per MFMA N tile
   constexpr int NT = kChunk / TK;                // tiles per chunk
@@ -510,6 +511,9 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   static_assert(CHUNK_GRAN % (kIdxRows * kWave) == 0 && STAGE_BYTES == 16 * CHUNK_GRAN, "chunk copy split");
   static_assert(CPW <= (F8 ? KS : NMF), "a chunk's copies fit beside the MFMAs of one tile");
   static_assert(NTH == 2 || NTH == 4, "a half chunk is joined from two or four tiles");
+  // LNF: the wave's CPW blocks of a chunk are the KS K steps of 16-key tile `wave`, i.e. all d_I dims
+  // of 16 keys, four lanes per key: the layout the fused key LayerNorm relies on.
+  static_assert(!LNF || (!F8 && D_I == 128 && CPW == KS && NT == kIdxRows), "fused LN: BF16, d_I = 128, one tile per wave");
   using QOp = typename std::conditional<F8, i32x8, bf16x8>::type;
   using Acc = typename std::conditional<F8, f32x16, f32x4>::type;
 
@@ -522,6 +526,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   __shared__ uint32_t s_sel[4 * kIdxRows];        // selection scratch
   constexpr int WROW = ((H_I + 31) / 32) * 32;
   __shared__ __attribute__((aligned(16))) float s_w[kIdxRows][WROW];  // head weights of each row (0 past H_I)
+  __shared__ __attribute__((aligned(16))) float s_gb[LNF ? 2 * D_I : 4];  // fused LN: affine weight, then bias
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // = the row slot of this wave
   const int lane = threadIdx.x % kWave;
@@ -678,11 +683,79 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // The last chunk may reach up to 127 rows past the last key row (see kIdxKeyPad): those rows of
   // the padded LNk are staged but never scored. A copy for the chunk after the last one refills the
   // free slot with the last chunk instead, which nothing reads.
+  u32x4 raw[LNF ? CPW : 1];  // fused LN: this lane's raw k_I granules of the next chunk
   auto issue_copy = [&](int c, int j) {
     const int K0 = kb + min(c, nchunks - 1) * kChunk;
     const uint32_t lds = ring + (c & 1) * STAGE_BYTES + 1024 * (CPW * wave + j);
-    if constexpr (F8) copy16_to_lds_imm<0>(a.LNk8 + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
-    else copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+    if constexpr (LNF) {
+      // key 16*wave + lane%16 of the chunk (rows past the last key read the last key: never scored),
+      // dims 32j + 8(lane/16) .. +8: the lane's granule of block CPW*wave + j
+      const int key = min(K0 + 16 * wave + (lane & 15), a.T - 1);
+      raw[j] = *reinterpret_cast<const u32x4*>(a.k_raw + static_cast<int64_t>(key) * D_I + 32 * j + 8 * (lane >> 4));
+    } else if constexpr (F8) {
+      copy16_to_lds_imm<0>(a.LNk8 + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+    } else {
+      copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+    }
+  };
+  // Fused LN: normalise the raw granules of chunk c (loaded by issue_copy) and write them to the
+  // chunk's staging slot as the B operand blocks. The four lanes lane%16 + 16m hold one key's 128
+  // values; mean and biased variance in double (every sum here is exact for bf16 inputs, so the order
+  // of the lane sums does not matter), then one rounding to bf16, as in the prologue.
+  auto ln_stage = [&](int c) {
+    if constexpr (LNF) {
+#pragma clang fp contract(off)
+      auto val = [&](int j, int e) -> double {  // value e of granule j, re-read from the raw registers
+        return static_cast<double>(bf16_to_f32(static_cast<uint16_t>(raw[j][e >> 1] >> (16 * (e & 1)))));
+      };
+      double sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += val(j, e);
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const double mean = sum / D_I;
+      // each pass converts the values again rather than keeping 32 doubles alive across the passes
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) asm volatile("" : "+v"(raw[j]));
+      double sq = 0.0;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double d = val(j, e) - mean;
+          sq += d * d;
+        }
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) asm volatile("" : "+v"(raw[j]));
+      const double inv = 1.0 / sqrt(sq / D_I + a.ln_eps);
+      const bool has_b = a.ln_beta != nullptr;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        u32x4 o;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t w2 = 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int e = 2 * e2 + h, dim = 32 * j + 8 * (lane >> 4) + e;
+            // the weight defaults to 1 (an exact product); the bias is selected, not added as 0, so
+            // that a -0 stays -0 as in the prologue
+            double r = (val(j, e) - mean) * inv;
+            r *= static_cast<double>(s_gb[dim]);
+            const double rb = r + static_cast<double>(s_gb[D_I + dim]);
+            r = has_b ? rb : r;
+            w2 |= static_cast<uint32_t>(f64_to_bf16(r)) << (16 * h);
+          }
+          o[e2] = w2;
+        }
+        *reinterpret_cast<DSA_LDS u32x4*>(lds_ptr(ring + (c & 1) * STAGE_BYTES + 1024 * (CPW * wave + j) + 16 * lane)) = o;
+        __builtin_amdgcn_sched_barrier(0);  // one granule at a time: bounds the live double temporaries
+      }
+    }
   };
   // Scores of a chunk come from NT tiles of TK keys (K = d_I), into accA and accB in turn. The loop
   // is software pipelined by one tile: the MFMAs of one tile run interleaved with the VALU
@@ -854,8 +927,16 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // FP8: the key scales of the previous chunk's second half (lane l: key 64 + l), loaded a step
   // before they are used
   float sk_prev = 1.0f;
+  if constexpr (LNF) {
+    for (int i = threadIdx.x; i < D_I; i += kIdxRows * kWave) {
+      s_gb[i] = a.ln_gamma != nullptr ? a.ln_gamma[i] : 1.0f;
+      s_gb[D_I + i] = a.ln_beta != nullptr ? a.ln_beta[i] : 0.0f;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int j = 0; j < CPW; ++j) issue_copy(0, j);
+  ln_stage(0);
   // Step c: tile 0 of chunk c (the next chunk's copies issued between its MFMAs); the selections
   // that the lists filled by step c-1 asked for; the other tiles, with the append of the second
   // half of chunk c-1 beside tile 1 and that of the first half of chunk c beside tile NTH + 1.
@@ -879,7 +960,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     if (act) {
       // a wave whose row ends before this chunk leaves its SIMD to the other wave there
       auto copies = [&](int st) {
-        if (st < CPW) issue_copy(c + 1, st);
+        if (!LNF && st < CPW) issue_copy(c + 1, st);
       };
       ph_prev[NTH - 1] = tile(c, std::integral_constant<int, 0>{}, accA, accB, copies);
       score_hi = join(ph_prev);
@@ -887,6 +968,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     } else if (c + 1 < nchunks) {
 #pragma unroll
       for (int j = 0; j < CPW; ++j) issue_copy(c + 1, j);
+      ln_stage(c + 1);
     }
     if ((f0[0] | f0[1] | f0[2] | f0[3] | f1[0] | f1[1] | f1[2] | f1[3]) != 0)
       run_selections(kSelSlack, c & 1);  // uniform, rare
@@ -901,6 +983,10 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
             if (st == 0) append(2 * c - 1, score_hi, (c + 1) & 1);
           } else if constexpr (n == NTH + 1) {
             if (st == 0) append(2 * c, score_lo, (c + 1) & 1);
+          } else if constexpr (LNF && n == NT - 1) {
+            // fused LN: the next chunk's raw keys, loaded beside the last tile (their registers are
+            // live only from here to the staging after it)
+            if (st < CPW && c + 1 < nchunks) issue_copy(c + 1, st);
           }
         };
         if constexpr (n % 2 == 0) pc[n - 1] = tile(c, nn, accA, accB, side);
@@ -915,6 +1001,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       });
 #pragma unroll
       for (int i = 0; i + 1 < NTH; ++i) ph_prev[i] = pc[NTH + i];
+      if (c + 1 < nchunks) ln_stage(c + 1);  // fused LN only; its LDS writes land before the next barrier
     } else if (act_prev) {
       ph_prev[NTH - 1] = tile_drain(accB);  // the last tile of chunk c-1 (odd: accB)
       float sc = join(ph_prev);
@@ -954,13 +1041,14 @@ static const void* index_kernel(int v) {
   switch (v) {
     case 0: return reinterpret_cast<const void*>(k_index_topk<64, 128, false>);
     case 1: return reinterpret_cast<const void*>(k_index_topk<4, 64, false>);
-    default: return reinterpret_cast<const void*>(k_index_topk<64, 128, true>);
+    case 2: return reinterpret_cast<const void*>(k_index_topk<64, 128, true>);
+    default: return reinterpret_cast<const void*>(k_index_topk<64, 128, false, true>);
   }
 }
 
 static int index_resident_blocks(int v) {
   static std::mutex mu;
-  static int cached[3][64] = {};
+  static int cached[4][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
   std::lock_guard<std::mutex> lock(mu);
@@ -973,17 +1061,21 @@ static int index_resident_blocks(int v) {
   return cached[v][dev];
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st) {
+hipError_t launch_index_topk(const IndexArgs& a, int H_I, int d_I, bool fp8, hipStream_t st, bool fused_ln) {
   if (a.nseg < 1 || a.nseg > kIdxMaxSeg || a.n_slots < 1) return hipErrorInvalidValue;
   const bool big = H_I == 64 && d_I == 128;
-  if (fp8 && !big) return hipErrorInvalidValue;
-  const int v = fp8 ? 2 : (big ? 0 : 1);
+  if ((fp8 || fused_ln) && !big) return hipErrorInvalidValue;
+  if (fp8 && fused_ln) return hipErrorInvalidValue;
+  const int v = fused_ln ? 3 : fp8 ? 2 : (big ? 0 : 1);
   const int resident = index_resident_blocks(v);
   if (resident < 1 || resident > a.n_slots) return hipErrorInvalidConfiguration;  // slots could run out
   dim3 grid(a.seg_blk0[a.nseg]), block(kIdxRows * kWave);
-  if (v == 2) hipLaunchKernelGGL((k_index_topk<64, 128, true>), grid, block, 0, st, a);
-  else if (v == 0) hipLaunchKernelGGL((k_index_topk<64, 128, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_index_topk<4, 64, false>), grid, block, 0, st, a);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((k_index_topk<64, 128, false>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_index_topk<4, 64, false>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_index_topk<64, 128, true>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_index_topk<64, 128, false, true>), grid, block, 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -1052,8 +1144,8 @@ __global__ __launch_bounds__(256) void k_index_prologue(const uint16_t* __restri
 }
 
 hipError_t launch_index_prologue(const uint16_t* k_I, const float* gamma, const float* beta, double eps, int d_I,
-                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st) {
-  const int nln = (a.T + 3) / 4;
+                                 uint16_t* LNk, const IndexArgs& a, hipStream_t st, bool do_ln) {
+  const int nln = do_ln ? (a.T + 3) / 4 : 0;
   const int nfill = a.nrows < 2048 ? a.nrows : 2048;
   dim3 grid(nln + nfill), block(256);
   if (d_I == 128) hipLaunchKernelGGL((k_index_prologue<128>), grid, block, 0, st, k_I, gamma, beta, eps, LNk, a, nln);

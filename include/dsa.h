@@ -106,6 +106,18 @@ dsa_status dsa_index_topk_fp8(const dsa_shape* shape, const uint16_t* q_I, const
                               const float* ln_gamma, const float* ln_beta, const uint16_t* w,
                               int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Steps 1-3 with the key LayerNorm fused into the indexer's key-chunk loads (archdiff "Kimi K3.1
+ * Pro" blueprint: LayerNorm on the indexer key; model-coverage page, Implementation Limits, 2nd
+ * bullet: one fused indexer). Each workgroup normalises the raw k_I rows of every chunk it stages, in
+ * double with one rounding to bf16, so LN(k_I) is never written; the results are identical to
+ * dsa_index_topk's. It normalises each key once per workgroup that stages it (about T/16 times), so
+ * it is the slower form; dsa_index_topk normalises each key once. Same arguments and workspace as
+ * dsa_index_topk, except that k_I must be 16-byte aligned; (H_I, d_I) = (64, 128) only (else
+ * DSA_ERR_UNSUPPORTED). */
+dsa_status dsa_index_topk_fused_ln(const dsa_shape* shape, const uint16_t* q_I, const uint16_t* k_I,
+                                   const float* ln_gamma, const float* ln_beta, const uint16_t* w,
+                                   int32_t* topk_idx, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The FP8 indexer's operand quantisation on its own: n_rows rows of 128 bf16 values (x, 16-byte
  * aligned) -> q8 [n_rows, 128] E4M3 codes (16-byte aligned) and scale [n_rows] float32, the row's
  * power of two 2^e as above. No workspace. */
@@ -114,7 +126,7 @@ dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, floa
 /* Steps 1-3 without a workspace and without allocating device memory, for callers that cannot
  * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same inputs, output and results as dsa_index_topk. The scratch it needs instead of the workspace
- * is a fixed 67,666,944-byte device array per GPU, held from the first call on that GPU until the
+ * is a fixed 110,134,272-byte device array per GPU, held from the first call on that GPU until the
  * process ends; it limits the shape to T <= 131072 and at most 64 documents (else
  * DSA_ERR_TOO_LARGE, checked on the host before any HIP call). Every call on a GPU uses that GPU's
  * one array and leaves its contents behind (each call clears what must start at zero itself):

@@ -20,7 +20,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == ["dsa_bwd_workspace_size", "dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
-                     "dsa_index_topk_fp8", "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb", "dsa_quantize_fp8",
+                     "dsa_index_topk_fp8", "dsa_index_topk_fused_ln", "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb",
+                     "dsa_quantize_fp8",
                      "dsa_sparse_attention_latent", "dsa_sparse_mla_bwd", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_ex",
                      "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
@@ -194,6 +195,21 @@ def test_fp8_entry_points_host_checks():
     assert L.dsa_quantize_fp8(-1, fake, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_quantize_fp8(4, None, fake, fake, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_quantize_fp8(4, fake, fake + 8, fake, None) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_fused_ln_indexer_host_checks():
+    """The fused-LN indexer takes only the 64x128 indexer shape, a 16-byte aligned k_I and the workspace."""
+    L = dsa.lib()
+    fake = 1 << 20
+    tiny = _shape(T=1024, topk=256, H_I=4, d_I=64, H=16)
+    n = dsa.dsa_workspace_size(tiny)
+    args = lambda k_I, ws_bytes: (fake, k_I, None, None, fake, fake, fake, ws_bytes, None)
+    assert L.dsa_index_topk_fused_ln(ctypes.byref(tiny), *args(fake, n)) == dsa.DSA_ERR_UNSUPPORTED
+    s = _shape()
+    n = dsa.dsa_workspace_size(s)
+    assert L.dsa_index_topk_fused_ln(ctypes.byref(s), *args(fake + 2, n)) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk_fused_ln(ctypes.byref(s), *args(None, n)) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_index_topk_fused_ln(ctypes.byref(s), *args(fake, n - 1)) == dsa.DSA_ERR_WORKSPACE
 
 
 def test_backward_host_checks():

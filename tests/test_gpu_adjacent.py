@@ -13,7 +13,7 @@ import dsa_indexer_top_index_amd as dsa
 import oracle
 import testgen as tg
 from tests import gpu_util as gu
-from tests.parity import check_outputs, gamma
+from tests.parity import check_index_row, check_outputs, gamma
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +109,61 @@ def test_o_proj_within_one_bf16_step(rows, H, d_model):
     absdot = np.abs(tg.bf16_to_f32(x[sel]).astype(np.float64)) @ np.abs(tg.bf16_to_f32(W).astype(np.float64)).T
     assert np.all(np.abs(g - exact) <= ulp + 2 * gamma(K) * absdot)
     _say(f"[gpu] o_proj rows={rows} K={K}: {np.mean(got[sel] == ref):.4f} of checked elements equal the oracle's rounding")
+
+
+def _fused_ln_pair(cfg, inp, g=None, bb=None):
+    """Indices of every row from dsa_index_topk and from dsa_index_topk_fused_ln on the same inputs."""
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg, dev.get("cu_seqlens"))
+    ws = dsa.alloc_workspace(shape)
+    gt = None if g is None else torch.from_numpy(g).cuda()
+    bt = None if bb is None else torch.from_numpy(bb).cuda()
+    ref = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
+    got = torch.full((cfg.T, cfg.topk), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_index_topk(shape, dev["q_I"], dev["k_I"], dev["w"], ref, ws, ln_gamma=gt, ln_beta=bt)
+    dsa.dsa_index_topk_fused_ln(shape, dev["q_I"], dev["k_I"], dev["w"], got, ws, ln_gamma=gt, ln_beta=bt)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+@pytest.mark.parametrize("case", ["t4096", "t4096-affine", "t8192", "ragged-docs", "const-and-neg-zero"])
+def test_fused_ln_indexer_equals_prologue_path(case):
+    """dsa_index_topk_fused_ln normalises every key it stages inside the indexer (archdiff blueprint:
+    LayerNorm on the indexer key), in double with one rounding to bf16 like the prologue, whose LN(k_I)
+    equals the oracle's bit for bit (test_key_layernorm_bit_exact_with_affine). Equal LN bits give equal
+    scores, so every row's indices must equal dsa_index_topk's exactly, ties and -1 padding included.
+    Cases: the T=4,096 and T=8,192 workloads (the latter with mid-stream selections), an affine weight
+    and bias, three documents with a ragged total (the last chunk's raw loads past T), and keys with
+    constant rows (zero variance) and negative zeros."""
+    g = bb = None
+    if case in ("t4096", "t8192"):
+        cfg = tg.get_config(case)
+    elif case == "t4096-affine":
+        cfg = tg.get_config("t4096")
+        rng = np.random.default_rng(5)
+        g = rng.uniform(0.5, 1.5, cfg.d_I).astype(np.float32)
+        bb = rng.uniform(-0.2, 0.2, cfg.d_I).astype(np.float32)
+    elif case == "ragged-docs":
+        cfg = tg.Config(case, 71, [2500, 1371, 3003], topk=512, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                        W_UV_std=0.02)
+    else:
+        cfg = tg.Config(case, 72, [1800], topk=300, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                        W_UV_std=0.02)
+    inp = tg.make_inputs(cfg)
+    if case == "const-and-neg-zero":
+        inp["k_I"][::5] = tg.f32_to_bf16(np.full((len(inp["k_I"][::5]), cfg.d_I), 0.75, np.float32))
+        inp["k_I"][1::5, ::3] = np.uint16(0x8000)
+    _say(f"[gpu] fused-LN indexer {case}: T={cfg.T} docs={cfg.n_docs} k={cfg.topk}")
+    ref, got = _fused_ln_pair(cfg, inp, g, bb)
+    bad = (ref != got).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"rows differing from the prologue path: {bad[:10]} ({len(bad)} rows)"
+    if case == "const-and-neg-zero":
+        # and against the oracle on a spread of rows (the prologue path's own parity covers the rest)
+        LNk = oracle.key_layernorm(inp["k_I"], cfg.ln_eps)
+        rows = np.arange(cfg.topk, cfg.T, 97)
+        o_idx, theta, keff = oracle.topk(rows, inp["q_I"][rows], inp["w"][rows], LNk, cfg.cu_seqlens, cfg.topk)
+        g_idx = got.cpu().numpy()
+        for j, t in enumerate(rows):
+            b = oracle.doc_begin(cfg.cu_seqlens, t)
+            msg = check_index_row(g_idx[t], o_idx[j], keff[j], b, t, cfg.topk, inp["q_I"][t], inp["w"][t], LNk, theta[j])
+            assert msg is None, msg
