@@ -136,3 +136,31 @@ def test_backward_t4096_sampled_rows():
     ok, err, mx = check_outputs(dkv.cpu().numpy()[4088:], ref["dkv"][4088:])
     assert ok, ("dkv of the last keys", err, mx)
     assert np.all(np.isfinite(dkv.cpu().numpy())) and np.all(np.isfinite(dW.cpu().numpy()))
+
+
+def test_backward_four_row_chunks_caller_indices():
+    """T=6,200 runs the backward in four 2,048-row chunks, so both double-buffered g / do_lat buffers are
+    reused while the other chunk's dkv contraction may still run on the library's second stream; every
+    gradient is compared in full. Caller indices (k=16, some invalid) keep the oracle's cost small."""
+    cfg = tg.Config("bwd-chunks", 104, [6200], topk=16, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                    W_UV_std=0.02)
+    inp = tg.make_inputs(cfg)
+    T, k, H = cfg.T, cfg.topk, cfg.H
+    rng = np.random.default_rng(6)
+    idx = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        keff = min(k, t + 1)
+        row = rng.integers(0, t + 1, keff).astype(np.int32)
+        row[rng.random(keff) < 0.1] = -1
+        idx[t, :keff] = row
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_workspace(shape)
+    idx_t = torch.from_numpy(idx).cuda()
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    _say("[gpu] backward over four row chunks")
+    dsa.dsa_sparse_mla_fwd(shape, dev["q"], dev["kv"], idx_t, dev["W_UV"], dev["gate"], out, ws, lse=lse)
+    dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128)
+    got = _run_bwd(cfg, inp, idx_t, out, lse, dout)
+    _compare("four row chunks", got, inp, idx, dout, cfg)
