@@ -37,7 +37,7 @@ KERNEL_SRC = {
 # The rocprofv3 names of the three path kernels as the bench's workloads launch them (BF16 indexer,
 # 96 heads), matched exactly: the backward's k_sparse_mla_bwd and the FP8 indexer instance are other kernels.
 KERNEL_NAME = {
-    "k_index_topk": "k_index_topk<64, 128, false>",
+    "k_index_topk": "k_index_topk<64, 128, false, false>",
     "k_sparse_mla": "k_sparse_mla<96>",
     "k_up_gate": "k_up_gate(",
 }
@@ -173,8 +173,8 @@ def pmc_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, workload, co
     for kernel in KERNEL_SRC:
         fv = _per_dispatch_kib(frows, kernel, "FETCH_SIZE")
         wv = _per_dispatch_kib(wrows, kernel, "WRITE_SIZE")
-        if not fv or not wv:
-            continue
+        if not fv or not wv:  # every path kernel runs in every bench workload
+            raise SystemExit(f"no launches of {KERNEL_NAME[kernel]} in the counter runs")
         f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
         fetch_b, write_b = f_kib * 1024.0 * f_scale, w_kib * 1024.0 * w_scale
         res = {
@@ -222,7 +222,7 @@ def pmc_mfma_summary(mfma_dir, workload, commands):
                 d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         ds = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
         if not ds:
-            continue
+            raise SystemExit(f"no launches of {KERNEL_NAME[name]} in the counter run")
         keep = _whole_workload({i: int(d["t"] * 1e9) for i, d in enumerate(ds)})
         ds = [d for i, d in enumerate(ds) if i in keep]
         t = float(np.mean([d["t"] for d in ds]))
