@@ -328,25 +328,41 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 // Backward workspace: the forward's layout, then for one row chunk do [rows, H, 128] bf16,
 // do_lat [rows, H, 512] bf16 and D [rows, H] f32 (the o_lat region holds the recomputed o_lat).
 // Backward workspace: the forward's regions (o_lat is recomputed into its region), then per row chunk
-//   do     [chunk rows, H, 128] bf16   sigma(g) dout
-//   do_lat [chunk rows, H, 512] bf16   do W_UV[h]^T
-//   delta  [chunk rows, H] f32         sum dout * out
-//   g      [chunk rows, g_stride, 2H] bf16   dS' and P of every selected key, for the dkv contraction
+// of at most kBwdChunkRows rows
+//   do      [chunk rows, H, 128] bf16        sigma(g) dout
+//   do_lat  [chunk rows, H, 512] bf16        do W_UV[h]^T
+//   delta   [chunk rows, H] f32              sum dout * out
+//   g       [chunk rows, g_stride, 2H] bf16  dS' and P of every selected key, for the dkv contraction
+//   contrib [chunk rows, k, 576] f32         each (row, selected key)'s dkv contribution
+//   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
+//   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
+constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (4.8 GB at k = 2048)
+
 struct BwdLayout {
-  size_t do_off, dolat_off, delta_off, g_off, total;
+  size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off, total;
   int g_stride;
+  int64_t chunk_rows;
 };
 
 static BwdLayout bwd_layout_of(const dsa_shape* s) {
   const Layout L = layout_of(s);
   BwdLayout B{};
-  const size_t cr = static_cast<size_t>(L.chunk_rows) * s->H;
+  const int64_t rows = rows_of(s);
+  B.chunk_rows = rows < kBwdChunkRows ? rows : kBwdChunkRows;
+  const size_t crows = static_cast<size_t>(B.chunk_rows);
+  const size_t cr = crows * s->H;
   B.g_stride = (s->topk + 31) / 32 * 32;
   B.do_off = L.total;
   B.dolat_off = B.do_off + align_up(cr * 128 * 2);
   B.delta_off = B.dolat_off + align_up(cr * 512 * 2);
   B.g_off = B.delta_off + align_up(cr * 4);
-  B.total = B.g_off + align_up(static_cast<size_t>(L.chunk_rows) * B.g_stride * 2 * s->H * 2);
+  B.contrib_off = B.g_off + align_up(crows * B.g_stride * 2 * s->H * 2);
+  B.count_off = B.contrib_off + align_up(crows * s->topk * 576 * 4);
+  B.start_off = B.count_off + align_up(static_cast<size_t>(s->T) * 4);
+  B.cursor_off = B.start_off + align_up((static_cast<size_t>(s->T) + 1) * 4);
+  B.list_off = B.cursor_off + align_up(static_cast<size_t>(s->T) * 4);
+  B.bsum_off = B.list_off + align_up(crows * s->topk * 4);
+  B.total = B.bsum_off + align_up((static_cast<size_t>(s->T) + dsa::kPairScanTile - 1) / dsa::kPairScanTile * 4);
   return B;
 }
 
@@ -379,12 +395,18 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
   uint16_t* dolat = reinterpret_cast<uint16_t*>(base + B.dolat_off);
   float* delta = reinterpret_cast<float*>(base + B.delta_off);
   uint16_t* g = reinterpret_cast<uint16_t*>(base + B.g_off);
+  float* contrib = reinterpret_cast<float*>(base + B.contrib_off);
+  int* count = reinterpret_cast<int*>(base + B.count_off);
+  int* start = reinterpret_cast<int*>(base + B.start_off);
+  int* cursor = reinterpret_cast<int*>(base + B.cursor_off);
+  int* list = reinterpret_cast<int*>(base + B.list_off);
+  int* bsum = reinterpret_cast<int*>(base + B.bsum_off);
   if (dsa::launch_fill_zero(dkv, static_cast<int64_t>(s->T) * 576, hs) != hipSuccess ||
       dsa::launch_fill_zero(dW_UV, static_cast<int64_t>(s->H) * 512 * 128, hs) != hipSuccess)
     return DSA_ERR_LAUNCH;
   const int64_t rows = rows_of(s);
-  for (int64_t c0 = 0; c0 < rows; c0 += L.chunk_rows) {
-    const int n = static_cast<int>(std::min<int64_t>(L.chunk_rows, rows - c0));
+  for (int64_t c0 = 0; c0 < rows; c0 += B.chunk_rows) {
+    const int n = static_cast<int>(std::min<int64_t>(B.chunk_rows, rows - c0));
     dsa::BwdPrepArgs p{dout, out, gate, d_o, delta, dgate, n, s->H, static_cast<int>(c0)};
     if (dsa::launch_bwd_prep(p, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     dsa::AbsorbArgs ab{d_o, nullptr, W_UV, dolat, n, s->H, 512};  // do_lat = do W_UV[h]^T
@@ -409,9 +431,12 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
     b.H = s->H;
     b.scale = s->softmax_scale;
     if (dsa::launch_sparse_mla_bwd(b, hs) != hipSuccess) return DSA_ERR_LAUNCH;
-    dsa::DkvArgs dk{g, q, dolat, topk_idx, dkv, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
-                    B.g_stride};
+    dsa::DkvArgs dk{g, q, dolat, topk_idx, contrib, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n,
+                    s->topk, B.g_stride};
     if (dsa::launch_dkv(dk, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::DkvListArgs dl{topk_idx, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
+                        count, start, cursor, bsum, list, contrib, dkv};
+    if (dsa::launch_dkv_reduce(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     // o_lat of the chunk again (the forward's attention kernel), for dW_UV
     if ((st = launch_attention(s, nullptr, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
     dsa::DwArgs dw{olat, d_o, dW_UV, n, s->H};

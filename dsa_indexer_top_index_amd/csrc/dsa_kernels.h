@@ -130,13 +130,15 @@ struct BwdArgs {
   float scale;
 };
 
-// dkv[idx[r, j]] += dS'[r, j, :] q[r] + P[r, j, :] do_lat[r] over all H heads, from g.
+// The dkv contribution of each (row r, selected key j) of a row chunk, over all H heads, from g:
+//   contrib[r, j, :] = dS'[r, j, :] q[r] + P[r, j, :] do_lat[r]
+// stored for the pairs with a usable index; k_dkv_reduce then adds each key's contributions to dkv.
 struct DkvArgs {
   const uint16_t* g;       // as BwdArgs::g
   const uint16_t* q;       // [nrows, H, 576]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
   const int32_t* idx;      // [nrows, k]
-  float* dkv;              // [T, 576], added to
+  float* contrib;          // [chunk_rows, k, 576] f32
   const int32_t* cu;
   int n_docs;
   int T;
@@ -145,6 +147,26 @@ struct DkvArgs {
   int chunk_rows;
   int k;
   int g_stride;
+};
+
+// Per-key lists of a row chunk's (row, j) pairs (a counting sort by key index), and their sum into dkv.
+constexpr int kPairScanTile = 4096;  // keys per workgroup of the scan over count
+struct DkvListArgs {
+  const int32_t* idx;      // [nrows, k]
+  const int32_t* cu;
+  int n_docs;
+  int T;
+  int row0;
+  int chunk_r0;
+  int chunk_rows;
+  int k;
+  int* count;              // [T] pairs per key (zeroed before the count pass)
+  int* start;              // [T + 1] exclusive prefix sums of count
+  int* cursor;             // [T] scatter positions
+  int* bsum;               // [ceil(T / kPairScanTile)] count sums of the scan's blocks
+  int* list;               // [chunk_rows * k] pair ids r * k + j, grouped by key
+  const float* contrib;    // as DkvArgs::contrib
+  float* dkv;              // [T, 576], added to
 };
 
 struct DwArgs {
@@ -173,6 +195,9 @@ hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkv(const DkvArgs& a, hipStream_t st);
+// count[key] = pairs of the chunk selecting key; start = exclusive scan (and cursor = start);
+// list = pair ids grouped by key; dkv[key] += the sum of the key's contributions. Four launches.
+hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st);
 hipError_t launch_dwuv(const DwArgs& a, hipStream_t st);
 
 }  // namespace dsa

@@ -209,12 +209,13 @@ __global__ __launch_bounds__(kBwWaves * kWave, 2) void k_sparse_mla_bwd(BwdArgs 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dkv rows of one row's selected keys for 64 latent dims: out[j, d] = sum_h dS'[j,h] q[h,d] + P[j,h] do_lat[h,d]
-// (the second term for d < 512), on 32x32x16 MFMAs with keys as M, dims as N and the 96 heads as K
-// (six K steps per operand pair). Q and do_lat of the workgroup's dims are the B operands, read once
-// (through LDS, transposed) into registers; each wave takes every fourth 32-key tile of the row, its
-// A operands (dS' and P rows of g) loaded straight from global memory, and adds its 32 x 64 results
-// to dkv with one atomic per element (lane: a dim; 32 consecutive dims of two keys per instruction).
+// dkv contributions of one row's selected keys for 64 latent dims:
+//   contrib[j, d] = sum_h dS'[j,h] q[h,d] + P[j,h] do_lat[h,d]  (the second term for d < 512),
+// on 32x32x16 MFMAs with keys as M, dims as N and the 96 heads as K (six K steps per operand pair).
+// Q and do_lat of the workgroup's dims are the B operands, read once (through LDS, transposed) into
+// registers; each wave takes every fourth 32-key tile of the row, its A operands (dS' and P rows of
+// g) loaded straight from global memory, and stores its 32 x 64 results (lane: a dim; 32 consecutive
+// dims of two keys per instruction). k_dkv_reduce adds them up per key.
 constexpr int kDkDims = 64;                 // latent dims per workgroup
 constexpr int kDkSlices = kLatent / kDkDims;  // 9
 constexpr int kDkWaves = 4;
@@ -270,15 +271,21 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
         bf[p][ks][nt] = __builtin_bit_cast(bf16x8, v);
       }
   const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
-  float* __restrict__ dkv = a.dkv + d0 + col;
-  for (int t = wave; t < ntiles; t += kDkWaves) {
-    // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1)
-    const uint16_t* ga = grow + static_cast<int64_t>(32 * t + col) * kGCols + 8 * hh;
-    bf16x8 af[2][6];
+  float* __restrict__ crow_out = a.contrib + static_cast<int64_t>(crow) * a.k * kLatent + d0 + col;
+  // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); the
+  // next tile's are loaded before this tile's products
+  const uint16_t* __restrict__ ga0 = grow + static_cast<int64_t>(col) * kGCols + 8 * hh;
+  bf16x8 af[2][6], an[2][6];
+  auto load_a = [&](int t, bf16x8 (&dst)[2][6]) {
+    const uint16_t* ga = ga0 + static_cast<int64_t>(32 * t) * kGCols;
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) af[p][ks] = *reinterpret_cast<const bf16x8*>(ga + 96 * p + 16 * ks);
+      for (int ks = 0; ks < 6; ++ks) dst[p][ks] = *reinterpret_cast<const bf16x8*>(ga + 96 * p + 16 * ks);
+  };
+  if (wave < ntiles) load_a(wave, af);
+  for (int t = wave; t < ntiles; t += kDkWaves) {
+    if (t + kDkWaves < ntiles) load_a(t + kDkWaves, an);
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks)
@@ -290,19 +297,163 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[1][ks], bf[1][ks][nt], acc[nt]);
     }
-    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 32nt + lane%32
+    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 32nt + lane%32; pairs without a usable
+    // index are never listed, so their rows are not stored
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_idx[32 * t + 8 * g + 4 * hh])));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (kk[e] >= 0) {
+          float* dst = crow_out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kLatent;
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) atomicAdd(dkv + static_cast<int64_t>(kk[e]) * kLatent + 32 * nt, acc[nt][4 * g + e]);
+          for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = acc[nt][4 * g + e];
         }
       }
     }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) af[p][ks] = an[p][ks];
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Summing the contributions per key without atomics on dkv: a counting sort of the chunk's usable
+// (row, j) pairs by key index (count, exclusive scan, scatter of pair ids), then one wave per key adds
+// its pairs' 576-float rows and adds the sum to dkv, which no other wave of the pass touches. The
+// counts and list positions come from integer atomics (one per pair, not one per element), so the
+// order of a key's pairs, and the last bits of its sum, may differ from run to run.
+__device__ __forceinline__ int pair_key(const DkvListArgs& a, int crow, int j) {
+  const int t_row = a.row0 + a.chunk_r0 + crow;
+  const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
+  if (j >= keff) return -1;
+  const int v = a.idx[static_cast<int64_t>(a.chunk_r0 + crow) * a.k + j];
+  return (v >= 0 && v < a.T) ? v : -1;
+}
+
+__global__ __launch_bounds__(256) void k_pairs_count(DkvListArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x, crow = blockIdx.y;
+  if (j >= a.k) return;
+  const int key = pair_key(a, crow, j);
+  if (key >= 0) atomicAdd(a.count + key, 1);
+}
+
+// Exclusive scan of count[0 .. T) into start (start[T] = total) and cursor, in two passes over
+// tiles of kPairScanTile keys: the tiles' sums, then each tile adds the sums of the tiles before it to
+// a workgroup scan of its own keys. 256 threads, 16 consecutive keys each.
+constexpr int kScanPer = kPairScanTile / 256;
+static_assert(kScanPer == 16, "four 16-byte loads per thread");
+
+__device__ __forceinline__ void load_counts(const DkvListArgs& a, int i0, int (&c)[kScanPer]) {
+  if (i0 + kScanPer <= a.T) {
+#pragma unroll
+    for (int v = 0; v < kScanPer / 4; ++v) {
+      const i32x4 x = *reinterpret_cast<const i32x4*>(a.count + i0 + 4 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[4 * v + e] = x[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) c[e] = i0 + e < a.T ? a.count[i0 + e] : 0;
+  }
+}
+
+// Sum over the workgroup of x (256 threads); every thread gets it.
+__device__ __forceinline__ int block_sum(int x, int* s_part) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if (threadIdx.x % kWave == 0) s_part[threadIdx.x / kWave] = x;
+  __syncthreads();
+  return s_part[0] + s_part[1] + s_part[2] + s_part[3];
+}
+
+__global__ __launch_bounds__(256) void k_pairs_tile_sums(DkvListArgs a) {
+  __shared__ int s_part[4];
+  int c[kScanPer];
+  load_counts(a, blockIdx.x * kPairScanTile + kScanPer * threadIdx.x, c);
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e) sum += c[e];
+  sum = block_sum(sum, s_part);
+  if (threadIdx.x == 0) a.bsum[blockIdx.x] = sum;
+}
+
+__global__ __launch_bounds__(256) void k_pairs_scan(DkvListArgs a) {
+  __shared__ int s_part[4];
+  __shared__ int s_wave[4];
+  const int b = blockIdx.x, lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int before = 0;  // the sums of the tiles before this one
+  for (int t = threadIdx.x; t < b; t += 256) before += a.bsum[t];
+  before = block_sum(before, s_part);
+  const int i0 = b * kPairScanTile + kScanPer * threadIdx.x;
+  int c[kScanPer];
+  load_counts(a, i0, c);
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e) sum += c[e];
+  // inclusive scan of the threads' sums: within the wave, then over the four wave totals
+  int x = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int run = before + x - sum;
+  for (int w = 0; w < wave; ++w) run += s_wave[w];
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e) {
+    if (i0 + e < a.T) {
+      a.start[i0 + e] = run;
+      a.cursor[i0 + e] = run;
+    }
+    run += c[e];
+  }
+  if (b == gridDim.x - 1 && threadIdx.x == 255) a.start[a.T] = run;  // the total
+}
+
+__global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
+  const int j = blockIdx.x * 256 + threadIdx.x, crow = blockIdx.y;
+  if (j >= a.k) return;
+  const int key = pair_key(a, crow, j);
+  if (key >= 0) a.list[atomicAdd(a.cursor + key, 1)] = crow * a.k + j;
+}
+
+// One wave per key: the sum of its pairs' contribution rows (lane: dims lane + 64m, m < 9), four pairs
+// in flight, added to dkv[key].
+__global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
+  const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (key >= a.T) return;
+  const int p0 = a.start[key], p1 = a.start[key + 1];
+  if (p0 == p1) return;  // uniform over the wave
+  constexpr int M = kLatent / kWave;  // 9
+  float acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+  int p = p0;
+  for (; p + 4 <= p1; p += 4) {
+    float v[4][M];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* src = a.contrib + static_cast<int64_t>(a.list[p + u]) * kLatent + lane;
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[u][m] = src[kWave * m];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] += v[u][m];
+  }
+  for (; p < p1; ++p) {
+    const float* src = a.contrib + static_cast<int64_t>(a.list[p]) * kLatent + lane;
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] += src[kWave * m];
+  }
+  float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + lane;
+#pragma unroll
+  for (int m = 0; m < M; ++m) dst[kWave * m] += acc[m];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -400,6 +551,19 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 16384);
   hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st) {
+  if (a.chunk_rows <= 0) return hipSuccess;
+  if (launch_fill_zero(reinterpret_cast<float*>(a.count), a.T, st) != hipSuccess) return hipGetLastError();  // int 0 == float +0 bits
+  const dim3 pairs((a.k + 255) / 256, a.chunk_rows);
+  hipLaunchKernelGGL(k_pairs_count, pairs, dim3(256), 0, st, a);
+  const dim3 tiles((a.T + kPairScanTile - 1) / kPairScanTile);
+  hipLaunchKernelGGL(k_pairs_tile_sums, tiles, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pairs_scan, tiles, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pairs_scatter, pairs, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_dkv_sum, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -220,8 +220,8 @@ dsa_status dsa_o_proj(const dsa_shape* shape, const uint16_t* x, const uint16_t*
  * L = sum(dout * out) of dsa_sparse_mla_fwd (per-head gate, no sink) on the same q, kv, topk_idx,
  * W_UV and gate, given that call's out [rows, H, 128] and lse [rows, H]:
  *   dq [rows, H, 576], dkv [T, 576], dW_UV [H, 512, 128], dgate [rows, H], all float32.
- * dkv and dW_UV are overwritten (zeroed, then accumulated over the rows with atomic adds, so their
- * last bits depend on the order); dq and dgate are written. H must be 96 (else
+ * dkv and dW_UV are overwritten (zeroed, then accumulated over the rows in an order that atomic
+ * operations decide, so their last bits may differ from call to call); dq and dgate are written. H must be 96 (else
  * DSA_ERR_UNSUPPORTED). Workspace: >= dsa_bwd_workspace_size(shape) bytes. */
 size_t dsa_bwd_workspace_size(const dsa_shape* shape);
 dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
