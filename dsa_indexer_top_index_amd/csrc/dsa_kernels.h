@@ -131,14 +131,14 @@ struct BwdArgs {
 };
 
 // The dkv contribution of each (row r, selected key j) of a row chunk, over all H heads, from g:
-//   contrib[r, j, :] = dS'[r, j, :] q[r] + P[r, j, :] do_lat[r]
+//   contrib(r, j) = dS'[r, j, :] q[r] + P[r, j, :] do_lat[r]  (576 floats)
 // stored for the pairs with a usable index; k_dkv_reduce then adds each key's contributions to dkv.
 struct DkvArgs {
   const uint16_t* g;       // as BwdArgs::g
   const uint16_t* q;       // [nrows, H, 576]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
   const int32_t* idx;      // [nrows, k]
-  float* contrib;          // [chunk_rows, k, 576] f32
+  float* contrib;          // [9][chunk_rows * k][64] f32: slice s holds dims 64s .. 64s + 63 of pair r * k + j
   const int32_t* cu;
   int n_docs;
   int T;

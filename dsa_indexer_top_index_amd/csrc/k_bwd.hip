@@ -271,7 +271,9 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
         bf[p][ks][nt] = __builtin_bit_cast(bf16x8, v);
       }
   const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
-  float* __restrict__ crow_out = a.contrib + static_cast<int64_t>(crow) * a.k * kLatent + d0 + col;
+  // contrib is slice-major, [9][chunk rows * k][64]: a tile's 32 pairs fill 8 KB in one piece
+  const int64_t npairs = static_cast<int64_t>(a.chunk_rows) * a.k;
+  float* __restrict__ crow_out = a.contrib + (sl * npairs + static_cast<int64_t>(crow) * a.k) * kDkDims + col;
   // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); the
   // next tile's are loaded before this tile's products
   const uint16_t* __restrict__ ga0 = grow + static_cast<int64_t>(col) * kGCols + 8 * hh;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (kk[e] >= 0) {
-          float* dst = crow_out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kLatent;
+          float* dst = crow_out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kDkDims;
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = acc[nt][4 * g + e];
         }
@@ -421,14 +423,15 @@ __global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
   if (key >= 0) a.list[atomicAdd(a.cursor + key, 1)] = crow * a.k + j;
 }
 
-// One wave per key: the sum of its pairs' contribution rows (lane: dims lane + 64m, m < 9), four pairs
-// in flight, added to dkv[key].
+// One wave per key: the sum of its pairs' contributions (lane: dims lane + 64m, m < 9, from slice m),
+// four pairs in flight, added to dkv[key].
 __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
   const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (key >= a.T) return;
   const int p0 = a.start[key], p1 = a.start[key + 1];
   if (p0 == p1) return;  // uniform over the wave
   constexpr int M = kLatent / kWave;  // 9
+  const int64_t slice = static_cast<int64_t>(a.chunk_rows) * a.k * kWave;  // floats per slice
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
@@ -437,9 +440,9 @@ __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
     float v[4][M];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float* src = a.contrib + static_cast<int64_t>(a.list[p + u]) * kLatent + lane;
+      const float* src = a.contrib + static_cast<int64_t>(a.list[p + u]) * kWave + lane;
 #pragma unroll
-      for (int m = 0; m < M; ++m) v[u][m] = src[kWave * m];
+      for (int m = 0; m < M; ++m) v[u][m] = src[slice * m];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -447,9 +450,9 @@ __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
       for (int m = 0; m < M; ++m) acc[m] += v[u][m];
   }
   for (; p < p1; ++p) {
-    const float* src = a.contrib + static_cast<int64_t>(a.list[p]) * kLatent + lane;
+    const float* src = a.contrib + static_cast<int64_t>(a.list[p]) * kWave + lane;
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] += src[kWave * m];
+    for (int m = 0; m < M; ++m) acc[m] += src[slice * m];
   }
   float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + lane;
 #pragma unroll
