@@ -6,6 +6,7 @@ max |g - g_ref| <= 2e-2 * max |g_ref| (the GPU rounds do, do_lat, P and dS to bf
 takes D = sum dout * out from the bf16 out)."""
 from __future__ import annotations
 
+import math
 import sys
 
 import numpy as np
@@ -164,3 +165,93 @@ def test_backward_four_row_chunks_caller_indices():
     dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128)
     got = _run_bwd(cfg, inp, idx_t, out, lse, dout)
     _compare("four row chunks", got, inp, idx, dout, cfg)
+
+
+def _dout_device(cfg, chunk_rows=4096):
+    """The seeded dout of every row, drawn in row chunks straight into device memory (the same values
+    as one draw over all rows: the generator is counter-based)."""
+    T, per = cfg.T, cfg.H * 128
+    t = torch.empty((T, per), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, T, chunk_rows):
+        n = min(chunk_rows, T - r0)
+        t[r0:r0 + n] = gu.bf16_np_to_tensor(tg.normal_bf16(cfg.seed, TAG_DOUT, r0 * per, n * per, 1.0).reshape(n, per))
+    return t.view(T, cfg.H, 128)
+
+
+def _dout_rows(cfg, rows):
+    per = cfg.H * 128
+    return np.stack([tg.normal_bf16(cfg.seed, TAG_DOUT, int(r) * per, per, 1.0) for r in rows]).reshape(len(rows), cfg.H, 128)
+
+
+def test_backward_t131072_sampled_rows_and_identities():
+    """Full-size T=131,072, top-2048, in the bench's launch configuration:
+    - dq and dgate of sampled rows against the oracle (each depends on its own row only): both sides of
+      the backward's 1,024-row chunk boundaries and of the forward's 2,048-row ones, the middle, the end;
+    - the complete dkv rows of the last eight keys (only the last eight rows can select them);
+    - on the full gradients, the closed forms of L = sum(dout * out) that the oracle's backward is
+      pinned to: <dW_UV[h], W_UV[h]> = sum_r <dout[r,h], out[r,h]> per head, and
+      sum_key <dkv, kv> - sum_(r,h) <dq, q> = sum_(r,h) <dout, out>; and dgate = (1 - sigmoid(gate)) *
+      <dout, out> on every row. These compare the backward with the forward's out, so they check the
+      whole dkv and dW_UV sums (every pair of every row) at this size, in float64 over the GPU's values.
+      The GPU's roundings to bf16 (P, dS', do, do_lat: about 4e-3 relative, unbiased) add errors of
+      random sign, so the bound is 0.05 of the root sum of squares of the per-key, per-(row, head) and
+      per-row terms, not of their absolute sums: dropping a few per mille of the pairs from dkv would
+      exceed it."""
+    cfg = tg.get_config("t131072")
+    T, H = cfg.T, cfg.H
+    _say(f"[gpu] backward t131072: inputs")
+    keys, dev = gu.device_inputs(cfg)
+    res = gu.run_fused(cfg, dev, with_lse=True)
+    dout_t = _dout_device(cfg)
+    shape = gu.shape_of(cfg)
+    ws = dsa.alloc_bwd_workspace(shape)
+    dq = torch.empty((T, H, 576), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((T, 576), dtype=torch.float32, device="cuda")
+    dW = torch.empty((H, 512, 128), dtype=torch.float32, device="cuda")
+    dg = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    _say("[gpu] backward t131072: dsa_sparse_mla_bwd")
+    dsa.dsa_sparse_mla_bwd(shape, dev["q"], dev["kv"], res["topk_idx"], dev["W_UV"], dev["gate"], res["out"],
+                           res["lse"], dout_t, dq, dkv, dW, dg, ws)
+    torch.cuda.synchronize()
+    del ws
+    _say("[gpu] backward t131072: sampled rows against the oracle")
+    rows = np.array([0, 1, 1023, 1024, 2047, 2048, 65535, 65536, 98304, 130047, 130048] + list(range(T - 8, T)))
+    rows_t = torch.from_numpy(rows).cuda()
+    qr = tg.query_rows(cfg, rows)
+    idx = res["topk_idx"][rows_t].cpu().numpy()
+    ref = oracle.sparse_mla_bwd(_f64(qr["q"].reshape(len(rows), H, 576)), _f64(keys["kv"]), idx, _f64(keys["W_UV"]),
+                                _f64(qr["gate"].reshape(len(rows), H)), cfg.softmax_scale, _f64(_dout_rows(cfg, rows)))
+    for k, g in [("dq", dq[rows_t].cpu().numpy()), ("dgate", dg[rows_t].cpu().numpy())]:
+        ok, err, mx = check_outputs(g, ref[k])
+        assert ok, (k, err, mx)
+    ok, err, mx = check_outputs(dkv[T - 8:].cpu().numpy(), ref["dkv"][T - 8:])
+    assert ok, ("dkv of the last keys", err, mx)
+    _say("[gpu] backward t131072: identities on the full gradients")
+    # D[r, h] = <dout, out> in float64, row chunk by row chunk; sum_(r,h) <dq, q> likewise
+    D = torch.empty((T, H), dtype=torch.float64, device="cuda")
+    dq_q = torch.zeros((), dtype=torch.float64, device="cuda")
+    dq_q_sq = torch.zeros((), dtype=torch.float64, device="cuda")
+    for r0 in range(0, T, 8192):
+        sl = slice(r0, min(r0 + 8192, T))
+        D[sl] = (dout_t[sl].double() * res["out"][sl].double()).sum(dim=2)
+        p = (dq[sl].double() * dev["q"][sl].double()).sum(dim=2)  # <dq[r,h], q[r,h]>
+        dq_q += p.sum()
+        dq_q_sq += (p ** 2).sum()
+    dq_q, dq_q_sq = float(dq_q), float(dq_q_sq)
+    per_key = (dkv.double() * dev["kv"].double()).sum(dim=1)  # <dkv[key], kv[key]>
+    lhs, rhs = float(per_key.sum() - dq_q), float(D.sum())
+    rss = math.sqrt(float((per_key ** 2).sum() + dq_q_sq + (D ** 2).sum()))
+    tol = 0.05 * rss
+    _say(f"[gpu] backward t131072: sum <dkv, kv> - sum <dq, q> = {lhs:.6e}, sum <dout, out> = {rhs:.6e}, "
+         f"difference {abs(lhs - rhs) / rss:.2e} of the root sum of squares")
+    assert abs(lhs - rhs) <= tol, ("sum <dkv, kv> - sum <dq, q>", lhs, rhs, tol)
+    lhs_w = (dW.double() * dev["W_UV"].double()).sum(dim=(1, 2))
+    rhs_w, rss_w = D.sum(dim=0), (D ** 2).sum(dim=0).sqrt()
+    worst = float(((lhs_w - rhs_w).abs() / rss_w).max())
+    _say(f"[gpu] backward t131072: <dW_UV[h], W_UV[h]> worst difference {worst:.2e} of the root sum of squares")
+    assert worst <= 0.05, ("<dW_UV[h], W_UV[h]>", worst)
+    sig = torch.sigmoid(dev["gate"].double())
+    dg_ref = (1 - sig) * D
+    err = float((dg.double() - dg_ref).abs().max())
+    assert err <= 1e-4 * float(dg_ref.abs().max()), ("dgate on every row", err)
+    assert bool(torch.isfinite(dkv).all()) and bool(torch.isfinite(dW).all())

@@ -766,6 +766,31 @@ def test_backward_against_finite_differences():
         assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
 
 
+def test_backward_inner_product_identities():
+    """Two closed forms of L = sum(dout * out) that the backward must satisfy at any size (the chain
+    rule through W_UV and through the logits): for each head h,
+      <dW_UV[h], W_UV[h]> = sum_r <dout[r,h], out[r,h]>,
+    and over everything,
+      sum_key <dkv[key], kv[key]> - sum_{r,h} <dq[r,h], q[r,h]> = sum_{r,h} <dout[r,h], out[r,h]>
+    (the key part of dkv pairs with q as dq does; its value part gives do_lat . o_lat = dout . out).
+    Duplicate and out-of-range indices included. The GPU test at T=131,072 checks these on the full
+    gradients."""
+    n, H, T, k = 6, 8, 40, 12
+    q, kv, idx, W, gate, dout = _bwd_case(53, n, H, T, k)
+    scale = 1 / math.sqrt(192)
+    g = oracle.sparse_mla_bwd(q, kv, idx, W, gate, scale, dout)
+    out = oracle.sparse_mla_f64in(q, kv, idx, W, gate, scale)[0]
+    D = (dout * out).sum(axis=2)  # [n, H]
+    lhs_w = (g["dW_UV"] * W).sum(axis=(1, 2))
+    assert np.allclose(lhs_w, D.sum(axis=0), rtol=1e-10, atol=1e-12 * np.abs(D).sum())
+    lhs = (g["dkv"] * kv).sum() - (g["dq"] * q).sum()
+    assert abs(lhs - D.sum()) <= 1e-10 * (np.abs(g["dkv"] * kv).sum() + np.abs(g["dq"] * q).sum())
+    # a planted mistake (the dkv row of one selected key halved) breaks the second form
+    bad = g["dkv"].copy()
+    bad[int(idx[2, 0])] *= 0.5
+    assert abs((bad * kv).sum() - (g["dq"] * q).sum() - D.sum()) > 1e-6 * np.abs(D).sum()
+
+
 def test_backward_against_torch_autograd():
     """Library cross-check: torch autograd in float64 on a dense gathered formulation of the same
     forward gives the same gradients."""
