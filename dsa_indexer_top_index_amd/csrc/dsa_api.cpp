@@ -333,10 +333,10 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 //   do_lat  [chunk rows, H, 512] bf16        do W_UV[h]^T
 //   delta   [chunk rows, H] f32              sum dout * out
 //   g       [chunk rows, g_stride, 2H] bf16  dS' and P of every selected key, for the dkv contraction
-//   contrib [chunk rows, k, 576] f32         each (row, selected key)'s dkv contribution
+//   contrib [9][chunk rows * k][64] bf16      each (row, selected key)'s dkv contribution, by 64-dim slice
 //   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
 //   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
-constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (4.8 GB at k = 2048)
+constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (2.4 GB at k = 2048)
 
 struct BwdLayout {
   size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off, total;
@@ -357,7 +357,7 @@ static BwdLayout bwd_layout_of(const dsa_shape* s) {
   B.delta_off = B.dolat_off + align_up(cr * 512 * 2);
   B.g_off = B.delta_off + align_up(cr * 4);
   B.contrib_off = B.g_off + align_up(crows * B.g_stride * 2 * s->H * 2);
-  B.count_off = B.contrib_off + align_up(crows * s->topk * 576 * 4);
+  B.count_off = B.contrib_off + align_up(crows * s->topk * 576 * 2);
   B.start_off = B.count_off + align_up(static_cast<size_t>(s->T) * 4);
   B.cursor_off = B.start_off + align_up((static_cast<size_t>(s->T) + 1) * 4);
   B.list_off = B.cursor_off + align_up(static_cast<size_t>(s->T) * 4);
@@ -395,7 +395,7 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
   uint16_t* dolat = reinterpret_cast<uint16_t*>(base + B.dolat_off);
   float* delta = reinterpret_cast<float*>(base + B.delta_off);
   uint16_t* g = reinterpret_cast<uint16_t*>(base + B.g_off);
-  float* contrib = reinterpret_cast<float*>(base + B.contrib_off);
+  uint16_t* contrib = reinterpret_cast<uint16_t*>(base + B.contrib_off);
   int* count = reinterpret_cast<int*>(base + B.count_off);
   int* start = reinterpret_cast<int*>(base + B.start_off);
   int* cursor = reinterpret_cast<int*>(base + B.cursor_off);

@@ -138,7 +138,7 @@ struct DkvArgs {
   const uint16_t* q;       // [nrows, H, 576]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
   const int32_t* idx;      // [nrows, k]
-  float* contrib;          // [9][chunk_rows * k][64] f32: slice s holds dims 64s .. 64s + 63 of pair r * k + j
+  uint16_t* contrib;       // [9][chunk_rows * k][64] bf16: slice s holds dims 64s .. 64s + 63 of pair r * k + j
   const int32_t* cu;
   int n_docs;
   int T;
@@ -165,7 +165,7 @@ struct DkvListArgs {
   int* cursor;             // [T] scatter positions
   int* bsum;               // [ceil(T / kPairScanTile)] count sums of the scan's blocks
   int* list;               // [chunk_rows * k] pair ids r * k + j, grouped by key
-  const float* contrib;    // as DkvArgs::contrib
+  const uint16_t* contrib; // as DkvArgs::contrib
   float* dkv;              // [T, 576], added to
 };
 

@@ -252,8 +252,9 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
           *reinterpret_cast<const u32x4*>(a.do_lat + (static_cast<int64_t>(crow) * kDkHeads + h) * kVDim + d0 + 8 * gg);
   }
   __syncthreads();
-  // B operands: part p (0: Q, 1: do_lat), K step ks (heads 16ks .. +16), N tile nt (dims 32nt .. +32 of
-  // the slice); lane: dim 32nt + lane%32, heads 16ks + 8(lane/32) .. +8
+  // B operands: part p (0: Q, 1: do_lat), K step ks (heads 16ks .. +16), N tile nt (the slice's dims of
+  // parity nt); lane: dim 2(lane%32) + nt, heads 16ks + 8(lane/32) .. +8. A lane's two accumulators
+  // then hold two adjacent dims of each key, stored as one bf16 pair.
   const int hh = lane >> 5, col = lane & 31;
   bf16x8 bf[2][6][2];
 #pragma unroll
@@ -265,15 +266,16 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
         u32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int h = 16 * ks + 8 * hh + 2 * i, d = 32 * nt + col;
+          const int h = 16 * ks + 8 * hh + 2 * i, d = 2 * col + nt;
           v[i] = static_cast<uint32_t>(s_x[p][h * kDkDims + d]) | (static_cast<uint32_t>(s_x[p][(h + 1) * kDkDims + d]) << 16);
         }
         bf[p][ks][nt] = __builtin_bit_cast(bf16x8, v);
       }
   const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
-  // contrib is slice-major, [9][chunk rows * k][64]: a tile's 32 pairs fill 8 KB in one piece
+  // contrib is slice-major, [9][chunk rows * k][64] bf16: a tile's 32 pairs fill 4 KB in one piece
   const int64_t npairs = static_cast<int64_t>(a.chunk_rows) * a.k;
-  float* __restrict__ crow_out = a.contrib + (sl * npairs + static_cast<int64_t>(crow) * a.k) * kDkDims + col;
+  uint32_t* __restrict__ crow_out =
+      reinterpret_cast<uint32_t*>(a.contrib + (sl * npairs + static_cast<int64_t>(crow) * a.k) * kDkDims) + col;
   // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); the
   // next tile's are loaded before this tile's products
   const uint16_t* __restrict__ ga0 = grow + static_cast<int64_t>(col) * kGCols + 8 * hh;
@@ -299,18 +301,17 @@ __global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[1][ks], bf[1][ks][nt], acc[nt]);
     }
-    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 32nt + lane%32; pairs without a usable
-    // index are never listed, so their rows are not stored
+    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 2(lane%32) + nt, rounded to bf16 once
+    // (the sum over the 96 heads is FP32); pairs without a usable index are never listed, so their
+    // rows are not stored
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_idx[32 * t + 8 * g + 4 * hh])));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (kk[e] >= 0) {
-          float* dst = crow_out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kDkDims;
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) dst[32 * nt] = acc[nt][4 * g + e];
-        }
+        if (kk[e] >= 0)
+          crow_out[static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * (kDkDims / 2)] =
+              pack_bf16x2(acc[0][4 * g + e], acc[1][4 * g + e]);
       }
     }
 #pragma unroll
@@ -423,40 +424,59 @@ __global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
   if (key >= 0) a.list[atomicAdd(a.cursor + key, 1)] = crow * a.k + j;
 }
 
-// One wave per key: the sum of its pairs' contributions (lane: dims lane + 64m, m < 9, from slice m),
-// four pairs in flight, added to dkv[key].
+// One wave per key: the sum of its pairs' contributions, added to dkv[key]. Each half wave takes every
+// other pair (four in flight), lane l%32 the bf16 pair of dims 64m + 2(l%32), +1 of each slice m; the
+// halves are added at the end.
 __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
   const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (key >= a.T) return;
   const int p0 = a.start[key], p1 = a.start[key + 1];
   if (p0 == p1) return;  // uniform over the wave
-  constexpr int M = kLatent / kWave;  // 9
-  const int64_t slice = static_cast<int64_t>(a.chunk_rows) * a.k * kWave;  // floats per slice
-  float acc[M];
+  constexpr int M = kLatent / kDkDims;  // 9 slices
+  const int half = lane >> 5, col = lane & 31;
+  const int64_t slice = static_cast<int64_t>(a.chunk_rows) * a.k * (kDkDims / 2);  // u32 words per slice
+  const uint32_t* __restrict__ base = reinterpret_cast<const uint32_t*>(a.contrib) + col;
+  float lo[M], hi[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-  int p = p0;
-  for (; p + 4 <= p1; p += 4) {
-    float v[4][M];
+  for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.0f;
+  auto add = [&](uint32_t w, int m) {
+    lo[m] += __uint_as_float(w << 16);
+    hi[m] += __uint_as_float(w & 0xffff0000u);
+  };
+  int p = p0 + half;
+  for (; p + 6 < p1; p += 8) {
+    uint32_t v[4][M];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float* src = a.contrib + static_cast<int64_t>(a.list[p + u]) * kWave + lane;
+      const uint32_t* src = base + static_cast<int64_t>(a.list[p + 2 * u]) * (kDkDims / 2);
 #pragma unroll
       for (int m = 0; m < M; ++m) v[u][m] = src[slice * m];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] += v[u][m];
+      for (int m = 0; m < M; ++m) add(v[u][m], m);
   }
-  for (; p < p1; ++p) {
-    const float* src = a.contrib + static_cast<int64_t>(a.list[p]) * kWave + lane;
+  for (; p < p1; p += 2) {
+    const uint32_t* src = base + static_cast<int64_t>(a.list[p]) * (kDkDims / 2);
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] += src[slice * m];
+    for (int m = 0; m < M; ++m) add(src[slice * m], m);
   }
-  float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + lane;
 #pragma unroll
-  for (int m = 0; m < M; ++m) dst[kWave * m] += acc[m];
+  for (int m = 0; m < M; ++m) {
+    lo[m] += __shfl_xor(lo[m], 32);
+    hi[m] += __shfl_xor(hi[m], 32);
+  }
+  if (half == 0) {
+    float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + 2 * col;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      f32x2 d = *reinterpret_cast<const f32x2*>(dst + kDkDims * m);
+      d[0] += lo[m];
+      d[1] += hi[m];
+      *reinterpret_cast<f32x2*>(dst + kDkDims * m) = d;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
