@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     s_slot = got;
   }
   __syncthreads();
-  const int slot = s_slot;
+  const int slot = __builtin_amdgcn_readfirstlane(s_slot);
   if (slot < 0) {
     if (select)
       for (int j = lane; j < k; j += kWave) out[j] = -1;
@@ -906,12 +906,19 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // take another chunk while the row still has keys after half u raises its flag for the next step.
   auto append = [&](int u, float score, int nbuf) {
     const int s_key = kb + u * kHalf + lane;
-    const uint32_t key = score_key(score);
-    const bool take = select && s_key >= b && s_key <= t && key >= thr;
-    const uint64_t msk = ballot(take);
+    // score_key's order, in fewer instructions: adding +0 turns a -0 score into +0 (one key for both
+    // zeros), then negative scores are complemented and the others get the sign bit
+    const uint32_t su = __float_as_uint(score + 0.0f);
+    const uint32_t key = su ^ (static_cast<uint32_t>(static_cast<int32_t>(su) >> 31) | 0x80000000u);
+    // every key of the block is at or after the document start kb, and half u = -1 (before the first
+    // chunk) takes nothing; bitwise ands keep the lane mask in scalar registers
+    const bool take = select & (u >= 0) & (s_key <= t) & (key >= thr);
+    const uint64_t msk = __builtin_amdgcn_ballot_w64(take);  // the lane mask itself, without a VGPR round trip
     const int pos = take ? cnt + lanes_below(msk) : kCap + lane;
-    ckeys[pos] = key;
-    cidx[pos] = s_key;
+    // 32-bit byte offsets from the lists' wave-uniform bases
+    const uint32_t off = static_cast<uint32_t>(pos) * 4u;
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ckeys) + off) = key;
+    *reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(cidx) + off) = s_key;
     cnt += __popcll(msk);
     const bool more = kb + (u + 1) * kHalf <= t;
     s_need[nbuf][wave] = cnt > kCap - kChunk && more ? cnt : 0;  // every lane writes the same value
