@@ -333,7 +333,7 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 //   do_lat  [chunk rows, H, 512] bf16        do W_UV[h]^T
 //   delta   [chunk rows, H] f32              sum dout * out
 //   g       [chunk rows, g_stride, 2H] bf16  dS' and P of every selected key, for the dkv contraction
-//   contrib [9][chunk rows * k][64] bf16      each (row, selected key)'s dkv contribution, by 64-dim slice
+//   contrib [3][chunk rows * k][192] bf16     each (row, selected key)'s dkv contribution, by 192-dim group
 //   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
 //   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
 constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (2.4 GB at k = 2048)

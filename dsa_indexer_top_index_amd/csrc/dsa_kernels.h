@@ -138,7 +138,7 @@ struct DkvArgs {
   const uint16_t* q;       // [nrows, H, 576]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
   const int32_t* idx;      // [nrows, k]
-  uint16_t* contrib;       // [9][chunk_rows * k][64] bf16: slice s holds dims 64s .. 64s + 63 of pair r * k + j
+  uint16_t* contrib;       // [3][chunk_rows * k][192] bf16: group q holds dims 192q .. 192q + 191 of pair r * k + j
   const int32_t* cu;
   int n_docs;
   int T;

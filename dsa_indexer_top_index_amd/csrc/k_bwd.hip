@@ -20,11 +20,12 @@
 //     in bf16 to LDS, from where waves 2 and 3 store them to the workspace (g) for k_dkv;
 //   - all waves: dq^T += K^T dS'^T on 32x32x16 MFMAs (K^T read transposed from the gathered tile,
 //     the latent dims split over the waves, accumulators kept across the row).
-// k_dkv: dkv rows of the selected keys, dS' Q + P do_lat, contracted over all 96 heads at once, so
-//   that each (key, dim) takes one FP32 atomic add per row (not one per head group): one workgroup
-//   per (row, 64 latent dims), Q and do_lat of its dims held in registers as MFMA operands, dS' and P
-//   streamed from g in 32-key tiles. FP32 atomics run at a fixed rate per lane (about 330 G lane
-//   operations per second on MI355X, whatever their scope or placement), which bounds the backward.
+// k_dkv: the dkv contribution of every (row, selected key) pair, dS' Q + P do_lat contracted over all
+//   96 heads at once, rounded to bf16 and stored per pair (one workgroup per row and 192 latent dims,
+//   Q and do_lat of its dims as MFMA B operands in LDS, dS' and P streamed from g in 32-key tiles).
+//   A counting sort groups the chunk's pairs by key (k_pairs_count, two scan passes,
+//   k_pairs_scatter) and k_dkv_sum adds each key's contributions to dkv, one wave per key: no float
+//   atomics, which run at a fixed rate per lane (about 330 G lane operations per second on MI355X).
 // k_dwuv: dW_UV[h] += o_lat^T do over a chunk of rows, 16 rows per K step staged in LDS in the
 //   forward's tile layout so that both operands are read transposed; partial sums added with atomics.
 #include "dsa_device.h"
@@ -209,115 +210,113 @@ __global__ __launch_bounds__(kBwWaves * kWave, 2) void k_sparse_mla_bwd(BwdArgs 
 }
 
 // ---------------------------------------------------------------------------------------------
-// dkv contributions of one row's selected keys for 64 latent dims:
-//   contrib[j, d] = sum_h dS'[j,h] q[h,d] + P[j,h] do_lat[h,d]  (the second term for d < 512),
-// on 32x32x16 MFMAs with keys as M, dims as N and the 96 heads as K (six K steps per operand pair).
-// Q and do_lat of the workgroup's dims are the B operands, read once (through LDS, transposed) into
-// registers; each wave takes every fourth 32-key tile of the row, its A operands (dS' and P rows of
-// g) loaded straight from global memory, and stores its 32 x 64 results (lane: a dim; 32 consecutive
-// dims of two keys per instruction). k_dkv_reduce adds them up per key.
-constexpr int kDkDims = 64;                 // latent dims per workgroup
-constexpr int kDkSlices = kLatent / kDkDims;  // 9
-constexpr int kDkWaves = 4;
+// k_dkv: the dkv contribution of each (row, selected key) pair over all 96 heads,
+//   contrib(r, j) = dS'[r, j, :] q[r] + P[r, j, :] do_lat[r]   (576 values),
+// rounded to bf16 once after the FP32 sum over the heads. One workgroup of eight waves per (row,
+// group of 192 latent dims); the three groups of a row are dealt to one XCD, so that the row's g
+// comes from HBM once. The group's B operands (q and do_lat of its dims, 96 heads each; do_lat is
+// zero past dim 512) are built once in LDS in MFMA operand order. Each wave takes 32-key tiles: the
+// tile's dS' and P rows of g are the A operands (the next tile's loaded ahead, and loaded once for
+// all 192 dims), over six 32-dim N tiles. N tile nt holds dims 6c + nt (c = lane % 32), so a lane
+// ends with six adjacent dims of each of its keys and stores them as 12 bytes.
+// contrib is [3][chunk rows * k][192] bf16: group, pair r * k + j, dim within the group.
+constexpr int kDkGroups = 3;
+constexpr int kDkGDims = kLatent / kDkGroups;  // 192
+constexpr int kDkNT = kDkGDims / 32;           // 6 N tiles of 32 dims
+constexpr int kDkWaves = 8;
 constexpr int kDkHeads = 96;
+constexpr int kDkKS = kDkHeads / 16;           // 6 K steps of 16 heads
+typedef __attribute__((ext_vector_type(3))) unsigned int u32x3;
 
-__global__ __launch_bounds__(kDkWaves * kWave, 2) void k_dkv(DkvArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[2][kDkHeads * kDkDims];  // Q, do_lat slices [head][dim]
+__global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
+  // fragment (p, ks, nt): 64 lanes x 16 bytes, lane l holding heads 16ks + 8(l/32) .. +8 of dim
+  // 6(l%32) + nt of part p (0: q, 1: do_lat)
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2 * kDkKS * kDkNT * 1024];
+  __shared__ __attribute__((aligned(16))) uint16_t s_nat[kDkHeads * kDkGDims];  // one part, [head][dim]
   __shared__ __attribute__((aligned(16))) int32_t s_idx[kBwMaxIdx + 32];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  // The nine slices of a row go to the same XCD (workgroups are dealt to the eight XCDs in turn),
-  // so that its g rows are read from HBM once and from that XCD's L2 afterwards.
   const int b = blockIdx.x, xcd = b % 8, loc = b / 8;
-  const int crow = (loc / kDkSlices) * 8 + xcd, sl = loc % kDkSlices;
+  const int crow = (loc / kDkGroups) * 8 + xcd, grp = loc % kDkGroups;
   if (crow >= a.chunk_rows) return;  // uniform over the workgroup
   const int r = a.chunk_r0 + crow;
   const int t_row = a.row0 + r;
   const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
   const int ntiles = (keff + 31) / 32;
-  const int d0 = kDkDims * sl;
-  const bool has_v = d0 < kVDim;  // this slice has a P do_lat term
+  const int d0 = kDkGDims * grp;
   const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
   for (int j = threadIdx.x; j < ntiles * 32; j += kDkWaves * kWave) {
     const int v = j < keff ? ix[j] : -1;
     s_idx[j] = (v >= 0 && v < a.T) ? v : -1;
   }
-  // Q[r, :, d0 .. d0 + 64) and do_lat[crow, :, d0 .. +64): 96 x 8 granules each
-  for (int gi = threadIdx.x; gi < kDkHeads * (kDkDims / 8); gi += kDkWaves * kWave) {
-    const int h = gi / (kDkDims / 8), gg = gi % (kDkDims / 8);
-    *reinterpret_cast<u32x4*>(&s_x[0][h * kDkDims + 8 * gg]) =
-        *reinterpret_cast<const u32x4*>(a.q + (static_cast<int64_t>(r) * kDkHeads + h) * kLatent + d0 + 8 * gg);
-    if (has_v)
-      *reinterpret_cast<u32x4*>(&s_x[1][h * kDkDims + 8 * gg]) =
-          *reinterpret_cast<const u32x4*>(a.do_lat + (static_cast<int64_t>(crow) * kDkHeads + h) * kVDim + d0 + 8 * gg);
+  for (int p = 0; p < 2; ++p) {
+    // the part's 96 x 192 values in natural order, 24 granules of 8 dims per head
+    for (int gi = threadIdx.x; gi < kDkHeads * (kDkGDims / 8); gi += kDkWaves * kWave) {
+      const int h = gi / (kDkGDims / 8), gg = gi % (kDkGDims / 8), d = d0 + 8 * gg;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (p == 0)
+        v = *reinterpret_cast<const u32x4*>(a.q + (static_cast<int64_t>(r) * kDkHeads + h) * kLatent + d);
+      else if (d < kVDim)
+        v = *reinterpret_cast<const u32x4*>(a.do_lat + (static_cast<int64_t>(crow) * kDkHeads + h) * kVDim + d);
+      *reinterpret_cast<u32x4*>(&s_nat[h * kDkGDims + 8 * gg]) = v;
+    }
+    __syncthreads();
+    for (int fi = threadIdx.x; fi < kDkKS * kDkNT * kWave; fi += kDkWaves * kWave) {
+      const int ks = fi / (kDkNT * kWave), nt = (fi / kWave) % kDkNT, l = fi % kWave;
+      const int h0 = 16 * ks + 8 * (l >> 5), d = 6 * (l & 31) + nt;
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = static_cast<uint32_t>(s_nat[(h0 + 2 * i) * kDkGDims + d]) |
+               (static_cast<uint32_t>(s_nat[(h0 + 2 * i + 1) * kDkGDims + d]) << 16);
+      *reinterpret_cast<u32x4*>(&s_b[((p * kDkKS + ks) * kDkNT + nt) * 1024 + 16 * l]) = v;
+    }
+    __syncthreads();  // the fragments are complete, and s_nat may be refilled
   }
-  __syncthreads();
-  // B operands: part p (0: Q, 1: do_lat), K step ks (heads 16ks .. +16), N tile nt (the slice's dims of
-  // parity nt); lane: dim 2(lane%32) + nt, heads 16ks + 8(lane/32) .. +8. A lane's two accumulators
-  // then hold two adjacent dims of each key, stored as one bf16 pair.
   const int hh = lane >> 5, col = lane & 31;
-  bf16x8 bf[2][6][2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int ks = 0; ks < 6; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        u32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 16 * ks + 8 * hh + 2 * i, d = 2 * col + nt;
-          v[i] = static_cast<uint32_t>(s_x[p][h * kDkDims + d]) | (static_cast<uint32_t>(s_x[p][(h + 1) * kDkDims + d]) << 16);
-        }
-        bf[p][ks][nt] = __builtin_bit_cast(bf16x8, v);
-      }
+  const uint32_t sb = lds_addr_of(&s_b[0]) + 16 * lane;
   const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
-  // contrib is slice-major, [9][chunk rows * k][64] bf16: a tile's 32 pairs fill 4 KB in one piece
   const int64_t npairs = static_cast<int64_t>(a.chunk_rows) * a.k;
-  uint32_t* __restrict__ crow_out =
-      reinterpret_cast<uint32_t*>(a.contrib + (sl * npairs + static_cast<int64_t>(crow) * a.k) * kDkDims) + col;
-  // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); the
-  // next tile's are loaded before this tile's products
+  uint16_t* __restrict__ out = a.contrib + (grp * npairs + static_cast<int64_t>(crow) * a.k) * kDkGDims + 6 * col;
+  // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); two
+  // waves per SIMD hide each other's loads
   const uint16_t* __restrict__ ga0 = grow + static_cast<int64_t>(col) * kGCols + 8 * hh;
-  bf16x8 af[2][6], an[2][6];
-  auto load_a = [&](int t, bf16x8 (&dst)[2][6]) {
+  for (int t = wave; t < ntiles; t += kDkWaves) {
+    bf16x8 af[2][kDkKS];
     const uint16_t* ga = ga0 + static_cast<int64_t>(32 * t) * kGCols;
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks) dst[p][ks] = *reinterpret_cast<const bf16x8*>(ga + 96 * p + 16 * ks);
-  };
-  if (wave < ntiles) load_a(wave, af);
-  for (int t = wave; t < ntiles; t += kDkWaves) {
-    if (t + kDkWaves < ntiles) load_a(t + kDkWaves, an);
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+      for (int ks = 0; ks < kDkKS; ++ks) af[p][ks] = *reinterpret_cast<const bf16x8*>(ga + 96 * p + 16 * ks);
+    f32x16 acc[kDkNT];
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks)
+    for (int nt = 0; nt < kDkNT; ++nt) acc[nt] = f32x16{};
+    // one K step at a time: its six B fragments from LDS, then its six MFMAs (the fragments of all
+    // twelve steps would not fit in registers beside the accumulators)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[0][ks], bf[0][ks][nt], acc[nt]);
-    if (has_v) {
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks)
+      for (int ks = 0; ks < kDkKS; ++ks) {
+        bf16x8 bv[kDkNT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(af[1][ks], bf[1][ks][nt], acc[nt]);
-    }
-    // element e: key 32t + 8(e/4) + 4(lane/32) + e%4, dim d0 + 2(lane%32) + nt, rounded to bf16 once
-    // (the sum over the 96 heads is FP32); pairs without a usable index are never listed, so their
-    // rows are not stored
+        for (int nt = 0; nt < kDkNT; ++nt) bv[nt] = lds_read16(lds_ptr(sb + ((p * kDkKS + ks) * kDkNT + nt) * 1024));
+#pragma unroll
+        for (int nt = 0; nt < kDkNT; ++nt) acc[nt] = mfma32(af[p][ks], bv[nt], acc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // element 4g + e: key 32t + 8g + 4(lane/32) + e, dims 6(lane%32) .. +6 of the group; pairs
+    // without a usable index are never listed, so they are not stored
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_idx[32 * t + 8 * g + 4 * hh])));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e;
         if (kk[e] >= 0)
-          crow_out[static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * (kDkDims / 2)] =
-              pack_bf16x2(acc[0][4 * g + e], acc[1][4 * g + e]);
+          *reinterpret_cast<u32x3*>(out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kDkGDims) =
+              u32x3{pack_bf16x2(acc[0][i], acc[1][i]), pack_bf16x2(acc[2][i], acc[3][i]), pack_bf16x2(acc[4][i], acc[5][i])};
       }
     }
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int ks = 0; ks < 6; ++ks) af[p][ks] = an[p][ks];
   }
 }
 
@@ -424,58 +423,51 @@ __global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
   if (key >= 0) a.list[atomicAdd(a.cursor + key, 1)] = crow * a.k + j;
 }
 
-// One wave per key: the sum of its pairs' contributions, added to dkv[key]. Each half wave takes every
-// other pair (four in flight), lane l%32 the bf16 pair of dims 64m + 2(l%32), +1 of each slice m; the
-// halves are added at the end.
+// One wave per key: the sum of its pairs' contributions (four pairs in flight; lane l < 48 takes
+// dims 4l .. 4l + 3 of each group), added to dkv[key].
 __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
   const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (key >= a.T) return;
   const int p0 = a.start[key], p1 = a.start[key + 1];
-  if (p0 == p1) return;  // uniform over the wave
-  constexpr int M = kLatent / kDkDims;  // 9 slices
-  const int half = lane >> 5, col = lane & 31;
-  const int64_t slice = static_cast<int64_t>(a.chunk_rows) * a.k * (kDkDims / 2);  // u32 words per slice
-  const uint32_t* __restrict__ base = reinterpret_cast<const uint32_t*>(a.contrib) + col;
-  float lo[M], hi[M];
+  if (p0 == p1 || lane >= kDkGDims / 4) return;
+  const int64_t gstride = static_cast<int64_t>(a.chunk_rows) * a.k * kDkGDims;  // bf16 per group
+  const uint16_t* __restrict__ base = a.contrib + 4 * lane;
+  float acc[kDkGroups][4];
 #pragma unroll
-  for (int m = 0; m < M; ++m) lo[m] = hi[m] = 0.0f;
-  auto add = [&](uint32_t w, int m) {
-    lo[m] += __uint_as_float(w << 16);
-    hi[m] += __uint_as_float(w & 0xffff0000u);
+  for (int q = 0; q < kDkGroups; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[q][i] = 0.0f;
+  auto add = [&](const u32x2& w, int q) {
+    acc[q][0] += __uint_as_float(w[0] << 16);
+    acc[q][1] += __uint_as_float(w[0] & 0xffff0000u);
+    acc[q][2] += __uint_as_float(w[1] << 16);
+    acc[q][3] += __uint_as_float(w[1] & 0xffff0000u);
   };
-  int p = p0 + half;
-  for (; p + 6 < p1; p += 8) {
-    uint32_t v[4][M];
+  int p = p0;
+  for (; p + 4 <= p1; p += 4) {
+    u32x2 v[4][kDkGroups];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t* src = base + static_cast<int64_t>(a.list[p + 2 * u]) * (kDkDims / 2);
+      const uint16_t* src = base + static_cast<int64_t>(a.list[p + u]) * kDkGDims;
 #pragma unroll
-      for (int m = 0; m < M; ++m) v[u][m] = src[slice * m];
+      for (int q = 0; q < kDkGroups; ++q) v[u][q] = *reinterpret_cast<const u32x2*>(src + gstride * q);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int m = 0; m < M; ++m) add(v[u][m], m);
+      for (int q = 0; q < kDkGroups; ++q) add(v[u][q], q);
   }
-  for (; p < p1; p += 2) {
-    const uint32_t* src = base + static_cast<int64_t>(a.list[p]) * (kDkDims / 2);
+  for (; p < p1; ++p) {
+    const uint16_t* src = base + static_cast<int64_t>(a.list[p]) * kDkGDims;
 #pragma unroll
-    for (int m = 0; m < M; ++m) add(src[slice * m], m);
+    for (int q = 0; q < kDkGroups; ++q) add(*reinterpret_cast<const u32x2*>(src + gstride * q), q);
   }
+  float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + 4 * lane;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    lo[m] += __shfl_xor(lo[m], 32);
-    hi[m] += __shfl_xor(hi[m], 32);
-  }
-  if (half == 0) {
-    float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + 2 * col;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      f32x2 d = *reinterpret_cast<const f32x2*>(dst + kDkDims * m);
-      d[0] += lo[m];
-      d[1] += hi[m];
-      *reinterpret_cast<f32x2*>(dst + kDkDims * m) = d;
-    }
+  for (int q = 0; q < kDkGroups; ++q) {
+    f32x4* d = reinterpret_cast<f32x4*>(dst + kDkGDims * q);
+    const f32x4 o = *d;
+    *d = f32x4{o[0] + acc[q][0], o[1] + acc[q][1], o[2] + acc[q][2], o[3] + acc[q][3]};
   }
 }
 
@@ -592,7 +584,7 @@ hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st) {
 
 hipError_t launch_dkv(const DkvArgs& a, hipStream_t st) {
   if (a.chunk_rows <= 0) return hipSuccess;
-  const int blocks = (a.chunk_rows + 7) / 8 * 8 * kDkSlices;
+  const int blocks = (a.chunk_rows + 7) / 8 * 8 * kDkGroups;
   hipLaunchKernelGGL(k_dkv, dim3(blocks), dim3(kDkWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
