@@ -75,6 +75,8 @@ def _load(path):
     L.oracle_q_absorb.argtypes = [i64, p, p, p, i32, p, p]
     L.oracle_o_proj.argtypes = [i64, p, p, i32, i32, p, p]
     L.oracle_sparse_mla_f64in.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, p, p]
+    L.oracle_sparse_mla_f64in_variant.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p]
+    L.oracle_sparse_mla_bwd_variant.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, i32, p, p, p, p, p, p, p]
     L.oracle_sparse_mla_bwd.argtypes = [i64, p, p, i64, p, i32, p, p, i32, d, p, p, p, p, p]
     L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     L.oracle_e4m3_decode.restype = d
@@ -321,9 +323,9 @@ def o_proj(x, W_o, want_f64=False):
 
 # ---- backward (inputs as float64 arrays; bf16 inputs are converted exactly by the caller)
 
-def sparse_mla_f64in(q, kv, idx, W_UV, gate, scale):
-    """Forward with double inputs: q [n,H,576], kv [T,576], idx [n,k], W_UV [H,512,128], gate [n,H].
-    Returns (out [n,H,128], lse [n,H])."""
+def sparse_mla_f64in(q, kv, idx, W_UV, gate, scale, gate_per_dim=False, sink=None):
+    """Forward with double inputs: q [n,H,576], kv [T,576], idx [n,k], W_UV [H,512,128], gate [n,H]
+    (or [n,H,128] with gate_per_dim), sink [H] or None. Returns (out [n,H,128], lse [n,H])."""
     q, pq = _c(q, np.float64)
     kvc, pkv = _c(kv, np.float64)
     ix, pi = _c(idx, np.int32)
@@ -332,13 +334,20 @@ def sparse_mla_f64in(q, kv, idx, W_UV, gate, scale):
     n, H = q.shape[0], q.shape[1]
     out = np.empty((n, H, 128))
     lse = np.empty((n, H))
-    lib().oracle_sparse_mla_f64in(n, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale, out.ctypes.data,
-                                  lse.ctypes.data)
+    if not gate_per_dim and sink is None:
+        lib().oracle_sparse_mla_f64in(n, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale, out.ctypes.data,
+                                      lse.ctypes.data)
+    else:
+        sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+        lib().oracle_sparse_mla_f64in_variant(n, pq, pkv, kvc.shape[0], pi, ix.shape[1], pw, pg, H, scale,
+                                              1 if gate_per_dim else 0, None if sk is None else sk.ctypes.data,
+                                              out.ctypes.data, lse.ctypes.data)
     return out, lse
 
 
-def sparse_mla_bwd(q, kv, idx, W_UV, gate, scale, dout):
-    """Gradients of L = sum(dout * out): returns dict dq [n,H,576], dkv [T,576], dW_UV [H,512,128], dgate [n,H]."""
+def sparse_mla_bwd(q, kv, idx, W_UV, gate, scale, dout, gate_per_dim=False, sink=None):
+    """Gradients of L = sum(dout * out): returns dict dq [n,H,576], dkv [T,576], dW_UV [H,512,128], dgate
+    [n,H] (or [n,H,128] with gate_per_dim) and, with a sink [H], dsink [H]."""
     q, pq = _c(q, np.float64)
     kvc, pkv = _c(kv, np.float64)
     ix, pi = _c(idx, np.int32)
@@ -348,7 +357,16 @@ def sparse_mla_bwd(q, kv, idx, W_UV, gate, scale, dout):
     n, H = q.shape[0], q.shape[1]
     T = kvc.shape[0]
     res = {"dq": np.empty((n, H, 576)), "dkv": np.zeros((T, 576)), "dW_UV": np.zeros((H, 512, 128)),
-           "dgate": np.empty((n, H))}
-    lib().oracle_sparse_mla_bwd(n, pq, pkv, T, pi, ix.shape[1], pw, pg, H, scale, pd, res["dq"].ctypes.data,
-                                res["dkv"].ctypes.data, res["dW_UV"].ctypes.data, res["dgate"].ctypes.data)
+           "dgate": np.empty((n, H, 128) if gate_per_dim else (n, H))}
+    if not gate_per_dim and sink is None:
+        lib().oracle_sparse_mla_bwd(n, pq, pkv, T, pi, ix.shape[1], pw, pg, H, scale, pd, res["dq"].ctypes.data,
+                                    res["dkv"].ctypes.data, res["dW_UV"].ctypes.data, res["dgate"].ctypes.data)
+        return res
+    sk = None if sink is None else np.ascontiguousarray(sink, dtype=np.float64)
+    if sk is not None:
+        res["dsink"] = np.zeros(H)
+    lib().oracle_sparse_mla_bwd_variant(n, pq, pkv, T, pi, ix.shape[1], pw, pg, H, scale, 1 if gate_per_dim else 0,
+                                        None if sk is None else sk.ctypes.data, pd, res["dq"].ctypes.data,
+                                        res["dkv"].ctypes.data, res["dW_UV"].ctypes.data, res["dgate"].ctypes.data,
+                                        None if sk is None else res["dsink"].ctypes.data)
     return res

@@ -500,6 +500,15 @@ void oracle_sparse_mla_f64in(int64_t n_rows, const double* q_rows, const double*
                                   out_f64, nullptr, lse, nullptr);
 }
 
+// The gate and sink variants of the same forward with double inputs (gate [n,H] or [n,H,128]).
+void oracle_sparse_mla_f64in_variant(int64_t n_rows, const double* q_rows, const double* kv, int64_t T,
+                                     const int32_t* idx, int32_t k, const double* W_UV, const double* gate_rows,
+                                     int32_t H, double scale, int32_t gate_per_dim, const double* sink,
+                                     double* out_f64, double* lse) {
+  sparse_mla_impl<double, double>(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, gate_per_dim, sink,
+                                  nullptr, out_f64, nullptr, lse, nullptr);
+}
+
 // Backward of sparse latent attention, the per-head V up-projection and the per-head sigmoid gate
 // ([KC] paragraph after the Implementation Limits bullets: the backward runs the native 96 heads;
 // 3rd bullet: hard top-k carries no gradient, so the indices are constants). For the loss
@@ -510,9 +519,19 @@ void oracle_sparse_mla_f64in(int64_t n_rows, const double* q_rows, const double*
 //   dp_j = do_lat . kv_j[:512];  D = sum_j p_j dp_j;  dl_j = p_j (dp_j - D)
 //   dq = scale sum_j dl_j kv_j (576 dims);  dkv_j += scale dl_j q (576) + p_j do_lat (512)
 // Outputs: dq [n,H,576] and dgate [n,H] (written), dkv [T,576] and dW [H,512,128] (added to).
-void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* kv, int64_t T, const int32_t* idx,
-                           int32_t k, const double* W_UV, const double* gate_rows, int32_t H, double scale,
-                           const double* dout, double* dq, double* dkv, double* dW, double* dgate) {
+//
+// The gate and sink variants ([AD] blueprint entry "Output gate + sink"), as in the forward:
+//  - gate_per_dim = 1: gate [n,H,128], sg_d = sigma(g_d) per output element, so
+//    dgate[d] = sg_d (1 - sg_d) dout[d] o[d] (dgate [n,H,128]) and do[d] = sg_d dout[d];
+//  - sink [H]: the softmax over the keys and the sink logit s (value row zero):
+//    p_j = exp(l_j - m) / z, p_s = exp(s - m) / z, z = sum_j exp(l_j - m) + exp(s - m). o_lat and
+//    D = sum_j p_j dp_j take the keys only (the sink's dp is 0), dl_j = p_j (dp_j - D) as before,
+//    and the sink logit's own gradient is p_s (0 - D): dsink[h] += -p_s D over the rows.
+void oracle_sparse_mla_bwd_variant(int64_t n_rows, const double* q_rows, const double* kv, int64_t T,
+                                   const int32_t* idx, int32_t k, const double* W_UV, const double* gate_rows,
+                                   int32_t H, double scale, int32_t gate_per_dim, const double* sink,
+                                   const double* dout, double* dq, double* dkv, double* dW, double* dgate,
+                                   double* dsink) {
   for (int64_t r = 0; r < n_rows; ++r) {
     std::vector<int64_t> sel;
     for (int32_t j = 0; j < k; ++j) {
@@ -534,19 +553,31 @@ void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* k
       }
       double m = -std::numeric_limits<double>::infinity();
       for (size_t j = 0; j < n; ++j) m = std::max(m, l[j]);
+      if (sink) m = std::max(m, sink[h]);
       double z = 0.0;
       for (size_t j = 0; j < n; ++j) z += std::exp(l[j] - m);
+      if (sink) z += std::exp(sink[h] - m);
       for (size_t j = 0; j < n; ++j) p[j] = std::exp(l[j] - m) / z;
+      const double ps = sink ? std::exp(sink[h] - m) / z : 0.0;
       for (size_t j = 0; j < n; ++j)
         for (int c = 0; c < kDV; ++c) ol[c] += p[j] * kv[sel[j] * kDL + c];
       for (int d = 0; d < kDO; ++d)
         for (int c = 0; c < kDV; ++c) o[d] += ol[c] * Wh[c * kDO + d];
-      const double sg = 1.0 / (1.0 + std::exp(-gate_rows[r * H + h]));
       const double* dorow = dout + (r * H + h) * static_cast<int64_t>(kDO);
-      double dgo = 0.0;
-      for (int d = 0; d < kDO; ++d) dgo += dorow[d] * o[d];
-      dgate[r * H + h] = sg * (1.0 - sg) * dgo;
-      for (int d = 0; d < kDO; ++d) dov[d] = sg * dorow[d];
+      if (gate_per_dim) {
+        for (int d = 0; d < kDO; ++d) {
+          const int64_t at = (r * H + h) * static_cast<int64_t>(kDO) + d;
+          const double sg = 1.0 / (1.0 + std::exp(-gate_rows[at]));
+          dgate[at] = sg * (1.0 - sg) * dorow[d] * o[d];
+          dov[d] = sg * dorow[d];
+        }
+      } else {
+        const double sg = 1.0 / (1.0 + std::exp(-gate_rows[r * H + h]));
+        double dgo = 0.0;
+        for (int d = 0; d < kDO; ++d) dgo += dorow[d] * o[d];
+        dgate[r * H + h] = sg * (1.0 - sg) * dgo;
+        for (int d = 0; d < kDO; ++d) dov[d] = sg * dorow[d];
+      }
       double* dWh = dW + static_cast<int64_t>(h) * kDV * kDO;
       for (int c = 0; c < kDV; ++c)
         for (int d = 0; d < kDO; ++d) {
@@ -560,6 +591,7 @@ void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* k
         dp[j] = acc;
         D += p[j] * acc;
       }
+      if (sink) dsink[h] += -ps * D;  // one iteration per head: no other thread writes dsink[h]
       double* dqh = dq + (r * H + h) * static_cast<int64_t>(kDL);
       for (int i = 0; i < kDL; ++i) dqh[i] = 0.0;
       for (size_t j = 0; j < n; ++j) {
@@ -576,6 +608,14 @@ void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* k
       for (size_t j = 0; j < n; ++j)
         for (int i = 0; i < kDL; ++i) dkv[sel[j] * kDL + i] += dkv_h[(static_cast<size_t>(h) * n + j) * kDL + i];
   }
+}
+
+// The per-head gate without a sink (the backward the GPU path computes by default).
+void oracle_sparse_mla_bwd(int64_t n_rows, const double* q_rows, const double* kv, int64_t T, const int32_t* idx,
+                           int32_t k, const double* W_UV, const double* gate_rows, int32_t H, double scale,
+                           const double* dout, double* dq, double* dkv, double* dW, double* dgate) {
+  oracle_sparse_mla_bwd_variant(n_rows, q_rows, kv, T, idx, k, W_UV, gate_rows, H, scale, 0, nullptr, dout, dq, dkv,
+                                dW, dgate, nullptr);
 }
 
 // Dense-mask reference ([KC] Implementation Limits 1st bullet: the eager/sdpa paths are

@@ -791,6 +791,68 @@ def test_backward_inner_product_identities():
     assert abs((bad * kv).sum() - (g["dq"] * q).sum() - D.sum()) > 1e-6 * np.abs(D).sum()
 
 
+@pytest.mark.parametrize("gate_per_dim,with_sink", [(True, False), (False, True), (True, True)])
+def test_backward_variants_against_finite_differences(gate_per_dim, with_sink):
+    """The gate and sink variants of the backward: directional derivatives of L = sum(dout * out) by
+    central differences of the oracle's own variant forward (double inputs) equal the gradients, for
+    q, kv, W_UV, the gate ([n,H,128] when per element) and the sink logits."""
+    n, H, T, k = 3, 4, 20, 7
+    q, kv, idx, W, gate, dout = _bwd_case(54, n, H, T, k)
+    rng = np.random.default_rng(8)
+    if gate_per_dim:
+        gate = rng.standard_normal((n, H, 128))
+    sink = rng.standard_normal(H) if with_sink else None
+    scale = 1 / math.sqrt(192)
+    g = oracle.sparse_mla_bwd(q, kv, idx, W, gate, scale, dout, gate_per_dim=gate_per_dim, sink=sink)
+    assert g["dgate"].shape == gate.shape and (("dsink" in g) == with_sink)
+
+    def L(q_, kv_, W_, g_, s_):
+        return float((oracle.sparse_mla_f64in(q_, kv_, idx, W_, g_, scale, gate_per_dim, s_)[0] * dout).sum())
+    eps = 1e-6
+    args = {"q": q, "kv": kv, "W_UV": W, "gate": gate, "sink": sink}
+    grads = [("q", g["dq"]), ("kv", g["dkv"]), ("W_UV", g["dW_UV"]), ("gate", g["dgate"])]
+    if with_sink:
+        grads.append(("sink", g["dsink"]))
+    for name, grad in grads:
+        v = rng.standard_normal(args[name].shape)
+        plus, minus = dict(args), dict(args)
+        plus[name], minus[name] = args[name] + eps * v, args[name] - eps * v
+        fd = (L(plus["q"], plus["kv"], plus["W_UV"], plus["gate"], plus["sink"])
+              - L(minus["q"], minus["kv"], minus["W_UV"], minus["gate"], minus["sink"])) / (2 * eps)
+        an = float((grad * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3), (name, fd, an)
+
+
+def test_backward_sink_against_torch_autograd():
+    """Library cross-check of the sink and per-element gate: torch autograd in float64 on a dense
+    formulation (the sink as one more softmax logit with a zero value row)."""
+    n, H, T, k = 4, 8, 30, 9
+    q, kv, idx, W, _, dout = _bwd_case(55, n, H, T, k)
+    rng = np.random.default_rng(9)
+    gate = rng.standard_normal((n, H, 128))
+    sink = rng.standard_normal(H)
+    scale = 1 / math.sqrt(192)
+    g = oracle.sparse_mla_bwd(q, kv, idx, W, gate, scale, dout, gate_per_dim=True, sink=sink)
+    tq = torch.tensor(q, requires_grad=True)
+    tkv = torch.tensor(kv, requires_grad=True)
+    tW = torch.tensor(W, requires_grad=True)
+    tg_ = torch.tensor(gate, requires_grad=True)
+    ts = torch.tensor(sink, requires_grad=True)
+    outs = []
+    for r in range(n):
+        sel = [int(s) for s in idx[r] if 0 <= s < T]
+        K = tkv[sel]
+        l = scale * torch.einsum("hi,mi->hm", tq[r], K)
+        p = torch.softmax(torch.cat([l, ts[:, None]], dim=1), dim=1)[:, :-1]   # the sink takes its share
+        o = torch.einsum("hc,hcd->hd", p @ K[:, :512], tW)
+        outs.append(torch.sigmoid(tg_[r]) * o)
+    (torch.stack(outs) * torch.tensor(dout)).sum().backward()
+    for name, ref, got in [("dq", tq.grad, g["dq"]), ("dkv", tkv.grad, g["dkv"]), ("dW_UV", tW.grad, g["dW_UV"]),
+                           ("dgate", tg_.grad, g["dgate"]), ("dsink", ts.grad, g["dsink"])]:
+        ref = ref.numpy()
+        assert np.abs(ref - got).max() <= 1e-12 * max(np.abs(ref).max(), 1e-30), name
+
+
 def test_backward_against_torch_autograd():
     """Library cross-check: torch autograd in float64 on a dense gathered formulation of the same
     forward gives the same gradients."""
