@@ -336,10 +336,12 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 //   contrib [3][chunk rows * k][192] bf16     each (row, selected key)'s dkv contribution, by 192-dim group
 //   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
 //   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
+//   sterm   [chunk rows, H] f32             with a sink: each (row, head)'s term of the sink's gradient
 constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (2.4 GB at k = 2048)
 
 struct BwdLayout {
-  size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off, total;
+  size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off,
+      sterm_off, total;
   int g_stride;
   int64_t chunk_rows;
 };
@@ -362,7 +364,8 @@ static BwdLayout bwd_layout_of(const dsa_shape* s) {
   B.cursor_off = B.start_off + align_up((static_cast<size_t>(s->T) + 1) * 4);
   B.list_off = B.cursor_off + align_up(static_cast<size_t>(s->T) * 4);
   B.bsum_off = B.list_off + align_up(crows * s->topk * 4);
-  B.total = B.bsum_off + align_up((static_cast<size_t>(s->T) + dsa::kPairScanTile - 1) / dsa::kPairScanTile * 4);
+  B.sterm_off = B.bsum_off + align_up((static_cast<size_t>(s->T) + dsa::kPairScanTile - 1) / dsa::kPairScanTile * 4);
+  B.total = B.sterm_off + align_up(cr * 4);
   return B;
 }
 
@@ -371,10 +374,10 @@ size_t dsa_bwd_workspace_size(const dsa_shape* s) {
   return bwd_layout_of(s).total;
 }
 
-dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
-                              const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out, const float* lse,
-                              const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate, void* ws,
-                              size_t ws_bytes, void* stream) {
+static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
+                          const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out,
+                          const float* lse, const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate,
+                          float* dsink, void* ws, size_t ws_bytes, void* stream) {
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (s->H != 96) return DSA_ERR_UNSUPPORTED;
@@ -384,6 +387,11 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
       !aligned(out, 16) || !aligned(lse, 4) || !aligned(dout, 16) || !aligned(dq, 4) || !aligned(dkv, 4) ||
       !aligned(dW_UV, 4) || !aligned(dgate, 4))
     return DSA_ERR_INVALID_ARG;
+  if ((st = check_variant(v, gate)) != DSA_OK) return st;
+  const bool per_dim = v && v->gate_per_dim;
+  const float* sink = v ? v->sink : nullptr;
+  if (per_dim && !aligned(dgate, 16)) return DSA_ERR_INVALID_ARG;
+  if ((sink != nullptr) != (dsink != nullptr) || (dsink && !aligned(dsink, 4))) return DSA_ERR_INVALID_ARG;
   const BwdLayout B = bwd_layout_of(s);
   if (ws == nullptr || ws_bytes < B.total) return DSA_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return DSA_ERR_INVALID_ARG;
@@ -401,14 +409,21 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
   int* cursor = reinterpret_cast<int*>(base + B.cursor_off);
   int* list = reinterpret_cast<int*>(base + B.list_off);
   int* bsum = reinterpret_cast<int*>(base + B.bsum_off);
+  float* sterm = reinterpret_cast<float*>(base + B.sterm_off);
   if (dsa::launch_fill_zero(dkv, static_cast<int64_t>(s->T) * 576, hs) != hipSuccess ||
-      dsa::launch_fill_zero(dW_UV, static_cast<int64_t>(s->H) * 512 * 128, hs) != hipSuccess)
+      dsa::launch_fill_zero(dW_UV, static_cast<int64_t>(s->H) * 512 * 128, hs) != hipSuccess ||
+      (dsink && dsa::launch_fill_zero(dsink, s->H, hs) != hipSuccess))
     return DSA_ERR_LAUNCH;
   const int64_t rows = rows_of(s);
   for (int64_t c0 = 0; c0 < rows; c0 += B.chunk_rows) {
     const int n = static_cast<int>(std::min<int64_t>(B.chunk_rows, rows - c0));
-    dsa::BwdPrepArgs p{dout, out, gate, d_o, delta, dgate, n, s->H, static_cast<int>(c0)};
+    dsa::BwdPrepArgs p{dout, out, gate, d_o, delta, dgate, n, s->H, static_cast<int>(c0), per_dim ? 1 : 0, sink, lse,
+                       sterm};
     if (dsa::launch_bwd_prep(p, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (sink) {
+      dsa::SinkSumArgs ss{sterm, dsink, n, s->H};
+      if (dsa::launch_sink_sum(ss, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    }
     dsa::AbsorbArgs ab{d_o, nullptr, W_UV, dolat, n, s->H, 512};  // do_lat = do W_UV[h]^T
     if (dsa::launch_q_absorb(ab, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     dsa::BwdArgs b{};
@@ -437,12 +452,28 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
     dsa::DkvListArgs dl{topk_idx, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
                         count, start, cursor, bsum, list, contrib, dkv};
     if (dsa::launch_dkv_reduce(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
-    // o_lat of the chunk again (the forward's attention kernel), for dW_UV
-    if ((st = launch_attention(s, nullptr, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
+    // o_lat of the chunk again (the forward's attention kernel, with the sink if any), for dW_UV
+    if ((st = launch_attention(s, v, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
     dsa::DwArgs dw{olat, d_o, dW_UV, n, s->H};
     if (dsa::launch_dwuv(dw, hs) != hipSuccess) return DSA_ERR_LAUNCH;
   }
   return DSA_OK;
+}
+
+dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint16_t* kv, const int32_t* topk_idx,
+                              const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out, const float* lse,
+                              const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return run_bwd(s, nullptr, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, nullptr, ws,
+                 ws_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_bwd_ex(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
+                                 const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
+                                 const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
+                                 float* dW_UV, float* dgate, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  return run_bwd(s, v, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, dsink, ws, ws_bytes,
+                 stream);
 }
 
 dsa_status dsa_quantize_fp8(int64_t n_rows, const uint16_t* x, uint8_t* q8, float* scale, void* stream) {

@@ -100,13 +100,25 @@ struct GemmArgs {
 struct BwdPrepArgs {
   const uint16_t* dout;  // [nrows, H, 128] bf16, caller rows
   const uint16_t* out;   // [nrows, H, 128] bf16, the forward's output
-  const uint16_t* gate;  // [nrows, H] bf16
+  const uint16_t* gate;  // [nrows, H] bf16, or [nrows, H, 128] with gate_per_dim
   uint16_t* d_o;         // [rows, H, 128] bf16, chunk-local: sigma(g) dout
   float* delta;          // [rows, H], chunk-local: sum_d dout * out
-  float* dgate;          // [nrows, H], caller rows
+  float* dgate;          // [nrows, H] (or [nrows, H, 128]), caller rows
   int rows;              // rows of this chunk
   int H;
   int row_off;           // first caller row of the chunk
+  int gate_per_dim;
+  const float* sink;     // [H] or nullptr
+  const float* lse;      // [nrows, H], caller rows (read with a sink)
+  float* sterm;          // [rows, H], chunk-local, with a sink: -exp(sink - lse) * delta
+};
+
+// dsink[h] += sum over the chunk's rows of sterm[row, h]: one workgroup per head.
+struct SinkSumArgs {
+  const float* sterm;    // [rows, H]
+  float* dsink;          // [H], added to
+  int rows;
+  int H;
 };
 
 struct BwdArgs {
@@ -198,6 +210,7 @@ hipError_t launch_dkv(const DkvArgs& a, hipStream_t st);
 // count[key] = pairs of the chunk selecting key; start = exclusive scan (and cursor = start);
 // list = pair ids grouped by key; dkv[key] += the sum of the key's contributions. Four launches.
 hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st);
+hipError_t launch_sink_sum(const SinkSumArgs& a, hipStream_t st);
 hipError_t launch_dwuv(const DwArgs& a, hipStream_t st);
 
 }  // namespace dsa

@@ -60,13 +60,43 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a) {
   float D = (d4[0] * o4[0] + d4[1] * o4[1]) + (d4[2] * o4[2] + d4[3] * o4[3]);
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) D += __shfl_xor(D, o, 32);
-  const float sg = 1.0f / (1.0f + __expf(-bf16_to_f32(a.gate[grh])));
-  const u32x2 dov = {pack_bf16x2(sg * d4[0], sg * d4[1]), pack_bf16x2(sg * d4[2], sg * d4[3])};
+  float sg[4];
+  if (a.gate_per_dim) {
+    // one gate logit per output element: dgate = (1 - sigma) dout out, element by element
+    const u32x2 gv = *reinterpret_cast<const u32x2*>(a.gate + grh * kODim + 4 * sub);
+    const float g4[4] = {bf16_to_f32(static_cast<uint16_t>(gv[0])), bf16_to_f32(static_cast<uint16_t>(gv[0] >> 16)),
+                         bf16_to_f32(static_cast<uint16_t>(gv[1])), bf16_to_f32(static_cast<uint16_t>(gv[1] >> 16))};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sg[i] = 1.0f / (1.0f + __expf(-g4[i]));
+    *reinterpret_cast<f32x4*>(a.dgate + grh * kODim + 4 * sub) =
+        f32x4{(1.0f - sg[0]) * d4[0] * o4[0], (1.0f - sg[1]) * d4[1] * o4[1], (1.0f - sg[2]) * d4[2] * o4[2],
+              (1.0f - sg[3]) * d4[3] * o4[3]};
+  } else {
+    const float s1 = 1.0f / (1.0f + __expf(-bf16_to_f32(a.gate[grh])));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sg[i] = s1;
+    if (sub == 0) a.dgate[grh] = (1.0f - s1) * D;
+  }
+  const u32x2 dov = {pack_bf16x2(sg[0] * d4[0], sg[1] * d4[1]), pack_bf16x2(sg[2] * d4[2], sg[3] * d4[3])};
   *reinterpret_cast<u32x2*>(a.d_o + rh * kODim + 4 * sub) = dov;
   if (sub == 0) {
     a.delta[rh] = D;
-    a.dgate[grh] = (1.0f - sg) * D;
+    // the sink logit's share of the softmax, exp(sink - lse), times its gradient 0 - D
+    if (a.sink) a.sterm[rh] = -__expf(a.sink[rh % a.H] - a.lse[grh]) * D;
   }
+}
+
+// dsink[h] += the chunk's sterm[:, h], summed in a fixed order (one workgroup per head).
+__global__ __launch_bounds__(256) void k_sink_sum(SinkSumArgs a) {
+  __shared__ float s_part[4];
+  const int h = blockIdx.x;
+  float sum = 0.0f;
+  for (int r = threadIdx.x; r < a.rows; r += 256) sum += a.sterm[static_cast<int64_t>(r) * a.H + h];
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (threadIdx.x % kWave == 0) s_part[threadIdx.x / kWave] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) a.dsink[h] += (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
@@ -555,6 +585,12 @@ __global__ __launch_bounds__(kDwWaves * kWave, 1) void k_dwuv(DwArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+hipError_t launch_sink_sum(const SinkSumArgs& a, hipStream_t st) {
+  if (a.rows <= 0 || a.H <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sink_sum, dim3(static_cast<unsigned>(a.H)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t st) {
   const int64_t n = static_cast<int64_t>(a.rows) * a.H;
   if (n <= 0) return hipSuccess;

@@ -221,14 +221,29 @@ dsa_status dsa_o_proj(const dsa_shape* shape, const uint16_t* x, const uint16_t*
  * W_UV and gate, given that call's out [rows, H, 128] and lse [rows, H]:
  *   dq [rows, H, 576], dkv [T, 576], dW_UV [H, 512, 128], dgate [rows, H], all float32.
  * dkv and dW_UV are overwritten (zeroed, then accumulated over the rows in an order that atomic
- * operations decide, so their last bits may differ from call to call); dq and dgate are written. H must be 96 (else
- * DSA_ERR_UNSUPPORTED). Workspace: >= dsa_bwd_workspace_size(shape) bytes. */
+ * operations decide, so their last bits may differ from call to call); dq and dgate are written.
+ * H must be 96 (else DSA_ERR_UNSUPPORTED). Workspace: >= dsa_bwd_workspace_size(shape) bytes. */
 size_t dsa_bwd_workspace_size(const dsa_shape* shape);
 dsa_status dsa_sparse_mla_bwd(const dsa_shape* shape, const uint16_t* q, const uint16_t* kv,
                               const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
                               const uint16_t* out, const float* lse, const uint16_t* dout, float* dq,
                               float* dkv, float* dW_UV, float* dgate, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* The same backward for the gate and sink variants of dsa_sparse_mla_fwd_ex (archdiff.com blueprint,
+ * "Output gate + sink"), given that call's out and lse (which includes the sink):
+ *   - variant->gate_per_dim = 1: gate [rows, H, 128] (16-byte aligned) and dgate [rows, H, 128]
+ *     (16-byte aligned), dgate = (1 - sigmoid(gate)) * dout * out element by element;
+ *   - variant->sink [H]: dsink [H] float32 receives dL/dsink[h] = -sum over rows of
+ *     exp(sink[h] - lse) * sum_d dout * out (the sink is a softmax logit with a zero value row);
+ *     dsink must be NULL without a sink and non-NULL with one (else DSA_ERR_INVALID_ARG).
+ * A NULL variant is dsa_sparse_mla_bwd. dsink is overwritten (summed over the rows in a fixed
+ * order). Workspace as dsa_sparse_mla_bwd. */
+dsa_status dsa_sparse_mla_bwd_ex(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q,
+                                 const uint16_t* kv, const int32_t* topk_idx, const uint16_t* W_UV,
+                                 const uint16_t* gate, const uint16_t* out, const float* lse,
+                                 const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate,
+                                 float* dsink, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);

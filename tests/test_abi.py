@@ -22,7 +22,8 @@ def test_library_exports_every_declared_symbol():
     assert names == ["dsa_bwd_workspace_size", "dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
                      "dsa_index_topk_fp8", "dsa_index_topk_fused_ln", "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb",
                      "dsa_quantize_fp8",
-                     "dsa_sparse_attention_latent", "dsa_sparse_mla_bwd", "dsa_sparse_mla_fwd", "dsa_sparse_mla_fwd_ex",
+                     "dsa_sparse_attention_latent", "dsa_sparse_mla_bwd", "dsa_sparse_mla_bwd_ex", "dsa_sparse_mla_fwd",
+                     "dsa_sparse_mla_fwd_ex",
                      "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
     for n in names:
@@ -221,18 +222,19 @@ def test_backward_host_checks():
     # the forward's workspace, then per chunk of (here all) 1,024 rows: do, do_lat, delta, g (dS' and P
     # of the 96 heads for every selected key, k rounded up to 32), the bf16 dkv contribution of every
     # (row, selected key) pair, and the counting sort of the pairs by key (count, start, cursor, list, and
-    # the scan's sums over tiles of 4,096 keys)
+    # the scan's sums over tiles of 4,096 keys), and the sink's per-(row, head) gradient terms
     al = lambda x: (x + 255) // 256 * 256
     cr, g_stride, T, k = 1024 * 96, (s.topk + 31) // 32 * 32, s.T, s.topk
     assert nb == (dsa.dsa_workspace_size(s) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4)
                   + al(1024 * g_stride * 192 * 2) + al(1024 * k * 576 * 2) + al(T * 4) + al((T + 1) * 4)
-                  + al(T * 4) + al(1024 * k * 4) + al((T + 4095) // 4096 * 4))
+                  + al(T * 4) + al(1024 * k * 4) + al((T + 4095) // 4096 * 4) + al(cr * 4))
     # longer inputs are taken in chunks of 1,024 rows, so the chunk regions stop growing there
     s2 = _shape(T=4096)
     g2 = (s2.topk + 31) // 32 * 32
     assert L.dsa_bwd_workspace_size(ctypes.byref(s2)) == (
         dsa.dsa_workspace_size(s2) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4) + al(1024 * g2 * 192 * 2)
-        + al(1024 * s2.topk * 576 * 2) + al(4096 * 4) + al(4097 * 4) + al(4096 * 4) + al(1024 * s2.topk * 4) + al(4))
+        + al(1024 * s2.topk * 576 * 2) + al(4096 * 4) + al(4097 * 4) + al(4096 * 4) + al(1024 * s2.topk * 4) + al(4)
+        + al(cr * 4))
     args = [fake] * 12
     assert L.dsa_sparse_mla_bwd(ctypes.byref(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)), *args, fake, nb,
                                 None) == dsa.DSA_ERR_UNSUPPORTED
@@ -240,3 +242,16 @@ def test_backward_host_checks():
     bad = list(args)
     bad[7] = None  # dout
     assert L.dsa_sparse_mla_bwd(ctypes.byref(s), *bad, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
+    # the variant form: a sink needs dsink and dsink needs a sink; a per-element dgate must be 16-byte aligned
+    var = dsa.Variant()
+    var.gate_per_dim, var.sink = 0, fake
+    assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, None, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
+    var.sink = None
+    assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, fake, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
+    var.gate_per_dim = 1
+    odd = list(args)
+    odd[11] = fake + 4  # dgate
+    assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *odd, None, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
+    var.gate_per_dim = 2
+    assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, None, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
+    assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, None, fake, nb - 1, None) == dsa.DSA_ERR_INVALID_ARG

@@ -76,6 +76,60 @@ def test_backward_after_fused_forward(case):
     _compare(case, got, inp, res["topk_idx"].cpu().numpy(), dout, cfg)
 
 
+def _bwd_sink(H):
+    s = np.random.default_rng(6).normal(0, 1, H)  # comparable with the logits: the sink takes a real share
+    s[0] = 60.0     # far above every logit: the forward's rescaled branch, the keys keep almost no weight
+    s[1] = -1.0e4   # no effect: its gradient is exactly 0
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", ["gate-per-dim", "sink", "both"])
+def test_backward_variants(mode):
+    """The backward of the gate and sink variants (dsa_sparse_mla_bwd_ex) after dsa_fused_fwd_ex on two
+    packed documents: every gradient, dsink included, against the oracle's variant backward."""
+    cfg = tg.Config("bwd-var", 104, [600, 200], topk=128, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                    W_UV_std=0.02)
+    T, H = cfg.T, cfg.H
+    per_dim, with_sink = mode != "sink", mode != "gate-per-dim"
+    _say(f"[gpu] backward variant {mode}: T={T} docs={cfg.n_docs} k={cfg.topk}")
+    inp = tg.make_inputs(cfg)
+    gate = tg.normal_bf16(cfg.seed, 50, 0, T * H * 128, 1.0).reshape(T, H, 128) if per_dim else inp["gate"]
+    sink = _bwd_sink(H) if with_sink else None
+    dev = gu.to_device(dict(inp, gate=gate))
+    shape = gu.shape_of(cfg, dev["cu_seqlens"])
+    ws = dsa.alloc_workspace(shape)
+    idx_t = torch.empty((T, cfg.topk), dtype=torch.int32, device="cuda")
+    out_t = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    sink_t = torch.from_numpy(sink).cuda() if with_sink else None
+    dsa.dsa_fused_fwd_ex(shape, dev["q_I"], dev["k_I"], dev["w"], dev["q"], dev["kv"], dev["W_UV"], dev["gate"], idx_t,
+                         out_t, ws, lse=lse_t, gate_per_dim=per_dim, sink=sink_t)
+    dout = tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128)
+    wsb = dsa.alloc_bwd_workspace(shape)
+    dq = torch.empty((T, H, 576), dtype=torch.float32, device="cuda")
+    dkv = torch.empty((T, 576), dtype=torch.float32, device="cuda")
+    dW = torch.empty((H, 512, 128), dtype=torch.float32, device="cuda")
+    dg = torch.empty(gate.shape, dtype=torch.float32, device="cuda")
+    dsink = torch.empty(H, dtype=torch.float32, device="cuda") if with_sink else None
+    dsa.dsa_sparse_mla_bwd_ex(shape, dev["q"], dev["kv"], idx_t, dev["W_UV"], dev["gate"], out_t, lse_t,
+                              gu.bf16_np_to_tensor(dout), dq, dkv, dW, dg, wsb, gate_per_dim=per_dim, sink=sink_t,
+                              dsink=dsink)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_mla_bwd(_f64(inp["q"]), _f64(inp["kv"]), idx_t.cpu().numpy(), _f64(inp["W_UV"]), _f64(gate),
+                                cfg.softmax_scale, _f64(dout), gate_per_dim=per_dim,
+                                sink=sink.astype(np.float64) if with_sink else None)
+    got = {"dq": dq.cpu().numpy(), "dkv": dkv.cpu().numpy(), "dW_UV": dW.cpu().numpy(), "dgate": dg.cpu().numpy()}
+    if with_sink:
+        got["dsink"] = dsink.cpu().numpy()
+        assert got["dsink"][1] == 0.0
+    msgs = []
+    for k in got:
+        ok, err, mx = check_outputs(got[k], ref[k])
+        msgs.append(f"{k} {err / mx:.2e}")
+        assert ok, (mode, k, err, mx)
+    _say(f"[gpu] backward variant {mode}: max error / max |ref|: " + ", ".join(msgs))
+
+
 def test_backward_caller_indices():
     """Caller indices with duplicates, -1 and out-of-range entries, and a row with no usable index."""
     cfg = tg.Config("bwd-idx", 103, [400], topk=64, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
