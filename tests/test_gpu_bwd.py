@@ -59,10 +59,14 @@ def _compare(name, got, inp, idx, dout, cfg):
     _say(f"[gpu] backward {name}: max error / max |ref|: " + ", ".join(msgs))
 
 
-@pytest.mark.parametrize("case", ["single", "packed"])
+@pytest.mark.parametrize("case", ["single", "packed", "odd-k"])
 def test_backward_after_fused_forward(case):
     if case == "single":
         cfg = tg.Config("bwd", 101, [700], topk=256, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24, W_UV_std=0.02)
+    elif case == "odd-k":
+        # k = 100: the last 32-key tile of a full row reaches past k (the next row's pairs)
+        cfg = tg.Config("bwd-oddk", 105, [500], topk=100, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                        W_UV_std=0.02)
     else:
         cfg = tg.Config("bwd-packed", 102, [300, 1, 40, 500], topk=128, H=96, H_I=64, d_I=128, w_scale=1 / 8,
                         q_std=1 / 24, W_UV_std=0.02)
