@@ -325,8 +325,6 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
   return dsa::launch_gemm_nt(g, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH;
 }
 
-// Backward workspace: the forward's layout, then for one row chunk do [rows, H, 128] bf16,
-// do_lat [rows, H, 512] bf16 and D [rows, H] f32 (the o_lat region holds the recomputed o_lat).
 // Backward workspace: the forward's regions (o_lat is recomputed into its region), then per row chunk
 // of at most kBwdChunkRows rows
 //   do      [chunk rows, H, 128] bf16        sigma(g) dout
@@ -337,7 +335,7 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 //   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
 //   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
 //   sterm   [chunk rows, H] f32             with a sink: each (row, head)'s term of the sink's gradient
-constexpr int64_t kBwdChunkRows = 1024;  // bounds contrib (2.4 GB at k = 2048)
+constexpr int64_t kBwdChunkRows = 2048;  // bounds contrib (4.8 GB at k = 2048)
 
 struct BwdLayout {
   size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off,

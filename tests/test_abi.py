@@ -228,13 +228,13 @@ def test_backward_host_checks():
     assert nb == (dsa.dsa_workspace_size(s) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4)
                   + al(1024 * g_stride * 192 * 2) + al(1024 * k * 576 * 2) + al(T * 4) + al((T + 1) * 4)
                   + al(T * 4) + al(1024 * k * 4) + al((T + 4095) // 4096 * 4) + al(cr * 4))
-    # longer inputs are taken in chunks of 1,024 rows, so the chunk regions stop growing there
-    s2 = _shape(T=4096)
-    g2 = (s2.topk + 31) // 32 * 32
+    # longer inputs are taken in chunks of 2,048 rows, so the chunk regions stop growing there
+    s2 = _shape(T=8192)
+    g2, c2, T2 = (s2.topk + 31) // 32 * 32, 2048 * 96, 8192
     assert L.dsa_bwd_workspace_size(ctypes.byref(s2)) == (
-        dsa.dsa_workspace_size(s2) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4) + al(1024 * g2 * 192 * 2)
-        + al(1024 * s2.topk * 576 * 2) + al(4096 * 4) + al(4097 * 4) + al(4096 * 4) + al(1024 * s2.topk * 4) + al(4)
-        + al(cr * 4))
+        dsa.dsa_workspace_size(s2) + al(c2 * 128 * 2) + al(c2 * 512 * 2) + al(c2 * 4) + al(2048 * g2 * 192 * 2)
+        + al(2048 * s2.topk * 576 * 2) + al(T2 * 4) + al((T2 + 1) * 4) + al(T2 * 4) + al(2048 * s2.topk * 4)
+        + al((T2 + 4095) // 4096 * 4) + al(c2 * 4))
     args = [fake] * 12
     assert L.dsa_sparse_mla_bwd(ctypes.byref(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)), *args, fake, nb,
                                 None) == dsa.DSA_ERR_UNSUPPORTED
