@@ -138,7 +138,7 @@ struct BwdArgs {
   int chunk_r0;
   int chunk_rows;
   int k;
-  int H;                   // a multiple of 32
+  int H;                   // 96
   float scale;
 };
 

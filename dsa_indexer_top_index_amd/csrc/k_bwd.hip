@@ -11,15 +11,15 @@
 //   dW_UV[h] += o_lat^T do                           (o_lat recomputed by the forward kernel)
 //
 // k_bwd_prep: D, dgate and do, half a wave per (row, head).
-// k_sparse_mla_bwd: one workgroup per (row, group of 32 heads), four waves. Per 16-key tile of the
-//   row's selected keys (gathered into LDS with the forward's tile layout, one tile ahead):
-//   - waves 0 and 1 recompute S^T (16 keys x 16 heads each, K = 576) with their q fragments in
-//     registers; waves 2 and 3 compute dP^T = V do_lat^T (K = 512) with do_lat fragments in registers
-//     and pass it through LDS;
-//   - waves 0 and 1 form P = 2^(scale log2e S - log2e lse) and dS' = scale P (dP - D) and write both
-//     in bf16 to LDS, from where waves 2 and 3 store them to the workspace (g) for k_dkv;
-//   - all waves: dq^T += K^T dS'^T on 32x32x16 MFMAs (K^T read transposed from the gathered tile,
-//     the latent dims split over the waves, accumulators kept across the row).
+// k_sparse_mla_bwd_row: one workgroup per row and all 96 heads, eight waves. Per 16-key tile of the
+//   row's selected keys (gathered into LDS with the forward's tile layout, two tiles ahead):
+//   - six compute waves of 16 heads recompute S^T (K = 576) and dP^T = V do_lat^T (K = 512) on the
+//     same K fragments, with q and do_lat fragments in registers, then form P = 2^(scale log2e S -
+//     log2e lse) and dS' = scale P (dP - D) in bf16 in LDS and store them to the workspace (g) for
+//     k_dkv;
+//   - two copy waves issue the gathers;
+//   - every wave adds dq^T += K^T dS'^T for its share of the 32x32 tiles, one tile behind (K^T read
+//     transposed from the gathered tile, accumulators kept across the row).
 // k_dkv: the dkv contribution of every (row, selected key) pair, dS' Q + P do_lat contracted over all
 //   96 heads at once, rounded to bf16 and stored per pair (one workgroup per row and 192 latent dims,
 //   Q and do_lat of its dims as MFMA B operands in LDS, dS' and P streamed from g in 32-key tiles).
@@ -35,8 +35,6 @@
 
 namespace dsa {
 
-constexpr int kBwHeads = 32;   // heads per workgroup
-constexpr int kBwWaves = 4;
 constexpr int kBwKeys = 16;    // keys per gathered tile
 constexpr int kBwGran = kLatent * 2 / 16;             // 72 granules per latent row
 constexpr int kBwTileBytes = kBwKeys * kBwGran * 16;  // 18 KB
@@ -105,137 +103,173 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 }
 
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBwWaves * kWave, 2) void k_sparse_mla_bwd(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_ring[2][kBwTileBytes];       // 36 KB
-  __shared__ __attribute__((aligned(16))) float s_dp[2][kBwKeys * 16];             // dP [key][head] per head tile
-  __shared__ __attribute__((aligned(16))) uint16_t s_ds[kBwKeys * kBwHeads];       // dS' [key][head]
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[kBwKeys * kBwHeads];        // P [key][head]
-  __shared__ __attribute__((aligned(16))) uint16_t s_dsT[kBwHeads * kBwKeys];      // dS'^T [head][key]
+// k_sparse_mla_bwd_row: the same per-row work with all 96 heads in one workgroup, so that each selected
+// kv row is gathered once per row instead of once per 32-head group (the gather's copies per CU set
+// the pace). Eight waves, two barriers per 16-key tile:
+//  - waves 0..5 (compute): 16 heads each, their q and do_lat fragments in registers. Per tile S^T and
+//    dP^T on 16x16x32 MFMAs over the same K fragments of the tile, then P and dS' of their heads, in
+//    bf16 to LDS: s_g in g's [key][dS' of 96 heads | P of 96 heads] layout, s_dsT as [head][key];
+//  - waves 6 and 7 (copy): the tile gathers, two tiles ahead through a four-slot ring;
+//  - dq^T += K^T dS'^T over the 54 (32 dims x 32 heads) tiles, one tile behind the products (s_dsT is
+//    double buffered and the ring keeps the previous tile): the compute waves take four each before
+//    the next tile's S^T and dP^T, the copy waves fifteen each beside them. After the second barrier
+//    the compute waves store s_g to g, 1 KB each.
+constexpr int kBrHeads = 96;
+constexpr int kBrWaves = 8;
+constexpr int kBrCompute = 6;
+constexpr int kBrRing = 4;
+constexpr int kBrDqC = 4;   // dq tiles of a compute wave
+constexpr int kBrDqX = 15;  // of a copy wave
+static_assert(kBrCompute * kBrDqC + (kBrWaves - kBrCompute) * kBrDqX == 18 * 3, "every dq tile has an owner");
+static_assert(kBwKeys * kGCols * 2 == kBrCompute * 1024, "one 1 KB store of the tile's g rows per compute wave");
+
+__global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kBrRing][kBwTileBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t s_g[kBwKeys * kGCols];
+  __shared__ __attribute__((aligned(16))) uint16_t s_dsT[2][kBrHeads * kBwKeys];  // tile t in buffer t % 2
   __shared__ int32_t s_idx[kBwMaxIdx + kBwKeys];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int ng = a.H / kBwHeads;
-  const int crow = blockIdx.x / ng, hg = blockIdx.x % ng;  // chunk-local row, head group
-  const int r = a.chunk_r0 + crow;                        // local row
+  const int crow = blockIdx.x;
+  const int r = a.chunk_r0 + crow;
   const int t_row = a.row0 + r;
-  const int H = a.H, T = a.T;
   const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
   const int ntiles = (keff + kBwKeys - 1) / kBwKeys;
-  const int h0 = hg * kBwHeads;
-
-  // the row's indices (-1: no usable key)
   const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
-  for (int j = threadIdx.x; j < ntiles * kBwKeys; j += kBwWaves * kWave) {
+  for (int j = threadIdx.x; j < ntiles * kBwKeys; j += kBrWaves * kWave) {
     const int v = j < keff ? ix[j] : -1;
-    s_idx[j] = (v >= 0 && v < T) ? v : -1;
+    s_idx[j] = (v >= 0 && v < a.T) ? v : -1;
   }
-  const uint16_t* __restrict__ qrow = a.q + (static_cast<int64_t>(r) * H + h0) * kLatent;
-  const uint16_t* __restrict__ drow = a.do_lat + (static_cast<int64_t>(crow) * H + h0) * kVDim;
-  // this head group's columns of the row's g rows
-  uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols + h0;
-  // Waves 0 and 1: q fragments (B of S^T = K Q^T: head 16*wave + i16, dims 32*st + 8*g16); their
-  // heads' lse (log2 units) and D. Waves 2 and 3: do_lat fragments of heads 16*(wave-2) + i16.
-  const int my_h = 16 * (wave & 1) + i16;  // head within the group of this lane's score column
-  bf16x8 fr[18];
-  if (wave < 2) {
-#pragma unroll
-    for (int st = 0; st < 18; ++st) fr[st] = *reinterpret_cast<const bf16x8*>(qrow + my_h * kLatent + 32 * st + 8 * g16);
-  } else {
-#pragma unroll
-    for (int st = 0; st < 16; ++st) fr[st] = *reinterpret_cast<const bf16x8*>(drow + my_h * kVDim + 32 * st + 8 * g16);
-#pragma unroll
-    for (int st = 16; st < 18; ++st) fr[st] = bf16x8{};
-  }
-  const float lse2 = wave < 2 ? a.lse[static_cast<int64_t>(r) * H + h0 + my_h] * kLog2e : 0.0f;
-  const float Dh = wave < 2 ? a.delta[static_cast<int64_t>(crow) * H + h0 + my_h] : 0.0f;
-  const float sl2 = a.scale * kLog2e;
-
-  // dq^T accumulators: latent tiles dt = wave + 4*i (i < 5, dt < 18), 32 dims x 32 heads each
-  f32x16 dq[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) dq[i] = f32x16{};
-
-  // gather copies: tile column granule 4*c + g16 of row (i16 ^ 4*g16), c = 0..17 over the 4 waves
   const uint32_t ring = lds_addr_of(&s_ring[0][0]);
-  const int my_row = i16 ^ (4 * g16);
-  auto issue_tile = [&](int t) {
-    const int s_key = s_idx[t * kBwKeys + my_row];
-    const uint16_t* src = a.kv + static_cast<int64_t>(max(s_key, 0)) * kLatent + 8 * g16;
-    const uint32_t base = ring + (t & 1) * kBwTileBytes;
-    for (int c = wave; c < 18; c += kBwWaves) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
-  };
-  __syncthreads();  // indices
-  if (ntiles > 0) issue_tile(0);
-
-  // transposed reads of the tile (A = K^T: lane = latent dim, 8 keys), as in the forward's value waves
+  // transposed reads of the tile (A = K^T: lane = latent dim, 8 keys), and the S^T / dP^T operand reads
   const int hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
   const int vc = 2 * chh + (q4 >> 1);
   const uint32_t v_off1 = (vc * 16 + ((8 * hh + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1);
   const uint32_t v_off2 = (vc * 16 + ((8 * hh + 4 + s4) ^ (4 * vc))) * 16 + 8 * (q4 & 1);
-  const uint32_t qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // A of S^T / dP^T: key i16, dims 32*st + 8*g16
+  const uint32_t qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // key i16, dims 32*st + 8*g16
+  const uint32_t dsT = lds_addr_of(&s_dsT[0][0]) + (lane & 31) * 32 + 16 * hh;  // + 32 * 32 * ht: head 32ht + lane%32
+  constexpr uint32_t kDsTBytes = kBrHeads * kBwKeys * 2;
+  // dq^T += K^T dS'^T of tile t for dq tile (dt, ht) = (i % 18, i / 18)
+  auto dq_step = [&](f32x16& acc, int i, int t) {
+    const int dt = i % 18, ht = i / 18;
+    const uint32_t tb = ring + (t % kBrRing) * kBwTileBytes;
+    const u32x2 v1 = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * dt));
+    const u32x2 v2 = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * dt));
+    const u32x4 kt = {v1[0], v1[1], v2[0], v2[1]};
+    const bf16x8 b = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(dsT + (t & 1) * kDsTBytes + 32 * 32 * ht));
+    acc = mfma32(__builtin_bit_cast(bf16x8, kt), b, acc);
+  };
+  // lane: head 32ht + lane%32, dims 32dt + 8(e/4) + 4(lane/32) + e%4
+  auto dq_store = [&](const f32x16& acc, int i) {
+    const int dt = i % 18, ht = i / 18;
+    float* __restrict__ dst = a.dq + (static_cast<int64_t>(r) * kBrHeads + 32 * ht + (lane & 31)) * kLatent + 32 * dt;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dst[8 * (e >> 2) + 4 * hh + (e & 3)] = acc[e];
+  };
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmem();
-    barrier_lds();  // tile t has landed; every wave is done with tile t - 1 and its P / dS'
-    if (t + 1 < ntiles) issue_tile(t + 1);
-    const uint32_t tb = ring + (t & 1) * kBwTileBytes;
-    // ---- S^T (waves 0, 1) or dP^T (waves 2, 3): 16 keys x 16 heads
-    // 18 K steps in both products (the dP waves' last two fragments are zero), so that the chain
-    // unrolls with constant register indices
-    f32x4 acc = f32x4{};
+  if (wave < kBrCompute) {
+    // ================================ compute wave ================================
+    const int h = 16 * wave + i16;  // this lane's head (column of S^T and dP^T)
+    bf16x8 qf[18], df[16];
+    const uint16_t* __restrict__ qh = a.q + (static_cast<int64_t>(r) * kBrHeads + h) * kLatent + 8 * g16;
+    const uint16_t* __restrict__ dh = a.do_lat + (static_cast<int64_t>(crow) * kBrHeads + h) * kVDim + 8 * g16;
 #pragma unroll
-    for (int st = 0; st < 18; ++st) acc = mfma16(lds_read16(lds_ptr(tb + qk_off + 1024 * st)), fr[st], acc);
-    // lane: head column i16, keys 4*g16 + e
-    if (wave >= 2) {
+    for (int st = 0; st < 18; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qh + 32 * st);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_dp[wave - 2][(4 * g16 + e) * 16 + i16] = acc[e];
-    }
-    barrier_lds();
-    if (wave < 2) {
+    for (int st = 0; st < 16; ++st) df[st] = *reinterpret_cast<const bf16x8*>(dh + 32 * st);
+    const float lse2 = a.lse[static_cast<int64_t>(r) * kBrHeads + h] * kLog2e;
+    const float Dh = a.delta[static_cast<int64_t>(crow) * kBrHeads + h];
+    const float sl2 = a.scale * kLog2e;
+    f32x16 dq[kBrDqC];
+#pragma unroll
+    for (int i = 0; i < kBrDqC; ++i) dq[i] = f32x16{};
+    uint16_t* __restrict__ gdst = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols + 512 * wave + 8 * lane;
+    __syncthreads();  // indices (the copy waves issue tiles 0 and 1 meanwhile)
+    for (int t = 0; t < ntiles; ++t) {
+      barrier_lds();  // (A) tile t has landed; every wave is done with tile t - 1's s_g
+      const uint32_t tb = ring + (t % kBrRing) * kBwTileBytes;
+      // this tile's S^T and dP^T, with tile t - 1's four dq steps between them: independent MFMAs for
+      // the matrix core while the chain waits for its next K fragment
+      f32x4 sacc = f32x4{}, pacc = f32x4{};
+#pragma unroll
+      for (int st = 0; st < 18; ++st) {
+        const bf16x8 kf = lds_read16(lds_ptr(tb + qk_off + 1024 * st));
+        if (st % 4 == 1 && st / 4 < kBrDqC && t > 0) dq_step(dq[st / 4], kBrDqC * wave + st / 4, t - 1);
+        sacc = mfma16(kf, qf[st], sacc);
+        if (st < 16) pacc = mfma16(kf, df[st], pacc);  // V = the first 512 dims
+      }
+      // lane: head h, keys 4*g16 + e. s_g's 16-byte chunks are swizzled by key (chunk c of key row k at
+      // c ^ 2((k / 4) % 4)), so that the four key rows one write instruction touches fall on
+      // different banks; dS'^T takes the lane's four keys in one 8-byte write.
+      uint16_t dsb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = 4 * g16 + e;
         const bool ok = s_idx[t * kBwKeys + key] >= 0;
-        const float p = ok ? fast_exp2(__builtin_fmaf(acc[e], sl2, -lse2)) : 0.0f;
-        const float ds = a.scale * p * (s_dp[wave][key * 16 + i16] - Dh);
-        const uint16_t pb = f32_to_bf16(p), db = f32_to_bf16(ds);
-        s_p[key * kBwHeads + my_h] = pb;
-        s_ds[key * kBwHeads + my_h] = db;
-        s_dsT[my_h * kBwKeys + key] = db;
+        const float p = ok ? fast_exp2(__builtin_fmaf(sacc[e], sl2, -lse2)) : 0.0f;
+        const float ds = a.scale * p * (pacc[e] - Dh);
+        dsb[e] = f32_to_bf16(ds);
+        const int sw = 16 * g16;  // 2((key / 4) % 4) chunks of 8 values
+        s_g[key * kGCols + (h ^ sw)] = dsb[e];
+        s_g[key * kGCols + ((kBrHeads + h) ^ sw)] = f32_to_bf16(p);
+      }
+      *reinterpret_cast<DSA_LDS u32x2*>(lds_ptr(lds_addr_of(&s_dsT[t & 1][0]) + (h * kBwKeys + 4 * g16) * 2)) =
+          u32x2{static_cast<uint32_t>(dsb[0]) | (static_cast<uint32_t>(dsb[1]) << 16),
+                static_cast<uint32_t>(dsb[2]) | (static_cast<uint32_t>(dsb[3]) << 16)};
+      barrier_lds();  // (B) the tile's P and dS' are in LDS
+      {
+        // chunk q = 64 * wave + lane of the tile's 384 (key q / 24, chunk q % 24), stored in place
+        const int q = kWave * wave + lane, key = q / 24, c = q % 24;
+        const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(
+            lds_ptr(lds_addr_of(&s_g[0]) + key * kGCols * 2 + 16 * (c ^ (2 * ((key >> 2) & 3)))));
+        *reinterpret_cast<u32x4*>(gdst + static_cast<int64_t>(t * kBwKeys) * kGCols) = v;
       }
     }
-    barrier_lds();
-    // ---- dq^T += K^T dS'^T: M = 32 latent dims, N = 32 heads, K = 16 keys
-    const bf16x8 bds = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(lds_addr_of(s_dsT) + (lane & 31) * 32 + 16 * hh));
+    if (ntiles > 0) {
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int dt = wave + 4 * i;
-      if (dt < 18) {
-        const u32x2 v1 = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * dt));
-        const u32x2 v2 = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * dt));
-        const u32x4 kt = {v1[0], v1[1], v2[0], v2[1]};
-        dq[i] = mfma32(__builtin_bit_cast(bf16x8, kt), bds, dq[i]);
+      for (int i = 0; i < kBrDqC; ++i) dq_step(dq[i], kBrDqC * wave + i, ntiles - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < kBrDqC; ++i) dq_store(dq[i], kBrDqC * wave + i);
+  } else {
+    // ================================ copy wave ================================
+    const int cw = wave - kBrCompute;  // copies cw, cw + 2, ... of each tile: tile column granules 4c + g16
+    const int my_row = i16 ^ (4 * g16);
+    auto issue_tile = [&](int t) {
+      const int s_key = s_idx[t * kBwKeys + my_row];
+      const uint16_t* src = a.kv + static_cast<int64_t>(max(s_key, 0)) * kLatent + 8 * g16;
+      const uint32_t base = ring + (t % kBrRing) * kBwTileBytes;
+#pragma unroll
+      for (int c = cw; c < 18; c += 2) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
+    };
+    f32x16 dq[kBrDqX];
+#pragma unroll
+    for (int i = 0; i < kBrDqX; ++i) dq[i] = f32x16{};
+    const int i0 = kBrCompute * kBrDqC + kBrDqX * cw;
+    __syncthreads();  // indices
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t's copies are complete; tile t + 1's (nine per wave) may still be in flight
+      if (t + 1 < ntiles) wait_vmem_le<9>();
+      else wait_vmem();
+      barrier_lds();  // (A)
+      if (t + 2 < ntiles) issue_tile(t + 2);  // into the slot of tile t - 2, which every wave is done with
+      // tile t - 1's dq, beside the compute waves' S^T and dP^T of tile t
+      if (t > 0) {
+#pragma unroll
+        for (int i = 0; i < kBrDqX; ++i) dq_step(dq[i], i0 + i, t - 1);
       }
+      barrier_lds();  // (B)
     }
-    // ---- the tile's dS' and P (16 keys x 32 heads each) to g, for k_dkv: one 16-byte store per lane
-    if (wave >= 2) {
-      const uint32_t src = wave == 2 ? lds_addr_of(&s_ds[0]) : lds_addr_of(&s_p[0]);
-      const int key = lane >> 2, gr = lane & 3;
-      const u32x4 v = *reinterpret_cast<const DSA_LDS u32x4*>(lds_ptr(src + key * 64 + 16 * gr));
-      *reinterpret_cast<u32x4*>(grow + static_cast<int64_t>(t * kBwKeys + key) * kGCols + (wave - 2) * 96 + 8 * gr) = v;
-    }
-  }
-  // dq of the row: lane holds head (lane % 32), dims 32*dt + 8*(e/4) + 4*hh + e%4
-  float* __restrict__ dqrow = a.dq + (static_cast<int64_t>(r) * H + h0 + (lane & 31)) * kLatent;
+    if (ntiles > 0) {
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int dt = wave + 4 * i;
-    if (dt < 18) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dqrow[32 * dt + 8 * (e >> 2) + 4 * hh + (e & 3)] = dq[i][e];
+      for (int i = 0; i < kBrDqX; ++i) dq_step(dq[i], i0 + i, ntiles - 1);
     }
+#pragma unroll
+    for (int i = 0; i < kBrDqX; ++i) dq_store(dq[i], i0 + i);
   }
 }
 
@@ -626,9 +660,8 @@ hipError_t launch_dkv(const DkvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st) {
-  if (a.H % kBwHeads != 0 || a.k > kBwMaxIdx || a.chunk_rows < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sparse_mla_bwd, dim3(static_cast<unsigned>(a.chunk_rows) * (a.H / kBwHeads)), dim3(kBwWaves * kWave), 0,
-                     st, a);
+  if (a.H != kBrHeads || a.k > kBwMaxIdx || a.chunk_rows < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sparse_mla_bwd_row, dim3(static_cast<unsigned>(a.chunk_rows)), dim3(kBrWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 
