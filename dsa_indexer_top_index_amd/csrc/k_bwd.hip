@@ -103,17 +103,17 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_sparse_mla_bwd_row: the same per-row work with all 96 heads in one workgroup, so that each selected
-// kv row is gathered once per row instead of once per 32-head group (the gather's copies per CU set
-// the pace). Eight waves, two barriers per 16-key tile:
+// k_sparse_mla_bwd_row: the backward of one row with all 96 heads in one workgroup, so that each
+// selected kv row is gathered once per row (a workgroup per group of 32 heads would gather it three
+// times, and the gather's copies per CU set the pace). Eight waves, two barriers per 16-key tile:
 //  - waves 0..5 (compute): 16 heads each, their q and do_lat fragments in registers. Per tile S^T and
 //    dP^T on 16x16x32 MFMAs over the same K fragments of the tile, then P and dS' of their heads, in
 //    bf16 to LDS: s_g in g's [key][dS' of 96 heads | P of 96 heads] layout, s_dsT as [head][key];
 //  - waves 6 and 7 (copy): the tile gathers, two tiles ahead through a four-slot ring;
 //  - dq^T += K^T dS'^T over the 54 (32 dims x 32 heads) tiles, one tile behind the products (s_dsT is
-//    double buffered and the ring keeps the previous tile): the compute waves take four each before
-//    the next tile's S^T and dP^T, the copy waves fifteen each beside them. After the second barrier
-//    the compute waves store s_g to g, 1 KB each.
+//    double buffered and the ring keeps the previous tile): the compute waves take four each, spread
+//    through the next tile's S^T and dP^T chain, the copy waves fifteen each beside it. After the
+//    second barrier the compute waves store s_g to g, 1 KB each.
 constexpr int kBrHeads = 96;
 constexpr int kBrWaves = 8;
 constexpr int kBrCompute = 6;
