@@ -668,6 +668,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   // operand of K step s of 32-key tile n: key 32n + i%32, K bytes 64s + 32(i/32) + 16h .. +16.
   // Copy j of this wave fills block CPW*wave + j.
   uint32_t cp_off[CPW];
+  constexpr uint32_t kCopyBias = 1024 * (CPW - 1);
+  static_assert(CPW <= 4, "copy offsets within the immediate range");
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int blk_j = CPW * wave + j;
@@ -678,24 +680,37 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       const int n = blk_j / KS, st = blk_j % KS;
       cp_off[j] = static_cast<uint32_t>(((16 * n + (lane & 15)) * D_I + 32 * st + 8 * (lane >> 4)) * 2);
     }
+    // Copy j takes 1024 j as its immediate offset, which moves its LDS address (so that one base per
+    // slot serves all the wave's copies) and its global address (taken back here, against a scalar
+    // base lowered by kCopyBias so that every per-lane offset stays non-negative).
+    cp_off[j] += kCopyBias - 1024 * j;
   }
   const uint32_t ring = lds_addr_of(&s_ring[0]);
   // The last chunk may reach up to 127 rows past the last key row (see kIdxKeyPad): those rows of
   // the padded LNk are staged but never scored. A copy for the chunk after the last one refills the
   // free slot with the last chunk instead, which nothing reads.
   u32x4 raw[LNF ? CPW : 1];  // fused LN: this lane's raw k_I granules of the next chunk
+  auto copy_j = [&](const void* chunk_base, int j, uint32_t lds_base) {
+    const void* sb = reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(chunk_base) - kCopyBias);
+    switch (j) {
+      case 0: copy16_to_lds_imm<0>(sb, cp_off[0], lds_base); break;
+      case 1: if constexpr (CPW > 1) copy16_to_lds_imm<1024>(sb, cp_off[1], lds_base); break;
+      case 2: if constexpr (CPW > 2) copy16_to_lds_imm<2048>(sb, cp_off[2], lds_base); break;
+      default: if constexpr (CPW > 3) copy16_to_lds_imm<3072>(sb, cp_off[3], lds_base); break;
+    }
+  };
   auto issue_copy = [&](int c, int j) {
     const int K0 = kb + min(c, nchunks - 1) * kChunk;
-    const uint32_t lds = ring + (c & 1) * STAGE_BYTES + 1024 * (CPW * wave + j);
+    const uint32_t lds = ring + (c & 1) * STAGE_BYTES + 1024 * CPW * wave;  // + 1024 j, the immediate
     if constexpr (LNF) {
       // key 16*wave + lane%16 of the chunk (rows past the last key read the last key: never scored),
       // dims 32j + 8(lane/16) .. +8: the lane's granule of block CPW*wave + j
       const int key = min(K0 + 16 * wave + (lane & 15), a.T - 1);
       raw[j] = *reinterpret_cast<const u32x4*>(a.k_raw + static_cast<int64_t>(key) * D_I + 32 * j + 8 * (lane >> 4));
     } else if constexpr (F8) {
-      copy16_to_lds_imm<0>(a.LNk8 + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+      copy_j(a.LNk8 + static_cast<int64_t>(K0) * D_I, j, lds);
     } else {
-      copy16_to_lds_imm<0>(LNk + static_cast<int64_t>(K0) * D_I, cp_off[j], lds);
+      copy_j(LNk + static_cast<int64_t>(K0) * D_I, j, lds);
     }
   };
   // Fused LN: normalise the raw granules of chunk c (loaded by issue_copy) and write them to the
