@@ -648,7 +648,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       const uint32_t th = wg_select_topk<kIdxRows>(kr, reinterpret_cast<int32_t*>(kr + kCandStride), hist, sel_scratch,
                                                    c_rw, k, slack, &kept);
       if (rw == wave) {
-        cnt = kept;
+        cnt = __builtin_amdgcn_readfirstlane(kept);  // wave-uniform: the list count stays in an SGPR
         thr = th;
       }
     }
@@ -686,6 +686,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     cp_off[j] += kCopyBias - 1024 * j;
   }
   const uint32_t ring = lds_addr_of(&s_ring[0]);
+  uint32_t cbase = 0;  // this lane's LDS address in the slot of the chunk being scored, set per chunk
   // The last chunk may reach up to 127 rows past the last key row (see kIdxKeyPad): those rows of
   // the padded LNk are staged but never scored. A copy for the chunk after the last one refills the
   // free slot with the last chunk instead, which nothing reads.
@@ -807,12 +808,12 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     constexpr int PF_M = MT >= 2 ? MT - 2 : 0;  // the M tile beside whose MFMAs the next tile's operands are read
     bf16x8 (&bk)[KS] = bkr[n & 1];
     bf16x8 (&bn)[KS] = bkr[(n + 1) & 1];
-    uint32_t a0 = ring + (c & 1) * STAGE_BYTES + n * TILE_BYTES + 16 * lane;
-    asm volatile("" : "+v"(a0));
+    const uint32_t a0 = cbase + n * TILE_BYTES;  // the tile's offsets fold into the reads' immediates
     if constexpr (n == 0) {
 #pragma unroll
       for (int s = 0; s < KS; ++s) bk[s] = lds_read16(lds_ptr(a0 + 1024 * s));
     }
+    // one running sum when each MFMA has one epilogue element beside it, else two
     float part[2] = {0.0f, 0.0f};
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -823,7 +824,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
         if constexpr (!F8) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][s], bk[s], s == 0 ? Acc{} : acc[mt], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < EPM; ++e) part[e & 1] = epi(prev, j * EPM + e, part[e & 1]);
-        asm volatile("" : "+v"(part[0]), "+v"(part[1]));
+        if constexpr (EPM == 1) asm volatile("" : "+v"(part[0]));
+        else asm volatile("" : "+v"(part[0]), "+v"(part[1]));
         const bool rd = n + 1 < NT && mt == PF_M;
         if (rd) bn[s] = lds_read16(lds_ptr(a0 + TILE_BYTES + 1024 * s));
         side(j);
@@ -834,15 +836,15 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    return part[0] + part[1];
+    if constexpr (EPM == 1) return part[0];
+    else return part[0] + part[1];
   };
   // FP8: one 32-key tile n of chunk c; its two K steps read as four 1 KB blocks at once, each K
   // step one 32x32x64 MFMA per M tile beside its half of the epilogue (kept in four partial sums).
   auto tile_step8 = [&](int c, auto nn, Acc (&acc)[MT], const Acc (&prev)[MT], auto&& side) -> float {
     constexpr int n = decltype(nn)::value;
     constexpr int kEps = MT * EL / KS;  // epilogue elements per K step
-    uint32_t a0 = ring + (c & 1) * STAGE_BYTES + n * TILE_BYTES + 16 * lane;
-    asm volatile("" : "+v"(a0));
+    const uint32_t a0 = cbase + n * TILE_BYTES;
     i32x8 bk[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -893,7 +895,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       for (int j = 0; j < NMF; ++j)
 #pragma unroll
         for (int e = 0; e < EPM; ++e) part[e & 1] = epi(prev, j * EPM + e, part[e & 1]);
-      return part[0] + part[1];
+      if constexpr (EPM == 1) return part[0];
+      else return part[0] + part[1];
     }
   };
   // One score per lane for the 64 keys of a half chunk, from the partial head sums of its tiles.
@@ -926,12 +929,17 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     const uint32_t su = __float_as_uint(score + 0.0f);
     const uint32_t key = su ^ (static_cast<uint32_t>(static_cast<int32_t>(su) >> 31) | 0x80000000u);
     // every key of the block is at or after the document start kb, and half u = -1 (before the first
-    // chunk) takes nothing; bitwise ands keep the lane mask in scalar registers
-    const bool take = select & (u >= 0) & (s_key <= t) & (key >= thr);
-    const uint64_t msk = __builtin_amdgcn_ballot_w64(take);  // the lane mask itself, without a VGPR round trip
-    const int pos = take ? cnt + lanes_below(msk) : kCap + lane;
-    // 32-bit byte offsets from the lists' wave-uniform bases
-    const uint32_t off = static_cast<uint32_t>(pos) * 4u;
+    // chunk) takes nothing. The ballots of the two comparisons are their compare masks as they stand;
+    // the wave-uniform condition selects the whole mask.
+    const bool on = select & (u >= 0);
+    const bool in_row = s_key <= t, above = key >= thr;
+    const uint64_t msk = __builtin_amdgcn_ballot_w64(in_row) & __builtin_amdgcn_ballot_w64(above) & (0ull - static_cast<uint64_t>(on));
+    const bool take = on & in_row & above;
+    // 32-bit byte offsets from the lists' wave-uniform bases: every lane's rank among the taken ones
+    // (one shift-and-add), then one select by the mask (no exec-masked region)
+    uint32_t off_take = (static_cast<uint32_t>(lanes_below(msk)) << 2) + static_cast<uint32_t>(cnt) * 4u;
+    asm volatile("" : "+v"(off_take));
+    const uint32_t off = take ? off_take : static_cast<uint32_t>(kCap + lane) * 4u;
     *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ckeys) + off) = key;
     *reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(cidx) + off) = s_key;
     cnt += __popcll(msk);
@@ -969,6 +977,8 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
     // flags of the lists that step c-1 filled: read now, used after tile 0
     const i32x4 f0 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][0])));
     const i32x4 f1 = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_need[c & 1][4])));
+    cbase = ring + (c & 1) * STAGE_BYTES + 16 * lane;
+    asm volatile("" : "+v"(cbase));  // one VGPR for the whole chunk
     const bool act = select && c < nchunks && kb + c * kChunk <= t;                 // row has keys in chunk c
     const bool act_prev = select && c > 0 && kb + (c - 1) * kChunk + kHalf <= t;  // and in the second half of chunk c-1
     float sk_lo = 1.0f, sk_hi = 1.0f;
