@@ -96,6 +96,15 @@ static_assert(kCap >= kIdxMaxTopk + kSelSlack + kChunk, "a list takes a chunk af
 static_assert(kCap % (kIdxRows * kWave) == 0, "whole wave slices in the workgroup selection");
 static_assert(kIdxSlotWords == kIdxRows * 2 * kCandStride, "slot size");
 
+// Running head sums per lane in the FP8 epilogue (element j of a K step goes to sum j % kF8Parts),
+// and their combination: the drain of a row's last tile uses the same order.
+constexpr int kF8Parts = 1;
+__device__ __forceinline__ float sum_parts(const float (&p)[kF8Parts]) {
+  if constexpr (kF8Parts == 1) return p[0];
+  else if constexpr (kF8Parts == 2) return p[0] + p[1];
+  else return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
 // max(x, +0) as an integer max on the bit pattern: negative values and -0 (sign bit set) give +0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
@@ -852,7 +861,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       const i32x4 hi = __builtin_bit_cast(i32x4, lds_read16(lds_ptr(a0 + 2048 * s + 1024)));
       bk[s] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    constexpr int NP = 4;
+    constexpr int NP = kF8Parts;
     float part[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j) part[j] = 0.0f;
@@ -874,7 +883,7 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
       __builtin_amdgcn_sched_group_barrier(0x002, kEps + 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return (part[0] + part[1]) + (part[2] + part[3]);
+    return sum_parts(part);
   };
   // The epilogue of `prev` alone (a row's last chunk, or a wave whose row has ended), summed in
   // exactly the order of the tile functions above, so that equal keys get bit-identical scores
@@ -882,12 +891,14 @@ __global__ __launch_bounds__(kIdxRows * kWave, 1) void k_index_topk(IndexArgs a)
   auto tile_drain = [&](const Acc (&prev)[MT]) -> float {
     if constexpr (F8) {
       constexpr int kEps = MT * EL / KS;
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float part[kF8Parts];
+#pragma unroll
+      for (int j = 0; j < kF8Parts; ++j) part[j] = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int j = 0; j < kEps; ++j) part[j % 4] = epi(prev, s * kEps + j, part[j % 4]);
-      return (part[0] + part[1]) + (part[2] + part[3]);
+        for (int j = 0; j < kEps; ++j) part[j % kF8Parts] = epi(prev, s * kEps + j, part[j % kF8Parts]);
+      return sum_parts(part);
     } else {
       constexpr int EPM = MT * EL / NMF;
       float part[2] = {0.0f, 0.0f};
