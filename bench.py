@@ -454,7 +454,18 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
             evb[i][1].record(stream)
         torch.cuda.synchronize()
         t_bwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evb]))
-        del lse, dout, wsb, dq, dkv, dW, dg
+        # the same backward given the forward's o_lat (kept from the latent attention call), which
+        # it then reads instead of running the attention again
+        o_lat = torch.empty((T, cfg.H, 512), dtype=torch.bfloat16, device="cuda")
+        dsa.dsa_sparse_attention_latent(shape, dev["q"], dev["kv"], topk_idx, o_lat)
+        for i in range(n_bwd):
+            evb[i][0].record(stream)
+            dsa.dsa_sparse_mla_bwd_saved(shape, dev["q"], dev["kv"], topk_idx, dev["W_UV"], dev["gate"], out, lse, o_lat,
+                                         dout, dq, dkv, dW, dg, wsb)
+            evb[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_bwd_saved = float(np.mean([e[0].elapsed_time(e[1]) for e in evb]))
+        del lse, dout, wsb, dq, dkv, dW, dg, o_lat
     cold = []
     if cold_steps > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -505,6 +516,10 @@ def run_workload(name, steps, warmup, cold_steps, want_inputs=False):
         bwd_flop = 2.0 * cfg.H * (576 + 512 + 576 + 576 + 512 + 1088) * w["keff_sum"] + 2.0 * 2 * cfg.H * 512 * 128 * T
         res.update({"bwd_ms": round(t_bwd, 4), "bwd_tflops": round(bwd_flop / (t_bwd * 1e-3) / 1e12, 1),
                     "bwd_frac": round(bwd_flop / (t_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        # with the forward's o_lat given: no attention recompute (its 1,088 flop per selected key and head)
+        saved_flop = bwd_flop - 2.0 * cfg.H * 1088 * w["keff_sum"]
+        res.update({"bwd_saved_olat_ms": round(t_bwd_saved, 4),
+                    "bwd_saved_olat_frac": round(saved_flop / (t_bwd_saved * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
     if t_idx8 is not None:
         res.update({
             # FP8 indexer: the same algorithmic flops against the dense fp8 MFMA peak

@@ -23,6 +23,9 @@ Entry points (same names as the C ABI):
   dsa_sparse_mla_fwd_ex / dsa_fused_fwd_ex: the same with gate_per_dim=False, sink=None (elementwise
   gate [rows,H,128] and per-head sink logits [H] float32)
   dsa_sparse_mla_bwd_ex(shape, ..., dgate, workspace, gate_per_dim=False, sink=None, dsink=None)
+  dsa_sparse_attention_latent_ex(shape, q, kv, topk_idx, o_lat, lse=None, sink=None)
+  dsa_sparse_mla_bwd_saved(shape, q, kv, topk_idx, W_UV, gate, out, lse, o_lat, dout, dq, dkv, dW_UV, dgate,
+                           workspace, gate_per_dim=False, sink=None, dsink=None)
 """
 from __future__ import annotations
 
@@ -117,6 +120,10 @@ def lib():
         L.dsa_fused_fwd_ex.restype = ctypes.c_int
         L.dsa_sparse_mla_bwd_ex.argtypes = [P, V, v, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
         L.dsa_sparse_mla_bwd_ex.restype = ctypes.c_int
+        L.dsa_sparse_attention_latent_ex.argtypes = [P, V, v, v, v, v, v, v]
+        L.dsa_sparse_attention_latent_ex.restype = ctypes.c_int
+        L.dsa_sparse_mla_bwd_saved.argtypes = [P, V, v, v, v, v, v, v, v, v, v, v, v, v, v, v, v, ctypes.c_size_t, v]
+        L.dsa_sparse_mla_bwd_saved.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -370,20 +377,47 @@ def dsa_sparse_mla_fwd_ex(shape, q, kv, topk_idx, W_UV, gate, out, workspace, ls
     _raise(st, "dsa_sparse_mla_fwd_ex")
 
 
+def _bwd_variant_call(name, shape, q, kv, topk_idx, W_UV, gate, out, lse, o_lat, dout, dq, dkv, dW_UV, dgate,
+                      workspace, gate_per_dim, sink, dsink):
+    bf, f, n = torch.bfloat16, torch.float32, _sizes(shape)
+    var, n_gate = _variant(shape, gate_per_dim, sink)
+    head = [ctypes.byref(shape), ctypes.byref(var), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
+            _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(W_UV, bf, "W_UV", numel=n["W_UV"]),
+            _p(gate, bf, "gate", numel=n_gate), _p(out, bf, "out", numel=n["out"]), _p(lse, f, "lse", numel=n["lse"])]
+    if name == "dsa_sparse_mla_bwd_saved":
+        head.append(_p(o_lat, bf, "o_lat", numel=n["o_lat"]))
+    st = getattr(lib(), name)(
+        *head, _p(dout, bf, "dout", numel=n["out"]), _p(dq, f, "dq", numel=n["q"]), _p(dkv, f, "dkv", numel=n["kv"]),
+        _p(dW_UV, f, "dW_UV", numel=n["W_UV"]), _p(dgate, f, "dgate", numel=n_gate),
+        _p(dsink, f, "dsink", True, shape.H), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _raise(st, name)
+
+
 def dsa_sparse_mla_bwd_ex(shape, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, workspace,
                           gate_per_dim=False, sink=None, dsink=None):
     """dsa_sparse_mla_bwd for the gate/sink variant of dsa_sparse_mla_fwd_ex: gate and dgate [rows,H] or,
     with gate_per_dim, [rows,H,128]; with sink [H] float32, dsink [H] float32 receives its gradient."""
-    bf, f, n = torch.bfloat16, torch.float32, _sizes(shape)
-    var, n_gate = _variant(shape, gate_per_dim, sink)
-    st = lib().dsa_sparse_mla_bwd_ex(
+    _bwd_variant_call("dsa_sparse_mla_bwd_ex", shape, q, kv, topk_idx, W_UV, gate, out, lse, None, dout, dq, dkv,
+                      dW_UV, dgate, workspace, gate_per_dim, sink, dsink)
+
+
+def dsa_sparse_mla_bwd_saved(shape, q, kv, topk_idx, W_UV, gate, out, lse, o_lat, dout, dq, dkv, dW_UV, dgate,
+                             workspace, gate_per_dim=False, sink=None, dsink=None):
+    """dsa_sparse_mla_bwd_ex given the forward's latent attention output o_lat [rows,H,512] bf16 (from
+    dsa_sparse_attention_latent(_ex) with the same variant), which it reads instead of recomputing."""
+    _bwd_variant_call("dsa_sparse_mla_bwd_saved", shape, q, kv, topk_idx, W_UV, gate, out, lse, o_lat, dout, dq,
+                      dkv, dW_UV, dgate, workspace, gate_per_dim, sink, dsink)
+
+
+def dsa_sparse_attention_latent_ex(shape, q, kv, topk_idx, o_lat, lse=None, sink=None):
+    """dsa_sparse_attention_latent with per-head sink logits [H] float32 (natural-log units) or None."""
+    bf, n = torch.bfloat16, _sizes(shape)
+    var, _ = _variant(shape, False, sink)
+    st = lib().dsa_sparse_attention_latent_ex(
         ctypes.byref(shape), ctypes.byref(var), _p(q, bf, "q", numel=n["q"]), _p(kv, bf, "kv", numel=n["kv"]),
-        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(W_UV, bf, "W_UV", numel=n["W_UV"]),
-        _p(gate, bf, "gate", numel=n_gate), _p(out, bf, "out", numel=n["out"]), _p(lse, f, "lse", numel=n["lse"]),
-        _p(dout, bf, "dout", numel=n["out"]), _p(dq, f, "dq", numel=n["q"]), _p(dkv, f, "dkv", numel=n["kv"]),
-        _p(dW_UV, f, "dW_UV", numel=n["W_UV"]), _p(dgate, f, "dgate", numel=n_gate),
-        _p(dsink, f, "dsink", True, shape.H), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
-    _raise(st, "dsa_sparse_mla_bwd_ex")
+        _p(topk_idx, torch.int32, "topk_idx", numel=n["topk_idx"]), _p(o_lat, bf, "o_lat", numel=n["o_lat"]),
+        _p(lse, torch.float32, "lse", True, n["lse"]), _stream())
+    _raise(st, "dsa_sparse_attention_latent_ex")
 
 
 def dsa_fused_fwd_ex(shape, q_I, k_I, w, q, kv, W_UV, gate, topk_idx, out, workspace, ln_gamma=None, ln_beta=None,

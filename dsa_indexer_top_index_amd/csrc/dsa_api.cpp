@@ -374,8 +374,8 @@ size_t dsa_bwd_workspace_size(const dsa_shape* s) {
 
 static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q, const uint16_t* kv,
                           const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out,
-                          const float* lse, const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate,
-                          float* dsink, void* ws, size_t ws_bytes, void* stream) {
+                          const float* lse, const uint16_t* olat_saved, const uint16_t* dout, float* dq, float* dkv,
+                          float* dW_UV, float* dgate, float* dsink, void* ws, size_t ws_bytes, void* stream) {
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (s->H != 96) return DSA_ERR_UNSUPPORTED;
@@ -390,6 +390,7 @@ static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const ui
   const float* sink = v ? v->sink : nullptr;
   if (per_dim && !aligned(dgate, 16)) return DSA_ERR_INVALID_ARG;
   if ((sink != nullptr) != (dsink != nullptr) || (dsink && !aligned(dsink, 4))) return DSA_ERR_INVALID_ARG;
+  if (!aligned(olat_saved, 16)) return DSA_ERR_INVALID_ARG;
   const BwdLayout B = bwd_layout_of(s);
   if (ws == nullptr || ws_bytes < B.total) return DSA_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return DSA_ERR_INVALID_ARG;
@@ -450,9 +451,12 @@ static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const ui
     dsa::DkvListArgs dl{topk_idx, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
                         count, start, cursor, bsum, list, contrib, dkv};
     if (dsa::launch_dkv_reduce(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
-    // o_lat of the chunk again (the forward's attention kernel, with the sink if any), for dW_UV
-    if ((st = launch_attention(s, v, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
-    dsa::DwArgs dw{olat, d_o, dW_UV, n, s->H};
+    // o_lat of the chunk for dW_UV: the caller's saved rows, or the forward's attention kernel again
+    // (with the sink if any)
+    const uint16_t* olat_c = olat;
+    if (olat_saved != nullptr) olat_c = olat_saved + c0 * s->H * 512;
+    else if ((st = launch_attention(s, v, q, kv, topk_idx, olat, nullptr, c0, n, hs)) != DSA_OK) return st;
+    dsa::DwArgs dw{olat_c, d_o, dW_UV, n, s->H};
     if (dsa::launch_dwuv(dw, hs) != hipSuccess) return DSA_ERR_LAUNCH;
   }
   return DSA_OK;
@@ -462,7 +466,7 @@ dsa_status dsa_sparse_mla_bwd(const dsa_shape* s, const uint16_t* q, const uint1
                               const uint16_t* W_UV, const uint16_t* gate, const uint16_t* out, const float* lse,
                               const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate, void* ws,
                               size_t ws_bytes, void* stream) {
-  return run_bwd(s, nullptr, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, nullptr, ws,
+  return run_bwd(s, nullptr, q, kv, topk_idx, W_UV, gate, out, lse, nullptr, dout, dq, dkv, dW_UV, dgate, nullptr, ws,
                  ws_bytes, stream);
 }
 
@@ -470,7 +474,17 @@ dsa_status dsa_sparse_mla_bwd_ex(const dsa_shape* s, const dsa_mla_variant* v, c
                                  const int32_t* topk_idx, const uint16_t* W_UV, const uint16_t* gate,
                                  const uint16_t* out, const float* lse, const uint16_t* dout, float* dq, float* dkv,
                                  float* dW_UV, float* dgate, float* dsink, void* ws, size_t ws_bytes, void* stream) {
-  return run_bwd(s, v, q, kv, topk_idx, W_UV, gate, out, lse, dout, dq, dkv, dW_UV, dgate, dsink, ws, ws_bytes,
+  return run_bwd(s, v, q, kv, topk_idx, W_UV, gate, out, lse, nullptr, dout, dq, dkv, dW_UV, dgate, dsink, ws, ws_bytes,
+                 stream);
+}
+
+dsa_status dsa_sparse_mla_bwd_saved(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q,
+                                    const uint16_t* kv, const int32_t* topk_idx, const uint16_t* W_UV,
+                                    const uint16_t* gate, const uint16_t* out, const float* lse, const uint16_t* o_lat,
+                                    const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate,
+                                    float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  if (o_lat == nullptr) return DSA_ERR_INVALID_ARG;
+  return run_bwd(s, v, q, kv, topk_idx, W_UV, gate, out, lse, o_lat, dout, dq, dkv, dW_UV, dgate, dsink, ws, ws_bytes,
                  stream);
 }
 
@@ -503,14 +517,21 @@ dsa_status dsa_sparse_mla_fwd(const dsa_shape* s, const uint16_t* q, const uint1
   return dsa_sparse_mla_fwd_ex(s, nullptr, q, kv, topk_idx, W_UV, gate, out, lse, ws, ws_bytes, stream);
 }
 
-dsa_status dsa_sparse_attention_latent(const dsa_shape* s, const uint16_t* q, const uint16_t* kv,
-                                       const int32_t* topk_idx, uint16_t* o_lat, float* lse, void* stream) {
+dsa_status dsa_sparse_attention_latent_ex(const dsa_shape* s, const dsa_mla_variant* v, const uint16_t* q,
+                                          const uint16_t* kv, const int32_t* topk_idx, uint16_t* o_lat, float* lse,
+                                          void* stream) {
   dsa_status st = dsa_check_shape(s);
   if (st != DSA_OK) return st;
   if (!q || !kv || !topk_idx || !o_lat) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(topk_idx, 4) || !aligned(o_lat, 16) || !aligned(lse, 4))
     return DSA_ERR_INVALID_ARG;
-  return launch_attention(s, nullptr, q, kv, topk_idx, o_lat, lse, 0, rows_of(s), static_cast<hipStream_t>(stream));
+  if (v && ((v->gate_per_dim != 0 && v->gate_per_dim != 1) || !aligned(v->sink, 4))) return DSA_ERR_INVALID_ARG;
+  return launch_attention(s, v, q, kv, topk_idx, o_lat, lse, 0, rows_of(s), static_cast<hipStream_t>(stream));
+}
+
+dsa_status dsa_sparse_attention_latent(const dsa_shape* s, const uint16_t* q, const uint16_t* kv,
+                                       const int32_t* topk_idx, uint16_t* o_lat, float* lse, void* stream) {
+  return dsa_sparse_attention_latent_ex(s, nullptr, q, kv, topk_idx, o_lat, lse, stream);
 }
 
 dsa_status dsa_up_gate(const dsa_shape* s, const uint16_t* o_lat, const uint16_t* W_UV, const uint16_t* gate,

@@ -173,6 +173,12 @@ typedef struct dsa_mla_variant {
                              to 1 - exp(sink[h] - lse), and lse includes the sink. */
 } dsa_mla_variant;
 
+/* dsa_sparse_attention_latent with a variant: only its sink changes o_lat and lse (the gate is not
+ * applied here). NULL: identical to dsa_sparse_attention_latent. No workspace. */
+dsa_status dsa_sparse_attention_latent_ex(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q,
+                                          const uint16_t* kv, const int32_t* topk_idx, uint16_t* o_lat, float* lse,
+                                          void* stream);
+
 /* dsa_sparse_mla_fwd with a variant (NULL: identical to dsa_sparse_mla_fwd). */
 dsa_status dsa_sparse_mla_fwd_ex(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q,
                                  const uint16_t* kv, const int32_t* topk_idx, const uint16_t* W_UV,
@@ -244,6 +250,20 @@ dsa_status dsa_sparse_mla_bwd_ex(const dsa_shape* shape, const dsa_mla_variant* 
                                  const uint16_t* gate, const uint16_t* out, const float* lse,
                                  const uint16_t* dout, float* dq, float* dkv, float* dW_UV, float* dgate,
                                  float* dsink, void* workspace, size_t workspace_bytes, void* stream);
+
+/* dsa_sparse_mla_bwd_ex given the forward's latent attention output o_lat [rows, H, 512] bf16
+ * (16-byte aligned), as dsa_sparse_attention_latent(_ex) wrote it for the same q, kv, topk_idx and
+ * variant. dW_UV = sum over rows of o_lat^T (sigmoid(gate) * dout) then reads these rows instead of
+ * recomputing the attention for them; with the forward's own o_lat every output is the one
+ * dsa_sparse_mla_bwd_ex gives (the attention is deterministic). This trades rows * H * 1024 bytes
+ * kept from the forward for one attention pass. o_lat must not be NULL (DSA_ERR_INVALID_ARG).
+ * Other arguments, outputs and workspace as dsa_sparse_mla_bwd_ex. */
+dsa_status dsa_sparse_mla_bwd_saved(const dsa_shape* shape, const dsa_mla_variant* variant, const uint16_t* q,
+                                    const uint16_t* kv, const int32_t* topk_idx, const uint16_t* W_UV,
+                                    const uint16_t* gate, const uint16_t* out, const float* lse,
+                                    const uint16_t* o_lat, const uint16_t* dout, float* dq, float* dkv,
+                                    float* dW_UV, float* dgate, float* dsink, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Static English text of a status. Never NULL. */
 const char* dsa_status_string(dsa_status status);

@@ -22,7 +22,8 @@ def test_library_exports_every_declared_symbol():
     assert names == ["dsa_bwd_workspace_size", "dsa_check_shape", "dsa_fused_fwd", "dsa_fused_fwd_ex", "dsa_index_topk",
                      "dsa_index_topk_fp8", "dsa_index_topk_fused_ln", "dsa_index_topk_noalloc", "dsa_o_proj", "dsa_q_absorb",
                      "dsa_quantize_fp8",
-                     "dsa_sparse_attention_latent", "dsa_sparse_mla_bwd", "dsa_sparse_mla_bwd_ex", "dsa_sparse_mla_fwd",
+                     "dsa_sparse_attention_latent", "dsa_sparse_attention_latent_ex", "dsa_sparse_mla_bwd",
+                     "dsa_sparse_mla_bwd_ex", "dsa_sparse_mla_bwd_saved", "dsa_sparse_mla_fwd",
                      "dsa_sparse_mla_fwd_ex",
                      "dsa_status_string", "dsa_up_gate", "dsa_workspace_size"]
     L = dsa.lib()
@@ -255,3 +256,17 @@ def test_backward_host_checks():
     var.gate_per_dim = 2
     assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, None, fake, nb, None) == dsa.DSA_ERR_INVALID_ARG
     assert L.dsa_sparse_mla_bwd_ex(ctypes.byref(s), ctypes.byref(var), *args, None, fake, nb - 1, None) == dsa.DSA_ERR_INVALID_ARG
+    # the form with the forward's o_lat: it must be given, 16-byte aligned, and the workspace is the same
+    var.gate_per_dim = 0
+    saved = lambda o_lat, n_ws: L.dsa_sparse_mla_bwd_saved(ctypes.byref(s), ctypes.byref(var), *args[:7], o_lat,
+                                                          *args[7:], None, fake, n_ws, None)
+    assert saved(None, nb) == dsa.DSA_ERR_INVALID_ARG
+    assert saved(fake + 8, nb) == dsa.DSA_ERR_INVALID_ARG
+    assert saved(fake, nb - 1) == dsa.DSA_ERR_WORKSPACE
+    # the latent attention with a variant checks the variant's fields
+    var.gate_per_dim, var.sink = 2, None
+    assert L.dsa_sparse_attention_latent_ex(ctypes.byref(s), ctypes.byref(var), fake, fake, fake, fake, None,
+                                            None) == dsa.DSA_ERR_INVALID_ARG
+    var.gate_per_dim, var.sink = 0, fake + 2
+    assert L.dsa_sparse_attention_latent_ex(ctypes.byref(s), ctypes.byref(var), fake, fake, fake, fake, None,
+                                            None) == dsa.DSA_ERR_INVALID_ARG

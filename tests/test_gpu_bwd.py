@@ -134,6 +134,65 @@ def test_backward_variants(mode):
     _say(f"[gpu] backward variant {mode}: max error / max |ref|: " + ", ".join(msgs))
 
 
+@pytest.mark.parametrize("mode", ["plain", "sink"])
+def test_backward_saved_olat(mode):
+    """dsa_sparse_mla_bwd_saved with the forward's o_lat from dsa_sparse_attention_latent_ex, on 4,200 rows
+    (three backward chunks of up to 2,048 rows): every output equals dsa_sparse_mla_bwd_ex's (dq, dgate
+    and dsink bit for bit; dkv and dW_UV, whose sums run in an order that atomics decide, to 1e-5 of their
+    largest value). With o_lat doubled (exact in bf16) dW_UV doubles and nothing else moves, so the saved
+    rows are what dW_UV reads, chunk by chunk. The latent attention's lse equals the fused forward's."""
+    cfg = tg.Config("bwd-saved", 105, [2500, 1700], topk=128, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                    W_UV_std=0.02)
+    T, H = cfg.T, cfg.H
+    with_sink = mode == "sink"
+    _say(f"[gpu] backward with saved o_lat ({mode}): T={T} docs={cfg.n_docs} k={cfg.topk}")
+    inp = tg.make_inputs(cfg)
+    dev = gu.to_device(inp)
+    shape = gu.shape_of(cfg, dev["cu_seqlens"])
+    ws = dsa.alloc_workspace(shape)
+    sink_t = torch.from_numpy(_bwd_sink(H)).cuda() if with_sink else None
+    idx_t = torch.empty((T, cfg.topk), dtype=torch.int32, device="cuda")
+    out_t = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    lse_t = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dsa.dsa_fused_fwd_ex(shape, dev["q_I"], dev["k_I"], dev["w"], dev["q"], dev["kv"], dev["W_UV"], dev["gate"], idx_t,
+                         out_t, ws, lse=lse_t, sink=sink_t)
+    o_lat = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty_like(lse_t)
+    dsa.dsa_sparse_attention_latent_ex(shape, dev["q"], dev["kv"], idx_t, o_lat, lse=lse2, sink=sink_t)
+    dout_t = gu.bf16_np_to_tensor(tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128))
+    wsb = dsa.alloc_bwd_workspace(shape)
+
+    def grads(fn, *olat):
+        g = {"dq": torch.empty((T, H, 576), dtype=torch.float32, device="cuda"),
+             "dkv": torch.empty((T, 576), dtype=torch.float32, device="cuda"),
+             "dW_UV": torch.empty((H, 512, 128), dtype=torch.float32, device="cuda"),
+             "dgate": torch.empty((T, H), dtype=torch.float32, device="cuda")}
+        if with_sink:
+            g["dsink"] = torch.empty(H, dtype=torch.float32, device="cuda")
+        fn(shape, dev["q"], dev["kv"], idx_t, dev["W_UV"], dev["gate"], out_t, lse_t, *olat, dout_t, g["dq"], g["dkv"],
+           g["dW_UV"], g["dgate"], wsb, sink=sink_t, dsink=g.get("dsink"))
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in g.items()}
+
+    ref = grads(dsa.dsa_sparse_mla_bwd_ex)
+    got = grads(dsa.dsa_sparse_mla_bwd_saved, o_lat)
+    got2 = grads(dsa.dsa_sparse_mla_bwd_saved, o_lat * 2)
+    assert torch.equal(lse2, lse_t)
+    for k in ref:
+        if k in ("dkv", "dW_UV"):
+            mx = np.abs(ref[k]).max()
+            assert mx > 0 and np.abs(got[k] - ref[k]).max() <= 1e-5 * mx, k
+        else:
+            assert np.array_equal(got[k], ref[k]), k
+        if k == "dW_UV":
+            assert np.abs(got2[k] - 2 * ref[k]).max() <= 2e-5 * mx, k
+        elif k == "dkv":
+            assert np.abs(got2[k] - ref[k]).max() <= 1e-5 * mx, k
+        else:
+            assert np.array_equal(got2[k], ref[k]), k
+    _say(f"[gpu] backward with saved o_lat ({mode}): equal to the recomputing backward")
+
+
 def test_backward_caller_indices():
     """Caller indices with duplicates, -1 and out-of-range entries, and a row with no usable index."""
     cfg = tg.Config("bwd-idx", 103, [400], topk=64, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
