@@ -151,16 +151,21 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
   const uint32_t qk_off = (g16 * 16 + (i16 ^ (4 * g16))) * 16;  // key i16, dims 32*st + 8*g16
   const uint32_t dsT = lds_addr_of(&s_dsT[0][0]) + (lane & 31) * 32 + 16 * hh;  // + 32 * 32 * ht: head 32ht + lane%32
   constexpr uint32_t kDsTBytes = kBrHeads * kBwKeys * 2;
-  // dq^T += K^T dS'^T of tile t for dq tile (dt, ht) = (i % 18, i / 18)
-  auto dq_step = [&](f32x16& acc, int i, int t) {
-    const int dt = i % 18, ht = i / 18;
+  // dS'^T fragment of head tile ht of tile t (B operand of the dq products)
+  auto ds_frag = [&](int ht, int t) -> bf16x8 {
+    return *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(dsT + (t & 1) * kDsTBytes + 32 * 32 * ht));
+  };
+  // dq^T += K^T dS'^T of tile t for dq tile (dt, ht) = (i % 18, i / 18), given head tile ht's dS'^T
+  // fragment b
+  auto dq_step_b = [&](f32x16& acc, int i, int t, const bf16x8& b) {
+    const int dt = i % 18;
     const uint32_t tb = ring + (t % kBrRing) * kBwTileBytes;
     const u32x2 v1 = lds_read_tr16(lds_ptr(tb + v_off1 + 1024 * dt));
     const u32x2 v2 = lds_read_tr16(lds_ptr(tb + v_off2 + 1024 * dt));
     const u32x4 kt = {v1[0], v1[1], v2[0], v2[1]};
-    const bf16x8 b = *reinterpret_cast<const DSA_LDS bf16x8*>(lds_ptr(dsT + (t & 1) * kDsTBytes + 32 * 32 * ht));
     acc = mfma32(__builtin_bit_cast(bf16x8, kt), b, acc);
   };
+  auto dq_step = [&](f32x16& acc, int i, int t) { dq_step_b(acc, i, t, ds_frag(i / 18, t)); };
   // lane: head 32ht + lane%32, dims 32dt + 8(e/4) + 4(lane/32) + e%4
   auto dq_store = [&](const f32x16& acc, int i) {
     const int dt = i % 18, ht = i / 18;
@@ -235,41 +240,50 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
     for (int i = 0; i < kBrDqC; ++i) dq_store(dq[i], kBrDqC * wave + i);
   } else {
     // ================================ copy wave ================================
-    const int cw = wave - kBrCompute;  // copies cw, cw + 2, ... of each tile: tile column granules 4c + g16
-    const int my_row = i16 ^ (4 * g16);
-    auto issue_tile = [&](int t) {
-      const int s_key = s_idx[t * kBwKeys + my_row];
-      const uint16_t* src = a.kv + static_cast<int64_t>(max(s_key, 0)) * kLatent + 8 * g16;
-      const uint32_t base = ring + (t % kBrRing) * kBwTileBytes;
+    // Specialised per copy wave, so that its dq tiles (and their head tiles) are known at compile
+    // time: each tile's dS'^T fragment of a head tile is then read once for all of the wave's dq
+    // tiles in it (the wave's fifteen tiles span at most two head tiles).
+    auto copy_wave = [&](auto cw_c) {
+      constexpr int cw = decltype(cw_c)::value;  // copies cw, cw + 2, ... of each tile: tile column granules 4c + g16
+      constexpr int i0 = kBrCompute * kBrDqC + kBrDqX * cw;
+      const int my_row = i16 ^ (4 * g16);
+      auto issue_tile = [&](int t) {
+        const int s_key = s_idx[t * kBwKeys + my_row];
+        const uint16_t* src = a.kv + static_cast<int64_t>(max(s_key, 0)) * kLatent + 8 * g16;
+        const uint32_t base = ring + (t % kBrRing) * kBwTileBytes;
 #pragma unroll
-      for (int c = cw; c < 18; c += 2) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
-    };
-    f32x16 dq[kBrDqX];
+        for (int c = cw; c < 18; c += 2) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
+      };
+      f32x16 dq[kBrDqX];
 #pragma unroll
-    for (int i = 0; i < kBrDqX; ++i) dq[i] = f32x16{};
-    const int i0 = kBrCompute * kBrDqC + kBrDqX * cw;
-    __syncthreads();  // indices
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    for (int t = 0; t < ntiles; ++t) {
-      // tile t's copies are complete; tile t + 1's (nine per wave) may still be in flight
-      if (t + 1 < ntiles) wait_vmem_le<9>();
-      else wait_vmem();
-      barrier_lds();  // (A)
-      if (t + 2 < ntiles) issue_tile(t + 2);  // into the slot of tile t - 2, which every wave is done with
-      // tile t - 1's dq, beside the compute waves' S^T and dP^T of tile t
-      if (t > 0) {
+      for (int i = 0; i < kBrDqX; ++i) dq[i] = f32x16{};
+      auto dq_steps = [&](int t) {
+        bf16x8 b;
 #pragma unroll
-        for (int i = 0; i < kBrDqX; ++i) dq_step(dq[i], i0 + i, t - 1);
+        for (int i = 0; i < kBrDqX; ++i) {  // unrolled: the head-tile test folds to a constant
+          if (i == 0 || (i0 + i) / 18 != (i0 + i - 1) / 18) b = ds_frag((i0 + i) / 18, t);
+          dq_step_b(dq[i], i0 + i, t, b);
+        }
+      };
+      __syncthreads();  // indices
+      if (ntiles > 0) issue_tile(0);
+      if (ntiles > 1) issue_tile(1);
+      for (int t = 0; t < ntiles; ++t) {
+        // tile t's copies are complete; tile t + 1's (nine per wave) may still be in flight
+        if (t + 1 < ntiles) wait_vmem_le<9>();
+        else wait_vmem();
+        barrier_lds();  // (A)
+        if (t + 2 < ntiles) issue_tile(t + 2);  // into the slot of tile t - 2, which every wave is done with
+        // tile t - 1's dq, beside the compute waves' S^T and dP^T of tile t
+        if (t > 0) dq_steps(t - 1);
+        barrier_lds();  // (B)
       }
-      barrier_lds();  // (B)
-    }
-    if (ntiles > 0) {
+      if (ntiles > 0) dq_steps(ntiles - 1);
 #pragma unroll
-      for (int i = 0; i < kBrDqX; ++i) dq_step(dq[i], i0 + i, ntiles - 1);
-    }
-#pragma unroll
-    for (int i = 0; i < kBrDqX; ++i) dq_store(dq[i], i0 + i);
+      for (int i = 0; i < kBrDqX; ++i) dq_store(dq[i], i0 + i);
+    };
+    if (wave == kBrCompute) copy_wave(std::integral_constant<int, 0>{});
+    else copy_wave(std::integral_constant<int, 1>{});
   }
 }
 
