@@ -165,7 +165,6 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
     const u32x4 kt = {v1[0], v1[1], v2[0], v2[1]};
     acc = mfma32(__builtin_bit_cast(bf16x8, kt), b, acc);
   };
-  auto dq_step = [&](f32x16& acc, int i, int t) { dq_step_b(acc, i, t, ds_frag(i / 18, t)); };
   // lane: head 32ht + lane%32, dims 32dt + 8(e/4) + 4(lane/32) + e%4
   auto dq_store = [&](const f32x16& acc, int i) {
     const int dt = i % 18, ht = i / 18;
@@ -191,6 +190,16 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
 #pragma unroll
     for (int i = 0; i < kBrDqC; ++i) dq[i] = f32x16{};
     uint16_t* __restrict__ gdst = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols + 512 * wave + 8 * lane;
+    // dq tiles of compute wave w: (dims 3w + j, head tile 0) for j < 3 and (dims w, head tile 1) for
+    // j = 3, so that the dS'^T fragment read for j = 0 serves j = 1 and 2 as well (the copy waves own
+    // tiles 24 .. 53)
+    static_assert(kBrDqC == 4 && kBrCompute == 6, "compute waves' dq tiles: all of head tile 0, dims 0..5 of 1");
+    auto ci = [&](int j) { return j < 3 ? 3 * wave + j : 18 + wave; };
+    bf16x8 bq;
+    auto dq_step_c = [&](int j, int t) {
+      if (j == 0 || j == 3) bq = ds_frag(j == 0 ? 0 : 1, t);
+      dq_step_b(dq[j], ci(j), t, bq);
+    };
     __syncthreads();  // indices (the copy waves issue tiles 0 and 1 meanwhile)
     for (int t = 0; t < ntiles; ++t) {
       barrier_lds();  // (A) tile t has landed; every wave is done with tile t - 1's s_g
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
 #pragma unroll
       for (int st = 0; st < 18; ++st) {
         const bf16x8 kf = lds_read16(lds_ptr(tb + qk_off + 1024 * st));
-        if (st % 4 == 1 && st / 4 < kBrDqC && t > 0) dq_step(dq[st / 4], kBrDqC * wave + st / 4, t - 1);
+        if (st % 4 == 1 && st / 4 < kBrDqC && t > 0) dq_step_c(st / 4, t - 1);
         sacc = mfma16(kf, qf[st], sacc);
         if (st < 16) pacc = mfma16(kf, df[st], pacc);  // V = the first 512 dims
       }
@@ -234,10 +243,10 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
     }
     if (ntiles > 0) {
 #pragma unroll
-      for (int i = 0; i < kBrDqC; ++i) dq_step(dq[i], kBrDqC * wave + i, ntiles - 1);
+      for (int j = 0; j < kBrDqC; ++j) dq_step_c(j, ntiles - 1);
     }
 #pragma unroll
-    for (int i = 0; i < kBrDqC; ++i) dq_store(dq[i], kBrDqC * wave + i);
+    for (int j = 0; j < kBrDqC; ++j) dq_store(dq[j], ci(j));
   } else {
     // ================================ copy wave ================================
     // Specialised per copy wave, so that its dq tiles (and their head tiles) are known at compile
