@@ -193,6 +193,48 @@ def test_backward_saved_olat(mode):
     _say(f"[gpu] backward with saved o_lat ({mode}): equal to the recomputing backward")
 
 
+def test_backward_row_ranges_sum_to_the_whole():
+    """The backward over query-row ranges (dsa_shape's q_begin/q_end, one range per rank when the rows
+    are sharded): on two packed documents split at a row inside the first document, each range's dq
+    and dgate equal those rows of the whole-range run bit for bit, and the two ranges' dkv and dW_UV
+    (partial sums over their rows, which ranks would add up) sum to the whole run's within FP32
+    reordering (1e-5 of the largest value)."""
+    cfg = tg.Config("bwd-ranges", 106, [2600, 900], topk=256, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,
+                    W_UV_std=0.02)
+    T, H, k = cfg.T, cfg.H, cfg.topk
+    _say(f"[gpu] backward over row ranges: T={T} docs={cfg.n_docs} k={k}")
+    inp = tg.make_inputs(cfg)
+    dev = gu.to_device(inp)
+    res = gu.run_fused(cfg, dev, with_lse=True)
+    idx_t, out_t, lse_t = res["topk_idx"], res["out"], res["lse"]
+    dout_t = gu.bf16_np_to_tensor(tg.normal_bf16(cfg.seed, TAG_DOUT, 0, T * H * 128, 1.0).reshape(T, H, 128))
+
+    def bwd(b, e):
+        shape = gu.shape_of(cfg, dev["cu_seqlens"], q_begin=b, q_end=e)
+        n = e - b
+        g = {"dq": torch.empty((n, H, 576), dtype=torch.float32, device="cuda"),
+             "dkv": torch.empty((T, 576), dtype=torch.float32, device="cuda"),
+             "dW_UV": torch.empty((H, 512, 128), dtype=torch.float32, device="cuda"),
+             "dgate": torch.empty((n, H), dtype=torch.float32, device="cuda")}
+        dsa.dsa_sparse_mla_bwd(shape, dev["q"][b:e].contiguous(), dev["kv"], idx_t[b:e].contiguous(), dev["W_UV"],
+                               dev["gate"][b:e].contiguous(), out_t[b:e].contiguous(), lse_t[b:e].contiguous(),
+                               dout_t[b:e].contiguous(), g["dq"], g["dkv"], g["dW_UV"], g["dgate"],
+                               dsa.alloc_bwd_workspace(shape))
+        torch.cuda.synchronize()
+        return {key: v.cpu().numpy() for key, v in g.items()}
+
+    whole = bwd(0, T)
+    cut = 1300
+    lo, hi = bwd(0, cut), bwd(cut, T)
+    assert np.array_equal(lo["dq"], whole["dq"][:cut]) and np.array_equal(hi["dq"], whole["dq"][cut:])
+    assert np.array_equal(lo["dgate"], whole["dgate"][:cut]) and np.array_equal(hi["dgate"], whole["dgate"][cut:])
+    for key in ("dkv", "dW_UV"):
+        mx = np.abs(whole[key]).max()
+        err = np.abs(lo[key].astype(np.float64) + hi[key] - whole[key]).max()
+        assert mx > 0 and err <= 1e-5 * mx, (key, err, mx)
+    _say("[gpu] backward over row ranges: the ranges' gradients make up the whole run's")
+
+
 def test_backward_caller_indices():
     """Caller indices with duplicates, -1 and out-of-range entries, and a row with no usable index."""
     cfg = tg.Config("bwd-idx", 103, [400], topk=64, H=96, H_I=64, d_I=128, w_scale=1 / 8, q_std=1 / 24,

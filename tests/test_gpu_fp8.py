@@ -86,8 +86,8 @@ def _fp8_cases():
                     W_UV_std=0.02)
     packed = tg.Config("fp8-packed", 82, [700, 1, 33, 900, 256, 257, 1400], topk=256, H=96, H_I=64, d_I=128,
                        w_scale=1 / 8, q_std=1.0, W_UV_std=0.02)
-    return {"mid": (mid, None), "packed-small": (packed, None), "t4096": (tg.get_config("t4096"), "sample"),
-            "t131072": (tg.get_config("t131072"), "sample")}
+    return {"mid": (mid, None), "mid-affine": (mid, "affine"), "packed-small": (packed, None),
+            "t4096": (tg.get_config("t4096"), "sample"), "t131072": (tg.get_config("t131072"), "sample")}
 
 
 def _ws_fp8_keys(ws, cfg):
@@ -101,22 +101,29 @@ def _ws_fp8_keys(ws, cfg):
     return k8, sk
 
 
-@pytest.mark.parametrize("case", ["mid", "packed-small", "t4096", "t131072"])
+@pytest.mark.parametrize("case", ["mid", "mid-affine", "packed-small", "t4096", "t131072"])
 def test_fp8_indexer_parity(case):
+    """mid-affine: the key LayerNorm with a weight and a bias, which the quantisation then sees."""
     cfg, mode = _fp8_cases()[case]
     _say(f"[gpu] fp8 indexer {case}: T={cfg.T} docs={cfg.n_docs} k={cfg.topk}")
     keys, dev = gu.device_inputs(cfg)
     shape = gu.shape_of(cfg, dev["cu_seqlens"])
     ws = dsa.alloc_workspace(shape)
+    ln_g = ln_b = None
+    if mode == "affine":
+        rng = np.random.default_rng(12)
+        ln_g = rng.uniform(0.5, 1.5, cfg.d_I).astype(np.float32)
+        ln_b = rng.uniform(-0.2, 0.2, cfg.d_I).astype(np.float32)
+    ln_kw = {} if ln_g is None else {"ln_gamma": torch.from_numpy(ln_g).cuda(), "ln_beta": torch.from_numpy(ln_b).cuda()}
     idx_t = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
-    dsa.dsa_index_topk_fp8(shape, dev["q_I"], dev["k_I"], dev["w"], idx_t, ws)
+    dsa.dsa_index_topk_fp8(shape, dev["q_I"], dev["k_I"], dev["w"], idx_t, ws, **ln_kw)
     idx2 = torch.empty_like(idx_t)
-    dsa.dsa_index_topk_fp8(shape, dev["q_I"], dev["k_I"], dev["w"], idx2, ws)
+    dsa.dsa_index_topk_fp8(shape, dev["q_I"], dev["k_I"], dev["w"], idx2, ws, **ln_kw)
     torch.cuda.synchronize()
     assert torch.equal(idx_t, idx2), "FP8 indexer is not deterministic"
     idx = idx_t.cpu().numpy()
     _check_structure(cfg, idx)
-    LNk = oracle.key_layernorm(keys["k_I"], cfg.ln_eps)
+    LNk = oracle.key_layernorm(keys["k_I"], cfg.ln_eps, ln_g, ln_b)
     k8, ek = oracle.quantize_fp8_rows(LNk)
     g8, gsk = _ws_fp8_keys(ws, cfg)
     assert np.array_equal(g8, k8) and np.array_equal(gsk, np.ldexp(np.float32(1), ek).astype(np.float32))
