@@ -82,6 +82,11 @@ __global__ __launch_bounds__(kUpWaves * kWave, kUpWavesPerSimd) void k_up_gate(U
   // the gate of the wave's row `lane`, as the sigmoid in FP32 (per-head gates only)
   const float gate_v = a.gate_per_dim ? 0.0f : bf16_to_f32(a.gate[(static_cast<int64_t>(a.chunk_r0) + min(row0 + lane, a.chunk_rows - 1)) * H + h]);
   wait_vmem();
+  // af is complete (see the end of the chunk loop)
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(af[mt][s]));
   __syncthreads();
   const float sig_row = 1.0f / (1.0f + __expf(-gate_v));
   constexpr int nchunks = kVDim / kUpChunk;
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(kUpWaves * kWave, kUpWavesPerSimd) void k_up_gate(U
 #pragma unroll
         for (int s = 0; s < 4; ++s) an[mt][s] = *reinterpret_cast<const bf16x8*>(arow_p[mt] + kUpChunk * (cc + 1) + 16 * s);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the next chunk's loads go out before this chunk's products
     const DSA_LDS uint8_t* wb = (const DSA_LDS uint8_t*)(&s_w[buf][0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -116,6 +122,13 @@ __global__ __launch_bounds__(kUpWaves * kWave, kUpWavesPerSimd) void k_up_gate(U
         for (int s = 0; s < 4; ++s) af[mt][s] = an[mt][s];
     }
     wait_vmem();
+    // The compiler does not count the weight copies (inline assembly) among the loads in flight, so
+    // it would otherwise wait for them before the next chunk's first products to be sure of af;
+    // passing af through an empty asm statement here, after the wait, makes af complete for it.
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(af[mt][s]));
     __syncthreads();
   }
 
