@@ -11,9 +11,9 @@
 // are staged in LDS by asynchronous 16-byte global->LDS copies (eight per wave and step), double
 // buffered with one barrier per step, so the next step's copies run under this step's MFMAs. A tile
 // row is 128 bytes; its 16-byte granules are XOR-swizzled by (row / 2) % 8, so that the 16 lanes of
-// each operand read hit 16 distinct bank groups. Blocks are renumbered so that consecutive output
-// tiles of one row band run on the same XCD and share its L2 copy of the x band. The epilogue stages
-// bf16 outputs in the then idle LDS and stores 16 bytes per lane.
+// each operand read hit 16 distinct bank groups. Blocks are renumbered so that each XCD runs
+// patches of four row bands by a few column bands at a time, whose operand bands its L2 shares. The
+// epilogue stages bf16 outputs in the then idle LDS and stores 16 bytes per lane.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -30,9 +30,16 @@ __global__ __launch_bounds__(kGWaves * kWave, 1) void k_gemm_nt(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t[2][2][kGTileBytes];  // [buffer][x, W_o]: 128 KB
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int nbn = a.N / kGN;
+  const int nbn = a.N / kGN, nbm = (a.M + kGM - 1) / kGM;
+  // Consecutive logical blocks run on one XCD; they walk groups of kGroupM row bands column by
+  // column, so that the XCD's resident workgroups share a few x bands and a few W_o bands in L2
+  // (a 4 x 8 patch of tiles reads 12 operand bands where a 1 x 28 row reads 29).
+  constexpr int kGroupM = 4;
   const int lb = xcd_local_block(blockIdx.x, gridDim.x);
-  const int bm = lb / nbn, bn = lb % nbn;
+  const int grp = lb / (kGroupM * nbn), first_bm = grp * kGroupM;
+  const int gsz = min(kGroupM, nbm - first_bm);
+  const int in_grp = lb - grp * kGroupM * nbn;
+  const int bm = first_bm + in_grp % gsz, bn = in_grp / gsz;
   const int m0 = bm * kGM, n0 = bn * kGN;
   const int wm = wave >> 2, wn = wave & 3;  // this wave: rows wm*128 .. +128, columns wn*64 .. +64
   const int K = a.K, nk = K / kGK;
