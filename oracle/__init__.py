@@ -42,6 +42,24 @@ def build_native() -> str:
     return path
 
 
+# The sanitizer build (tests only): AddressSanitizer and UndefinedBehaviorSanitizer, stopping at the
+# first report. The process that loads it must preload the ASan runtime.
+SANITIZE_CXXFLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                     "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared"]
+
+
+def build_sanitized(path: str) -> str:
+    subprocess.run(["g++", *SANITIZE_CXXFLAGS, _SRC, "-o", path], check=True)
+    return path
+
+
+def use_library(path: str):
+    """Switches this module to another build of the same source (the sanitizer test's)."""
+    global _lib
+    _lib = _load(path)
+    return _lib
+
+
 def use_native():
     """Switches this module to a host-optimised build of the same source (for timing only)."""
     global _lib

@@ -37,13 +37,28 @@ def build(force: bool = False) -> str:
 
 
 _lib = None
+_lib_path = None  # a different build of the same source to load instead (the sanitizer test's)
+
+
+def build_sanitized(path: str) -> str:
+    """The generator built with AddressSanitizer and UndefinedBehaviorSanitizer (tests only; the
+    process that loads it must preload the ASan runtime)."""
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fPIC", "-shared", "-fopenmp", "-std=c11", os.path.join(_HERE, "testgen.c"), "-o", path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
+def use_library(path: str) -> None:
+    """Loads `path` (a build of testgen.c) instead of the default build."""
+    global _lib, _lib_path
+    _lib, _lib_path = None, path
 
 
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(_lib_path if _lib_path else build())
         u64, i64, p = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
         L.tg_normal_bf16.argtypes = [u64, u64, i64, i64, ctypes.c_double, p]
         L.tg_uniform_bf16.argtypes = [u64, u64, i64, i64, ctypes.c_double, p]
