@@ -445,12 +445,14 @@ static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const ui
     b.H = s->H;
     b.scale = s->softmax_scale;
     if (dsa::launch_sparse_mla_bwd(b, hs) != hipSuccess) return DSA_ERR_LAUNCH;
-    dsa::DkvArgs dk{g, q, dolat, topk_idx, contrib, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n,
-                    s->topk, B.g_stride};
-    if (dsa::launch_dkv(dk, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    // the chunk's pairs sorted by key first, so that k_dkv stores each key's contributions together
     dsa::DkvListArgs dl{topk_idx, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
                         count, start, cursor, bsum, list, contrib, dkv};
-    if (dsa::launch_dkv_reduce(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (dsa::launch_pairs_sort(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    dsa::DkvArgs dk{g, q, dolat, list, contrib, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n,
+                    s->topk, B.g_stride};
+    if (dsa::launch_dkv(dk, hs) != hipSuccess) return DSA_ERR_LAUNCH;
+    if (dsa::launch_dkv_sum(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     // o_lat of the chunk for dW_UV: the caller's saved rows, or the forward's attention kernel again
     // (with the sink if any)
     const uint16_t* olat_c = olat;

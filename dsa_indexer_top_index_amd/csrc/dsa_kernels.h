@@ -144,13 +144,14 @@ struct BwdArgs {
 
 // The dkv contribution of each (row r, selected key j) of a row chunk, over all H heads, from g:
 //   contrib(r, j) = dS'[r, j, :] q[r] + P[r, j, :] do_lat[r]  (576 floats)
-// stored for the pairs with a usable index; k_dkv_reduce then adds each key's contributions to dkv.
+// stored, for the pairs with a usable index, at the pair's position in key order (from the pair sort),
+// so that k_dkv_sum reads each key's contributions contiguously.
 struct DkvArgs {
   const uint16_t* g;       // as BwdArgs::g
   const uint16_t* q;       // [nrows, H, 576]
   const uint16_t* do_lat;  // [chunk_rows, H, 512]
-  const int32_t* idx;      // [nrows, k]
-  uint16_t* contrib;       // [3][chunk_rows * k][192] bf16: group q holds dims 192q .. 192q + 191 of pair r * k + j
+  const int32_t* pos;      // [chunk_rows * k] position of pair r * k + j in key order, or -1 (DkvListArgs::list)
+  uint16_t* contrib;       // [3][chunk_rows * k][192] bf16: group q holds dims 192q .. 192q + 191 of the pair at position p
   const int32_t* cu;
   int n_docs;
   int T;
@@ -176,7 +177,7 @@ struct DkvListArgs {
   int* start;              // [T + 1] exclusive prefix sums of count
   int* cursor;             // [T] scatter positions
   int* bsum;               // [ceil(T / kPairScanTile)] count sums of the scan's blocks
-  int* list;               // [chunk_rows * k] pair ids r * k + j, grouped by key
+  int* list;               // [chunk_rows * k] position of pair r * k + j in key order (-1: no usable key)
   const uint16_t* contrib; // as DkvArgs::contrib
   float* dkv;              // [T, 576], added to
 };
@@ -208,8 +209,10 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkv(const DkvArgs& a, hipStream_t st);
 // count[key] = pairs of the chunk selecting key; start = exclusive scan (and cursor = start);
-// list = pair ids grouped by key; dkv[key] += the sum of the key's contributions. Four launches.
-hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st);
+// list = each pair's position in key order. Before k_dkv, which stores at those positions.
+hipError_t launch_pairs_sort(const DkvListArgs& a, hipStream_t st);
+// dkv[key] += the sum of the key's contributions (positions start[key] .. start[key + 1] - 1).
+hipError_t launch_dkv_sum(const DkvListArgs& a, hipStream_t st);
 hipError_t launch_sink_sum(const SinkSumArgs& a, hipStream_t st);
 hipError_t launch_dwuv(const DwArgs& a, hipStream_t st);
 

@@ -23,9 +23,10 @@
 // k_dkv: the dkv contribution of every (row, selected key) pair, dS' Q + P do_lat contracted over all
 //   96 heads at once, rounded to bf16 and stored per pair (one workgroup per row and 192 latent dims,
 //   Q and do_lat of its dims as MFMA B operands in LDS, dS' and P streamed from g in 32-key tiles).
-//   A counting sort groups the chunk's pairs by key (k_pairs_count, two scan passes,
-//   k_pairs_scatter) and k_dkv_sum adds each key's contributions to dkv, one wave per key: no float
-//   atomics, which run at a fixed rate per lane (about 330 G lane operations per second on MI355X).
+//   A counting sort of the chunk's pairs by key (k_pairs_count, two scan passes, k_pairs_scatter)
+//   runs first and gives each pair its position in key order; k_dkv stores each contribution there,
+//   and k_dkv_sum adds each key's contiguous contributions to dkv, one wave per key: no float atomics,
+//   which run at a fixed rate per lane (about 330 G lane operations per second on MI355X).
 // k_dwuv: dW_UV[h] += o_lat^T do over a chunk of rows, 16 rows per K step staged in LDS in the
 //   forward's tile layout so that both operands are read transposed; partial sums added with atomics.
 #include "dsa_device.h"
@@ -306,7 +307,8 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
 // tile's dS' and P rows of g are the A operands (the next tile's loaded ahead, and loaded once for
 // all 192 dims), over six 32-dim N tiles. N tile nt holds dims 6c + nt (c = lane % 32), so a lane
 // ends with six adjacent dims of each of its keys and stores them as 12 bytes.
-// contrib is [3][chunk rows * k][192] bf16: group, pair r * k + j, dim within the group.
+// contrib is [3][chunk rows * k][192] bf16: group, the pair's position in key order (from the pair
+// sort), dim within the group.
 constexpr int kDkGroups = 3;
 constexpr int kDkGDims = kLatent / kDkGroups;  // 192
 constexpr int kDkNT = kDkGDims / 32;           // 6 N tiles of 32 dims
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
   // 6(l%32) + nt of part p (0: q, 1: do_lat)
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2 * kDkKS * kDkNT * 1024];
   __shared__ __attribute__((aligned(16))) uint16_t s_nat[kDkHeads * kDkGDims];  // one part, [head][dim]
-  __shared__ __attribute__((aligned(16))) int32_t s_idx[kBwMaxIdx + 32];
+  __shared__ __attribute__((aligned(16))) int32_t s_pos[kBwMaxIdx + 32];  // the row's pairs' positions in key order
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int b = blockIdx.x, xcd = b % 8, loc = b / 8;
@@ -331,11 +333,8 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
   const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
   const int ntiles = (keff + 31) / 32;
   const int d0 = kDkGDims * grp;
-  const int32_t* __restrict__ ix = a.idx + static_cast<int64_t>(r) * a.k;
-  for (int j = threadIdx.x; j < ntiles * 32; j += kDkWaves * kWave) {
-    const int v = j < keff ? ix[j] : -1;
-    s_idx[j] = (v >= 0 && v < a.T) ? v : -1;
-  }
+  const int32_t* __restrict__ pr = a.pos + static_cast<int64_t>(crow) * a.k;
+  for (int j = threadIdx.x; j < ntiles * 32; j += kDkWaves * kWave) s_pos[j] = j < keff ? pr[j] : -1;
   for (int p = 0; p < 2; ++p) {
     // the part's 96 x 192 values in natural order, 24 granules of 8 dims per head
     for (int gi = threadIdx.x; gi < kDkHeads * (kDkGDims / 8); gi += kDkWaves * kWave) {
@@ -364,7 +363,7 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
   const uint32_t sb = lds_addr_of(&s_b[0]) + 16 * lane;
   const uint16_t* __restrict__ grow = a.g + static_cast<int64_t>(crow) * a.g_stride * kGCols;
   const int64_t npairs = static_cast<int64_t>(a.chunk_rows) * a.k;
-  uint16_t* __restrict__ out = a.contrib + (grp * npairs + static_cast<int64_t>(crow) * a.k) * kDkGDims + 6 * col;
+  uint16_t* __restrict__ out = a.contrib + grp * npairs * kDkGDims + 6 * col;
   // A operands: key 32t + lane%32, heads 16ks + 8(lane/32) .. +8 of dS' (p = 0) and P (p = 1); two
   // waves per SIMD hide each other's loads
   const uint16_t* __restrict__ ga0 = grow + static_cast<int64_t>(col) * kGCols + 8 * hh;
@@ -391,16 +390,16 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
         for (int nt = 0; nt < kDkNT; ++nt) acc[nt] = mfma32(af[p][ks], bv[nt], acc[nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    // element 4g + e: key 32t + 8g + 4(lane/32) + e, dims 6(lane%32) .. +6 of the group; pairs
-    // without a usable index are never listed, so they are not stored
+    // element 4g + e: key 32t + 8g + 4(lane/32) + e, dims 6(lane%32) .. +6 of the group, stored at
+    // the pair's position in key order; pairs without a usable index have none and are not stored
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_idx[32 * t + 8 * g + 4 * hh])));
+      const i32x4 kk = *reinterpret_cast<const DSA_LDS i32x4*>(lds_ptr(lds_addr_of(&s_pos[32 * t + 8 * g + 4 * hh])));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * g + e;
         if (kk[e] >= 0)
-          *reinterpret_cast<u32x3*>(out + static_cast<int64_t>(32 * t + 8 * g + 4 * hh + e) * kDkGDims) =
+          *reinterpret_cast<u32x3*>(out + static_cast<int64_t>(kk[e]) * kDkGDims) =
               u32x3{pack_bf16x2(acc[0][i], acc[1][i]), pack_bf16x2(acc[2][i], acc[3][i]), pack_bf16x2(acc[4][i], acc[5][i])};
       }
     }
@@ -409,10 +408,11 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Summing the contributions per key without atomics on dkv: a counting sort of the chunk's usable
-// (row, j) pairs by key index (count, exclusive scan, scatter of pair ids), then one wave per key adds
-// its pairs' 576-float rows and adds the sum to dkv, which no other wave of the pass touches. The
-// counts and list positions come from integer atomics (one per pair, not one per element), so the
-// order of a key's pairs, and the last bits of its sum, may differ from run to run.
+// (row, j) pairs by key index (count, exclusive scan, and each pair's position in key order), then
+// k_dkv stores each pair's contribution at its position and one wave per key adds its contiguous
+// 576-float rows to dkv, which no other wave of the pass touches. The positions within a key come
+// from integer atomics (one per pair, not one per element), so the order of a key's pairs, and the
+// last bits of its sum, may differ from run to run.
 __device__ __forceinline__ int pair_key(const DkvListArgs& a, int crow, int j) {
   const int t_row = a.row0 + a.chunk_r0 + crow;
   const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
@@ -503,15 +503,18 @@ __global__ __launch_bounds__(256) void k_pairs_scan(DkvListArgs a) {
   if (b == gridDim.x - 1 && threadIdx.x == 255) a.start[a.T] = run;  // the total
 }
 
+// Each pair's position in key order (-1 for a pair without a usable key): k_dkv stores the pair's
+// contribution there, so that each key's contributions are contiguous for k_dkv_sum.
 __global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
   const int j = blockIdx.x * 256 + threadIdx.x, crow = blockIdx.y;
   if (j >= a.k) return;
   const int key = pair_key(a, crow, j);
-  if (key >= 0) a.list[atomicAdd(a.cursor + key, 1)] = crow * a.k + j;
+  a.list[static_cast<int64_t>(crow) * a.k + j] = key >= 0 ? atomicAdd(a.cursor + key, 1) : -1;
 }
 
-// One wave per key: the sum of its pairs' contributions (four pairs in flight; lane l < 48 takes
-// dims 4l .. 4l + 3 of each group), added to dkv[key].
+// One wave per key: the sum of its pairs' contributions, contiguous in contrib at positions
+// start[key] .. start[key + 1] - 1 (four pairs in flight; lane l < 48 takes dims 4l .. 4l + 3 of
+// each group), added to dkv[key].
 __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
   const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (key >= a.T) return;
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
     u32x2 v[4][kDkGroups];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint16_t* src = base + static_cast<int64_t>(a.list[p + u]) * kDkGDims;
+      const uint16_t* src = base + static_cast<int64_t>(p + u) * kDkGDims;
 #pragma unroll
       for (int q = 0; q < kDkGroups; ++q) v[u][q] = *reinterpret_cast<const u32x2*>(src + gstride * q);
     }
@@ -545,7 +548,7 @@ __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
       for (int q = 0; q < kDkGroups; ++q) add(v[u][q], q);
   }
   for (; p < p1; ++p) {
-    const uint16_t* src = base + static_cast<int64_t>(a.list[p]) * kDkGDims;
+    const uint16_t* src = base + static_cast<int64_t>(p) * kDkGDims;
 #pragma unroll
     for (int q = 0; q < kDkGroups; ++q) add(*reinterpret_cast<const u32x2*>(src + gstride * q), q);
   }
@@ -662,7 +665,7 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st) {
+hipError_t launch_pairs_sort(const DkvListArgs& a, hipStream_t st) {
   if (a.chunk_rows <= 0) return hipSuccess;
   if (launch_fill_zero(reinterpret_cast<float*>(a.count), a.T, st) != hipSuccess) return hipGetLastError();  // int 0 == float +0 bits
   const dim3 pairs((a.k + 255) / 256, a.chunk_rows);
@@ -671,6 +674,11 @@ hipError_t launch_dkv_reduce(const DkvListArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_pairs_tile_sums, tiles, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pairs_scan, tiles, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pairs_scatter, pairs, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_sum(const DkvListArgs& a, hipStream_t st) {
+  if (a.chunk_rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_dkv_sum, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
