@@ -332,13 +332,13 @@ dsa_status dsa_o_proj(const dsa_shape* s, const uint16_t* x, const uint16_t* W_o
 //   delta   [chunk rows, H] f32              sum dout * out
 //   g       [chunk rows, g_stride, 2H] bf16  dS' and P of every selected key, for the dkv contraction
 //   contrib [3][chunk rows * k][192] bf16     each (row, selected key)'s dkv contribution, by 192-dim group
-//   count, cursor [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
+//   count [T] and start [T + 1] int32, list [chunk rows * k] int32: the pairs grouped by key
 //   bsum    [ceil(T / 4096)] int32          the key scan's tile sums
 //   sterm   [chunk rows, H] f32             with a sink: each (row, head)'s term of the sink's gradient
 constexpr int64_t kBwdChunkRows = 2048;  // bounds contrib (4.8 GB at k = 2048)
 
 struct BwdLayout {
-  size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, cursor_off, list_off, bsum_off,
+  size_t do_off, dolat_off, delta_off, g_off, contrib_off, count_off, start_off, list_off, bsum_off,
       sterm_off, total;
   int g_stride;
   int64_t chunk_rows;
@@ -359,8 +359,7 @@ static BwdLayout bwd_layout_of(const dsa_shape* s) {
   B.contrib_off = B.g_off + align_up(crows * B.g_stride * 2 * s->H * 2);
   B.count_off = B.contrib_off + align_up(crows * s->topk * 576 * 2);
   B.start_off = B.count_off + align_up(static_cast<size_t>(s->T) * 4);
-  B.cursor_off = B.start_off + align_up((static_cast<size_t>(s->T) + 1) * 4);
-  B.list_off = B.cursor_off + align_up(static_cast<size_t>(s->T) * 4);
+  B.list_off = B.start_off + align_up((static_cast<size_t>(s->T) + 1) * 4);
   B.bsum_off = B.list_off + align_up(crows * s->topk * 4);
   B.sterm_off = B.bsum_off + align_up((static_cast<size_t>(s->T) + dsa::kPairScanTile - 1) / dsa::kPairScanTile * 4);
   B.total = B.sterm_off + align_up(cr * 4);
@@ -405,7 +404,6 @@ static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const ui
   uint16_t* contrib = reinterpret_cast<uint16_t*>(base + B.contrib_off);
   int* count = reinterpret_cast<int*>(base + B.count_off);
   int* start = reinterpret_cast<int*>(base + B.start_off);
-  int* cursor = reinterpret_cast<int*>(base + B.cursor_off);
   int* list = reinterpret_cast<int*>(base + B.list_off);
   int* bsum = reinterpret_cast<int*>(base + B.bsum_off);
   float* sterm = reinterpret_cast<float*>(base + B.sterm_off);
@@ -447,7 +445,7 @@ static dsa_status run_bwd(const dsa_shape* s, const dsa_mla_variant* v, const ui
     if (dsa::launch_sparse_mla_bwd(b, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     // the chunk's pairs sorted by key first, so that k_dkv stores each key's contributions together
     dsa::DkvListArgs dl{topk_idx, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n, s->topk,
-                        count, start, cursor, bsum, list, contrib, dkv};
+                        count, start, bsum, list, contrib, dkv};
     if (dsa::launch_pairs_sort(dl, hs) != hipSuccess) return DSA_ERR_LAUNCH;
     dsa::DkvArgs dk{g, q, dolat, list, contrib, b.cu, s->n_docs, s->T, s->q_begin, static_cast<int>(c0), n,
                     s->topk, B.g_stride};

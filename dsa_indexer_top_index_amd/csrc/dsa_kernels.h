@@ -175,7 +175,6 @@ struct DkvListArgs {
   int k;
   int* count;              // [T] pairs per key (zeroed before the count pass)
   int* start;              // [T + 1] exclusive prefix sums of count
-  int* cursor;             // [T] scatter positions
   int* bsum;               // [ceil(T / kPairScanTile)] count sums of the scan's blocks
   int* list;               // [chunk_rows * k] position of pair r * k + j in key order (-1: no usable key)
   const uint16_t* contrib; // as DkvArgs::contrib
@@ -208,7 +207,7 @@ hipError_t launch_bwd_prep(const BwdPrepArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_sparse_mla_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkv(const DkvArgs& a, hipStream_t st);
-// count[key] = pairs of the chunk selecting key; start = exclusive scan (and cursor = start);
+// count[key] = pairs of the chunk selecting key; start = exclusive scan;
 // list = each pair's position in key order. Before k_dkv, which stores at those positions.
 hipError_t launch_pairs_sort(const DkvListArgs& a, hipStream_t st);
 // dkv[key] += the sum of the key's contributions (positions start[key] .. start[key + 1] - 1).

@@ -23,7 +23,7 @@
 // k_dkv: the dkv contribution of every (row, selected key) pair, dS' Q + P do_lat contracted over all
 //   96 heads at once, rounded to bf16 and stored per pair (one workgroup per row and 192 latent dims,
 //   Q and do_lat of its dims as MFMA B operands in LDS, dS' and P streamed from g in 32-key tiles).
-//   A counting sort of the chunk's pairs by key (k_pairs_count, two scan passes, k_pairs_scatter)
+//   A counting sort of the chunk's pairs by key (k_pairs_count, two scan passes, k_pairs_place)
 //   runs first and gives each pair its position in key order; k_dkv stores each contribution there,
 //   and k_dkv_sum adds each key's contiguous contributions to dkv, one wave per key: no float atomics,
 //   which run at a fixed rate per lane (about 330 G lane operations per second on MI355X).
@@ -410,9 +410,9 @@ __global__ __launch_bounds__(kDkWaves * kWave, 1) void k_dkv(DkvArgs a) {
 // Summing the contributions per key without atomics on dkv: a counting sort of the chunk's usable
 // (row, j) pairs by key index (count, exclusive scan, and each pair's position in key order), then
 // k_dkv stores each pair's contribution at its position and one wave per key adds its contiguous
-// 576-float rows to dkv, which no other wave of the pass touches. The positions within a key come
-// from integer atomics (one per pair, not one per element), so the order of a key's pairs, and the
-// last bits of its sum, may differ from run to run.
+// 576-float rows to dkv, which no other wave of the pass touches. A pair's rank among its key's pairs
+// is the value its count's integer atomic returns (one per pair, not one per element), so the order of
+// a key's pairs, and the last bits of its sum, may differ from run to run.
 __device__ __forceinline__ int pair_key(const DkvListArgs& a, int crow, int j) {
   const int t_row = a.row0 + a.chunk_r0 + crow;
   const int keff = min(a.k, t_row - doc_begin(a.cu, a.n_docs, t_row) + 1);
@@ -421,14 +421,15 @@ __device__ __forceinline__ int pair_key(const DkvListArgs& a, int crow, int j) {
   return (v >= 0 && v < a.T) ? v : -1;
 }
 
+// count[key] += 1 per pair; list takes the pair's rank among its key's pairs (-1 without a usable key).
 __global__ __launch_bounds__(256) void k_pairs_count(DkvListArgs a) {
   const int j = blockIdx.x * 256 + threadIdx.x, crow = blockIdx.y;
   if (j >= a.k) return;
   const int key = pair_key(a, crow, j);
-  if (key >= 0) atomicAdd(a.count + key, 1);
+  a.list[static_cast<int64_t>(crow) * a.k + j] = key >= 0 ? atomicAdd(a.count + key, 1) : -1;
 }
 
-// Exclusive scan of count[0 .. T) into start (start[T] = total) and cursor, in two passes over
+// Exclusive scan of count[0 .. T) into start (start[T] = total), in two passes over
 // tiles of kPairScanTile keys: the tiles' sums, then each tile adds the sums of the tiles before it to
 // a workgroup scan of its own keys. 256 threads, 16 consecutive keys each.
 constexpr int kScanPer = kPairScanTile / 256;
@@ -494,22 +495,21 @@ __global__ __launch_bounds__(256) void k_pairs_scan(DkvListArgs a) {
   for (int w = 0; w < wave; ++w) run += s_wave[w];
 #pragma unroll
   for (int e = 0; e < kScanPer; ++e) {
-    if (i0 + e < a.T) {
-      a.start[i0 + e] = run;
-      a.cursor[i0 + e] = run;
-    }
+    if (i0 + e < a.T) a.start[i0 + e] = run;
     run += c[e];
   }
   if (b == gridDim.x - 1 && threadIdx.x == 255) a.start[a.T] = run;  // the total
 }
 
-// Each pair's position in key order (-1 for a pair without a usable key): k_dkv stores the pair's
-// contribution there, so that each key's contributions are contiguous for k_dkv_sum.
-__global__ __launch_bounds__(256) void k_pairs_scatter(DkvListArgs a) {
+// Each pair's position in key order, start[key] + its rank (-1 stays for a pair without a usable
+// key): k_dkv stores the pair's contribution there, so that each key's contributions are contiguous
+// for k_dkv_sum.
+__global__ __launch_bounds__(256) void k_pairs_place(DkvListArgs a) {
   const int j = blockIdx.x * 256 + threadIdx.x, crow = blockIdx.y;
   if (j >= a.k) return;
-  const int key = pair_key(a, crow, j);
-  a.list[static_cast<int64_t>(crow) * a.k + j] = key >= 0 ? atomicAdd(a.cursor + key, 1) : -1;
+  int* slot = a.list + static_cast<int64_t>(crow) * a.k + j;
+  const int rank = *slot;
+  if (rank >= 0) *slot = a.start[pair_key(a, crow, j)] + rank;
 }
 
 // One wave per key: the sum of its pairs' contributions, contiguous in contrib at positions
@@ -673,7 +673,7 @@ hipError_t launch_pairs_sort(const DkvListArgs& a, hipStream_t st) {
   const dim3 tiles((a.T + kPairScanTile - 1) / kPairScanTile);
   hipLaunchKernelGGL(k_pairs_tile_sums, tiles, dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_pairs_scan, tiles, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_pairs_scatter, pairs, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_pairs_place, pairs, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

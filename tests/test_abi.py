@@ -222,19 +222,19 @@ def test_backward_host_checks():
     nb = L.dsa_bwd_workspace_size(ctypes.byref(s))
     # the forward's workspace, then per chunk of (here all) 1,024 rows: do, do_lat, delta, g (dS' and P
     # of the 96 heads for every selected key, k rounded up to 32), the bf16 dkv contribution of every
-    # (row, selected key) pair, and the counting sort of the pairs by key (count, start, cursor, list, and
+    # (row, selected key) pair, and the counting sort of the pairs by key (count, start, list, and
     # the scan's sums over tiles of 4,096 keys), and the sink's per-(row, head) gradient terms
     al = lambda x: (x + 255) // 256 * 256
     cr, g_stride, T, k = 1024 * 96, (s.topk + 31) // 32 * 32, s.T, s.topk
     assert nb == (dsa.dsa_workspace_size(s) + al(cr * 128 * 2) + al(cr * 512 * 2) + al(cr * 4)
                   + al(1024 * g_stride * 192 * 2) + al(1024 * k * 576 * 2) + al(T * 4) + al((T + 1) * 4)
-                  + al(T * 4) + al(1024 * k * 4) + al((T + 4095) // 4096 * 4) + al(cr * 4))
+                  + al(1024 * k * 4) + al((T + 4095) // 4096 * 4) + al(cr * 4))
     # longer inputs are taken in chunks of 2,048 rows, so the chunk regions stop growing there
     s2 = _shape(T=8192)
     g2, c2, T2 = (s2.topk + 31) // 32 * 32, 2048 * 96, 8192
     assert L.dsa_bwd_workspace_size(ctypes.byref(s2)) == (
         dsa.dsa_workspace_size(s2) + al(c2 * 128 * 2) + al(c2 * 512 * 2) + al(c2 * 4) + al(2048 * g2 * 192 * 2)
-        + al(2048 * s2.topk * 576 * 2) + al(T2 * 4) + al((T2 + 1) * 4) + al(T2 * 4) + al(2048 * s2.topk * 4)
+        + al(2048 * s2.topk * 576 * 2) + al(T2 * 4) + al((T2 + 1) * 4) + al(2048 * s2.topk * 4)
         + al((T2 + 4095) // 4096 * 4) + al(c2 * 4))
     args = [fake] * 12
     assert L.dsa_sparse_mla_bwd(ctypes.byref(_shape(T=1024, topk=256, H_I=4, d_I=64, H=16)), *args, fake, nb,
