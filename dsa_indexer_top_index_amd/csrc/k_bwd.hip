@@ -562,15 +562,19 @@ __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dW_UV[h] += o_lat[rows, h]^T do[rows, h]: a workgroup per (head, 256 rows), eight waves of 64
+// dW_UV[h] += o_lat[rows, h]^T do[rows, h]: a workgroup per (head, kDwRows rows), eight waves of 64
 // latent dims x 128 outputs; K = rows in steps of 16 staged in LDS (o_lat 16 x 512, do 16 x 128) in
-// the forward's tile layout and read transposed for both operands.
-constexpr int kDwRows = 256;
+// the forward's tile layout and read transposed for both operands. The copies run kDwDepth steps
+// ahead through a ring of kDwDepth + 1 buffers, and each workgroup adds its 512 x 128 partial sums
+// with atomics once, so the rows per workgroup set the number of atomics.
+constexpr int kDwRows = 1024;
 constexpr int kDwWaves = 8;
+constexpr int kDwDepth = 4;
+constexpr int kDwRing = kDwDepth + 1;
 
 __global__ __launch_bounds__(kDwWaves * kWave, 1) void k_dwuv(DwArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_o[2][16 * kVDim * 2];  // 2 x 16 KB
-  __shared__ __attribute__((aligned(16))) uint8_t s_d[2][16 * kODim * 2];  // 2 x 4 KB
+  __shared__ __attribute__((aligned(16))) uint8_t s_o[kDwRing][16 * kVDim * 2];  // 16 KB each
+  __shared__ __attribute__((aligned(16))) uint8_t s_d[kDwRing][16 * kODim * 2];  // 4 KB each
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int g16 = lane >> 4, i16 = lane & 15;
@@ -579,14 +583,14 @@ __global__ __launch_bounds__(kDwWaves * kWave, 1) void k_dwuv(DwArgs a) {
   const int nsteps = (min(kDwRows, a.rows - r0) + 15) / 16;
   const int H = a.H;
   const int my_row = i16 ^ (4 * g16);
-  // copies of step s: o_lat columns 4c + g16 (c < 16) and do columns 4c + g16 (c < 4): 20 copies, waves
-  // take copies wave, wave + 8, wave + 16
-  auto issue = [&](int s) {
+  // copies of step s into ring slot b: o_lat columns 4c + g16 (c < 16) and do columns 4c + g16
+  // (c < 4): 20 copies, waves take copies wave, wave + 8, wave + 16 (three for waves 0-3, two for 4-7)
+  auto issue = [&](int s, int b) {
     const int row = min(r0 + 16 * s + my_row, a.rows - 1);
     const int64_t rh = static_cast<int64_t>(row) * H + h;
     for (int c = wave; c < 20; c += kDwWaves) {
-      if (c < 16) copy16_to_lds(a.o_lat + rh * kVDim + 8 * (4 * c + g16), lds_ptr(lds_addr_of(&s_o[s & 1][0]) + 1024 * c));
-      else copy16_to_lds(a.d_o + rh * kODim + 8 * (4 * (c - 16) + g16), lds_ptr(lds_addr_of(&s_d[s & 1][0]) + 1024 * (c - 16)));
+      if (c < 16) copy16_to_lds(a.o_lat + rh * kVDim + 8 * (4 * c + g16), lds_ptr(lds_addr_of(&s_o[b][0]) + 1024 * c));
+      else copy16_to_lds(a.d_o + rh * kODim + 8 * (4 * (c - 16) + g16), lds_ptr(lds_addr_of(&s_d[b][0]) + 1024 * (c - 16)));
     }
   };
   const int hh = lane >> 5, chh = g16 & 1, s4 = i16 >> 2, q4 = i16 & 3;
@@ -600,12 +604,20 @@ __global__ __launch_bounds__(kDwWaves * kWave, 1) void k_dwuv(DwArgs a) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16{};
-  issue(0);
+  for (int s = 0; s < kDwDepth && s < nsteps; ++s) issue(s, s);
+  int slot = 0;  // ring slot of step s
   for (int s = 0; s < nsteps; ++s) {
-    wait_vmem();
-    __syncthreads();
-    if (s + 1 < nsteps) issue(s + 1);
-    const uint32_t ob = lds_addr_of(&s_o[s & 1][0]), db = lds_addr_of(&s_d[s & 1][0]);
+    // step s's copies of this wave have landed once at most the later steps' copies are outstanding
+    if (s + kDwDepth - 1 < nsteps) {
+      if (wave < 4) wait_vmem_le<3 * (kDwDepth - 1)>();
+      else wait_vmem_le<2 * (kDwDepth - 1)>();
+    } else {
+      wait_vmem();
+    }
+    barrier_lds();  // every wave's copies of step s have landed; step s - 1's slot is free
+    if (s + kDwDepth < nsteps) issue(s + kDwDepth, slot == 0 ? kDwRing - 1 : slot - 1);
+    const uint32_t ob = lds_addr_of(&s_o[slot][0]), db = lds_addr_of(&s_d[slot][0]);
+    slot = slot == kDwRing - 1 ? 0 : slot + 1;
     // this lane's 8 K values are rows 16*s + 8*hh + (0..3) and + 4 .. 7
     const int valid_lo = min(max(a.rows - (r0 + 16 * s + 8 * hh), 0), 8);
     u32x4 bv[4];
