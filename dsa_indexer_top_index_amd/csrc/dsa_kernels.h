@@ -176,7 +176,8 @@ struct DkvListArgs {
   int* count;              // [T] pairs per key (zeroed before the count pass)
   int* start;              // [T + 1] exclusive prefix sums of count
   int* bsum;               // [ceil(T / kPairScanTile)] count sums of the scan's blocks
-  int* list;               // [chunk_rows * k] position of pair r * k + j in key order (-1: no usable key)
+  int* list;               // [chunk_rows * k] position of pair r * k + j in key order (-1: no usable key);
+                           // the count pass leaves the pair's rank among its key's pairs there first
   const uint16_t* contrib; // as DkvArgs::contrib
   float* dkv;              // [T, 576], added to
 };
