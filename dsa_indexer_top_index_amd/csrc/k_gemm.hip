@@ -8,12 +8,13 @@
 // Kernel design (both operands K-contiguous): a workgroup computes a 256 x 256 output tile with
 // eight waves of 128 x 64 (four 32-row M tiles x two 32-column N tiles, 128 FP32 accumulators per
 // lane) on v_mfma_f32_32x32x16_bf16. K advances in steps of 64: the 256 x 64 tiles of x and W_o
-// are staged in LDS by asynchronous 16-byte global->LDS copies (eight per wave and step), double
-// buffered with one barrier per step, so the next step's copies run under this step's MFMAs. A tile
-// row is 128 bytes; its 16-byte granules are XOR-swizzled by (row / 2) % 8, so that the 16 lanes of
-// each operand read hit 16 distinct bank groups. Blocks are renumbered so that each XCD runs
-// patches of four row bands by a few column bands at a time, whose operand bands its L2 shares. The
-// epilogue stages bf16 outputs in the then idle LDS and stores 16 bytes per lane.
+// are staged in LDS by asynchronous 16-byte global->LDS copies (eight per wave and step, from a
+// scalar base with 32-bit lane offsets), double buffered with one barrier per step, so the next
+// step's copies run under this step's MFMAs. A tile row is 128 bytes; its 16-byte granules are
+// XOR-swizzled by (row / 2) % 8, so that the 16 lanes of each operand read hit 16 distinct bank
+// groups. Blocks are renumbered so that each XCD runs patches of four row bands by a few column
+// bands at a time, whose operand bands its L2 shares. The epilogue stages bf16 outputs in the then
+// idle LDS and stores 16 bytes per lane.
 #include "dsa_device.h"
 #include "dsa_kernels.h"
 
@@ -28,7 +29,7 @@ __device__ __forceinline__ uint32_t g_off(int r, int g) { return 128u * r + 16u 
 
 __global__ __launch_bounds__(kGWaves * kWave, 1) void k_gemm_nt(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t[2][2][kGTileBytes];  // [buffer][x, W_o]: 128 KB
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int nbn = a.N / kGN, nbm = (a.M + kGM - 1) / kGM;
   // Consecutive logical blocks run on one XCD; they walk groups of kGroupM row bands column by
@@ -46,22 +47,26 @@ __global__ __launch_bounds__(kGWaves * kWave, 1) void k_gemm_nt(GemmArgs a) {
 
   // Copy j of this wave (0..7) fills rows 8*part .. +8 of tile `tile` (0: x, 1: W_o), part =
   // (8*wave + j) % 32: lane i brings granule (i % 8) ^ ((row / 2) % 8) of row 8*part + i/8.
-  const uint16_t* src[8];
-  uint32_t dst[8];
+  // The copies of a wave read one operand (waves 0-3: x, 4-7: W_o) from a scalar base, the first row
+  // of the workgroup's band, with 32-bit per-lane byte offsets (under 256 rows x K x 2 bytes).
+  const int tile = wave >> 2;
+  const uint16_t* sbase = tile == 0 ? a.A + static_cast<int64_t>(m0) * K : a.B + static_cast<int64_t>(n0) * K;
+  uint32_t voff[8], dst[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int c = 8 * wave + j, tile = c >> 5, part = c & 31;
+    const int part = (8 * wave + j) & 31;
     const int row = 8 * part + (lane >> 3);
     const int g = (lane & 7) ^ ((row >> 1) & 7);
-    const int64_t grow = tile == 0 ? min(m0 + row, a.M - 1) : n0 + row;
-    src[j] = (tile == 0 ? a.A : a.B) + grow * K + 8 * g;
+    const int brow = tile == 0 ? min(m0 + row, a.M - 1) - m0 : row;
+    voff[j] = static_cast<uint32_t>(brow * K + 8 * g) * 2u;
     dst[j] = static_cast<uint32_t>(tile * kGTileBytes + 1024 * part);
   }
   const uint32_t lds0 = lds_addr_of(&s_t[0][0][0]);
   auto issue = [&](int kt) {
     const uint32_t b = lds0 + (kt & 1) * 2 * kGTileBytes;
+    const uint16_t* sb = sbase + kt * kGK;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) copy16_to_lds(src[j] + kt * kGK, lds_ptr(b + dst[j]));
+    for (int j = 0; j < 8; ++j) copy16_to_lds_imm<0>(sb, voff[j], __builtin_amdgcn_readfirstlane(b + dst[j]));
   };
 
   f32x16 acc[4][2];
