@@ -43,6 +43,16 @@ constexpr int kBwMaxIdx = 2048;
 constexpr int kGCols = 2 * 96;  // g: dS' of the 96 heads, then P
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Copies C, C + 2, .. < 18 of a gathered 16-key tile: lane i of copy c reads 16 bytes at
+// kv + voff + 64c and writes them to the tile at 1024c + 16i.
+template <int C>
+__device__ __forceinline__ void bw_gather_copies(const uint16_t* kv, uint32_t voff, uint32_t base) {
+  if constexpr (C < 18) {
+    copy16_to_lds_imm<64 * C>(kv, voff, base + (1024 - 64) * C);
+    bw_gather_copies<C + 2>(kv, voff, base);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdPrepArgs a) {
   const int64_t rh = static_cast<int64_t>(blockIdx.x) * 8 + threadIdx.x / 32;  // (row, head) within the chunk
@@ -258,11 +268,10 @@ __global__ __launch_bounds__(kBrWaves * kWave, 1) void k_sparse_mla_bwd_row(BwdA
       constexpr int i0 = kBrCompute * kBrDqC + kBrDqX * cw;
       const int my_row = i16 ^ (4 * g16);
       auto issue_tile = [&](int t) {
-        const int s_key = s_idx[t * kBwKeys + my_row];
-        const uint16_t* src = a.kv + static_cast<int64_t>(max(s_key, 0)) * kLatent + 8 * g16;
-        const uint32_t base = ring + (t % kBrRing) * kBwTileBytes;
-#pragma unroll
-        for (int c = cw; c < 18; c += 2) copy16_to_lds(src + 32 * c, lds_ptr(base + 1024 * c));
+        // one 32-bit byte offset per tile (row s_key of kv, granule g16); copy c's 64-byte step is
+        // the immediate offset, which moves the LDS address too
+        const uint32_t voff = static_cast<uint32_t>(max(s_idx[t * kBwKeys + my_row], 0)) * (kLatent * 2) + 16 * g16;
+        bw_gather_copies<cw>(a.kv, voff, ring + (t % kBrRing) * kBwTileBytes);
       };
       f32x16 dq[kBrDqX];
 #pragma unroll
