@@ -522,51 +522,66 @@ __global__ __launch_bounds__(256) void k_pairs_place(DkvListArgs a) {
 }
 
 // One wave per key: the sum of its pairs' contributions, contiguous in contrib at positions
-// start[key] .. start[key + 1] - 1 (four pairs in flight; lane l < 48 takes dims 4l .. 4l + 3 of
-// each group), added to dkv[key].
+// start[key] .. start[key + 1] - 1, added to dkv[key]. The two half-waves take alternate pairs (lane
+// 32h + l, l < 24, takes pairs start + h, start + h + 2, .. and dims 8l .. 8l + 7 of each group, in
+// 16-byte loads, four pairs in flight), and the halves' sums are added before the store.
 __global__ __launch_bounds__(256) void k_dkv_sum(DkvListArgs a) {
   const int key = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (key >= a.T) return;
   const int p0 = a.start[key], p1 = a.start[key + 1];
-  if (p0 == p1 || lane >= kDkGDims / 4) return;
+  if (p0 == p1) return;  // uniform over the wave
+  const int h = lane >> 5, l = lane & 31;
+  const bool active = l < kDkGDims / 8;
   const int64_t gstride = static_cast<int64_t>(a.chunk_rows) * a.k * kDkGDims;  // bf16 per group
-  const uint16_t* __restrict__ base = a.contrib + 4 * lane;
-  float acc[kDkGroups][4];
+  const uint16_t* __restrict__ base = a.contrib + 8 * (active ? l : 0);
+  float acc[kDkGroups][8];
 #pragma unroll
   for (int q = 0; q < kDkGroups; ++q)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[q][i] = 0.0f;
-  auto add = [&](const u32x2& w, int q) {
-    acc[q][0] += __uint_as_float(w[0] << 16);
-    acc[q][1] += __uint_as_float(w[0] & 0xffff0000u);
-    acc[q][2] += __uint_as_float(w[1] << 16);
-    acc[q][3] += __uint_as_float(w[1] & 0xffff0000u);
-  };
-  int p = p0;
-  for (; p + 4 <= p1; p += 4) {
-    u32x2 v[4][kDkGroups];
+    for (int i = 0; i < 8; ++i) acc[q][i] = 0.0f;
+  auto add = [&](const u32x4& w, int q) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint16_t* src = base + static_cast<int64_t>(p + u) * kDkGDims;
-#pragma unroll
-      for (int q = 0; q < kDkGroups; ++q) v[u][q] = *reinterpret_cast<const u32x2*>(src + gstride * q);
+    for (int i = 0; i < 4; ++i) {
+      acc[q][2 * i] += __uint_as_float(w[i] << 16);
+      acc[q][2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
     }
+  };
+  if (active) {
+    int p = p0 + h;
+    for (; p + 6 < p1; p += 8) {
+      u32x4 v[4][kDkGroups];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t* src = base + static_cast<int64_t>(p + 2 * u) * kDkGDims;
 #pragma unroll
-      for (int q = 0; q < kDkGroups; ++q) add(v[u][q], q);
+        for (int q = 0; q < kDkGroups; ++q) v[u][q] = *reinterpret_cast<const u32x4*>(src + gstride * q);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kDkGroups; ++q) add(v[u][q], q);
+    }
+    for (; p < p1; p += 2) {
+      const uint16_t* src = base + static_cast<int64_t>(p) * kDkGDims;
+#pragma unroll
+      for (int q = 0; q < kDkGroups; ++q) add(*reinterpret_cast<const u32x4*>(src + gstride * q), q);
+    }
   }
-  for (; p < p1; ++p) {
-    const uint16_t* src = base + static_cast<int64_t>(p) * kDkGDims;
+  // the upper half's sums onto the lower half (every lane takes part in the exchange)
 #pragma unroll
-    for (int q = 0; q < kDkGroups; ++q) add(*reinterpret_cast<const u32x2*>(src + gstride * q), q);
-  }
-  float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + 4 * lane;
+  for (int q = 0; q < kDkGroups; ++q)
 #pragma unroll
-  for (int q = 0; q < kDkGroups; ++q) {
-    f32x4* d = reinterpret_cast<f32x4*>(dst + kDkGDims * q);
-    const f32x4 o = *d;
-    *d = f32x4{o[0] + acc[q][0], o[1] + acc[q][1], o[2] + acc[q][2], o[3] + acc[q][3]};
+    for (int i = 0; i < 8; ++i) acc[q][i] += __shfl_xor(acc[q][i], 32);
+  if (h == 0 && active) {
+    float* dst = a.dkv + static_cast<int64_t>(key) * kLatent + 8 * l;
+#pragma unroll
+    for (int q = 0; q < kDkGroups; ++q)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x4* d = reinterpret_cast<f32x4*>(dst + kDkGDims * q + 4 * c);
+        const f32x4 o = *d;
+        *d = f32x4{o[0] + acc[q][4 * c], o[1] + acc[q][4 * c + 1], o[2] + acc[q][4 * c + 2], o[3] + acc[q][4 * c + 3]};
+      }
   }
 }
 
